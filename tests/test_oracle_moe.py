@@ -1,0 +1,207 @@
+"""Pins of the oracle's float64 MoE forward, dgrad and LoRA gradients.
+
+Pinned against: explicit scalar loops of the definition, torch float64 autograd
+of the same forward (weights held as constants), central finite differences,
+and invariants (routed-only dequantization, W4A4 batch invariance).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as fm
+from oracle import moe as om
+from oracle import quant as oq
+from oracle import routing as orr
+
+
+def _bf16(a):
+    return fm.bf16_round(np.asarray(a, dtype=np.float32))
+
+
+def make_layer(E=4, H=32, I=16, k=2, T=6, r=4, seed=0, fmt="nvfp4", act_quant=False, s=1.0):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal((T, H)))
+    wgu = _bf16(rng.standard_normal((E, 2 * I, H)) * 0.2)
+    wdn = _bf16(rng.standard_normal((E, H, I)) * 0.2)
+    A_gu = _bf16(rng.standard_normal((E, r, H)) * 0.1)
+    B_gu = _bf16(rng.standard_normal((E, 2 * I, r)) * 0.1)
+    A_dn = _bf16(rng.standard_normal((E, r, I)) * 0.1)
+    B_dn = _bf16(rng.standard_normal((E, H, r)) * 0.1)
+    if fmt == "nvfp4":
+        gu, dn = oq.quantize_nvfp4(wgu), oq.quantize_nvfp4(wdn)
+    else:
+        gu, dn = oq.quantize_nf4(wgu), oq.quantize_nf4(wdn)
+    w = om.MoEWeights(fmt, gu, dn, A_gu, B_gu, A_dn, B_dn, lora_scale=s, act_quant=act_quant)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    idx, tw = orr.route(lg, k)
+    dout = _bf16(rng.standard_normal((T, H)))
+    return w, x, idx, tw, dout, (wgu, wdn)
+
+
+def _loops_forward(w, x, idx, tw, round_points=True):
+    """The definition with scalar Python loops (float64), no matrix products."""
+    T, H = x.shape
+    k = idx.shape[1]
+    s = w.lora_scale
+    out = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            Wgu = om.expert_matrix(w.gu, e)
+            Wdn = om.expert_matrix(w.dn, e)
+            I = Wdn.shape[1]
+            r = w.A_gu.shape[1]
+            xt = [float(v) for v in x[t]]
+            U = [sum(float(w.A_gu[e, q, c]) * xt[c] for c in range(H)) for q in range(r)]
+            h = []
+            for n in range(2 * I):
+                base = sum(Wgu[n, c] * xt[c] for c in range(H))
+                lora = sum(float(w.B_gu[e, n, q]) * U[q] for q in range(r))
+                h.append(base + s * lora)
+            a = []
+            for i in range(I):
+                g, u = h[i], h[I + i]
+                val = g / (1.0 + np.exp(-g)) * u
+                a.append(float(_bf16([val])[0]) if round_points else val)
+            Ud = [sum(float(w.A_dn[e, q, i]) * a[i] for i in range(I)) for q in range(r)]
+            for c in range(H):
+                y = sum(Wdn[c, i] * a[i] for i in range(I))
+                y += s * sum(float(w.B_dn[e, c, q]) * Ud[q] for q in range(r))
+                out[t, c] += tw[t, j] * y
+    return out
+
+
+def test_forward_matches_scalar_loops():
+    w, x, idx, tw, _, _ = make_layer(E=3, H=16, I=16, k=2, T=4, r=2, seed=1, s=0.5)
+    out, _ = om.forward(w, x, idx, tw)
+    ref = _loops_forward(w, x, idx, tw)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def _torch_layer(w, x, idx, tw):
+    """Same forward in torch float64 (pure chain, no rounding points) for autograd."""
+    xs = torch.tensor(np.asarray(x, np.float64), requires_grad=True)
+    tws = torch.tensor(np.asarray(tw, np.float64), requires_grad=True)
+    lora = {n: torch.tensor(getattr(w, n).astype(np.float64), requires_grad=True)
+            for n in ("A_gu", "B_gu", "A_dn", "B_dn")}
+    T, H = x.shape
+    k = idx.shape[1]
+    s = w.lora_scale
+    out = torch.zeros((T, H), dtype=torch.float64)
+    for e in range(w.A_gu.shape[0]):
+        tt, jj = np.nonzero(idx == e)
+        if tt.size == 0:
+            continue
+        Wgu = torch.tensor(om.expert_matrix(w.gu, e))
+        Wdn = torch.tensor(om.expert_matrix(w.dn, e))
+        X = xs[tt]
+        h = X @ Wgu.T + s * (X @ lora["A_gu"][e].T) @ lora["B_gu"][e].T
+        I = Wdn.shape[1]
+        g, u = h[:, :I], h[:, I:]
+        a = torch.nn.functional.silu(g) * u
+        y = a @ Wdn.T + s * (a @ lora["A_dn"][e].T) @ lora["B_dn"][e].T
+        out = out.index_add(0, torch.tensor(tt), y * tws[tt, jj][:, None])
+    return out, xs, tws, lora
+
+
+def test_dgrad_and_lora_grads_match_torch_autograd():
+    w, x, idx, tw, dout, _ = make_layer(E=4, H=32, I=16, k=2, T=9, r=4, seed=2, s=0.7)
+    out, cache = om.forward(w, x, idx, tw, round_points=False)
+    dX, dtw, bwd = om.dgrad(w, cache, dout, tw, round_points=False)
+    dA_gu, dB_gu, dA_dn, dB_dn = om.lora_grad(w, cache, bwd, E=4)
+    tout, xs, tws, lora = _torch_layer(w, x, idx, tw)
+    assert np.allclose(out, tout.detach().numpy(), rtol=1e-12, atol=1e-12)
+    tout.backward(torch.tensor(np.asarray(dout, np.float64)))
+    assert np.allclose(dX, xs.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dtw, tws.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for mine, name in ((dA_gu, "A_gu"), (dB_gu, "B_gu"), (dA_dn, "A_dn"), (dB_dn, "B_dn")):
+        assert np.allclose(mine, lora[name].grad.numpy(), rtol=1e-10, atol=1e-12), name
+
+
+def test_dgrad_central_finite_differences():
+    w, x, idx, tw, dout, _ = make_layer(E=3, H=16, I=16, k=2, T=5, r=2, seed=3)
+    x64 = np.asarray(x, np.float64)
+    d64 = np.asarray(dout, np.float64)
+    _, cache = om.forward(w, x64, idx, tw, round_points=False)
+    dX, dtw, _ = om.dgrad(w, cache, d64, tw, round_points=False)
+    rng = np.random.default_rng(0)
+    v = rng.standard_normal(x64.shape)
+    eps = 1e-3
+    fp = (om.forward(w, x64 + eps * v, idx, tw, round_points=False)[0] * d64).sum()
+    fm_ = (om.forward(w, x64 - eps * v, idx, tw, round_points=False)[0] * d64).sum()
+    fd = (fp - fm_) / (2 * eps)
+    assert np.isclose(fd, (dX * v).sum(), rtol=1e-6)
+    vw = rng.standard_normal(tw.shape)
+    fp = (om.forward(w, x64, idx, tw + eps * vw, round_points=False)[0] * d64).sum()
+    fm_ = (om.forward(w, x64, idx, tw - eps * vw, round_points=False)[0] * d64).sum()
+    assert np.isclose((fp - fm_) / (2 * eps), (dtw * vw).sum(), rtol=1e-8)
+
+
+def test_rounding_points_are_small_perturbations():
+    w, x, idx, tw, dout, _ = make_layer(E=4, H=64, I=32, k=2, T=16, r=4, seed=4)
+    o1, c1 = om.forward(w, x, idx, tw, round_points=True)
+    o0, c0 = om.forward(w, x, idx, tw, round_points=False)
+    fro, _ = om.rel_errors(o1, o0)
+    assert 0 < fro < 5e-3
+    d1, _, _ = om.dgrad(w, c1, dout, tw, round_points=True)
+    d0, _, _ = om.dgrad(w, c0, dout, tw, round_points=False)
+    fro, _ = om.rel_errors(d1, d0)
+    assert 0 < fro < 5e-3
+
+
+def test_token_subset_rows_equal_full_rows():
+    for aq in (False, True):
+        w, x, idx, tw, dout, _ = make_layer(E=4, H=32, I=16, k=2, T=12, r=4, seed=5, act_quant=aq)
+        full, cf = om.forward(w, x, idx, tw)
+        sub, cs = om.forward(w, x, idx, tw, tokens=[2, 7, 11])
+        # equal up to float64 summation order inside the matrix products
+        assert np.allclose(sub, full[[2, 7, 11]], rtol=1e-12, atol=1e-14)
+        dfull, _, _ = om.dgrad(w, cf, dout, tw)
+        dsub, _, _ = om.dgrad(w, cs, dout, tw)
+        assert np.allclose(dsub, dfull[[2, 7, 11]], rtol=1e-12, atol=1e-14)
+
+
+def test_w4a4_uses_quantized_activations_and_differs_from_w4a16():
+    w, x, idx, tw, _, _ = make_layer(E=4, H=64, I=32, k=2, T=10, r=4, seed=6, act_quant=True)
+    out_q, _ = om.forward(w, x, idx, tw)
+    w.act_quant = False
+    out_b, _ = om.forward(w, x, idx, tw)
+    fro, _ = om.rel_errors(out_q, out_b)
+    assert 0.01 < fro < 0.3
+
+
+def test_routed_only_dequantization():
+    """Experts that get no token are never read: poisoning their scales changes nothing."""
+    w, x, idx, tw, dout, _ = make_layer(E=6, H=32, I=16, k=2, T=5, r=4, seed=7)
+    idx = np.where(idx >= 4, idx % 4, idx)           # experts 4, 5 get no token
+    idx[:, 1] = np.where(idx[:, 1] == idx[:, 0], (idx[:, 0] + 1) % 4, idx[:, 1])
+    out, c = om.forward(w, x, idx, tw)
+    dX, dtw, _ = om.dgrad(w, c, dout, tw)
+    w.gu.scales[4:] = 0x7F                           # E4M3 NaN
+    w.dn.scales[4:] = 0x7F
+    out2, c2 = om.forward(w, x, idx, tw)
+    dX2, dtw2, b2 = om.dgrad(w, c2, dout, tw)
+    assert np.isfinite(out2).all() and (out2 == out).all() and (dX2 == dX).all()
+    grads = om.lora_grad(w, c2, b2, E=6)
+    for g in grads:
+        assert (g[4:] == 0).all()
+
+
+def test_nf4_against_bf16_sanity_band():
+    """NF4 vs unquantized weights: output error of the order the nf4moe page reports (0.15)."""
+    w, x, idx, tw, dout, (wgu, wdn) = make_layer(E=4, H=128, I=64, k=2, T=32, r=4, seed=8, fmt="nf4")
+    out_q, cq = om.forward(w, x, idx, tw)
+    dq, _, _ = om.dgrad(w, cq, dout, tw)
+    ref = om.MoEWeights("nvfp4", None, None, w.A_gu, w.B_gu, w.A_dn, w.B_dn)
+    saved = om.expert_matrix
+    try:
+        om.expert_matrix = lambda q, e: (wgu if q == "gu" else wdn)[e].astype(np.float64)
+        ref.gu, ref.dn = "gu", "dn"
+        out_b, cb = om.forward(ref, x, idx, tw)
+        db, _, _ = om.dgrad(ref, cb, dout, tw)
+    finally:
+        om.expert_matrix = saved
+    fro, _ = om.rel_errors(out_q, out_b)
+    cos = (dq * db).sum() / np.linalg.norm(dq) / np.linalg.norm(db)
+    assert 0.03 < fro < 0.3
+    assert cos > 0.97
