@@ -1,0 +1,536 @@
+// NVFP4 (Four-Over-Six) and NF4 quantizers and dequantizers for gfx950.
+//
+// NVFP4: one E4M3 scale per 16 consecutive elements along the last axis and
+// one FP32 scale per 2-D matrix (weights) or per row (token activations); each
+// block tries the scale t/6 and t/4 and keeps the one whose FP32 squared error,
+// measured against the target scaled down once by the inverse of
+// amax / (6 * M), is lower (4-bitter page, section "Four-Over-Six for RL
+// Weights and Activations"; GLM page, section "Why can't we just transpose the
+// one copy?").  NF4: blocksize 64, FP32 absmax (nf4moe page, section "The fix:
+// dequant-on-forward for routed experts").
+//
+// Every rounding is a single IEEE round-to-nearest-even operation (this file is
+// compiled with -ffp-contract=off and correctly rounded FP32 division), so codes
+// and scales are deterministic bit patterns.
+//
+// Memory layout: one thread owns one 16-element block (32 bytes of bf16 in,
+// 8 bytes of codes and 1 scale byte out); consecutive threads own consecutive
+// blocks, so a wave reads 2 KB and writes 512 B of codes contiguously.  The
+// per-tensor amax is a separate pass over groups of matrices small enough that
+// the quantize pass re-reads them from the 256 MB Infinity Cache.
+#include "common.h"
+#include "nf4_levels.inc"
+
+namespace bqm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 1024;
+
+// Round a non-negative finite float to the E4M3FN grid (nearest, ties to even,
+// saturating at 448) and return its code 0..126.
+__device__ __forceinline__ uint32_t e4m3_rne_satfinite(float t) {
+  uint32_t code;
+  if (t < 0x1p-6f) {
+    // subnormal step 2^-9 is the ulp of 2^14: one correctly rounded add
+    float s = t + 16384.0f;
+    code = __float_as_uint(s) - 0x46800000u;
+  } else {
+    uint32_t u = __float_as_uint(t);
+    code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
+  }
+  return code < 126u ? code : 126u;
+}
+
+// Round a non-negative float to the E2M1 grid {0,.5,1,1.5,2,3,4,6} (nearest,
+// ties to the even code, saturating at 6).  Adding C = 2^22, 2^23 or 2^24 makes
+// the float32 ulp equal to the grid step of the value's range (0.5, 1, 2), so
+// one correctly rounded add performs the rounding; code parity equals the
+// parity of the float32 mantissa there.
+__device__ __forceinline__ float e2m1_round(float v) {
+  float c = v < 2.0f ? 0x1p22f : (v < 4.0f ? 0x1p23f : 0x1p24f);
+  float q = (v + c) - c;
+  return fminf(q, 6.0f);
+}
+
+// grid value -> magnitude code
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  return q <= 2.0f ? (uint32_t)(q * 2.0f) : (q == 3.0f ? 5u : (q == 4.0f ? 6u : 7u));
+}
+
+// One scale candidate: codes (magnitudes only) and the squared error, summed in
+// element order 0..15 in FP32.
+__device__ __forceinline__ float candidate(const float (&ay)[16], float sb, uint32_t &c_lo,
+                                           uint32_t &c_hi) {
+  float r = sb > 0.0f ? 1.0f / sb : 0.0f;
+  float err = 0.0f;
+  c_lo = 0u;
+  c_hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float v = ay[i] * r;
+    float q = e2m1_round(v);
+    float d = ay[i] - q * sb;  // q*sb is exact (<= 6 significant bits)
+    err = err + d * d;
+    uint32_t c = e2m1_code(q);
+    if (i < 8)
+      c_lo |= c << (4 * i);
+    else
+      c_hi |= c << (4 * (i - 8));
+  }
+  return err;
+}
+
+// Quantize one block of 16 bf16 values held as 8 words; returns the E4M3 code.
+template <bool kFos>
+__device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float s_enc, uint32_t &lo,
+                                                  uint32_t &hi) {
+  float ay[16];
+  float t = 0.0f;
+  uint32_t sg_lo = 0u, sg_hi = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y0 = bf16_lo(w[i]) * s_enc;
+    float y1 = bf16_hi(w[i]) * s_enc;
+    ay[2 * i] = fabsf(y0);
+    ay[2 * i + 1] = fabsf(y1);
+    t = fmaxf(t, fmaxf(ay[2 * i], ay[2 * i + 1]));
+    uint32_t s0 = (w[i] >> 15) & 1u, s1 = w[i] >> 31;
+    if (i < 4) {
+      sg_lo |= (s0 << (8 * i + 3)) | (s1 << (8 * i + 7));
+    } else {
+      sg_hi |= (s0 << (8 * (i - 4) + 3)) | (s1 << (8 * (i - 4) + 7));
+    }
+  }
+  uint32_t sb6 = e4m3_rne_satfinite(t / 6.0f);
+  uint32_t l6, h6;
+  float e6 = candidate(ay, e4m3_to_f32(sb6), l6, h6);
+  uint32_t sb = sb6;
+  lo = l6;
+  hi = h6;
+  if (kFos) {
+    uint32_t sb4 = e4m3_rne_satfinite(t * 0.25f);  // == t/4 exactly rounded
+    uint32_t l4, h4;
+    float e4 = candidate(ay, e4m3_to_f32(sb4), l4, h4);
+    if (e4 < e6) {
+      sb = sb4;
+      lo = l4;
+      hi = h4;
+    }
+  }
+  lo |= sg_lo;
+  hi |= sg_hi;
+  return sb;
+}
+
+__device__ __forceinline__ void load_block16(const uint4 *p, uint32_t (&w)[8]) {
+  uint4 a = p[0], b = p[1];
+  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+}
+
+__device__ __forceinline__ uint32_t absmax_bits_u32(uint32_t w) {
+  uint32_t a = w & 0x7FFFu, b = (w >> 16) & 0x7FFFu;
+  return a > b ? a : b;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint32_t t = __shfl_xor(v, o, 64);
+    v = v > t ? v : t;
+  }
+  return v;
+}
+
+// Block-wide max of non-negative values; every thread gets the result.
+__device__ __forceinline__ uint32_t block_max_u(uint32_t v, uint32_t *red) {
+  v = wave_max_u(v);
+  int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  uint32_t m = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = m > red[i] ? m : red[i];
+  __syncthreads();
+  return m;
+}
+
+// Decode scale from amax: s_dec = fl(A / fl(6M)), s_enc = fl(1 / s_dec).
+__device__ __forceinline__ void global_scale(float amax, float denom, float &s_dec, float &s_enc) {
+  s_dec = amax > 0.0f ? amax / denom : 1.0f;
+  s_enc = 1.0f / s_dec;
+}
+
+// ---------------------------------------------------------------------------
+// kernels
+// ---------------------------------------------------------------------------
+// Pass 1 of the per-tensor quantizer: partial amax (as bf16 magnitude bits) of
+// P contiguous chunks of each matrix.  grid = (P, n_mat_chunk).
+__global__ void __launch_bounds__(kThreads) nvfp4_amax_partials(const uint4 *__restrict__ x,
+                                                                int64_t vec_per_mat, int P,
+                                                                uint32_t *__restrict__ partials) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.y;
+  const uint4 *xm = x + m * vec_per_mat;
+  int64_t cs = (vec_per_mat + P - 1) / P;
+  int64_t b = (int64_t)blockIdx.x * cs, e = b + cs < vec_per_mat ? b + cs : vec_per_mat;
+  uint32_t mx = 0u;
+  for (int64_t i = b + threadIdx.x; i < e; i += kThreads) {
+    uint4 v = xm[i];
+    uint32_t a = absmax_bits_u32(v.x), c = absmax_bits_u32(v.y);
+    uint32_t d = absmax_bits_u32(v.z), f = absmax_bits_u32(v.w);
+    a = a > c ? a : c;
+    d = d > f ? d : f;
+    a = a > d ? a : d;
+    mx = mx > a ? mx : a;
+  }
+  mx = block_max_u(mx, red);
+  if (threadIdx.x == 0) partials[m * P + blockIdx.x] = mx;
+}
+
+// Pass 2 of the per-tensor quantizer.  grid = (G, n_mat_chunk).
+template <bool kFos>
+__global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
+    const uint4 *__restrict__ x, int64_t blocks_per_mat, const uint32_t *__restrict__ partials, int P,
+    const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.y;
+  float s_dec, s_enc;
+  if (s_dec_in) {
+    s_dec = s_dec_in[m];
+    s_enc = 1.0f / s_dec;
+  } else {
+    uint32_t a = 0u;
+    for (int i = threadIdx.x; i < P; i += kThreads) {
+      uint32_t v = partials[m * P + i];
+      a = a > v ? a : v;
+    }
+    a = block_max_u(a, red);
+    global_scale(__uint_as_float(a << 16), denom, s_dec, s_enc);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) s_dec_out[m] = s_dec;
+  const uint4 *xm = x + m * blocks_per_mat * 2;
+  uint2 *cm = codes + m * blocks_per_mat;
+  uint8_t *sm = scales + m * blocks_per_mat;
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < blocks_per_mat;
+       blk += (int64_t)gridDim.x * kThreads) {
+    uint32_t w[8];
+    load_block16(xm + 2 * blk, w);
+    uint32_t lo, hi;
+    uint32_t sb = quant_block16<kFos>(w, s_enc, lo, hi);
+    cm[blk] = make_uint2(lo, hi);
+    sm[blk] = (uint8_t)sb;
+  }
+}
+
+// Per-row quantizer: one wave per row (the per-token activation scale, computed
+// across the row in the same kernel).  rows_total = n_mat * rows.
+template <bool kFos>
+__global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
+    const uint4 *__restrict__ x, int64_t rows_total, int64_t blocks_per_row,
+    const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes,
+    uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= rows_total) return;
+  const uint4 *xr = x + row * blocks_per_row * 2;
+  float s_dec, s_enc;
+  if (s_dec_in) {
+    s_dec = s_dec_in[row];
+    s_enc = 1.0f / s_dec;
+  } else {
+    uint32_t mx = 0u;
+    for (int64_t i = lane; i < blocks_per_row * 2; i += 64) {
+      uint4 v = xr[i];
+      uint32_t a = absmax_bits_u32(v.x), c = absmax_bits_u32(v.y);
+      uint32_t d = absmax_bits_u32(v.z), f = absmax_bits_u32(v.w);
+      a = a > c ? a : c;
+      d = d > f ? d : f;
+      a = a > d ? a : d;
+      mx = mx > a ? mx : a;
+    }
+    mx = wave_max_u(mx);
+    global_scale(__uint_as_float(mx << 16), denom, s_dec, s_enc);
+  }
+  if (lane == 0) s_dec_out[row] = s_dec;
+  for (int64_t blk = lane; blk < blocks_per_row; blk += 64) {
+    uint32_t w[8];
+    load_block16(xr + 2 * blk, w);
+    uint32_t lo, hi;
+    uint32_t sb = quant_block16<kFos>(w, s_enc, lo, hi);
+    codes[row * blocks_per_row + blk] = make_uint2(lo, hi);
+    scales[row * blocks_per_row + blk] = (uint8_t)sb;
+  }
+}
+
+// NVFP4 dequantize: bf16(fl(fl(val*sb) * s_dec)); one thread per 16-block.
+__global__ void __launch_bounds__(kThreads) nvfp4_dequant(const uint2 *__restrict__ codes,
+                                                          const uint8_t *__restrict__ scales,
+                                                          const float *__restrict__ s_dec,
+                                                          int64_t nblocks, int64_t blocks_per_scale,
+                                                          uint4 *__restrict__ y) {
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+       blk += (int64_t)gridDim.x * kThreads) {
+    uint2 c = codes[blk];
+    float sb = e4m3_to_f32(scales[blk]);
+    float sd = s_dec[blk / blocks_per_scale];
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t nib = ((i < 8 ? c.x : c.y) >> (4 * (i & 7))) & 0xFu;
+      float v = __uint_as_float(e2m1_mag_bits(nib & 7u) | ((nib & 8u) << 28));
+      float r = (v * sb) * sd;
+      uint32_t b = f32_to_bf16(r);
+      if (i & 1)
+        out[i >> 1] |= b << 16;
+      else
+        out[i >> 1] = b;
+    }
+    y[2 * blk] = make_uint4(out[0], out[1], out[2], out[3]);
+    y[2 * blk + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+  }
+}
+
+__constant__ float c_nf4_levels[16] = BQM_NF4_LEVELS;
+__constant__ float c_nf4_mids[15] = BQM_NF4_MIDPOINTS;
+
+// NF4 quantize: one thread per 64-block (128 B in, 32 B codes + 4 B absmax out).
+__global__ void __launch_bounds__(kThreads) nf4_quant(const uint4 *__restrict__ x, int64_t nblocks,
+                                                      uint4 *__restrict__ codes,
+                                                      float *__restrict__ absmax) {
+  float mids[15];
+#pragma unroll
+  for (int j = 0; j < 15; ++j) mids[j] = c_nf4_mids[j];
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+       blk += (int64_t)gridDim.x * kThreads) {
+    uint32_t w[32];
+    const uint4 *p = x + 8 * blk;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint4 v = p[i];
+      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      uint32_t a = absmax_bits_u32(w[i]);
+      mx = mx > a ? mx : a;
+    }
+    float a = __uint_as_float(mx << 16);
+    float r = a > 0.0f ? 1.0f / a : 0.0f;
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      float xv = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+      float xn = xv * r;
+      uint32_t code = 0u;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) code += xn > mids[j] ? 1u : 0u;
+      if ((i & 7) == 0)
+        out[i >> 3] = code;
+      else
+        out[i >> 3] |= code << (4 * (i & 7));
+    }
+    codes[2 * blk] = make_uint4(out[0], out[1], out[2], out[3]);
+    codes[2 * blk + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+    absmax[blk] = a;
+  }
+}
+
+// NF4 dequantize: bf16(fl(level[code] * absmax)).
+__global__ void __launch_bounds__(kThreads) nf4_dequant(const uint4 *__restrict__ codes,
+                                                        const float *__restrict__ absmax,
+                                                        int64_t nblocks, uint4 *__restrict__ y) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = c_nf4_levels[threadIdx.x];
+  __syncthreads();
+  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
+       blk += (int64_t)gridDim.x * kThreads) {
+    uint4 c0 = codes[2 * blk], c1 = codes[2 * blk + 1];
+    uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    float a = absmax[blk];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t b = f32_to_bf16(lv[(c[q] >> (4 * i)) & 0xFu] * a);
+        if (i & 1)
+          o[i >> 1] |= b << 16;
+        else
+          o[i >> 1] = b;
+      }
+      y[8 * blk + q] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+int grid_for(int64_t work_items, int per_block = kThreads, int cap = 65536) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (int)(g < cap ? g : cap);
+}
+
+bqm_status check_qtensor(const bqm_qtensor *q, const char *who, bool need_sdec) {
+  BQM_REQUIRE(q, BQM_ERR_INVALID_ARG, "%s: qtensor is NULL", who);
+  BQM_REQUIRE(q->fmt == BQM_FMT_NVFP4 || q->fmt == BQM_FMT_NF4, BQM_ERR_INVALID_ARG,
+              "%s: unknown format %d", who, q->fmt);
+  BQM_REQUIRE(q->n_mat >= 0 && q->rows >= 0 && q->cols >= 0, BQM_ERR_INVALID_ARG,
+              "%s: negative size", who);
+  int64_t blk = q->fmt == BQM_FMT_NVFP4 ? 16 : 64;
+  BQM_REQUIRE(q->cols % blk == 0, BQM_ERR_SHAPE, "%s: cols=%lld is not a multiple of %lld", who,
+              (long long)q->cols, (long long)blk);
+  int64_t n = q->n_mat * q->rows * q->cols;
+  if (n == 0) return BQM_OK;
+  BQM_REQUIRE(q->codes && q->scales, BQM_ERR_INVALID_ARG, "%s: codes/scales pointer is NULL", who);
+  BQM_REQUIRE(aligned16(q->codes) && aligned16(q->scales), BQM_ERR_ALIGN,
+              "%s: codes/scales not 16-byte aligned", who);
+  if (q->fmt == BQM_FMT_NVFP4) {
+    BQM_REQUIRE(q->scale_mode == BQM_SCALE_PER_TENSOR || q->scale_mode == BQM_SCALE_PER_ROW,
+                BQM_ERR_INVALID_ARG, "%s: bad scale_mode %d", who, q->scale_mode);
+    if (need_sdec) {
+      BQM_REQUIRE(q->s_dec, BQM_ERR_INVALID_ARG, "%s: s_dec pointer is NULL", who);
+      BQM_REQUIRE(aligned16(q->s_dec), BQM_ERR_ALIGN, "%s: s_dec not 16-byte aligned", who);
+    }
+  }
+  return BQM_OK;
+}
+
+int64_t amax_partials_per_mat(int64_t elems) {
+  int64_t p = cdiv(elems, 65536);
+  if (p < 1) p = 1;
+  return p < kMaxPartials ? p : kMaxPartials;
+}
+
+// Matrices per amax+quantize group: the group's bf16 bytes stay below this so
+// the second read of the group is served by the Infinity Cache.
+constexpr int64_t kGroupBytes = 192ll << 20;
+
+}  // namespace
+}  // namespace bqm
+
+using namespace bqm;
+
+extern "C" size_t bqm_quantize_nvfp4_workspace_size(int64_t n_mat, int64_t rows, int64_t cols,
+                                                    int32_t scale_mode) {
+  if (scale_mode == BQM_SCALE_PER_ROW || n_mat <= 0) return 0;
+  return (size_t)n_mat * (size_t)amax_partials_per_mat(rows * cols) * sizeof(uint32_t);
+}
+
+extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six,
+                                         const float *s_dec_in, bqm_qtensor *out, void *ws,
+                                         size_t ws_bytes, void *stream) {
+  bqm_status st = check_qtensor(out, "bqm_quantize_nvfp4", true);
+  if (st != BQM_OK) return st;
+  BQM_REQUIRE(out->fmt == BQM_FMT_NVFP4, BQM_ERR_INVALID_ARG,
+              "bqm_quantize_nvfp4: out->fmt must be BQM_FMT_NVFP4");
+  const int64_t n_mat = out->n_mat, rows = out->rows, cols = out->cols;
+  const int64_t per_mat = rows * cols;
+  if (n_mat * per_mat == 0) return BQM_OK;
+  BQM_REQUIRE(x, BQM_ERR_INVALID_ARG, "bqm_quantize_nvfp4: x is NULL");
+  BQM_REQUIRE(aligned16(x), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: x not 16-byte aligned");
+  BQM_REQUIRE(!s_dec_in || aligned16(s_dec_in), BQM_ERR_ALIGN,
+              "bqm_quantize_nvfp4: s_dec_in not 16-byte aligned");
+  out->four_over_six = four_over_six ? 1 : 0;
+  const float denom = four_over_six ? 6.0f * 256.0f : 6.0f * 448.0f;
+  hipStream_t s = as_stream(stream);
+  const uint4 *xv = reinterpret_cast<const uint4 *>(x);
+  uint2 *cv = reinterpret_cast<uint2 *>(out->codes);
+  uint8_t *sv = reinterpret_cast<uint8_t *>(out->scales);
+  if (out->scale_mode == BQM_SCALE_PER_ROW) {
+    const int64_t rows_total = n_mat * rows;
+    const int64_t bpr = cols / 16;
+    int grid = (int)cdiv(rows_total, kThreads / 64);
+    if (four_over_six)
+      nvfp4_quant_rows<true><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
+                                                       out->s_dec);
+    else
+      nvfp4_quant_rows<false><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
+                                                        out->s_dec);
+    return launch_status("nvfp4_quant_rows");
+  }
+  const int P = (int)amax_partials_per_mat(per_mat);
+  const size_t need = s_dec_in ? 0 : bqm_quantize_nvfp4_workspace_size(n_mat, rows, cols, 0);
+  BQM_REQUIRE(ws_bytes >= need && (need == 0 || ws), BQM_ERR_WORKSPACE,
+              "bqm_quantize_nvfp4: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  BQM_REQUIRE(!ws || aligned16(ws), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: ws not 16-byte aligned");
+  uint32_t *partials = reinterpret_cast<uint32_t *>(ws);
+  const int64_t blocks_per_mat = per_mat / 16;
+  int64_t group = kGroupBytes / (per_mat * 2);
+  if (group < 1) group = 1;
+  if (group > 65535) group = 65535;
+  // enough workgroups per matrix to fill the chip with the whole group in flight
+  int64_t g = cdiv(2048, group);
+  int64_t gmax = cdiv(blocks_per_mat, kThreads);
+  if (g > gmax) g = gmax;
+  if (g < 1) g = 1;
+  for (int64_t m0 = 0; m0 < n_mat; m0 += group) {
+    int64_t nm = n_mat - m0 < group ? n_mat - m0 : group;
+    const uint4 *xg = xv + m0 * (per_mat / 8);
+    uint32_t *pg = partials ? partials + m0 * P : nullptr;
+    if (!s_dec_in) {
+      nvfp4_amax_partials<<<dim3(P, (unsigned)nm), kThreads, 0, s>>>(xg, per_mat / 8, P, pg);
+      st = launch_status("nvfp4_amax_partials");
+      if (st != BQM_OK) return st;
+    }
+    const float *sdi = s_dec_in ? s_dec_in + m0 : nullptr;
+    if (four_over_six)
+      nvfp4_quant_tensor<true><<<dim3((unsigned)g, (unsigned)nm), kThreads, 0, s>>>(
+          xg, blocks_per_mat, pg, P, sdi, denom, cv + m0 * blocks_per_mat, sv + m0 * blocks_per_mat,
+          out->s_dec + m0);
+    else
+      nvfp4_quant_tensor<false><<<dim3((unsigned)g, (unsigned)nm), kThreads, 0, s>>>(
+          xg, blocks_per_mat, pg, P, sdi, denom, cv + m0 * blocks_per_mat, sv + m0 * blocks_per_mat,
+          out->s_dec + m0);
+    st = launch_status("nvfp4_quant_tensor");
+    if (st != BQM_OK) return st;
+  }
+  return BQM_OK;
+}
+
+extern "C" bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out, void *stream) {
+  bqm_status st = check_qtensor(out, "bqm_quantize_nf4", false);
+  if (st != BQM_OK) return st;
+  BQM_REQUIRE(out->fmt == BQM_FMT_NF4, BQM_ERR_INVALID_ARG,
+              "bqm_quantize_nf4: out->fmt must be BQM_FMT_NF4");
+  const int64_t n = out->n_mat * out->rows * out->cols;
+  if (n == 0) return BQM_OK;
+  BQM_REQUIRE(x, BQM_ERR_INVALID_ARG, "bqm_quantize_nf4: x is NULL");
+  BQM_REQUIRE(aligned16(x), BQM_ERR_ALIGN, "bqm_quantize_nf4: x not 16-byte aligned");
+  const int64_t nb = n / 64;
+  nf4_quant<<<grid_for(nb), kThreads, 0, as_stream(stream)>>>(
+      reinterpret_cast<const uint4 *>(x), nb, reinterpret_cast<uint4 *>(out->codes),
+      reinterpret_cast<float *>(out->scales));
+  return launch_status("nf4_quant");
+}
+
+extern "C" bqm_status bqm_dequantize(const bqm_qtensor *q, uint16_t *y, void *stream) {
+  bqm_status st = check_qtensor(q, "bqm_dequantize", true);
+  if (st != BQM_OK) return st;
+  const int64_t n = q->n_mat * q->rows * q->cols;
+  if (n == 0) return BQM_OK;
+  BQM_REQUIRE(y, BQM_ERR_INVALID_ARG, "bqm_dequantize: y is NULL");
+  BQM_REQUIRE(aligned16(y), BQM_ERR_ALIGN, "bqm_dequantize: y not 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  if (q->fmt == BQM_FMT_NVFP4) {
+    const int64_t nb = n / 16;
+    const int64_t per_scale =
+        q->scale_mode == BQM_SCALE_PER_ROW ? q->cols / 16 : q->rows * q->cols / 16;
+    nvfp4_dequant<<<grid_for(nb), kThreads, 0, s>>>(
+        reinterpret_cast<const uint2 *>(q->codes), reinterpret_cast<const uint8_t *>(q->scales),
+        q->s_dec, nb, per_scale, reinterpret_cast<uint4 *>(y));
+    return launch_status("nvfp4_dequant");
+  }
+  const int64_t nb = n / 64;
+  nf4_dequant<<<grid_for(nb), kThreads, 0, s>>>(reinterpret_cast<const uint4 *>(q->codes),
+                                               reinterpret_cast<const float *>(q->scales), nb,
+                                               reinterpret_cast<uint4 *>(y));
+  return launch_status("nf4_dequant");
+}

@@ -1,0 +1,248 @@
+// Softmax top-k routing and the stable counting-sort permutation of routed rows.
+//
+// The expert module of the nf4moe page receives top_k_index / top_k_weights
+// [T, k] and visits, for every expert that was hit, its tokens in token order
+// (a one-hot mask per expert, then torch.where).  Here the R = T*k pairs
+// f = t*k + j are sorted by expert with a deterministic three-pass counting sort
+// (chunk histograms -> per-expert prefix over chunks and experts -> in-order
+// scatter), so the GEMMs find every expert's rows as one contiguous segment of
+// the permutation and no count ever travels to the host.
+#include "common.h"
+#include "internal.h"
+
+namespace bqm {
+namespace {
+
+constexpr int kChunk = 2048;  // routed pairs per histogram/scatter chunk
+
+// One wave per token: the E logits are spread over the 64 lanes (up to 16 per lane).
+__global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ logits, int64_t T,
+                                                   int E, int k, int renorm,
+                                                   int32_t *__restrict__ topk_idx,
+                                                   float *__restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float *lg = logits + t * E;
+  float v[16];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int e = lane + 64 * j;
+    v[j] = e < E ? lg[e] : -INFINITY;
+    mx = fmaxf(mx, v[j]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int e = lane + 64 * j;
+    if (e < E) sum += expf(v[j] - mx);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  uint32_t taken = 0u;  // bit j: this lane's slot j already chosen
+  float wsum = 0.0f;
+  float wsel[16];
+  int isel[16];
+  for (int r = 0; r < k; ++r) {
+    // lane-local best among untaken slots (larger value, then lower index)
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      int e = lane + 64 * j;
+      bool ok = e < E && !((taken >> j) & 1u);
+      if (ok && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      float ov = __shfl_xor(bv, o, 64);
+      int oi = __shfl_xor(bi, o, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    float w = expf(bv - mx) / sum;
+    wsel[r] = w;
+    isel[r] = bi;
+    wsum += w;
+  }
+  if (lane == 0) {
+    for (int r = 0; r < k; ++r) {
+      topk_idx[t * k + r] = isel[r];
+      topk_w[t * k + r] = renorm ? wsel[r] / wsum : wsel[r];
+    }
+  }
+}
+
+// Pass 1: per-chunk expert histogram.
+__global__ void __launch_bounds__(256) perm_hist(const int32_t *__restrict__ idx, int64_t R, int E,
+                                                 int32_t *__restrict__ counts) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  int64_t b = (int64_t)blockIdx.x * kChunk;
+  for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
+    int64_t f = b + i;
+    if (f < R) atomicAdd(&hist[idx[f]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = hist[e];
+}
+
+// Pass 2 (one block): base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e];
+// offsets = exclusive prefix of the per-expert totals.  Optionally the prefix
+// of ceil(count / bm) (row tiles per expert) for the grouped GEMMs.
+__global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, int nchunks, int E,
+                                                  int32_t *__restrict__ offsets, int bm,
+                                                  int32_t *__restrict__ tile_off) {
+  __shared__ int32_t tot[1025];
+  __shared__ int32_t til[1025];
+  int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) {
+      int32_t v = counts[(int64_t)c * E + e];
+      counts[(int64_t)c * E + e] = run;
+      run += v;
+    }
+    tot[e] = run;
+    til[e] = bm > 0 ? (run + bm - 1) / bm : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t s = 0, st = 0;
+    for (int i = 0; i < E; ++i) {
+      int32_t v = tot[i], w = til[i];
+      tot[i] = s;
+      til[i] = st;
+      s += v;
+      st += w;
+    }
+    tot[E] = s;
+    til[E] = st;
+  }
+  __syncthreads();
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += tot[e];
+    offsets[e] = tot[e];
+    if (tile_off) tile_off[e] = til[e];
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = tot[E];
+    if (tile_off) tile_off[E] = til[E];
+  }
+}
+
+// Pass 3: one wave scatters its chunk in order; equal experts inside a group of
+// 64 pairs are ranked by lane, so the result is the stable order.
+__global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ idx, int64_t R, int E,
+                                                   const int32_t *__restrict__ base,
+                                                   int32_t *__restrict__ perm,
+                                                   int32_t *__restrict__ inv) {
+  extern __shared__ int32_t cnt[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  const int64_t b = (int64_t)blockIdx.x * kChunk;
+  for (int s = 0; s < kChunk; s += 64) {
+    int64_t f = b + s + lane;
+    int e = f < R ? idx[f] : -1;
+    int rank = 0;
+    bool last = true;
+    for (int q = 0; q < 64; ++q) {
+      int eq = __shfl(e, q, 64);
+      if (eq == e) {
+        if (q < lane) ++rank;
+        if (q > lane) last = false;
+      }
+    }
+    int pos = 0;
+    if (e >= 0) pos = cnt[e] + rank;
+    __syncthreads();
+    if (e >= 0) {
+      perm[pos] = (int32_t)f;
+      inv[f] = pos;
+      if (last) cnt[e] = pos + 1;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int64_t R, int E) {
+  return (size_t)cdiv(R, kChunk) * (size_t)E * sizeof(int32_t);
+}
+
+bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
+                          int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off,
+                          hipStream_t s) {
+  const int nchunks = (int)cdiv(R, kChunk);
+  if (R > 0) {
+    perm_hist<<<nchunks, 256, E * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws);
+    bqm_status st = launch_status("perm_hist");
+    if (st != BQM_OK) return st;
+  }
+  perm_scan<<<1, 1024, 0, s>>>(counts_ws, nchunks, E, offsets, bm, tile_off);
+  bqm_status st = launch_status("perm_scan");
+  if (st != BQM_OK) return st;
+  if (R > 0) {
+    perm_scatter<<<nchunks, 64, E * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws, perm, inv);
+    st = launch_status("perm_scatter");
+  }
+  return st;
+}
+
+}  // namespace bqm
+
+using namespace bqm;
+
+extern "C" bqm_status bqm_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renorm,
+                                int32_t *topk_idx, float *topk_w, void *stream) {
+  BQM_REQUIRE(T >= 0, BQM_ERR_INVALID_ARG, "bqm_route: T < 0");
+  BQM_REQUIRE(E >= 1 && E <= 1024, BQM_ERR_SHAPE, "bqm_route: E=%d outside [1, 1024]", E);
+  BQM_REQUIRE(k >= 1 && k <= E && k <= 16, BQM_ERR_SHAPE, "bqm_route: k=%d outside [1, min(E,16)]",
+              k);
+  if (T == 0) return BQM_OK;
+  BQM_REQUIRE(logits && topk_idx && topk_w, BQM_ERR_INVALID_ARG, "bqm_route: NULL pointer");
+  BQM_REQUIRE(aligned16(logits) && aligned16(topk_idx) && aligned16(topk_w), BQM_ERR_ALIGN,
+              "bqm_route: pointer not 16-byte aligned");
+  route_kernel<<<(unsigned)cdiv(T, 4), 256, 0, as_stream(stream)>>>(logits, T, E, k, renorm,
+                                                                    topk_idx, topk_w);
+  return launch_status("route_kernel");
+}
+
+extern "C" size_t bqm_permute_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || k < 1) return 0;
+  return permute_ws_bytes(T * k, E);
+}
+
+extern "C" bqm_status bqm_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
+                                  int32_t *perm, int32_t *inv, int32_t *offsets, void *ws,
+                                  size_t ws_bytes, void *stream) {
+  BQM_REQUIRE(T >= 0, BQM_ERR_INVALID_ARG, "bqm_permute: T < 0");
+  BQM_REQUIRE(E >= 1 && E <= 1024, BQM_ERR_SHAPE, "bqm_permute: E=%d outside [1, 1024]", E);
+  BQM_REQUIRE(k >= 1 && k <= E, BQM_ERR_SHAPE, "bqm_permute: k=%d outside [1, E]", k);
+  BQM_REQUIRE(offsets, BQM_ERR_INVALID_ARG, "bqm_permute: offsets is NULL");
+  BQM_REQUIRE(aligned16(offsets), BQM_ERR_ALIGN, "bqm_permute: offsets not 16-byte aligned");
+  const int64_t R = T * k;
+  size_t need = permute_ws_bytes(R, E);
+  BQM_REQUIRE((need == 0 || ws) && ws_bytes >= need, BQM_ERR_WORKSPACE,
+              "bqm_permute: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  BQM_REQUIRE(!ws || aligned16(ws), BQM_ERR_ALIGN, "bqm_permute: ws not 16-byte aligned");
+  if (R > 0) {
+    BQM_REQUIRE(topk_idx && perm && inv, BQM_ERR_INVALID_ARG, "bqm_permute: NULL pointer");
+    BQM_REQUIRE(aligned16(topk_idx) && aligned16(perm) && aligned16(inv), BQM_ERR_ALIGN,
+                "bqm_permute: pointer not 16-byte aligned");
+  }
+  return permute_launch(topk_idx, R, E, perm, inv, offsets, reinterpret_cast<int32_t *>(ws), 0,
+                        nullptr, as_stream(stream));
+}

@@ -1,0 +1,201 @@
+/*
+ * bqm.h - C ABI of the MI355X (gfx950) library for the routed-expert MoE layer
+ * over frozen 4-bit block-quantized expert weights with a trainable bf16 LoRA.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless the comment says "host".  The caller
+ *     owns every buffer, including workspaces, and keeps it alive until the
+ *     work queued on `stream` has finished.  The library allocates and frees
+ *     nothing and keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on it: no host synchronisation, no
+ *     device-to-host copy.
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are dense
+ *     row-major (the last index is contiguous).
+ *   - Arguments are checked on the host before anything is launched.  A failed
+ *     check returns a negative bqm_status and sets a thread-local message
+ *     (bqm_last_error); nothing is enqueued in that case.  A launch failure
+ *     returns BQM_ERR_HIP with the HIP error string.  Non-finite input data are
+ *     outside the contract and are not scanned for.
+ *   - Device pointers must be 16-byte aligned.
+ *
+ * Page references are to the source pages: "Getting GLM-5.2 NVFP4 Post-Training
+ * off the ground" (GLM page), "The 4-bitter Lesson: Balancing Stability and
+ * Performance in NVFP4 RL" (4-bitter page) and "nf4moe - QLoRA for a 743B
+ * Fused-MoE" (nf4moe page).
+ */
+#ifndef BQM_H
+#define BQM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQM_ABI_VERSION 1
+
+typedef enum {
+  BQM_OK = 0,
+  BQM_ERR_INVALID_ARG = -1, /* null pointer, bad enum, negative size */
+  BQM_ERR_SHAPE = -2,       /* sizes that break a block or tile rule */
+  BQM_ERR_ALIGN = -3,       /* a device pointer not 16-byte aligned */
+  BQM_ERR_UNSUPPORTED = -4, /* a valid request this build does not implement */
+  BQM_ERR_WORKSPACE = -5,   /* workspace missing or too small */
+  BQM_ERR_HIP = -6          /* a HIP launch or runtime error */
+} bqm_status;
+
+typedef enum { BQM_FMT_NVFP4 = 1, BQM_FMT_NF4 = 2 } bqm_format;
+typedef enum { BQM_SCALE_PER_TENSOR = 0, BQM_SCALE_PER_ROW = 1 } bqm_scale_mode;
+
+/* A rowwise-quantized stack [n_mat, rows, cols]; blocks run along cols (the
+ * input dimension of a weight), the only copy ever stored (GLM page, section
+ * "The 4-bit base that was actually using 8-bit memory": the columnwise copy is
+ * dropped and the backward reads this one transposed).
+ *   codes : uint8 [n_mat, rows, cols/2]; element 2j is the low nibble of byte j,
+ *           element 2j+1 the high nibble.  NVFP4: E2M1 with the sign in bit 3.
+ *           NF4: index 0..15 into the NormalFloat codebook.
+ *   scales: NVFP4: uint8 E4M3FN bits [n_mat, rows, cols/16];
+ *           NF4: float absmax [n_mat, rows, cols/64].
+ *   s_dec : NVFP4 only: float [n_mat] (per tensor) or [n_mat*rows] (per row);
+ *           the value of an element is e2m1(code) * e4m3(scale) * s_dec.
+ *           NULL for NF4.
+ *   four_over_six: the mode the stack was quantized with (metadata). */
+typedef struct {
+  int32_t fmt; /* bqm_format */
+  int32_t scale_mode; /* bqm_scale_mode (NVFP4) */
+  int64_t n_mat, rows, cols;
+  uint8_t *codes;
+  void *scales;
+  float *s_dec;
+  int32_t four_over_six;
+  int32_t reserved;
+} bqm_qtensor;
+
+/* ABI version of the loaded library (BQM_ABI_VERSION). */
+int bqm_abi_version(void);
+
+/* Message for the last non-OK status returned on this host thread ("" if none).
+ * The string is owned by the library and valid until the next call on this thread. */
+const char *bqm_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * NVFP4 quantization with the Four-Over-Six block-scale choice.
+ * 4-bitter page, sections "Method" and "Four-Over-Six for RL Weights and
+ * Activations"; GLM page, section "Why can't we just transpose the one copy?".
+ *
+ * x: bf16 [n_mat, rows, cols], cols % 16 == 0.  out->fmt must be BQM_FMT_NVFP4
+ * and out->n_mat/rows/cols must equal the input sizes; out->codes, out->scales
+ * and out->s_dec receive the result, out->scale_mode selects
+ *   BQM_SCALE_PER_TENSOR: one FP32 scale per 2-D matrix (weights): A = max|x|
+ *                         over the matrix, s_dec = A / (6*M);
+ *   BQM_SCALE_PER_ROW:    one per row (per-token activation scales).
+ * M = 256 with four_over_six != 0 (then each 16-block tries the scale t/6 and
+ * t/4 and keeps the one with the lower FP32 squared error, ties keeping t/6),
+ * M = 448 otherwise.  s_dec_in (nullable, same shape as out->s_dec) replaces
+ * the amax-derived scale.  All rounding is round-to-nearest-even, E4M3 and E2M1
+ * saturate.  Result codes and scales are deterministic bit patterns.
+ * ws: per-tensor mode needs bqm_quantize_nvfp4_workspace_size() bytes of
+ * scratch (amax partials); per-row mode needs none (ws may be NULL). */
+size_t bqm_quantize_nvfp4_workspace_size(int64_t n_mat, int64_t rows, int64_t cols,
+                                         int32_t scale_mode);
+bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six, const float *s_dec_in,
+                              bqm_qtensor *out /* host struct */, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* NF4 quantization, blocksize 64 along cols, FP32 absmax per block: each
+ * element is multiplied by the FP32 reciprocal of its block's absmax and takes
+ * the nearest of the 16 NormalFloat levels, ties going to the lower level.
+ * nf4moe page, section "The fix: dequant-on-forward for routed experts".
+ * x: bf16 [n_mat, rows, cols], cols % 64 == 0; out->fmt == BQM_FMT_NF4. */
+bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out /* host struct */, void *stream);
+
+/* Dequantize a stack to bf16 [n_mat, rows, cols]:
+ *   NVFP4: bf16_rne(fl32(e2m1(code) * e4m3(scale)) * s_dec)  (one FP32 rounding)
+ *   NF4:   bf16_rne(fl32(level[code] * absmax))
+ * The same values (without the s_dec factor, which the GEMMs apply to their
+ * FP32 accumulators) are what the MoE GEMMs multiply. */
+bqm_status bqm_dequantize(const bqm_qtensor *q /* host struct */, uint16_t *y, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Routing (nf4moe page, the expert module's forward receives top_k_index and
+ * top_k_weights [T, k]).  Softmax over the E fp32 logits of each token, the k
+ * largest logits chosen in descending order, equal logits going to the lower
+ * expert index; weights are the chosen softmax probabilities (divided by their
+ * sum if renorm != 0).  logits f32 [T, E] -> topk_idx i32 [T, k], topk_w f32
+ * [T, k].  1 <= k <= E <= 1024, k <= 16.  T == 0 is a no-op. */
+bqm_status bqm_route(const float *logits, int64_t T, int32_t E, int32_t k, int32_t renorm,
+                     int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Stable counting sort of the R = T*k routed pairs f = t*k + j by expert (the
+ * order in which the nf4moe module visits them: expert, then token, then slot).
+ * perm i32 [R]: perm[pos] = f.  inv i32 [R]: inv[f] = pos.  offsets i32 [E+1]:
+ * exclusive prefix sum of per-expert counts.  Bit-exact, no atomics on the
+ * result order.  Indices must lie in [0, E) (not checked on the device).
+ * ws: bqm_permute_workspace_size() bytes. */
+size_t bqm_permute_workspace_size(int64_t T, int32_t E, int32_t k);
+bqm_status bqm_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_t *perm,
+                       int32_t *inv, int32_t *offsets, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The MoE layer.  Expert weights are stacks w_gu [E, 2I, H] (gate rows 0..I-1,
+ * up rows I..2I-1, the chunk(2, -1) split of the nf4moe module) and w_dn
+ * [E, H, I], both rowwise quantized (NVFP4 per-tensor, or NF4).  LoRA per
+ * expert in bf16: A_gu [E, r, H], B_gu [E, 2I, r], A_dn [E, r, I], B_dn [E, H, r]
+ * (all NULL when r == 0).  H % 64 == 0, I % 64 == 0, 1 <= k <= min(E, 16),
+ * 0 <= r <= 128.  act_quant = 1 selects the W4A4 path: the base GEMMs read
+ * per-token NVFP4 (Four-Over-Six) activations while LoRA reads bf16 ones
+ * (4-bitter page, section "Method"); NVFP4 weights only.
+ */
+typedef struct {
+  int64_t T, H, I;
+  int32_t E, k, r;
+  int32_t act_quant;
+  float lora_scale;
+  int32_t reserved;
+  bqm_qtensor w_gu;
+  bqm_qtensor w_dn;
+  const uint16_t *A_gu, *B_gu, *A_dn, *B_dn;
+} bqm_moe_desc;
+
+/* Bytes of the workspace shared by bqm_moe_fwd, bqm_moe_dgrad and
+ * bqm_lora_grad for this descriptor (host only).  The forward saves the
+ * routing permutation, the gate/up activations h [R, 2I], a [R, I], the LoRA
+ * intermediates and the expert outputs y [R, H] in it; the dgrad adds
+ * dh [R, 2I] and its LoRA intermediates for bqm_lora_grad. */
+size_t bqm_moe_workspace_size(const bqm_moe_desc *d);
+
+/* Forward: out[t] = sum_j topk_w[t,j] * y(t,j) with, for expert e = topk_idx[t,j],
+ *   h = X~ DQ(W_gu[e])^T + s (X A_gu[e]^T) B_gu[e]^T,  a = silu(h[:, :I]) * h[:, I:],
+ *   y = a~ DQ(W_dn[e])^T + s (a A_dn[e]^T) B_dn[e]^T
+ * (nf4moe page, the QuantizedNaiveMoe forward; only experts that receive tokens
+ * are read).  x bf16 [T, H], topk_idx i32 [T, k], topk_w f32 [T, k], y bf16
+ * [T, H] (the layer output).  Accumulation is FP32; h, a, y are stored bf16. */
+bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, const int32_t *topk_idx,
+                       const float *topk_w, uint16_t *out, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* Input gradient through DQ(Q(W)) (GLM page, section "The 4-bit base that was
+ * actually using 8-bit memory": dX = dY W contracts the output dimension, read
+ * from the single rowwise copy transposed, in bf16; 4-bitter page, section
+ * "Improving Gradient Stability").  Must follow bqm_moe_fwd with the same
+ * descriptor and workspace.  dy bf16 [T, H] -> dx bf16 [T, H] and, if
+ * dtopk_w != NULL, f32 [T, k] with dtopk_w[t,j] = <dy[t], y(t,j)>.
+ * Activation quantizers (W4A4) are the identity in this pass. */
+bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, void *ws, size_t ws_bytes,
+                         uint16_t *dx, float *dtopk_w, void *stream);
+
+/* LoRA weight gradients from the state the forward and dgrad left in ws (the
+ * adapter is the trained part; per-expert A/B on the 3-D stacks, nf4moe page,
+ * section "Does it actually train?").  f32 outputs dA_gu [E, r, H], dB_gu
+ * [E, 2I, r], dA_dn [E, r, I], dB_dn [E, H, r]; experts without tokens get
+ * zeros.  Requires r > 0. */
+bqm_status bqm_lora_grad(const bqm_moe_desc *d, void *ws, size_t ws_bytes, float *dA_gu,
+                         float *dB_gu, float *dA_dn, float *dB_dn, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BQM_H */

@@ -1,0 +1,90 @@
+"""The C ABI on the CPU: every declared symbol is exported, and argument checks
+fail with the documented status before anything is launched (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bqm.h")
+
+bqm = pytest.importorskip("bit_quantized_moe_amd._lib")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bqm.LIB_PATH):
+        pytest.fail("libbqm.so is not built (python -m bit_quantized_moe_amd.build)")
+    return bqm.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bqm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(bqm.EXPORTS)
+
+
+def test_abi_version(lib):
+    assert lib.bqm_abi_version() == 1
+
+
+def _q(fmt=1, n=1, rows=4, cols=32, mode=0, codes=16, scales=16, sdec=16):
+    return bqm.QTensorC(fmt, mode, n, rows, cols, codes, scales, sdec, 1, 0)
+
+
+def test_quantize_rejects_bad_shapes_and_pointers(lib):
+    q = _q(cols=24)
+    st = lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q), None, 0, None)
+    assert st == -2 and "multiple of 16" in bqm.bqm_last_error()
+    q = _q(codes=None)
+    assert lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q), None, 0, None) == -1
+    q = _q(codes=17)
+    assert lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q), None, 0, None) == -3
+    q = _q()
+    assert lib.bqm_quantize_nvfp4(None, 1, None, C.byref(q), None, 0, None) == -1
+    # per-tensor mode needs the amax workspace
+    assert lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q), None, 0, None) == -5
+    q = _q(fmt=2, cols=64)
+    assert lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q), None, 0, None) == -1
+    q = _q(fmt=2, cols=96)
+    assert lib.bqm_quantize_nf4(16, C.byref(q), None) == -2
+    q = _q(fmt=7)
+    assert lib.bqm_dequantize(C.byref(q), 16, None) == -1
+    q = _q(mode=5)
+    assert lib.bqm_dequantize(C.byref(q), 16, None) == -1
+
+
+def test_workspace_sizes(lib):
+    assert lib.bqm_quantize_nvfp4_workspace_size(4, 64, 256, 1) == 0
+    assert lib.bqm_quantize_nvfp4_workspace_size(4, 64, 256, 0) == 4 * 4
+    assert lib.bqm_quantize_nvfp4_workspace_size(2, 4096, 6144, 0) == 2 * 384 * 4
+    assert lib.bqm_permute_workspace_size(16384, 256, 8) == 64 * 256 * 4
+
+
+def test_route_and_permute_reject_bad_args(lib):
+    assert lib.bqm_route(16, 4, 8, 9, 0, 16, 16, None) == -2          # k > E
+    assert lib.bqm_route(16, 4, 2000, 2, 0, 16, 16, None) == -2       # E too large
+    assert lib.bqm_route(16, -1, 8, 2, 0, 16, 16, None) == -1
+    assert lib.bqm_route(None, 4, 8, 2, 0, 16, 16, None) == -1
+    assert lib.bqm_route(16, 4, 8, 2, 0, 20, 16, None) == -3
+    assert lib.bqm_route(None, 0, 8, 2, 0, None, None, None) == 0     # T == 0 is a no-op
+    assert lib.bqm_permute(16, 4, 8, 2, 16, 16, 16, None, 0, None) == -5
+    assert lib.bqm_permute(16, 4, 8, 0, 16, 16, 16, 16, 4096, None) == -2
+    assert lib.bqm_permute(16, 4, 8, 2, 16, 16, None, 16, 4096, None) == -1
+
+
+def test_empty_inputs_are_noops(lib):
+    q = _q(n=0)
+    assert lib.bqm_quantize_nvfp4(None, 1, None, C.byref(q), None, 0, None) == 0
+    assert lib.bqm_dequantize(C.byref(q), None, None) == 0
+    q = _q(fmt=2, n=0, cols=64)
+    assert lib.bqm_quantize_nf4(None, C.byref(q), None) == 0

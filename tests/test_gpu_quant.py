@@ -1,0 +1,189 @@
+"""GPU parity of the quantizers, dequantizers, router and permutation (bit-exact)."""
+import numpy as np
+import pytest
+
+from oracle import formats as fm
+from oracle import quant as oq
+from oracle import routing as orr
+from tests.gpu_util import gpu, log, np_f32, np_u8
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _bqm():
+    import bit_quantized_moe_amd as bqm
+    return bqm
+
+
+def gpu_quant_nvfp4(x, fos=True, per_row=False, s_dec_in=None):
+    import torch
+    bqm = _bqm()
+    n, rows, cols = x.shape
+    mode = bqm.SCALE_PER_ROW if per_row else bqm.SCALE_PER_TENSOR
+    q = bqm.alloc_qtensor(bqm.FMT_NVFP4, n, rows, cols, device=x.device, scale_mode=mode)
+    wsb = bqm.bqm_quantize_nvfp4_workspace_size(n, rows, cols, mode)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=x.device)
+    bqm.bqm_quantize_nvfp4(x, int(fos), s_dec_in, q, ws)
+    return q
+
+
+def check_nvfp4_against_oracle(x_dev, q, fos, per_row, s_dec_in=None, mats=None):
+    n_mat = x_dev.shape[0]
+    mats = range(n_mat) if mats is None else mats
+    for m in mats:
+        x = np_f32(x_dev[m:m + 1])
+        sdi = None
+        if s_dec_in is not None:
+            sdi = np_f32(s_dec_in).reshape((n_mat, -1) if per_row else (-1,))[m:m + 1]
+        ref = oq.quantize_nvfp4(x, four_over_six=fos, per_row=per_row, s_dec_in=sdi)
+        got_c = np_u8(q.codes[m])
+        got_s = np_u8(q.scales[m])
+        if per_row:
+            got_sd = np_f32(q.s_dec.view(n_mat, -1)[m])
+        else:
+            got_sd = np_f32(q.s_dec[m:m + 1])
+        bad = np.nonzero(got_c != ref.codes[0])
+        assert bad[0].size == 0, f"matrix {m}: {bad[0].size} code bytes differ, first at {bad[0][0]},{bad[1][0]}"
+        assert (got_s == ref.scales[0]).all(), f"matrix {m}: scales differ"
+        assert (got_sd.view(np.uint32) == ref.s_dec.reshape(-1).view(np.uint32)).all(), f"matrix {m}: s_dec"
+
+
+@pytest.mark.parametrize("fos", [True, False])
+@pytest.mark.parametrize("shape", [(3, 64, 256), (2, 37, 48), (1, 1, 16), (5, 130, 160)])
+def test_nvfp4_per_tensor_bit_exact(shape, fos):
+    dev = gpu()
+    log(f"nvfp4 per-tensor {shape} fos={fos}")
+    x = synth.normal(shape, 0.02, (90, shape[1], shape[2]), device="cpu", outliers=True).to(dev)
+    q = gpu_quant_nvfp4(x, fos=fos)
+    check_nvfp4_against_oracle(x, q, fos, per_row=False)
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 2048), (2, 33, 768), (1, 3, 6144)])
+def test_nvfp4_per_row_bit_exact(shape):
+    dev = gpu()
+    log(f"nvfp4 per-row {shape}")
+    x = synth.normal(shape, 1.0, (91, shape[1], shape[2]), device="cpu").to(dev)
+    q = gpu_quant_nvfp4(x, fos=True, per_row=True)
+    check_nvfp4_against_oracle(x, q, True, per_row=True)
+
+
+def test_nvfp4_given_scale_and_edge_blocks():
+    import torch
+    dev = gpu()
+    log("nvfp4 s_dec_in, zero blocks, worked example")
+    x = synth.normal((2, 16, 64), 0.02, (92,), device="cpu", outliers=True)
+    x[0, 3, 16:32] = 0.0
+    x[1] = 0.0                                   # an all-zero matrix: s_dec = 1
+    x[0, 5, :16] = -0.0
+    x = x.to(dev)
+    q = gpu_quant_nvfp4(x)
+    check_nvfp4_against_oracle(x, q, True, per_row=False)
+    sdi = torch.tensor([3e-4, 1.0], dtype=torch.float32, device=dev)
+    q2 = gpu_quant_nvfp4(x, s_dec_in=sdi)
+    check_nvfp4_against_oracle(x, q2, True, per_row=False, s_dec_in=sdi)
+    # the GLM page's worked example, padded to one 16-block per row
+    w = torch.zeros((1, 2, 16), dtype=torch.bfloat16)
+    w[0, :, :3] = torch.tensor([[1, 2, 3], [4, 5, 6]], dtype=torch.bfloat16)
+    q3 = gpu_quant_nvfp4(w.to(dev), fos=True)
+    y = torch.empty((1, 2, 16), dtype=torch.bfloat16, device=dev)
+    _bqm().bqm_dequantize(q3, y)
+    assert np_f32(y)[0, :, :3].tolist() == [[1, 2, 3], [4.5, 4.5, 6]]
+
+
+@pytest.mark.parametrize("per_row", [False, True])
+def test_nvfp4_dequantize_bit_exact(per_row):
+    import torch
+    dev = gpu()
+    x = synth.normal((3, 48, 128), 0.02, (93,), device="cpu", outliers=True).to(dev)
+    q = gpu_quant_nvfp4(x, per_row=per_row)
+    y = torch.empty_like(x)
+    _bqm().bqm_dequantize(q, y)
+    ref = oq.dequantize_nvfp4(oq.NVFP4Tensor(np_u8(q.codes), np_u8(q.scales),
+                                             np_f32(q.s_dec).reshape((3, -1) if per_row else (-1,)),
+                                             True, per_row))
+    assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("shape", [(2, 64, 256), (3, 5, 64), (1, 130, 192)])
+def test_nf4_quantize_dequantize_bit_exact(shape):
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    log(f"nf4 {shape}")
+    x = synth.normal(shape, 0.02, (94, shape[1]), device="cpu", outliers=True)
+    x[0, 0, :64] = 0.0
+    x = x.to(dev)
+    q = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev)
+    bqm.bqm_quantize_nf4(x, q)
+    ref = oq.quantize_nf4(np_f32(x))
+    assert (np_u8(q.codes) == ref.codes).all()
+    assert (np_f32(q.scales) == ref.absmax).all()
+    y = torch.empty_like(x)
+    bqm.bqm_dequantize(q, y)
+    assert (np_f32(y).view(np.uint32) == oq.dequantize_nf4(ref).view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(64, 8, 2, "normal"), (1000, 256, 8, "uniform"),
+                                        (333, 128, 8, "ties"), (50, 64, 16, "zipf"), (1, 1, 1, "normal")])
+def test_route_and_permute_bit_exact(T, E, k, kind):
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    log(f"route/permute T={T} E={E} k={k} {kind}")
+    rng = np.random.default_rng(T + E)
+    if kind == "ties":
+        lg = (rng.integers(-4, 4, size=(T, E)) * 0.25).astype(np.float32)
+    elif kind == "zipf":
+        lg = (rng.gumbel(size=(T, E)) - 1.1 * np.log(rng.permutation(E) + 1.0)).astype(np.float32)
+        lg[:, :8] = -np.inf
+    elif kind == "uniform":
+        lg = rng.random((T, E), dtype=np.float32)
+    else:
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+    lgd = torch.from_numpy(lg).to(dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    bqm.bqm_route(lgd, T, E, k, 0, idx, w)
+    ridx, rw = orr.route(lg, k)
+    assert (idx.cpu().numpy() == ridx).all()
+    assert np.allclose(w.cpu().numpy(), rw, rtol=2e-6, atol=1e-9)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(bqm.bqm_permute_workspace_size(T, E, k), 16), dtype=torch.uint8, device=dev)
+    bqm.bqm_permute(idx, T, E, k, perm, inv, off, ws)
+    p, iv, o = orr.permute(ridx, E)
+    assert (perm.cpu().numpy() == p).all() and (inv.cpu().numpy() == iv).all()
+    assert (off.cpu().numpy() == o).all()
+    _, rwr = orr.route(lg, k, renorm=True)
+    bqm.bqm_route(lgd, T, E, k, 1, idx, w)
+    assert np.allclose(w.cpu().numpy(), rwr, rtol=2e-6, atol=1e-9)
+
+
+def test_quantizer_full_size_sampled():
+    """The quantizer workload at full size (gate_up [256,4096,6144], down [256,6144,2048]);
+    sampled matrices are checked bit-exactly, every matrix against the closed-form s_dec."""
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    log("full-size quantizer: generating 19.3 GB of bf16 weights on the device")
+    wgu, wdn = synth.quantizer_stacks(device=dev)
+    for name, w, mats in (("gate_up", wgu, [0, 131, 255]), ("down", wdn, [7, 200])):
+        q = gpu_quant_nvfp4(w, fos=True)
+        torch.cuda.synchronize()
+        amax = w.view(w.shape[0], -1).abs().amax(dim=1).float().cpu()
+        s_ref = amax / 1536.0                      # IEEE division on the host
+        assert torch.equal(q.s_dec.cpu(), s_ref), name
+        log(f"  {name}: s_dec closed form ok; checking matrices {mats} against the oracle")
+        check_nvfp4_against_oracle(w, q, True, per_row=False, mats=mats)
+        # DQ(Q(DQ(Q(W)))) == DQ(Q(W)) with the scale held fixed, on the whole stack
+        y = torch.empty_like(w)
+        bqm.bqm_dequantize(q, y)
+        q2 = gpu_quant_nvfp4(y, fos=True, s_dec_in=q.s_dec)
+        y2 = torch.empty_like(w)
+        bqm.bqm_dequantize(q2, y2)
+        assert torch.equal(y2.view(torch.int16), y.view(torch.int16)), name
+        log(f"  {name}: round trip idempotent")
+        del y, y2, q2, q
+        torch.cuda.empty_cache()
