@@ -75,7 +75,7 @@ def load(path: str = LIB_PATH):
         "bqm_moe_workspace_size": (sz, [C.POINTER(MoEDescC)]),
         "bqm_moe_fwd": (C.c_int, [C.POINTER(MoEDescC), vp, vp, vp, vp, vp, sz, vp]),
         "bqm_moe_dgrad": (C.c_int, [C.POINTER(MoEDescC), vp, vp, sz, vp, vp, vp]),
-        "bqm_lora_grad": (C.c_int, [C.POINTER(MoEDescC), vp, sz, vp, vp, vp, vp, vp]),
+        "bqm_lora_grad": (C.c_int, [C.POINTER(MoEDescC), vp, vp, vp, sz, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -228,7 +228,7 @@ def bqm_moe_dgrad(d: MoEDesc, dy, ws, dx, dtopk_w=None, stream=None):
                                 _ptr(dx), _ptr(dtopk_w), _stream(stream)))
 
 
-def bqm_lora_grad(d: MoEDesc, ws, dA_gu, dB_gu, dA_dn, dB_dn, stream=None):
+def bqm_lora_grad(d: MoEDesc, x, dy, ws, dA_gu, dB_gu, dA_dn, dB_dn, stream=None):
     dc = d.c()
-    _check(load().bqm_lora_grad(C.byref(dc), _ptr(ws), ws.numel() * ws.element_size(), _ptr(dA_gu),
-                                _ptr(dB_gu), _ptr(dA_dn), _ptr(dB_dn), _stream(stream)))
+    _check(load().bqm_lora_grad(C.byref(dc), _ptr(x), _ptr(dy), _ptr(ws), ws.numel() * ws.element_size(),
+                                _ptr(dA_gu), _ptr(dB_gu), _ptr(dA_dn), _ptr(dB_dn), _stream(stream)))

@@ -1,16 +1,1084 @@
-// MoE layer entry points (placeholder until the grouped GEMMs land).
+// The routed-expert MoE layer over rowwise 4-bit expert weights with a bf16 LoRA:
+// forward, dgrad through DQ(Q(W)) and the LoRA weight gradients, on gfx950.
+//
+// Forward (nf4moe page, the QuantizedNaiveMoe forward): for each routed pair
+// (t, j) with expert e, h = X~ W~_gu^T + s (X A_gu^T) B_gu^T, a = silu(gate) * up
+// (the chunk(2, -1) halves of h), y = a~ W~_dn^T + s (a A_dn^T) B_dn^T, and the
+// layer output adds y times the routing weight back onto token t.  Dgrad (GLM
+// page, section "The 4-bit base that was actually using 8-bit memory"): the
+// input gradient contracts the output dimension of each weight, so it reads
+// the single rowwise copy transposed, dequantized to bf16; no columnwise copy
+// exists.  Only experts that received rows are ever read.
+//
+// Structure: the routed pairs are sorted by expert (route.hip), so each expert
+// owns a contiguous segment of rows.  One templated grouped-GEMM kernel runs
+// every contraction: a 128 x BN output tile of one expert, a K loop in steps of
+// 64 through two LDS stages, the weight tile dequantized from 4-bit codes to
+// bf16 while it is staged (e2m1 * e4m3 and the NF4 levels are exact in bf16, the
+// FP32 per-tensor scale is applied to the accumulator), bf16 MFMA 32x32x16 with
+// FP32 accumulation, then an optional second K segment (the LoRA up-projection,
+// K = r) and a fused epilogue (SwiGLU, routing weight, SwiGLU backward).
+// Workgroups are mapped so that each of the 8 XCDs walks a contiguous range of
+// tiles: the tiles in flight on one XCD share an expert's activation rows and
+// weight rows in that XCD's L2.
 #include "common.h"
+#include "internal.h"
+#include "nf4_levels.inc"
 
-extern "C" size_t bqm_moe_workspace_size(const bqm_moe_desc *) { return 0; }
-extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *, const uint16_t *, const int32_t *, const float *,
-                                  uint16_t *, void *, size_t, void *) {
-  return bqm::fail(BQM_ERR_UNSUPPORTED, "bqm_moe_fwd: not built yet");
+namespace bqm {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int BM = 128;       // output rows per tile (routed rows of one expert)
+constexpr int BK = 64;        // K step (one NF4 block, four NVFP4 blocks)
+constexpr int SK = BK + 8;    // LDS row stride in bf16 (16-byte pad)
+constexpr int NTHR = 256;
+
+enum ASrc { A_GATHER = 0, A_ROWS = 1, A_GATHER_Q = 2, A_ROWS_Q = 3 };
+enum BSrc { B_Q4_K = 0, B_Q4_N = 1, B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
+enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2 };
+
+// One K segment of a contraction: A rows times one expert slice of a B stack.
+struct Seg {
+  const void *a;        // bf16 rows, or NVFP4 codes of per-row quantized rows
+  const uint8_t *a_sc;  // A E4M3 scales (quantized A)
+  const float *a_sd;    // A per-row decode scales (quantized A)
+  int64_t a_ld;         // elements per A row
+  const void *b;        // B stack: 4-bit codes or bf16
+  const void *b_sc;     // NVFP4 E4M3 scales / NF4 absmax
+  const float *b_sd;    // NVFP4 per-expert decode scales
+  int64_t b_rows, b_cols;  // one expert slice of the B stack is [b_rows, b_cols]
+  int K;
+};
+
+struct GemmParams {
+  const int32_t *perm, *offsets, *tile_off;
+  int E, k;
+  int N;   // output columns
+  int I;   // gate/up split point
+  int NT;  // output column tiles
+  Seg s1, s2;  // s2.K == 0: no second segment
+  float out_scale;
+  uint16_t *out0, *out1;
+  const uint16_t *h_in;  // saved gate/up activations (dgrad epilogue)
+  const float *tw;       // routing weight of pair f (dgrad epilogue)
+};
+
+__constant__ float c_nf4[16] = BQM_NF4_LEVELS;
+
+// ---------------------------------------------------------------------------
+// dequantization to bf16 bits (exact)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t fp4_bf16(uint32_t nib, float sb) {
+  float v = __uint_as_float(e2m1_mag_bits(nib & 7u) | ((nib & 8u) << 28)) * sb;
+  return __float_as_uint(v) >> 16;  // exact product: <= 6 significant bits
 }
-extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *, const uint16_t *, void *, size_t, uint16_t *,
-                                    float *, void *) {
-  return bqm::fail(BQM_ERR_UNSUPPORTED, "bqm_moe_dgrad: not built yet");
+
+// 8 nibbles of one dword (element 2i in the low nibble of byte i) -> 4 dwords of bf16 pairs
+__device__ __forceinline__ void fp4x8(uint32_t c, float sb, uint32_t *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = fp4_bf16((c >> (8 * i)) & 0xFu, sb) | (fp4_bf16((c >> (8 * i + 4)) & 0xFu, sb) << 16);
 }
-extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *, void *, size_t, float *, float *, float *, float *,
-                                    void *) {
-  return bqm::fail(BQM_ERR_UNSUPPORTED, "bqm_lora_grad: not built yet");
+
+__device__ __forceinline__ uint32_t nf4_bf16(const float *lut, uint32_t code, float a) {
+  return f32_to_bf16(lut[code] * a);
+}
+
+__device__ __forceinline__ void nf4x8(const float *lut, uint32_t c, float a, uint32_t *o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = nf4_bf16(lut, (c >> (8 * i)) & 0xFu, a) | (nf4_bf16(lut, (c >> (8 * i + 4)) & 0xFu, a) << 16);
+}
+
+__device__ __forceinline__ float bfv(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// ---------------------------------------------------------------------------
+// tile-column -> weight-row mapping
+// ---------------------------------------------------------------------------
+// Gate/up interleave: in each 64-column group of the tile the first 32 columns
+// are gate rows i and the next 32 the matching up rows I + i, so the epilogue
+// finds g and u of the same element in the same lane and register.
+template <int EPI, int BN>
+__device__ __forceinline__ int64_t b_row_of_col(int j, int nt, int N, int I) {
+  if constexpr (EPI == EPI_GATEUP) {
+    int i = nt * (BN / 2) + (j >> 6) * 32 + (j & 31);
+    if (i >= I) return -1;
+    return (j & 32) ? (int64_t)I + i : (int64_t)i;
+  } else {
+    int n = nt * BN + j;
+    return n < N ? n : -1;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// A tile: BM rows x BK, staged to LDS as bf16 [BM][SK]
+// ---------------------------------------------------------------------------
+struct ARegs {
+  uint4 v[4];
+};
+
+template <int ASRC>
+__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[4], int k0, ARegs &r) {
+  const int tid = threadIdx.x;
+  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + NTHR * i;
+      int kk = k0 + (c & 7) * 8;
+      if (arow[i] >= 0 && kk < s.K)
+        r.v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.a) +
+                                                  arow[i] * s.a_ld + kk);
+      else
+        r.v[i] = make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    // quantized rows: thread -> (row = tid/2, 32 elements): 16 B codes + 2 scale bytes
+    const int half = tid & 1;
+    if (arow[0] >= 0) {
+      const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.a) + arow[0] * (s.a_ld / 2) + (k0 + half * 32) / 2;
+      r.v[0] = *reinterpret_cast<const uint4 *>(cp);
+      const uint8_t *sp = s.a_sc + arow[0] * (s.a_ld / 16) + (k0 + half * 32) / 16;
+      r.v[1].x = sp[0];
+      r.v[1].y = sp[1];
+    } else {
+      r.v[0] = make_uint4(0, 0, 0, 0);
+      r.v[1].x = r.v[1].y = 0;
+    }
+  }
+}
+
+template <int ASRC>
+__device__ __forceinline__ void a_store(uint16_t *As, const ARegs &r) {
+  const int tid = threadIdx.x;
+  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int c = tid + NTHR * i;
+      *reinterpret_cast<uint4 *>(As + (c >> 3) * SK + (c & 7) * 8) = r.v[i];
+    }
+  } else {
+    const int row = tid >> 1, half = tid & 1;
+    uint32_t cw[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+    uint32_t o[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fp4x8(cw[q], e4m3_to_f32(q < 2 ? r.v[1].x : r.v[1].y), o + 4 * q);
+    uint4 *dst = reinterpret_cast<uint4 *>(As + row * SK + half * 32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// B tile: BN output columns x BK, staged to LDS as bf16 [BN][SK] (k contiguous)
+// ---------------------------------------------------------------------------
+struct BRegs {
+  uint32_t w[32];
+};
+
+template <int BSRC, int BN, int EPI>
+__device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I, int k0, BRegs &r) {
+  const int tid = threadIdx.x;
+  const int64_t slice = s.b_rows * s.b_cols;
+  if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
+    // K-major quantized weight [N rows][K cols]; EPT elements of one row per thread
+    constexpr int EPT = BN / 4;           // 64 (BN=256) or 16 (BN=64)
+    constexpr int TPR = BK / EPT;         // threads per row
+    const int j = tid / TPR, kofs = (tid % TPR) * EPT;
+    const int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
+    if (wr < 0) {
+#pragma unroll
+      for (int i = 0; i < EPT / 8 + 1; ++i) r.w[i] = 0u;
+      r.w[EPT / 8] = 0u;
+      return;
+    }
+    const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + wr * (s.b_cols / 2) + (k0 + kofs) / 2;
+    if constexpr (EPT == 64) {
+      uint4 a = reinterpret_cast<const uint4 *>(cp)[0], b = reinterpret_cast<const uint4 *>(cp)[1];
+      r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+      r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+    } else {
+      uint2 a = *reinterpret_cast<const uint2 *>(cp);
+      r.w[0] = a.x; r.w[1] = a.y;
+    }
+    if constexpr (BSRC == B_Q4_K) {
+      const uint8_t *sp = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) + wr * (s.b_cols / 16) + (k0 + kofs) / 16;
+      if constexpr (EPT == 64)
+        r.w[8] = *reinterpret_cast<const uint32_t *>(sp);
+      else
+        r.w[2] = sp[0];
+    } else {
+      const float *ap = reinterpret_cast<const float *>(s.b_sc) + e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64;
+      r.w[EPT / 8] = __float_as_uint(*ap);
+    }
+  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
+    // N-major quantized weight [K rows][N cols]: 8 k rows x 8 columns per thread
+    constexpr int NG = BN / 8;
+    if (tid >= NG * 8) return;
+    const int ng = tid % NG, kg = tid / NG;
+    const int n = nt * BN + ng * 8;
+    if (n >= N) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) r.w[q] = 0u;
+      return;
+    }
+    const uint8_t *cb = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + n / 2;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t kk = k0 + kg * 8 + q;
+      r.w[q] = *reinterpret_cast<const uint32_t *>(cb + kk * (s.b_cols / 2));
+      if constexpr (BSRC == B_Q4_N)
+        r.w[8 + q] = reinterpret_cast<const uint8_t *>(s.b_sc)[e * (slice / 16) + kk * (s.b_cols / 16) + n / 16];
+      else
+        r.w[8 + q] = __float_as_uint(
+            reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
+    }
+  } else if constexpr (BSRC == B_BF_K) {
+    // bf16 [N rows][K cols]: BN*8 chunks of 16 B
+    constexpr int CH = BN * 8 / NTHR;  // 8 or 2
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      int c = tid + NTHR * i;
+      int j = c >> 3, kk = k0 + (c & 7) * 8;
+      int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (wr >= 0 && kk < s.K)
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + wr * s.b_cols + kk);
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (BSRC == B_BF_N) {
+    // bf16 [K rows][N cols]: 8 k rows x 8 columns per thread, transposed at store
+    constexpr int NG = BN / 8;
+    if (tid >= NG * 8) return;
+    const int ng = tid % NG, kg = tid / NG;
+    const int n = nt * BN + ng * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int kk = k0 + kg * 8 + q;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < N && kk < s.K)
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + (int64_t)kk * s.b_cols + n);
+      r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
+    }
+  }
+}
+
+template <int BSRC, int BN>
+__device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const float *lut) {
+  const int tid = threadIdx.x;
+  if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
+    constexpr int EPT = BN / 4;
+    constexpr int TPR = BK / EPT;
+    const int j = tid / TPR, kofs = (tid % TPR) * EPT;
+    uint4 *dst = reinterpret_cast<uint4 *>(Bs + j * SK + kofs);
+#pragma unroll
+    for (int q = 0; q < EPT / 8; ++q) {
+      uint32_t o[4];
+      if constexpr (BSRC == B_Q4_K) {
+        uint32_t sc = EPT == 64 ? (r.w[8] >> (8 * (q >> 1))) & 0xFFu : r.w[2];
+        fp4x8(r.w[q], e4m3_to_f32(sc), o);
+      } else {
+        nf4x8(lut, r.w[q], __uint_as_float(r.w[EPT / 8]), o);
+      }
+      dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
+    constexpr int NG = BN / 8;
+    if (tid >= NG * 8) return;
+    const int ng = tid % NG, kg = tid / NG;
+    // element (k row q, column c) = nibble c of r.w[q]
+    uint32_t o[8][4];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t nib = (r.w[q] >> (4 * c)) & 0xFu;
+        uint32_t b;
+        if constexpr (BSRC == B_Q4_N)
+          b = fp4_bf16(nib, e4m3_to_f32(r.w[8 + q]));
+        else
+          b = nf4_bf16(lut, nib, __uint_as_float(r.w[8 + q]));
+        if (q & 1)
+          o[c][q >> 1] |= b << 16;
+        else
+          o[c][q >> 1] = b;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<uint4 *>(Bs + (ng * 8 + c) * SK + kg * 8) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+  } else if constexpr (BSRC == B_BF_K) {
+    constexpr int CH = BN * 8 / NTHR;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      int c = tid + NTHR * i;
+      *reinterpret_cast<uint4 *>(Bs + (c >> 3) * SK + (c & 7) * 8) =
+          make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]);
+    }
+  } else if constexpr (BSRC == B_BF_N) {
+    constexpr int NG = BN / 8;
+    if (tid >= NG * 8) return;
+    const int ng = tid % NG, kg = tid / NG;
+    // r.w[4q + c/2] holds columns c (low half if c even) of k row q
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint32_t o[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t w0 = r.w[4 * (2 * p) + (c >> 1)], w1 = r.w[4 * (2 * p + 1) + (c >> 1)];
+        uint32_t b0 = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
+        uint32_t b1 = (c & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
+        o[p] = b0 | (b1 << 16);
+      }
+      *reinterpret_cast<uint4 *>(Bs + (ng * 8 + c) * SK + kg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the grouped GEMM
+// ---------------------------------------------------------------------------
+template <int BN>
+struct Shape {
+  static constexpr int WM = BN == 256 ? 2 : 4;  // waves along M
+  static constexpr int WN = 4 / WM;             // waves along N
+  static constexpr int TM = BM / WM / 32;       // 32x32 MFMA tiles per wave along M
+  static constexpr int TN = BN / WN / 32;       // ... along N
+};
+
+template <int BN>
+__device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs,
+                                          f32x16 (&acc)[Shape<BN>::TM][Shape<BN>::TN]) {
+  constexpr int TM = Shape<BN>::TM, TN = Shape<BN>::TN, WN = Shape<BN>::WN;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8 af[TM], bfr[TN];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+      af[tm] = *reinterpret_cast<const bf16x8 *>(As + (wm * TM * 32 + tm * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      bfr[tn] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * TN * 32 + tn * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
+  }
+}
+
+// Runs one K segment into acc.  arow: the 4 A source rows of this thread's loads.
+template <int BN, int ASRC, int BSRC, int EPI>
+__device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[4],
+                                            uint16_t (*As)[BM * SK], uint16_t (*Bs)[BN * SK], const float *lut,
+                                            f32x16 (&acc)[Shape<BN>::TM][Shape<BN>::TN]) {
+  const int nk = (s.K + BK - 1) / BK;
+  ARegs ar;
+  BRegs br;
+  a_load<ASRC>(s, arow, 0, ar);
+  b_load<BSRC, BN, EPI>(s, e, nt, N, I, 0, br);
+  a_store<ASRC>(As[0], ar);
+  b_store<BSRC, BN>(Bs[0], br, lut);
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    const int cur = ks & 1;
+    const bool more = ks + 1 < nk;
+    if (more) {
+      a_load<ASRC>(s, arow, (ks + 1) * BK, ar);
+      b_load<BSRC, BN, EPI>(s, e, nt, N, I, (ks + 1) * BK, br);
+    }
+    mma_stage<BN>(As[cur], Bs[cur], acc);
+    if (more) {
+      a_store<ASRC>(As[cur ^ 1], ar);
+      b_store<BSRC, BN>(Bs[cur ^ 1], br, lut);
+    }
+    __syncthreads();
+  }
+}
+
+template <int BN, int ASRC, int BSRC, int B2SRC, int EPI>
+__global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
+  constexpr int TM = Shape<BN>::TM, TN = Shape<BN>::TN, WN = Shape<BN>::WN;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * SK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * SK];
+  __shared__ float lut[16];
+
+  // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
+  const int total = p.tile_off[p.E] * p.NT;
+  const int per = (total + 7) / 8;
+  const int li = blockIdx.x >> 3;
+  if (li >= per) return;
+  const int L = (blockIdx.x & 7) * per + li;
+  if (L >= total) return;
+  const int mt = L / p.NT, nt = L % p.NT;
+  int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= mt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int rb = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - rb;
+  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WN, wn = wid % WN;
+
+  if constexpr (BSRC == B_NF4_K || BSRC == B_NF4_N) {
+    if (tid < 16) lut[tid] = c_nf4[tid];
+    __syncthreads();
+  }
+
+  // source rows of this thread's A loads (segment 1)
+  int64_t arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int row = (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) ? (tid >> 1) : ((tid + NTHR * i) >> 3);
+    int pos = m0 + row;
+    if (pos >= n_e) {
+      arow[i] = -1;
+    } else if (ASRC == A_GATHER || ASRC == A_GATHER_Q) {
+      arow[i] = p.perm[rb + pos] / p.k;
+    } else {
+      arow[i] = rb + pos;
+    }
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+
+  run_segment<BN, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, As, Bs, lut, acc);
+
+  // FP32 decode scales of segment 1: per expert (NVFP4 weights) x per row (NVFP4 activations)
+  if constexpr (BSRC == B_Q4_K || BSRC == B_Q4_N || ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
+    float sb = 1.0f;
+    if constexpr (BSRC == B_Q4_K || BSRC == B_Q4_N) sb = p.s1.b_sd[e];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float sc = sb;
+        if constexpr (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
+          int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (pos < n_e) {
+            int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+            sc = sb * p.s1.a_sd[src];
+          }
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) acc[tm][tn][v] *= sc;
+      }
+  }
+
+  if constexpr (B2SRC != B_NONE) {
+    if (p.s2.K > 0) {
+      int64_t arow2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int pos = m0 + ((tid + NTHR * i) >> 3);
+        arow2[i] = pos < n_e ? (int64_t)(rb + pos) : -1;
+      }
+      run_segment<BN, A_ROWS, B2SRC, EPI>(p.s2, e, nt, p.N, p.I, arow2, As, Bs, lut, acc);
+    }
+  }
+
+  // epilogue
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (pos >= n_e) continue;
+      const int64_t grow = rb + pos;
+      if constexpr (EPI == EPI_GATEUP) {
+#pragma unroll
+        for (int q = 0; q < TN / 2; ++q) {
+          const int i = nt * (BN / 2) + wn * 64 + q * 32 + (lane & 31);
+          if (i >= p.I) continue;
+          const float g = acc[tm][2 * q][v], u = acc[tm][2 * q + 1][v];
+          const float a = g / (1.0f + __expf(-g)) * u;
+          p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(g);
+          p.out0[grow * 2 * p.I + p.I + i] = (uint16_t)f32_to_bf16(u);
+          p.out1[grow * p.I + i] = (uint16_t)f32_to_bf16(a);
+        }
+      } else if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
+          if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * p.out_scale);
+        }
+      } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
+        const float w = p.tw[p.perm[grow]];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int i = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
+          if (i >= p.N) continue;
+          const float g = bfv(p.h_in[grow * 2 * p.I + i]);
+          const float u = bfv(p.h_in[grow * 2 * p.I + p.I + i]);
+          const float sg = 1.0f / (1.0f + __expf(-g));
+          const float da = w * acc[tm][tn][v];
+          const float dg = da * u * sg * (1.0f + g * (1.0f - sg));
+          const float du = da * g * sg;
+          p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(dg);
+          p.out0[grow * 2 * p.I + p.I + i] = (uint16_t)f32_to_bf16(du);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LoRA weight gradients: C[e] [M, N] = sum over the expert's rows of P[row][m] * Q[row][n]
+// ---------------------------------------------------------------------------
+struct WgradParams {
+  const int32_t *perm, *offsets;
+  const float *tw;  // routing weights by pair (scales P rows when scale_p)
+  int k, M, N;
+  const uint16_t *P;
+  int64_t p_ld;
+  int p_gather;     // P rows gathered by token
+  int scale_p;      // multiply P rows by the routing weight
+  const uint16_t *Q;
+  int64_t q_ld;
+  int q_gather;
+  float *C;
+};
+
+constexpr int WB = 64;  // wgrad tile (M and N) and row step
+
+__global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[WB * SK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[WB * SK];
+  const int e = blockIdx.y;
+  const int ntn = (p.N + WB - 1) / WB;
+  const int mt = blockIdx.x / ntn, ntile = blockIdx.x % ntn;
+  const int m0 = mt * WB, n0 = ntile * WB;
+  const int rb = p.offsets[e], n_e = p.offsets[e + 1] - rb;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  // loader role: threads 0..63 stage P^T, 64..127 stage Q^T; 8 rows x 8 columns each
+  const int role = tid >> 6, item = tid & 63;
+  const int cg = item & 7, rg = item >> 3;
+  for (int r0 = 0; r0 < n_e; r0 += WB) {
+    if (role < 2) {
+      const uint16_t *src = role == 0 ? p.P : p.Q;
+      const int64_t ld = role == 0 ? p.p_ld : p.q_ld;
+      const int gather = role == 0 ? p.p_gather : p.q_gather;
+      const int lim = role == 0 ? p.M : p.N;
+      const int c0 = (role == 0 ? m0 : n0) + cg * 8;
+      uint32_t w[32];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int pos = r0 + rg * 8 + q;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (pos < n_e && c0 < lim) {
+          const int64_t grow = rb + pos;
+          const int64_t srow = gather ? (int64_t)(p.perm[grow] / p.k) : grow;
+          v = *reinterpret_cast<const uint4 *>(src + srow * ld + c0);
+          if (role == 0 && p.scale_p) {
+            const float s = p.tw[p.perm[grow]];
+            uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              x[h] = f32_to_bf16(bf16_lo(x[h]) * s) | (f32_to_bf16(bf16_hi(x[h]) * s) << 16);
+            v = make_uint4(x[0], x[1], x[2], x[3]);
+          }
+        }
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+      uint16_t *dstb = role == 0 ? As : Bs;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        uint32_t o[4];
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          uint32_t w0 = w[4 * (2 * pp) + (c >> 1)], w1 = w[4 * (2 * pp + 1) + (c >> 1)];
+          uint32_t b0 = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
+          uint32_t b1 = (c & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
+          o[pp] = b0 | (b1 << 16);
+        }
+        *reinterpret_cast<uint4 *>(dstb + (cg * 8 + c) * SK + rg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < WB / 16; ++kk) {
+      bf16x8 a = *reinterpret_cast<const bf16x8 *>(As + (wm * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+      bf16x8 b = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = m0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+    const int n = n0 + wn * 32 + (lane & 31);
+    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[v];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine, routing-weight gradient
+// ---------------------------------------------------------------------------
+// out[t][c] = sum_j w[t,j] * rows[inv[t*k+j]][c] (w = 1 when tw == NULL), j ascending
+__global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict__ rows, const int32_t *__restrict__ inv,
+                                                     const float *__restrict__ tw, int64_t T, int k, int64_t H,
+                                                     uint16_t *__restrict__ out) {
+  const int64_t cpr = H / 8;
+  for (int64_t it = (int64_t)blockIdx.x * NTHR + threadIdx.x; it < T * cpr; it += (int64_t)gridDim.x * NTHR) {
+    const int64_t t = it / cpr, c = (it % cpr) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < k; ++j) {
+      const int64_t f = t * k + j;
+      const float w = tw ? tw[f] : 1.0f;
+      const uint4 v = *reinterpret_cast<const uint4 *>(rows + (int64_t)inv[f] * H + c);
+      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc[2 * h] += w * bf16_lo(x[h]);
+        acc[2 * h + 1] += w * bf16_hi(x[h]);
+      }
+    }
+    uint32_t o[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) o[h] = f32_to_bf16(acc[2 * h]) | (f32_to_bf16(acc[2 * h + 1]) << 16);
+    *reinterpret_cast<uint4 *>(out + t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// dtw[f] = <dy[t], y[inv[f]]>, one wave per routed pair
+__global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict__ dy, const uint16_t *__restrict__ y,
+                                                     const int32_t *__restrict__ inv, int64_t R, int k, int64_t H,
+                                                     float *__restrict__ dtw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t f = (int64_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6);
+  if (f >= R) return;
+  const uint16_t *a = dy + (f / k) * H;
+  const uint16_t *b = y + (int64_t)inv[f] * H;
+  float s = 0.0f;
+  for (int64_t c = lane * 8; c < H; c += 64 * 8) {
+    uint4 va = *reinterpret_cast<const uint4 *>(a + c), vb = *reinterpret_cast<const uint4 *>(b + c);
+    uint32_t xa[4] = {va.x, va.y, va.z, va.w}, xb[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) s += bf16_lo(xa[h]) * bf16_lo(xb[h]) + bf16_hi(xa[h]) * bf16_hi(xb[h]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) dtw[f] = s;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t perm, inv, off, tile_off, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, aq_c, aq_s, aq_d, vdn, dh, vgu, dxr;
+  size_t total;
+};
+
+Layout layout(const bqm_moe_desc *d) {
+  const size_t T = d->T, H = d->H, I = d->I, E = d->E, k = d->k, r = d->r;
+  const size_t R = T * k;
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  L.perm = take(R * 4);
+  L.inv = take(R * 4);
+  L.off = take((E + 1) * 4);
+  L.tile_off = take((E + 1) * 4);
+  L.counts = take(permute_ws_bytes((int64_t)R, (int)E));
+  L.tw = take(R * 4);
+  L.ugu = take(R * r * 2);
+  L.udn = take(R * r * 2);
+  L.h = take(R * 2 * I * 2);
+  L.a = take(R * I * 2);
+  L.y = take(R * H * 2);
+  const bool aq = d->act_quant != 0;
+  L.xq_c = take(aq ? T * H / 2 : 0);
+  L.xq_s = take(aq ? T * H / 16 : 0);
+  L.xq_d = take(aq ? T * 4 : 0);
+  L.aq_c = take(aq ? R * I / 2 : 0);
+  L.aq_s = take(aq ? R * I / 16 : 0);
+  L.aq_d = take(aq ? R * 4 : 0);
+  L.vdn = take(R * r * 2);
+  L.dh = take(R * 2 * I * 2);
+  L.vgu = take(R * r * 2);
+  L.dxr = take(R * H * 2);
+  L.total = o;
+  return L;
+}
+
+bqm_status check_desc(const bqm_moe_desc *d, const char *who) {
+  BQM_REQUIRE(d, BQM_ERR_INVALID_ARG, "%s: descriptor is NULL", who);
+  BQM_REQUIRE(d->T >= 0 && d->H > 0 && d->I > 0, BQM_ERR_INVALID_ARG, "%s: bad T/H/I", who);
+  BQM_REQUIRE(d->H % 64 == 0 && d->I % 64 == 0, BQM_ERR_SHAPE, "%s: H and I must be multiples of 64", who);
+  BQM_REQUIRE(d->E >= 1 && d->E <= 1024, BQM_ERR_SHAPE, "%s: E=%d outside [1, 1024]", who, d->E);
+  BQM_REQUIRE(d->k >= 1 && d->k <= d->E && d->k <= 16, BQM_ERR_SHAPE, "%s: k=%d outside [1, min(E,16)]", who, d->k);
+  BQM_REQUIRE(d->r >= 0 && d->r <= 128 && d->r % 8 == 0, BQM_ERR_SHAPE,
+              "%s: r=%d must be a multiple of 8 in [0, 128]", who, d->r);
+  BQM_REQUIRE(d->T * d->k < (int64_t)1 << 31, BQM_ERR_SHAPE, "%s: too many routed rows", who);
+  const bqm_qtensor *w[2] = {&d->w_gu, &d->w_dn};
+  const int64_t rows[2] = {2 * d->I, d->H}, cols[2] = {d->H, d->I};
+  for (int i = 0; i < 2; ++i) {
+    BQM_REQUIRE(w[i]->fmt == BQM_FMT_NVFP4 || w[i]->fmt == BQM_FMT_NF4, BQM_ERR_INVALID_ARG, "%s: bad weight format", who);
+    BQM_REQUIRE(w[i]->fmt == d->w_gu.fmt, BQM_ERR_UNSUPPORTED, "%s: gate_up and down formats differ", who);
+    BQM_REQUIRE(w[i]->n_mat == d->E && w[i]->rows == rows[i] && w[i]->cols == cols[i], BQM_ERR_SHAPE,
+                "%s: %s stack must be [%d, %lld, %lld]", who, i ? "down" : "gate_up", d->E, (long long)rows[i],
+                (long long)cols[i]);
+    BQM_REQUIRE(w[i]->codes && w[i]->scales, BQM_ERR_INVALID_ARG, "%s: weight pointers NULL", who);
+    BQM_REQUIRE(aligned16(w[i]->codes) && aligned16(w[i]->scales), BQM_ERR_ALIGN, "%s: weight pointers not aligned",
+                who);
+    if (w[i]->fmt == BQM_FMT_NVFP4) {
+      BQM_REQUIRE(w[i]->scale_mode == BQM_SCALE_PER_TENSOR, BQM_ERR_UNSUPPORTED,
+                  "%s: NVFP4 weights need one scale per expert matrix", who);
+      BQM_REQUIRE(w[i]->s_dec && aligned16(w[i]->s_dec), BQM_ERR_INVALID_ARG, "%s: weight s_dec NULL/unaligned", who);
+    }
+  }
+  BQM_REQUIRE(!d->act_quant || d->w_gu.fmt == BQM_FMT_NVFP4, BQM_ERR_UNSUPPORTED,
+              "%s: act_quant needs NVFP4 weights", who);
+  if (d->r > 0) {
+    const void *l[4] = {d->A_gu, d->B_gu, d->A_dn, d->B_dn};
+    for (int i = 0; i < 4; ++i) {
+      BQM_REQUIRE(l[i], BQM_ERR_INVALID_ARG, "%s: LoRA pointer NULL with r > 0", who);
+      BQM_REQUIRE(aligned16(l[i]), BQM_ERR_ALIGN, "%s: LoRA pointer not aligned", who);
+    }
+  }
+  return BQM_OK;
+}
+
+struct Ws {
+  char *base;
+  Layout L;
+  template <class T>
+  T *at(size_t off) const {
+    return reinterpret_cast<T *>(base + off);
+  }
+};
+
+bqm_status check_ws(const bqm_moe_desc *d, void *ws, size_t ws_bytes, const char *who, Ws &w) {
+  w.L = layout(d);
+  BQM_REQUIRE(ws && ws_bytes >= w.L.total, BQM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who,
+              w.L.total, ws_bytes);
+  BQM_REQUIRE(aligned16(ws), BQM_ERR_ALIGN, "%s: workspace not 16-byte aligned", who);
+  w.base = reinterpret_cast<char *>(ws);
+  return BQM_OK;
+}
+
+int gemm_grid(int64_t R, int E, int NT) {
+  int64_t mt = cdiv(R, BM) + E;
+  int64_t g = mt * NT;
+  return (int)((g + 7) / 8 * 8);
+}
+
+Seg seg_bf16(const void *a, int64_t a_ld, const void *b, int64_t b_rows, int64_t b_cols, int K) {
+  Seg s{};
+  s.a = a;
+  s.a_ld = a_ld;
+  s.b = b;
+  s.b_rows = b_rows;
+  s.b_cols = b_cols;
+  s.K = K;
+  return s;
+}
+
+Seg seg_q(const void *a, int64_t a_ld, const bqm_qtensor &w, int K) {
+  Seg s{};
+  s.a = a;
+  s.a_ld = a_ld;
+  s.b = w.codes;
+  s.b_sc = w.scales;
+  s.b_sd = w.s_dec;
+  s.b_rows = w.rows;
+  s.b_cols = w.cols;
+  s.K = K;
+  return s;
+}
+
+template <int BN, int ASRC, int BSRC, int B2SRC, int EPI>
+bqm_status launch(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+  const int grid = gemm_grid(R, p.E, p.NT);
+  moe_gemm<BN, ASRC, BSRC, B2SRC, EPI><<<grid, NTHR, 0, s>>>(p);
+  return launch_status(what);
+}
+
+GemmParams base_params(const bqm_moe_desc *d, const Ws &w) {
+  GemmParams p{};
+  p.perm = w.at<int32_t>(w.L.perm);
+  p.offsets = w.at<int32_t>(w.L.off);
+  p.tile_off = w.at<int32_t>(w.L.tile_off);
+  p.E = d->E;
+  p.k = d->k;
+  p.I = (int)d->I;
+  p.out_scale = 1.0f;
+  return p;
+}
+
+#define BQM_TRY(expr)                  \
+  do {                                 \
+    bqm_status st_ = (expr);           \
+    if (st_ != BQM_OK) return st_;     \
+  } while (0)
+
+// rows [n_rows, cols] -> per-row NVFP4 (Four-Over-Six) into the given buffers
+bqm_status quantize_rows(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_t *codes, uint8_t *scales, float *sd,
+                         hipStream_t s) {
+  bqm_qtensor q{};
+  q.fmt = BQM_FMT_NVFP4;
+  q.scale_mode = BQM_SCALE_PER_ROW;
+  q.n_mat = 1;
+  q.rows = n_rows;
+  q.cols = cols;
+  q.codes = codes;
+  q.scales = scales;
+  q.s_dec = sd;
+  return bqm_quantize_nvfp4(x, 1, nullptr, &q, nullptr, 0, s);
+}
+
+template <int ASRC_X>
+bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int64_t R, hipStream_t s, bool nf4) {
+  const int H = (int)d->H, I = (int)d->I, r = d->r;
+  const float ls = d->lora_scale;
+  uint16_t *ugu = w.at<uint16_t>(w.L.ugu), *udn = w.at<uint16_t>(w.L.udn);
+  uint16_t *h = w.at<uint16_t>(w.L.h), *a = w.at<uint16_t>(w.L.a), *y = w.at<uint16_t>(w.L.y);
+  // U_gu = s X A_gu^T   [R, r]
+  if (r > 0) {
+    GemmParams p = base_params(d, w);
+    p.N = r;
+    p.NT = (int)cdiv(r, 64);
+    p.s1 = seg_bf16(x, H, d->A_gu, r, H, H);
+    p.out_scale = ls;
+    p.out0 = ugu;
+    BQM_TRY((launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a gate_up")));
+  }
+  // h = X~ W~_gu^T + U_gu B_gu^T; a = silu(g) u
+  {
+    GemmParams p = base_params(d, w);
+    p.N = 2 * I;
+    p.NT = (int)cdiv(I, 128);
+    const void *xa = ASRC_X == A_GATHER_Q ? (const void *)w.at<uint8_t>(w.L.xq_c) : (const void *)x;
+    p.s1 = seg_q(xa, H, d->w_gu, H);
+    if (ASRC_X == A_GATHER_Q) {
+      p.s1.a_sc = w.at<uint8_t>(w.L.xq_s);
+      p.s1.a_sd = w.at<float>(w.L.xq_d);
+    }
+    p.s2 = seg_bf16(ugu, r, d->B_gu, 2 * I, r, r);
+    p.out0 = h;
+    p.out1 = a;
+    if (nf4)
+      BQM_TRY((launch<256, ASRC_X, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+    else
+      BQM_TRY((launch<256, ASRC_X, B_Q4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+  }
+  const bool aq = ASRC_X == A_GATHER_Q;
+  if (aq) BQM_TRY(quantize_rows(a, R, I, w.at<uint8_t>(w.L.aq_c), w.at<uint8_t>(w.L.aq_s), w.at<float>(w.L.aq_d), s));
+  // U_dn = s a A_dn^T  [R, r]
+  if (r > 0) {
+    GemmParams p = base_params(d, w);
+    p.N = r;
+    p.NT = (int)cdiv(r, 64);
+    p.s1 = seg_bf16(a, I, d->A_dn, r, I, I);
+    p.out_scale = ls;
+    p.out0 = udn;
+    BQM_TRY((launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a down")));
+  }
+  // y = a~ W~_dn^T + U_dn B_dn^T
+  {
+    GemmParams p = base_params(d, w);
+    p.N = H;
+    p.NT = (int)cdiv(H, 256);
+    p.s1 = seg_q(aq ? (const void *)w.at<uint8_t>(w.L.aq_c) : (const void *)a, I, d->w_dn, I);
+    if (aq) {
+      p.s1.a_sc = w.at<uint8_t>(w.L.aq_s);
+      p.s1.a_sd = w.at<float>(w.L.aq_d);
+    }
+    p.s2 = seg_bf16(udn, r, d->B_dn, H, r, r);
+    p.out0 = y;
+    if (nf4)
+      BQM_TRY((launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
+    else if (aq)
+      BQM_TRY((launch<256, A_ROWS_Q, B_Q4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
+    else
+      BQM_TRY((launch<256, A_ROWS, B_Q4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
+  }
+  return BQM_OK;
+}
+
+}  // namespace
+}  // namespace bqm
+
+using namespace bqm;
+
+extern "C" size_t bqm_moe_workspace_size(const bqm_moe_desc *d) {
+  if (!d || d->T < 0 || d->k < 1 || d->E < 1 || d->r < 0) return 0;
+  return layout(d).total;
+}
+
+extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, const int32_t *topk_idx,
+                                  const float *topk_w, uint16_t *out, void *ws, size_t ws_bytes, void *stream) {
+  BQM_TRY(check_desc(d, "bqm_moe_fwd"));
+  Ws w;
+  BQM_TRY(check_ws(d, ws, ws_bytes, "bqm_moe_fwd", w));
+  const int64_t R = d->T * d->k;
+  hipStream_t s = as_stream(stream);
+  if (d->T > 0) {
+    BQM_REQUIRE(x && topk_idx && topk_w && out, BQM_ERR_INVALID_ARG, "bqm_moe_fwd: NULL pointer");
+    BQM_REQUIRE(aligned16(x) && aligned16(topk_idx) && aligned16(topk_w) && aligned16(out), BQM_ERR_ALIGN,
+                "bqm_moe_fwd: pointer not 16-byte aligned");
+  }
+  BQM_TRY(permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
+                         w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off), s));
+  if (R == 0) return BQM_OK;
+  if (hipMemcpyAsync(w.at<float>(w.L.tw), topk_w, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return launch_status("bqm_moe_fwd: copy of routing weights");
+  const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
+  if (d->act_quant) {
+    BQM_TRY(quantize_rows(x, d->T, d->H, w.at<uint8_t>(w.L.xq_c), w.at<uint8_t>(w.L.xq_s), w.at<float>(w.L.xq_d), s));
+    BQM_TRY(fwd_gemms<A_GATHER_Q>(d, w, x, R, s, nf4));
+  } else {
+    BQM_TRY(fwd_gemms<A_GATHER>(d, w, x, R, s, nf4));
+  }
+  const int64_t items = d->T * (d->H / 8);
+  combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(
+      w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), w.at<float>(w.L.tw), d->T, d->k, d->H, out);
+  return launch_status("combine fwd");
+}
+
+extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, void *ws, size_t ws_bytes, uint16_t *dx,
+                                    float *dtopk_w, void *stream) {
+  BQM_TRY(check_desc(d, "bqm_moe_dgrad"));
+  Ws w;
+  BQM_TRY(check_ws(d, ws, ws_bytes, "bqm_moe_dgrad", w));
+  const int64_t R = d->T * d->k;
+  if (R == 0) return BQM_OK;
+  BQM_REQUIRE(dy && dx, BQM_ERR_INVALID_ARG, "bqm_moe_dgrad: NULL pointer");
+  BQM_REQUIRE(aligned16(dy) && aligned16(dx) && (!dtopk_w || aligned16(dtopk_w)), BQM_ERR_ALIGN,
+              "bqm_moe_dgrad: pointer not 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  const int H = (int)d->H, I = (int)d->I, r = d->r;
+  const float ls = d->lora_scale;
+  const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
+  uint16_t *vdn = w.at<uint16_t>(w.L.vdn), *vgu = w.at<uint16_t>(w.L.vgu);
+  uint16_t *dh = w.at<uint16_t>(w.L.dh), *dxr = w.at<uint16_t>(w.L.dxr);
+  if (dtopk_w) {
+    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), R, d->k,
+                                                          d->H, dtopk_w);
+    BQM_TRY(launch_status("dtopk"));
+  }
+  // V_dn = s dY B_dn  [R, r]
+  if (r > 0) {
+    GemmParams p = base_params(d, w);
+    p.N = r;
+    p.NT = (int)cdiv(r, 64);
+    p.s1 = seg_bf16(dy, H, d->B_dn, H, r, H);
+    p.out_scale = ls;
+    p.out0 = vdn;
+    BQM_TRY((launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T down")));
+  }
+  // da_u = dY W~_dn + V_dn A_dn; dh = SwiGLU'(w da_u)
+  {
+    GemmParams p = base_params(d, w);
+    p.N = I;
+    p.NT = (int)cdiv(I, 256);
+    p.s1 = seg_q(dy, H, d->w_dn, H);
+    p.s2 = seg_bf16(vdn, r, d->A_dn, r, I, r);
+    p.out0 = dh;
+    p.h_in = w.at<uint16_t>(w.L.h);
+    p.tw = w.at<float>(w.L.tw);
+    if (nf4)
+      BQM_TRY((launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+    else
+      BQM_TRY((launch<256, A_GATHER, B_Q4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+  }
+  // V_gu = s dh B_gu  [R, r]
+  if (r > 0) {
+    GemmParams p = base_params(d, w);
+    p.N = r;
+    p.NT = (int)cdiv(r, 64);
+    p.s1 = seg_bf16(dh, 2 * I, d->B_gu, 2 * I, r, 2 * I);
+    p.out_scale = ls;
+    p.out0 = vgu;
+    BQM_TRY((launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T gate_up")));
+  }
+  // dX_row = dh W~_gu + V_gu A_gu
+  {
+    GemmParams p = base_params(d, w);
+    p.N = H;
+    p.NT = (int)cdiv(H, 256);
+    p.s1 = seg_q(dh, 2 * I, d->w_gu, 2 * I);
+    p.s2 = seg_bf16(vgu, r, d->A_gu, r, H, r);
+    p.out0 = dxr;
+    if (nf4)
+      BQM_TRY((launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+    else
+      BQM_TRY((launch<256, A_ROWS, B_Q4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+  }
+  const int64_t items = d->T * (d->H / 8);
+  combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(dxr, w.at<int32_t>(w.L.inv), nullptr,
+                                                                                  d->T, d->k, d->H, dx);
+  return launch_status("combine dgrad");
+}
+
+extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, const uint16_t *dy, void *ws,
+                                    size_t ws_bytes, float *dA_gu, float *dB_gu, float *dA_dn, float *dB_dn,
+                                    void *stream) {
+  BQM_TRY(check_desc(d, "bqm_lora_grad"));
+  BQM_REQUIRE(d->r > 0, BQM_ERR_INVALID_ARG, "bqm_lora_grad: r must be > 0");
+  Ws w;
+  BQM_TRY(check_ws(d, ws, ws_bytes, "bqm_lora_grad", w));
+  BQM_REQUIRE(dA_gu && dB_gu && dA_dn && dB_dn, BQM_ERR_INVALID_ARG, "bqm_lora_grad: NULL output");
+  BQM_REQUIRE(aligned16(dA_gu) && aligned16(dB_gu) && aligned16(dA_dn) && aligned16(dB_dn), BQM_ERR_ALIGN,
+              "bqm_lora_grad: output not 16-byte aligned");
+  if (d->T > 0) {
+    BQM_REQUIRE(x && dy, BQM_ERR_INVALID_ARG, "bqm_lora_grad: x and dy are required");
+    BQM_REQUIRE(aligned16(x) && aligned16(dy), BQM_ERR_ALIGN, "bqm_lora_grad: x/dy not 16-byte aligned");
+  }
+  hipStream_t s = as_stream(stream);
+  const int H = (int)d->H, I = (int)d->I, r = d->r;
+  WgradParams p{};
+  p.perm = w.at<int32_t>(w.L.perm);
+  p.offsets = w.at<int32_t>(w.L.off);
+  p.tw = w.at<float>(w.L.tw);
+  p.k = d->k;
+  auto go = [&](int M, int N, const uint16_t *P, int64_t pld, int pg, int sp, const uint16_t *Q, int64_t qld, int qg,
+                float *C, const char *what) {
+    p.M = M;
+    p.N = N;
+    p.P = P;
+    p.p_ld = pld;
+    p.p_gather = pg;
+    p.scale_p = sp;
+    p.Q = Q;
+    p.q_ld = qld;
+    p.q_gather = qg;
+    p.C = C;
+    dim3 grid((unsigned)(cdiv(M, WB) * cdiv(N, WB)), (unsigned)d->E);
+    lora_wgrad<<<grid, NTHR, 0, s>>>(p);
+    return launch_status(what);
+  };
+  const uint16_t *dh = w.at<uint16_t>(w.L.dh), *ugu = w.at<uint16_t>(w.L.ugu), *vgu = w.at<uint16_t>(w.L.vgu);
+  const uint16_t *udn = w.at<uint16_t>(w.L.udn), *vdn = w.at<uint16_t>(w.L.vdn), *a = w.at<uint16_t>(w.L.a);
+  // dB_gu [2I, r] = dh^T U_gu' ; dA_gu [r, H] = V_gu'^T X ; U' and V' already carry the LoRA scale
+  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, r, 0, dB_gu, "lora dB_gu"));
+  BQM_TRY(go(r, H, vgu, r, 0, 0, x, H, 1, dA_gu, "lora dA_gu"));
+  // dB_dn [H, r] = (w dY)^T U_dn' ; dA_dn [r, I] = (w V_dn')^T a
+  BQM_TRY(go(H, r, dy, H, 1, 1, udn, r, 0, dB_dn, "lora dB_dn"));
+  BQM_TRY(go(r, I, vdn, r, 0, 1, a, I, 0, dA_dn, "lora dA_dn"));
+  return BQM_OK;
 }

@@ -186,13 +186,19 @@ bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, const int32_t *
 bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, void *ws, size_t ws_bytes,
                          uint16_t *dx, float *dtopk_w, void *stream);
 
-/* LoRA weight gradients from the state the forward and dgrad left in ws (the
- * adapter is the trained part; per-expert A/B on the 3-D stacks, nf4moe page,
- * section "Does it actually train?").  f32 outputs dA_gu [E, r, H], dB_gu
- * [E, 2I, r], dA_dn [E, r, I], dB_dn [E, H, r]; experts without tokens get
- * zeros.  Requires r > 0. */
-bqm_status bqm_lora_grad(const bqm_moe_desc *d, void *ws, size_t ws_bytes, float *dA_gu,
-                         float *dB_gu, float *dA_dn, float *dB_dn, void *stream);
+/* LoRA weight gradients (the adapter is the trained part; per-expert A/B on
+ * the 3-D stacks, nf4moe page, section "Does it actually train?"), from the
+ * state bqm_moe_fwd and bqm_moe_dgrad left in ws plus the two layer inputs the
+ * library does not keep: x bf16 [T, H] (the forward input) and dy bf16 [T, H]
+ * (the dgrad input).  With s = lora_scale and w the routing weight of a row:
+ *   dB_gu = s dh^T (X A_gu^T)      dA_gu = s (dh B_gu)^T X
+ *   dB_dn = s (w dy)^T (a A_dn^T)  dA_dn = s (w dy B_dn)^T a
+ * summed over each expert's rows, FP32 accumulation.  f32 outputs dA_gu
+ * [E, r, H], dB_gu [E, 2I, r], dA_dn [E, r, I], dB_dn [E, H, r]; experts
+ * without rows get zeros.  Requires r > 0. */
+bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, const uint16_t *dy, void *ws,
+                         size_t ws_bytes, float *dA_gu, float *dB_gu, float *dA_dn, float *dB_dn,
+                         void *stream);
 
 #ifdef __cplusplus
 }

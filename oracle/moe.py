@@ -66,8 +66,32 @@ class MoEWeights:
         return 0 if self.A_gu is None else self.A_gu.shape[1]
 
 
+class LazyExperts:
+    """An expert stack quantized by this oracle one expert at a time, on first use.
+
+    fetch(e) returns expert e's bf16 weights as float32 [rows, cols]; fmt is
+    "nvfp4" (per-tensor scale, Four-Over-Six) or "nf4".  Used for the full-size
+    workloads, where only the experts a sampled token touches are needed.
+    """
+
+    def __init__(self, fetch, fmt: str, four_over_six: bool = True):
+        self.fetch, self.fmt, self.fos = fetch, fmt, four_over_six
+        self.cache = {}
+
+    def matrix(self, e: int) -> np.ndarray:
+        if e not in self.cache:
+            x = fm.f32(self.fetch(e))[None]
+            if self.fmt == "nvfp4":
+                self.cache[e] = oq.dequantize_nvfp4_exact(oq.quantize_nvfp4(x, self.fos))[0]
+            else:
+                self.cache[e] = oq.dequantize_nf4(oq.quantize_nf4(x))[0].astype(np.float64)
+        return self.cache[e]
+
+
 def expert_matrix(q, e: int) -> np.ndarray:
     """Exact float64 DQ of expert e's 2-D slice (the GEMM operand)."""
+    if isinstance(q, LazyExperts):
+        return q.matrix(e)
     if isinstance(q, oq.NVFP4Tensor):
         one = oq.NVFP4Tensor(q.codes[e:e + 1], q.scales[e:e + 1], q.s_dec[e:e + 1],
                              q.four_over_six, q.per_row)

@@ -1,0 +1,139 @@
+"""GPU parity of the MoE layer (forward, dgrad through DQ(Q(W)), LoRA gradients)
+against the float64 oracle, on small layers that span several tiles with ragged
+expert segments, on the tiny workload, and sampled at the full workload sizes."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_util import assert_close, gpu, log, np_f32
+from tests.moe_harness import HostInputs, gpu_layer, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def small(name, **kw):
+    base = dict(E=16, H=512, I=256, k=4, T=300, r=16, seed=7, outliers=True)
+    base.update(kw)
+    return synth.Shape(name, **base)
+
+
+def compare_full(shape, lora_scale=1.0, poison_empty=False):
+    dev = gpu()
+    log(f"layer {shape}")
+    inp = synth.layer_inputs(shape, device="cpu")
+    g = gpu_layer(inp, dev, lora_scale=lora_scale, poison_empty=poison_empty)
+    h = HostInputs(inp)
+    o = oracle_layer(h, lora_scale=lora_scale)
+    assert (g["idx"].cpu().numpy() == o["idx"]).all(), "routing indices"
+    errs = {}
+    errs["out"] = assert_close(np_f32(g["out"]), o["out"], "out")
+    errs["dx"] = assert_close(np_f32(g["dx"]), o["dx"], "dx")
+    errs["dtw"] = assert_close(g["dtw"].cpu().numpy(), o["dtw"], "dtopk_w")
+    if shape.r:
+        for name, ref in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), o["lora"]):
+            got = g[name].cpu().numpy()
+            errs[name] = assert_close(got, ref, name)
+            hit = np.zeros(shape.E, bool)
+            hit[o["idx"].reshape(-1)] = True
+            assert (got[~hit] == 0).all(), f"{name}: experts without rows must get zeros"
+    log("  " + ", ".join(f"{k}={v[0]:.2e}/{v[1]:.2e}" for k, v in errs.items()))
+    return g, o
+
+
+def test_small_nvfp4_lora():
+    compare_full(small("small"), lora_scale=0.5)
+
+
+def test_small_nvfp4_no_lora():
+    compare_full(small("small_r0", r=0, T=97, k=2))
+
+
+def test_small_w4a4():
+    compare_full(small("small_w4a4", act_quant=True, H=768, I=384))
+
+
+def test_small_nf4_skewed_with_empty_experts():
+    g, o = compare_full(small("small_nf4", fmt="nf4", logits="zipf", E=64, T=200, k=4, r=8), poison_empty=True)
+    counts = np.bincount(o["idx"].reshape(-1), minlength=64)
+    assert (counts == 0).sum() >= 16
+
+
+def test_nvfp4_routed_only_poisoned_experts():
+    shape = small("small_zipf", logits="zipf", E=48, T=128, k=4, r=8)
+    g, o = compare_full(shape, poison_empty=True)
+    assert np.isfinite(np_f32(g["out"])).all() and np.isfinite(np_f32(g["dx"])).all()
+
+
+def test_tiny_workload():
+    compare_full(synth.TINY)
+
+
+def test_single_token_and_empty_batch():
+    compare_full(small("one", T=1, k=4, E=8))
+    import torch
+    import bit_quantized_moe_amd as bqm
+    dev = gpu()
+    shape = small("empty", T=0)
+    inp = synth.layer_inputs(dataclasses.replace(shape, T=1), device="cpu")
+    g = gpu_layer(inp, dev)            # builds the weights; then call with T = 0
+    d = g["desc"]
+    d.T = 0
+    ws = torch.empty(max(bqm.bqm_moe_workspace_size(d), 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, shape.H), dtype=torch.bfloat16, device=dev)
+    bqm.bqm_moe_fwd(d, None, None, None, None, ws)
+    bqm.bqm_moe_dgrad(d, None, ws, None, None)
+    torch.cuda.synchronize()
+
+
+def test_deterministic_bitwise():
+    import torch
+    dev = gpu()
+    shape = small("det", T=150)
+    inp = synth.layer_inputs(shape, device="cpu")
+    a = gpu_layer(inp, dev)
+    b = gpu_layer(inp, dev)
+    for k in ("out", "dx", "dtw", "dA_gu", "dB_gu", "dA_dn", "dB_dn"):
+        assert torch.equal(a[k].view(torch.uint8) if a[k].dtype == torch.bfloat16 else a[k],
+                           b[k].view(torch.uint8) if b[k].dtype == torch.bfloat16 else b[k]), k
+
+
+# ----------------------------------------------------------------------------
+# full workload sizes: the GPU runs everything, the oracle checks sampled tokens
+# (their output and input-gradient rows) and the LoRA gradients of sampled experts
+# ----------------------------------------------------------------------------
+def sampled_full(shape, tokens, lora_experts):
+    import torch
+    dev = gpu()
+    log(f"full-size {shape.name}: generating inputs on the device")
+    inp = synth.layer_inputs(shape, device=dev)
+    g = gpu_layer(inp, dev)
+    log(f"  GPU layer done; oracle on tokens {tokens} and experts {lora_experts}")
+    h = HostInputs(inp)
+    o = oracle_layer(h, tokens=tokens, lora_experts=lora_experts)
+    assert (g["idx"].cpu().numpy() == o["idx"]).all(), "routing indices"
+    toks = o["tokens"]
+    assert_close(np_f32(g["out"][toks]), o["out"], "out rows")
+    assert_close(np_f32(g["dx"][toks]), o["dx"], "dx rows")
+    assert_close(g["dtw"].cpu().numpy()[toks], o["dtw"][toks], "dtopk_w rows")
+    for name, ref in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), o["lora"]):
+        for e in lora_experts:
+            assert_close(g[name][e].cpu().numpy(), ref[e], f"{name}[{e}]")
+    # properties over the whole output: finite, and rows of tokens are not all zero
+    assert torch.isfinite(g["out"].float()).all() and torch.isfinite(g["dx"].float()).all()
+    log("  sampled parity ok")
+    del g, inp
+    torch.cuda.empty_cache()
+
+
+def test_full_glm_sampled():
+    sampled_full(synth.GLM, tokens=[0, 12345], lora_experts=[3])
+
+
+def test_full_qwen_w4a4_sampled():
+    sampled_full(synth.QWEN, tokens=[5, 8000], lora_experts=[100])
+
+
+def test_full_glm_nf4_sampled():
+    sampled_full(synth.GLM_NF4, tokens=[1, 9000], lora_experts=[0])
