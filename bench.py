@@ -1,0 +1,224 @@
+"""Benchmark of the routed-expert MoE layer over NVFP4 (Four-Over-Six) experts with a bf16 LoRA.
+
+One step = the whole layer training step on one batch of synthetic input at the
+GLM-5.2 expert shape (E=256, H=6144, I=2048, top-8, T=16384 tokens, LoRA r=64):
+route -> permute -> forward (gate_up GEMM + SwiGLU, down GEMM, combine) ->
+dgrad through DQ(Q(W)) -> LoRA weight gradients, all in libbqm.so.  The frozen
+weights are quantized once before timing (the quantizer runs per load, not per
+step); its throughput on the same gate_up [256,4096,6144] and down
+[256,6144,2048] stacks is measured in the same run and reported beside.
+
+Prints one JSON line.  Usage: python bench.py [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch uses (one runtime per process)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime)
+        self.hip = C.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            ev = C.c_void_p()
+            assert self.hip.hipEventCreate(C.byref(ev)) == 0
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b):
+        ms = C.c_float()
+        rc = self.hip.hipEventElapsedTime(C.byref(ms), a, b)
+        return ms.value if rc == 0 else None
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, stream) == 0
+
+
+def layer_flops(s):
+    """Algorithmic flops of forward + dgrad (base + LoRA) and of the LoRA grads."""
+    R, H, I, r = s.T * s.k, s.H, s.I, s.r
+    base = 2 * R * (2 * I * H + H * I)
+    lora = 2 * R * r * (H + 2 * I) + 2 * R * r * (I + H)
+    return 2 * (base + lora), 2 * R * r * (2 * I + H + H + I)
+
+
+def stage_flops(s):
+    R, H, I, r = s.T * s.k, s.H, s.I, s.r
+    return {
+        "gate_up_fwd": 2 * R * 2 * I * H + 2 * R * r * 2 * I,
+        "down_fwd": 2 * R * H * I + 2 * R * r * H,
+        "down_dgrad": 2 * R * H * I + 2 * R * r * I,
+        "gate_up_dgrad": 2 * R * 2 * I * H + 2 * R * r * H,
+        "lora_a_gu": 2 * R * r * H, "lora_a_dn": 2 * R * r * I,
+        "lora_b_dn": 2 * R * r * H, "lora_b_gu": 2 * R * r * 2 * I,
+    }
+
+
+def cpu_baseline(inp, shape, experts=(0, 1, 2, 3)):
+    """The oracle (float64 CPU definition) on all routed rows of a few experts, timed on the host."""
+    import numpy as np
+    from oracle import moe as om
+    from oracle import routing as orr
+    from tests.moe_harness import HostInputs
+    h = HostInputs(inp)
+    w = h.weights()
+    idx, tw = orr.route(h.logits, shape.k)
+    rows = int(sum((idx == e).sum() for e in experts))
+    t0 = time.perf_counter()
+    _, cache = om.forward(w, h.x, idx, tw, experts=set(experts))
+    _, _, bwd = om.dgrad(w, cache, h.dout, tw)
+    om.lora_grad(w, cache, bwd, shape.E)
+    dt = time.perf_counter() - t0
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i.get("num_threads", 1) for i in threadpool_info()) or threads
+    except Exception:
+        pass
+    return {"value": (rows / shape.k) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 oracle forward+dgrad+LoRA grads (incl. its own quantization of the touched "
+                      f"experts) over all {rows} routed rows of experts {list(experts)}; tokens = rows / k; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantizer", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
+              "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_quantized_moe_amd as bqm
+    import synth
+    from tests.moe_harness import quantize_stack_gpu
+
+    dev = torch.device("cuda")
+    bqm.load()
+    shape = synth.GLM
+    s = shape
+    inp = synth.layer_inputs(shape, device=dev)
+    ev = HipEvents()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    # --- quantizer (per load): gate_up + down stacks, timed with events ---
+    quant = None
+    if not args.no_quantizer:
+        qgu = bqm.alloc_qtensor(bqm.FMT_NVFP4, s.E, 2 * s.I, s.H, device=dev)
+        qdn = bqm.alloc_qtensor(bqm.FMT_NVFP4, s.E, s.H, s.I, device=dev)
+        wsq = torch.empty(bqm.bqm_quantize_nvfp4_workspace_size(s.E, 2 * s.I, s.H, 0), dtype=torch.uint8,
+                          device=dev)
+        times = []
+        for it in range(4):
+            e = ev.create(2)
+            ev.record(e[0], sh)
+            bqm.bqm_quantize_nvfp4(inp.w_gu, 1, None, qgu, wsq)
+            bqm.bqm_quantize_nvfp4(inp.w_dn, 1, None, qdn, wsq)
+            ev.record(e[1], sh)
+            torch.cuda.synchronize()
+            if it:
+                times.append(ev.elapsed_ms(e[0], e[1]))
+        n_el = s.E * (2 * s.I * s.H + s.H * s.I)
+        qbytes = n_el * (2 + 0.5 + 1 / 16)
+        qms = sum(times) / len(times)
+        quant = {"workload": "gate_up [256,4096,6144] + down [256,6144,2048] bf16 -> NVFP4 4/6",
+                 "ms": qms, "GB/s": qbytes / qms / 1e6, "hbm_frac": qbytes / qms / 1e6 / PEAK_HBM_GBS,
+                 "algorithmic_bytes": qbytes}
+        wgu, wdn = qgu, qdn
+    else:
+        wgu = quantize_stack_gpu(inp.w_gu, "nvfp4")
+        wdn = quantize_stack_gpu(inp.w_dn, "nvfp4")
+    lora = dict(A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn, B_dn=inp.B_dn)
+    d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, **lora)
+    ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+    idx = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(out)
+    dtw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    g = [torch.empty(sz, dtype=torch.float32, device=dev) for sz in
+         ((s.E, s.r, s.H), (s.E, 2 * s.I, s.r), (s.E, s.r, s.I), (s.E, s.H, s.r))]
+
+    def step(events=None):
+        d.stage_events = C.addressof(events) if events is not None else None
+        bqm.bqm_route(inp.logits, s.T, s.E, s.k, 0, idx, tw)
+        bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
+        bqm.bqm_moe_dgrad(d, inp.dout, ws, dx, dtw)
+        bqm.bqm_lora_grad(d, inp.x, inp.dout, ws, *g)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [ev.create(2 * bqm.STAGE_COUNT) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    stages = {}
+    for si, name in enumerate(bqm.STAGES):
+        v = [ev.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]
+        v = [x for x in v if x is not None]
+        if v:
+            stages[name] = sum(v) / len(v)
+    sf = stage_flops(s)
+    gemms = {k: v for k, v in stages.items() if k in ("gate_up_fwd", "down_fwd", "down_dgrad", "gate_up_dgrad")}
+    dom = max(gemms, key=gemms.get)
+    ach = sf[dom] / (gemms[dom] * 1e-3) / 1e12
+    fl, fl_lora = layer_flops(s)
+    result = {
+        "metric": "NVFP4 MoE layer fwd+dgrad tokens/s (GLM-5.2 shape); quantizer GB/s",
+        "value": s.T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "glm5.2-moe-layer-train-step", "E": s.E, "H": s.H, "I": s.I, "k": s.k,
+                   "T": s.T, "r": s.r, "weights": "nvfp4-4over6-rowwise", "step": "route+fwd+dgrad+lora_grad",
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "algorithmic_flop_per_launch": sf[dom], "launch_ms": gemms[dom]},
+        "layer_tflops": (fl + fl_lora) / (ms * 1e-3) / 1e12,
+        "fwd_dgrad_tokens_per_s": s.T / (sum(v for k, v in stages.items() if k != "lora_grad") * 1e-3),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "quantizer": quant,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, shape)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

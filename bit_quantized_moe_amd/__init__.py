@@ -4,7 +4,7 @@ The compute lives in libbqm.so (HIP kernels behind the C ABI of include/bqm.h);
 this package is its ctypes binding.  Importing it does not load the library:
 the first call does, and raises if the library has not been built.
 """
-from ._lib import (BQMError, FMT_NF4, FMT_NVFP4, MoEDesc, QTensor, SCALE_PER_ROW,
+from ._lib import (BQMError, FMT_NF4, FMT_NVFP4, MoEDesc, QTensor, SCALE_PER_ROW, STAGES, STAGE_COUNT,
                    SCALE_PER_TENSOR, alloc_qtensor, bqm_abi_version, bqm_dequantize,
                    bqm_last_error, bqm_lora_grad, bqm_moe_dgrad, bqm_moe_fwd,
                    bqm_moe_workspace_size, bqm_permute, bqm_permute_workspace_size,
@@ -12,5 +12,5 @@ from ._lib import (BQMError, FMT_NF4, FMT_NVFP4, MoEDesc, QTensor, SCALE_PER_ROW
                    bqm_route, load)
 
 __all__ = [n for n in dir() if n.startswith("bqm_")] + [
-    "BQMError", "FMT_NF4", "FMT_NVFP4", "MoEDesc", "QTensor", "SCALE_PER_ROW", "SCALE_PER_TENSOR",
+    "BQMError", "FMT_NF4", "FMT_NVFP4", "MoEDesc", "QTensor", "SCALE_PER_ROW", "SCALE_PER_TENSOR", "STAGES", "STAGE_COUNT",
     "alloc_qtensor", "load"]

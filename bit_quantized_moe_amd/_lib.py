@@ -20,6 +20,11 @@ FMT_NF4 = 2
 SCALE_PER_TENSOR = 0
 SCALE_PER_ROW = 1
 
+STAGES = ["permute", "act_quant_x", "lora_a_gu", "gate_up_fwd", "act_quant_a", "lora_a_dn", "down_fwd",
+          "combine_fwd", "dtopk", "lora_b_dn", "down_dgrad", "lora_b_gu", "gate_up_dgrad", "combine_dgrad",
+          "lora_grad"]
+STAGE_COUNT = len(STAGES)
+
 STATUS = {0: "BQM_OK", -1: "BQM_ERR_INVALID_ARG", -2: "BQM_ERR_SHAPE", -3: "BQM_ERR_ALIGN",
           -4: "BQM_ERR_UNSUPPORTED", -5: "BQM_ERR_WORKSPACE", -6: "BQM_ERR_HIP"}
 
@@ -47,7 +52,7 @@ class MoEDescC(C.Structure):
                 ("k", C.c_int32), ("r", C.c_int32), ("act_quant", C.c_int32),
                 ("lora_scale", C.c_float), ("reserved", C.c_int32), ("w_gu", QTensorC),
                 ("w_dn", QTensorC), ("A_gu", C.c_void_p), ("B_gu", C.c_void_p),
-                ("A_dn", C.c_void_p), ("B_dn", C.c_void_p)]
+                ("A_dn", C.c_void_p), ("B_dn", C.c_void_p), ("stage_events", C.c_void_p)]
 
 
 _lib = None
@@ -60,6 +65,9 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with python -m bit_quantized_moe_amd.build")
+    # torch first, so that the library binds to the HIP runtime torch already uses
+    # (same soname: one runtime per process, shared streams and allocations)
+    import torch  # noqa: F401
     lib = C.CDLL(path)
     vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     sig = {
@@ -204,11 +212,12 @@ class MoEDesc:
     B_dn: object = None
     lora_scale: float = 1.0
     act_quant: int = 0
+    stage_events: Optional[int] = None   # address of a host array of 2*STAGE_COUNT hipEvent_t
 
     def c(self) -> MoEDescC:
         return MoEDescC(self.T, self.H, self.I, self.E, self.k, self.r, int(self.act_quant),
                         float(self.lora_scale), 0, self.w_gu.c(), self.w_dn.c(), _ptr(self.A_gu),
-                        _ptr(self.B_gu), _ptr(self.A_dn), _ptr(self.B_dn))
+                        _ptr(self.B_gu), _ptr(self.A_dn), _ptr(self.B_dn), self.stage_events)
 
 
 def bqm_moe_workspace_size(d: MoEDesc) -> int:

@@ -38,7 +38,7 @@ constexpr int NTHR = 256;
 
 enum ASrc { A_GATHER = 0, A_ROWS = 1, A_GATHER_Q = 2, A_ROWS_Q = 3 };
 enum BSrc { B_Q4_K = 0, B_Q4_N = 1, B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
-enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2 };
+enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_F32 = 3 };
 
 // One K segment of a contraction: A rows times one expert slice of a B stack.
 struct Seg {
@@ -61,9 +61,10 @@ struct GemmParams {
   int NT;  // output column tiles
   Seg s1, s2;  // s2.K == 0: no second segment
   float out_scale;
-  uint16_t *out0, *out1;
-  const uint16_t *h_in;  // saved gate/up activations (dgrad epilogue)
-  const float *tw;       // routing weight of pair f (dgrad epilogue)
+  uint16_t *out0, *out1;  // bf16 outputs
+  float *outf;            // FP32 output (h, y, dX rows)
+  const float *h_in;      // saved FP32 gate/up activations (dgrad epilogue)
+  const float *tw;        // routing weight of pair f (dgrad epilogue)
 };
 
 __constant__ float c_nf4[16] = BQM_NF4_LEVELS;
@@ -508,8 +509,8 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
           if (i >= p.I) continue;
           const float g = acc[tm][2 * q][v], u = acc[tm][2 * q + 1][v];
           const float a = g / (1.0f + __expf(-g)) * u;
-          p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(g);
-          p.out0[grow * 2 * p.I + p.I + i] = (uint16_t)f32_to_bf16(u);
+          p.outf[grow * 2 * p.I + i] = g;
+          p.outf[grow * 2 * p.I + p.I + i] = u;
           p.out1[grow * p.I + i] = (uint16_t)f32_to_bf16(a);
         }
       } else if constexpr (EPI == EPI_STORE) {
@@ -518,14 +519,20 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
           const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
           if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * p.out_scale);
         }
+      } else if constexpr (EPI == EPI_STORE_F32) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
+          if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * p.out_scale;
+        }
       } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
         const float w = p.tw[p.perm[grow]];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int i = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
           if (i >= p.N) continue;
-          const float g = bfv(p.h_in[grow * 2 * p.I + i]);
-          const float u = bfv(p.h_in[grow * 2 * p.I + p.I + i]);
+          const float g = p.h_in[grow * 2 * p.I + i];
+          const float u = p.h_in[grow * 2 * p.I + p.I + i];
           const float sg = 1.0f / (1.0f + __expf(-g));
           const float da = w * acc[tm][tn][v];
           const float dg = da * u * sg * (1.0f + g * (1.0f - sg));
@@ -635,7 +642,7 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
 // combine, routing-weight gradient
 // ---------------------------------------------------------------------------
 // out[t][c] = sum_j w[t,j] * rows[inv[t*k+j]][c] (w = 1 when tw == NULL), j ascending
-__global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict__ rows, const int32_t *__restrict__ inv,
+__global__ void __launch_bounds__(NTHR) combine_rows(const float *__restrict__ rows, const int32_t *__restrict__ inv,
                                                      const float *__restrict__ tw, int64_t T, int k, int64_t H,
                                                      uint16_t *__restrict__ out) {
   const int64_t cpr = H / 8;
@@ -645,13 +652,10 @@ __global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict_
     for (int j = 0; j < k; ++j) {
       const int64_t f = t * k + j;
       const float w = tw ? tw[f] : 1.0f;
-      const uint4 v = *reinterpret_cast<const uint4 *>(rows + (int64_t)inv[f] * H + c);
-      const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        acc[2 * h] += w * bf16_lo(x[h]);
-        acc[2 * h + 1] += w * bf16_hi(x[h]);
-      }
+      const float4 *src = reinterpret_cast<const float4 *>(rows + (int64_t)inv[f] * H + c);
+      const float4 v0 = src[0], v1 = src[1];
+      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
+      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
     }
     uint32_t o[4];
 #pragma unroll
@@ -661,20 +665,20 @@ __global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict_
 }
 
 // dtw[f] = <dy[t], y[inv[f]]>, one wave per routed pair
-__global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict__ dy, const uint16_t *__restrict__ y,
+__global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict__ dy, const float *__restrict__ y,
                                                      const int32_t *__restrict__ inv, int64_t R, int k, int64_t H,
                                                      float *__restrict__ dtw) {
   const int lane = threadIdx.x & 63;
   const int64_t f = (int64_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6);
   if (f >= R) return;
   const uint16_t *a = dy + (f / k) * H;
-  const uint16_t *b = y + (int64_t)inv[f] * H;
+  const float *b = y + (int64_t)inv[f] * H;
   float s = 0.0f;
   for (int64_t c = lane * 8; c < H; c += 64 * 8) {
-    uint4 va = *reinterpret_cast<const uint4 *>(a + c), vb = *reinterpret_cast<const uint4 *>(b + c);
-    uint32_t xa[4] = {va.x, va.y, va.z, va.w}, xb[4] = {vb.x, vb.y, vb.z, vb.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) s += bf16_lo(xa[h]) * bf16_lo(xb[h]) + bf16_hi(xa[h]) * bf16_hi(xb[h]);
+    uint4 va = *reinterpret_cast<const uint4 *>(a + c);
+    const float4 b0 = *reinterpret_cast<const float4 *>(b + c), b1 = *reinterpret_cast<const float4 *>(b + c + 4);
+    s += bf16_lo(va.x) * b0.x + bf16_hi(va.x) * b0.y + bf16_lo(va.y) * b0.z + bf16_hi(va.y) * b0.w;
+    s += bf16_lo(va.z) * b1.x + bf16_hi(va.z) * b1.y + bf16_lo(va.w) * b1.z + bf16_hi(va.w) * b1.w;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -707,9 +711,9 @@ Layout layout(const bqm_moe_desc *d) {
   L.tw = take(R * 4);
   L.ugu = take(R * r * 2);
   L.udn = take(R * r * 2);
-  L.h = take(R * 2 * I * 2);
+  L.h = take(R * 2 * I * 4);
   L.a = take(R * I * 2);
-  L.y = take(R * H * 2);
+  L.y = take(R * H * 4);
   const bool aq = d->act_quant != 0;
   L.xq_c = take(aq ? T * H / 2 : 0);
   L.xq_s = take(aq ? T * H / 16 : 0);
@@ -720,7 +724,7 @@ Layout layout(const bqm_moe_desc *d) {
   L.vdn = take(R * r * 2);
   L.dh = take(R * 2 * I * 2);
   L.vgu = take(R * r * 2);
-  L.dxr = take(R * H * 2);
+  L.dxr = take(R * H * 4);
   L.total = o;
   return L;
 }
@@ -836,6 +840,18 @@ GemmParams base_params(const bqm_moe_desc *d, const Ws &w) {
     if (st_ != BQM_OK) return st_;     \
   } while (0)
 
+// Records the caller's stage event (start or end) if it asked for timing.
+inline void mark(const bqm_moe_desc *d, int stage, int end, hipStream_t s) {
+  if (d->stage_events && d->stage_events[2 * stage + end])
+    (void)hipEventRecord(reinterpret_cast<hipEvent_t>(d->stage_events[2 * stage + end]), s);
+}
+#define BQM_STAGE(d, st, s, expr) \
+  do {                            \
+    mark(d, st, 0, s);            \
+    BQM_TRY(expr);                \
+    mark(d, st, 1, s);            \
+  } while (0)
+
 // rows [n_rows, cols] -> per-row NVFP4 (Four-Over-Six) into the given buffers
 bqm_status quantize_rows(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_t *codes, uint8_t *scales, float *sd,
                          hipStream_t s) {
@@ -856,7 +872,8 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
   const int H = (int)d->H, I = (int)d->I, r = d->r;
   const float ls = d->lora_scale;
   uint16_t *ugu = w.at<uint16_t>(w.L.ugu), *udn = w.at<uint16_t>(w.L.udn);
-  uint16_t *h = w.at<uint16_t>(w.L.h), *a = w.at<uint16_t>(w.L.a), *y = w.at<uint16_t>(w.L.y);
+  float *h = w.at<float>(w.L.h), *y = w.at<float>(w.L.y);
+  uint16_t *a = w.at<uint16_t>(w.L.a);
   // U_gu = s X A_gu^T   [R, r]
   if (r > 0) {
     GemmParams p = base_params(d, w);
@@ -865,7 +882,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.s1 = seg_bf16(x, H, d->A_gu, r, H, H);
     p.out_scale = ls;
     p.out0 = ugu;
-    BQM_TRY((launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a gate_up")));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a gate_up")));
   }
   // h = X~ W~_gu^T + U_gu B_gu^T; a = silu(g) u
   {
@@ -879,15 +896,17 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       p.s1.a_sd = w.at<float>(w.L.xq_d);
     }
     p.s2 = seg_bf16(ugu, r, d->B_gu, 2 * I, r, r);
-    p.out0 = h;
+    p.outf = h;
     p.out1 = a;
     if (nf4)
-      BQM_TRY((launch<256, ASRC_X, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, ASRC_X, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
     else
-      BQM_TRY((launch<256, ASRC_X, B_Q4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, ASRC_X, B_Q4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
   }
   const bool aq = ASRC_X == A_GATHER_Q;
-  if (aq) BQM_TRY(quantize_rows(a, R, I, w.at<uint8_t>(w.L.aq_c), w.at<uint8_t>(w.L.aq_s), w.at<float>(w.L.aq_d), s));
+  if (aq)
+    BQM_STAGE(d, BQM_STAGE_ACT_QUANT_A, s,
+              quantize_rows(a, R, I, w.at<uint8_t>(w.L.aq_c), w.at<uint8_t>(w.L.aq_s), w.at<float>(w.L.aq_d), s));
   // U_dn = s a A_dn^T  [R, r]
   if (r > 0) {
     GemmParams p = base_params(d, w);
@@ -896,7 +915,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.s1 = seg_bf16(a, I, d->A_dn, r, I, I);
     p.out_scale = ls;
     p.out0 = udn;
-    BQM_TRY((launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a down")));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a down")));
   }
   // y = a~ W~_dn^T + U_dn B_dn^T
   {
@@ -909,13 +928,13 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       p.s1.a_sd = w.at<float>(w.L.aq_d);
     }
     p.s2 = seg_bf16(udn, r, d->B_dn, H, r, r);
-    p.out0 = y;
+    p.outf = y;
     if (nf4)
-      BQM_TRY((launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
     else if (aq)
-      BQM_TRY((launch<256, A_ROWS_Q, B_Q4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS_Q, B_Q4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
     else
-      BQM_TRY((launch<256, A_ROWS, B_Q4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_Q4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
   }
   return BQM_OK;
 }
@@ -942,21 +961,24 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
     BQM_REQUIRE(aligned16(x) && aligned16(topk_idx) && aligned16(topk_w) && aligned16(out), BQM_ERR_ALIGN,
                 "bqm_moe_fwd: pointer not 16-byte aligned");
   }
-  BQM_TRY(permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
+  BQM_STAGE(d, BQM_STAGE_PERMUTE, s, permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
                          w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off), s));
   if (R == 0) return BQM_OK;
   if (hipMemcpyAsync(w.at<float>(w.L.tw), topk_w, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return launch_status("bqm_moe_fwd: copy of routing weights");
   const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
   if (d->act_quant) {
-    BQM_TRY(quantize_rows(x, d->T, d->H, w.at<uint8_t>(w.L.xq_c), w.at<uint8_t>(w.L.xq_s), w.at<float>(w.L.xq_d), s));
+    BQM_STAGE(d, BQM_STAGE_ACT_QUANT_X, s,
+              quantize_rows(x, d->T, d->H, w.at<uint8_t>(w.L.xq_c), w.at<uint8_t>(w.L.xq_s), w.at<float>(w.L.xq_d), s));
     BQM_TRY(fwd_gemms<A_GATHER_Q>(d, w, x, R, s, nf4));
   } else {
     BQM_TRY(fwd_gemms<A_GATHER>(d, w, x, R, s, nf4));
   }
   const int64_t items = d->T * (d->H / 8);
+  mark(d, BQM_STAGE_COMBINE_FWD, 0, s);
   combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(
-      w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), w.at<float>(w.L.tw), d->T, d->k, d->H, out);
+      w.at<float>(w.L.y), w.at<int32_t>(w.L.inv), w.at<float>(w.L.tw), d->T, d->k, d->H, out);
+  mark(d, BQM_STAGE_COMBINE_FWD, 1, s);
   return launch_status("combine fwd");
 }
 
@@ -975,10 +997,13 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
   const float ls = d->lora_scale;
   const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
   uint16_t *vdn = w.at<uint16_t>(w.L.vdn), *vgu = w.at<uint16_t>(w.L.vgu);
-  uint16_t *dh = w.at<uint16_t>(w.L.dh), *dxr = w.at<uint16_t>(w.L.dxr);
+  uint16_t *dh = w.at<uint16_t>(w.L.dh);
+  float *dxr = w.at<float>(w.L.dxr);
   if (dtopk_w) {
-    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), R, d->k,
+    mark(d, BQM_STAGE_DTOPK, 0, s);
+    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<float>(w.L.y), w.at<int32_t>(w.L.inv), R, d->k,
                                                           d->H, dtopk_w);
+    mark(d, BQM_STAGE_DTOPK, 1, s);
     BQM_TRY(launch_status("dtopk"));
   }
   // V_dn = s dY B_dn  [R, r]
@@ -989,7 +1014,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.s1 = seg_bf16(dy, H, d->B_dn, H, r, H);
     p.out_scale = ls;
     p.out0 = vdn;
-    BQM_TRY((launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T down")));
+    BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T down")));
   }
   // da_u = dY W~_dn + V_dn A_dn; dh = SwiGLU'(w da_u)
   {
@@ -999,12 +1024,12 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.s1 = seg_q(dy, H, d->w_dn, H);
     p.s2 = seg_bf16(vdn, r, d->A_dn, r, I, r);
     p.out0 = dh;
-    p.h_in = w.at<uint16_t>(w.L.h);
+    p.h_in = w.at<float>(w.L.h);
     p.tw = w.at<float>(w.L.tw);
     if (nf4)
-      BQM_TRY((launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
     else
-      BQM_TRY((launch<256, A_GATHER, B_Q4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch<256, A_GATHER, B_Q4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
   }
   // V_gu = s dh B_gu  [R, r]
   if (r > 0) {
@@ -1014,7 +1039,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.s1 = seg_bf16(dh, 2 * I, d->B_gu, 2 * I, r, 2 * I);
     p.out_scale = ls;
     p.out0 = vgu;
-    BQM_TRY((launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T gate_up")));
+    BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T gate_up")));
   }
   // dX_row = dh W~_gu + V_gu A_gu
   {
@@ -1023,15 +1048,17 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.NT = (int)cdiv(H, 256);
     p.s1 = seg_q(dh, 2 * I, d->w_gu, 2 * I);
     p.s2 = seg_bf16(vgu, r, d->A_gu, r, H, r);
-    p.out0 = dxr;
+    p.outf = dxr;
     if (nf4)
-      BQM_TRY((launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
     else
-      BQM_TRY((launch<256, A_ROWS, B_Q4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_Q4_N, B_BF_N, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
   }
   const int64_t items = d->T * (d->H / 8);
+  mark(d, BQM_STAGE_COMBINE_DGRAD, 0, s);
   combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(dxr, w.at<int32_t>(w.L.inv), nullptr,
                                                                                   d->T, d->k, d->H, dx);
+  mark(d, BQM_STAGE_COMBINE_DGRAD, 1, s);
   return launch_status("combine dgrad");
 }
 
@@ -1075,10 +1102,12 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   const uint16_t *dh = w.at<uint16_t>(w.L.dh), *ugu = w.at<uint16_t>(w.L.ugu), *vgu = w.at<uint16_t>(w.L.vgu);
   const uint16_t *udn = w.at<uint16_t>(w.L.udn), *vdn = w.at<uint16_t>(w.L.vdn), *a = w.at<uint16_t>(w.L.a);
   // dB_gu [2I, r] = dh^T U_gu' ; dA_gu [r, H] = V_gu'^T X ; U' and V' already carry the LoRA scale
+  mark(d, BQM_STAGE_LORA_GRAD, 0, s);
   BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, r, 0, dB_gu, "lora dB_gu"));
   BQM_TRY(go(r, H, vgu, r, 0, 0, x, H, 1, dA_gu, "lora dA_gu"));
   // dB_dn [H, r] = (w dY)^T U_dn' ; dA_dn [r, I] = (w V_dn')^T a
   BQM_TRY(go(H, r, dy, H, 1, 1, udn, r, 0, dB_dn, "lora dB_dn"));
   BQM_TRY(go(r, I, vdn, r, 0, 1, a, I, 0, dA_dn, "lora dA_dn"));
+  mark(d, BQM_STAGE_LORA_GRAD, 1, s);
   return BQM_OK;
 }

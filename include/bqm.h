@@ -148,6 +148,26 @@ bqm_status bqm_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
  * per-token NVFP4 (Four-Over-Six) activations while LoRA reads bf16 ones
  * (4-bitter page, section "Method"); NVFP4 weights only.
  */
+/* Stages of the layer, for optional per-stage timing (stage_events below). */
+typedef enum {
+  BQM_STAGE_PERMUTE = 0,     /* counting sort of routed rows by expert */
+  BQM_STAGE_ACT_QUANT_X,     /* W4A4: per-token NVFP4 of x */
+  BQM_STAGE_LORA_A_GU,       /* U_gu = s x A_gu^T */
+  BQM_STAGE_GATE_UP_FWD,     /* h, a = SwiGLU(x W_gu^T + U_gu B_gu^T) */
+  BQM_STAGE_ACT_QUANT_A,     /* W4A4: per-token NVFP4 of a */
+  BQM_STAGE_LORA_A_DN,       /* U_dn = s a A_dn^T */
+  BQM_STAGE_DOWN_FWD,        /* y = a W_dn^T + U_dn B_dn^T */
+  BQM_STAGE_COMBINE_FWD,     /* out = sum_j w y */
+  BQM_STAGE_DTOPK,           /* d topk_w */
+  BQM_STAGE_LORA_B_DN,       /* V_dn = s dy B_dn */
+  BQM_STAGE_DOWN_DGRAD,      /* dh = SwiGLU'(w (dy W_dn + V_dn A_dn)) */
+  BQM_STAGE_LORA_B_GU,       /* V_gu = s dh B_gu */
+  BQM_STAGE_GATE_UP_DGRAD,   /* dX rows = dh W_gu + V_gu A_gu */
+  BQM_STAGE_COMBINE_DGRAD,   /* dx = sum_j dX rows */
+  BQM_STAGE_LORA_GRAD,       /* the four LoRA weight gradients */
+  BQM_STAGE_COUNT
+} bqm_stage;
+
 typedef struct {
   int64_t T, H, I;
   int32_t E, k, r;
@@ -157,6 +177,10 @@ typedef struct {
   bqm_qtensor w_gu;
   bqm_qtensor w_dn;
   const uint16_t *A_gu, *B_gu, *A_dn, *B_dn;
+  /* Optional (NULL: no timing).  Host array of 2*BQM_STAGE_COUNT hipEvent_t
+   * handles created by the caller; every stage that runs records events
+   * [2*stage] before and [2*stage+1] after its kernels on the call's stream. */
+  void *const *stage_events;
 } bqm_moe_desc;
 
 /* Bytes of the workspace shared by bqm_moe_fwd, bqm_moe_dgrad and
