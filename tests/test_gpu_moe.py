@@ -132,7 +132,14 @@ def test_full_glm_sampled():
 
 
 def test_full_qwen_w4a4_sampled():
-    sampled_full(synth.QWEN, tokens=[5, 8000], lora_experts=[100])
+    # W4A4 quantizes a = silu(g) u per token after a GEMM: last-bit differences in
+    # g, u (FP32 accumulation here, float64 in the oracle) move about 6e-4 of the
+    # bf16 values of a to the other rounding neighbour, and when that element is
+    # a row's amax the whole row is quantized with the neighbouring scale (both are
+    # valid roundings).  Such rows are rare, so the Frobenius error is estimated on
+    # 24 tokens (192 routed rows) rather than 2.
+    toks = list(range(0, 8192, 8192 // 24))[:24]
+    sampled_full(synth.QWEN, tokens=toks, lora_experts=[100])
 
 
 def test_full_glm_nf4_sampled():
