@@ -111,6 +111,73 @@ class HostInputs:
         return om.MoEWeights(s.fmt, gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant)
 
 
+def _bf16_neighbours(a):
+    """For float64 values: (nearest bf16, the other bf16 neighbour, distance to the rounding midpoint)."""
+    from oracle import formats as fm
+    a32 = a.astype(np.float32)
+    near = fm.bf16_round(a32).astype(np.float64)
+    bits = a32.view(np.uint32) & np.uint32(0xFFFF0000)
+    lo = bits.view(np.float32).astype(np.float64)                      # truncation toward zero
+    hi = (bits + np.uint32(0x10000)).view(np.float32).astype(np.float64)
+    other = np.where(near == lo, hi, lo)
+    mid = (lo + hi) / 2
+    return near, other, np.abs(a - mid)
+
+
+def resolve_w4a4_alternatives(g_out, g_dtw, o, h: HostInputs, rel_eps=2.0 ** -14):
+    """W4A4 quantizes a = silu(g) u per token after a GEMM.  Where an element of
+    a lies within rel_eps of a bf16 rounding midpoint, either rounding is a valid
+    result of FP32 accumulation, and when that element decides the row's amax the
+    whole row is quantized with the neighbouring scale.  For every such routed
+    row this evaluates the alternative with the oracle's own arithmetic and keeps,
+    per token, the valid combination closest to the GPU result (out and dtopk_w
+    rows of the oracle result are replaced).  Returns the number of rows that had
+    an alternative."""
+    s = h.shape
+    if not s.act_quant:
+        return 0
+    w = o["w"]
+    k = s.k
+    tokens = list(o["tokens"])
+    row_of = {int(t): n for n, t in enumerate(tokens)}
+    cache = o["cache"]
+    n_alt = 0
+    for e, c in cache["per_expert"].items():
+        a = om.silu(c["g"]) * c["u"]
+        near, other, dist = _bf16_neighbours(a)
+        amb = dist <= rel_eps * np.abs(a)
+        amax = np.abs(near).max(axis=1)
+        Wdn = om.expert_matrix(w.dn, e)
+        for i in range(a.shape[0]):
+            cand = np.nonzero(amb[i] & ((np.abs(other[i]) > amax[i]) | (np.abs(near[i]) == amax[i])))[0]
+            if cand.size == 0:
+                continue
+            f = int(c["fs"][i])
+            t, j = f // k, f % k
+            if t not in row_of:
+                continue
+            n = row_of[t]
+            wt = o["tw"][t, j]
+            best = None
+            for col in cand:
+                alt = near[i].copy()
+                alt[col] = other[i][col]
+                y_alt = om.act_dq(alt[None])[0] @ Wdn.T
+                if w.r:
+                    y_alt = y_alt + w.lora_scale * ((alt @ w.A_dn[e].astype(np.float64).T)
+                                                    @ w.B_dn[e].astype(np.float64).T)
+                out_alt = o["out"][n] - wt * c["y"][i] + wt * y_alt
+                err = np.abs(out_alt - g_out[n]).max()
+                if best is None or err < best[0]:
+                    best = (err, out_alt, float(h.dout[t].astype(np.float64) @ y_alt))
+            err0 = np.abs(o["out"][n] - g_out[n]).max()
+            if best[0] < err0:
+                o["out"][n] = best[1]
+                o["dtw"][t, j] = best[2]
+            n_alt += 1
+    return n_alt
+
+
 def oracle_layer(h: HostInputs, lora_scale=1.0, tokens=None, lora_experts=None):
     """Oracle forward + dgrad for the chosen tokens (all if None), and LoRA grads
     for lora_experts (all experts if None and tokens is None)."""
@@ -119,7 +186,7 @@ def oracle_layer(h: HostInputs, lora_scale=1.0, tokens=None, lora_experts=None):
     idx, tw = orr.route(h.logits, s.k)
     out, cache = om.forward(w, h.x, idx, tw, tokens=tokens)
     dx, dtw, bwd = om.dgrad(w, cache, h.dout, tw)
-    res = dict(idx=idx, tw=tw, out=out, dx=dx, dtw=dtw, tokens=cache["tokens"], w=w)
+    res = dict(idx=idx, tw=tw, out=out, dx=dx, dtw=dtw, tokens=cache["tokens"], w=w, cache=cache)
     if s.r and (tokens is None or lora_experts is not None):
         if lora_experts is not None:
             _, c2 = om.forward(w, h.x, idx, tw, experts=set(lora_experts))
