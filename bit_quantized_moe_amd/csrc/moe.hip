@@ -38,7 +38,7 @@ constexpr int NTHR = 256;
 
 enum ASrc { A_GATHER = 0, A_ROWS = 1, A_GATHER_Q = 2, A_ROWS_Q = 3 };
 enum BSrc { B_Q4_K = 0, B_Q4_N = 1, B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
-enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_F32 = 3 };
+enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_F32 = 3, EPI_STORE_SPLIT = 4 };
 
 // One K segment of a contraction: A rows times one expert slice of a B stack.
 struct Seg {
@@ -51,6 +51,7 @@ struct Seg {
   const float *b_sd;    // NVFP4 per-expert decode scales
   int64_t b_rows, b_cols;  // one expert slice of the B stack is [b_rows, b_cols]
   int K;
+  int kmod;  // > 0: B is indexed at k mod kmod (A holds a hi/lo pair of K = 2*kmod)
 };
 
 struct GemmParams {
@@ -245,8 +246,9 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       int j = c >> 3, kk = k0 + (c & 7) * 8;
       int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
       uint4 v = make_uint4(0, 0, 0, 0);
+      const int kb = s.kmod ? kk % s.kmod : kk;
       if (wr >= 0 && kk < s.K)
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + wr * s.b_cols + kk);
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + wr * s.b_cols + kb);
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   } else if constexpr (BSRC == B_BF_N) {
@@ -258,9 +260,10 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int kk = k0 + kg * 8 + q;
+      const int kb = s.kmod ? kk % s.kmod : kk;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (n < N && kk < s.K)
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + (int64_t)kk * s.b_cols + n);
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + (int64_t)kb * s.b_cols + n);
       r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
     }
   }
@@ -519,6 +522,19 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
           const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
           if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * p.out_scale);
         }
+      } else if constexpr (EPI == EPI_STORE_SPLIT) {
+        // FP32 value kept as an unevaluated pair of bf16 (hi in columns [0, N), lo in [N, 2N))
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
+          if (n < p.N) {
+            const float val = acc[tm][tn][v] * p.out_scale;
+            const uint32_t hb = f32_to_bf16(val);
+            const float lo = val - __uint_as_float(hb << 16);
+            p.out0[grow * 2 * p.N + n] = (uint16_t)hb;
+            p.out0[grow * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo);
+          }
+        }
       } else if constexpr (EPI == EPI_STORE_F32) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -709,8 +725,8 @@ Layout layout(const bqm_moe_desc *d) {
   L.tile_off = take((E + 1) * 4);
   L.counts = take(permute_ws_bytes((int64_t)R, (int)E));
   L.tw = take(R * 4);
-  L.ugu = take(R * r * 2);
-  L.udn = take(R * r * 2);
+  L.ugu = take(R * 2 * r * 2);
+  L.udn = take(R * 2 * r * 2);
   L.h = take(R * 2 * I * 4);
   L.a = take(R * I * 2);
   L.y = take(R * H * 4);
@@ -721,9 +737,9 @@ Layout layout(const bqm_moe_desc *d) {
   L.aq_c = take(aq ? R * I / 2 : 0);
   L.aq_s = take(aq ? R * I / 16 : 0);
   L.aq_d = take(aq ? R * 4 : 0);
-  L.vdn = take(R * r * 2);
+  L.vdn = take(R * 2 * r * 2);
   L.dh = take(R * 2 * I * 2);
-  L.vgu = take(R * r * 2);
+  L.vgu = take(R * 2 * r * 2);
   L.dxr = take(R * H * 4);
   L.total = o;
   return L;
@@ -799,6 +815,13 @@ Seg seg_bf16(const void *a, int64_t a_ld, const void *b, int64_t b_rows, int64_t
   s.b_rows = b_rows;
   s.b_cols = b_cols;
   s.K = K;
+  return s;
+}
+
+// The LoRA up-projection segment: A = [R, 2r] hi/lo bf16 pairs, B indexed at k mod r.
+Seg seg_lora(const void *pair_rows, const void *b, int64_t b_rows, int64_t b_cols, int r) {
+  Seg s = seg_bf16(pair_rows, 2 * r, b, b_rows, b_cols, 2 * r);
+  s.kmod = r;
   return s;
 }
 
@@ -882,7 +905,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.s1 = seg_bf16(x, H, d->A_gu, r, H, H);
     p.out_scale = ls;
     p.out0 = ugu;
-    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a gate_up")));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_a gate_up")));
   }
   // h = X~ W~_gu^T + U_gu B_gu^T; a = silu(g) u
   {
@@ -895,7 +918,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       p.s1.a_sc = w.at<uint8_t>(w.L.xq_s);
       p.s1.a_sd = w.at<float>(w.L.xq_d);
     }
-    p.s2 = seg_bf16(ugu, r, d->B_gu, 2 * I, r, r);
+    p.s2 = seg_lora(ugu, d->B_gu, 2 * I, r, r);
     p.outf = h;
     p.out1 = a;
     if (nf4)
@@ -915,7 +938,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.s1 = seg_bf16(a, I, d->A_dn, r, I, I);
     p.out_scale = ls;
     p.out0 = udn;
-    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE>(p, R, s, "lora_a down")));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_a down")));
   }
   // y = a~ W~_dn^T + U_dn B_dn^T
   {
@@ -927,7 +950,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       p.s1.a_sc = w.at<uint8_t>(w.L.aq_s);
       p.s1.a_sd = w.at<float>(w.L.aq_d);
     }
-    p.s2 = seg_bf16(udn, r, d->B_dn, H, r, r);
+    p.s2 = seg_lora(udn, d->B_dn, H, r, r);
     p.outf = y;
     if (nf4)
       BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
@@ -1014,7 +1037,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.s1 = seg_bf16(dy, H, d->B_dn, H, r, H);
     p.out_scale = ls;
     p.out0 = vdn;
-    BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T down")));
+    BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_b^T down")));
   }
   // da_u = dY W~_dn + V_dn A_dn; dh = SwiGLU'(w da_u)
   {
@@ -1022,7 +1045,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.N = I;
     p.NT = (int)cdiv(I, 256);
     p.s1 = seg_q(dy, H, d->w_dn, H);
-    p.s2 = seg_bf16(vdn, r, d->A_dn, r, I, r);
+    p.s2 = seg_lora(vdn, d->A_dn, r, I, r);
     p.out0 = dh;
     p.h_in = w.at<float>(w.L.h);
     p.tw = w.at<float>(w.L.tw);
@@ -1039,7 +1062,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.s1 = seg_bf16(dh, 2 * I, d->B_gu, 2 * I, r, 2 * I);
     p.out_scale = ls;
     p.out0 = vgu;
-    BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE>(p, R, s, "lora_b^T gate_up")));
+    BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_b^T gate_up")));
   }
   // dX_row = dh W~_gu + V_gu A_gu
   {
@@ -1047,7 +1070,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.N = H;
     p.NT = (int)cdiv(H, 256);
     p.s1 = seg_q(dh, 2 * I, d->w_gu, 2 * I);
-    p.s2 = seg_bf16(vgu, r, d->A_gu, r, H, r);
+    p.s2 = seg_lora(vgu, d->A_gu, r, H, r);
     p.outf = dxr;
     if (nf4)
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
@@ -1103,11 +1126,11 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   const uint16_t *udn = w.at<uint16_t>(w.L.udn), *vdn = w.at<uint16_t>(w.L.vdn), *a = w.at<uint16_t>(w.L.a);
   // dB_gu [2I, r] = dh^T U_gu' ; dA_gu [r, H] = V_gu'^T X ; U' and V' already carry the LoRA scale
   mark(d, BQM_STAGE_LORA_GRAD, 0, s);
-  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, r, 0, dB_gu, "lora dB_gu"));
-  BQM_TRY(go(r, H, vgu, r, 0, 0, x, H, 1, dA_gu, "lora dA_gu"));
+  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, 2 * r, 0, dB_gu, "lora dB_gu"));
+  BQM_TRY(go(r, H, vgu, 2 * r, 0, 0, x, H, 1, dA_gu, "lora dA_gu"));
   // dB_dn [H, r] = (w dY)^T U_dn' ; dA_dn [r, I] = (w V_dn')^T a
-  BQM_TRY(go(H, r, dy, H, 1, 1, udn, r, 0, dB_dn, "lora dB_dn"));
-  BQM_TRY(go(r, I, vdn, r, 0, 1, a, I, 0, dA_dn, "lora dA_dn"));
+  BQM_TRY(go(H, r, dy, H, 1, 1, udn, 2 * r, 0, dB_dn, "lora dB_dn"));
+  BQM_TRY(go(r, I, vdn, 2 * r, 0, 1, a, I, 0, dA_dn, "lora dA_dn"));
   mark(d, BQM_STAGE_LORA_GRAD, 1, s);
   return BQM_OK;
 }
