@@ -36,6 +36,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.hip.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
         self.hip.hipEventDestroy.argtypes = [C.c_void_p]
+        self.hip.hipEventQuery.argtypes = [C.c_void_p]
 
     def create(self, n):
         arr = (C.c_void_p * n)()
@@ -48,7 +49,10 @@ class HipEvents:
     def elapsed_ms(self, a, b):
         ms = C.c_float()
         rc = self.hip.hipEventElapsedTime(C.byref(ms), a, b)
-        return ms.value if rc == 0 else None
+        if rc != 0:
+            self.hip.hipGetLastError()        # do not leave the error for the next caller
+            return None
+        return ms.value
 
     def record(self, ev, stream):
         assert self.hip.hipEventRecord(ev, stream) == 0
@@ -187,7 +191,10 @@ def main():
     ms = (t1 - t0) * 1e3 / args.steps
 
     stages = {}
+    ran = [n for n in bqm.STAGES if s.act_quant or not n.startswith("act_quant")]
     for si, name in enumerate(bqm.STAGES):
+        if name not in ran:
+            continue
         v = [ev.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]
         v = [x for x in v if x is not None]
         if v:
