@@ -25,13 +25,15 @@
 #include "internal.h"
 #include "nf4_levels.inc"
 
+#include <type_traits>
+
 namespace bqm {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BM = 128;       // output rows per tile (routed rows of one expert)
+constexpr int BM = 256;       // output rows per tile (routed rows of one expert)
 constexpr int BK = 64;        // K step (one NF4 block, four NVFP4 blocks)
 constexpr int SK = BK + 8;    // LDS row stride in bf16 (16-byte pad)
 constexpr int NTHR = 256;
@@ -116,28 +118,76 @@ __device__ __forceinline__ int64_t b_row_of_col(int j, int nt, int N, int I) {
 }
 
 // ---------------------------------------------------------------------------
+// tile shapes
+// ---------------------------------------------------------------------------
+// A tile is BM routed rows x BN output columns; WM x WN waves each own a
+// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.  The main GEMMs use 256 x 256
+// with 8 waves (two per SIMD, so one wave's dequantization overlaps the other's
+// MFMAs); the LoRA down-projections (N = r) use 256 x 64 with 4 waves.
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  static constexpr int ACH = BM * 8 / NTHR;  // 16-byte A chunks per thread per K step
+};
+using BigCfg = Cfg<256, 256, 4, 2>;
+using SmallCfg = Cfg<256, 64, 4, 1>;
+
+// Raw staging of an N-major 4-bit tile (64 k rows x 256 columns): codes with a
+// one-dword pad per row (conflict-free transposing reads) and the row's scales.
+constexpr int RAW_STRIDE = 33;  // dwords per raw code row (32 + 1 pad)
+
+// ---------------------------------------------------------------------------
+// exact 4-bit -> bf16 conversion with the hardware FP4 converter
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// bf16 bits of two exactly representable floats, packed (lo, hi)
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// byte `sel` of c holds two E2M1 codes (low nibble first) -> their values times sb
+template <int SEL>
+__device__ __forceinline__ f32x2 fp4pair(uint32_t c, float sb) {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, SEL);
+  return v * sb;  // exact: <= 6 significant bits
+}
+
+// 8 codes of one dword -> 4 dwords of bf16 pairs along the dword's elements
+__device__ __forceinline__ void fp4x8_hw(uint32_t c, float sb, uint32_t *o) {
+  f32x2 a = fp4pair<0>(c, sb), b = fp4pair<1>(c, sb), d = fp4pair<2>(c, sb), e = fp4pair<3>(c, sb);
+  o[0] = pack_exact(a.x, a.y);
+  o[1] = pack_exact(b.x, b.y);
+  o[2] = pack_exact(d.x, d.y);
+  o[3] = pack_exact(e.x, e.y);
+}
+
+// ---------------------------------------------------------------------------
 // A tile: BM rows x BK, staged to LDS as bf16 [BM][SK]
 // ---------------------------------------------------------------------------
+template <class C>
 struct ARegs {
-  uint4 v[4];
+  uint4 v[C::ACH > 2 ? C::ACH : 2];
 };
 
-template <int ASRC>
-__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[4], int k0, ARegs &r) {
+template <class C, int ASRC>
+__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[C::ACH], int k0, ARegs<C> &r) {
   const int tid = threadIdx.x;
   if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + NTHR * i;
-      int kk = k0 + (c & 7) * 8;
+    for (int i = 0; i < C::ACH; ++i) {
+      const int c = tid + C::NTHR * i;
+      const int kk = k0 + (c & 7) * 8;
       if (arow[i] >= 0 && kk < s.K)
-        r.v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.a) +
-                                                  arow[i] * s.a_ld + kk);
+        r.v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.a) + arow[i] * s.a_ld + kk);
       else
         r.v[i] = make_uint4(0, 0, 0, 0);
     }
   } else {
-    // quantized rows: thread -> (row = tid/2, 32 elements): 16 B codes + 2 scale bytes
+    // per-row quantized rows: thread -> (row = tid/2, 32 elements): 16 B codes + 2 scale bytes
+    static_assert(C::NTHR == 2 * C::BM, "quantized A needs two threads per row");
     const int half = tid & 1;
     if (arow[0] >= 0) {
       const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.a) + arow[0] * (s.a_ld / 2) + (k0 + half * 32) / 2;
@@ -152,24 +202,25 @@ __device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[4], i
   }
 }
 
-template <int ASRC>
-__device__ __forceinline__ void a_store(uint16_t *As, const ARegs &r) {
+template <class C, int ASRC>
+__device__ __forceinline__ void a_store(uint16_t *As, const ARegs<C> &r) {
   const int tid = threadIdx.x;
   if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int c = tid + NTHR * i;
+    for (int i = 0; i < C::ACH; ++i) {
+      const int c = tid + C::NTHR * i;
       *reinterpret_cast<uint4 *>(As + (c >> 3) * SK + (c & 7) * 8) = r.v[i];
     }
   } else {
     const int row = tid >> 1, half = tid & 1;
-    uint32_t cw[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-    uint32_t o[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) fp4x8(cw[q], e4m3_to_f32(q < 2 ? r.v[1].x : r.v[1].y), o + 4 * q);
+    const uint32_t cw[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
     uint4 *dst = reinterpret_cast<uint4 *>(As + row * SK + half * 32);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    for (int q = 0; q < 4; ++q) {
+      uint32_t o[4];
+      fp4x8_hw(cw[q], e4m3_to_f32(q < 2 ? r.v[1].x : r.v[1].y), o);
+      dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
   }
 }
 
@@ -180,71 +231,62 @@ struct BRegs {
   uint32_t w[32];
 };
 
-template <int BSRC, int BN, int EPI>
+template <int BSRC>
+constexpr bool raw_staged() {
+  return BSRC == B_Q4_N || BSRC == B_NF4_N;
+}
+
+template <class C, int BSRC, int EPI>
 __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I, int k0, BRegs &r) {
+  constexpr int BN = C::BN;
   const int tid = threadIdx.x;
   const int64_t slice = s.b_rows * s.b_cols;
   if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
-    // K-major quantized weight [N rows][K cols]; EPT elements of one row per thread
-    constexpr int EPT = BN / 4;           // 64 (BN=256) or 16 (BN=64)
-    constexpr int TPR = BK / EPT;         // threads per row
-    const int j = tid / TPR, kofs = (tid % TPR) * EPT;
+    // K-major 4-bit weight [N rows][K cols]: 32 elements (16 B of codes) of one row per thread
+    static_assert(BN * BK / C::NTHR == 32, "K-major 4-bit tile expects 32 elements per thread");
+    const int j = tid >> 1, kofs = (tid & 1) * 32;
     const int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
     if (wr < 0) {
-#pragma unroll
-      for (int i = 0; i < EPT / 8 + 1; ++i) r.w[i] = 0u;
-      r.w[EPT / 8] = 0u;
+      r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
       return;
     }
     const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + wr * (s.b_cols / 2) + (k0 + kofs) / 2;
-    if constexpr (EPT == 64) {
-      uint4 a = reinterpret_cast<const uint4 *>(cp)[0], b = reinterpret_cast<const uint4 *>(cp)[1];
-      r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
-    } else {
-      uint2 a = *reinterpret_cast<const uint2 *>(cp);
-      r.w[0] = a.x; r.w[1] = a.y;
-    }
+    const uint4 a = *reinterpret_cast<const uint4 *>(cp);
+    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
     if constexpr (BSRC == B_Q4_K) {
       const uint8_t *sp = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) + wr * (s.b_cols / 16) + (k0 + kofs) / 16;
-      if constexpr (EPT == 64)
-        r.w[8] = *reinterpret_cast<const uint32_t *>(sp);
-      else
-        r.w[2] = sp[0];
+      r.w[4] = *reinterpret_cast<const uint16_t *>(sp);
     } else {
-      const float *ap = reinterpret_cast<const float *>(s.b_sc) + e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64;
-      r.w[EPT / 8] = __float_as_uint(*ap);
+      r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64]);
     }
-  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
-    // N-major quantized weight [K rows][N cols]: 8 k rows x 8 columns per thread
-    constexpr int NG = BN / 8;
-    if (tid >= NG * 8) return;
-    const int ng = tid % NG, kg = tid / NG;
-    const int n = nt * BN + ng * 8;
-    if (n >= N) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) r.w[q] = 0u;
-      return;
-    }
-    const uint8_t *cb = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + n / 2;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int64_t kk = k0 + kg * 8 + q;
-      r.w[q] = *reinterpret_cast<const uint32_t *>(cb + kk * (s.b_cols / 2));
-      if constexpr (BSRC == B_Q4_N)
-        r.w[8 + q] = reinterpret_cast<const uint8_t *>(s.b_sc)[e * (slice / 16) + kk * (s.b_cols / 16) + n / 16];
-      else
-        r.w[8 + q] = __float_as_uint(
-            reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
+  } else if constexpr (raw_staged<BSRC>()) {
+    // N-major 4-bit weight [K rows][N cols]: the 64 x BN tile is loaded coalesced
+    // (one 16-byte chunk of codes per thread, plus the rows' scales) and staged raw
+    static_assert(BN == 256 && C::NTHR == 512, "raw staging expects a 256-column tile and 512 threads");
+    const int row = tid >> 3, chunk = tid & 7;  // 64 rows x 8 chunks of 16 B
+    const int n = nt * BN + chunk * 32;
+    const int64_t kk = k0 + row;
+    if (n < N) {
+      const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) +
+                                                       kk * (s.b_cols / 2) + n / 2);
+      r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+      if constexpr (BSRC == B_Q4_N) {
+        r.w[4] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) +
+                                                    kk * (s.b_cols / 16) + n / 16);
+      } else {
+        r.w[4] = (chunk & 1) ? 0u : __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
+      }
+    } else {
+      r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
     }
   } else if constexpr (BSRC == B_BF_K) {
     // bf16 [N rows][K cols]: BN*8 chunks of 16 B
-    constexpr int CH = BN * 8 / NTHR;  // 8 or 2
+    constexpr int CH = BN * 8 / C::NTHR;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      int c = tid + NTHR * i;
-      int j = c >> 3, kk = k0 + (c & 7) * 8;
-      int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
+      const int c = tid + C::NTHR * i;
+      const int j = c >> 3, kk = k0 + (c & 7) * 8;
+      const int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
       uint4 v = make_uint4(0, 0, 0, 0);
       const int kb = s.kmod ? kk % s.kmod : kk;
       if (wr >= 0 && kk < s.K)
@@ -252,10 +294,10 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   } else if constexpr (BSRC == B_BF_N) {
-    // bf16 [K rows][N cols]: 8 k rows x 8 columns per thread, transposed at store
+    // bf16 [K rows][N cols]: 8 k rows x 8 columns per thread, transposed at the store
     constexpr int NG = BN / 8;
     if (tid >= NG * 8) return;
-    const int ng = tid % NG, kg = tid / NG;
+    const int kg = tid & 7, ng = tid >> 3;
     const int n = nt * BN + ng * 8;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -269,71 +311,54 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
   }
 }
 
-template <int BSRC, int BN>
-__device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const float *lut) {
+// Writes the loaded registers: dequantized bf16 into Bs, or raw codes into the staging area.
+template <class C, int BSRC>
+__device__ __forceinline__ void b_store(uint16_t *Bs, uint32_t *raw, uint32_t *raw_sc, const BRegs &r,
+                                        const float *lut) {
+  constexpr int BN = C::BN;
   const int tid = threadIdx.x;
   if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
-    constexpr int EPT = BN / 4;
-    constexpr int TPR = BK / EPT;
-    const int j = tid / TPR, kofs = (tid % TPR) * EPT;
+    const int j = tid >> 1, kofs = (tid & 1) * 32;
     uint4 *dst = reinterpret_cast<uint4 *>(Bs + j * SK + kofs);
 #pragma unroll
-    for (int q = 0; q < EPT / 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
       uint32_t o[4];
-      if constexpr (BSRC == B_Q4_K) {
-        uint32_t sc = EPT == 64 ? (r.w[8] >> (8 * (q >> 1))) & 0xFFu : r.w[2];
-        fp4x8(r.w[q], e4m3_to_f32(sc), o);
-      } else {
-        nf4x8(lut, r.w[q], __uint_as_float(r.w[EPT / 8]), o);
-      }
+      if constexpr (BSRC == B_Q4_K)
+        fp4x8_hw(r.w[q], e4m3_to_f32((r.w[4] >> (8 * (q >> 1))) & 0xFFu), o);
+      else
+        nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
       dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
     }
-  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
-    constexpr int NG = BN / 8;
-    if (tid >= NG * 8) return;
-    const int ng = tid % NG, kg = tid / NG;
-    // element (k row q, column c) = nibble c of r.w[q]
-    uint32_t o[8][4];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint32_t nib = (r.w[q] >> (4 * c)) & 0xFu;
-        uint32_t b;
-        if constexpr (BSRC == B_Q4_N)
-          b = fp4_bf16(nib, e4m3_to_f32(r.w[8 + q]));
-        else
-          b = nf4_bf16(lut, nib, __uint_as_float(r.w[8 + q]));
-        if (q & 1)
-          o[c][q >> 1] |= b << 16;
-        else
-          o[c][q >> 1] = b;
-      }
+  } else if constexpr (raw_staged<BSRC>()) {
+    const int row = tid >> 3, chunk = tid & 7;
+    uint32_t *dst = raw + row * RAW_STRIDE + chunk * 4;
+    dst[0] = r.w[0]; dst[1] = r.w[1]; dst[2] = r.w[2]; dst[3] = r.w[3];
+    if constexpr (BSRC == B_Q4_N) {
+      reinterpret_cast<uint16_t *>(raw_sc)[row * 8 + chunk] = (uint16_t)r.w[4];
+    } else {
+      if (!(chunk & 1)) raw_sc[row * 4 + (chunk >> 1)] = r.w[4];
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      *reinterpret_cast<uint4 *>(Bs + (ng * 8 + c) * SK + kg * 8) = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
   } else if constexpr (BSRC == B_BF_K) {
-    constexpr int CH = BN * 8 / NTHR;
+    constexpr int CH = BN * 8 / C::NTHR;
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      int c = tid + NTHR * i;
+      const int c = tid + C::NTHR * i;
       *reinterpret_cast<uint4 *>(Bs + (c >> 3) * SK + (c & 7) * 8) =
           make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]);
     }
   } else if constexpr (BSRC == B_BF_N) {
     constexpr int NG = BN / 8;
     if (tid >= NG * 8) return;
-    const int ng = tid % NG, kg = tid / NG;
-    // r.w[4q + c/2] holds columns c (low half if c even) of k row q
+    const int kg = tid & 7, ng = tid >> 3;
+    // r.w[4q + c/2] holds column c (low half if c even) of k row q
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       uint32_t o[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        uint32_t w0 = r.w[4 * (2 * p) + (c >> 1)], w1 = r.w[4 * (2 * p + 1) + (c >> 1)];
-        uint32_t b0 = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-        uint32_t b1 = (c & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
+        const uint32_t w0 = r.w[4 * (2 * p) + (c >> 1)], w1 = r.w[4 * (2 * p + 1) + (c >> 1)];
+        const uint32_t b0 = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
+        const uint32_t b1 = (c & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
         o[p] = b0 | (b1 << 16);
       }
       *reinterpret_cast<uint4 *>(Bs + (ng * 8 + c) * SK + kg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -341,21 +366,56 @@ __device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const floa
   }
 }
 
+// Raw-staged N-major tile -> bf16 [BN][SK] with k contiguous.  Thread -> 4 k rows
+// x 8 columns (kg fastest across lanes: conflict-free 8-byte stores and reads).
+template <class C, int BSRC>
+__device__ __forceinline__ void b_dequant_raw(uint16_t *Bs, const uint32_t *raw, const uint32_t *raw_sc,
+                                              const float *lut) {
+  const int tid = threadIdx.x;
+  const int kg = tid & 15, ng = tid >> 4;  // 16 groups of 4 k rows, 32 groups of 8 columns
+  uint32_t c[4];
+  float sc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = kg * 4 + q;
+    c[q] = raw[row * RAW_STRIDE + ng];
+    if constexpr (BSRC == B_Q4_N)
+      sc[q] = e4m3_to_f32(reinterpret_cast<const uint8_t *>(raw_sc)[row * 16 + (ng >> 1)]);
+    else
+      sc[q] = __uint_as_float(raw_sc[row * 4 + (ng >> 3)]);
+  }
+  // o[col][pair]: bf16 pairs (k rows 2p, 2p+1) of column col
+  uint32_t o[8][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if constexpr (BSRC == B_Q4_N) {
+      const f32x2 a0 = fp4pair<0>(c[2 * p], sc[2 * p]), b0 = fp4pair<0>(c[2 * p + 1], sc[2 * p + 1]);
+      const f32x2 a1 = fp4pair<1>(c[2 * p], sc[2 * p]), b1 = fp4pair<1>(c[2 * p + 1], sc[2 * p + 1]);
+      const f32x2 a2 = fp4pair<2>(c[2 * p], sc[2 * p]), b2 = fp4pair<2>(c[2 * p + 1], sc[2 * p + 1]);
+      const f32x2 a3 = fp4pair<3>(c[2 * p], sc[2 * p]), b3 = fp4pair<3>(c[2 * p + 1], sc[2 * p + 1]);
+      o[0][p] = pack_exact(a0.x, b0.x); o[1][p] = pack_exact(a0.y, b0.y);
+      o[2][p] = pack_exact(a1.x, b1.x); o[3][p] = pack_exact(a1.y, b1.y);
+      o[4][p] = pack_exact(a2.x, b2.x); o[5][p] = pack_exact(a2.y, b2.y);
+      o[6][p] = pack_exact(a3.x, b3.x); o[7][p] = pack_exact(a3.y, b3.y);
+    } else {
+#pragma unroll
+      for (int col = 0; col < 8; ++col)
+        o[col][p] = nf4_bf16(lut, (c[2 * p] >> (4 * col)) & 0xFu, sc[2 * p]) |
+                    (nf4_bf16(lut, (c[2 * p + 1] >> (4 * col)) & 0xFu, sc[2 * p + 1]) << 16);
+    }
+  }
+#pragma unroll
+  for (int col = 0; col < 8; ++col)
+    *reinterpret_cast<uint2 *>(Bs + (ng * 8 + col) * SK + kg * 4) = make_uint2(o[col][0], o[col][1]);
+}
+
 // ---------------------------------------------------------------------------
 // the grouped GEMM
 // ---------------------------------------------------------------------------
-template <int BN>
-struct Shape {
-  static constexpr int WM = BN == 256 ? 2 : 4;  // waves along M
-  static constexpr int WN = 4 / WM;             // waves along N
-  static constexpr int TM = BM / WM / 32;       // 32x32 MFMA tiles per wave along M
-  static constexpr int TN = BN / WN / 32;       // ... along N
-};
-
-template <int BN>
+template <class C>
 __device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs,
-                                          f32x16 (&acc)[Shape<BN>::TM][Shape<BN>::TN]) {
-  constexpr int TM = Shape<BN>::TM, TN = Shape<BN>::TN, WN = Shape<BN>::WN;
+                                          f32x16 (&acc)[C::TM][C::TN]) {
+  constexpr int TM = C::TM, TN = C::TN, WN = C::WN;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid / WN, wn = wid % WN;
 #pragma unroll
@@ -375,40 +435,56 @@ __device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs
   }
 }
 
-// Runs one K segment into acc.  arow: the 4 A source rows of this thread's loads.
-template <int BN, int ASRC, int BSRC, int EPI>
-__device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[4],
-                                            uint16_t (*As)[BM * SK], uint16_t (*Bs)[BN * SK], const float *lut,
-                                            f32x16 (&acc)[Shape<BN>::TM][Shape<BN>::TN]) {
+template <class C>
+struct Smem {
+  uint16_t As[2][C::BM * SK];
+  uint16_t Bs[2][C::BN * SK];
+};
+
+// Runs one K segment into acc.  arow: the A source rows of this thread's loads;
+// active: this wave has at least one valid row (else it skips its MFMAs).
+template <class C, int ASRC, int BSRC, int EPI>
+__device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[C::ACH],
+                                            Smem<C> &sm, uint32_t *raw, uint32_t *raw_sc, const float *lut,
+                                            bool active, f32x16 (&acc)[C::TM][C::TN]) {
   const int nk = (s.K + BK - 1) / BK;
-  ARegs ar;
+  ARegs<C> ar;
   BRegs br;
-  a_load<ASRC>(s, arow, 0, ar);
-  b_load<BSRC, BN, EPI>(s, e, nt, N, I, 0, br);
-  a_store<ASRC>(As[0], ar);
-  b_store<BSRC, BN>(Bs[0], br, lut);
+  a_load<C, ASRC>(s, arow, 0, ar);
+  b_load<C, BSRC, EPI>(s, e, nt, N, I, 0, br);
+  a_store<C, ASRC>(sm.As[0], ar);
+  b_store<C, BSRC>(sm.Bs[0], raw, raw_sc, br, lut);
   __syncthreads();
+  if constexpr (raw_staged<BSRC>()) {
+    b_dequant_raw<C, BSRC>(sm.Bs[0], raw, raw_sc, lut);
+    __syncthreads();
+  }
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
     const bool more = ks + 1 < nk;
     if (more) {
-      a_load<ASRC>(s, arow, (ks + 1) * BK, ar);
-      b_load<BSRC, BN, EPI>(s, e, nt, N, I, (ks + 1) * BK, br);
+      a_load<C, ASRC>(s, arow, (ks + 1) * BK, ar);
+      b_load<C, BSRC, EPI>(s, e, nt, N, I, (ks + 1) * BK, br);
     }
-    mma_stage<BN>(As[cur], Bs[cur], acc);
+    if (active) mma_stage<C>(sm.As[cur], sm.Bs[cur], acc);
     if (more) {
-      a_store<ASRC>(As[cur ^ 1], ar);
-      b_store<BSRC, BN>(Bs[cur ^ 1], br, lut);
+      a_store<C, ASRC>(sm.As[cur ^ 1], ar);
+      b_store<C, BSRC>(sm.Bs[cur ^ 1], raw, raw_sc, br, lut);
+      if constexpr (raw_staged<BSRC>()) {
+        __syncthreads();
+        b_dequant_raw<C, BSRC>(sm.Bs[cur ^ 1], raw, raw_sc, lut);
+      }
     }
     __syncthreads();
   }
 }
 
-template <int BN, int ASRC, int BSRC, int B2SRC, int EPI>
-__global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
-  constexpr int TM = Shape<BN>::TM, TN = Shape<BN>::TN, WN = Shape<BN>::WN;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * SK];
+template <class C, int ASRC, int BSRC, int B2SRC, int EPI>
+__global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
+  constexpr int TM = C::TM, TN = C::TN, WN = C::WN, BN = C::BN, BMc = C::BM;
+  __shared__ __attribute__((aligned(16))) Smem<C> sm;
+  __shared__ __attribute__((aligned(16))) uint32_t raw[raw_staged<BSRC>() ? 64 * RAW_STRIDE : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t raw_sc[raw_staged<BSRC>() ? 64 * 4 : 1];
   __shared__ float lut[16];
 
   // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
@@ -421,7 +497,7 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
   const int mt = L / p.NT, nt = L % p.NT;
   int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
   while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
+    const int mid = (lo + hi) >> 1;
     if (p.tile_off[mid] <= mt)
       lo = mid;
     else
@@ -430,9 +506,10 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
   const int e = lo;
   const int rb = p.offsets[e];
   const int n_e = p.offsets[e + 1] - rb;
-  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int m0 = (mt - p.tile_off[e]) * BMc;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WN, wn = wid % WN;
+  const bool active = m0 + wm * TM * 32 < n_e;
 
   if constexpr (BSRC == B_NF4_K || BSRC == B_NF4_N) {
     if (tid < 16) lut[tid] = c_nf4[tid];
@@ -440,18 +517,17 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
   }
 
   // source rows of this thread's A loads (segment 1)
-  int64_t arow[4];
+  int64_t arow[C::ACH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int row = (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) ? (tid >> 1) : ((tid + NTHR * i) >> 3);
-    int pos = m0 + row;
-    if (pos >= n_e) {
+  for (int i = 0; i < C::ACH; ++i) {
+    const int row = (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) ? (tid >> 1) : ((tid + C::NTHR * i) >> 3);
+    const int pos = m0 + row;
+    if (pos >= n_e)
       arow[i] = -1;
-    } else if (ASRC == A_GATHER || ASRC == A_GATHER_Q) {
+    else if (ASRC == A_GATHER || ASRC == A_GATHER_Q)
       arow[i] = p.perm[rb + pos] / p.k;
-    } else {
+    else
       arow[i] = rb + pos;
-    }
   }
 
   f32x16 acc[TM][TN];
@@ -462,7 +538,7 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  run_segment<BN, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, As, Bs, lut, acc);
+  run_segment<C, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, sm, raw, raw_sc, lut, active, acc);
 
   // FP32 decode scales of segment 1: per expert (NVFP4 weights) x per row (NVFP4 activations)
   if constexpr (BSRC == B_Q4_K || BSRC == B_Q4_N || ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
@@ -474,9 +550,9 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
       for (int v = 0; v < 16; ++v) {
         float sc = sb;
         if constexpr (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
-          int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (pos < n_e) {
-            int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+            const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
             sc = sb * p.s1.a_sd[src];
           }
         }
@@ -487,17 +563,18 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
 
   if constexpr (B2SRC != B_NONE) {
     if (p.s2.K > 0) {
-      int64_t arow2[4];
+      int64_t arow2[C::ACH];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int pos = m0 + ((tid + NTHR * i) >> 3);
+      for (int i = 0; i < C::ACH; ++i) {
+        const int pos = m0 + ((tid + C::NTHR * i) >> 3);
         arow2[i] = pos < n_e ? (int64_t)(rb + pos) : -1;
       }
-      run_segment<BN, A_ROWS, B2SRC, EPI>(p.s2, e, nt, p.N, p.I, arow2, As, Bs, lut, acc);
+      run_segment<C, A_ROWS, B2SRC, EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, raw, raw_sc, lut, active, acc);
     }
   }
 
   // epilogue
+  if (!active) return;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -530,9 +607,9 @@ __global__ void __launch_bounds__(NTHR) moe_gemm(GemmParams p) {
           if (n < p.N) {
             const float val = acc[tm][tn][v] * p.out_scale;
             const uint32_t hb = f32_to_bf16(val);
-            const float lo = val - __uint_as_float(hb << 16);
+            const float lo2 = val - __uint_as_float(hb << 16);
             p.out0[grow * 2 * p.N + n] = (uint16_t)hb;
-            p.out0[grow * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo);
+            p.out0[grow * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
           }
         }
       } else if constexpr (EPI == EPI_STORE_F32) {
@@ -840,8 +917,10 @@ Seg seg_q(const void *a, int64_t a_ld, const bqm_qtensor &w, int K) {
 
 template <int BN, int ASRC, int BSRC, int B2SRC, int EPI>
 bqm_status launch(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+  using C = typename std::conditional<BN == 256, BigCfg, SmallCfg>::type;
+  static_assert(C::BM == BM, "tile offsets are computed for BM rows");
   const int grid = gemm_grid(R, p.E, p.NT);
-  moe_gemm<BN, ASRC, BSRC, B2SRC, EPI><<<grid, NTHR, 0, s>>>(p);
+  moe_gemm<C, ASRC, BSRC, B2SRC, EPI><<<grid, C::NTHR, 0, s>>>(p);
   return launch_status(what);
 }
 
