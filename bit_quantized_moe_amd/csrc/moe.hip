@@ -134,9 +134,25 @@ struct Cfg {
 using BigCfg = Cfg<256, 256, 4, 2>;
 using SmallCfg = Cfg<256, 64, 4, 1>;
 
-// Raw staging of an N-major 4-bit tile (64 k rows x 256 columns): codes with a
-// one-dword pad per row (conflict-free transposing reads) and the row's scales.
-constexpr int RAW_STRIDE = 33;  // dwords per raw code row (32 + 1 pad)
+// B tiles of N-major sources (the dgrad reads the rowwise weight transposed, and
+// the bf16 LoRA matrices there) stay in their natural [k][n] layout in LDS with a
+// row stride of BN + 32 bf16; MFMA fragments are read with the gfx950 transposing
+// LDS read.  Within each 16-lane group that read hands output lane 4a+b element b
+// of the 8-byte chunks addressed by lanes a, a+4, a+8, a+12, so lanes pointing at
+// rows k0 + s/4 and columns 4(s%4) deliver four consecutive k of one column each.
+template <int BN>
+constexpr int skt() {
+  return BN + 32;
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// E4M3 scale byte -> float (hardware OCP E4M3 decode; exact, subnormals included)
+template <int SEL>
+__device__ __forceinline__ float e4m3_hw(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8(w, SEL);
+}
 
 // ---------------------------------------------------------------------------
 // exact 4-bit -> bf16 conversion with the hardware FP4 converter
@@ -215,10 +231,11 @@ __device__ __forceinline__ void a_store(uint16_t *As, const ARegs<C> &r) {
     const int row = tid >> 1, half = tid & 1;
     const uint32_t cw[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
     uint4 *dst = reinterpret_cast<uint4 *>(As + row * SK + half * 32);
+    const float s0 = e4m3_hw<0>(r.v[1].x), s1 = e4m3_hw<0>(r.v[1].y);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t o[4];
-      fp4x8_hw(cw[q], e4m3_to_f32(q < 2 ? r.v[1].x : r.v[1].y), o);
+      fp4x8_hw(cw[q], q < 2 ? s0 : s1, o);
       dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
@@ -232,8 +249,8 @@ struct BRegs {
 };
 
 template <int BSRC>
-constexpr bool raw_staged() {
-  return BSRC == B_Q4_N || BSRC == B_NF4_N;
+constexpr bool trans_b() {
+  return BSRC == B_Q4_N || BSRC == B_NF4_N || BSRC == B_BF_N;
 }
 
 template <class C, int BSRC, int EPI>
@@ -259,23 +276,21 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
     } else {
       r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64]);
     }
-  } else if constexpr (raw_staged<BSRC>()) {
-    // N-major 4-bit weight [K rows][N cols]: the 64 x BN tile is loaded coalesced
-    // (one 16-byte chunk of codes per thread, plus the rows' scales) and staged raw
-    static_assert(BN == 256 && C::NTHR == 512, "raw staging expects a 256-column tile and 512 threads");
-    const int row = tid >> 3, chunk = tid & 7;  // 64 rows x 8 chunks of 16 B
+  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
+    // N-major 4-bit weight [K rows][N cols]: one k row, 32 columns (16 B of codes) per thread
+    static_assert(BN == 256 && C::NTHR == 512, "N-major 4-bit tile expects 256 columns and 512 threads");
+    const int row = tid >> 3, chunk = tid & 7;
     const int n = nt * BN + chunk * 32;
     const int64_t kk = k0 + row;
     if (n < N) {
       const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) +
                                                        kk * (s.b_cols / 2) + n / 2);
       r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      if constexpr (BSRC == B_Q4_N) {
+      if constexpr (BSRC == B_Q4_N)
         r.w[4] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) +
                                                     kk * (s.b_cols / 16) + n / 16);
-      } else {
-        r.w[4] = (chunk & 1) ? 0u : __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
-      }
+      else
+        r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
     } else {
       r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
     }
@@ -294,49 +309,62 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   } else if constexpr (BSRC == B_BF_N) {
-    // bf16 [K rows][N cols]: 8 k rows x 8 columns per thread, transposed at the store
-    constexpr int NG = BN / 8;
-    if (tid >= NG * 8) return;
-    const int kg = tid & 7, ng = tid >> 3;
-    const int n = nt * BN + ng * 8;
+    // bf16 [K rows][N cols]: 64 rows x BN/8 chunks of 16 B, kept in natural layout
+    constexpr int CPR = BN / 8;
+    constexpr int CH = 64 * CPR / C::NTHR;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int kk = k0 + kg * 8 + q;
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + C::NTHR * i;
+      const int row = c / CPR, n = nt * BN + (c % CPR) * 8;
+      const int kk = k0 + row;
       const int kb = s.kmod ? kk % s.kmod : kk;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (n < N && kk < s.K)
         v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + (int64_t)kb * s.b_cols + n);
-      r.w[4 * q] = v.x; r.w[4 * q + 1] = v.y; r.w[4 * q + 2] = v.z; r.w[4 * q + 3] = v.w;
+      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   }
 }
 
-// Writes the loaded registers: dequantized bf16 into Bs, or raw codes into the staging area.
+// Writes the loaded registers into Bs as bf16 (dequantizing 4-bit codes).
 template <class C, int BSRC>
-__device__ __forceinline__ void b_store(uint16_t *Bs, uint32_t *raw, uint32_t *raw_sc, const BRegs &r,
-                                        const float *lut) {
+__device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const float *lut) {
   constexpr int BN = C::BN;
   const int tid = threadIdx.x;
   if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
     const int j = tid >> 1, kofs = (tid & 1) * 32;
     uint4 *dst = reinterpret_cast<uint4 *>(Bs + j * SK + kofs);
+    float s0, s1;
+    if constexpr (BSRC == B_Q4_K) {
+      s0 = e4m3_hw<0>(r.w[4]);
+      s1 = e4m3_hw<1>(r.w[4]);
+    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t o[4];
       if constexpr (BSRC == B_Q4_K)
-        fp4x8_hw(r.w[q], e4m3_to_f32((r.w[4] >> (8 * (q >> 1))) & 0xFFu), o);
+        fp4x8_hw(r.w[q], q < 2 ? s0 : s1, o);
       else
         nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
       dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
     }
-  } else if constexpr (raw_staged<BSRC>()) {
+  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
+    // natural layout: row k, columns chunk*32 .. +32 (element pairs along n)
     const int row = tid >> 3, chunk = tid & 7;
-    uint32_t *dst = raw + row * RAW_STRIDE + chunk * 4;
-    dst[0] = r.w[0]; dst[1] = r.w[1]; dst[2] = r.w[2]; dst[3] = r.w[3];
+    uint4 *dst = reinterpret_cast<uint4 *>(Bs + row * skt<BN>() + chunk * 32);
+    float s0, s1;
     if constexpr (BSRC == B_Q4_N) {
-      reinterpret_cast<uint16_t *>(raw_sc)[row * 8 + chunk] = (uint16_t)r.w[4];
-    } else {
-      if (!(chunk & 1)) raw_sc[row * 4 + (chunk >> 1)] = r.w[4];
+      s0 = e4m3_hw<0>(r.w[4]);
+      s1 = e4m3_hw<1>(r.w[4]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t o[4];
+      if constexpr (BSRC == B_Q4_N)
+        fp4x8_hw(r.w[q], q < 2 ? s0 : s1, o);
+      else
+        nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
+      dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (BSRC == B_BF_K) {
     constexpr int CH = BN * 8 / C::NTHR;
@@ -347,72 +375,36 @@ __device__ __forceinline__ void b_store(uint16_t *Bs, uint32_t *raw, uint32_t *r
           make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]);
     }
   } else if constexpr (BSRC == B_BF_N) {
-    constexpr int NG = BN / 8;
-    if (tid >= NG * 8) return;
-    const int kg = tid & 7, ng = tid >> 3;
-    // r.w[4q + c/2] holds column c (low half if c even) of k row q
+    constexpr int CPR = BN / 8;
+    constexpr int CH = 64 * CPR / C::NTHR;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint32_t o[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = r.w[4 * (2 * p) + (c >> 1)], w1 = r.w[4 * (2 * p + 1) + (c >> 1)];
-        const uint32_t b0 = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-        const uint32_t b1 = (c & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
-        o[p] = b0 | (b1 << 16);
-      }
-      *reinterpret_cast<uint4 *>(Bs + (ng * 8 + c) * SK + kg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int i = 0; i < CH; ++i) {
+      const int c = tid + C::NTHR * i;
+      *reinterpret_cast<uint4 *>(Bs + (c / CPR) * skt<BN>() + (c % CPR) * 8) =
+          make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]);
     }
   }
-}
-
-// Raw-staged N-major tile -> bf16 [BN][SK] with k contiguous.  Thread -> 4 k rows
-// x 8 columns (kg fastest across lanes: conflict-free 8-byte stores and reads).
-template <class C, int BSRC>
-__device__ __forceinline__ void b_dequant_raw(uint16_t *Bs, const uint32_t *raw, const uint32_t *raw_sc,
-                                              const float *lut) {
-  const int tid = threadIdx.x;
-  const int kg = tid & 15, ng = tid >> 4;  // 16 groups of 4 k rows, 32 groups of 8 columns
-  uint32_t c[4];
-  float sc[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = kg * 4 + q;
-    c[q] = raw[row * RAW_STRIDE + ng];
-    if constexpr (BSRC == B_Q4_N)
-      sc[q] = e4m3_to_f32(reinterpret_cast<const uint8_t *>(raw_sc)[row * 16 + (ng >> 1)]);
-    else
-      sc[q] = __uint_as_float(raw_sc[row * 4 + (ng >> 3)]);
-  }
-  // o[col][pair]: bf16 pairs (k rows 2p, 2p+1) of column col
-  uint32_t o[8][2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    if constexpr (BSRC == B_Q4_N) {
-      const f32x2 a0 = fp4pair<0>(c[2 * p], sc[2 * p]), b0 = fp4pair<0>(c[2 * p + 1], sc[2 * p + 1]);
-      const f32x2 a1 = fp4pair<1>(c[2 * p], sc[2 * p]), b1 = fp4pair<1>(c[2 * p + 1], sc[2 * p + 1]);
-      const f32x2 a2 = fp4pair<2>(c[2 * p], sc[2 * p]), b2 = fp4pair<2>(c[2 * p + 1], sc[2 * p + 1]);
-      const f32x2 a3 = fp4pair<3>(c[2 * p], sc[2 * p]), b3 = fp4pair<3>(c[2 * p + 1], sc[2 * p + 1]);
-      o[0][p] = pack_exact(a0.x, b0.x); o[1][p] = pack_exact(a0.y, b0.y);
-      o[2][p] = pack_exact(a1.x, b1.x); o[3][p] = pack_exact(a1.y, b1.y);
-      o[4][p] = pack_exact(a2.x, b2.x); o[5][p] = pack_exact(a2.y, b2.y);
-      o[6][p] = pack_exact(a3.x, b3.x); o[7][p] = pack_exact(a3.y, b3.y);
-    } else {
-#pragma unroll
-      for (int col = 0; col < 8; ++col)
-        o[col][p] = nf4_bf16(lut, (c[2 * p] >> (4 * col)) & 0xFu, sc[2 * p]) |
-                    (nf4_bf16(lut, (c[2 * p + 1] >> (4 * col)) & 0xFu, sc[2 * p + 1]) << 16);
-    }
-  }
-#pragma unroll
-  for (int col = 0; col < 8; ++col)
-    *reinterpret_cast<uint2 *>(Bs + (ng * 8 + col) * SK + kg * 4) = make_uint2(o[col][0], o[col][1]);
 }
 
 // ---------------------------------------------------------------------------
 // the grouped GEMM
 // ---------------------------------------------------------------------------
-template <class C>
+// B fragment (8 consecutive k of one column per lane) from a natural [k][n] tile
+template <int BN>
+__device__ __forceinline__ bf16x8 b_frag_trans(const uint16_t *Bs, int kbase, int nbase, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = kbase + 8 * (g >> 1) + (s >> 2);
+  const int col = nbase + 16 * (g & 1) + 4 * (s & 3);
+  const uint16_t *p0 = Bs + row * skt<BN>() + col;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 4 * skt<BN>()));
+  const s16x4 h0 = lo, h1 = hi;
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <class C, bool TRANS>
 __device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs,
                                           f32x16 (&acc)[C::TM][C::TN]) {
   constexpr int TM = C::TM, TN = C::TN, WN = C::WN;
@@ -425,8 +417,12 @@ __device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs
     for (int tm = 0; tm < TM; ++tm)
       af[tm] = *reinterpret_cast<const bf16x8 *>(As + (wm * TM * 32 + tm * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      bfr[tn] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * TN * 32 + tn * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+    for (int tn = 0; tn < TN; ++tn) {
+      if constexpr (TRANS)
+        bfr[tn] = b_frag_trans<C::BN>(Bs, kk * 16, wn * TN * 32 + tn * 32, lane);
+      else
+        bfr[tn] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * TN * 32 + tn * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+    }
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -437,28 +433,25 @@ __device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs
 
 template <class C>
 struct Smem {
+  static constexpr int BSZ = C::BN * SK > BK * skt<C::BN>() ? C::BN * SK : BK * skt<C::BN>();
   uint16_t As[2][C::BM * SK];
-  uint16_t Bs[2][C::BN * SK];
+  uint16_t Bs[2][BSZ];
 };
 
 // Runs one K segment into acc.  arow: the A source rows of this thread's loads;
 // active: this wave has at least one valid row (else it skips its MFMAs).
 template <class C, int ASRC, int BSRC, int EPI>
 __device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[C::ACH],
-                                            Smem<C> &sm, uint32_t *raw, uint32_t *raw_sc, const float *lut,
-                                            bool active, f32x16 (&acc)[C::TM][C::TN]) {
+                                            Smem<C> &sm, const float *lut, bool active,
+                                            f32x16 (&acc)[C::TM][C::TN]) {
   const int nk = (s.K + BK - 1) / BK;
   ARegs<C> ar;
   BRegs br;
   a_load<C, ASRC>(s, arow, 0, ar);
   b_load<C, BSRC, EPI>(s, e, nt, N, I, 0, br);
   a_store<C, ASRC>(sm.As[0], ar);
-  b_store<C, BSRC>(sm.Bs[0], raw, raw_sc, br, lut);
+  b_store<C, BSRC>(sm.Bs[0], br, lut);
   __syncthreads();
-  if constexpr (raw_staged<BSRC>()) {
-    b_dequant_raw<C, BSRC>(sm.Bs[0], raw, raw_sc, lut);
-    __syncthreads();
-  }
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
     const bool more = ks + 1 < nk;
@@ -466,14 +459,10 @@ __device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, 
       a_load<C, ASRC>(s, arow, (ks + 1) * BK, ar);
       b_load<C, BSRC, EPI>(s, e, nt, N, I, (ks + 1) * BK, br);
     }
-    if (active) mma_stage<C>(sm.As[cur], sm.Bs[cur], acc);
+    if (active) mma_stage<C, trans_b<BSRC>()>(sm.As[cur], sm.Bs[cur], acc);
     if (more) {
       a_store<C, ASRC>(sm.As[cur ^ 1], ar);
-      b_store<C, BSRC>(sm.Bs[cur ^ 1], raw, raw_sc, br, lut);
-      if constexpr (raw_staged<BSRC>()) {
-        __syncthreads();
-        b_dequant_raw<C, BSRC>(sm.Bs[cur ^ 1], raw, raw_sc, lut);
-      }
+      b_store<C, BSRC>(sm.Bs[cur ^ 1], br, lut);
     }
     __syncthreads();
   }
@@ -483,8 +472,6 @@ template <class C, int ASRC, int BSRC, int B2SRC, int EPI>
 __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
   constexpr int TM = C::TM, TN = C::TN, WN = C::WN, BN = C::BN, BMc = C::BM;
   __shared__ __attribute__((aligned(16))) Smem<C> sm;
-  __shared__ __attribute__((aligned(16))) uint32_t raw[raw_staged<BSRC>() ? 64 * RAW_STRIDE : 1];
-  __shared__ __attribute__((aligned(16))) uint32_t raw_sc[raw_staged<BSRC>() ? 64 * 4 : 1];
   __shared__ float lut[16];
 
   // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
@@ -538,7 +525,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  run_segment<C, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, sm, raw, raw_sc, lut, active, acc);
+  run_segment<C, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, sm, lut, active, acc);
 
   // FP32 decode scales of segment 1: per expert (NVFP4 weights) x per row (NVFP4 activations)
   if constexpr (BSRC == B_Q4_K || BSRC == B_Q4_N || ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
@@ -569,7 +556,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
         const int pos = m0 + ((tid + C::NTHR * i) >> 3);
         arow2[i] = pos < n_e ? (int64_t)(rb + pos) : -1;
       }
-      run_segment<C, A_ROWS, B2SRC, EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, raw, raw_sc, lut, active, acc);
+      run_segment<C, A_ROWS, B2SRC, EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, lut, active, acc);
     }
   }
 
