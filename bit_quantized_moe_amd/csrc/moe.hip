@@ -64,6 +64,7 @@ struct GemmParams {
   int NT;  // output column tiles
   Seg s1, s2;  // s2.K == 0: no second segment
   float out_scale;
+  const float *div_e;     // EPI_STORE_SPLIT: per-expert divisor of the output (NULL: none)
   uint16_t *out0, *out1;  // bf16 outputs
   float *outf;            // FP32 output (h, y, dX rows)
   const float *h_in;      // saved FP32 gate/up activations (dgrad epilogue)
@@ -386,6 +387,9 @@ __device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const floa
   }
 }
 
+// logistic function with the hardware exponential and reciprocal (about 2 ulp)
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
 // ---------------------------------------------------------------------------
 // the grouped GEMM
 // ---------------------------------------------------------------------------
@@ -527,21 +531,26 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 
   run_segment<C, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, sm, lut, active, acc);
 
-  // FP32 decode scales of segment 1: per expert (NVFP4 weights) x per row (NVFP4 activations)
-  if constexpr (BSRC == B_Q4_K || BSRC == B_Q4_N || ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
+  // FP32 decode scales of segment 1.  NVFP4 weights with bf16 activations: the
+  // per-expert s_dec multiplies the whole accumulator in the epilogue (the
+  // producer of the LoRA segment's A operand divided it by s_dec).  NVFP4
+  // activations (per-row scales): segment 1 is rescaled before the LoRA segment.
+  constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
+  constexpr bool kQB = BSRC == B_Q4_K || BSRC == B_Q4_N;
+  float esc = 1.0f;
+  if constexpr (kQB && !kQA) esc = p.s1.b_sd[e];
+  if constexpr (kQA) {
     float sb = 1.0f;
-    if constexpr (BSRC == B_Q4_K || BSRC == B_Q4_N) sb = p.s1.b_sd[e];
+    if constexpr (kQB) sb = p.s1.b_sd[e];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         float sc = sb;
-        if constexpr (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) {
-          const int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          if (pos < n_e) {
-            const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
-            sc = sb * p.s1.a_sd[src];
-          }
+        const int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (pos < n_e) {
+          const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+          sc = sb * p.s1.a_sd[src];
         }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) acc[tm][tn][v] *= sc;
@@ -562,6 +571,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 
   // epilogue
   if (!active) return;
+  const float osc = p.div_e ? p.out_scale / p.div_e[e] : p.out_scale;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -574,8 +584,8 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
         for (int q = 0; q < TN / 2; ++q) {
           const int i = nt * (BN / 2) + wn * 64 + q * 32 + (lane & 31);
           if (i >= p.I) continue;
-          const float g = acc[tm][2 * q][v], u = acc[tm][2 * q + 1][v];
-          const float a = g / (1.0f + __expf(-g)) * u;
+          const float g = acc[tm][2 * q][v] * esc, u = acc[tm][2 * q + 1][v] * esc;
+          const float a = g * sigmoid_f(g) * u;
           p.outf[grow * 2 * p.I + i] = g;
           p.outf[grow * 2 * p.I + p.I + i] = u;
           p.out1[grow * p.I + i] = (uint16_t)f32_to_bf16(a);
@@ -584,7 +594,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * p.out_scale);
+          if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * esc * p.out_scale);
         }
       } else if constexpr (EPI == EPI_STORE_SPLIT) {
         // FP32 value kept as an unevaluated pair of bf16 (hi in columns [0, N), lo in [N, 2N))
@@ -592,7 +602,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
           if (n < p.N) {
-            const float val = acc[tm][tn][v] * p.out_scale;
+            const float val = acc[tm][tn][v] * osc;
             const uint32_t hb = f32_to_bf16(val);
             const float lo2 = val - __uint_as_float(hb << 16);
             p.out0[grow * 2 * p.N + n] = (uint16_t)hb;
@@ -603,7 +613,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * p.out_scale;
+          if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * esc * p.out_scale;
         }
       } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
         const float w = p.tw[p.perm[grow]];
@@ -613,8 +623,8 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
           if (i >= p.N) continue;
           const float g = p.h_in[grow * 2 * p.I + i];
           const float u = p.h_in[grow * 2 * p.I + p.I + i];
-          const float sg = 1.0f / (1.0f + __expf(-g));
-          const float da = w * acc[tm][tn][v];
+          const float sg = sigmoid_f(g);
+          const float da = w * (acc[tm][tn][v] * esc);
           const float dg = da * u * sg * (1.0f + g * (1.0f - sg));
           const float du = da * g * sg;
           p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(dg);
@@ -639,6 +649,7 @@ struct WgradParams {
   const uint16_t *Q;
   int64_t q_ld;
   int q_gather;
+  const float *c_scale;  // per-expert factor of the output (NULL: none)
   float *C;
 };
 
@@ -710,11 +721,12 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
     }
     __syncthreads();
   }
+  const float cs = p.c_scale ? p.c_scale[e] : 1.0f;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int m = m0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
     const int n = n0 + wn * 32 + (lane & 31);
-    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[v];
+    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[v] * cs;
   }
 }
 
@@ -911,6 +923,14 @@ bqm_status launch(const GemmParams &p, int64_t R, hipStream_t s, const char *wha
   return launch_status(what);
 }
 
+// NVFP4 weights with bf16 activations apply the per-expert s_dec to the whole
+// accumulator in the epilogue, so the LoRA intermediates (U in the forward, V in
+// the dgrad) that feed the same accumulator are stored divided by it.  With
+// NVFP4 activations (forward only) segment 1 is rescaled in-kernel instead.
+bool lora_folds_s_dec(const bqm_moe_desc *d, bool forward) {
+  return d->w_gu.fmt == BQM_FMT_NVFP4 && !(forward && d->act_quant);
+}
+
 GemmParams base_params(const bqm_moe_desc *d, const Ws &w) {
   GemmParams p{};
   p.perm = w.at<int32_t>(w.L.perm);
@@ -963,13 +983,15 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
   uint16_t *ugu = w.at<uint16_t>(w.L.ugu), *udn = w.at<uint16_t>(w.L.udn);
   float *h = w.at<float>(w.L.h), *y = w.at<float>(w.L.y);
   uint16_t *a = w.at<uint16_t>(w.L.a);
-  // U_gu = s X A_gu^T   [R, r]
+  const bool fold_fwd = lora_folds_s_dec(d, true);
+  // U_gu = s X A_gu^T   [R, r]  (divided by the expert's s_dec when that folds)
   if (r > 0) {
     GemmParams p = base_params(d, w);
     p.N = r;
     p.NT = (int)cdiv(r, 64);
     p.s1 = seg_bf16(x, H, d->A_gu, r, H, H);
     p.out_scale = ls;
+    p.div_e = fold_fwd ? d->w_gu.s_dec : nullptr;
     p.out0 = ugu;
     BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_a gate_up")));
   }
@@ -1003,6 +1025,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.NT = (int)cdiv(r, 64);
     p.s1 = seg_bf16(a, I, d->A_dn, r, I, I);
     p.out_scale = ls;
+    p.div_e = fold_fwd ? d->w_dn.s_dec : nullptr;
     p.out0 = udn;
     BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_a down")));
   }
@@ -1102,6 +1125,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.NT = (int)cdiv(r, 64);
     p.s1 = seg_bf16(dy, H, d->B_dn, H, r, H);
     p.out_scale = ls;
+    p.div_e = lora_folds_s_dec(d, false) ? d->w_dn.s_dec : nullptr;
     p.out0 = vdn;
     BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_b^T down")));
   }
@@ -1127,6 +1151,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.NT = (int)cdiv(r, 64);
     p.s1 = seg_bf16(dh, 2 * I, d->B_gu, 2 * I, r, 2 * I);
     p.out_scale = ls;
+    p.div_e = lora_folds_s_dec(d, false) ? d->w_gu.s_dec : nullptr;
     p.out0 = vgu;
     BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_b^T gate_up")));
   }
@@ -1173,7 +1198,7 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   p.tw = w.at<float>(w.L.tw);
   p.k = d->k;
   auto go = [&](int M, int N, const uint16_t *P, int64_t pld, int pg, int sp, const uint16_t *Q, int64_t qld, int qg,
-                float *C, const char *what) {
+                const float *cs, float *C, const char *what) {
     p.M = M;
     p.N = N;
     p.P = P;
@@ -1183,6 +1208,7 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
     p.Q = Q;
     p.q_ld = qld;
     p.q_gather = qg;
+    p.c_scale = cs;
     p.C = C;
     dim3 grid((unsigned)(cdiv(M, WB) * cdiv(N, WB)), (unsigned)d->E);
     lora_wgrad<<<grid, NTHR, 0, s>>>(p);
@@ -1192,11 +1218,16 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   const uint16_t *udn = w.at<uint16_t>(w.L.udn), *vdn = w.at<uint16_t>(w.L.vdn), *a = w.at<uint16_t>(w.L.a);
   // dB_gu [2I, r] = dh^T U_gu' ; dA_gu [r, H] = V_gu'^T X ; U' and V' already carry the LoRA scale
   mark(d, BQM_STAGE_LORA_GRAD, 0, s);
-  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, 2 * r, 0, dB_gu, "lora dB_gu"));
-  BQM_TRY(go(r, H, vgu, 2 * r, 0, 0, x, H, 1, dA_gu, "lora dA_gu"));
+  // (U, V divided by s_dec where that folds: the expert's factor is restored on the output)
+  const float *fu_gu = lora_folds_s_dec(d, true) ? d->w_gu.s_dec : nullptr;
+  const float *fv_gu = lora_folds_s_dec(d, false) ? d->w_gu.s_dec : nullptr;
+  const float *fu_dn = lora_folds_s_dec(d, true) ? d->w_dn.s_dec : nullptr;
+  const float *fv_dn = lora_folds_s_dec(d, false) ? d->w_dn.s_dec : nullptr;
+  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, 2 * r, 0, fu_gu, dB_gu, "lora dB_gu"));
+  BQM_TRY(go(r, H, vgu, 2 * r, 0, 0, x, H, 1, fv_gu, dA_gu, "lora dA_gu"));
   // dB_dn [H, r] = (w dY)^T U_dn' ; dA_dn [r, I] = (w V_dn')^T a
-  BQM_TRY(go(H, r, dy, H, 1, 1, udn, 2 * r, 0, dB_dn, "lora dB_dn"));
-  BQM_TRY(go(r, I, vdn, 2 * r, 0, 1, a, I, 0, dA_dn, "lora dA_dn"));
+  BQM_TRY(go(H, r, dy, H, 1, 1, udn, 2 * r, 0, fu_dn, dB_dn, "lora dB_dn"));
+  BQM_TRY(go(r, I, vdn, 2 * r, 0, 1, a, I, 0, fv_dn, dA_dn, "lora dA_dn"));
   mark(d, BQM_STAGE_LORA_GRAD, 1, s);
   return BQM_OK;
 }
