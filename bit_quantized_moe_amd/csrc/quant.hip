@@ -16,16 +16,17 @@
 // Memory layout: one thread owns one 16-element block (32 bytes of bf16 in,
 // 8 bytes of codes and 1 scale byte out); consecutive threads own consecutive
 // blocks, so a wave reads 2 KB and writes 512 B of codes contiguously.  The
-// per-tensor amax is a separate pass over groups of matrices small enough that
-// the quantize pass re-reads them from the 256 MB Infinity Cache.
+// per-tensor amax is a separate pass (one atomicMax per workgroup into the
+// matrix's slot) before the quantize pass.
 #include "common.h"
 #include "nf4_levels.inc"
+
+#include <algorithm>
 
 namespace bqm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxPartials = 1024;
 
 // Round a non-negative finite float to the E4M3FN grid (nearest, ties to even,
 // saturating at 448) and return its code 0..126.
@@ -42,85 +43,85 @@ __device__ __forceinline__ uint32_t e4m3_rne_satfinite(float t) {
   return code < 126u ? code : 126u;
 }
 
-// Round a non-negative float to the E2M1 grid {0,.5,1,1.5,2,3,4,6} (nearest,
-// ties to the even code, saturating at 6).  Adding C = 2^22, 2^23 or 2^24 makes
-// the float32 ulp equal to the grid step of the value's range (0.5, 1, 2), so
-// one correctly rounded add performs the rounding; code parity equals the
-// parity of the float32 mantissa there.
-__device__ __forceinline__ float e2m1_round(float v) {
-  float c = v < 2.0f ? 0x1p22f : (v < 4.0f ? 0x1p23f : 0x1p24f);
-  float q = (v + c) - c;
-  return fminf(q, 6.0f);
-}
+// One scale candidate: E2M1 codes of y * r (the hardware conversion rounds to
+// nearest, ties to even, saturating at 6, and keeps the sign) and the squared
+// error of the decoded values against y, summed in element order 0..15 in FP32.
+// Signs cancel in the error: |y| - |q| sb = +-(y - q sb).
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 
-// grid value -> magnitude code
-__device__ __forceinline__ uint32_t e2m1_code(float q) {
-  return q <= 2.0f ? (uint32_t)(q * 2.0f) : (q == 3.0f ? 5u : (q == 4.0f ? 6u : 7u));
-}
-
-// One scale candidate: codes (magnitudes only) and the squared error, summed in
-// element order 0..15 in FP32.
-__device__ __forceinline__ float candidate(const float (&ay)[16], float sb, uint32_t &c_lo,
+__device__ __forceinline__ float candidate(const float (&y)[16], float sb, float r, uint32_t &c_lo,
                                            uint32_t &c_hi) {
-  float r = sb > 0.0f ? 1.0f / sb : 0.0f;
-  float err = 0.0f;
-  c_lo = 0u;
-  c_hi = 0u;
+  uint32_t c[2] = {0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = ay[i] * r;
-    float q = e2m1_round(v);
-    float d = ay[i] - q * sb;  // q*sb is exact (<= 6 significant bits)
-    err = err + d * d;
-    uint32_t c = e2m1_code(q);
-    if (i < 8)
-      c_lo |= c << (4 * i);
-    else
-      c_hi |= c << (4 * (i - 8));
+  for (int p = 0; p < 8; ++p) {
+    const float v0 = y[2 * p] * r, v1 = y[2 * p + 1] * r;
+    switch (p & 3) {
+      case 0: c[p >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[p >> 2], v0, v1, 1.0f, 0); break;
+      case 1: c[p >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[p >> 2], v0, v1, 1.0f, 1); break;
+      case 2: c[p >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[p >> 2], v0, v1, 1.0f, 2); break;
+      default: c[p >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c[p >> 2], v0, v1, 1.0f, 3); break;
+    }
   }
+  float err = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    f32x2 q;
+    switch (p & 3) {
+      case 0: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 0); break;
+      case 1: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 1); break;
+      case 2: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 2); break;
+      default: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 3); break;
+    }
+    // q*sb is exact (<= 6 significant bits), so the fused form rounds y - q*sb once, as
+    // the separate product and difference do
+    const float d0 = __builtin_fmaf(-q.x, sb, y[2 * p]);
+    err = err + d0 * d0;
+    const float d1 = __builtin_fmaf(-q.y, sb, y[2 * p + 1]);
+    err = err + d1 * d1;
+  }
+  c_lo = c[0];
+  c_hi = c[1];
   return err;
 }
 
 // Quantize one block of 16 bf16 values held as 8 words; returns the E4M3 code.
+// rcp[c] = fl(1 / e4m3(c)) (0 for c = 0).
 template <bool kFos>
-__device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float s_enc, uint32_t &lo,
-                                                  uint32_t &hi) {
-  float ay[16];
+__device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float s_enc, const float *rcp,
+                                                  uint32_t &lo, uint32_t &hi) {
+  float y[16];
   float t = 0.0f;
-  uint32_t sg_lo = 0u, sg_hi = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float y0 = bf16_lo(w[i]) * s_enc;
-    float y1 = bf16_hi(w[i]) * s_enc;
-    ay[2 * i] = fabsf(y0);
-    ay[2 * i + 1] = fabsf(y1);
-    t = fmaxf(t, fmaxf(ay[2 * i], ay[2 * i + 1]));
-    uint32_t s0 = (w[i] >> 15) & 1u, s1 = w[i] >> 31;
-    if (i < 4) {
-      sg_lo |= (s0 << (8 * i + 3)) | (s1 << (8 * i + 7));
-    } else {
-      sg_hi |= (s0 << (8 * (i - 4) + 3)) | (s1 << (8 * (i - 4) + 7));
-    }
+    y[2 * i] = bf16_lo(w[i]) * s_enc;
+    y[2 * i + 1] = bf16_hi(w[i]) * s_enc;
+    t = fmaxf(t, fmaxf(fabsf(y[2 * i]), fabsf(y[2 * i + 1])));
   }
-  uint32_t sb6 = e4m3_rne_satfinite(t / 6.0f);
-  uint32_t l6, h6;
-  float e6 = candidate(ay, e4m3_to_f32(sb6), l6, h6);
+  const uint32_t sb6 = e4m3_rne_satfinite(t / 6.0f);
+  const float e6 = candidate(y, __builtin_amdgcn_cvt_f32_fp8(sb6, 0), rcp[sb6], lo, hi);
   uint32_t sb = sb6;
-  lo = l6;
-  hi = h6;
   if (kFos) {
-    uint32_t sb4 = e4m3_rne_satfinite(t * 0.25f);  // == t/4 exactly rounded
-    uint32_t l4, h4;
-    float e4 = candidate(ay, e4m3_to_f32(sb4), l4, h4);
-    if (e4 < e6) {
-      sb = sb4;
-      lo = l4;
-      hi = h4;
+    const uint32_t sb4 = e4m3_rne_satfinite(t * 0.25f);  // == t/4 exactly rounded
+    if (sb4 != sb6) {
+      uint32_t l4, h4;
+      const float e4 = candidate(y, __builtin_amdgcn_cvt_f32_fp8(sb4, 0), rcp[sb4], l4, h4);
+      if (e4 < e6) {
+        sb = sb4;
+        lo = l4;
+        hi = h4;
+      }
     }
   }
-  lo |= sg_lo;
-  hi |= sg_hi;
   return sb;
+}
+
+// Fills rcp[0..127) with fl(1 / e4m3(c)) (rcp[0] = 0); the block synchronizes.
+__device__ __forceinline__ void fill_rcp(float *rcp) {
+  if (threadIdx.x < 127) {
+    const float v = e4m3_to_f32(threadIdx.x);
+    rcp[threadIdx.x] = threadIdx.x ? 1.0f / v : 0.0f;
+  }
+  __syncthreads();
 }
 
 __device__ __forceinline__ void load_block16(const uint4 *p, uint32_t (&w)[8]) {
@@ -170,61 +171,65 @@ __device__ __forceinline__ void global_scale(float amax, float denom, float &s_d
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
-// Pass 1 of the per-tensor quantizer: partial amax (as bf16 magnitude bits) of
-// P contiguous chunks of each matrix.  grid = (P, n_mat_chunk).
-__global__ void __launch_bounds__(kThreads) nvfp4_amax_partials(const uint4 *__restrict__ x,
-                                                                int64_t vec_per_mat, int P,
-                                                                uint32_t *__restrict__ partials) {
-  __shared__ uint32_t red[kThreads / 64];
-  const int64_t m = blockIdx.y;
-  const uint4 *xm = x + m * vec_per_mat;
-  int64_t cs = (vec_per_mat + P - 1) / P;
-  int64_t b = (int64_t)blockIdx.x * cs, e = b + cs < vec_per_mat ? b + cs : vec_per_mat;
-  uint32_t mx = 0u;
-  for (int64_t i = b + threadIdx.x; i < e; i += kThreads) {
-    uint4 v = xm[i];
-    uint32_t a = absmax_bits_u32(v.x), c = absmax_bits_u32(v.y);
-    uint32_t d = absmax_bits_u32(v.z), f = absmax_bits_u32(v.w);
-    a = a > c ? a : c;
-    d = d > f ? d : f;
-    a = a > d ? a : d;
-    mx = mx > a ? mx : a;
-  }
-  mx = block_max_u(mx, red);
-  if (threadIdx.x == 0) partials[m * P + blockIdx.x] = mx;
+// Per-tensor quantizer in two launches over the whole stack: the amax pass
+// (every 16-byte vector read once, a block max, one atomicMax per workgroup
+// into the matrix's slot) and the quantize pass, which reads the final amax.
+// The second read of the input is inherent to a per-tensor scale; callers
+// that already hold the scales pass them in and skip the first launch.
+constexpr int64_t kAmaxVec = 16384;     // 128K elements per amax chunk
+constexpr int64_t kQuantBlocks = 2048;  // 32K elements per quantize chunk
+
+__global__ void __launch_bounds__(kThreads) clear_u32(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) p[i] = 0u;
 }
 
-// Pass 2 of the per-tensor quantizer.  grid = (G, n_mat_chunk).
+// grid = n_mat * P workgroups
+__global__ void __launch_bounds__(kThreads) nvfp4_amax(const uint4 *__restrict__ x, int64_t vec_per_mat, int64_t P,
+                                                       uint32_t *__restrict__ amax) {
+  __shared__ uint32_t red[kThreads / 64];
+  const int64_t m = blockIdx.x / P, c = blockIdx.x % P;
+  const uint4 *xm = x + m * vec_per_mat;
+  const int64_t b = c * kAmaxVec, e = b + kAmaxVec < vec_per_mat ? b + kAmaxVec : vec_per_mat;
+  uint32_t mx = 0u;
+  for (int64_t j = b + threadIdx.x; j < e; j += kThreads) {
+    const uint4 v = xm[j];
+    uint32_t a0 = absmax_bits_u32(v.x), a1 = absmax_bits_u32(v.y);
+    uint32_t a2 = absmax_bits_u32(v.z), a3 = absmax_bits_u32(v.w);
+    a0 = a0 > a1 ? a0 : a1;
+    a2 = a2 > a3 ? a2 : a3;
+    a0 = a0 > a2 ? a0 : a2;
+    mx = mx > a0 ? mx : a0;
+  }
+  mx = block_max_u(mx, red);
+  if (threadIdx.x == 0) atomicMax(&amax[m], mx);
+}
+
+// grid = n_mat * G workgroups; s_dec from amax (bf16 magnitude bits) or s_dec_in
 template <bool kFos>
 __global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
-    const uint4 *__restrict__ x, int64_t blocks_per_mat, const uint32_t *__restrict__ partials, int P,
-    const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes,
-    uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
-  __shared__ uint32_t red[kThreads / 64];
-  const int64_t m = blockIdx.y;
+    const uint4 *__restrict__ x, int64_t blocks_per_mat, int64_t G, const uint32_t *__restrict__ amax,
+    const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes, uint8_t *__restrict__ scales,
+    float *__restrict__ s_dec_out) {
+  __shared__ float rcp[128];
+  fill_rcp(rcp);
+  const int64_t m = blockIdx.x / G, c = blockIdx.x % G;
   float s_dec, s_enc;
   if (s_dec_in) {
     s_dec = s_dec_in[m];
     s_enc = 1.0f / s_dec;
   } else {
-    uint32_t a = 0u;
-    for (int i = threadIdx.x; i < P; i += kThreads) {
-      uint32_t v = partials[m * P + i];
-      a = a > v ? a : v;
-    }
-    a = block_max_u(a, red);
-    global_scale(__uint_as_float(a << 16), denom, s_dec, s_enc);
+    global_scale(__uint_as_float(amax[m] << 16), denom, s_dec, s_enc);
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) s_dec_out[m] = s_dec;
+  if (c == 0 && threadIdx.x == 0) s_dec_out[m] = s_dec;
   const uint4 *xm = x + m * blocks_per_mat * 2;
   uint2 *cm = codes + m * blocks_per_mat;
   uint8_t *sm = scales + m * blocks_per_mat;
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < blocks_per_mat;
-       blk += (int64_t)gridDim.x * kThreads) {
+  const int64_t b = c * kQuantBlocks, e = b + kQuantBlocks < blocks_per_mat ? b + kQuantBlocks : blocks_per_mat;
+  for (int64_t blk = b + threadIdx.x; blk < e; blk += kThreads) {
     uint32_t w[8];
     load_block16(xm + 2 * blk, w);
     uint32_t lo, hi;
-    uint32_t sb = quant_block16<kFos>(w, s_enc, lo, hi);
+    const uint32_t sb = quant_block16<kFos>(w, s_enc, rcp, lo, hi);
     cm[blk] = make_uint2(lo, hi);
     sm[blk] = (uint8_t)sb;
   }
@@ -237,6 +242,8 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
     const uint4 *__restrict__ x, int64_t rows_total, int64_t blocks_per_row,
     const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes,
     uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
+  __shared__ float rcp[128];
+  fill_rcp(rcp);
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= rows_total) return;
@@ -264,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
     uint32_t w[8];
     load_block16(xr + 2 * blk, w);
     uint32_t lo, hi;
-    uint32_t sb = quant_block16<kFos>(w, s_enc, lo, hi);
+    uint32_t sb = quant_block16<kFos>(w, s_enc, rcp, lo, hi);
     codes[row * blocks_per_row + blk] = make_uint2(lo, hi);
     scales[row * blocks_per_row + blk] = (uint8_t)sb;
   }
@@ -403,15 +410,6 @@ bqm_status check_qtensor(const bqm_qtensor *q, const char *who, bool need_sdec) 
   return BQM_OK;
 }
 
-int64_t amax_partials_per_mat(int64_t elems) {
-  int64_t p = cdiv(elems, 65536);
-  if (p < 1) p = 1;
-  return p < kMaxPartials ? p : kMaxPartials;
-}
-
-// Matrices per amax+quantize group: the group's bf16 bytes stay below this so
-// the second read of the group is served by the Infinity Cache.
-constexpr int64_t kGroupBytes = 192ll << 20;
 
 }  // namespace
 }  // namespace bqm
@@ -420,8 +418,10 @@ using namespace bqm;
 
 extern "C" size_t bqm_quantize_nvfp4_workspace_size(int64_t n_mat, int64_t rows, int64_t cols,
                                                     int32_t scale_mode) {
+  (void)rows;
+  (void)cols;
   if (scale_mode == BQM_SCALE_PER_ROW || n_mat <= 0) return 0;
-  return (size_t)n_mat * (size_t)amax_partials_per_mat(rows * cols) * sizeof(uint32_t);
+  return (size_t)n_mat * sizeof(uint32_t);
 }
 
 extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six,
@@ -456,43 +456,30 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
                                                         out->s_dec);
     return launch_status("nvfp4_quant_rows");
   }
-  const int P = (int)amax_partials_per_mat(per_mat);
-  const size_t need = s_dec_in ? 0 : bqm_quantize_nvfp4_workspace_size(n_mat, rows, cols, 0);
-  BQM_REQUIRE(ws_bytes >= need && (need == 0 || ws), BQM_ERR_WORKSPACE,
-              "bqm_quantize_nvfp4: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-  BQM_REQUIRE(!ws || aligned16(ws), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: ws not 16-byte aligned");
-  uint32_t *partials = reinterpret_cast<uint32_t *>(ws);
   const int64_t blocks_per_mat = per_mat / 16;
-  int64_t group = kGroupBytes / (per_mat * 2);
-  if (group < 1) group = 1;
-  if (group > 65535) group = 65535;
-  // enough workgroups per matrix to fill the chip with the whole group in flight
-  int64_t g = cdiv(2048, group);
-  int64_t gmax = cdiv(blocks_per_mat, kThreads);
-  if (g > gmax) g = gmax;
-  if (g < 1) g = 1;
-  for (int64_t m0 = 0; m0 < n_mat; m0 += group) {
-    int64_t nm = n_mat - m0 < group ? n_mat - m0 : group;
-    const uint4 *xg = xv + m0 * (per_mat / 8);
-    uint32_t *pg = partials ? partials + m0 * P : nullptr;
-    if (!s_dec_in) {
-      nvfp4_amax_partials<<<dim3(P, (unsigned)nm), kThreads, 0, s>>>(xg, per_mat / 8, P, pg);
-      st = launch_status("nvfp4_amax_partials");
-      if (st != BQM_OK) return st;
-    }
-    const float *sdi = s_dec_in ? s_dec_in + m0 : nullptr;
-    if (four_over_six)
-      nvfp4_quant_tensor<true><<<dim3((unsigned)g, (unsigned)nm), kThreads, 0, s>>>(
-          xg, blocks_per_mat, pg, P, sdi, denom, cv + m0 * blocks_per_mat, sv + m0 * blocks_per_mat,
-          out->s_dec + m0);
-    else
-      nvfp4_quant_tensor<false><<<dim3((unsigned)g, (unsigned)nm), kThreads, 0, s>>>(
-          xg, blocks_per_mat, pg, P, sdi, denom, cv + m0 * blocks_per_mat, sv + m0 * blocks_per_mat,
-          out->s_dec + m0);
-    st = launch_status("nvfp4_quant_tensor");
+  const int64_t P = cdiv(per_mat / 8, kAmaxVec), G = cdiv(blocks_per_mat, kQuantBlocks);
+  BQM_REQUIRE(n_mat * std::max(P, G) < ((int64_t)1 << 31), BQM_ERR_SHAPE, "bqm_quantize_nvfp4: tensor too large");
+  uint32_t *amax = nullptr;
+  if (!s_dec_in) {
+    const size_t need = bqm_quantize_nvfp4_workspace_size(n_mat, rows, cols, 0);
+    BQM_REQUIRE(ws && ws_bytes >= need, BQM_ERR_WORKSPACE,
+                "bqm_quantize_nvfp4: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    BQM_REQUIRE(aligned16(ws), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: ws not 16-byte aligned");
+    amax = reinterpret_cast<uint32_t *>(ws);
+    clear_u32<<<(int)std::min<int64_t>(cdiv(n_mat, kThreads), 1024), kThreads, 0, s>>>(amax, n_mat);
+    st = launch_status("clear_u32");
+    if (st != BQM_OK) return st;
+    nvfp4_amax<<<(int)(n_mat * P), kThreads, 0, s>>>(xv, per_mat / 8, P, amax);
+    st = launch_status("nvfp4_amax");
     if (st != BQM_OK) return st;
   }
-  return BQM_OK;
+  if (four_over_six)
+    nvfp4_quant_tensor<true><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom, cv,
+                                                                   sv, out->s_dec);
+  else
+    nvfp4_quant_tensor<false><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom, cv,
+                                                                    sv, out->s_dec);
+  return launch_status("nvfp4_quant_tensor");
 }
 
 extern "C" bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out, void *stream) {

@@ -96,8 +96,10 @@ const char *bqm_last_error(void);
  * M = 448 otherwise.  s_dec_in (nullable, same shape as out->s_dec) replaces
  * the amax-derived scale.  All rounding is round-to-nearest-even, E4M3 and E2M1
  * saturate.  Result codes and scales are deterministic bit patterns.
- * ws: per-tensor mode needs bqm_quantize_nvfp4_workspace_size() bytes of
- * scratch (amax partials); per-row mode needs none (ws may be NULL). */
+ * ws: per-tensor mode without s_dec_in needs bqm_quantize_nvfp4_workspace_size()
+ * bytes of device scratch (the running amax of each matrix; the call clears it
+ * on its stream, so calls sharing one ws must not overlap); per-row mode and
+ * s_dec_in need none (ws may be NULL). */
 size_t bqm_quantize_nvfp4_workspace_size(int64_t n_mat, int64_t rows, int64_t cols,
                                          int32_t scale_mode);
 bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six, const float *s_dec_in,

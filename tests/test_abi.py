@@ -65,8 +65,9 @@ def test_quantize_rejects_bad_shapes_and_pointers(lib):
 
 def test_workspace_sizes(lib):
     assert lib.bqm_quantize_nvfp4_workspace_size(4, 64, 256, 1) == 0
+    # the running amax of each matrix
     assert lib.bqm_quantize_nvfp4_workspace_size(4, 64, 256, 0) == 4 * 4
-    assert lib.bqm_quantize_nvfp4_workspace_size(2, 4096, 6144, 0) == 2 * 384 * 4
+    assert lib.bqm_quantize_nvfp4_workspace_size(2, 4096, 6144, 0) == 2 * 4
     assert lib.bqm_permute_workspace_size(16384, 256, 8) == 64 * 256 * 4
 
 
