@@ -26,6 +26,23 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def measured_traffic(stage):
+    """HBM bytes per launch of a GEMM stage from the committed FETCH_SIZE/WRITE_SIZE
+    summary, if moe.hip is still the source those counters were taken from."""
+    import hashlib
+    import re
+    try:
+        txt = open(os.path.join(ROOT, "profiles", "moe_gemm_hbm_traffic_glm.md")).read()
+        blob = json.loads(re.search(r"```json\n(.*?)\n```", txt, re.S).group(1))
+        src = open(os.path.join(ROOT, blob["source"]), "rb").read()
+    except (OSError, AttributeError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != blob["source_sha256"]:
+        return None
+    st = blob["stages"].get(stage)
+    return None if st is None else st["hbm_bytes"]
+
+
 class HipEvents:
     """hipEvent_t handles from the HIP runtime torch uses (one runtime per process)."""
 
@@ -226,7 +243,7 @@ def main():
                    "T": s.T, "r": s.r, "weights": "nvfp4-4over6-rowwise", "step": "route+fwd+dgrad+lora_grad",
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
                      "algorithmic_flop_per_launch": sf[dom], "launch_ms": gemms[dom]},
         "layer_tflops": (fl + fl_lora) / (ms * 1e-3) / 1e12,
         "fwd_dgrad_tokens_per_s": s.T / (sum(v for k, v in stages.items() if k != "lora_grad") * 1e-3),
