@@ -32,6 +32,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int BM = 256;       // output rows per tile (routed rows of one expert)
 constexpr int BK = 64;        // K step (one NF4 block, four NVFP4 blocks)
@@ -472,6 +473,78 @@ __device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// epilogues: acc[tm][tn] element v of a wave holds row row0 + tm*32 + 8(v/4) +
+// 4(lane/32) + v%4 and column col0 + tn*32 + lane%32 of the tile
+// ---------------------------------------------------------------------------
+template <int TM, int TN, int BN, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc)[TM][TN], int e, int nt, int m0,
+                                         int n_e, int rb, int row0, int col0, int lane, float esc) {
+  const float osc = p.div_e ? p.out_scale / p.div_e[e] : p.out_scale;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (pos >= n_e) continue;
+      const int64_t grow = rb + pos;
+      if constexpr (EPI == EPI_GATEUP) {
+        // in each 64-column group of the tile: 32 gate columns, then the matching up columns
+#pragma unroll
+        for (int q = 0; q < TN / 2; ++q) {
+          const int i = nt * (BN / 2) + col0 / 2 + q * 32 + (lane & 31);
+          if (i >= p.I) continue;
+          const float g = acc[tm][2 * q][v] * esc, u = acc[tm][2 * q + 1][v] * esc;
+          const float a = g * sigmoid_f(g) * u;
+          p.outf[grow * 2 * p.I + i] = g;
+          p.outf[grow * 2 * p.I + p.I + i] = u;
+          p.out1[grow * p.I + i] = (uint16_t)f32_to_bf16(a);
+        }
+      } else if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = nt * BN + col0 + tn * 32 + (lane & 31);
+          if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * esc * p.out_scale);
+        }
+      } else if constexpr (EPI == EPI_STORE_SPLIT) {
+        // FP32 value kept as an unevaluated pair of bf16 (hi in columns [0, N), lo in [N, 2N))
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = nt * BN + col0 + tn * 32 + (lane & 31);
+          if (n < p.N) {
+            const float val = acc[tm][tn][v] * osc;
+            const uint32_t hb = f32_to_bf16(val);
+            const float lo2 = val - __uint_as_float(hb << 16);
+            p.out0[grow * 2 * p.N + n] = (uint16_t)hb;
+            p.out0[grow * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
+          }
+        }
+      } else if constexpr (EPI == EPI_STORE_F32) {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int n = nt * BN + col0 + tn * 32 + (lane & 31);
+          if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * esc * p.out_scale;
+        }
+      } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
+        const float w = p.tw[p.perm[grow]];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int i = nt * BN + col0 + tn * 32 + (lane & 31);
+          if (i >= p.N) continue;
+          const float g = p.h_in[grow * 2 * p.I + i];
+          const float u = p.h_in[grow * 2 * p.I + p.I + i];
+          const float sg = sigmoid_f(g);
+          const float da = w * (acc[tm][tn][v] * esc);
+          const float dg = da * u * sg * (1.0f + g * (1.0f - sg));
+          const float du = da * g * sg;
+          p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(dg);
+          p.out0[grow * 2 * p.I + p.I + i] = (uint16_t)f32_to_bf16(du);
+        }
+      }
+    }
+  }
+}
+
 template <class C, int ASRC, int BSRC, int B2SRC, int EPI>
 __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
   constexpr int TM = C::TM, TN = C::TN, WN = C::WN, BN = C::BN, BMc = C::BM;
@@ -571,69 +644,410 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 
   // epilogue
   if (!active) return;
-  const float osc = p.div_e ? p.out_scale / p.div_e[e] : p.out_scale;
+  epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, wm * TM * 32, wn * TN * 32, lane, esc);
+}
+
+// x *= s on an accumulator element that stays in its AGPR (VALU arithmetic cannot
+// read AGPRs; going through the compiler moves the whole accumulator into VGPRs)
+__device__ __forceinline__ void scale_acc(float &x, float s) {
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "v_mul_f32 %1, %2, %1\n\t"
+      "v_accvgpr_write_b32 %0, %1"
+      : "+a"(x), "=&v"(t)
+      : "v"(s));
+}
+
+// valid 32-row tiles of a wave: all, or a run-time count (ragged tail)
+constexpr int VT_ALL = 1000, VT_DYN = -1;
+
+// ---------------------------------------------------------------------------
+// Forward grouped GEMM over K-major NVFP4 weights (gate_up and down forward)
+// ---------------------------------------------------------------------------
+// The 4-bit codes and E4M3 scales of the weight tile go global -> LDS with the
+// direct-to-LDS load (8 KB + 1 KB per 64-deep K step, instead of 32 KB of
+// dequantized bf16 written by the waves), and every wave decodes its own MFMA
+// B fragments in registers right before use.  The four waves each own a
+// 256 x 64 slab of the 256 x 256 tile, so no two waves decode the same columns.
+// bf16 A rows are copied global -> LDS the same way, into 128-byte rows whose
+// 16-byte chunk c sits at position c ^ ((row >> 1) & 7), so the 16 lanes of a
+// fragment read hit 16 different bank groups.
+// Inside a K step, lane group g of a fragment covers k = 32g + 8kk .. +8 in
+// slice kk (one fixed permutation of k for A and B alike), so a lane's four
+// slices of one weight column are 16 contiguous code bytes and two scale bytes.
+namespace fq {
+constexpr int BM = 256, BN = 256, NTHR = 256, TM = 8, TN = 2, ACH = 8;
+
+constexpr int NST = 3;  // LDS stages: copies run two K steps ahead
+
+struct Smem {
+  uint16_t a[NST][BM * BK];  // bf16, swizzled 128-byte rows
+  uint8_t b[NST][BN * 32];   // codes, 32 bytes per output column
+  uint32_t s[NST][BN];       // the column's 4 E4M3 block scales of the K step
+};
+
+// Workgroup barrier that orders LDS (waits for this wave's LDS operations, then
+// s_barrier) without waiting for outstanding global loads: __syncthreads() also
+// drains vmcnt, which would wait for the copies issued for later steps.  The
+// "memory" clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt with vmcnt(n) and no wait on the other counters
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ int a_off(int r, int c) { return r * BK + 8 * (c ^ ((r >> 1) & 7)); }
+
+// row of the tile owned by this thread's j-th A chunk
+__device__ __forceinline__ int a_row(int j) { return 64 * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// bf16 A rows of K step k0 -> stage As (direct-to-LDS; no registers)
+__device__ __forceinline__ void a_dma(const Seg &s, const int64_t (&arow)[ACH], int k0, uint16_t *As) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+  for (int j = 0; j < ACH; ++j) {
+    const int r = 64 * w + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);  // the chunk that lands at this lane's position
+    __builtin_amdgcn_global_load_lds(a + arow[j] * s.a_ld + k0 + 8 * c, (lds_void *)(As + (64 * w + 8 * j) * BK), 16,
+                                     0, 0);
+  }
+}
+
+// NVFP4 weight tile of K step k0: 256 columns x 32 code bytes and 4 scale bytes
+template <int EPI>
+__device__ __forceinline__ void b_dma(const Seg &s, int e, int nt, int N, int I, int k0, uint8_t *Bs, uint32_t *Ss) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t slice = s.b_rows * s.b_cols;
+  const uint8_t *codes = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + k0 / 2;
+  const uint8_t *scales = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) + k0 / 16;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (pos >= n_e) continue;
-      const int64_t grow = rb + pos;
-      if constexpr (EPI == EPI_GATEUP) {
+  for (int j = 0; j < 2; ++j) {
+    const int ins = 2 * w + j;  // 32 columns x 32 bytes per instruction
+    const int col = ins * 32 + (lane >> 1);
+    int64_t wr = b_row_of_col<EPI, BN>(col, nt, N, I);
+    wr = wr < 0 ? 0 : wr;
+    __builtin_amdgcn_global_load_lds(codes + wr * (s.b_cols / 2) + 16 * (lane & 1), (lds_void *)(Bs + ins * 1024), 16,
+                                     0, 0);
+  }
+  const int col = 64 * w + lane;
+  int64_t wr = b_row_of_col<EPI, BN>(col, nt, N, I);
+  wr = wr < 0 ? 0 : wr;
+  __builtin_amdgcn_global_load_lds(scales + wr * (s.b_cols / 16), (lds_void *)(Ss + 64 * w), 4, 0, 0);
+}
+
+// A through registers: the LoRA segment (k >= K zeroed) and NVFP4 activation rows
+struct ARegs {
+  u32x4 v[ACH];
+};
+
+template <int ASRC, bool MASKK>
+__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[ACH], int k0, ARegs &r) {
+  const int tid = threadIdx.x;
+  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
+    const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
 #pragma unroll
-        for (int q = 0; q < TN / 2; ++q) {
-          const int i = nt * (BN / 2) + wn * 64 + q * 32 + (lane & 31);
-          if (i >= p.I) continue;
-          const float g = acc[tm][2 * q][v] * esc, u = acc[tm][2 * q + 1][v] * esc;
-          const float a = g * sigmoid_f(g) * u;
-          p.outf[grow * 2 * p.I + i] = g;
-          p.outf[grow * 2 * p.I + p.I + i] = u;
-          p.out1[grow * p.I + i] = (uint16_t)f32_to_bf16(a);
-        }
-      } else if constexpr (EPI == EPI_STORE) {
+    for (int i = 0; i < ACH; ++i) {
+      const int kk = k0 + (tid & 7) * 8;
+      const bool ok = !MASKK || kk < s.K;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(a + arow[i] * s.a_ld + (ok ? kk : 0));
+      r.v[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    // NVFP4 rows: items (row = item / 2, 32-element half item % 2), 2 per thread
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * esc * p.out_scale);
-        }
-      } else if constexpr (EPI == EPI_STORE_SPLIT) {
-        // FP32 value kept as an unevaluated pair of bf16 (hi in columns [0, N), lo in [N, 2N))
+    for (int it = 0; it < 2; ++it) {
+      const int half = (tid + NTHR * it) & 1;
+      const int kq = k0 + half * 32;
+      const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.a) + arow[it] * (s.a_ld / 2) + kq / 2;
+      r.v[2 * it] = *reinterpret_cast<const u32x4 *>(cp);
+      r.v[2 * it + 1].x = *reinterpret_cast<const uint16_t *>(s.a_sc + arow[it] * (s.a_ld / 16) + kq / 16);
+    }
+  }
+}
+
+template <int ASRC>
+__device__ __forceinline__ void a_store(uint16_t *As, const ARegs &r) {
+  const int tid = threadIdx.x;
+  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (n < p.N) {
-            const float val = acc[tm][tn][v] * osc;
-            const uint32_t hb = f32_to_bf16(val);
-            const float lo2 = val - __uint_as_float(hb << 16);
-            p.out0[grow * 2 * p.N + n] = (uint16_t)hb;
-            p.out0[grow * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
-          }
-        }
-      } else if constexpr (EPI == EPI_STORE_F32) {
+    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4 *>(As + a_off(a_row(i), tid & 7)) = r.v[i];
+  } else {
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int n = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * esc * p.out_scale;
-        }
-      } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
-        const float w = p.tw[p.perm[grow]];
+    for (int it = 0; it < 2; ++it) {
+      const int item = tid + NTHR * it;
+      const int row = item >> 1, half = item & 1;
+      const uint32_t cw[4] = {r.v[2 * it].x, r.v[2 * it].y, r.v[2 * it].z, r.v[2 * it].w};
+      const float s0 = e4m3_hw<0>(r.v[2 * it + 1].x), s1 = e4m3_hw<1>(r.v[2 * it + 1].x);
 #pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int i = nt * BN + wn * TN * 32 + tn * 32 + (lane & 31);
-          if (i >= p.N) continue;
-          const float g = p.h_in[grow * 2 * p.I + i];
-          const float u = p.h_in[grow * 2 * p.I + p.I + i];
-          const float sg = sigmoid_f(g);
-          const float da = w * (acc[tm][tn][v] * esc);
-          const float dg = da * u * sg * (1.0f + g * (1.0f - sg));
-          const float du = da * g * sg;
-          p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(dg);
-          p.out0[grow * 2 * p.I + p.I + i] = (uint16_t)f32_to_bf16(du);
-        }
+      for (int q = 0; q < 4; ++q) {
+        uint32_t o[4];
+        fp4x8_hw(cw[q], q < 2 ? s0 : s1, o);
+        *reinterpret_cast<uint4 *>(As + a_off(row, half * 4 + q)) = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
   }
 }
+
+// A fragments of slice kk for row tiles 0..TM-1
+__device__ __forceinline__ void a_frags(const uint16_t *As, int kk, int lane, bf16x8 (&af)[TM]) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+    af[tm] = *reinterpret_cast<const bf16x8 *>(As + a_off(tm * 32 + (lane & 31), 4 * (lane >> 5) + kk));
+}
+
+// this lane's codes (4 slices) and the two block scales of its weight columns
+struct BCodes {
+  u32x4 c[TN];
+  float s[TN][2];
+};
+
+__device__ __forceinline__ void b_codes(const uint8_t *Bs, const uint32_t *Ss, int wn, int lane, BCodes &b) {
+  const int g = lane >> 5;
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int col = wn * 64 + tn * 32 + (lane & 31);
+    b.c[tn] = *reinterpret_cast<const u32x4 *>(Bs + col * 32 + 16 * g);
+    const uint32_t sw = Ss[col] >> (16 * g);  // blocks 2g, 2g+1
+    b.s[tn][0] = e4m3_hw<0>(sw);
+    b.s[tn][1] = e4m3_hw<1>(sw);
+  }
+}
+
+__device__ __forceinline__ void b_decode(const BCodes &b, int kk, bf16x8 (&bf)[TN]) {
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    uint32_t o[4];
+    fp4x8_hw(b.c[tn][kk], b.s[tn][kk >> 1], o);
+    const u32x4 v = {o[0], o[1], o[2], o[3]};
+    bf[tn] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <int VT>
+__device__ __forceinline__ void mfmas(const bf16x8 (&af)[TM], const bf16x8 (&bf)[TN], int vt,
+                                      f32x16 (&acc)[TM][TN]) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    if (VT != VT_DYN || tm < vt) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+    }
+  }
+}
+
+// Segment 1: A (bf16 rows by DMA, or NVFP4 rows through registers) x NVFP4 weights.
+// Step ks multiplies stage ks % 3.  At its start the copies of K step ks+2 go to
+// a third stage (and NVFP4 A rows of step ks+1 to registers, written out before
+// the closing barrier), so a copy has two steps to land; the reads and decode
+// of slice kk+1 run before the MFMAs of slice kk; the last slice's MFMAs run
+// after the closing barrier, behind the reads of the next step's first slice.
+template <int ASRC, int EPI, int VT>
+__device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
+                                       Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
+  constexpr bool DIRECT = ASRC == A_GATHER || ASRC == A_ROWS;
+  constexpr int NDMA = (DIRECT ? ACH : 0) + 3;  // copy instructions per step and wave
+  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+  const int nk = s.K / BK;
+  ARegs ar;
+  // prologue: stage 0 <- step 0, stage 1 <- step 1 (copies), wait for stage 0
+  if constexpr (DIRECT) {
+    a_dma(s, arow, 0, sm.a[0]);
+  } else {
+    a_load<ASRC, false>(s, arow, 0, ar);
+    a_store<ASRC>(sm.a[0], ar);
+  }
+  b_dma<EPI>(s, e, nt, N, I, 0, sm.b[0], sm.s[0]);
+  if (nk > 1) {
+    if constexpr (DIRECT) {
+      a_dma(s, arow, BK, sm.a[1]);
+    } else {
+      a_load<ASRC, false>(s, arow, BK, ar);
+      a_store<ASRC>(sm.a[1], ar);
+    }
+    b_dma<EPI>(s, e, nt, N, I, BK, sm.b[1], sm.s[1]);
+    wait_vm<NDMA>();
+  } else {
+    wait_vm<0>();
+  }
+  __syncthreads();
+  bf16x8 af[2][TM], bf[2][TN];
+  BCodes bc;
+  a_frags(sm.a[0], 0, lane, af[0]);
+  b_codes(sm.b[0], sm.s[0], wn, lane, bc);
+  b_decode(bc, 0, bf[0]);
+  int cur = 0;
+  for (int ks = 0; ks < nk; ++ks) {
+    const int nxt = cur == NST - 1 ? 0 : cur + 1;
+    const int nn = nxt == NST - 1 ? 0 : nxt + 1;
+    const bool more = ks + 1 < nk, more2 = ks + 2 < nk;
+    if constexpr (!DIRECT)
+      if (more2) a_load<ASRC, false>(s, arow, (ks + 2) * BK, ar);
+    if (more2) {
+      if constexpr (DIRECT) a_dma(s, arow, (ks + 2) * BK, sm.a[nn]);
+      b_dma<EPI>(s, e, nt, N, I, (ks + 2) * BK, sm.b[nn], sm.s[nn]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int nb = (kk + 1) & 1;
+      if (kk + 1 < BK / 16) {
+        if (VT != VT_DYN || vt > 0) a_frags(sm.a[cur], kk + 1, lane, af[nb]);
+        b_decode(bc, kk + 1, bf[nb]);
+      } else {
+        if (more2)
+          wait_vm<NDMA>();  // step ks+1's copies have landed; step ks+2's may fly on
+        else
+          wait_vm<0>();
+        if constexpr (!DIRECT)
+          if (more2) a_store<ASRC>(sm.a[nn], ar);  // stage nn was last read two steps ago
+        barrier_lds();
+        if (more) {
+          a_frags(sm.a[nxt], 0, lane, af[nb]);
+          b_codes(sm.b[nxt], sm.s[nxt], wn, lane, bc);
+          b_decode(bc, 0, bf[nb]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas<VT>(af[kk & 1], bf[kk & 1], vt, acc);
+    }
+    cur = nxt;
+  }
+  __syncthreads();  // the stages are reused by the next segment
+}
+
+// Segment 2 (LoRA up-projection): A = hi/lo pair rows through registers (k >= K
+// zeroed), B = the bf16 LoRA matrix [N rows][kmod], fragments loaded straight
+// from global memory (it is small and stays in L2).
+template <int EPI>
+__device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
+                                         Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
+  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6, g = lane >> 5;
+  const int nk = (s.K + BK - 1) / BK;
+  const int64_t slice = s.b_rows * s.b_cols;
+  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * slice;
+  int64_t wr[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    int64_t w = b_row_of_col<EPI, BN>(wn * 64 + tn * 32 + (lane & 31), nt, N, I);
+    wr[tn] = w < 0 ? 0 : w;
+  }
+  for (int ks = 0; ks < nk; ++ks) {
+    ARegs ar;
+    a_load<A_ROWS, true>(s, arow, ks * BK, ar);
+    a_store<A_ROWS>(sm.a[0], ar);
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 bl[TN], af[TM];
+      const int kb = (ks * BK + 32 * g + 8 * kk) % s.kmod;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) bl[tn] = *reinterpret_cast<const bf16x8 *>(bsrc + wr[tn] * s.b_cols + kb);
+      a_frags(sm.a[0], kk, lane, af);
+      mfmas<VT_DYN>(af, bl, vt, acc);
+    }
+    __syncthreads();
+  }
+}
+
+template <int ASRC, int EPI>
+__global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
+  const int total = p.tile_off[p.E] * p.NT;
+  const int per = (total + 7) / 8;
+  const int li = blockIdx.x >> 3;
+  if (li >= per) return;
+  const int L = (blockIdx.x & 7) * per + li;
+  if (L >= total) return;
+  const int mt = L / p.NT, nt = L % p.NT;
+  int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= mt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int rb = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - rb;
+  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
+  const int rows_left = n_e - m0;
+  const int vt = rows_left >= TM * 32 ? TM : (rows_left + 31) / 32;  // >= 1: a tile has rows
+
+  constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
+  int64_t arow[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int row = kQA ? ((tid + NTHR * i) >> 1) : a_row(i);
+    const int pos = min(m0 + row, n_e - 1);  // rows past the segment: clamped (results dropped)
+    if (ASRC == A_GATHER || ASRC == A_GATHER_Q)
+      arow[i] = p.perm[rb + pos] / p.k;
+    else
+      arow[i] = rb + pos;
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+
+  if (vt == TM)
+    seg_q4<ASRC, EPI, VT_ALL>(p.s1, e, nt, p.N, p.I, arow, sm, vt, acc);
+  else
+    seg_q4<ASRC, EPI, VT_DYN>(p.s1, e, nt, p.N, p.I, arow, sm, vt, acc);
+
+  // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
+  // per row (NVFP4 activations) before the LoRA segment
+  float esc = 1.0f;
+  if constexpr (!kQA) esc = p.s1.b_sd[e];
+  if constexpr (kQA) {
+    const float sb = p.s1.b_sd[e];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      float sc[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sc[v] = sb;
+        const int pos = m0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (pos < n_e) {
+          const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+          sc[v] = sb * p.s1.a_sd[src];
+        }
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = acc[tm][tn][v];
+          scale_acc(x, sc[v]);
+          acc[tm][tn][v] = x;
+        }
+    }
+  }
+
+  if (p.s2.K > 0) {
+    int64_t arow2[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row(i), n_e - 1);
+    seg_lora<EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
+  }
+
+  epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc);
+}
+}  // namespace fq
 
 // ---------------------------------------------------------------------------
 // LoRA weight gradients: C[e] [M, N] = sum over the expert's rows of P[row][m] * Q[row][n]
@@ -931,6 +1345,15 @@ bool lora_folds_s_dec(const bqm_moe_desc *d, bool forward) {
   return d->w_gu.fmt == BQM_FMT_NVFP4 && !(forward && d->act_quant);
 }
 
+// forward GEMM over NVFP4 weights: codes staged in LDS, decoded in registers
+template <int ASRC, int EPI>
+bqm_status launch_fq(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+  static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
+  const int grid = gemm_grid(R, p.E, p.NT);
+  fq::gemm_fwd_q4<ASRC, EPI><<<grid, fq::NTHR, 0, s>>>(p);
+  return launch_status(what);
+}
+
 GemmParams base_params(const bqm_moe_desc *d, const Ws &w) {
   GemmParams p{};
   p.perm = w.at<int32_t>(w.L.perm);
@@ -1012,7 +1435,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     if (nf4)
       BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, ASRC_X, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
     else
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, ASRC_X, B_Q4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd")));
   }
   const bool aq = ASRC_X == A_GATHER_Q;
   if (aq)
@@ -1044,9 +1467,9 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     if (nf4)
       BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
     else if (aq)
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS_Q, B_Q4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE_F32>(p, R, s, "down fwd")));
     else
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_Q4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE_F32>(p, R, s, "down fwd")));
   }
   return BQM_OK;
 }
