@@ -395,6 +395,21 @@ __device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rc
 // the grouped GEMM
 // ---------------------------------------------------------------------------
 // B fragment (8 consecutive k of one column per lane) from a natural [k][n] tile
+// Fragment (8 consecutive rows k of one column per lane) from a natural
+// [k][col] tile with row stride STRIDE bf16, via the transposing LDS read.
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 b_frag_trans_s(const uint16_t *Bs, int kbase, int nbase, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = kbase + 8 * (g >> 1) + (s >> 2);
+  const int col = nbase + 16 * (g & 1) + 4 * (s & 3);
+  const uint16_t *p0 = Bs + row * STRIDE + col;
+  const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0));
+  const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 4 * STRIDE));
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int BN>
 __device__ __forceinline__ bf16x8 b_frag_trans(const uint16_t *Bs, int kbase, int nbase, int lane) {
   const int g = lane >> 4, s = lane & 15;
@@ -1069,9 +1084,55 @@ struct WgradParams {
 
 constexpr int WB = 64;  // wgrad tile (M and N) and row step
 
+// One 64x64 tile of C[e] per workgroup; rows of the expert's segment in steps
+// of 64.  All 256 threads load: each owns 2 16-byte chunks of the P rows and 2
+// of the Q rows of a step (rows row = c / 8, 8 columns at 8 * (c % 8)), held in
+// registers one step ahead; tiles stay in their natural [row][col] layout in
+// one LDS stage (18 KB, so eight workgroups share a CU and keep many loads in
+// flight) and the MFMA fragments (8 consecutive rows of one column) come from
+// the gfx950 transposing LDS read.
+constexpr int WS = WB + 8;  // LDS row stride in bf16 (64 columns + 16-byte pad)
+
+__device__ __forceinline__ void wgrad_load(const WgradParams &p, int rb, int n_e, int r0, int m0, int n0,
+                                           uint4 (&v)[4]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool isq = i >= 2;
+    const int c = tid + NTHR * (i & 1);  // 0..511: row c / 8, columns 8 * (c % 8)
+    const int pos = r0 + (c >> 3);
+    const int col = (isq ? n0 : m0) + 8 * (c & 7);
+    const int lim = isq ? p.N : p.M;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (pos < n_e && col < lim) {
+      const int64_t grow = rb + pos;
+      const int gather = isq ? p.q_gather : p.p_gather;
+      const int64_t srow = gather ? (int64_t)(p.perm[grow] / p.k) : grow;
+      x = *reinterpret_cast<const uint4 *>((isq ? p.Q : p.P) + srow * (isq ? p.q_ld : p.p_ld) + col);
+      if (!isq && p.scale_p) {
+        const float s = p.tw[p.perm[grow]];
+        uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) w[h] = f32_to_bf16(bf16_lo(w[h]) * s) | (f32_to_bf16(bf16_hi(w[h]) * s) << 16);
+        x = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+    v[i] = x;
+  }
+}
+
+__device__ __forceinline__ void wgrad_store(uint16_t *Ps, uint16_t *Qs, const uint4 (&v)[4]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + NTHR * (i & 1);
+    *reinterpret_cast<uint4 *>((i >= 2 ? Qs : Ps) + (c >> 3) * WS + 8 * (c & 7)) = v[i];
+  }
+}
+
 __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[WB * SK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[WB * SK];
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[WB * WS];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[WB * WS];
   const int e = blockIdx.y;
   const int ntn = (p.N + WB - 1) / WB;
   const int mt = blockIdx.x / ntn, ntile = blockIdx.x % ntn;
@@ -1082,65 +1143,33 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
   f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  // loader role: threads 0..63 stage P^T, 64..127 stage Q^T; 8 rows x 8 columns each
-  const int role = tid >> 6, item = tid & 63;
-  const int cg = item & 7, rg = item >> 3;
-  for (int r0 = 0; r0 < n_e; r0 += WB) {
-    if (role < 2) {
-      const uint16_t *src = role == 0 ? p.P : p.Q;
-      const int64_t ld = role == 0 ? p.p_ld : p.q_ld;
-      const int gather = role == 0 ? p.p_gather : p.q_gather;
-      const int lim = role == 0 ? p.M : p.N;
-      const int c0 = (role == 0 ? m0 : n0) + cg * 8;
-      uint32_t w[32];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int pos = r0 + rg * 8 + q;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (pos < n_e && c0 < lim) {
-          const int64_t grow = rb + pos;
-          const int64_t srow = gather ? (int64_t)(p.perm[grow] / p.k) : grow;
-          v = *reinterpret_cast<const uint4 *>(src + srow * ld + c0);
-          if (role == 0 && p.scale_p) {
-            const float s = p.tw[p.perm[grow]];
-            uint32_t x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-              x[h] = f32_to_bf16(bf16_lo(x[h]) * s) | (f32_to_bf16(bf16_hi(x[h]) * s) << 16);
-            v = make_uint4(x[0], x[1], x[2], x[3]);
-          }
-        }
-        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-      }
-      uint16_t *dstb = role == 0 ? As : Bs;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint32_t o[4];
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          uint32_t w0 = w[4 * (2 * pp) + (c >> 1)], w1 = w[4 * (2 * pp + 1) + (c >> 1)];
-          uint32_t b0 = (c & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-          uint32_t b1 = (c & 1) ? (w1 >> 16) : (w1 & 0xFFFFu);
-          o[pp] = b0 | (b1 << 16);
-        }
-        *reinterpret_cast<uint4 *>(dstb + (cg * 8 + c) * SK + rg * 8) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    }
-    __syncthreads();
+  const int nk = (n_e + WB - 1) / WB;
+  uint4 v[4];
+  if (nk > 0) {
+    wgrad_load(p, rb, n_e, 0, m0, n0, v);
+    wgrad_store(Ps, Qs, v);
+  }
+  __syncthreads();
+  for (int ks = 0; ks < nk; ++ks) {
+    if (ks + 1 < nk) wgrad_load(p, rb, n_e, (ks + 1) * WB, m0, n0, v);
 #pragma unroll
     for (int kk = 0; kk < WB / 16; ++kk) {
-      bf16x8 a = *reinterpret_cast<const bf16x8 *>(As + (wm * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
-      bf16x8 b = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
+      const bf16x8 a = b_frag_trans_s<WS>(Ps, kk * 16, wm * 32, lane);
+      const bf16x8 b = b_frag_trans_s<WS>(Qs, kk * 16, wn * 32, lane);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
     }
-    __syncthreads();
+    __syncthreads();  // every wave is done reading the stage
+    if (ks + 1 < nk) {
+      wgrad_store(Ps, Qs, v);
+      __syncthreads();
+    }
   }
   const float cs = p.c_scale ? p.c_scale[e] : 1.0f;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int m = m0 + wm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+  for (int vv = 0; vv < 16; ++vv) {
+    const int m = m0 + wm * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
     const int n = n0 + wn * 32 + (lane & 31);
-    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[v] * cs;
+    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[vv] * cs;
   }
 }
 
