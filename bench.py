@@ -122,6 +122,53 @@ def cpu_baseline(inp, shape, experts=(0, 1, 2, 3)):
                       f"{dt:.1f} s"}
 
 
+def token_sweep(shape, wgu, wdn, ev, sh, tokens=(438, 1024, 2048, 4096, 8192), reps=5):
+    """Layer step (route + fwd + dgrad + LoRA grads) at smaller token counts over the
+    same quantized experts: where the per-step read of the hit experts' weights
+    (5.44 GB when every expert is hit) gives way to MFMA time."""
+    import dataclasses
+    import torch
+    import bit_quantized_moe_amd as bqm
+    import synth
+    dev = torch.device("cuda")
+    rows = []
+    for T in tokens:
+        s = dataclasses.replace(shape, T=T, name=f"{shape.name}_T{T}")
+        inp = synth.layer_inputs(s, device=dev, with_weights=False)
+        d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn,
+                        B_dn=inp.B_dn)
+        ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+        idx = torch.empty((T, s.k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, s.k), dtype=torch.float32, device=dev)
+        out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty_like(out)
+        dtw = torch.empty((T, s.k), dtype=torch.float32, device=dev)
+        g = [torch.empty(sz, dtype=torch.float32, device=dev) for sz in
+             ((s.E, s.r, s.H), (s.E, 2 * s.I, s.r), (s.E, s.r, s.I), (s.E, s.H, s.r))]
+
+        def run():
+            bqm.bqm_route(inp.logits, T, s.E, s.k, 0, idx, tw)
+            bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
+            bqm.bqm_moe_dgrad(d, inp.dout, ws, dx, dtw)
+            bqm.bqm_lora_grad(d, inp.x, inp.dout, ws, *g)
+
+        run()
+        torch.cuda.synchronize()
+        e = ev.create(2)
+        ev.record(e[0], sh)
+        for _ in range(reps):
+            run()
+        ev.record(e[1], sh)
+        torch.cuda.synchronize()
+        ms = ev.elapsed_ms(e[0], e[1]) / reps
+        hit = int(torch.unique(idx).numel())
+        rows.append({"T": T, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                     "experts_hit": hit})
+        del inp, d, ws, idx, tw, out, dx, dtw, g
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +176,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
@@ -250,6 +298,10 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "quantizer": quant,
     }
+    if not args.no_sweep:
+        del ws
+        torch.cuda.empty_cache()
+        result["token_sweep"] = token_sweep(shape, wgu, wdn, ev, sh)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, shape)
     print(json.dumps(result), flush=True)

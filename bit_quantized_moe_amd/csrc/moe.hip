@@ -692,7 +692,9 @@ constexpr int VT_ALL = 1000, VT_DYN = -1;
 // slice kk (one fixed permutation of k for A and B alike), so a lane's four
 // slices of one weight column are 16 contiguous code bytes and two scale bytes.
 namespace fq {
-constexpr int BM = 256, BN = 256, NTHR = 256, TM = 8, TN = 2, ACH = 8;
+constexpr int BM = 256, BN = 256, NTHR = 256, ACH = 8;
+constexpr int WMG = 1, WNG = 4;  // wave grid: WMG x WNG waves of TM x TN 32x32 tiles
+constexpr int TM = BM / WMG / 32, TN = BN / WNG / 32;
 
 constexpr int NST = 3;  // LDS stages: copies run two K steps ahead
 
@@ -811,10 +813,10 @@ __device__ __forceinline__ void a_store(uint16_t *As, const ARegs &r) {
 }
 
 // A fragments of slice kk for row tiles 0..TM-1
-__device__ __forceinline__ void a_frags(const uint16_t *As, int kk, int lane, bf16x8 (&af)[TM]) {
+__device__ __forceinline__ void a_frags(const uint16_t *As, int kk, int row0, int lane, bf16x8 (&af)[TM]) {
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
-    af[tm] = *reinterpret_cast<const bf16x8 *>(As + a_off(tm * 32 + (lane & 31), 4 * (lane >> 5) + kk));
+    af[tm] = *reinterpret_cast<const bf16x8 *>(As + a_off(row0 + tm * 32 + (lane & 31), 4 * (lane >> 5) + kk));
 }
 
 // this lane's codes (4 slices) and the two block scales of its weight columns
@@ -827,7 +829,7 @@ __device__ __forceinline__ void b_codes(const uint8_t *Bs, const uint32_t *Ss, i
   const int g = lane >> 5;
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    const int col = wn * 64 + tn * 32 + (lane & 31);
+    const int col = wn * TN * 32 + tn * 32 + (lane & 31);
     b.c[tn] = *reinterpret_cast<const u32x4 *>(Bs + col * 32 + 16 * g);
     const uint32_t sw = Ss[col] >> (16 * g);  // blocks 2g, 2g+1
     b.s[tn][0] = e4m3_hw<0>(sw);
@@ -869,7 +871,7 @@ __device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I
                                        Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
   constexpr bool DIRECT = ASRC == A_GATHER || ASRC == A_ROWS;
   constexpr int NDMA = (DIRECT ? ACH : 0) + 3;  // copy instructions per step and wave
-  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
   const int nk = s.K / BK;
   ARegs ar;
   // prologue: stage 0 <- step 0, stage 1 <- step 1 (copies), wait for stage 0
@@ -895,7 +897,7 @@ __device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I
   __syncthreads();
   bf16x8 af[2][TM], bf[2][TN];
   BCodes bc;
-  a_frags(sm.a[0], 0, lane, af[0]);
+  a_frags(sm.a[0], 0, row0, lane, af[0]);
   b_codes(sm.b[0], sm.s[0], wn, lane, bc);
   b_decode(bc, 0, bf[0]);
   int cur = 0;
@@ -914,7 +916,7 @@ __device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int nb = (kk + 1) & 1;
       if (kk + 1 < BK / 16) {
-        if (VT != VT_DYN || vt > 0) a_frags(sm.a[cur], kk + 1, lane, af[nb]);
+        if (VT != VT_DYN || vt > 0) a_frags(sm.a[cur], kk + 1, row0, lane, af[nb]);
         b_decode(bc, kk + 1, bf[nb]);
       } else {
         if (more2)
@@ -925,7 +927,7 @@ __device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I
           if (more2) a_store<ASRC>(sm.a[nn], ar);  // stage nn was last read two steps ago
         barrier_lds();
         if (more) {
-          a_frags(sm.a[nxt], 0, lane, af[nb]);
+          a_frags(sm.a[nxt], 0, row0, lane, af[nb]);
           b_codes(sm.b[nxt], sm.s[nxt], wn, lane, bc);
           b_decode(bc, 0, bf[nb]);
         }
@@ -944,14 +946,15 @@ __device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I
 template <int EPI>
 __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
                                          Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
-  const int lane = threadIdx.x & 63, wn = threadIdx.x >> 6, g = lane >> 5;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, g = lane >> 5;
+  const int row0 = (wid / WNG) * TM * 32;
   const int nk = (s.K + BK - 1) / BK;
   const int64_t slice = s.b_rows * s.b_cols;
   const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * slice;
   int64_t wr[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
-    int64_t w = b_row_of_col<EPI, BN>(wn * 64 + tn * 32 + (lane & 31), nt, N, I);
+    int64_t w = b_row_of_col<EPI, BN>(wn * TN * 32 + tn * 32 + (lane & 31), nt, N, I);
     wr[tn] = w < 0 ? 0 : w;
   }
   for (int ks = 0; ks < nk; ++ks) {
@@ -965,7 +968,7 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
       const int kb = (ks * BK + 32 * g + 8 * kk) % s.kmod;
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) bl[tn] = *reinterpret_cast<const bf16x8 *>(bsrc + wr[tn] * s.b_cols + kb);
-      a_frags(sm.a[0], kk, lane, af);
+      a_frags(sm.a[0], kk, row0, lane, af);
       mfmas<VT_DYN>(af, bl, vt, acc);
     }
     __syncthreads();
@@ -995,9 +998,9 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   const int rb = p.offsets[e];
   const int n_e = p.offsets[e + 1] - rb;
   const int m0 = (mt - p.tile_off[e]) * BM;
-  const int tid = threadIdx.x, lane = tid & 63, wn = tid >> 6;
-  const int rows_left = n_e - m0;
-  const int vt = rows_left >= TM * 32 ? TM : (rows_left + 31) / 32;  // >= 1: a tile has rows
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int rows_left = n_e - m0 - row0;  // this wave's valid 32-row tiles: vt (0 skips every MFMA)
+  const int vt = rows_left <= 0 ? 0 : (rows_left >= TM * 32 ? TM : (rows_left + 31) / 32);
 
   constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
   int64_t arow[ACH];
@@ -1036,7 +1039,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         sc[v] = sb;
-        const int pos = m0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (pos < n_e) {
           const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
           sc[v] = sb * p.s1.a_sd[src];
@@ -1060,7 +1063,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
     seg_lora<EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
   }
 
-  epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc);
+  if (vt > 0) epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
 }
 }  // namespace fq
 
