@@ -163,7 +163,8 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 
 // bf16 bits of two exactly representable floats, packed (lo, hi)
 __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  // bytes 2,3 of lo then bytes 2,3 of hi: (lo >> 16) | (hi & 0xFFFF0000) in one byte permute
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
 // byte `sel` of c holds two E2M1 codes (low nibble first) -> their values times sb
@@ -724,6 +725,21 @@ __device__ __forceinline__ int a_row(int j) { return 64 * (threadIdx.x >> 6) + 8
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Direct-to-LDS copies (lane i's 16 or 4 bytes land at lds + 16 i or 4 i), written as
+// inline assembly: the compiler's wait-count bookkeeping treats its own form of this
+// copy as an LDS event of unknown order and then drains every outstanding LDS read
+// (lgkmcnt(0)) before each use of an LDS result, exposing the read latency.  The
+// copies are waited for explicitly (wait_vm) before their stage is read.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)p);
+}
+__device__ __forceinline__ void dma_b128(const void *g, const void *lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void *g, const void *lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
+}
+
 // bf16 A rows of K step k0 -> stage As (direct-to-LDS; no registers)
 __device__ __forceinline__ void a_dma(const Seg &s, const int64_t (&arow)[ACH], int k0, uint16_t *As) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -732,8 +748,7 @@ __device__ __forceinline__ void a_dma(const Seg &s, const int64_t (&arow)[ACH], 
   for (int j = 0; j < ACH; ++j) {
     const int r = 64 * w + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);  // the chunk that lands at this lane's position
-    __builtin_amdgcn_global_load_lds(a + arow[j] * s.a_ld + k0 + 8 * c, (lds_void *)(As + (64 * w + 8 * j) * BK), 16,
-                                     0, 0);
+    dma_b128(a + arow[j] * s.a_ld + k0 + 8 * c, As + (64 * w + 8 * j) * BK);
   }
 }
 
@@ -750,13 +765,12 @@ __device__ __forceinline__ void b_dma(const Seg &s, int e, int nt, int N, int I,
     const int col = ins * 32 + (lane >> 1);
     int64_t wr = b_row_of_col<EPI, BN>(col, nt, N, I);
     wr = wr < 0 ? 0 : wr;
-    __builtin_amdgcn_global_load_lds(codes + wr * (s.b_cols / 2) + 16 * (lane & 1), (lds_void *)(Bs + ins * 1024), 16,
-                                     0, 0);
+    dma_b128(codes + wr * (s.b_cols / 2) + 16 * (lane & 1), Bs + ins * 1024);
   }
   const int col = 64 * w + lane;
   int64_t wr = b_row_of_col<EPI, BN>(col, nt, N, I);
   wr = wr < 0 ? 0 : wr;
-  __builtin_amdgcn_global_load_lds(scales + wr * (s.b_cols / 16), (lds_void *)(Ss + 64 * w), 4, 0, 0);
+  dma_b32(scales + wr * (s.b_cols / 16), Ss + 64 * w);
 }
 
 // A through registers: the LoRA segment (k >= K zeroed) and NVFP4 activation rows
@@ -940,6 +954,215 @@ __device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I
   __syncthreads();  // the stages are reused by the next segment
 }
 
+// ---- Segment 1 with A rows copied straight to LDS: software-pipelined K loop ----
+// One wave per SIMD has no other wave to hide its waits behind, so the step is
+// written out in issue order: each 32-row tile's two MFMAs of slice kk are followed
+// by that tile's A-fragment read for slice kk+1 and one bf16 pair of the slice-kk+1
+// weight decode (and, in slice 0, one copy of step ks+2), pinned in that order by
+// scheduling barriers.  The reads then have a whole slice of MFMAs to land, and the
+// decode and address arithmetic issue in the shadow of the matrix pipe.
+
+// per-thread copy sources at K step 0 (advanced by the step's K offset)
+struct DmaSrc {
+  const uint16_t *a[ACH];
+  const uint8_t *c[2];
+  const uint8_t *s;
+};
+
+template <int EPI>
+__device__ __forceinline__ void dma_src(const Seg &s, const int64_t (&arow)[ACH], int e, int nt, int N, int I,
+                                        DmaSrc &d) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) {
+    const int r = 64 * w + 8 * j + (lane >> 3);
+    d.a[j] = a + arow[j] * s.a_ld + 8 * ((lane & 7) ^ ((r >> 1) & 7));
+  }
+  const int64_t slice = s.b_rows * s.b_cols;
+  const uint8_t *codes = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2);
+  const uint8_t *scales = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int64_t wr = b_row_of_col<EPI, BN>((2 * w + j) * 32 + (lane >> 1), nt, N, I);
+    wr = wr < 0 ? 0 : wr;
+    d.c[j] = codes + wr * (s.b_cols / 2) + 16 * (lane & 1);
+  }
+  int64_t wr = b_row_of_col<EPI, BN>(64 * w + lane, nt, N, I);
+  wr = wr < 0 ? 0 : wr;
+  d.s = scales + wr * (s.b_cols / 16);
+}
+
+// copy number j (0..ACH+2) of the K step at k0 into one stage
+__device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, uint16_t *As, uint8_t *Bs, uint32_t *Ss) {
+  const int w = threadIdx.x >> 6;
+  if (j < ACH)
+    dma_b128(d.a[j] + k0, As + (64 * w + 8 * j) * BK);
+  else if (j < ACH + 2)
+    dma_b128(d.c[j - ACH] + k0 / 2, Bs + (2 * w + j - ACH) * 1024);
+  else
+    dma_b32(d.s + k0 / 16, Ss + 64 * w);
+}
+
+__device__ __forceinline__ bf16x8 a_frag(const uint16_t *As, int kk, int row, int lane) {
+  return *reinterpret_cast<const bf16x8 *>(As + a_off(row + (lane & 31), 4 * (lane >> 5) + kk));
+}
+
+// raw codes and scale words of this lane's weight columns (LDS reads only)
+struct BRaw {
+  u32x4 c[TN];
+  uint32_t sw[TN];
+};
+
+__device__ __forceinline__ void b_raw(const uint8_t *Bs, const uint32_t *Ss, int wn, int lane, BRaw &r) {
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int col = wn * TN * 32 + tn * 32 + (lane & 31);
+    r.c[tn] = *reinterpret_cast<const u32x4 *>(Bs + col * 32 + 16 * (lane >> 5));
+    r.sw[tn] = Ss[col];
+  }
+}
+
+__device__ __forceinline__ void b_cook(const BRaw &r, int lane, BCodes &b) {
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    b.c[tn] = r.c[tn];
+    const uint32_t sw = r.sw[tn] >> (16 * (lane >> 5));  // blocks 2g, 2g+1
+    b.s[tn][0] = e4m3_hw<0>(sw);
+    b.s[tn][1] = e4m3_hw<1>(sw);
+  }
+}
+
+// bf16 pair p (0..3) of column tile tn's fragment of slice kk
+__device__ __forceinline__ uint32_t dec_pair(const BCodes &b, int tn, int kk, int p) {
+  const uint32_t c = b.c[tn][kk];
+  f32x2 v;
+  if (p == 0)
+    v = fp4pair<0>(c, b.s[tn][kk >> 1]);
+  else if (p == 1)
+    v = fp4pair<1>(c, b.s[tn][kk >> 1]);
+  else if (p == 2)
+    v = fp4pair<2>(c, b.s[tn][kk >> 1]);
+  else
+    v = fp4pair<3>(c, b.s[tn][kk >> 1]);
+  return pack_exact(v.x, v.y);
+}
+
+__device__ __forceinline__ void mfma1(const bf16x8 &a, const u32x4 &b, f32x16 &acc) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+#define FQ_PIN() __builtin_amdgcn_sched_barrier(0)
+
+// One K step.  On entry af[0] / bf[0] hold slice 0 of stage `cur` and bc its codes.
+// DMA: issue the copies of the step at k2 into stage n2.  NEXT: a following step
+// exists (stage nx), whose slice 0 is loaded into af[0] / bf[0] at the end.
+template <int VT, bool DMA, bool NEXT>
+__device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrc &d, int wn, int row0,
+                                        int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], BCodes &bc,
+                                        f32x16 (&acc)[TM][TN]) {
+  constexpr int NDMA = ACH + 3;
+  const uint16_t *As = sm.a[cur];
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    const int c = kk & 1, n = c ^ 1;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
+      if (tm < VT) af[n][tm] = a_frag(As, kk + 1, row0 + 32 * tm, lane);
+      if (DMA && kk == 0) {
+        dma_one(d, tm, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
+        if (tm >= 5) dma_one(d, tm + 3, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
+      }
+      FQ_PIN();
+      if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
+      bf[n][tm >> 2][tm & 3] = dec_pair(bc, tm >> 2, kk + 1, tm & 3);
+      FQ_PIN();
+    }
+  }
+  // slice 3: its MFMAs around the step boundary, then the next step's slice 0
+  BRaw raw;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    if (tm < VT) mfma1(af[1][tm], bf[1][0], acc[tm][0]);
+    if (NEXT && tm >= 2 && tm - 2 < VT) af[0][tm - 2] = a_frag(sm.a[nx], 0, row0 + 32 * (tm - 2), lane);
+    if (NEXT && tm == 7) {
+      if (VT > 6) af[0][6] = a_frag(sm.a[nx], 0, row0 + 192, lane);
+      if (VT > 7) af[0][7] = a_frag(sm.a[nx], 0, row0 + 224, lane);
+    }
+    FQ_PIN();
+    if (tm < VT) mfma1(af[1][tm], bf[1][1], acc[tm][1]);
+    if (NEXT && tm == 0) {
+      // stage nx has landed for every wave, and every wave is done reading stage
+      // cur (its last reads were issued in slice 2 and are drained here), so the
+      // next step may copy into it
+      FQ_PIN();
+      if (DMA)
+        wait_vm<NDMA>();
+      else
+        wait_vm<0>();
+      barrier_lds();
+      FQ_PIN();
+      b_raw(sm.b[nx], sm.s[nx], wn, lane, raw);
+    }
+    if (NEXT && tm == 3) b_cook(raw, lane, bc);
+    if (NEXT && tm >= 4) {
+      const int q = 2 * (tm - 4);  // pairs q, q+1 of slice 0
+      bf[0][q >> 2][q & 3] = dec_pair(bc, q >> 2, 0, q & 3);
+      bf[0][(q + 1) >> 2][(q + 1) & 3] = dec_pair(bc, (q + 1) >> 2, 0, (q + 1) & 3);
+    }
+    FQ_PIN();
+  }
+}
+
+template <int EPI, int VT>
+__device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
+                                              Smem &sm, f32x16 (&acc)[TM][TN]) {
+  constexpr int NDMA = ACH + 3;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int nk = s.K / BK;
+  DmaSrc d;
+  dma_src<EPI>(s, arow, e, nt, N, I, d);
+  // prologue: stage 0 <- step 0, stage 1 <- step 1; wait for stage 0 only
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma_one(d, j, 0, sm.a[0], sm.b[0], sm.s[0]);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) dma_one(d, j, BK, sm.a[1], sm.b[1], sm.s[1]);
+    wait_vm<NDMA>();
+  } else {
+    wait_vm<0>();
+  }
+  barrier_lds();
+  bf16x8 af[2][TM];
+  u32x4 bf[2][TN];
+  BCodes bc;
+  {
+    BRaw raw;
+    b_raw(sm.b[0], sm.s[0], wn, lane, raw);
+#pragma unroll
+    for (int tm = 0; tm < VT; ++tm) af[0][tm] = a_frag(sm.a[0], 0, row0 + 32 * tm, lane);
+    b_cook(raw, lane, bc);
+#pragma unroll
+    for (int q = 0; q < 4 * TN; ++q) bf[0][q >> 2][q & 3] = dec_pair(bc, q >> 2, 0, q & 3);
+  }
+  int cur = 0, ks = 0;
+  for (; ks + 2 < nk; ++ks) {
+    const int nx = cur == NST - 1 ? 0 : cur + 1;
+    const int n2 = nx == NST - 1 ? 0 : nx + 1;
+    step_q4<VT, true, true>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, bc, acc);
+    cur = nx;
+  }
+  if (ks + 1 < nk) {
+    const int nx = cur == NST - 1 ? 0 : cur + 1;
+    step_q4<VT, false, true>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
+    cur = nx;
+  }
+  step_q4<VT, false, false>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
+  __syncthreads();  // the stages are reused by the next segment
+}
+#undef FQ_PIN
+
 // Segment 2 (LoRA up-projection): A = hi/lo pair rows through registers (k >= K
 // zeroed), B = the bf16 LoRA matrix [N rows][kmod], fragments loaded straight
 // from global memory (it is small and stays in L2).
@@ -1022,10 +1245,21 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  if (vt == TM)
+  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
+    // row tiles rounded up to even counts (rows past the segment are dropped)
+    if (vt > 6)
+      seg_q4_direct<EPI, 8>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    else if (vt > 4)
+      seg_q4_direct<EPI, 6>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    else if (vt > 2)
+      seg_q4_direct<EPI, 4>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    else
+      seg_q4_direct<EPI, 2>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  } else if (vt == TM) {
     seg_q4<ASRC, EPI, VT_ALL>(p.s1, e, nt, p.N, p.I, arow, sm, vt, acc);
-  else
+  } else {
     seg_q4<ASRC, EPI, VT_DYN>(p.s1, e, nt, p.N, p.I, arow, sm, vt, acc);
+  }
 
   // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
   // per row (NVFP4 activations) before the LoRA segment
