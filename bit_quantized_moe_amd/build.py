@@ -45,6 +45,11 @@ def _compile(src: str, objdir: str) -> str:
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
     flags = list(COMMON_FLAGS)
     flags.append("-ffp-contract=off" if src in NO_CONTRACT else "-ffp-contract=fast")
+    if src == "moe.hip":
+        # the GEMM epilogues index 256 accumulator registers with constant indices only
+        # after their loops are fully unrolled; the default limit for an unroll pragma
+        # leaves the largest (SwiGLU backward) rolled and the accumulator in scratch
+        flags += ["-mllvm", "-pragma-unroll-threshold=200000"]
     cmd = [_hipcc(), *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -493,9 +493,68 @@ __device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, 
 // epilogues: acc[tm][tn] element v of a wave holds row row0 + tm*32 + 8(v/4) +
 // 4(lane/32) + v%4 and column col0 + tn*32 + lane%32 of the tile
 // ---------------------------------------------------------------------------
+// SwiGLU backward of the down dgrad: da = w * da_u, dh = [dg, du] from the saved FP32
+// gate/up activations.  One 32-row block at a time, every load of the block (the
+// 16 rows' routing weights and their gate/up values) is issued before any store,
+// through restrict pointers, so the loads of a block overlap one another instead
+// of each waiting for the previous row's stores.
+template <int TM, int TN, int BN>
+__device__ __forceinline__ void epilogue_down_dgrad(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0,
+                                                    int n_e, int rb, int row0, int col0, int lane, float esc) {
+  const int32_t *__restrict__ perm = p.perm;
+  const float *__restrict__ tw = p.tw;
+  const float *__restrict__ hin = p.h_in;
+  uint16_t *__restrict__ out = p.out0;
+  const int64_t ld = 2 * (int64_t)p.I;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    int64_t grow[16];
+    int pf[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      grow[v] = rb + min(pos, n_e - 1);  // rows past the segment: loads of a valid row, no store
+      pf[v] = perm[grow[v]];
+    }
+    float w[16], g[16][TN], u[16][TN];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        int i = nt * BN + col0 + tn * 32 + (lane & 31);
+        i = i < p.N ? i : 0;
+        g[v][tn] = hin[grow[v] * ld + i];
+        u[v][tn] = hin[grow[v] * ld + p.I + i];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) w[v] = tw[pf[v]];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (pos >= n_e) continue;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        const int i = nt * BN + col0 + tn * 32 + (lane & 31);
+        if (i >= p.N) continue;
+        const float sg = sigmoid_f(g[v][tn]);
+        const float da = w[v] * (acc[tm][tn][v] * esc);
+        const float dg = da * u[v][tn] * sg * (1.0f + g[v][tn] * (1.0f - sg));
+        const float du = da * g[v][tn] * sg;
+        out[grow[v] * ld + i] = (uint16_t)f32_to_bf16(dg);
+        out[grow[v] * ld + p.I + i] = (uint16_t)f32_to_bf16(du);
+      }
+    }
+  }
+}
+
 template <int TM, int TN, int BN, int EPI>
 __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc)[TM][TN], int e, int nt, int m0,
                                          int n_e, int rb, int row0, int col0, int lane, float esc) {
+  if constexpr (EPI == EPI_DOWN_DGRAD) {
+    epilogue_down_dgrad<TM, TN, BN>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+    return;
+  }
   const float osc = p.div_e ? p.out_scale / p.div_e[e] : p.out_scale;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
@@ -540,21 +599,6 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + col0 + tn * 32 + (lane & 31);
           if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * esc * p.out_scale;
-        }
-      } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
-        const float w = p.tw[p.perm[grow]];
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int i = nt * BN + col0 + tn * 32 + (lane & 31);
-          if (i >= p.N) continue;
-          const float g = p.h_in[grow * 2 * p.I + i];
-          const float u = p.h_in[grow * 2 * p.I + p.I + i];
-          const float sg = sigmoid_f(g);
-          const float da = w * (acc[tm][tn][v] * esc);
-          const float dg = da * u * sg * (1.0f + g * (1.0f - sg));
-          const float du = da * g * sg;
-          p.out0[grow * 2 * p.I + i] = (uint16_t)f32_to_bf16(dg);
-          p.out0[grow * 2 * p.I + p.I + i] = (uint16_t)f32_to_bf16(du);
         }
       }
     }
@@ -701,8 +745,9 @@ constexpr int NST = 3;  // LDS stages: copies run two K steps ahead
 
 struct Smem {
   uint16_t a[NST][BM * BK];  // bf16, swizzled 128-byte rows
-  uint8_t b[NST][BN * 32];   // codes, 32 bytes per output column
-  uint32_t s[NST][BN];       // the column's 4 E4M3 block scales of the K step
+  uint8_t b[NST][BN * 32];   // codes: 32 bytes per output column (forward), 128 per weight row (dgrad)
+  uint32_t s[NST][BN];       // E4M3 block scales of the K step
+  uint8_t t[BN / 64][256];   // dgrad: each wave's scales regrouped per 16-column block
 };
 
 // Workgroup barrier that orders LDS (waits for this wave's LDS operations, then
@@ -1198,6 +1243,340 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
   }
 }
 
+// ---- dgrad over the rowwise NVFP4 weight, read transposed ----
+// dX[r, h] = sum_j dH[r, j] DQ(W)[j, h]: the contraction runs over the weight's rows
+// j, while its 16-element scale blocks run along h.  Each K step copies 64 weight
+// rows of the tile's 256 columns (64 x 128 code bytes, 16-byte chunk c of row j at
+// position c ^ (j & 7)) and their 64 x 16 scale bytes to LDS as they are stored.
+// The gfx950 4-bit transposing LDS read then hands every lane of a 16-lane group
+// one column (= one scale block) with 16 consecutive rows of codes; the 16 scales
+// of those rows are regrouped per block in a small per-wave LDS area.  A step's k
+// order: slice kk = 2m + t, lane group g covers rows 32m + 16g + 8t .. +8, for the
+// A fragments and the weight alike.
+
+struct DmaSrcD {
+  const uint16_t *a[ACH];
+  const uint8_t *c[2];
+  const uint8_t *s;
+  int64_t cstride, sstride;  // bytes per weight row: codes, scales
+};
+
+__device__ __forceinline__ void dma_src_d(const Seg &s, const int64_t (&arow)[ACH], int e, int nt, int N,
+                                          DmaSrcD &d) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
+#pragma unroll
+  for (int j = 0; j < ACH; ++j) {
+    const int r = 64 * w + 8 * j + (lane >> 3);
+    d.a[j] = a + arow[j] * s.a_ld + 8 * ((lane & 7) ^ ((r >> 1) & 7));
+  }
+  const int64_t slice = s.b_rows * s.b_cols;
+  d.cstride = s.b_cols / 2;
+  d.sstride = s.b_cols / 16;
+  const uint8_t *codes = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2);
+  const uint8_t *scales = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * w + 8 * j + (lane >> 3);
+    int c = (lane & 7) ^ (row & 7);                 // the chunk that lands at this lane's position
+    if (nt * BN + 32 * c >= N) c = 0;               // columns past N: any valid bytes (dropped)
+    d.c[j] = codes + row * d.cstride + nt * (BN / 2) + 16 * c;
+  }
+  const int row = 16 * w + (lane >> 2);
+  int q = lane & 3;
+  if (nt * (BN / 16) + 4 * q >= N / 16) q = 0;
+  d.s = scales + row * d.sstride + nt * (BN / 16) + 4 * q;
+}
+
+// copy j (0..ACH+2) of the K step at k0 into one stage
+__device__ __forceinline__ void dma_one_d(const DmaSrcD &d, int j, int k0, uint16_t *As, uint8_t *Bs, uint32_t *Ss) {
+  const int w = threadIdx.x >> 6;
+  if (j < ACH)
+    dma_b128(d.a[j] + k0, As + (64 * w + 8 * j) * BK);
+  else if (j < ACH + 2)
+    dma_b128(d.c[j - ACH] + k0 * d.cstride, Bs + (16 * w + 8 * (j - ACH)) * 128);
+  else
+    dma_b32(d.s + k0 * d.sstride, Ss + 64 * w);
+}
+
+__device__ __forceinline__ bf16x8 a_frag_d(const uint16_t *As, int kk, int row, int lane) {
+  const int c = 4 * (kk >> 1) + 2 * (lane >> 5) + (kk & 1);
+  return *reinterpret_cast<const bf16x8 *>(As + a_off(row + (lane & 31), c));
+}
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// this lane's codes of column tile tn for rows 32m + 16g .. +16 (nibble i = row +i)
+__device__ __forceinline__ i32x2 codes_tr(const uint8_t *Bs, int wn, int tn, int m, int lane) {
+  const int q = lane >> 4, row = 32 * m + 16 * (q >> 1) + (lane & 15);
+  const int c = 2 * wn + tn;  // 16-byte chunk of the wave's column tile; half q & 1
+  const uint8_t *p = Bs + row * 128 + 16 * (c ^ (row & 7)) + 8 * (q & 1);
+  return __builtin_amdgcn_ds_read_tr4_b64_v2i32((lds_i32x2 *)(p));
+}
+
+struct DRaw {
+  i32x2 c[TN][2];   // codes per column tile and row half-step m
+  u32x4 s[TN][2];   // the 16 scale bytes of those rows, in row order
+};
+
+// bf16 pair p of column tile tn's fragment of slice kk
+__device__ __forceinline__ uint32_t dec_pair_d(const DRaw &r, int tn, int kk, int p) {
+  const int m = kk >> 1, t = kk & 1;
+  const uint32_t c = (uint32_t)r.c[tn][m][t];
+  const uint32_t sw = r.s[tn][m][2 * t + (p >> 1)];
+  f32x2 v;
+  if (p == 0)
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+  else if (p == 1)
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+  else if (p == 2)
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+  else
+    v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+  const f32x2 sc = (p & 1) ? __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)sw, false);
+  v = v * sc;  // exact: <= 6 significant bits
+  return pack_exact(v.x, v.y);
+}
+
+#define FQ_PIN() __builtin_amdgcn_sched_barrier(0)
+
+template <int VT, bool DMA, bool NEXT>
+__device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrcD &d, int wn, int row0,
+                                        int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], DRaw &raw,
+                                        f32x16 (&acc)[TM][TN]) {
+  constexpr int NDMA = ACH + 3;
+  const uint16_t *As = sm.a[cur];
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+    const int c = kk & 1, n = c ^ 1;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
+      if (tm < VT) af[n][tm] = a_frag_d(As, kk + 1, row0 + 32 * tm, lane);
+      if (DMA && kk == 0) {
+        dma_one_d(d, tm, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
+        if (tm >= 5) dma_one_d(d, tm + 3, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
+      }
+      FQ_PIN();
+      if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
+      bf[n][tm >> 2][tm & 3] = dec_pair_d(raw, tm >> 2, kk + 1, tm & 3);
+      FQ_PIN();
+    }
+  }
+  // slice 3 around the step boundary; then slice 0 of the next step
+  uint32_t sw = 0;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    if (tm < VT) mfma1(af[1][tm], bf[1][0], acc[tm][0]);
+    if (NEXT) {
+      if (tm == 1 || tm == 4 || tm == 5) {
+        const int i = tm == 1 ? 0 : (tm == 4 ? 4 : 6);
+        if (i < VT) af[0][i] = a_frag_d(sm.a[nx], 0, row0 + 32 * i, lane);
+        if (i + 1 < VT) af[0][i + 1] = a_frag_d(sm.a[nx], 0, row0 + 32 * (i + 1), lane);
+      }
+      if (tm == 2 && 2 < VT) af[0][2] = a_frag_d(sm.a[nx], 0, row0 + 64, lane);
+      if (tm == 3 && 3 < VT) af[0][3] = a_frag_d(sm.a[nx], 0, row0 + 96, lane);
+      if (tm == 2) {
+        // regroup this wave's 4 x 64 scale bytes per column block
+        uint8_t *t = sm.t[wn];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) t[64 * b + lane] = (uint8_t)(sw >> (8 * b));
+      }
+      if (tm == 3) {
+        const uint8_t *t = sm.t[wn];
+        const int q = lane >> 4;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            raw.s[tn][m] = *reinterpret_cast<const u32x4 *>(t + 64 * (2 * tn + (q & 1)) + 32 * m + 16 * (q >> 1));
+      }
+    }
+    FQ_PIN();
+    if (tm < VT) mfma1(af[1][tm], bf[1][1], acc[tm][1]);
+    if (NEXT && tm == 0) {
+      // stage nx has landed for every wave and every wave is done reading stage cur
+      FQ_PIN();
+      if (DMA)
+        wait_vm<NDMA>();
+      else
+        wait_vm<0>();
+      barrier_lds();
+      FQ_PIN();
+      sw = sm.s[nx][16 * lane / 4 + wn];  // scale dword (row lane, blocks 4wn .. 4wn+3)
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int m = 0; m < 2; ++m) raw.c[tn][m] = codes_tr(sm.b[nx], wn, tn, m, lane);
+    }
+    if (NEXT && tm >= 6) {
+      const int tn = tm - 6;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bf[0][tn][q] = dec_pair_d(raw, tn, 0, q);
+    }
+    FQ_PIN();
+  }
+}
+
+template <int EPI, int VT>
+__device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
+                                              f32x16 (&acc)[TM][TN]) {
+  constexpr int NDMA = ACH + 3;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int nk = s.K / BK;
+  DmaSrcD d;
+  dma_src_d(s, arow, e, nt, N, d);
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, 0, sm.a[0], sm.b[0], sm.s[0]);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, BK, sm.a[1], sm.b[1], sm.s[1]);
+    wait_vm<NDMA>();
+  } else {
+    wait_vm<0>();
+  }
+  barrier_lds();
+  bf16x8 af[2][TM];
+  u32x4 bf[2][TN];
+  DRaw raw;
+  {
+    const uint32_t sw = sm.s[0][16 * lane / 4 + wn];
+    uint8_t *t = sm.t[wn];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) t[64 * b + lane] = (uint8_t)(sw >> (8 * b));
+    const int q = lane >> 4;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        raw.c[tn][m] = codes_tr(sm.b[0], wn, tn, m, lane);
+        raw.s[tn][m] = *reinterpret_cast<const u32x4 *>(t + 64 * (2 * tn + (q & 1)) + 32 * m + 16 * (q >> 1));
+      }
+#pragma unroll
+    for (int tm = 0; tm < VT; ++tm) af[0][tm] = a_frag_d(sm.a[0], 0, row0 + 32 * tm, lane);
+#pragma unroll
+    for (int q2 = 0; q2 < 4 * TN; ++q2) bf[0][q2 >> 2][q2 & 3] = dec_pair_d(raw, q2 >> 2, 0, q2 & 3);
+  }
+  int cur = 0, ks = 0;
+  for (; ks + 2 < nk; ++ks) {
+    const int nx = cur == NST - 1 ? 0 : cur + 1;
+    const int n2 = nx == NST - 1 ? 0 : nx + 1;
+    step_dq<VT, true, true>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, raw, acc);
+    cur = nx;
+  }
+  if (ks + 1 < nk) {
+    const int nx = cur == NST - 1 ? 0 : cur + 1;
+    step_dq<VT, false, true>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
+    cur = nx;
+  }
+  step_dq<VT, false, false>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
+  __syncthreads();  // the stages are reused by the next segment
+}
+#undef FQ_PIN
+
+// Segment 2 of the dgrad (LoRA): A = hi/lo pair rows (k >= K zeroed), B = the bf16
+// LoRA matrix [kmod rows][N cols] taken at row k mod kmod; its 64 x 256 tile is
+// staged in natural layout (row stride BN + 8) and read with the 16-bit
+// transposing LDS read.
+constexpr int LSTR = BN + 8;
+
+__device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
+                                           int vt, f32x16 (&acc)[TM][TN]) {
+  static_assert(sizeof(sm.a[1]) * 2 >= BK * LSTR * 2, "LoRA tile fits two A stages");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int nk = (s.K + BK - 1) / BK;
+  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * (s.b_rows * s.b_cols);
+  uint16_t *Bt = sm.a[1];
+  for (int ks = 0; ks < nk; ++ks) {
+    ARegs ar;
+    a_load<A_ROWS, true>(s, arow, ks * BK, ar);
+    u32x4 bv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + NTHR * i, row = c >> 5, col = nt * BN + 8 * (c & 31);
+      const int kb = (ks * BK + row) % s.kmod;
+      bv[i] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)kb * s.b_cols + (col < N ? col : 0));
+    }
+    a_store<A_ROWS>(sm.a[0], ar);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + NTHR * i;
+      *reinterpret_cast<u32x4 *>(Bt + (c >> 5) * LSTR + 8 * (c & 31)) = bv[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 af[TM], bl[TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) bl[tn] = b_frag_trans_s<LSTR>(Bt, 16 * kk, wn * TN * 32 + tn * 32, lane);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+        af[tm] = *reinterpret_cast<const bf16x8 *>(sm.a[0] + a_off(row0 + tm * 32 + (lane & 31), 2 * kk + (lane >> 5)));
+      mfmas<VT_DYN>(af, bl, vt, acc);
+    }
+    __syncthreads();
+  }
+}
+
+template <int ASRC, int EPI>
+__global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int total = p.tile_off[p.E] * p.NT;
+  const int per = (total + 7) / 8;
+  const int li = blockIdx.x >> 3;
+  if (li >= per) return;
+  const int L = (blockIdx.x & 7) * per + li;
+  if (L >= total) return;
+  const int mt = L / p.NT, nt = L % p.NT;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= mt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int rb = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - rb;
+  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int rows_left = n_e - m0 - row0;
+  const int vt = rows_left <= 0 ? 0 : (rows_left >= TM * 32 ? TM : (rows_left + 31) / 32);
+  int64_t arow[ACH];
+#pragma unroll
+  for (int i = 0; i < ACH; ++i) {
+    const int pos = min(m0 + a_row(i), n_e - 1);
+    arow[i] = ASRC == A_GATHER ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+  }
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  if (vt > 6)
+    seg_dq_direct<EPI, 8>(p.s1, e, nt, p.N, arow, sm, acc);
+  else if (vt > 4)
+    seg_dq_direct<EPI, 6>(p.s1, e, nt, p.N, arow, sm, acc);
+  else if (vt > 2)
+    seg_dq_direct<EPI, 4>(p.s1, e, nt, p.N, arow, sm, acc);
+  else
+    seg_dq_direct<EPI, 2>(p.s1, e, nt, p.N, arow, sm, acc);
+  // the per-expert FP32 decode scale multiplies the whole accumulator (the LoRA
+  // segment's A operand was stored divided by it)
+  const float esc = p.s1.b_sd[e];
+  if (p.s2.K > 0) {
+    int64_t arow2[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row(i), n_e - 1);
+    seg_lora_n(p.s2, e, nt, p.N, arow2, sm, vt, acc);
+  }
+  if (vt > 0) epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
+}
+
 template <int ASRC, int EPI>
 __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
@@ -1620,6 +1999,15 @@ bqm_status launch_fq(const GemmParams &p, int64_t R, hipStream_t s, const char *
   return launch_status(what);
 }
 
+// dgrad GEMM over the rowwise NVFP4 weight read transposed (codes staged in LDS)
+template <int ASRC, int EPI>
+bqm_status launch_fd(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+  static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
+  const int grid = gemm_grid(R, p.E, p.NT);
+  fq::gemm_dgrad_q4<ASRC, EPI><<<grid, fq::NTHR, 0, s>>>(p);
+  return launch_status(what);
+}
+
 GemmParams base_params(const bqm_moe_desc *d, const Ws &w) {
   GemmParams p{};
   p.perm = w.at<int32_t>(w.L.perm);
@@ -1831,7 +2219,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     if (nf4)
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
     else
-      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch<256, A_GATHER, B_Q4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fd<A_GATHER, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
   }
   // V_gu = s dh B_gu  [R, r]
   if (r > 0) {
@@ -1855,7 +2243,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     if (nf4)
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
     else
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_Q4_N, B_BF_N, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
   }
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_DGRAD, 0, s);
