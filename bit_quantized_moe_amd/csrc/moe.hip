@@ -389,6 +389,14 @@ __device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const floa
   }
 }
 
+// A wave-uniform float loaded once into a scalar register.  Loaded into a vector
+// register instead, its first use sits inside the epilogue's per-element branches,
+// and the wait for the load is then repeated before every store (each such wait
+// also drains the stores already issued).
+__device__ __forceinline__ float uniform_load(const float *ptr) {
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(*ptr)));
+}
+
 // logistic function with the hardware exponential and reciprocal (about 2 ulp)
 __device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
@@ -555,7 +563,7 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc
     epilogue_down_dgrad<TM, TN, BN>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
     return;
   }
-  const float osc = p.div_e ? p.out_scale / p.div_e[e] : p.out_scale;
+  const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -671,7 +679,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
   constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
   constexpr bool kQB = BSRC == B_Q4_K || BSRC == B_Q4_N;
   float esc = 1.0f;
-  if constexpr (kQB && !kQA) esc = p.s1.b_sd[e];
+  if constexpr (kQB && !kQA) esc = uniform_load(p.s1.b_sd + e);
   if constexpr (kQA) {
     float sb = 1.0f;
     if constexpr (kQB) sb = p.s1.b_sd[e];
@@ -1567,7 +1575,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
     seg_dq_direct<EPI, 2>(p.s1, e, nt, p.N, arow, sm, acc);
   // the per-expert FP32 decode scale multiplies the whole accumulator (the LoRA
   // segment's A operand was stored divided by it)
-  const float esc = p.s1.b_sd[e];
+  const float esc = uniform_load(p.s1.b_sd + e);
   if (p.s2.K > 0) {
     int64_t arow2[ACH];
 #pragma unroll
@@ -1643,7 +1651,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
   // per row (NVFP4 activations) before the LoRA segment
   float esc = 1.0f;
-  if constexpr (!kQA) esc = p.s1.b_sd[e];
+  if constexpr (!kQA) esc = uniform_load(p.s1.b_sd + e);
   if constexpr (kQA) {
     const float sb = p.s1.b_sd[e];
 #pragma unroll
