@@ -506,7 +506,7 @@ __device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, 
 // 16 rows' routing weights and their gate/up values) is issued before any store,
 // through restrict pointers, so the loads of a block overlap one another instead
 // of each waiting for the previous row's stores.
-template <int TM, int TN, int BN>
+template <int TM, int TN, int BN, bool FULL>
 __device__ __forceinline__ void epilogue_down_dgrad(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0,
                                                     int n_e, int rb, int row0, int col0, int lane, float esc) {
   const int32_t *__restrict__ perm = p.perm;
@@ -514,69 +514,73 @@ __device__ __forceinline__ void epilogue_down_dgrad(const GemmParams &p, const f
   const float *__restrict__ hin = p.h_in;
   uint16_t *__restrict__ out = p.out0;
   const int64_t ld = 2 * (int64_t)p.I;
+  constexpr int VB = 32 / TN;  // rows per batch: 64 gate/up values in flight
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
-    int64_t grow[16];
-    int pf[16];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      grow[v] = rb + min(pos, n_e - 1);  // rows past the segment: loads of a valid row, no store
-      pf[v] = perm[grow[v]];
-    }
-    float w[16], g[16][TN], u[16][TN];
+    for (int v0 = 0; v0 < 16; v0 += VB) {
+      int64_t grow[VB];
+      int pf[VB];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        int i = nt * BN + col0 + tn * 32 + (lane & 31);
-        i = i < p.N ? i : 0;
-        g[v][tn] = hin[grow[v] * ld + i];
-        u[v][tn] = hin[grow[v] * ld + p.I + i];
+      for (int j = 0; j < VB; ++j) {
+        const int v = v0 + j;
+        const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        grow[j] = rb + min(pos, n_e - 1);  // rows past the segment: loads of a valid row, no store
+        pf[j] = perm[grow[j]];
       }
-    }
+      float w[VB], g[VB][TN], u[VB][TN];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) w[v] = tw[pf[v]];
+      for (int j = 0; j < VB; ++j) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (pos >= n_e) continue;
+        for (int tn = 0; tn < TN; ++tn) {
+          int i = nt * BN + col0 + tn * 32 + (lane & 31);
+          i = i < p.N ? i : 0;
+          g[j][tn] = hin[grow[j] * ld + i];
+          u[j][tn] = hin[grow[j] * ld + p.I + i];
+        }
+      }
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) {
-        const int i = nt * BN + col0 + tn * 32 + (lane & 31);
-        if (i >= p.N) continue;
-        const float sg = sigmoid_f(g[v][tn]);
-        const float da = w[v] * (acc[tm][tn][v] * esc);
-        const float dg = da * u[v][tn] * sg * (1.0f + g[v][tn] * (1.0f - sg));
-        const float du = da * g[v][tn] * sg;
-        out[grow[v] * ld + i] = (uint16_t)f32_to_bf16(dg);
-        out[grow[v] * ld + p.I + i] = (uint16_t)f32_to_bf16(du);
+      for (int j = 0; j < VB; ++j) w[j] = tw[pf[j]];
+#pragma unroll
+      for (int j = 0; j < VB; ++j) {
+        const int v = v0 + j;
+        const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (!FULL && pos >= n_e) continue;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const int i = nt * BN + col0 + tn * 32 + (lane & 31);
+          if (!FULL && i >= p.N) continue;
+          const float sg = sigmoid_f(g[j][tn]);
+          const float da = w[j] * (acc[tm][tn][v] * esc);
+          const float dg = da * u[j][tn] * sg * (1.0f + g[j][tn] * (1.0f - sg));
+          const float du = da * g[j][tn] * sg;
+          out[grow[j] * ld + i] = (uint16_t)f32_to_bf16(dg);
+          out[grow[j] * ld + p.I + i] = (uint16_t)f32_to_bf16(du);
+        }
       }
     }
   }
 }
 
-template <int TM, int TN, int BN, int EPI>
-__device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc)[TM][TN], int e, int nt, int m0,
-                                         int n_e, int rb, int row0, int col0, int lane, float esc) {
-  if constexpr (EPI == EPI_DOWN_DGRAD) {
-    epilogue_down_dgrad<TM, TN, BN>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
-    return;
-  }
-  const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
+// FULL: every row and column of this wave's block is inside the output (the common
+// case), so the per-element bounds tests and their branches are left out.
+template <int TM, int TN, int BN, int EPI, bool FULL>
+__device__ __forceinline__ void epilogue_body(const GemmParams &p, const f32x16 (&acc)[TM][TN], float osc, int nt,
+                                              int m0, int n_e, int rb, int row0, int col0, int lane, float esc) {
+  const float sc = esc * p.out_scale;
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      if (pos >= n_e) continue;
+      if (!FULL && pos >= n_e) continue;
       const int64_t grow = rb + pos;
       if constexpr (EPI == EPI_GATEUP) {
         // in each 64-column group of the tile: 32 gate columns, then the matching up columns
 #pragma unroll
         for (int q = 0; q < TN / 2; ++q) {
           const int i = nt * (BN / 2) + col0 / 2 + q * 32 + (lane & 31);
-          if (i >= p.I) continue;
+          if (!FULL && i >= p.I) continue;
           const float g = acc[tm][2 * q][v] * esc, u = acc[tm][2 * q + 1][v] * esc;
           const float a = g * sigmoid_f(g) * u;
           p.outf[grow * 2 * p.I + i] = g;
@@ -587,14 +591,14 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + col0 + tn * 32 + (lane & 31);
-          if (n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * esc * p.out_scale);
+          if (FULL || n < p.N) p.out0[grow * p.N + n] = (uint16_t)f32_to_bf16(acc[tm][tn][v] * sc);
         }
       } else if constexpr (EPI == EPI_STORE_SPLIT) {
         // FP32 value kept as an unevaluated pair of bf16 (hi in columns [0, N), lo in [N, 2N))
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + col0 + tn * 32 + (lane & 31);
-          if (n < p.N) {
+          if (FULL || n < p.N) {
             const float val = acc[tm][tn][v] * osc;
             const uint32_t hb = f32_to_bf16(val);
             const float lo2 = val - __uint_as_float(hb << 16);
@@ -606,11 +610,31 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
           const int n = nt * BN + col0 + tn * 32 + (lane & 31);
-          if (n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * esc * p.out_scale;
+          if (FULL || n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * sc;
         }
       }
     }
   }
+}
+
+template <int TM, int TN, int BN, int EPI>
+__device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc)[TM][TN], int e, int nt, int m0,
+                                         int n_e, int rb, int row0, int col0, int lane, float esc) {
+  const bool rows_in = m0 + row0 + TM * 32 <= n_e;
+  if constexpr (EPI == EPI_DOWN_DGRAD) {
+    if (rows_in && nt * BN + col0 + TN * 32 <= p.N)
+      epilogue_down_dgrad<TM, TN, BN, true>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+    else
+      epilogue_down_dgrad<TM, TN, BN, false>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+    return;
+  }
+  const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
+  const bool cols_in = EPI == EPI_GATEUP ? nt * (BN / 2) + col0 / 2 + (TN / 2) * 32 <= p.I
+                                         : nt * BN + col0 + TN * 32 <= p.N;
+  if (rows_in && cols_in)
+    epilogue_body<TM, TN, BN, EPI, true>(p, acc, osc, nt, m0, n_e, rb, row0, col0, lane, esc);
+  else
+    epilogue_body<TM, TN, BN, EPI, false>(p, acc, osc, nt, m0, n_e, rb, row0, col0, lane, esc);
 }
 
 template <class C, int ASRC, int BSRC, int B2SRC, int EPI>
