@@ -1242,11 +1242,30 @@ __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N
 
 // Segment 2 (LoRA up-projection): A = hi/lo pair rows through registers (k >= K
 // zeroed), B = the bf16 LoRA matrix [N rows][kmod], fragments loaded straight
-// from global memory (it is small and stays in L2).
+// from global memory (it is small and stays in L2).  The loads of step ks+1 are
+// issued before the MFMAs of step ks, alternating between two LDS A buffers, so
+// the segment waits for global memory once, not once per slice.
+struct LoraRegs {
+  ARegs a;
+  bf16x8 b[4][TN];
+};
+
+template <int EPI>
+__device__ __forceinline__ void lora_load(const Seg &s, const int64_t (&arow)[ACH], const uint16_t *bsrc,
+                                          const int64_t (&wr)[TN], int ks, int lane, LoraRegs &r) {
+  a_load<A_ROWS, true>(s, arow, ks * BK, r.a);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int kb = (ks * BK + 32 * (lane >> 5) + 8 * kk) % s.kmod;
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) r.b[kk][tn] = *reinterpret_cast<const bf16x8 *>(bsrc + wr[tn] * s.b_cols + kb);
+  }
+}
+
 template <int EPI>
 __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
                                          Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, g = lane >> 5;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG;
   const int row0 = (wid / WNG) * TM * 32;
   const int nk = (s.K + BK - 1) / BK;
   const int64_t slice = s.b_rows * s.b_cols;
@@ -1257,22 +1276,24 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
     int64_t w = b_row_of_col<EPI, BN>(wn * TN * 32 + tn * 32 + (lane & 31), nt, N, I);
     wr[tn] = w < 0 ? 0 : w;
   }
-  for (int ks = 0; ks < nk; ++ks) {
-    ARegs ar;
-    a_load<A_ROWS, true>(s, arow, ks * BK, ar);
-    a_store<A_ROWS>(sm.a[0], ar);
-    __syncthreads();
+  LoraRegs r[2];
+  lora_load<EPI>(s, arow, bsrc, wr, 0, lane, r[0]);
+  for (int ks = 0; ks < nk; ks += 2) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 bl[TN], af[TM];
-      const int kb = (ks * BK + 32 * g + 8 * kk) % s.kmod;
+    for (int h = 0; h < 2; ++h) {
+      if (ks + h >= nk) break;
+      a_store<A_ROWS>(sm.a[h], r[h].a);
+      if (ks + h + 1 < nk) lora_load<EPI>(s, arow, bsrc, wr, ks + h + 1, lane, r[h ^ 1]);
+      __syncthreads();
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn) bl[tn] = *reinterpret_cast<const bf16x8 *>(bsrc + wr[tn] * s.b_cols + kb);
-      a_frags(sm.a[0], kk, row0, lane, af);
-      mfmas<VT_DYN>(af, bl, vt, acc);
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8 af[TM];
+        a_frags(sm.a[h], kk, row0, lane, af);
+        mfmas<VT_DYN>(af, r[h].b[kk], vt, acc);
+      }
     }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
 // ---- dgrad over the rowwise NVFP4 weight, read transposed ----
@@ -1513,6 +1534,18 @@ __device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N
 // transposing LDS read.
 constexpr int LSTR = BN + 8;
 
+__device__ __forceinline__ void lora_n_load(const Seg &s, const int64_t (&arow)[ACH], const uint16_t *bsrc, int nt,
+                                            int N, int ks, ARegs &a, u32x4 (&bv)[8]) {
+  const int tid = threadIdx.x;
+  a_load<A_ROWS, true>(s, arow, ks * BK, a);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + NTHR * i, row = c >> 5, col = nt * BN + 8 * (c & 31);
+    const int kb = (ks * BK + row) % s.kmod;
+    bv[i] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)kb * s.b_cols + (col < N ? col : 0));
+  }
+}
+
 __device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
                                            int vt, f32x16 (&acc)[TM][TN]) {
   static_assert(sizeof(sm.a[1]) * 2 >= BK * LSTR * 2, "LoRA tile fits two A stages");
@@ -1520,22 +1553,17 @@ __device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, c
   const int nk = (s.K + BK - 1) / BK;
   const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * (s.b_rows * s.b_cols);
   uint16_t *Bt = sm.a[1];
+  ARegs ar;
+  u32x4 bv[8];
+  lora_n_load(s, arow, bsrc, nt, N, 0, ar, bv);
   for (int ks = 0; ks < nk; ++ks) {
-    ARegs ar;
-    a_load<A_ROWS, true>(s, arow, ks * BK, ar);
-    u32x4 bv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + NTHR * i, row = c >> 5, col = nt * BN + 8 * (c & 31);
-      const int kb = (ks * BK + row) % s.kmod;
-      bv[i] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)kb * s.b_cols + (col < N ? col : 0));
-    }
     a_store<A_ROWS>(sm.a[0], ar);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + NTHR * i;
       *reinterpret_cast<u32x4 *>(Bt + (c >> 5) * LSTR + 8 * (c & 31)) = bv[i];
     }
+    if (ks + 1 < nk) lora_n_load(s, arow, bsrc, nt, N, ks + 1, ar, bv);  // lands during this step's MFMAs
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
