@@ -775,12 +775,28 @@ constexpr int TM = BM / WMG / 32, TN = BN / WNG / 32;
 
 constexpr int NST = 3;  // LDS stages: copies run two K steps ahead
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 struct Smem {
   uint16_t a[NST][BM * BK];  // bf16, swizzled 128-byte rows
   uint8_t b[NST][BN * 32];   // codes: 32 bytes per output column (forward), 128 per weight row (dgrad)
   uint32_t s[NST][BN];       // E4M3 block scales of the K step
   uint8_t t[BN / 64][256];   // dgrad: each wave's scales regrouped per 16-column block
 };
+
+// LDS byte addresses of a stage's A, B and scale areas and the wave index, all
+// computed in scalar registers (the copies take their LDS address from M0)
+__device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ uint32_t smem_u32(const Smem &sm) { return (uint32_t)(uintptr_t)(const lds_void *)&sm; }
+__device__ __forceinline__ uint32_t lds_a(const Smem &sm, int st) {
+  return smem_u32(sm) + (uint32_t)offsetof(Smem, a) + (uint32_t)st * (uint32_t)sizeof(sm.a[0]);
+}
+__device__ __forceinline__ uint32_t lds_b(const Smem &sm, int st) {
+  return smem_u32(sm) + (uint32_t)offsetof(Smem, b) + (uint32_t)st * (uint32_t)sizeof(sm.b[0]);
+}
+__device__ __forceinline__ uint32_t lds_s(const Smem &sm, int st) {
+  return smem_u32(sm) + (uint32_t)offsetof(Smem, s) + (uint32_t)st * (uint32_t)sizeof(sm.s[0]);
+}
 
 // Workgroup barrier that orders LDS (waits for this wave's LDS operations, then
 // s_barrier) without waiting for outstanding global loads: __syncthreads() also
@@ -800,7 +816,6 @@ __device__ __forceinline__ int a_off(int r, int c) { return r * BK + 8 * (c ^ ((
 // row of the tile owned by this thread's j-th A chunk
 __device__ __forceinline__ int a_row(int j) { return 64 * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3); }
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct-to-LDS copies (lane i's 16 or 4 bytes land at lds + 16 i or 4 i), written as
 // inline assembly: the compiler's wait-count bookkeeping treats its own form of this
@@ -810,12 +825,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)p);
 }
-__device__ __forceinline__ void dma_b128(const void *g, const void *lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
+// lds: the wave-uniform LDS byte address (M0), kept in a scalar register
+__device__ __forceinline__ void dma_b128(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void dma_b32(const void *g, const void *lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds_addr(lds)) : "memory", "m0");
+__device__ __forceinline__ void dma_b32(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
 }
+__device__ __forceinline__ void dma_b128(const void *g, const void *lds) { dma_b128(g, lds_addr(lds)); }
+__device__ __forceinline__ void dma_b32(const void *g, const void *lds) { dma_b32(g, lds_addr(lds)); }
 
 // bf16 A rows of K step k0 -> stage As (direct-to-LDS; no registers)
 __device__ __forceinline__ void a_dma(const Seg &s, const int64_t (&arow)[ACH], int k0, uint16_t *As) {
@@ -1070,15 +1088,15 @@ __device__ __forceinline__ void dma_src(const Seg &s, const int64_t (&arow)[ACH]
   d.s = scales + wr * (s.b_cols / 16);
 }
 
-// copy number j (0..ACH+2) of the K step at k0 into one stage
-__device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, uint16_t *As, uint8_t *Bs, uint32_t *Ss) {
-  const int w = threadIdx.x >> 6;
+// copy number j (0..ACH+2) of the K step at k0 into stage st
+__device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, const Smem &sm, int st) {
+  const uint32_t w = wave_id();
   if (j < ACH)
-    dma_b128(d.a[j] + k0, As + (64 * w + 8 * j) * BK);
+    dma_b128(d.a[j] + k0, lds_a(sm, st) + (64 * w + 8 * j) * BK * 2);
   else if (j < ACH + 2)
-    dma_b128(d.c[j - ACH] + k0 / 2, Bs + (2 * w + j - ACH) * 1024);
+    dma_b128(d.c[j - ACH] + k0 / 2, lds_b(sm, st) + (2 * w + j - ACH) * 1024);
   else
-    dma_b32(d.s + k0 / 16, Ss + 64 * w);
+    dma_b32(d.s + k0 / 16, lds_s(sm, st) + 256 * w);
 }
 
 __device__ __forceinline__ bf16x8 a_frag(const uint16_t *As, int kk, int row, int lane) {
@@ -1148,8 +1166,8 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag(As, kk + 1, row0 + 32 * tm, lane);
       if (DMA && kk == 0) {
-        dma_one(d, tm, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
-        if (tm >= 5) dma_one(d, tm + 3, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
+        dma_one(d, tm, k2, sm, n2);
+        if (tm >= 5) dma_one(d, tm + 3, k2, sm, n2);
       }
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
@@ -1202,10 +1220,10 @@ __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N
   dma_src<EPI>(s, arow, e, nt, N, I, d);
   // prologue: stage 0 <- step 0, stage 1 <- step 1; wait for stage 0 only
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma_one(d, j, 0, sm.a[0], sm.b[0], sm.s[0]);
+  for (int j = 0; j < NDMA; ++j) dma_one(d, j, 0, sm, 0);
   if (nk > 1) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one(d, j, BK, sm.a[1], sm.b[1], sm.s[1]);
+    for (int j = 0; j < NDMA; ++j) dma_one(d, j, BK, sm, 1);
     wait_vm<NDMA>();
   } else {
     wait_vm<0>();
@@ -1341,15 +1359,15 @@ __device__ __forceinline__ void dma_src_d(const Seg &s, const int64_t (&arow)[AC
   d.s = scales + row * d.sstride + nt * (BN / 16) + 4 * q;
 }
 
-// copy j (0..ACH+2) of the K step at k0 into one stage
-__device__ __forceinline__ void dma_one_d(const DmaSrcD &d, int j, int k0, uint16_t *As, uint8_t *Bs, uint32_t *Ss) {
-  const int w = threadIdx.x >> 6;
+// copy j (0..ACH+2) of the K step at k0 into stage st
+__device__ __forceinline__ void dma_one_d(const DmaSrcD &d, int j, int k0, const Smem &sm, int st) {
+  const uint32_t w = wave_id();
   if (j < ACH)
-    dma_b128(d.a[j] + k0, As + (64 * w + 8 * j) * BK);
+    dma_b128(d.a[j] + k0, lds_a(sm, st) + (64 * w + 8 * j) * BK * 2);
   else if (j < ACH + 2)
-    dma_b128(d.c[j - ACH] + k0 * d.cstride, Bs + (16 * w + 8 * (j - ACH)) * 128);
+    dma_b128(d.c[j - ACH] + k0 * d.cstride, lds_b(sm, st) + (16 * w + 8 * (j - ACH)) * 128);
   else
-    dma_b32(d.s + k0 * d.sstride, Ss + 64 * w);
+    dma_b32(d.s + k0 * d.sstride, lds_s(sm, st) + 256 * w);
 }
 
 __device__ __forceinline__ bf16x8 a_frag_d(const uint16_t *As, int kk, int row, int lane) {
@@ -1408,8 +1426,8 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag_d(As, kk + 1, row0 + 32 * tm, lane);
       if (DMA && kk == 0) {
-        dma_one_d(d, tm, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
-        if (tm >= 5) dma_one_d(d, tm + 3, k2, sm.a[n2], sm.b[n2], sm.s[n2]);
+        dma_one_d(d, tm, k2, sm, n2);
+        if (tm >= 5) dma_one_d(d, tm + 3, k2, sm, n2);
       }
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
@@ -1481,10 +1499,10 @@ __device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N
   DmaSrcD d;
   dma_src_d(s, arow, e, nt, N, d);
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, 0, sm.a[0], sm.b[0], sm.s[0]);
+  for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, 0, sm, 0);
   if (nk > 1) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, BK, sm.a[1], sm.b[1], sm.s[1]);
+    for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, BK, sm, 1);
     wait_vm<NDMA>();
   } else {
     wait_vm<0>();
