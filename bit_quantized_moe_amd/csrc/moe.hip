@@ -1099,6 +1099,14 @@ __device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, const Sm
     dma_b32(d.s + k0 / 16, lds_s(sm, st) + 256 * w);
 }
 
+// Where the ACH + 3 copies of step ks+2 are issued inside step ks: spread over
+// slices 0..2 (one MFMA pair in two or three carries one), so that the four waves'
+// copies do not queue up behind each other in one slice.  -1: none here.
+__device__ __forceinline__ constexpr int dma_slot(int kk, int tm) {
+  return kk < 2 ? ((tm & 1) ? -1 : 4 * kk + tm / 2) : (kk == 2 && tm % 3 == 0 ? 8 + tm / 3 : -1);
+}
+static_assert(ACH + 3 == 11, "dma_slot places 11 copies");
+
 __device__ __forceinline__ bf16x8 a_frag(const uint16_t *As, int kk, int row, int lane) {
   return *reinterpret_cast<const bf16x8 *>(As + a_off(row + (lane & 31), 4 * (lane >> 5) + kk));
 }
@@ -1165,10 +1173,7 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
     for (int tm = 0; tm < TM; ++tm) {
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag(As, kk + 1, row0 + 32 * tm, lane);
-      if (DMA && kk == 0) {
-        dma_one(d, tm, k2, sm, n2);
-        if (tm >= 5) dma_one(d, tm + 3, k2, sm, n2);
-      }
+      if (DMA && dma_slot(kk, tm) >= 0) dma_one(d, dma_slot(kk, tm), k2, sm, n2);
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
       bf[n][tm >> 2][tm & 3] = dec_pair(bc, tm >> 2, kk + 1, tm & 3);
@@ -1425,10 +1430,7 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
     for (int tm = 0; tm < TM; ++tm) {
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag_d(As, kk + 1, row0 + 32 * tm, lane);
-      if (DMA && kk == 0) {
-        dma_one_d(d, tm, k2, sm, n2);
-        if (tm >= 5) dma_one_d(d, tm + 3, k2, sm, n2);
-      }
+      if (DMA && dma_slot(kk, tm) >= 0) dma_one_d(d, dma_slot(kk, tm), k2, sm, n2);
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
       bf[n][tm >> 2][tm & 3] = dec_pair_d(raw, tm >> 2, kk + 1, tm & 3);
