@@ -1099,12 +1099,16 @@ __device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, const Sm
     dma_b32(d.s + k0 / 16, lds_s(sm, st) + 256 * w);
 }
 
-// Where the ACH + 3 copies of step ks+2 are issued inside step ks: spread over
-// slices 0..2 (one MFMA pair in two or three carries one), so that the four waves'
-// copies do not queue up behind each other in one slice.  -1: none here.
+// Where the ACH + 3 copies of step ks+2 are issued inside step ks: one every third
+// MFMA pair over all four slices, so the four waves' copies do not queue up behind
+// each other.  Stage (ks+2) % 3 was last read in step ks-1, so any point of step ks
+// may write it.  DMA_EARLY copies come before the wait in slice 3, which must let
+// exactly those stay in flight.  -1: none here.
 __device__ __forceinline__ constexpr int dma_slot(int kk, int tm) {
-  return kk < 2 ? ((tm & 1) ? -1 : 4 * kk + tm / 2) : (kk == 2 && tm % 3 == 0 ? 8 + tm / 3 : -1);
+  return (8 * kk + tm) % 3 == (kk == 3 ? 1 : 0) && (kk < 3 || tm >= 1) ? (kk < 3 ? (8 * kk + tm) / 3 : 8 + (tm - 1) / 3)
+                                                                       : -1;
 }
+constexpr int DMA_EARLY = 8;
 static_assert(ACH + 3 == 11, "dma_slot places 11 copies");
 
 __device__ __forceinline__ bf16x8 a_frag(const uint16_t *As, int kk, int row, int lane) {
@@ -1198,13 +1202,14 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
       // next step may copy into it
       FQ_PIN();
       if (DMA)
-        wait_vm<NDMA>();
+        wait_vm<DMA_EARLY>();
       else
         wait_vm<0>();
       barrier_lds();
       FQ_PIN();
       b_raw(sm.b[nx], sm.s[nx], wn, lane, raw);
     }
+    if (DMA && dma_slot(3, tm) >= 0) dma_one(d, dma_slot(3, tm), k2, sm, n2);
     if (NEXT && tm == 3) b_cook(raw, lane, bc);
     if (NEXT && tm >= 4) {
       const int q = 2 * (tm - 4);  // pairs q, q+1 of slice 0
@@ -1468,11 +1473,12 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
     }
     FQ_PIN();
     if (tm < VT) mfma1(af[1][tm], bf[1][1], acc[tm][1]);
+    if (DMA && dma_slot(3, tm) >= 0) dma_one_d(d, dma_slot(3, tm), k2, sm, n2);
     if (NEXT && tm == 0) {
       // stage nx has landed for every wave and every wave is done reading stage cur
       FQ_PIN();
       if (DMA)
-        wait_vm<NDMA>();
+        wait_vm<DMA_EARLY>();
       else
         wait_vm<0>();
       barrier_lds();
