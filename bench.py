@@ -176,8 +176,21 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
-    ap.add_argument("--no-sweep", action="store_true", help="skip the token-count sweep")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the layer step at smaller token counts (extra kernel calls at other sizes)")
+    ap.add_argument("--no-sweep", action="store_true", help=argparse.SUPPRESS)  # the default
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_call": 1 << 30, "calls": 3}), flush=True)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
               "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
@@ -298,7 +311,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "quantizer": quant,
     }
-    if not args.no_sweep:
+    if args.sweep:
         del ws
         torch.cuda.empty_cache()
         result["token_sweep"] = token_sweep(shape, wgu, wdn, ev, sh)
