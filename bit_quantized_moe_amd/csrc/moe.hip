@@ -1767,6 +1767,149 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
 }  // namespace fq
 
 // ---------------------------------------------------------------------------
+// LoRA projections (N = r): U = s X A^T (A K-major [r][K]) and V = s dY B
+// (B N-major [K][r]), per routed row, stored as hi/lo bf16 pairs.
+// ---------------------------------------------------------------------------
+// These stream the routed activation rows once (K = H, I or 2I deep, 64 columns),
+// so they are bound by memory: a 256 x 64 tile per workgroup of 4 waves (64 rows
+// each), two LDS stages of 40 KB filled by direct-to-LDS copies one step ahead, two
+// workgroups per CU.  Rows are the same XOR-swizzled 128-byte rows as the GEMMs;
+// an N-major B tile keeps its 64 k-rows of 128 bytes with 16-byte chunk c at
+// c ^ (k & 7) and is read with the 16-bit transposing LDS read.
+namespace lp {
+constexpr int BM = 256, BN = 64, NTHR = 256, NST = 2, TM = 2, TN = 2, NDMA = 10;
+
+struct Smem {
+  uint16_t a[NST][BM * BK];
+  uint16_t b[NST][BN * BK];
+};
+
+__device__ __forceinline__ uint32_t smem_u32(const Smem &sm) { return (uint32_t)(uintptr_t)(const fq::lds_void *)&sm; }
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+// B fragment of an N-major swizzled tile: lane L gets column nbase + (L & 31) and
+// rows kbase + 8 (L >> 5) + 0..7
+__device__ __forceinline__ bf16x8 b_frag_nm(const uint16_t *Bs, int kbase, int nbase, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int row = kbase + 8 * (g >> 1) + (sl >> 2), col = nbase + 16 * (g & 1) + 4 * (sl & 3);
+  const uint16_t *p0 = Bs + row * BK + 8 * ((col >> 3) ^ (row & 7)) + (col & 7);
+  const uint16_t *p1 = Bs + (row + 4) * BK + 8 * ((col >> 3) ^ ((row + 4) & 7)) + (col & 7);
+  const s16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p0));
+  const s16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p1));
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  const s16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int ASRC, bool BNM>
+__global__ void __launch_bounds__(NTHR, 2) gemm_lora_proj(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int total = p.tile_off[p.E] * p.NT;
+  const int per = (total + 7) / 8;
+  const int li = blockIdx.x >> 3;
+  if (li >= per) return;
+  const int L = (blockIdx.x & 7) * per + li;
+  if (L >= total) return;
+  const int mt = L / p.NT, nt = L % p.NT;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= mt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int rb = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - rb;
+  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int lane = threadIdx.x & 63;
+  const uint32_t w = fq::wave_id();
+  const int row0 = 64 * (int)w;
+  const int rows_left = n_e - m0 - row0;
+  const int vt = rows_left <= 0 ? 0 : (rows_left >= 64 ? 2 : (rows_left + 31) / 32);
+  const Seg &s = p.s1;
+  // copy sources at K step 0: 8 A chunks and 2 B chunks per thread
+  const uint16_t *asrc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 64 * (int)w + 8 * j + (lane >> 3);
+    const int pos = min(m0 + row, n_e - 1);
+    const int64_t arow = ASRC == A_GATHER ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+    asrc[j] = reinterpret_cast<const uint16_t *>(s.a) + arow * s.a_ld + 8 * ((lane & 7) ^ ((row >> 1) & 7));
+  }
+  const uint16_t *bsrc[2];
+  const uint16_t *bbase = reinterpret_cast<const uint16_t *>(s.b) + e * (s.b_rows * s.b_cols);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (int)w + 8 * i + (lane >> 3);
+    if constexpr (BNM) {  // row = k of the step; 8 columns per chunk
+      int c = (lane & 7) ^ (row & 7);
+      if (nt * BN + 8 * c >= p.N) c = 0;  // columns past r: any valid bytes (dropped)
+      bsrc[i] = bbase + (int64_t)row * s.b_cols + nt * BN + 8 * c;
+    } else {  // row = output column n
+      int n = nt * BN + row;
+      n = n < p.N ? n : 0;
+      bsrc[i] = bbase + (int64_t)n * s.b_cols + 8 * ((lane & 7) ^ ((row >> 1) & 7));
+    }
+  }
+  const int64_t bstep = BNM ? (int64_t)BK * s.b_cols : BK;  // elements per K step
+  const uint32_t sbase = smem_u32(sm);
+  auto issue = [&](int ks, int st) {
+    const uint32_t la = sbase + (uint32_t)offsetof(Smem, a) + (uint32_t)st * (uint32_t)sizeof(sm.a[0]);
+    const uint32_t lb = sbase + (uint32_t)offsetof(Smem, b) + (uint32_t)st * (uint32_t)sizeof(sm.b[0]);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fq::dma_b128(asrc[j] + ks * BK, la + (64 * w + 8 * j) * BK * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) fq::dma_b128(bsrc[i] + ks * bstep, lb + (16 * w + 8 * i) * BK * 2);
+  };
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  const int nk = s.K / BK;
+  issue(0, 0);
+  for (int ks = 0; ks < nk; ++ks) {
+    const int st = ks & 1;
+    if (ks + 1 < nk) {
+      issue(ks + 1, st ^ 1);
+      fq::wait_vm<NDMA>();
+    } else {
+      fq::wait_vm<0>();
+    }
+    fq::barrier_lds();
+    const uint16_t *As = sm.a[st], *Bs = sm.b[st];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 af[TM], bf[TN];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        if constexpr (BNM)
+          bf[tn] = b_frag_nm(Bs, 16 * kk, tn * 32, lane);
+        else
+          bf[tn] = *reinterpret_cast<const bf16x8 *>(Bs + fq::a_off(tn * 32 + (lane & 31), 2 * kk + (lane >> 5)));
+      }
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        af[tm] = *reinterpret_cast<const bf16x8 *>(As + fq::a_off(row0 + tm * 32 + (lane & 31), 2 * kk + (lane >> 5)));
+        if (tm < vt) {
+#pragma unroll
+          for (int tn = 0; tn < TN; ++tn)
+            acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+        }
+      }
+    }
+    fq::barrier_lds();  // the next step copies into this stage
+  }
+  if (vt > 0) epilogue<TM, TN, BN, EPI_STORE_SPLIT>(p, acc, e, nt, m0, n_e, rb, row0, 0, lane, 1.0f);
+}
+}  // namespace lp
+
+// ---------------------------------------------------------------------------
 // LoRA weight gradients: C[e] [M, N] = sum over the expert's rows of P[row][m] * Q[row][n]
 // ---------------------------------------------------------------------------
 struct WgradParams {
@@ -2085,6 +2228,15 @@ bqm_status launch_fq(const GemmParams &p, int64_t R, hipStream_t s, const char *
   return launch_status(what);
 }
 
+// LoRA projections (N = r) streamed through LDS by direct copies
+template <int ASRC, bool BNM>
+bqm_status launch_lp(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+  static_assert(lp::BM == BM, "tile offsets are computed for BM rows");
+  const int grid = gemm_grid(R, p.E, p.NT);
+  lp::gemm_lora_proj<ASRC, BNM><<<grid, lp::NTHR, 0, s>>>(p);
+  return launch_status(what);
+}
+
 // dgrad GEMM over the rowwise NVFP4 weight read transposed (codes staged in LDS)
 template <int ASRC, int EPI>
 bqm_status launch_fd(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
@@ -2156,7 +2308,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.out_scale = ls;
     p.div_e = fold_fwd ? d->w_gu.s_dec : nullptr;
     p.out0 = ugu;
-    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch<64, A_GATHER, B_BF_K, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_a gate_up")));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch_lp<A_GATHER, false>(p, R, s, "lora_a gate_up")));
   }
   // h = X~ W~_gu^T + U_gu B_gu^T; a = silu(g) u
   {
@@ -2190,7 +2342,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.out_scale = ls;
     p.div_e = fold_fwd ? d->w_dn.s_dec : nullptr;
     p.out0 = udn;
-    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch<64, A_ROWS, B_BF_K, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_a down")));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch_lp<A_ROWS, false>(p, R, s, "lora_a down")));
   }
   // y = a~ W~_dn^T + U_dn B_dn^T
   {
@@ -2290,7 +2442,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.out_scale = ls;
     p.div_e = lora_folds_s_dec(d, false) ? d->w_dn.s_dec : nullptr;
     p.out0 = vdn;
-    BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch<64, A_GATHER, B_BF_N, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_b^T down")));
+    BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch_lp<A_GATHER, true>(p, R, s, "lora_b^T down")));
   }
   // da_u = dY W~_dn + V_dn A_dn; dh = SwiGLU'(w da_u)
   {
@@ -2316,7 +2468,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.out_scale = ls;
     p.div_e = lora_folds_s_dec(d, false) ? d->w_gu.s_dec : nullptr;
     p.out0 = vgu;
-    BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch<64, A_ROWS, B_BF_N, B_NONE, EPI_STORE_SPLIT>(p, R, s, "lora_b^T gate_up")));
+    BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch_lp<A_ROWS, true>(p, R, s, "lora_b^T gate_up")));
   }
   // dX_row = dh W~_gu + V_gu A_gu
   {
