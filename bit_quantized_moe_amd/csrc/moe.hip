@@ -67,7 +67,7 @@ struct GemmParams {
   float out_scale;
   const float *div_e;     // EPI_STORE_SPLIT: per-expert divisor of the output (NULL: none)
   uint16_t *out0, *out1;  // bf16 outputs
-  float *outf;            // FP32 output (h, y, dX rows)
+  float *outf;            // FP32 output (the gate/up activations h)
   const float *h_in;      // saved FP32 gate/up activations (dgrad epilogue)
   const float *tw;        // routing weight of pair f (dgrad epilogue)
 };
@@ -2021,8 +2021,9 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
 // ---------------------------------------------------------------------------
 // combine, routing-weight gradient
 // ---------------------------------------------------------------------------
-// out[t][c] = sum_j w[t,j] * rows[inv[t*k+j]][c] (w = 1 when tw == NULL), j ascending
-__global__ void __launch_bounds__(NTHR) combine_rows(const float *__restrict__ rows, const int32_t *__restrict__ inv,
+// out[t][c] = sum_j w[t,j] * rows[inv[t*k+j]][c] (w = 1 when tw == NULL), j ascending,
+// FP32 accumulation over the bf16 routed rows
+__global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict__ rows, const int32_t *__restrict__ inv,
                                                      const float *__restrict__ tw, int64_t T, int k, int64_t H,
                                                      uint16_t *__restrict__ out) {
   const int64_t cpr = H / 8;
@@ -2032,10 +2033,9 @@ __global__ void __launch_bounds__(NTHR) combine_rows(const float *__restrict__ r
     for (int j = 0; j < k; ++j) {
       const int64_t f = t * k + j;
       const float w = tw ? tw[f] : 1.0f;
-      const float4 *src = reinterpret_cast<const float4 *>(rows + (int64_t)inv[f] * H + c);
-      const float4 v0 = src[0], v1 = src[1];
-      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
-      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+      const uint4 v = *reinterpret_cast<const uint4 *>(rows + (int64_t)inv[f] * H + c);
+      acc[0] += w * bf16_lo(v.x); acc[1] += w * bf16_hi(v.x); acc[2] += w * bf16_lo(v.y); acc[3] += w * bf16_hi(v.y);
+      acc[4] += w * bf16_lo(v.z); acc[5] += w * bf16_hi(v.z); acc[6] += w * bf16_lo(v.w); acc[7] += w * bf16_hi(v.w);
     }
     uint32_t o[4];
 #pragma unroll
@@ -2045,20 +2045,21 @@ __global__ void __launch_bounds__(NTHR) combine_rows(const float *__restrict__ r
 }
 
 // dtw[f] = <dy[t], y[inv[f]]>, one wave per routed pair
-__global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict__ dy, const float *__restrict__ y,
+__global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict__ dy, const uint16_t *__restrict__ y,
                                                      const int32_t *__restrict__ inv, int64_t R, int k, int64_t H,
                                                      float *__restrict__ dtw) {
   const int lane = threadIdx.x & 63;
   const int64_t f = (int64_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6);
   if (f >= R) return;
   const uint16_t *a = dy + (f / k) * H;
-  const float *b = y + (int64_t)inv[f] * H;
+  const uint16_t *b = y + (int64_t)inv[f] * H;
   float s = 0.0f;
   for (int64_t c = lane * 8; c < H; c += 64 * 8) {
-    uint4 va = *reinterpret_cast<const uint4 *>(a + c);
-    const float4 b0 = *reinterpret_cast<const float4 *>(b + c), b1 = *reinterpret_cast<const float4 *>(b + c + 4);
-    s += bf16_lo(va.x) * b0.x + bf16_hi(va.x) * b0.y + bf16_lo(va.y) * b0.z + bf16_hi(va.y) * b0.w;
-    s += bf16_lo(va.z) * b1.x + bf16_hi(va.z) * b1.y + bf16_lo(va.w) * b1.z + bf16_hi(va.w) * b1.w;
+    const uint4 va = *reinterpret_cast<const uint4 *>(a + c), vb = *reinterpret_cast<const uint4 *>(b + c);
+    s += bf16_lo(va.x) * bf16_lo(vb.x) + bf16_hi(va.x) * bf16_hi(vb.x) + bf16_lo(va.y) * bf16_lo(vb.y) +
+         bf16_hi(va.y) * bf16_hi(vb.y);
+    s += bf16_lo(va.z) * bf16_lo(vb.z) + bf16_hi(va.z) * bf16_hi(vb.z) + bf16_lo(va.w) * bf16_lo(vb.w) +
+         bf16_hi(va.w) * bf16_hi(vb.w);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -2093,7 +2094,7 @@ Layout layout(const bqm_moe_desc *d) {
   L.udn = take(R * 2 * r * 2);
   L.h = take(R * 2 * I * 4);
   L.a = take(R * I * 2);
-  L.y = take(R * H * 4);
+  L.y = take(R * H * 2);
   const bool aq = d->act_quant != 0;
   L.xq_c = take(aq ? T * H / 2 : 0);
   L.xq_s = take(aq ? T * H / 16 : 0);
@@ -2104,7 +2105,7 @@ Layout layout(const bqm_moe_desc *d) {
   L.vdn = take(R * 2 * r * 2);
   L.dh = take(R * 2 * I * 2);
   L.vgu = take(R * 2 * r * 2);
-  L.dxr = take(R * H * 4);
+  L.dxr = take(R * H * 2);
   L.total = o;
   return L;
 }
@@ -2296,7 +2297,8 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
   const int H = (int)d->H, I = (int)d->I, r = d->r;
   const float ls = d->lora_scale;
   uint16_t *ugu = w.at<uint16_t>(w.L.ugu), *udn = w.at<uint16_t>(w.L.udn);
-  float *h = w.at<float>(w.L.h), *y = w.at<float>(w.L.y);
+  float *h = w.at<float>(w.L.h);
+  uint16_t *y = w.at<uint16_t>(w.L.y);
   uint16_t *a = w.at<uint16_t>(w.L.a);
   const bool fold_fwd = lora_folds_s_dec(d, true);
   // U_gu = s X A_gu^T   [R, r]  (divided by the expert's s_dec when that folds)
@@ -2355,13 +2357,13 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       p.s1.a_sd = w.at<float>(w.L.aq_d);
     }
     p.s2 = seg_lora(udn, d->B_dn, H, r, r);
-    p.outf = y;
+    p.out0 = y;
     if (nf4)
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE_F32>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
     else if (aq)
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE_F32>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd")));
     else
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE_F32>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE>(p, R, s, "down fwd")));
   }
   return BQM_OK;
 }
@@ -2404,7 +2406,7 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_FWD, 0, s);
   combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(
-      w.at<float>(w.L.y), w.at<int32_t>(w.L.inv), w.at<float>(w.L.tw), d->T, d->k, d->H, out);
+      w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), w.at<float>(w.L.tw), d->T, d->k, d->H, out);
   mark(d, BQM_STAGE_COMBINE_FWD, 1, s);
   return launch_status("combine fwd");
 }
@@ -2425,10 +2427,10 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
   const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
   uint16_t *vdn = w.at<uint16_t>(w.L.vdn), *vgu = w.at<uint16_t>(w.L.vgu);
   uint16_t *dh = w.at<uint16_t>(w.L.dh);
-  float *dxr = w.at<float>(w.L.dxr);
+  uint16_t *dxr = w.at<uint16_t>(w.L.dxr);
   if (dtopk_w) {
     mark(d, BQM_STAGE_DTOPK, 0, s);
-    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<float>(w.L.y), w.at<int32_t>(w.L.inv), R, d->k,
+    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), R, d->k,
                                                           d->H, dtopk_w);
     mark(d, BQM_STAGE_DTOPK, 1, s);
     BQM_TRY(launch_status("dtopk"));
@@ -2477,11 +2479,11 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.NT = (int)cdiv(H, 256);
     p.s1 = seg_q(dh, 2 * I, d->w_gu, 2 * I);
     p.s2 = seg_lora(vgu, d->A_gu, r, H, r);
-    p.outf = dxr;
+    p.out0 = dxr;
     if (nf4)
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
     else
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE_F32>(p, R, s, "gate_up dgrad")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE>(p, R, s, "gate_up dgrad")));
   }
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_DGRAD, 0, s);

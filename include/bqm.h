@@ -197,8 +197,9 @@ size_t bqm_moe_workspace_size(const bqm_moe_desc *d);
  *   y = a~ DQ(W_dn[e])^T + s (a A_dn[e]^T) B_dn[e]^T
  * (nf4moe page, the QuantizedNaiveMoe forward; only experts that receive tokens
  * are read).  x bf16 [T, H], topk_idx i32 [T, k], topk_w f32 [T, k], y bf16
- * [T, H] (the layer output).  Accumulation is FP32; the workspace keeps h and y in
- * FP32 and a in bf16 (the bf16 operand of the down projection). */
+ * [T, H] (the layer output).  Accumulation is FP32; the workspace keeps h in FP32 and
+ * a (the down projection's bf16 operand) and the routed rows y in bf16, as the pages'
+ * bf16 module does; the combine sums the k rows of a token in FP32. */
 bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, const int32_t *topk_idx,
                        const float *topk_w, uint16_t *out, void *ws, size_t ws_bytes,
                        void *stream);
