@@ -47,6 +47,13 @@ def test_small_nvfp4_lora():
     compare_full(small("small"), lora_scale=0.5)
 
 
+def test_small_nvfp4_partial_tiles():
+    # H and I multiples of 64 but not of 256: partial column tiles in all four GEMMs
+    # (gate_up N = 2I = 384, down N = H = 320, dgrad N = I = 192 and H = 320) and
+    # odd K-step counts (5, 3, 5, 6)
+    compare_full(small("small_odd", H=320, I=192, T=260, E=12))
+
+
 def test_small_nvfp4_no_lora():
     compare_full(small("small_r0", r=0, T=97, k=2))
 
