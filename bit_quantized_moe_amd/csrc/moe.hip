@@ -637,6 +637,124 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc
     epilogue_body<TM, TN, BN, EPI, false>(p, acc, osc, nt, m0, n_e, rb, row0, col0, lane, esc);
 }
 
+// Epilogue of the accumulator transposed: the grouped GEMMs of namespace fq issue
+// their MFMAs as weights x activations, so element v of lane L holds output column
+// 8(v/4) + 4(L/32) + v%4 of row L%32.  Each lane then owns one row per 32-row tile
+// and 4 consecutive columns per group of 4 registers: one 8- or 16-byte store (or
+// load) per 4 values instead of one per value, and one routing weight per row.
+template <int TM, int TN, int BN, int EPI, bool FULL>
+__device__ __forceinline__ void epilogue_t_body(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0,
+                                                int n_e, int rb, int row0, int col0, int lane, float esc) {
+  static_assert(EPI == EPI_STORE || EPI == EPI_GATEUP || EPI == EPI_DOWN_DGRAD, "transposed epilogues");
+  const int g = lane >> 5;
+  const float sc = esc * p.out_scale;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int pos = m0 + row0 + tm * 32 + (lane & 31);
+    const bool row_ok = FULL || pos < n_e;
+    const int64_t grow = rb + (FULL ? pos : min(pos, n_e - 1));
+    if constexpr (EPI == EPI_STORE) {
+      if (row_ok) {
+        uint16_t *__restrict__ out = p.out0 + grow * p.N;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = nt * BN + col0 + tn * 32 + 8 * q + 4 * g;
+            if (FULL || n < p.N) {
+              const uint32_t lo = f32_to_bf16(acc[tm][tn][4 * q] * sc) | (f32_to_bf16(acc[tm][tn][4 * q + 1] * sc) << 16);
+              const uint32_t hi = f32_to_bf16(acc[tm][tn][4 * q + 2] * sc) | (f32_to_bf16(acc[tm][tn][4 * q + 3] * sc) << 16);
+              *reinterpret_cast<uint2 *>(out + n) = make_uint2(lo, hi);
+            }
+          }
+      }
+    } else if constexpr (EPI == EPI_GATEUP) {
+      // each 64-column group of the tile: 32 gate columns (tile tn = 2 qq), then the
+      // matching 32 up columns (tn = 2 qq + 1)
+      if (row_ok) {
+#pragma unroll
+        for (int qq = 0; qq < TN / 2; ++qq)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = nt * (BN / 2) + col0 / 2 + qq * 32 + 8 * q + 4 * g;
+            if (FULL || i < p.I) {
+              float gv[4], uv[4];
+              uint32_t a2[2];
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                gv[t] = acc[tm][2 * qq][4 * q + t] * esc;
+                uv[t] = acc[tm][2 * qq + 1][4 * q + t] * esc;
+              }
+#pragma unroll
+              for (int t = 0; t < 2; ++t)
+                a2[t] = f32_to_bf16(gv[2 * t] * sigmoid_f(gv[2 * t]) * uv[2 * t]) |
+                        (f32_to_bf16(gv[2 * t + 1] * sigmoid_f(gv[2 * t + 1]) * uv[2 * t + 1]) << 16);
+              float *hrow = p.outf + grow * 2 * p.I;
+              *reinterpret_cast<float4 *>(hrow + i) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+              *reinterpret_cast<float4 *>(hrow + p.I + i) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+              *reinterpret_cast<uint2 *>(p.out1 + grow * p.I + i) = make_uint2(a2[0], a2[1]);
+            }
+          }
+      }
+    } else {  // EPI_DOWN_DGRAD: da = w * da_u, SwiGLU backward -> dh = [dg, du]
+      const float *__restrict__ hrow = p.h_in + grow * 2 * p.I;
+      const float w = p.tw[p.perm[grow]];
+      float4 gv[TN][4], uv[TN][4];
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          int i = nt * BN + col0 + tn * 32 + 8 * q + 4 * g;
+          i = (FULL || i < p.N) ? i : 0;
+          gv[tn][q] = *reinterpret_cast<const float4 *>(hrow + i);
+          uv[tn][q] = *reinterpret_cast<const float4 *>(hrow + p.I + i);
+        }
+      if (row_ok) {
+        uint16_t *__restrict__ out = p.out0 + grow * 2 * p.I;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int i = nt * BN + col0 + tn * 32 + 8 * q + 4 * g;
+            if (FULL || i < p.N) {
+              const float gg[4] = {gv[tn][q].x, gv[tn][q].y, gv[tn][q].z, gv[tn][q].w};
+              const float uu[4] = {uv[tn][q].x, uv[tn][q].y, uv[tn][q].z, uv[tn][q].w};
+              uint32_t dg2[2], du2[2];
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                float dgv[2], duv[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                  const int j = 2 * t + h;
+                  const float sg = sigmoid_f(gg[j]);
+                  const float da = w * (acc[tm][tn][4 * q + j] * esc);
+                  dgv[h] = da * uu[j] * sg * (1.0f + gg[j] * (1.0f - sg));
+                  duv[h] = da * gg[j] * sg;
+                }
+                dg2[t] = f32_to_bf16(dgv[0]) | (f32_to_bf16(dgv[1]) << 16);
+                du2[t] = f32_to_bf16(duv[0]) | (f32_to_bf16(duv[1]) << 16);
+              }
+              *reinterpret_cast<uint2 *>(out + i) = make_uint2(dg2[0], dg2[1]);
+              *reinterpret_cast<uint2 *>(out + p.I + i) = make_uint2(du2[0], du2[1]);
+            }
+          }
+      }
+    }
+  }
+}
+
+template <int TM, int TN, int BN, int EPI>
+__device__ __forceinline__ void epilogue_t(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0, int n_e,
+                                           int rb, int row0, int col0, int lane, float esc) {
+  const bool rows_in = m0 + row0 + TM * 32 <= n_e;
+  const bool cols_in = EPI == EPI_GATEUP ? nt * (BN / 2) + col0 / 2 + (TN / 2) * 32 <= p.I
+                                         : nt * BN + col0 + TN * 32 <= p.N;
+  if (rows_in && cols_in)
+    epilogue_t_body<TM, TN, BN, EPI, true>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+  else
+    epilogue_t_body<TM, TN, BN, EPI, false>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+}
+
 template <class C, int ASRC, int BSRC, int B2SRC, int EPI>
 __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
   constexpr int TM = C::TM, TN = C::TN, WN = C::WN, BN = C::BN, BMc = C::BM;
@@ -964,7 +1082,7 @@ __device__ __forceinline__ void mfmas(const bf16x8 (&af)[TM], const bf16x8 (&bf)
     if (VT != VT_DYN || tm < vt) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[tn], af[tm], acc[tm][tn], 0, 0, 0);
     }
   }
 }
@@ -1156,7 +1274,7 @@ __device__ __forceinline__ uint32_t dec_pair(const BCodes &b, int tn, int kk, in
 }
 
 __device__ __forceinline__ void mfma1(const bf16x8 &a, const u32x4 &b, f32x16 &acc) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), a, acc, 0, 0, 0);
 }
 
 #define FQ_PIN() __builtin_amdgcn_sched_barrier(0)
@@ -1660,7 +1778,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
     for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row(i), n_e - 1);
     seg_lora_n(p.s2, e, nt, p.N, arow2, sm, vt, acc);
   }
-  if (vt > 0) epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
+  if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
 }
 
 template <int ASRC, int EPI>
@@ -1734,22 +1852,19 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
     const float sb = p.s1.b_sd[e];
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-      float sc[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        sc[v] = sb;
-        const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (pos < n_e) {
-          const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
-          sc[v] = sb * p.s1.a_sd[src];
-        }
+      // the accumulator is transposed: lane L holds row L % 32 of the tile
+      float sc = sb;
+      const int pos = m0 + row0 + tm * 32 + (lane & 31);
+      if (pos < n_e) {
+        const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+        sc = sb * p.s1.a_sd[src];
       }
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           float x = acc[tm][tn][v];
-          scale_acc(x, sc[v]);
+          scale_acc(x, sc);
           acc[tm][tn][v] = x;
         }
     }
@@ -1762,7 +1877,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
     seg_lora<EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
   }
 
-  if (vt > 0) epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
+  if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
 }
 }  // namespace fq
 
