@@ -169,6 +169,122 @@ def token_sweep(shape, wgu, wdn, ev, sh, tokens=(438, 1024, 2048, 4096, 8192), r
     return rows
 
 
+def stage_bytes(s):
+    """Algorithmic HBM bytes of the memory-bound stages (R = T k routed rows; the LoRA
+    intermediates U and V are hi/lo bf16 pairs, 2r values per row; the LoRA weight
+    gradients are written in FP32)."""
+    T, R, H, I, r, E = s.T, s.T * s.k, s.H, s.I, s.r, s.E
+    uv = R * 2 * r * 2
+    return {
+        "lora_a_gu": R * H * 2 + E * r * H * 2 + uv,
+        "lora_a_dn": R * I * 2 + E * r * I * 2 + uv,
+        "lora_b_dn": R * H * 2 + E * H * r * 2 + uv,
+        "lora_b_gu": R * 2 * I * 2 + E * 2 * I * r * 2 + uv,
+        "combine_fwd": R * H * 2 + T * H * 2 + R * 8,
+        "combine_dgrad": R * H * 2 + T * H * 2 + R * 4,
+        "dtopk": T * H * 2 + R * H * 2 + R * 8,
+        "lora_grad": R * (2 * I + H + H + I) * 2 + 4 * uv + R * 4 + E * r * (2 * H + 3 * I) * 4,
+        "act_quant_x": T * H * (2 + 0.5 + 1 / 16) + T * 4,
+        "act_quant_a": R * I * (2 + 0.5 + 1 / 16) + R * 4,
+    }
+
+
+def time_layer(s, inp, wgu, wdn, ev, sh, steps, warmup):
+    """Time the layer step (route + fwd + dgrad + LoRA grads) of shape s over quantized
+    experts wgu / wdn: whole-step wall time over `steps` steps after `warmup`, and each
+    stage from hipEvents that the library records on the launch stream."""
+    import torch
+    import bit_quantized_moe_amd as bqm
+    dev = torch.device("cuda")
+    lora = dict(A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn, B_dn=inp.B_dn) if s.r else {}
+    d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, act_quant=int(s.act_quant), **lora)
+    ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+    idx = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(out)
+    dtw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    g = [torch.empty(sz, dtype=torch.float32, device=dev) for sz in
+         ((s.E, s.r, s.H), (s.E, 2 * s.I, s.r), (s.E, s.r, s.I), (s.E, s.H, s.r))] if s.r else [None] * 4
+
+    def step(events=None):
+        d.stage_events = C.addressof(events) if events is not None else None
+        bqm.bqm_route(inp.logits, s.T, s.E, s.k, 0, idx, tw)
+        bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
+        bqm.bqm_moe_dgrad(d, inp.dout, ws, dx, dtw)
+        if s.r:
+            bqm.bqm_lora_grad(d, inp.x, inp.dout, ws, *g)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [ev.create(2 * bqm.STAGE_COUNT) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / steps
+
+    stages = {}
+    for si, name in enumerate(bqm.STAGES):
+        if name.startswith("act_quant") and not s.act_quant:
+            continue
+        v = [ev.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]
+        v = [x for x in v if x is not None]
+        if v:
+            stages[name] = sum(v) / len(v)
+    sf = stage_flops(s)
+    sb = stage_bytes(s)
+    gemms = {k: v for k, v in stages.items() if k in ("gate_up_fwd", "down_fwd", "down_dgrad", "gate_up_dgrad")}
+    dom = max(gemms, key=gemms.get)
+    roof = {}
+    for k, v in stages.items():
+        if k in gemms:
+            roof[k] = {"bound": "mfma", "frac": round(sf[k] / (v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        elif k in sb:
+            roof[k] = {"bound": "hbm", "GB/s": round(sb[k] / (v * 1e-3) / 1e9, 1),
+                       "frac": round(sb[k] / (v * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    fl, fl_lora = layer_flops(s)
+    res = {
+        "tokens_per_s": s.T / (ms * 1e-3), "ms_per_step": ms,
+        "fwd_dgrad_tokens_per_s": s.T / (sum(v for k, v in stages.items() if k != "lora_grad") * 1e-3),
+        "layer_tflops": (fl + fl_lora) / (ms * 1e-3) / 1e12,
+        "dominant_gemm": dom, "dominant_ms": gemms[dom],
+        "dominant_tflops": sf[dom] / (gemms[dom] * 1e-3) / 1e12,
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stage_roofline": roof,
+    }
+    del d, ws, idx, tw, out, dx, dtw, g
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_calls(ev, sh, fn, reps=3):
+    """Mean hipEvent time of fn() over reps calls after one untimed call."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e = ev.create(2)
+    ev.record(e[0], sh)
+    for _ in range(reps):
+        fn()
+    ev.record(e[1], sh)
+    torch.cuda.synchronize()
+    return ev.elapsed_ms(e[0], e[1]) / reps
+
+
+def config_block(s, res, weights):
+    return {"workload": s.name, "E": s.E, "H": s.H, "I": s.I, "k": s.k, "T": s.T, "r": s.r,
+            "weights": weights, "act_quant": bool(s.act_quant), "routing": s.logits,
+            "tokens_per_s": res["tokens_per_s"], "ms_per_step": res["ms_per_step"],
+            "fwd_dgrad_tokens_per_s": res["fwd_dgrad_tokens_per_s"], "layer_tflops": res["layer_tflops"],
+            "dominant_gemm": res["dominant_gemm"],
+            "dominant_frac": res["dominant_tflops"] / PEAK_BF16_TFLOPS,
+            "stages_ms": res["stages_ms"], "stage_roofline": res["stage_roofline"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +292,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantizer", action="store_true")
+    ap.add_argument("--main-only", action="store_true",
+                    help="only the GLM NVFP4 layer step (and the quantizer unless --no-quantizer): no NF4, "
+                         "W4A4 or format-conversion figures")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the layer step at smaller token counts (extra kernel calls at other sizes)")
     ap.add_argument("--no-sweep", action="store_true", help=argparse.SUPPRESS)  # the default
@@ -210,9 +329,12 @@ def main():
     ev = HipEvents()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    n_el = s.E * (2 * s.I * s.H + s.H * s.I)
+    conv_bytes = n_el * (2 + 0.5 + 1 / 16)    # bf16 <-> 4-bit codes + 1 scale byte (or 1/4 float) per 16
 
     # --- quantizer (per load): gate_up + down stacks, timed with events ---
     quant = None
+    formats = {}
     if not args.no_quantizer:
         qgu = bqm.alloc_qtensor(bqm.FMT_NVFP4, s.E, 2 * s.I, s.H, device=dev)
         qdn = bqm.alloc_qtensor(bqm.FMT_NVFP4, s.E, s.H, s.I, device=dev)
@@ -231,73 +353,33 @@ def main():
                     times.append(ev.elapsed_ms(e[0], e[1]))
             return sum(times) / len(times)
 
-        n_el = s.E * (2 * s.I * s.H + s.H * s.I)
-        qbytes = n_el * (2 + 0.5 + 1 / 16)
         qms = time_quant(None, None)
         # the same quantization with the per-tensor scales handed in (frozen weights
         # re-quantized with known scales): one read of the input instead of two
         sd_gu, sd_dn = qgu.s_dec.clone(), qdn.s_dec.clone()
         gms = time_quant(sd_gu, sd_dn)
         quant = {"workload": "gate_up [256,4096,6144] + down [256,6144,2048] bf16 -> NVFP4 4/6",
-                 "ms": qms, "GB/s": qbytes / qms / 1e6, "hbm_frac": qbytes / qms / 1e6 / PEAK_HBM_GBS,
-                 "algorithmic_bytes": qbytes,
+                 "ms": qms, "GB/s": conv_bytes / qms / 1e6, "hbm_frac": conv_bytes / qms / 1e6 / PEAK_HBM_GBS,
+                 "algorithmic_bytes": conv_bytes,
                  "note": "per-tensor scale from the stack's own amax: the input is read twice (amax pass, "
                          "then quantize pass); algorithmic bytes count one read",
-                 "given_scale": {"ms": gms, "GB/s": qbytes / gms / 1e6,
-                                 "hbm_frac": qbytes / gms / 1e6 / PEAK_HBM_GBS}}
+                 "given_scale": {"ms": gms, "GB/s": conv_bytes / gms / 1e6,
+                                 "hbm_frac": conv_bytes / gms / 1e6 / PEAK_HBM_GBS}}
         wgu, wdn = qgu, qdn
+        del wsq
     else:
         wgu = quantize_stack_gpu(inp.w_gu, "nvfp4")
         wdn = quantize_stack_gpu(inp.w_dn, "nvfp4")
-    lora = dict(A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn, B_dn=inp.B_dn)
-    d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, **lora)
-    ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
-    idx = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
-    tw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
-    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
-    dx = torch.empty_like(out)
-    dtw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
-    g = [torch.empty(sz, dtype=torch.float32, device=dev) for sz in
-         ((s.E, s.r, s.H), (s.E, 2 * s.I, s.r), (s.E, s.r, s.I), (s.E, s.H, s.r))]
 
-    def step(events=None):
-        d.stage_events = C.addressof(events) if events is not None else None
-        bqm.bqm_route(inp.logits, s.T, s.E, s.k, 0, idx, tw)
-        bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
-        bqm.bqm_moe_dgrad(d, inp.dout, ws, dx, dtw)
-        bqm.bqm_lora_grad(d, inp.x, inp.dout, ws, *g)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [ev.create(2 * bqm.STAGE_COUNT) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-
-    stages = {}
-    ran = [n for n in bqm.STAGES if s.act_quant or not n.startswith("act_quant")]
-    for si, name in enumerate(bqm.STAGES):
-        if name not in ran:
-            continue
-        v = [ev.elapsed_ms(e[2 * si], e[2 * si + 1]) for e in evs]
-        v = [x for x in v if x is not None]
-        if v:
-            stages[name] = sum(v) / len(v)
+    res = time_layer(s, inp, wgu, wdn, ev, sh, args.steps, args.warmup)
     sf = stage_flops(s)
-    gemms = {k: v for k, v in stages.items() if k in ("gate_up_fwd", "down_fwd", "down_dgrad", "gate_up_dgrad")}
-    dom = max(gemms, key=gemms.get)
-    ach = sf[dom] / (gemms[dom] * 1e-3) / 1e12
-    fl, fl_lora = layer_flops(s)
+    dom = res["dominant_gemm"]
+    ach = res["dominant_tflops"]
     result = {
         "metric": "NVFP4 MoE layer fwd+dgrad tokens/s (GLM-5.2 shape); quantizer GB/s",
-        "value": s.T / (ms * 1e-3),
+        "value": res["tokens_per_s"],
         "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "glm5.2-moe-layer-train-step", "E": s.E, "H": s.H, "I": s.I, "k": s.k,
@@ -305,14 +387,57 @@ def main():
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dom),
-                     "algorithmic_flop_per_launch": sf[dom], "launch_ms": gemms[dom]},
-        "layer_tflops": (fl + fl_lora) / (ms * 1e-3) / 1e12,
-        "fwd_dgrad_tokens_per_s": s.T / (sum(v for k, v in stages.items() if k != "lora_grad") * 1e-3),
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+                     "algorithmic_flop_per_launch": sf[dom], "launch_ms": res["dominant_ms"]},
+        "layer_tflops": res["layer_tflops"],
+        "fwd_dgrad_tokens_per_s": res["fwd_dgrad_tokens_per_s"],
+        "stages_ms": res["stages_ms"],
+        "stage_roofline": res["stage_roofline"],
         "quantizer": quant,
     }
+
+    if not args.main_only:
+        # --- format conversions on the same stacks: NVFP4 dequantize, NF4 quantize / dequantize ---
+        ybuf = torch.empty_like(inp.w_gu)
+        ydn = ybuf.view(-1)[: inp.w_dn.numel()].view(inp.w_dn.shape)
+        if not args.no_quantizer:
+            ms = time_calls(ev, sh, lambda: (bqm.bqm_dequantize(wgu, ybuf), bqm.bqm_dequantize(wdn, ydn)))
+            formats["nvfp4_dequantize"] = {"ms": ms, "GB/s": conv_bytes / ms / 1e6,
+                                           "hbm_frac": conv_bytes / ms / 1e6 / PEAK_HBM_GBS}
+        ngu = bqm.alloc_qtensor(bqm.FMT_NF4, s.E, 2 * s.I, s.H, device=dev)
+        ndn = bqm.alloc_qtensor(bqm.FMT_NF4, s.E, s.H, s.I, device=dev)
+        nf4_bytes = n_el * (2 + 0.5 + 4 / 64)
+        ms = time_calls(ev, sh, lambda: (bqm.bqm_quantize_nf4(inp.w_gu, ngu), bqm.bqm_quantize_nf4(inp.w_dn, ndn)))
+        formats["nf4_quantize"] = {"ms": ms, "GB/s": nf4_bytes / ms / 1e6,
+                                   "hbm_frac": nf4_bytes / ms / 1e6 / PEAK_HBM_GBS}
+        ms = time_calls(ev, sh, lambda: (bqm.bqm_dequantize(ngu, ybuf), bqm.bqm_dequantize(ndn, ydn)))
+        formats["nf4_dequantize"] = {"ms": ms, "GB/s": nf4_bytes / ms / 1e6,
+                                     "hbm_frac": nf4_bytes / ms / 1e6 / PEAK_HBM_GBS}
+        formats["workload"] = "gate_up [256,4096,6144] + down [256,6144,2048]; bytes = 2 (bf16) + 0.5 (codes) " \
+                              "+ scale bytes per element"
+        result["formats"] = formats
+        del ybuf, ydn
+        torch.cuda.empty_cache()
+
+        # --- the other layer workloads: GLM shape over NF4 experts with skewed routing
+        # (16 experts empty), and the Qwen3-30B-A3B shape with NVFP4 activations (W4A4) ---
+        others = {}
+        s5 = synth.GLM_NF4
+        inp5 = synth.layer_inputs(s5, device=dev, with_weights=False)
+        r5 = time_layer(s5, inp5, ngu, ndn, ev, sh, max(3, args.steps // 2), 2)
+        others["glm_nf4_zipf"] = config_block(s5, r5, "nf4-blocksize64")
+        del inp5, ngu, ndn
+        torch.cuda.empty_cache()
+        s3 = synth.QWEN
+        inp3 = synth.layer_inputs(s3, device=dev)
+        q3gu = quantize_stack_gpu(inp3.w_gu, "nvfp4")
+        q3dn = quantize_stack_gpu(inp3.w_dn, "nvfp4")
+        r3 = time_layer(s3, inp3, q3gu, q3dn, ev, sh, max(3, args.steps), 2)
+        others["qwen3_30b_a3b_w4a4"] = config_block(s3, r3, "nvfp4-4over6-rowwise, activations nvfp4 per token")
+        del inp3, q3gu, q3dn
+        torch.cuda.empty_cache()
+        result["other_configs"] = others
+
     if args.sweep:
-        del ws
         torch.cuda.empty_cache()
         result["token_sweep"] = token_sweep(shape, wgu, wdn, ev, sh)
     if not args.no_cpu_baseline:

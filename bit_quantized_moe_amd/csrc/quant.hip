@@ -277,107 +277,183 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
   }
 }
 
-// NVFP4 dequantize: bf16(fl(fl(val*sb) * s_dec)); one thread per 16-block.
-__global__ void __launch_bounds__(kThreads) nvfp4_dequant(const uint2 *__restrict__ codes,
+// ---------------------------------------------------------------------------
+// Dequantizers and the NF4 quantizer: one lane per 8 consecutive elements (one
+// 32-bit word of codes, 16 bytes of bf16), so every load and store instruction
+// of a wave covers contiguous memory; a workgroup takes kDqUnits consecutive
+// 8-element units.
+// ---------------------------------------------------------------------------
+constexpr int kDqIter = 4;
+constexpr int64_t kDqUnits = (int64_t)kDqIter * kThreads;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> bf16 pair (a in the low half), round to nearest even
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Segment (a run of seg_units units sharing one decode scale) of unit u, for the
+// units of one workgroup: seg0 is the segment of its first unit, `first` that
+// segment's first unit, so u - first < kDqUnits + seg_units.
+__device__ __forceinline__ int64_t seg_of(int64_t u, int64_t seg0, int64_t first, int64_t seg_units) {
+  const uint32_t off = (uint32_t)(u - first);
+  if (seg_units >= kDqUnits) return seg0 + (off >= (uint32_t)seg_units ? 1 : 0);
+  return seg0 + off / (uint32_t)seg_units;
+}
+
+// byte P of a code word: elements 2P (low nibble) and 2P+1, decoded with their sign
+// (a zero magnitude with the sign bit set gives -0) and scaled: fl(fl(v * sb) * sd)
+// with v * sb exact
+template <int P>
+__device__ __forceinline__ uint32_t nvfp4_dq_pair(uint32_t c, float sb, float sd) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, P);
+  return pack_bf16_rne((v.x * sb) * sd, (v.y * sb) * sd);
+}
+
+// NVFP4 dequantize: bf16(fl(fl(val * sb) * s_dec)).  seg_units: units per s_dec
+// (a whole matrix, or one row in per-row mode).
+__global__ void __launch_bounds__(kThreads) nvfp4_dequant(const uint32_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
-                                                          const float *__restrict__ s_dec,
-                                                          int64_t nblocks, int64_t blocks_per_scale,
-                                                          uint4 *__restrict__ y) {
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-       blk += (int64_t)gridDim.x * kThreads) {
-    uint2 c = codes[blk];
-    float sb = e4m3_to_f32(scales[blk]);
-    float sd = s_dec[blk / blocks_per_scale];
-    uint32_t out[8];
+                                                          const float *__restrict__ s_dec, int64_t nunits,
+                                                          int64_t seg_units, uint4 *__restrict__ y) {
+  const int64_t base = (int64_t)blockIdx.x * kDqUnits;
+  const int64_t seg0 = base / seg_units, first = seg0 * seg_units;
+  uint32_t c[kDqIter];
+  uint32_t sbc[kDqIter];
+  float sd[kDqIter];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      uint32_t nib = ((i < 8 ? c.x : c.y) >> (4 * (i & 7))) & 0xFu;
-      float v = __uint_as_float(e2m1_mag_bits(nib & 7u) | ((nib & 8u) << 28));
-      float r = (v * sb) * sd;
-      uint32_t b = f32_to_bf16(r);
-      if (i & 1)
-        out[i >> 1] |= b << 16;
-      else
-        out[i >> 1] = b;
+  for (int it = 0; it < kDqIter; ++it) {
+    const int64_t u0 = base + it * kThreads + threadIdx.x;
+    const int64_t u = u0 < nunits ? u0 : nunits - 1;
+    c[it] = codes[u];
+    sbc[it] = scales[u >> 1];
+    sd[it] = s_dec[seg_of(u, seg0, first, seg_units)];
+  }
+#pragma unroll
+  for (int it = 0; it < kDqIter; ++it) {
+    const int64_t u = base + it * kThreads + threadIdx.x;
+    if (u < nunits) {
+      const float sb = __builtin_amdgcn_cvt_f32_fp8(sbc[it], 0);
+      y[u] = make_uint4(nvfp4_dq_pair<0>(c[it], sb, sd[it]), nvfp4_dq_pair<1>(c[it], sb, sd[it]),
+                        nvfp4_dq_pair<2>(c[it], sb, sd[it]), nvfp4_dq_pair<3>(c[it], sb, sd[it]));
     }
-    y[2 * blk] = make_uint4(out[0], out[1], out[2], out[3]);
-    y[2 * blk + 1] = make_uint4(out[4], out[5], out[6], out[7]);
   }
 }
 
 __constant__ float c_nf4_levels[16] = BQM_NF4_LEVELS;
 __constant__ float c_nf4_mids[15] = BQM_NF4_MIDPOINTS;
 
-// NF4 quantize: one thread per 64-block (128 B in, 32 B codes + 4 B absmax out).
-__global__ void __launch_bounds__(kThreads) nf4_quant(const uint4 *__restrict__ x, int64_t nblocks,
-                                                      uint4 *__restrict__ codes,
-                                                      float *__restrict__ absmax) {
-  float mids[15];
-#pragma unroll
-  for (int j = 0; j < 15; ++j) mids[j] = c_nf4_mids[j];
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-       blk += (int64_t)gridDim.x * kThreads) {
-    uint32_t w[32];
-    const uint4 *p = x + 8 * blk;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint4 v = p[i];
-      w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+// NF4 code of xn = #{j : xn > mid_j} from one table entry: bucket b = trunc(64 xn + 64)
+// clamped to [0, 127] covers xn in about [b/64 - 1, (b+1)/64 - 1]; entry b holds the
+// number of midpoints below that range (widened by kNf4Margin, far more than the
+// rounding of the bucket arithmetic) and the one midpoint inside it, or +inf.  The
+// midpoints are at least 0.08 apart, so no widened range holds two.
+constexpr float kNf4Margin = 1e-5f;
+
+__device__ __forceinline__ void fill_nf4_table(uint2 *tbl) {
+  if (threadIdx.x < 128) {
+    const int b = threadIdx.x;
+    const float lo = b == 0 ? -INFINITY : (float)(b - 64) / 64.0f - kNf4Margin;
+    const float hi = b == 127 ? INFINITY : (float)(b - 63) / 64.0f + kNf4Margin;
+    uint32_t below = 0;
+    float inside = INFINITY;
+    for (int j = 0; j < 15; ++j) {
+      const float m = c_nf4_mids[j];
+      if (m < lo)
+        ++below;
+      else if (m <= hi)
+        inside = m;
     }
+    tbl[b] = make_uint2(below, __float_as_uint(inside));
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t nf4_code(float xn, const uint2 *tbl) {
+  int b = (int)__builtin_fmaf(xn, 64.0f, 64.0f);
+  b = b < 0 ? 0 : (b > 127 ? 127 : b);
+  const uint2 t = tbl[b];
+  return t.x + (xn > __uint_as_float(t.y) ? 1u : 0u);
+}
+
+// NF4 quantize: 8 lanes per 64-block (absmax reduced across them), each lane
+// codes its 8 elements into one word.
+__global__ void __launch_bounds__(kThreads) nf4_quant(const uint4 *__restrict__ x, int64_t nunits,
+                                                      uint32_t *__restrict__ codes, float *__restrict__ absmax) {
+  __shared__ uint2 tbl[128];
+  fill_nf4_table(tbl);
+  const int64_t base = (int64_t)blockIdx.x * kDqUnits;
+  uint4 v[kDqIter];
+#pragma unroll
+  for (int it = 0; it < kDqIter; ++it) {
+    const int64_t u0 = base + it * kThreads + threadIdx.x;
+    v[it] = x[u0 < nunits ? u0 : nunits - 1];
+  }
+#pragma unroll
+  for (int it = 0; it < kDqIter; ++it) {
+    const int64_t u = base + it * kThreads + threadIdx.x;
+    const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
     uint32_t mx = 0u;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      uint32_t a = absmax_bits_u32(w[i]);
-      mx = mx > a ? mx : a;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t m = absmax_bits_u32(w[i]);
+      mx = mx > m ? mx : m;
     }
-    float a = __uint_as_float(mx << 16);
-    float r = a > 0.0f ? 1.0f / a : 0.0f;
-    uint32_t out[8];
+    // nunits is a multiple of 8, so an 8-lane group is entirely in range or entirely out
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
-      float xv = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
-      float xn = xv * r;
-      uint32_t code = 0u;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) code += xn > mids[j] ? 1u : 0u;
-      if ((i & 7) == 0)
-        out[i >> 3] = code;
-      else
-        out[i >> 3] |= code << (4 * (i & 7));
+    for (int o = 1; o < 8; o <<= 1) {
+      const uint32_t t = __shfl_xor(mx, o, 64);
+      mx = mx > t ? mx : t;
     }
-    codes[2 * blk] = make_uint4(out[0], out[1], out[2], out[3]);
-    codes[2 * blk + 1] = make_uint4(out[4], out[5], out[6], out[7]);
-    absmax[blk] = a;
+    const float a = __uint_as_float(mx << 16);
+    const float r = a > 0.0f ? 1.0f / a : 0.0f;
+    uint32_t code = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xv = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+      code |= nf4_code(xv * r, tbl) << (4 * i);
+    }
+    if (u < nunits) {
+      codes[u] = code;
+      if ((threadIdx.x & 7) == 0) absmax[u >> 3] = a;
+    }
   }
 }
 
 // NF4 dequantize: bf16(fl(level[code] * absmax)).
-__global__ void __launch_bounds__(kThreads) nf4_dequant(const uint4 *__restrict__ codes,
-                                                        const float *__restrict__ absmax,
-                                                        int64_t nblocks, uint4 *__restrict__ y) {
+__global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restrict__ codes,
+                                                        const float *__restrict__ absmax, int64_t nunits,
+                                                        uint4 *__restrict__ y) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = c_nf4_levels[threadIdx.x];
   __syncthreads();
-  for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblocks;
-       blk += (int64_t)gridDim.x * kThreads) {
-    uint4 c0 = codes[2 * blk], c1 = codes[2 * blk + 1];
-    uint32_t c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-    float a = absmax[blk];
+  const int64_t base = (int64_t)blockIdx.x * kDqUnits;
+  uint32_t c[kDqIter];
+  float a[kDqIter];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+  for (int it = 0; it < kDqIter; ++it) {
+    const int64_t u0 = base + it * kThreads + threadIdx.x;
+    const int64_t u = u0 < nunits ? u0 : nunits - 1;
+    c[it] = codes[u];
+    a[it] = absmax[u >> 3];
+  }
+#pragma unroll
+  for (int it = 0; it < kDqIter; ++it) {
+    const int64_t u = base + it * kThreads + threadIdx.x;
+    if (u < nunits) {
       uint32_t o[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t b = f32_to_bf16(lv[(c[q] >> (4 * i)) & 0xFu] * a);
-        if (i & 1)
-          o[i >> 1] |= b << 16;
-        else
-          o[i >> 1] = b;
-      }
-      y[8 * blk + q] = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int p = 0; p < 4; ++p)
+        o[p] = pack_bf16_rne(lv[(c[it] >> (8 * p)) & 0xFu] * a[it], lv[(c[it] >> (8 * p + 4)) & 0xFu] * a[it]);
+      y[u] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
+
+// workgroups for n elements in units of 8, kDqUnits units each
+int dq_grid(int64_t n) { return (int)((n / 8 + kDqUnits - 1) / kDqUnits); }
 
 int grid_for(int64_t work_items, int per_block = kThreads, int cap = 65536) {
   int64_t g = (work_items + per_block - 1) / per_block;
@@ -491,9 +567,9 @@ extern "C" bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out, void
   if (n == 0) return BQM_OK;
   BQM_REQUIRE(x, BQM_ERR_INVALID_ARG, "bqm_quantize_nf4: x is NULL");
   BQM_REQUIRE(aligned16(x), BQM_ERR_ALIGN, "bqm_quantize_nf4: x not 16-byte aligned");
-  const int64_t nb = n / 64;
-  nf4_quant<<<grid_for(nb), kThreads, 0, as_stream(stream)>>>(
-      reinterpret_cast<const uint4 *>(x), nb, reinterpret_cast<uint4 *>(out->codes),
+  BQM_REQUIRE(n / 8 / kDqUnits < INT32_MAX, BQM_ERR_SHAPE, "bqm_quantize_nf4: tensor too large");
+  nf4_quant<<<dq_grid(n), kThreads, 0, as_stream(stream)>>>(
+      reinterpret_cast<const uint4 *>(x), n / 8, reinterpret_cast<uint32_t *>(out->codes),
       reinterpret_cast<float *>(out->scales));
   return launch_status("nf4_quant");
 }
@@ -505,19 +581,18 @@ extern "C" bqm_status bqm_dequantize(const bqm_qtensor *q, uint16_t *y, void *st
   if (n == 0) return BQM_OK;
   BQM_REQUIRE(y, BQM_ERR_INVALID_ARG, "bqm_dequantize: y is NULL");
   BQM_REQUIRE(aligned16(y), BQM_ERR_ALIGN, "bqm_dequantize: y not 16-byte aligned");
+  BQM_REQUIRE(n / 8 / kDqUnits < INT32_MAX, BQM_ERR_SHAPE, "bqm_dequantize: tensor too large");
   hipStream_t s = as_stream(stream);
   if (q->fmt == BQM_FMT_NVFP4) {
-    const int64_t nb = n / 16;
-    const int64_t per_scale =
-        q->scale_mode == BQM_SCALE_PER_ROW ? q->cols / 16 : q->rows * q->cols / 16;
-    nvfp4_dequant<<<grid_for(nb), kThreads, 0, s>>>(
-        reinterpret_cast<const uint2 *>(q->codes), reinterpret_cast<const uint8_t *>(q->scales),
-        q->s_dec, nb, per_scale, reinterpret_cast<uint4 *>(y));
+    const int64_t seg_units = q->scale_mode == BQM_SCALE_PER_ROW ? q->cols / 8 : q->rows * q->cols / 8;
+    BQM_REQUIRE(seg_units < (int64_t)1 << 31, BQM_ERR_SHAPE, "bqm_dequantize: matrix too large");
+    nvfp4_dequant<<<dq_grid(n), kThreads, 0, s>>>(
+        reinterpret_cast<const uint32_t *>(q->codes), reinterpret_cast<const uint8_t *>(q->scales), q->s_dec,
+        n / 8, seg_units, reinterpret_cast<uint4 *>(y));
     return launch_status("nvfp4_dequant");
   }
-  const int64_t nb = n / 64;
-  nf4_dequant<<<grid_for(nb), kThreads, 0, s>>>(reinterpret_cast<const uint4 *>(q->codes),
-                                               reinterpret_cast<const float *>(q->scales), nb,
-                                               reinterpret_cast<uint4 *>(y));
+  nf4_dequant<<<dq_grid(n), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(q->codes),
+                                              reinterpret_cast<const float *>(q->scales), n / 8,
+                                              reinterpret_cast<uint4 *>(y));
   return launch_status("nf4_dequant");
 }

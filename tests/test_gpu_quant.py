@@ -124,6 +124,56 @@ def test_nf4_quantize_dequantize_bit_exact(shape):
     assert (np_f32(y).view(np.uint32) == oq.dequantize_nf4(ref).view(np.uint32)).all()
 
 
+def test_nf4_codes_at_midpoints_and_bucket_edges():
+    """NF4 coding near its decision points: in blocks whose absmax is 1 (so x / absmax
+    is x), every midpoint between two levels, its bf16 neighbours, every multiple of
+    1/64 in [-1, 1] and their bf16 neighbours; the same blocks scaled by 2^-7, and by -3."""
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    mids = fm.nf4_midpoints().astype(np.float32)
+    grid = (np.arange(-64, 65, dtype=np.float32) / 64.0).astype(np.float32)
+    pts = np.concatenate([mids, grid]).astype(np.float32)
+    b = fm.bf16_rne_bits(pts).astype(np.int64)
+    vals = fm.bf16_bits_to_f32(np.concatenate([b - 1, b, b + 1]).astype(np.uint16))
+    vals = vals[(np.abs(vals) <= 1.0) & ((vals == 0) | (np.abs(vals) >= 2.0 ** -60))]   # no bf16 subnormals
+    per = 63                                        # the 64th element of each block is its absmax, 1
+    nblk = -(-vals.size // per)
+    v = np.zeros(nblk * per, dtype=np.float32)
+    v[:vals.size] = vals
+    blocks = np.concatenate([v.reshape(nblk, per), np.ones((nblk, 1), np.float32)], axis=1)
+    # (the third copy, times -3, is rounded to bf16: near the decision points, not on them)
+    x = np.concatenate([blocks, blocks * np.float32(2.0 ** -7), fm.bf16_round(-blocks * np.float32(3.0))], axis=0)
+    x = x.reshape(1, -1, 64)
+    log(f"nf4 decision points: {x.size} elements")
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(xt.float().numpy(), x)    # every value is a bf16
+    q = bqm.alloc_qtensor(bqm.FMT_NF4, *x.shape, device=dev)
+    bqm.bqm_quantize_nf4(xt.to(dev), q)
+    ref = oq.quantize_nf4(x)
+    assert (np_u8(q.codes) == ref.codes).all()
+    assert (np_f32(q.scales) == ref.absmax).all()
+
+
+@pytest.mark.parametrize("shape,per_row", [((3, 64, 256), False), ((3, 37, 272), False), ((2, 37, 272), True),
+                                           ((1, 1, 16), False), ((2, 1024, 1024), False)])
+def test_nvfp4_dequantize_shapes(shape, per_row):
+    """Dequantize when a matrix spans many workgroups, when a workgroup spans many rows,
+    and with a total that is not a multiple of a workgroup's share."""
+    import torch
+    dev = gpu()
+    log(f"nvfp4 dequantize {shape} per_row={per_row}")
+    x = synth.normal(shape, 0.02, (95, shape[1], shape[2]), device="cpu", outliers=True).to(dev)
+    q = gpu_quant_nvfp4(x, per_row=per_row)
+    y = torch.empty_like(x)
+    _bqm().bqm_dequantize(q, y)
+    n = shape[0]
+    ref = oq.dequantize_nvfp4(oq.NVFP4Tensor(np_u8(q.codes), np_u8(q.scales),
+                                             np_f32(q.s_dec).reshape((n, -1) if per_row else (-1,)),
+                                             True, per_row))
+    assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
+
+
 @pytest.mark.parametrize("T,E,k,kind", [(64, 8, 2, "normal"), (1000, 256, 8, "uniform"),
                                         (333, 128, 8, "ties"), (50, 64, 16, "zipf"), (1, 1, 1, "normal")])
 def test_route_and_permute_bit_exact(T, E, k, kind):
