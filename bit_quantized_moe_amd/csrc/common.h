@@ -31,6 +31,16 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bqm_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float bqm_f32x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> bf16 pair (a in the low half), round to nearest even (one
+// v_cvt_pk_bf16_f32; the same bits as f32_to_bf16 for finite inputs)
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const bqm_f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bqm_bf16x2));
+}
+
 // E4M3FN code (0..126) -> float
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   return c < 8u ? (float)c * 0x1p-9f : __uint_as_float((c + 960u) << 20);

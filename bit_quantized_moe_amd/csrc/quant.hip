@@ -286,14 +286,6 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
 constexpr int kDqIter = 4;
 constexpr int64_t kDqUnits = (int64_t)kDqIter * kThreads;
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// two floats -> bf16 pair (a in the low half), round to nearest even
-__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
 // Segment (a run of seg_units units sharing one decode scale) of unit u, for the
 // units of one workgroup: seg0 is the segment of its first unit, `first` that
 // segment's first unit, so u - first < kDqUnits + seg_units.
