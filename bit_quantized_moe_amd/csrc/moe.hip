@@ -39,15 +39,17 @@ constexpr int BK = 64;        // K step (one NF4 block, four NVFP4 blocks)
 constexpr int SK = BK + 8;    // LDS row stride in bf16 (16-byte pad)
 constexpr int NTHR = 256;
 
+// A operand rows: bf16 activations gathered by token (A_GATHER) or in routed order
+// (A_ROWS); the _Q forms are per-row NVFP4 activations expanded to bf16 val * sb
+// (exact), whose per-row decode scales (Seg::a_sd) multiply the accumulator.
 enum ASrc { A_GATHER = 0, A_ROWS = 1, A_GATHER_Q = 2, A_ROWS_Q = 3 };
 enum BSrc { B_Q4_K = 0, B_Q4_N = 1, B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
 enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_F32 = 3, EPI_STORE_SPLIT = 4 };
 
 // One K segment of a contraction: A rows times one expert slice of a B stack.
 struct Seg {
-  const void *a;        // bf16 rows, or NVFP4 codes of per-row quantized rows
-  const uint8_t *a_sc;  // A E4M3 scales (quantized A)
-  const float *a_sd;    // A per-row decode scales (quantized A)
+  const void *a;        // bf16 rows
+  const float *a_sd;    // per-row decode scales of the _Q sources
   int64_t a_ld;         // elements per A row
   const void *b;        // B stack: 4-bit codes or bf16
   const void *b_sc;     // NVFP4 E4M3 scales / NF4 absmax
@@ -194,53 +196,24 @@ struct ARegs {
 template <class C, int ASRC>
 __device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[C::ACH], int k0, ARegs<C> &r) {
   const int tid = threadIdx.x;
-  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
 #pragma unroll
-    for (int i = 0; i < C::ACH; ++i) {
-      const int c = tid + C::NTHR * i;
-      const int kk = k0 + (c & 7) * 8;
-      if (arow[i] >= 0 && kk < s.K)
-        r.v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.a) + arow[i] * s.a_ld + kk);
-      else
-        r.v[i] = make_uint4(0, 0, 0, 0);
-    }
-  } else {
-    // per-row quantized rows: thread -> (row = tid/2, 32 elements): 16 B codes + 2 scale bytes
-    static_assert(C::NTHR == 2 * C::BM, "quantized A needs two threads per row");
-    const int half = tid & 1;
-    if (arow[0] >= 0) {
-      const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.a) + arow[0] * (s.a_ld / 2) + (k0 + half * 32) / 2;
-      r.v[0] = *reinterpret_cast<const uint4 *>(cp);
-      const uint8_t *sp = s.a_sc + arow[0] * (s.a_ld / 16) + (k0 + half * 32) / 16;
-      r.v[1].x = sp[0];
-      r.v[1].y = sp[1];
-    } else {
-      r.v[0] = make_uint4(0, 0, 0, 0);
-      r.v[1].x = r.v[1].y = 0;
-    }
+  for (int i = 0; i < C::ACH; ++i) {
+    const int c = tid + C::NTHR * i;
+    const int kk = k0 + (c & 7) * 8;
+    if (arow[i] >= 0 && kk < s.K)
+      r.v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.a) + arow[i] * s.a_ld + kk);
+    else
+      r.v[i] = make_uint4(0, 0, 0, 0);
   }
 }
 
 template <class C, int ASRC>
 __device__ __forceinline__ void a_store(uint16_t *As, const ARegs<C> &r) {
   const int tid = threadIdx.x;
-  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
 #pragma unroll
-    for (int i = 0; i < C::ACH; ++i) {
-      const int c = tid + C::NTHR * i;
-      *reinterpret_cast<uint4 *>(As + (c >> 3) * SK + (c & 7) * 8) = r.v[i];
-    }
-  } else {
-    const int row = tid >> 1, half = tid & 1;
-    const uint32_t cw[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-    uint4 *dst = reinterpret_cast<uint4 *>(As + row * SK + half * 32);
-    const float s0 = e4m3_hw<0>(r.v[1].x), s1 = e4m3_hw<0>(r.v[1].y);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t o[4];
-      fp4x8_hw(cw[q], q < 2 ? s0 : s1, o);
-      dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
+  for (int i = 0; i < C::ACH; ++i) {
+    const int c = tid + C::NTHR * i;
+    *reinterpret_cast<uint4 *>(As + (c >> 3) * SK + (c & 7) * 8) = r.v[i];
   }
 }
 
@@ -794,7 +767,7 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
   int64_t arow[C::ACH];
 #pragma unroll
   for (int i = 0; i < C::ACH; ++i) {
-    const int row = (ASRC == A_GATHER_Q || ASRC == A_ROWS_Q) ? (tid >> 1) : ((tid + C::NTHR * i) >> 3);
+    const int row = (tid + C::NTHR * i) >> 3;
     const int pos = m0 + row;
     if (pos >= n_e)
       arow[i] = -1;
@@ -869,8 +842,8 @@ __device__ __forceinline__ void scale_acc(float &x, float s) {
       : "v"(s));
 }
 
-// valid 32-row tiles of a wave: all, or a run-time count (ragged tail)
-constexpr int VT_ALL = 1000, VT_DYN = -1;
+// valid 32-row tiles of a wave: a run-time count (ragged tail)
+constexpr int VT_DYN = -1;
 
 // ---------------------------------------------------------------------------
 // Forward grouped GEMM over K-major NVFP4 weights (gate_up and down forward)
@@ -953,40 +926,7 @@ __device__ __forceinline__ void dma_b32(const void *g, uint32_t lds) {
 __device__ __forceinline__ void dma_b128(const void *g, const void *lds) { dma_b128(g, lds_addr(lds)); }
 __device__ __forceinline__ void dma_b32(const void *g, const void *lds) { dma_b32(g, lds_addr(lds)); }
 
-// bf16 A rows of K step k0 -> stage As (direct-to-LDS; no registers)
-__device__ __forceinline__ void a_dma(const Seg &s, const int64_t (&arow)[ACH], int k0, uint16_t *As) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
-#pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int r = 64 * w + 8 * j + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);  // the chunk that lands at this lane's position
-    dma_b128(a + arow[j] * s.a_ld + k0 + 8 * c, As + (64 * w + 8 * j) * BK);
-  }
-}
-
-// NVFP4 weight tile of K step k0: 256 columns x 32 code bytes and 4 scale bytes
-template <int EPI>
-__device__ __forceinline__ void b_dma(const Seg &s, int e, int nt, int N, int I, int k0, uint8_t *Bs, uint32_t *Ss) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t slice = s.b_rows * s.b_cols;
-  const uint8_t *codes = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + k0 / 2;
-  const uint8_t *scales = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) + k0 / 16;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ins = 2 * w + j;  // 32 columns x 32 bytes per instruction
-    const int col = ins * 32 + (lane >> 1);
-    int64_t wr = b_row_of_col<EPI, BN>(col, nt, N, I);
-    wr = wr < 0 ? 0 : wr;
-    dma_b128(codes + wr * (s.b_cols / 2) + 16 * (lane & 1), Bs + ins * 1024);
-  }
-  const int col = 64 * w + lane;
-  int64_t wr = b_row_of_col<EPI, BN>(col, nt, N, I);
-  wr = wr < 0 ? 0 : wr;
-  dma_b32(scales + wr * (s.b_cols / 16), Ss + 64 * w);
-}
-
-// A through registers: the LoRA segment (k >= K zeroed) and NVFP4 activation rows
+// A rows through registers (the LoRA segment; k >= K zeroed when MASKK)
 struct ARegs {
   u32x4 v[ACH];
 };
@@ -994,49 +934,21 @@ struct ARegs {
 template <int ASRC, bool MASKK>
 __device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[ACH], int k0, ARegs &r) {
   const int tid = threadIdx.x;
-  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
-    const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
+  const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-      const int kk = k0 + (tid & 7) * 8;
-      const bool ok = !MASKK || kk < s.K;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(a + arow[i] * s.a_ld + (ok ? kk : 0));
-      r.v[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  } else {
-    // NVFP4 rows: items (row = item / 2, 32-element half item % 2), 2 per thread
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int half = (tid + NTHR * it) & 1;
-      const int kq = k0 + half * 32;
-      const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.a) + arow[it] * (s.a_ld / 2) + kq / 2;
-      r.v[2 * it] = *reinterpret_cast<const u32x4 *>(cp);
-      r.v[2 * it + 1].x = *reinterpret_cast<const uint16_t *>(s.a_sc + arow[it] * (s.a_ld / 16) + kq / 16);
-    }
+  for (int i = 0; i < ACH; ++i) {
+    const int kk = k0 + (tid & 7) * 8;
+    const bool ok = !MASKK || kk < s.K;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(a + arow[i] * s.a_ld + (ok ? kk : 0));
+    r.v[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
 template <int ASRC>
 __device__ __forceinline__ void a_store(uint16_t *As, const ARegs &r) {
   const int tid = threadIdx.x;
-  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4 *>(As + a_off(a_row(i), tid & 7)) = r.v[i];
-  } else {
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = tid + NTHR * it;
-      const int row = item >> 1, half = item & 1;
-      const uint32_t cw[4] = {r.v[2 * it].x, r.v[2 * it].y, r.v[2 * it].z, r.v[2 * it].w};
-      const float s0 = e4m3_hw<0>(r.v[2 * it + 1].x), s1 = e4m3_hw<1>(r.v[2 * it + 1].x);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t o[4];
-        fp4x8_hw(cw[q], q < 2 ? s0 : s1, o);
-        *reinterpret_cast<uint4 *>(As + a_off(row, half * 4 + q)) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
-    }
-  }
+  for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4 *>(As + a_off(a_row(i), tid & 7)) = r.v[i];
 }
 
 // A fragments of slice kk for row tiles 0..TM-1
@@ -1052,28 +964,6 @@ struct BCodes {
   float s[TN][2];
 };
 
-__device__ __forceinline__ void b_codes(const uint8_t *Bs, const uint32_t *Ss, int wn, int lane, BCodes &b) {
-  const int g = lane >> 5;
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int col = wn * TN * 32 + tn * 32 + (lane & 31);
-    b.c[tn] = *reinterpret_cast<const u32x4 *>(Bs + col * 32 + 16 * g);
-    const uint32_t sw = Ss[col] >> (16 * g);  // blocks 2g, 2g+1
-    b.s[tn][0] = e4m3_hw<0>(sw);
-    b.s[tn][1] = e4m3_hw<1>(sw);
-  }
-}
-
-__device__ __forceinline__ void b_decode(const BCodes &b, int kk, bf16x8 (&bf)[TN]) {
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    uint32_t o[4];
-    fp4x8_hw(b.c[tn][kk], b.s[tn][kk >> 1], o);
-    const u32x4 v = {o[0], o[1], o[2], o[3]};
-    bf[tn] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-
 template <int VT>
 __device__ __forceinline__ void mfmas(const bf16x8 (&af)[TM], const bf16x8 (&bf)[TN], int vt,
                                       f32x16 (&acc)[TM][TN]) {
@@ -1085,86 +975,6 @@ __device__ __forceinline__ void mfmas(const bf16x8 (&af)[TM], const bf16x8 (&bf)
         acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[tn], af[tm], acc[tm][tn], 0, 0, 0);
     }
   }
-}
-
-// Segment 1: A (bf16 rows by DMA, or NVFP4 rows through registers) x NVFP4 weights.
-// Step ks multiplies stage ks % 3.  At its start the copies of K step ks+2 go to
-// a third stage (and NVFP4 A rows of step ks+1 to registers, written out before
-// the closing barrier), so a copy has two steps to land; the reads and decode
-// of slice kk+1 run before the MFMAs of slice kk; the last slice's MFMAs run
-// after the closing barrier, behind the reads of the next step's first slice.
-template <int ASRC, int EPI, int VT>
-__device__ __forceinline__ void seg_q4(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
-                                       Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
-  constexpr bool DIRECT = ASRC == A_GATHER || ASRC == A_ROWS;
-  constexpr int NDMA = (DIRECT ? ACH : 0) + 3;  // copy instructions per step and wave
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
-  const int nk = s.K / BK;
-  ARegs ar;
-  // prologue: stage 0 <- step 0, stage 1 <- step 1 (copies), wait for stage 0
-  if constexpr (DIRECT) {
-    a_dma(s, arow, 0, sm.a[0]);
-  } else {
-    a_load<ASRC, false>(s, arow, 0, ar);
-    a_store<ASRC>(sm.a[0], ar);
-  }
-  b_dma<EPI>(s, e, nt, N, I, 0, sm.b[0], sm.s[0]);
-  if (nk > 1) {
-    if constexpr (DIRECT) {
-      a_dma(s, arow, BK, sm.a[1]);
-    } else {
-      a_load<ASRC, false>(s, arow, BK, ar);
-      a_store<ASRC>(sm.a[1], ar);
-    }
-    b_dma<EPI>(s, e, nt, N, I, BK, sm.b[1], sm.s[1]);
-    wait_vm<NDMA>();
-  } else {
-    wait_vm<0>();
-  }
-  __syncthreads();
-  bf16x8 af[2][TM], bf[2][TN];
-  BCodes bc;
-  a_frags(sm.a[0], 0, row0, lane, af[0]);
-  b_codes(sm.b[0], sm.s[0], wn, lane, bc);
-  b_decode(bc, 0, bf[0]);
-  int cur = 0;
-  for (int ks = 0; ks < nk; ++ks) {
-    const int nxt = cur == NST - 1 ? 0 : cur + 1;
-    const int nn = nxt == NST - 1 ? 0 : nxt + 1;
-    const bool more = ks + 1 < nk, more2 = ks + 2 < nk;
-    if constexpr (!DIRECT)
-      if (more2) a_load<ASRC, false>(s, arow, (ks + 2) * BK, ar);
-    if (more2) {
-      if constexpr (DIRECT) a_dma(s, arow, (ks + 2) * BK, sm.a[nn]);
-      b_dma<EPI>(s, e, nt, N, I, (ks + 2) * BK, sm.b[nn], sm.s[nn]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int nb = (kk + 1) & 1;
-      if (kk + 1 < BK / 16) {
-        if (VT != VT_DYN || vt > 0) a_frags(sm.a[cur], kk + 1, row0, lane, af[nb]);
-        b_decode(bc, kk + 1, bf[nb]);
-      } else {
-        if (more2)
-          wait_vm<NDMA>();  // step ks+1's copies have landed; step ks+2's may fly on
-        else
-          wait_vm<0>();
-        if constexpr (!DIRECT)
-          if (more2) a_store<ASRC>(sm.a[nn], ar);  // stage nn was last read two steps ago
-        barrier_lds();
-        if (more) {
-          a_frags(sm.a[nxt], 0, row0, lane, af[nb]);
-          b_codes(sm.b[nxt], sm.s[nxt], wn, lane, bc);
-          b_decode(bc, 0, bf[nb]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas<VT>(af[kk & 1], bf[kk & 1], vt, acc);
-    }
-    cur = nxt;
-  }
-  __syncthreads();  // the stages are reused by the next segment
 }
 
 // ---- Segment 1 with A rows copied straight to LDS: software-pipelined K loop ----
@@ -1812,8 +1622,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   int64_t arow[ACH];
 #pragma unroll
   for (int i = 0; i < ACH; ++i) {
-    const int row = kQA ? ((tid + NTHR * i) >> 1) : a_row(i);
-    const int pos = min(m0 + row, n_e - 1);  // rows past the segment: clamped (results dropped)
+    const int pos = min(m0 + a_row(i), n_e - 1);  // rows past the segment: clamped (results dropped)
     if (ASRC == A_GATHER || ASRC == A_GATHER_Q)
       arow[i] = p.perm[rb + pos] / p.k;
     else
@@ -1828,24 +1637,18 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  if constexpr (ASRC == A_GATHER || ASRC == A_ROWS) {
-    // row tiles rounded up to even counts (rows past the segment are dropped)
-    if (vt > 6)
-      seg_q4_direct<EPI, 8>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-    else if (vt > 4)
-      seg_q4_direct<EPI, 6>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-    else if (vt > 2)
-      seg_q4_direct<EPI, 4>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-    else
-      seg_q4_direct<EPI, 2>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-  } else if (vt == TM) {
-    seg_q4<ASRC, EPI, VT_ALL>(p.s1, e, nt, p.N, p.I, arow, sm, vt, acc);
-  } else {
-    seg_q4<ASRC, EPI, VT_DYN>(p.s1, e, nt, p.N, p.I, arow, sm, vt, acc);
-  }
+  // row tiles rounded up to even counts (rows past the segment are dropped)
+  if (vt > 6)
+    seg_q4_direct<EPI, 8>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  else if (vt > 4)
+    seg_q4_direct<EPI, 6>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  else if (vt > 2)
+    seg_q4_direct<EPI, 4>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  else
+    seg_q4_direct<EPI, 2>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
 
   // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
-  // per row (NVFP4 activations) before the LoRA segment
+  // per row and expert (NVFP4 activations, val * sb rows) before the LoRA segment
   float esc = 1.0f;
   if constexpr (!kQA) esc = uniform_load(p.s1.b_sd + e);
   if constexpr (kQA) {
@@ -2185,7 +1988,8 @@ __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict_
 // host side
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t perm, inv, off, tile_off, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, aq_c, aq_s, aq_d, vdn, dh, vgu, dxr;
+  size_t perm, inv, off, tile_off, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
+      vgu, dxr;
   size_t total;
 };
 
@@ -2214,9 +2018,11 @@ Layout layout(const bqm_moe_desc *d) {
   L.xq_c = take(aq ? T * H / 2 : 0);
   L.xq_s = take(aq ? T * H / 16 : 0);
   L.xq_d = take(aq ? T * 4 : 0);
+  L.xq_b = take(aq ? T * H * 2 : 0);
   L.aq_c = take(aq ? R * I / 2 : 0);
   L.aq_s = take(aq ? R * I / 16 : 0);
   L.aq_d = take(aq ? R * 4 : 0);
+  L.aq_b = take(aq ? R * I * 2 : 0);
   L.vdn = take(R * 2 * r * 2);
   L.dh = take(R * 2 * I * 2);
   L.vgu = take(R * 2 * r * 2);
@@ -2392,9 +2198,11 @@ inline void mark(const bqm_moe_desc *d, int stage, int end, hipStream_t s) {
     mark(d, st, 1, s);            \
   } while (0)
 
-// rows [n_rows, cols] -> per-row NVFP4 (Four-Over-Six) into the given buffers
+// rows [n_rows, cols] -> per-row NVFP4 (Four-Over-Six) into the given buffers, then the
+// rows of val * sb in bf16 (exact) that the forward GEMMs multiply, their per-row s_dec
+// applied to the accumulator
 bqm_status quantize_rows(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_t *codes, uint8_t *scales, float *sd,
-                         hipStream_t s) {
+                         uint16_t *expanded, hipStream_t s) {
   bqm_qtensor q{};
   q.fmt = BQM_FMT_NVFP4;
   q.scale_mode = BQM_SCALE_PER_ROW;
@@ -2404,7 +2212,8 @@ bqm_status quantize_rows(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_
   q.codes = codes;
   q.scales = scales;
   q.s_dec = sd;
-  return bqm_quantize_nvfp4(x, 1, nullptr, &q, nullptr, 0, s);
+  BQM_TRY(bqm_quantize_nvfp4(x, 1, nullptr, &q, nullptr, 0, s));
+  return nvfp4_expand(codes, scales, n_rows * cols, expanded, s);
 }
 
 template <int ASRC_X>
@@ -2432,24 +2241,23 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     GemmParams p = base_params(d, w);
     p.N = 2 * I;
     p.NT = (int)cdiv(I, 128);
-    const void *xa = ASRC_X == A_GATHER_Q ? (const void *)w.at<uint8_t>(w.L.xq_c) : (const void *)x;
-    p.s1 = seg_q(xa, H, d->w_gu, H);
-    if (ASRC_X == A_GATHER_Q) {
-      p.s1.a_sc = w.at<uint8_t>(w.L.xq_s);
-      p.s1.a_sd = w.at<float>(w.L.xq_d);
-    }
+    constexpr bool aq = ASRC_X == A_GATHER_Q;
+    p.s1 = seg_q(aq ? (const void *)w.at<uint16_t>(w.L.xq_b) : (const void *)x, H, d->w_gu, H);
+    if (aq) p.s1.a_sd = w.at<float>(w.L.xq_d);
     p.s2 = seg_lora(ugu, d->B_gu, 2 * I, r, r);
     p.outf = h;
     p.out1 = a;
+    // (NF4 weights take bf16 activations only: check_desc rejects act_quant with them)
     if (nf4)
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, ASRC_X, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, A_GATHER, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
     else
       BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd")));
   }
-  const bool aq = ASRC_X == A_GATHER_Q;
+  constexpr bool aq = ASRC_X == A_GATHER_Q;
   if (aq)
     BQM_STAGE(d, BQM_STAGE_ACT_QUANT_A, s,
-              quantize_rows(a, R, I, w.at<uint8_t>(w.L.aq_c), w.at<uint8_t>(w.L.aq_s), w.at<float>(w.L.aq_d), s));
+              quantize_rows(a, R, I, w.at<uint8_t>(w.L.aq_c), w.at<uint8_t>(w.L.aq_s), w.at<float>(w.L.aq_d),
+                            w.at<uint16_t>(w.L.aq_b), s));
   // U_dn = s a A_dn^T  [R, r]
   if (r > 0) {
     GemmParams p = base_params(d, w);
@@ -2466,11 +2274,8 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     GemmParams p = base_params(d, w);
     p.N = H;
     p.NT = (int)cdiv(H, 256);
-    p.s1 = seg_q(aq ? (const void *)w.at<uint8_t>(w.L.aq_c) : (const void *)a, I, d->w_dn, I);
-    if (aq) {
-      p.s1.a_sc = w.at<uint8_t>(w.L.aq_s);
-      p.s1.a_sd = w.at<float>(w.L.aq_d);
-    }
+    p.s1 = seg_q(aq ? (const void *)w.at<uint16_t>(w.L.aq_b) : (const void *)a, I, d->w_dn, I);
+    if (aq) p.s1.a_sd = w.at<float>(w.L.aq_d);
     p.s2 = seg_lora(udn, d->B_dn, H, r, r);
     p.out0 = y;
     if (nf4)
@@ -2513,7 +2318,8 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
   const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
   if (d->act_quant) {
     BQM_STAGE(d, BQM_STAGE_ACT_QUANT_X, s,
-              quantize_rows(x, d->T, d->H, w.at<uint8_t>(w.L.xq_c), w.at<uint8_t>(w.L.xq_s), w.at<float>(w.L.xq_d), s));
+              quantize_rows(x, d->T, d->H, w.at<uint8_t>(w.L.xq_c), w.at<uint8_t>(w.L.xq_s), w.at<float>(w.L.xq_d),
+                            w.at<uint16_t>(w.L.xq_b), s));
     BQM_TRY(fwd_gemms<A_GATHER_Q>(d, w, x, R, s, nf4));
   } else {
     BQM_TRY(fwd_gemms<A_GATHER>(d, w, x, R, s, nf4));

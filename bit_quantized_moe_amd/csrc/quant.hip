@@ -19,6 +19,7 @@
 // per-tensor amax is a separate pass (one atomicMax per workgroup into the
 // matrix's slot) before the quantize pass.
 #include "common.h"
+#include "internal.h"
 #include "nf4_levels.inc"
 
 #include <algorithm>
@@ -305,7 +306,10 @@ __device__ __forceinline__ uint32_t nvfp4_dq_pair(uint32_t c, float sb, float sd
 }
 
 // NVFP4 dequantize: bf16(fl(fl(val * sb) * s_dec)).  seg_units: units per s_dec
-// (a whole matrix, or one row in per-row mode).
+// (a whole matrix, or one row in per-row mode).  Without kSdec the output is val * sb
+// alone, exact in bf16 (at most 6 significant bits): the scaled-domain values that a
+// GEMM multiplies, with s_dec applied to its accumulator.
+template <bool kSdec>
 __global__ void __launch_bounds__(kThreads) nvfp4_dequant(const uint32_t *__restrict__ codes,
                                                           const uint8_t *__restrict__ scales,
                                                           const float *__restrict__ s_dec, int64_t nunits,
@@ -321,7 +325,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_dequant(const uint32_t *__rest
     const int64_t u = u0 < nunits ? u0 : nunits - 1;
     c[it] = codes[u];
     sbc[it] = scales[u >> 1];
-    sd[it] = s_dec[seg_of(u, seg0, first, seg_units)];
+    sd[it] = kSdec ? s_dec[seg_of(u, seg0, first, seg_units)] : 1.0f;
   }
 #pragma unroll
   for (int it = 0; it < kDqIter; ++it) {
@@ -578,7 +582,7 @@ extern "C" bqm_status bqm_dequantize(const bqm_qtensor *q, uint16_t *y, void *st
   if (q->fmt == BQM_FMT_NVFP4) {
     const int64_t seg_units = q->scale_mode == BQM_SCALE_PER_ROW ? q->cols / 8 : q->rows * q->cols / 8;
     BQM_REQUIRE(seg_units < (int64_t)1 << 31, BQM_ERR_SHAPE, "bqm_dequantize: matrix too large");
-    nvfp4_dequant<<<dq_grid(n), kThreads, 0, s>>>(
+    nvfp4_dequant<true><<<dq_grid(n), kThreads, 0, s>>>(
         reinterpret_cast<const uint32_t *>(q->codes), reinterpret_cast<const uint8_t *>(q->scales), q->s_dec,
         n / 8, seg_units, reinterpret_cast<uint4 *>(y));
     return launch_status("nvfp4_dequant");
@@ -588,3 +592,13 @@ extern "C" bqm_status bqm_dequantize(const bqm_qtensor *q, uint16_t *y, void *st
                                               reinterpret_cast<uint4 *>(y));
   return launch_status("nf4_dequant");
 }
+
+namespace bqm {
+// Per-row NVFP4 codes -> bf16 rows of val * sb (no s_dec), n elements.
+bqm_status nvfp4_expand(const uint8_t *codes, const uint8_t *scales, int64_t n, uint16_t *y, hipStream_t s) {
+  if (n == 0) return BQM_OK;
+  nvfp4_dequant<false><<<dq_grid(n), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(codes), scales, nullptr,
+                                                       n / 8, n / 8, reinterpret_cast<uint4 *>(y));
+  return launch_status("nvfp4_expand");
+}
+}  // namespace bqm
