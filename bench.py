@@ -261,6 +261,42 @@ def time_layer(s, inp, wgu, wdn, ev, sh, steps, warmup):
     return res
 
 
+def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 64, 256), reps=20):
+    """Decode-shaped forward (route + moe_fwd only) at a few tokens over the same
+    quantized experts and LoRA: the time against reading each hit expert's NVFP4
+    weights (codes + E4M3 scales of gate_up and down) once."""
+    import dataclasses
+    import torch
+    import bit_quantized_moe_amd as bqm
+    import synth
+    dev = torch.device("cuda")
+    per_expert = (2 * shape.I * shape.H + shape.H * shape.I) * (0.5 + 1 / 16)
+    rows = []
+    for T in tokens:
+        s = dataclasses.replace(shape, T=T, name=f"{shape.name}_decode_T{T}")
+        inp = synth.layer_inputs(s, device=dev, with_weights=False)
+        d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn,
+                        B_dn=inp.B_dn)
+        ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+        idx = torch.empty((T, s.k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, s.k), dtype=torch.float32, device=dev)
+        out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
+
+        def run():
+            bqm.bqm_route(inp.logits, T, s.E, s.k, 0, idx, tw)
+            bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
+
+        ms = time_calls(ev, sh, run, reps)
+        hit = int(torch.unique(idx).numel())
+        wbytes = hit * per_expert
+        rows.append({"T": T, "ms_per_forward": round(ms, 4), "experts_hit": hit,
+                     "hit_weight_bytes": int(wbytes), "weight_read_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
+                     "weight_read_frac": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        del inp, d, ws, idx, tw, out
+        torch.cuda.empty_cache()
+    return rows
+
+
 def time_calls(ev, sh, fn, reps=3):
     """Mean hipEvent time of fn() over reps calls after one untimed call."""
     import torch
@@ -436,6 +472,9 @@ def main():
         del inp3, q3gu, q3dn
         torch.cuda.empty_cache()
         result["other_configs"] = others
+        # decode-shaped forward over the GLM experts (serving side: weight-read-bound)
+        result["decode_forward"] = {"workload": "glm5.2 shape, forward only (route + moe_fwd), nvfp4 weights, "
+                                                "LoRA r=64", "rows": decode_sweep(shape, wgu, wdn, ev, sh)}
 
     if args.sweep:
         torch.cuda.empty_cache()

@@ -1850,14 +1850,20 @@ constexpr int WB = 64;  // wgrad tile (M and N) and row step
 // One 64x64 tile of C[e] per workgroup; rows of the expert's segment in steps
 // of 64.  All 256 threads load: each owns 2 16-byte chunks of the P rows and 2
 // of the Q rows of a step (rows row = c / 8, 8 columns at 8 * (c % 8)), held in
-// registers one step ahead; tiles stay in their natural [row][col] layout in
-// one LDS stage (18 KB, so eight workgroups share a CU and keep many loads in
-// flight) and the MFMA fragments (8 consecutive rows of one column) come from
-// the gfx950 transposing LDS read.
+// registers one step ahead; the routing weight that scales P rows is applied when
+// the step is written to LDS, so the loads are not waited for before the MFMAs of
+// the current step.  Tiles stay in their natural [row][col] layout in one LDS stage
+// (18 KB, so eight workgroups share a CU and keep many loads in flight; two or three
+// steps in flight per workgroup measured slower) and the MFMA fragments (8
+// consecutive rows of one column) come from the gfx950 transposing LDS read.
 constexpr int WS = WB + 8;  // LDS row stride in bf16 (64 columns + 16-byte pad)
 
-__device__ __forceinline__ void wgrad_load(const WgradParams &p, int rb, int n_e, int r0, int m0, int n0,
-                                           uint4 (&v)[4]) {
+struct WRegs {
+  uint4 v[4];  // P chunks 0, 1; Q chunks 0, 1
+  float w[2];  // routing weights of the two P rows (scale_p)
+};
+
+__device__ __forceinline__ void wgrad_load(const WgradParams &p, int rb, int n_e, int r0, int m0, int n0, WRegs &r) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1872,24 +1878,26 @@ __device__ __forceinline__ void wgrad_load(const WgradParams &p, int rb, int n_e
       const int gather = isq ? p.q_gather : p.p_gather;
       const int64_t srow = gather ? (int64_t)(p.perm[grow] / p.k) : grow;
       x = *reinterpret_cast<const uint4 *>((isq ? p.Q : p.P) + srow * (isq ? p.q_ld : p.p_ld) + col);
-      if (!isq && p.scale_p) {
-        const float s = p.tw[p.perm[grow]];
-        uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) w[h] = f32_to_bf16(bf16_lo(w[h]) * s) | (f32_to_bf16(bf16_hi(w[h]) * s) << 16);
-        x = make_uint4(w[0], w[1], w[2], w[3]);
-      }
     }
-    v[i] = x;
+    r.v[i] = x;
+    if (!isq && p.scale_p) r.w[i] = pos < n_e ? p.tw[p.perm[rb + pos]] : 0.0f;
   }
 }
 
-__device__ __forceinline__ void wgrad_store(uint16_t *Ps, uint16_t *Qs, const uint4 (&v)[4]) {
+__device__ __forceinline__ void wgrad_store(const WgradParams &p, uint16_t *Ps, uint16_t *Qs, const WRegs &r) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + NTHR * (i & 1);
-    *reinterpret_cast<uint4 *>((i >= 2 ? Qs : Ps) + (c >> 3) * WS + 8 * (c & 7)) = v[i];
+    uint4 x = r.v[i];
+    if (i < 2 && p.scale_p) {
+      const float s = r.w[i];
+      uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) w[h] = f32_to_bf16(bf16_lo(w[h]) * s) | (f32_to_bf16(bf16_hi(w[h]) * s) << 16);
+      x = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    *reinterpret_cast<uint4 *>((i >= 2 ? Qs : Ps) + (c >> 3) * WS + 8 * (c & 7)) = x;
   }
 }
 
@@ -1907,14 +1915,14 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
   const int nk = (n_e + WB - 1) / WB;
-  uint4 v[4];
+  WRegs r;
   if (nk > 0) {
-    wgrad_load(p, rb, n_e, 0, m0, n0, v);
-    wgrad_store(Ps, Qs, v);
+    wgrad_load(p, rb, n_e, 0, m0, n0, r);
+    wgrad_store(p, Ps, Qs, r);
   }
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) wgrad_load(p, rb, n_e, (ks + 1) * WB, m0, n0, v);
+    if (ks + 1 < nk) wgrad_load(p, rb, n_e, (ks + 1) * WB, m0, n0, r);
 #pragma unroll
     for (int kk = 0; kk < WB / 16; ++kk) {
       const bf16x8 a = b_frag_trans_s<WS>(Ps, kk * 16, wm * 32, lane);
@@ -1923,7 +1931,7 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
     }
     __syncthreads();  // every wave is done reading the stage
     if (ks + 1 < nk) {
-      wgrad_store(Ps, Qs, v);
+      wgrad_store(p, Ps, Qs, r);
       __syncthreads();
     }
   }
