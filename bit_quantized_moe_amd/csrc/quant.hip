@@ -29,19 +29,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Round a non-negative finite float to the E4M3FN grid (nearest, ties to even,
-// saturating at 448) and return its code 0..126.
-__device__ __forceinline__ uint32_t e4m3_rne_satfinite(float t) {
-  uint32_t code;
-  if (t < 0x1p-6f) {
-    // subnormal step 2^-9 is the ulp of 2^14: one correctly rounded add
-    float s = t + 16384.0f;
-    code = __float_as_uint(s) - 0x46800000u;
-  } else {
-    uint32_t u = __float_as_uint(t);
-    code = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - 960u;
-  }
-  return code < 126u ? code : 126u;
+// fl(t / 6) without a division: q = fl(t * fl(1/6)), the remainder t - 6 q exact in one
+// fma, then one fma correction.  Checked exhaustively against the correctly rounded
+// quotient: equal for every finite float t >= 2^-119; below that both are far under the
+// smallest E4M3 step (2^-9), so the block scale is code 0 either way.
+__device__ __forceinline__ float div6(float t) {
+  const float r6 = 0x1.555556p-3f;  // fl(1/6)
+  const float q = t * r6;
+  const float r = __builtin_fmaf(-q, 6.0f, t);
+  return __builtin_fmaf(r, r6, q);
+}
+
+// E4M3FN codes of two non-negative finite floats, each rounded to nearest even and
+// saturated at 448, in one hardware conversion.  Clamping to 448 first is the same
+// saturation: every value in [448, 464) rounds to 448, and E4M3FN has nothing above.
+__device__ __forceinline__ void e4m3_pair(float a, float b, uint32_t &ca, uint32_t &cb) {
+  const uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(a, 448.0f), fminf(b, 448.0f), 0, false);
+  ca = p & 0xFFu;
+  cb = (p >> 8) & 0xFFu;
 }
 
 // One scale candidate: E2M1 codes of y * r (the hardware conversion rounds to
@@ -98,11 +103,11 @@ __device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float 
     y[2 * i + 1] = bf16_hi(w[i]) * s_enc;
     t = fmaxf(t, fmaxf(fabsf(y[2 * i]), fabsf(y[2 * i + 1])));
   }
-  const uint32_t sb6 = e4m3_rne_satfinite(t / 6.0f);
+  uint32_t sb6, sb4;
+  e4m3_pair(div6(t), t * 0.25f, sb6, sb4);  // t * 0.25 == t/4 exactly rounded
   const float e6 = candidate(y, __builtin_amdgcn_cvt_f32_fp8(sb6, 0), rcp[sb6], lo, hi);
   uint32_t sb = sb6;
   if (kFos) {
-    const uint32_t sb4 = e4m3_rne_satfinite(t * 0.25f);  // == t/4 exactly rounded
     if (sb4 != sb6) {
       uint32_t l4, h4;
       const float e4 = candidate(y, __builtin_amdgcn_cvt_f32_fp8(sb4, 0), rcp[sb4], l4, h4);

@@ -105,6 +105,28 @@ def test_nvfp4_dequantize_bit_exact(per_row):
     assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("fos", [True, False])
+def test_nvfp4_block_scales_over_the_e4m3_range(fos):
+    """Block scales E4M3(t/6) and E4M3(t/4) for every bf16 block maximum t in [2^-30, 2^13]:
+    with a given s_dec of 1 the target is x itself, so this covers the E4M3 subnormals, every
+    rounding boundary between E4M3 values and the saturation at 448 (t/6 > 448 above 2688)."""
+    import torch
+    dev = gpu()
+    log(f"nvfp4 block scales over the E4M3 range, fos={fos}")
+    bits = np.arange(0x3080, 0x4600, dtype=np.uint32)          # bf16 patterns 2^-30 .. 2^13 (exclusive)
+    t = fm.bf16_bits_to_f32(bits.astype(np.uint16))
+    x = np.zeros((t.size, 16), dtype=np.float32)
+    x[:, 0] = t
+    x[:, 5] = fm.bf16_round(-t * np.float32(0.3))
+    x[:, 11] = fm.bf16_round(t * np.float32(0.55))
+    x = x.reshape(1, t.size, 16)
+    xt = torch.from_numpy(x).to(torch.bfloat16)
+    assert np.array_equal(xt.float().numpy(), x)
+    sdi = torch.ones(1, dtype=torch.float32, device=dev)
+    q = gpu_quant_nvfp4(xt.to(dev), fos=fos, s_dec_in=sdi)
+    check_nvfp4_against_oracle(xt.to(dev), q, fos, per_row=False, s_dec_in=sdi)
+
+
 @pytest.mark.parametrize("shape", [(2, 64, 256), (3, 5, 64), (1, 130, 192)])
 def test_nf4_quantize_dequantize_bit_exact(shape):
     import torch
