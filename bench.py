@@ -365,6 +365,14 @@ def main():
     ev = HipEvents()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    # a plain device-to-device copy of 2 GiB: the HBM rate reachable in practice, beside the 8 TB/s spec
+    cbuf = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(cbuf)
+    copy_ms = time_calls(ev, sh, lambda: cdst.copy_(cbuf), 5)
+    hbm_copy = {"bytes_moved": 2 * (1 << 31), "ms": copy_ms, "GB/s": 2 * (1 << 31) / copy_ms / 1e6,
+                "frac_of_spec": 2 * (1 << 31) / copy_ms / 1e6 / PEAK_HBM_GBS}
+    del cbuf, cdst
+    torch.cuda.empty_cache()
     n_el = s.E * (2 * s.I * s.H + s.H * s.I)
     conv_bytes = n_el * (2 + 0.5 + 1 / 16)    # bf16 <-> 4-bit codes + 1 scale byte (or 1/4 float) per 16
 
@@ -429,6 +437,7 @@ def main():
         "stages_ms": res["stages_ms"],
         "stage_roofline": res["stage_roofline"],
         "quantizer": quant,
+        "hbm_copy": hbm_copy,
     }
 
     if not args.main_only:

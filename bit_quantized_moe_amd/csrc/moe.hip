@@ -907,6 +907,23 @@ __device__ __forceinline__ int a_off(int r, int c) { return r * BK + 8 * (c ^ ((
 // row of the tile owned by this thread's j-th A chunk
 __device__ __forceinline__ int a_row(int j) { return 64 * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3); }
 
+// A row of this lane's direct copy j when a tile holds VT valid 32-row tiles: each wave
+// copies 8 VT rows (VT copies of 8 rows), so a tile copies only the 32 VT rows its
+// MFMAs read
+template <int VT>
+__device__ __forceinline__ int dma_row(int j) { return 8 * VT * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3); }
+
+// source rows of the direct copies (routed rows past the expert's segment clamped; their
+// results are dropped)
+template <int ASRC, int VT>
+__device__ __forceinline__ void dma_rows(const GemmParams &p, int rb, int n_e, int m0, int64_t (&arow)[ACH]) {
+#pragma unroll
+  for (int j = 0; j < VT; ++j) {
+    const int pos = min(m0 + dma_row<VT>(j), n_e - 1);
+    arow[j] = (ASRC == A_GATHER || ASRC == A_GATHER_Q) ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+  }
+}
+
 
 // Direct-to-LDS copies (lane i's 16 or 4 bytes land at lds + 16 i or 4 i), written as
 // inline assembly: the compiler's wait-count bookkeeping treats its own form of this
@@ -992,14 +1009,14 @@ struct DmaSrc {
   const uint8_t *s;
 };
 
-template <int EPI>
+template <int EPI, int VT>
 __device__ __forceinline__ void dma_src(const Seg &s, const int64_t (&arow)[ACH], int e, int nt, int N, int I,
                                         DmaSrc &d) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
 #pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int r = 64 * w + 8 * j + (lane >> 3);
+  for (int j = 0; j < VT; ++j) {
+    const int r = dma_row<VT>(j);
     d.a[j] = a + arow[j] * s.a_ld + 8 * ((lane & 7) ^ ((r >> 1) & 7));
   }
   const int64_t slice = s.b_rows * s.b_cols;
@@ -1016,28 +1033,33 @@ __device__ __forceinline__ void dma_src(const Seg &s, const int64_t (&arow)[ACH]
   d.s = scales + wr * (s.b_cols / 16);
 }
 
-// copy number j (0..ACH+2) of the K step at k0 into stage st
+// copy number j (0..VT+2) of the K step at k0 into stage st: A rows (j < VT), codes, scales
+template <int VT>
 __device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, const Smem &sm, int st) {
   const uint32_t w = wave_id();
-  if (j < ACH)
-    dma_b128(d.a[j] + k0, lds_a(sm, st) + (64 * w + 8 * j) * BK * 2);
-  else if (j < ACH + 2)
-    dma_b128(d.c[j - ACH] + k0 / 2, lds_b(sm, st) + (2 * w + j - ACH) * 1024);
+  if (j < VT)
+    dma_b128(d.a[j] + k0, lds_a(sm, st) + (8 * VT * w + 8 * j) * BK * 2);
+  else if (j < VT + 2)
+    dma_b128(d.c[j - VT] + k0 / 2, lds_b(sm, st) + (2 * w + j - VT) * 1024);
   else
     dma_b32(d.s + k0 / 16, lds_s(sm, st) + 256 * w);
 }
 
-// Where the ACH + 3 copies of step ks+2 are issued inside step ks: one every third
-// MFMA pair over all four slices, so the four waves' copies do not queue up behind
-// each other.  Stage (ks+2) % 3 was last read in step ks-1, so any point of step ks
-// may write it.  DMA_EARLY copies come before the wait in slice 3, which must let
-// exactly those stay in flight.  -1: none here.
+// Where the VT + 3 copies of step ks+2 are issued inside step ks: the VT copies of A
+// rows spread over the MFMA pairs of slices 0-2 (position 8 kk + tm), the code and
+// scale copies in slice 3, so the four waves' copies do not queue up behind each
+// other.  Stage (ks+2) % 3 was last read in step ks-1, so any point of step ks may
+// write it.  The A copies come before the wait in slice 3, which lets exactly those
+// (VT of them) stay in flight.  -1: none here.
+template <int VT>
 __device__ __forceinline__ constexpr int dma_slot(int kk, int tm) {
-  return (8 * kk + tm) % 3 == (kk == 3 ? 1 : 0) && (kk < 3 || tm >= 1) ? (kk < 3 ? (8 * kk + tm) / 3 : 8 + (tm - 1) / 3)
-                                                                       : -1;
+  if (kk < 3) {
+    for (int j = 0; j < VT; ++j)
+      if ((24 * j) / VT == 8 * kk + tm) return j;
+    return -1;
+  }
+  return tm == 1 ? VT : (tm == 4 ? VT + 1 : (tm == 7 ? VT + 2 : -1));
 }
-constexpr int DMA_EARLY = 8;
-static_assert(ACH + 3 == 11, "dma_slot places 11 copies");
 
 __device__ __forceinline__ bf16x8 a_frag(const uint16_t *As, int kk, int row, int lane) {
   return *reinterpret_cast<const bf16x8 *>(As + a_off(row + (lane & 31), 4 * (lane >> 5) + kk));
@@ -1096,7 +1118,6 @@ template <int VT, bool DMA, bool NEXT>
 __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrc &d, int wn, int row0,
                                         int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], BCodes &bc,
                                         f32x16 (&acc)[TM][TN]) {
-  constexpr int NDMA = ACH + 3;
   const uint16_t *As = sm.a[cur];
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
@@ -1105,7 +1126,7 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
     for (int tm = 0; tm < TM; ++tm) {
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag(As, kk + 1, row0 + 32 * tm, lane);
-      if (DMA && dma_slot(kk, tm) >= 0) dma_one(d, dma_slot(kk, tm), k2, sm, n2);
+      if (DMA && dma_slot<VT>(kk, tm) >= 0) dma_one<VT>(d, dma_slot<VT>(kk, tm), k2, sm, n2);
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
       bf[n][tm >> 2][tm & 3] = dec_pair(bc, tm >> 2, kk + 1, tm & 3);
@@ -1130,14 +1151,14 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
       // next step may copy into it
       FQ_PIN();
       if (DMA)
-        wait_vm<DMA_EARLY>();
+        wait_vm<VT>();
       else
         wait_vm<0>();
       barrier_lds();
       FQ_PIN();
       b_raw(sm.b[nx], sm.s[nx], wn, lane, raw);
     }
-    if (DMA && dma_slot(3, tm) >= 0) dma_one(d, dma_slot(3, tm), k2, sm, n2);
+    if (DMA && dma_slot<VT>(3, tm) >= 0) dma_one<VT>(d, dma_slot<VT>(3, tm), k2, sm, n2);
     if (NEXT && tm == 3) b_cook(raw, lane, bc);
     if (NEXT && tm >= 4) {
       const int q = 2 * (tm - 4);  // pairs q, q+1 of slice 0
@@ -1151,17 +1172,17 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
 template <int EPI, int VT>
 __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
                                               Smem &sm, f32x16 (&acc)[TM][TN]) {
-  constexpr int NDMA = ACH + 3;
+  constexpr int NDMA = VT + 3;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
   const int nk = s.K / BK;
   DmaSrc d;
-  dma_src<EPI>(s, arow, e, nt, N, I, d);
+  dma_src<EPI, VT>(s, arow, e, nt, N, I, d);
   // prologue: stage 0 <- step 0, stage 1 <- step 1; wait for stage 0 only
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma_one(d, j, 0, sm, 0);
+  for (int j = 0; j < NDMA; ++j) dma_one<VT>(d, j, 0, sm, 0);
   if (nk > 1) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one(d, j, BK, sm, 1);
+    for (int j = 0; j < NDMA; ++j) dma_one<VT>(d, j, BK, sm, 1);
     wait_vm<NDMA>();
   } else {
     wait_vm<0>();
@@ -1270,13 +1291,14 @@ struct DmaSrcD {
   int64_t cstride, sstride;  // bytes per weight row: codes, scales
 };
 
+template <int VT>
 __device__ __forceinline__ void dma_src_d(const Seg &s, const int64_t (&arow)[ACH], int e, int nt, int N,
                                           DmaSrcD &d) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
 #pragma unroll
-  for (int j = 0; j < ACH; ++j) {
-    const int r = 64 * w + 8 * j + (lane >> 3);
+  for (int j = 0; j < VT; ++j) {
+    const int r = dma_row<VT>(j);
     d.a[j] = a + arow[j] * s.a_ld + 8 * ((lane & 7) ^ ((r >> 1) & 7));
   }
   const int64_t slice = s.b_rows * s.b_cols;
@@ -1297,13 +1319,14 @@ __device__ __forceinline__ void dma_src_d(const Seg &s, const int64_t (&arow)[AC
   d.s = scales + row * d.sstride + nt * (BN / 16) + 4 * q;
 }
 
-// copy j (0..ACH+2) of the K step at k0 into stage st
+// copy j (0..VT+2) of the K step at k0 into stage st: A rows (j < VT), codes, scales
+template <int VT>
 __device__ __forceinline__ void dma_one_d(const DmaSrcD &d, int j, int k0, const Smem &sm, int st) {
   const uint32_t w = wave_id();
-  if (j < ACH)
-    dma_b128(d.a[j] + k0, lds_a(sm, st) + (64 * w + 8 * j) * BK * 2);
-  else if (j < ACH + 2)
-    dma_b128(d.c[j - ACH] + k0 * d.cstride, lds_b(sm, st) + (16 * w + 8 * (j - ACH)) * 128);
+  if (j < VT)
+    dma_b128(d.a[j] + k0, lds_a(sm, st) + (8 * VT * w + 8 * j) * BK * 2);
+  else if (j < VT + 2)
+    dma_b128(d.c[j - VT] + k0 * d.cstride, lds_b(sm, st) + (16 * w + 8 * (j - VT)) * 128);
   else
     dma_b32(d.s + k0 * d.sstride, lds_s(sm, st) + 256 * w);
 }
@@ -1354,7 +1377,6 @@ template <int VT, bool DMA, bool NEXT>
 __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrcD &d, int wn, int row0,
                                         int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], DRaw &raw,
                                         f32x16 (&acc)[TM][TN]) {
-  constexpr int NDMA = ACH + 3;
   const uint16_t *As = sm.a[cur];
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
@@ -1363,7 +1385,7 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
     for (int tm = 0; tm < TM; ++tm) {
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag_d(As, kk + 1, row0 + 32 * tm, lane);
-      if (DMA && dma_slot(kk, tm) >= 0) dma_one_d(d, dma_slot(kk, tm), k2, sm, n2);
+      if (DMA && dma_slot<VT>(kk, tm) >= 0) dma_one_d<VT>(d, dma_slot<VT>(kk, tm), k2, sm, n2);
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
       bf[n][tm >> 2][tm & 3] = dec_pair_d(raw, tm >> 2, kk + 1, tm & 3);
@@ -1401,12 +1423,12 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
     }
     FQ_PIN();
     if (tm < VT) mfma1(af[1][tm], bf[1][1], acc[tm][1]);
-    if (DMA && dma_slot(3, tm) >= 0) dma_one_d(d, dma_slot(3, tm), k2, sm, n2);
+    if (DMA && dma_slot<VT>(3, tm) >= 0) dma_one_d<VT>(d, dma_slot<VT>(3, tm), k2, sm, n2);
     if (NEXT && tm == 0) {
       // stage nx has landed for every wave and every wave is done reading stage cur
       FQ_PIN();
       if (DMA)
-        wait_vm<DMA_EARLY>();
+        wait_vm<VT>();
       else
         wait_vm<0>();
       barrier_lds();
@@ -1429,16 +1451,16 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
 template <int EPI, int VT>
 __device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
                                               f32x16 (&acc)[TM][TN]) {
-  constexpr int NDMA = ACH + 3;
+  constexpr int NDMA = VT + 3;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
   const int nk = s.K / BK;
   DmaSrcD d;
-  dma_src_d(s, arow, e, nt, N, d);
+  dma_src_d<VT>(s, arow, e, nt, N, d);
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, 0, sm, 0);
+  for (int j = 0; j < NDMA; ++j) dma_one_d<VT>(d, j, 0, sm, 0);
   if (nk > 1) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one_d(d, j, BK, sm, 1);
+    for (int j = 0; j < NDMA; ++j) dma_one_d<VT>(d, j, BK, sm, 1);
     wait_vm<NDMA>();
   } else {
     wait_vm<0>();
@@ -1559,11 +1581,6 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
   const int rows_left = n_e - m0 - row0;
   const int vt = rows_left <= 0 ? 0 : (rows_left >= TM * 32 ? TM : (rows_left + 31) / 32);
   int64_t arow[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int pos = min(m0 + a_row(i), n_e - 1);
-    arow[i] = ASRC == A_GATHER ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
-  }
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm)
@@ -1571,14 +1588,21 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
     for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
-  if (vt > 6)
+  // row tiles rounded up to even counts; the copies cover the tile's 32 vt rows only
+  const int vtu = __builtin_amdgcn_readfirstlane(vt);  // every wave starts at row 0: vt is the tile's
+  if (vtu > 6) {
+    dma_rows<ASRC, 8>(p, rb, n_e, m0, arow);
     seg_dq_direct<EPI, 8>(p.s1, e, nt, p.N, arow, sm, acc);
-  else if (vt > 4)
+  } else if (vtu > 4) {
+    dma_rows<ASRC, 6>(p, rb, n_e, m0, arow);
     seg_dq_direct<EPI, 6>(p.s1, e, nt, p.N, arow, sm, acc);
-  else if (vt > 2)
+  } else if (vtu > 2) {
+    dma_rows<ASRC, 4>(p, rb, n_e, m0, arow);
     seg_dq_direct<EPI, 4>(p.s1, e, nt, p.N, arow, sm, acc);
-  else
+  } else {
+    dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
     seg_dq_direct<EPI, 2>(p.s1, e, nt, p.N, arow, sm, acc);
+  }
   // the per-expert FP32 decode scale multiplies the whole accumulator (the LoRA
   // segment's A operand was stored divided by it)
   const float esc = uniform_load(p.s1.b_sd + e);
@@ -1620,14 +1644,6 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
 
   constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
   int64_t arow[ACH];
-#pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int pos = min(m0 + a_row(i), n_e - 1);  // rows past the segment: clamped (results dropped)
-    if (ASRC == A_GATHER || ASRC == A_GATHER_Q)
-      arow[i] = p.perm[rb + pos] / p.k;
-    else
-      arow[i] = rb + pos;
-  }
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -1637,15 +1653,22 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
 
-  // row tiles rounded up to even counts (rows past the segment are dropped)
-  if (vt > 6)
+  // row tiles rounded up to even counts (rows past the segment are dropped); the copies
+  // cover the tile's 32 vt rows only
+  const int vtu = __builtin_amdgcn_readfirstlane(vt);  // every wave starts at row 0: vt is the tile's
+  if (vtu > 6) {
+    dma_rows<ASRC, 8>(p, rb, n_e, m0, arow);
     seg_q4_direct<EPI, 8>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-  else if (vt > 4)
+  } else if (vtu > 4) {
+    dma_rows<ASRC, 6>(p, rb, n_e, m0, arow);
     seg_q4_direct<EPI, 6>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-  else if (vt > 2)
+  } else if (vtu > 2) {
+    dma_rows<ASRC, 4>(p, rb, n_e, m0, arow);
     seg_q4_direct<EPI, 4>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
-  else
+  } else {
+    dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
     seg_q4_direct<EPI, 2>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  }
 
   // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
   // per row and expert (NVFP4 activations, val * sb rows) before the LoRA segment
