@@ -29,6 +29,24 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Streaming (non-temporal) accesses: every byte these kernels read or write is touched
+// once, so the loads and stores carry the non-temporal hint (measured: per-tensor
+// quantize 8.4 -> 7.9 ms, NF4 quantize 5.0 -> 4.6 ms over the two GLM stacks).
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4 *p) {
+  const nt_u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4 *>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+__device__ __forceinline__ void st_nt(uint4 *p, uint4 v) {
+  const nt_u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<nt_u32x4 *>(p));
+}
+__device__ __forceinline__ void st_nt(uint2 *p, uint2 v) {
+  const nt_u32x2 x = {v.x, v.y};
+  __builtin_nontemporal_store(x, reinterpret_cast<nt_u32x2 *>(p));
+}
+
 // fl(t / 6) without a division: q = fl(t * fl(1/6)), the remainder t - 6 q exact in one
 // fma, then one fma correction.  Checked exhaustively against the correctly rounded
 // quotient: equal for every finite float t >= 2^-119; below that both are far under the
@@ -131,7 +149,7 @@ __device__ __forceinline__ void fill_rcp(float *rcp) {
 }
 
 __device__ __forceinline__ void load_block16(const uint4 *p, uint32_t (&w)[8]) {
-  uint4 a = p[0], b = p[1];
+  const uint4 a = ld_nt(p), b = ld_nt(p + 1);
   w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
@@ -198,7 +216,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_amax(const uint4 *__restrict__
   const int64_t b = c * kAmaxVec, e = b + kAmaxVec < vec_per_mat ? b + kAmaxVec : vec_per_mat;
   uint32_t mx = 0u;
   for (int64_t j = b + threadIdx.x; j < e; j += kThreads) {
-    const uint4 v = xm[j];
+    const uint4 v = ld_nt(&xm[j]);
     uint32_t a0 = absmax_bits_u32(v.x), a1 = absmax_bits_u32(v.y);
     uint32_t a2 = absmax_bits_u32(v.z), a3 = absmax_bits_u32(v.w);
     a0 = a0 > a1 ? a0 : a1;
@@ -236,8 +254,8 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
     load_block16(xm + 2 * blk, w);
     uint32_t lo, hi;
     const uint32_t sb = quant_block16<kFos>(w, s_enc, rcp, lo, hi);
-    cm[blk] = make_uint2(lo, hi);
-    sm[blk] = (uint8_t)sb;
+    st_nt(&cm[blk], make_uint2(lo, hi));
+    __builtin_nontemporal_store((uint8_t)sb, &sm[blk]);
   }
 }
 
@@ -337,8 +355,8 @@ __global__ void __launch_bounds__(kThreads) nvfp4_dequant(const uint32_t *__rest
     const int64_t u = base + it * kThreads + threadIdx.x;
     if (u < nunits) {
       const float sb = __builtin_amdgcn_cvt_f32_fp8(sbc[it], 0);
-      y[u] = make_uint4(nvfp4_dq_pair<0>(c[it], sb, sd[it]), nvfp4_dq_pair<1>(c[it], sb, sd[it]),
-                        nvfp4_dq_pair<2>(c[it], sb, sd[it]), nvfp4_dq_pair<3>(c[it], sb, sd[it]));
+      st_nt(&y[u], make_uint4(nvfp4_dq_pair<0>(c[it], sb, sd[it]), nvfp4_dq_pair<1>(c[it], sb, sd[it]),
+                              nvfp4_dq_pair<2>(c[it], sb, sd[it]), nvfp4_dq_pair<3>(c[it], sb, sd[it])));
     }
   }
 }
@@ -390,7 +408,7 @@ __global__ void __launch_bounds__(kThreads) nf4_quant(const uint4 *__restrict__ 
 #pragma unroll
   for (int it = 0; it < kDqIter; ++it) {
     const int64_t u0 = base + it * kThreads + threadIdx.x;
-    v[it] = x[u0 < nunits ? u0 : nunits - 1];
+    v[it] = ld_nt(&x[u0 < nunits ? u0 : nunits - 1]);
   }
 #pragma unroll
   for (int it = 0; it < kDqIter; ++it) {
@@ -417,7 +435,7 @@ __global__ void __launch_bounds__(kThreads) nf4_quant(const uint4 *__restrict__ 
       code |= nf4_code(xv * r, tbl) << (4 * i);
     }
     if (u < nunits) {
-      codes[u] = code;
+      __builtin_nontemporal_store(code, &codes[u]);
       if ((threadIdx.x & 7) == 0) absmax[u >> 3] = a;
     }
   }
@@ -448,7 +466,7 @@ __global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restri
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         o[p] = pack_bf16_rne(lv[(c[it] >> (8 * p)) & 0xFu] * a[it], lv[(c[it] >> (8 * p + 4)) & 0xFu] * a[it]);
-      y[u] = make_uint4(o[0], o[1], o[2], o[3]);
+      st_nt(&y[u], make_uint4(o[0], o[1], o[2], o[3]));
     }
   }
 }
