@@ -43,8 +43,10 @@ constexpr int NTHR = 256;
 // (A_ROWS); the _Q forms are per-row NVFP4 activations expanded to bf16 val * sb
 // (exact), whose per-row decode scales (Seg::a_sd) multiply the accumulator.
 enum ASrc { A_GATHER = 0, A_ROWS = 1, A_GATHER_Q = 2, A_ROWS_Q = 3 };
-enum BSrc { B_Q4_K = 0, B_Q4_N = 1, B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
-enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_F32 = 3, EPI_STORE_SPLIT = 4 };
+// B operand of the older staged kernel (moe_gemm): NF4 weights K-major (forward) or N-major (dgrad),
+// bf16 LoRA matrices, or none.  (NVFP4 weights run on the kernels of namespace fq.)
+enum BSrc { B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
+enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_SPLIT = 4 };
 
 // One K segment of a contraction: A rows times one expert slice of a B stack.
 struct Seg {
@@ -76,21 +78,6 @@ struct GemmParams {
 
 __constant__ float c_nf4[16] = BQM_NF4_LEVELS;
 
-// ---------------------------------------------------------------------------
-// dequantization to bf16 bits (exact)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t fp4_bf16(uint32_t nib, float sb) {
-  float v = __uint_as_float(e2m1_mag_bits(nib & 7u) | ((nib & 8u) << 28)) * sb;
-  return __float_as_uint(v) >> 16;  // exact product: <= 6 significant bits
-}
-
-// 8 nibbles of one dword (element 2i in the low nibble of byte i) -> 4 dwords of bf16 pairs
-__device__ __forceinline__ void fp4x8(uint32_t c, float sb, uint32_t *o) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = fp4_bf16((c >> (8 * i)) & 0xFu, sb) | (fp4_bf16((c >> (8 * i + 4)) & 0xFu, sb) << 16);
-}
-
 __device__ __forceinline__ uint32_t nf4_bf16(const float *lut, uint32_t code, float a) {
   return f32_to_bf16(lut[code] * a);
 }
@@ -100,8 +87,6 @@ __device__ __forceinline__ void nf4x8(const float *lut, uint32_t c, float a, uin
   for (int i = 0; i < 4; ++i)
     o[i] = nf4_bf16(lut, (c >> (8 * i)) & 0xFu, a) | (nf4_bf16(lut, (c >> (8 * i + 4)) & 0xFu, a) << 16);
 }
-
-__device__ __forceinline__ float bfv(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // ---------------------------------------------------------------------------
 // tile-column -> weight-row mapping
@@ -136,7 +121,6 @@ struct Cfg {
   static constexpr int ACH = BM * 8 / NTHR;  // 16-byte A chunks per thread per K step
 };
 using BigCfg = Cfg<256, 256, 4, 2>;
-using SmallCfg = Cfg<256, 64, 4, 1>;
 
 // B tiles of N-major sources (the dgrad reads the rowwise weight transposed, and
 // the bf16 LoRA matrices there) stay in their natural [k][n] layout in LDS with a
@@ -174,15 +158,6 @@ template <int SEL>
 __device__ __forceinline__ f32x2 fp4pair(uint32_t c, float sb) {
   f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, SEL);
   return v * sb;  // exact: <= 6 significant bits
-}
-
-// 8 codes of one dword -> 4 dwords of bf16 pairs along the dword's elements
-__device__ __forceinline__ void fp4x8_hw(uint32_t c, float sb, uint32_t *o) {
-  f32x2 a = fp4pair<0>(c, sb), b = fp4pair<1>(c, sb), d = fp4pair<2>(c, sb), e = fp4pair<3>(c, sb);
-  o[0] = pack_exact(a.x, a.y);
-  o[1] = pack_exact(b.x, b.y);
-  o[2] = pack_exact(d.x, d.y);
-  o[3] = pack_exact(e.x, e.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -226,7 +201,7 @@ struct BRegs {
 
 template <int BSRC>
 constexpr bool trans_b() {
-  return BSRC == B_Q4_N || BSRC == B_NF4_N || BSRC == B_BF_N;
+  return BSRC == B_NF4_N || BSRC == B_BF_N;
 }
 
 template <class C, int BSRC, int EPI>
@@ -234,7 +209,7 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
   constexpr int BN = C::BN;
   const int tid = threadIdx.x;
   const int64_t slice = s.b_rows * s.b_cols;
-  if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
+  if constexpr (BSRC == B_NF4_K) {
     // K-major 4-bit weight [N rows][K cols]: 32 elements (16 B of codes) of one row per thread
     static_assert(BN * BK / C::NTHR == 32, "K-major 4-bit tile expects 32 elements per thread");
     const int j = tid >> 1, kofs = (tid & 1) * 32;
@@ -246,13 +221,8 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
     const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + wr * (s.b_cols / 2) + (k0 + kofs) / 2;
     const uint4 a = *reinterpret_cast<const uint4 *>(cp);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-    if constexpr (BSRC == B_Q4_K) {
-      const uint8_t *sp = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) + wr * (s.b_cols / 16) + (k0 + kofs) / 16;
-      r.w[4] = *reinterpret_cast<const uint16_t *>(sp);
-    } else {
-      r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64]);
-    }
-  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
+    r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64]);
+  } else if constexpr (BSRC == B_NF4_N) {
     // N-major 4-bit weight [K rows][N cols]: one k row, 32 columns (16 B of codes) per thread
     static_assert(BN == 256 && C::NTHR == 512, "N-major 4-bit tile expects 256 columns and 512 threads");
     const int row = tid >> 3, chunk = tid & 7;
@@ -262,11 +232,7 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) +
                                                        kk * (s.b_cols / 2) + n / 2);
       r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      if constexpr (BSRC == B_Q4_N)
-        r.w[4] = *reinterpret_cast<const uint16_t *>(reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16) +
-                                                    kk * (s.b_cols / 16) + n / 16);
-      else
-        r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
+      r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
     } else {
       r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
     }
@@ -307,39 +273,23 @@ template <class C, int BSRC>
 __device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const float *lut) {
   constexpr int BN = C::BN;
   const int tid = threadIdx.x;
-  if constexpr (BSRC == B_Q4_K || BSRC == B_NF4_K) {
+  if constexpr (BSRC == B_NF4_K) {
     const int j = tid >> 1, kofs = (tid & 1) * 32;
     uint4 *dst = reinterpret_cast<uint4 *>(Bs + j * SK + kofs);
-    float s0, s1;
-    if constexpr (BSRC == B_Q4_K) {
-      s0 = e4m3_hw<0>(r.w[4]);
-      s1 = e4m3_hw<1>(r.w[4]);
-    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t o[4];
-      if constexpr (BSRC == B_Q4_K)
-        fp4x8_hw(r.w[q], q < 2 ? s0 : s1, o);
-      else
-        nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
+      nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
       dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
     }
-  } else if constexpr (BSRC == B_Q4_N || BSRC == B_NF4_N) {
+  } else if constexpr (BSRC == B_NF4_N) {
     // natural layout: row k, columns chunk*32 .. +32 (element pairs along n)
     const int row = tid >> 3, chunk = tid & 7;
     uint4 *dst = reinterpret_cast<uint4 *>(Bs + row * skt<BN>() + chunk * 32);
-    float s0, s1;
-    if constexpr (BSRC == B_Q4_N) {
-      s0 = e4m3_hw<0>(r.w[4]);
-      s1 = e4m3_hw<1>(r.w[4]);
-    }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       uint32_t o[4];
-      if constexpr (BSRC == B_Q4_N)
-        fp4x8_hw(r.w[q], q < 2 ? s0 : s1, o);
-      else
-        nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
+      nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
       dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   } else if constexpr (BSRC == B_BF_K) {
@@ -579,12 +529,6 @@ __device__ __forceinline__ void epilogue_body(const GemmParams &p, const f32x16 
             p.out0[grow * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
           }
         }
-      } else if constexpr (EPI == EPI_STORE_F32) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int n = nt * BN + col0 + tn * 32 + (lane & 31);
-          if (FULL || n < p.N) p.outf[grow * p.N + n] = acc[tm][tn][v] * sc;
-        }
       }
     }
   }
@@ -787,31 +731,10 @@ __global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
 
   run_segment<C, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, sm, lut, active, acc);
 
-  // FP32 decode scales of segment 1.  NVFP4 weights with bf16 activations: the
-  // per-expert s_dec multiplies the whole accumulator in the epilogue (the
-  // producer of the LoRA segment's A operand divided it by s_dec).  NVFP4
-  // activations (per-row scales): segment 1 is rescaled before the LoRA segment.
-  constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
-  constexpr bool kQB = BSRC == B_Q4_K || BSRC == B_Q4_N;
-  float esc = 1.0f;
-  if constexpr (kQB && !kQA) esc = uniform_load(p.s1.b_sd + e);
-  if constexpr (kQA) {
-    float sb = 1.0f;
-    if constexpr (kQB) sb = p.s1.b_sd[e];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float sc = sb;
-        const int pos = m0 + wm * TM * 32 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (pos < n_e) {
-          const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
-          sc = sb * p.s1.a_sd[src];
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) acc[tm][tn][v] *= sc;
-      }
-  }
+  // NF4 weights are dequantized exactly to their bf16 operand (no separate decode
+  // scale) and the activations are bf16 rows
+  static_assert(ASRC == A_GATHER || ASRC == A_ROWS, "bf16 activation rows");
+  const float esc = 1.0f;
 
   if constexpr (B2SRC != B_NONE) {
     if (p.s2.K > 0) {
@@ -930,9 +853,6 @@ __device__ __forceinline__ void dma_rows(const GemmParams &p, int rb, int n_e, i
 // copy as an LDS event of unknown order and then drains every outstanding LDS read
 // (lgkmcnt(0)) before each use of an LDS result, exposing the read latency.  The
 // copies are waited for explicitly (wait_vm) before their stage is read.
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void *)p);
-}
 // lds: the wave-uniform LDS byte address (M0), kept in a scalar register
 __device__ __forceinline__ void dma_b128(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
@@ -940,8 +860,6 @@ __device__ __forceinline__ void dma_b128(const void *g, uint32_t lds) {
 __device__ __forceinline__ void dma_b32(const void *g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(lds) : "memory", "m0");
 }
-__device__ __forceinline__ void dma_b128(const void *g, const void *lds) { dma_b128(g, lds_addr(lds)); }
-__device__ __forceinline__ void dma_b32(const void *g, const void *lds) { dma_b32(g, lds_addr(lds)); }
 
 // A rows through registers (the LoRA segment; k >= K zeroed when MASKK)
 struct ARegs {
@@ -2155,9 +2073,11 @@ Seg seg_q(const void *a, int64_t a_ld, const bqm_qtensor &w, int K) {
   return s;
 }
 
+// the older staged kernel (NF4 weights)
 template <int BN, int ASRC, int BSRC, int B2SRC, int EPI>
 bqm_status launch(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
-  using C = typename std::conditional<BN == 256, BigCfg, SmallCfg>::type;
+  static_assert(BN == 256, "NF4 tiles are 256 columns wide");
+  using C = BigCfg;
   static_assert(C::BM == BM, "tile offsets are computed for BM rows");
   const int grid = gemm_grid(R, p.E, p.NT);
   moe_gemm<C, ASRC, BSRC, B2SRC, EPI><<<grid, C::NTHR, 0, s>>>(p);
