@@ -297,6 +297,59 @@ def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 64, 256), reps=20):
     return rows
 
 
+def colwise_comparison(s, inp, wgu, wdn, ev, sh, reps=5):
+    """The two-copy scheme as a comparison: the dgrad over a second, columnwise NVFP4
+    quantization (Q(W^T), read K-major) against the transposed read of the single
+    rowwise copy, at the same layer and routing.  Reports both dgrads' GEMM times, the
+    weight bytes each scheme holds, and how far the two dX results are apart (the
+    columnwise copy dequantizes to different values)."""
+    import torch
+    import bit_quantized_moe_amd as bqm
+    from tests.moe_harness import quantize_stack_gpu
+    dev = torch.device("cuda")
+    t = inp.w_gu.transpose(1, 2).contiguous()
+    cgu = quantize_stack_gpu(t, "nvfp4")
+    del t
+    t = inp.w_dn.transpose(1, 2).contiguous()
+    cdn = quantize_stack_gpu(t, "nvfp4")
+    del t
+    torch.cuda.empty_cache()
+    d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn,
+                    B_dn=inp.B_dn)
+    ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+    idx = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
+    dx_row, dx_col = torch.empty_like(out), torch.empty_like(out)
+    bqm.bqm_route(inp.logits, s.T, s.E, s.k, 0, idx, tw)
+    bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
+
+    def stages(fn):
+        res = {}
+        for it in range(reps + 1):
+            e = ev.create(2 * bqm.STAGE_COUNT)
+            d.stage_events = C.addressof(e)
+            fn()
+            torch.cuda.synchronize()
+            if it:
+                for si, n in enumerate(bqm.STAGES):
+                    if n in ("down_dgrad", "gate_up_dgrad"):
+                        res.setdefault(n, []).append(ev.elapsed_ms(e[2 * si], e[2 * si + 1]))
+        d.stage_events = None
+        return {k: round(sum(v) / len(v), 4) for k, v in res.items()}
+
+    row = stages(lambda: bqm.bqm_moe_dgrad(d, inp.dout, ws, dx_row, None))
+    col = stages(lambda: bqm.bqm_moe_dgrad_colwise(d, cgu, cdn, inp.dout, ws, dx_col, None))
+    diff = float((dx_col.float() - dx_row.float()).norm() / dx_row.float().norm())
+    wbytes = sum(q.codes.numel() + q.scales.numel() + q.s_dec.numel() * 4 for q in (wgu, wdn))
+    res = {"workload": "glm5.2 layer dgrad (T=16384), nvfp4 weights", "rowwise_transposed_read_ms": row,
+           "columnwise_copy_ms": col, "weight_bytes_one_copy": wbytes, "weight_bytes_two_copies": 2 * wbytes,
+           "dx_rel_diff_between_schemes": diff}
+    del cgu, cdn, d, ws, idx, tw, out, dx_row, dx_col
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_calls(ev, sh, fn, reps=3):
     """Mean hipEvent time of fn() over reps calls after one untimed call."""
     import torch
@@ -481,6 +534,8 @@ def main():
         del inp3, q3gu, q3dn
         torch.cuda.empty_cache()
         result["other_configs"] = others
+        # the two-copy scheme (a columnwise second quantization for the dgrad) as a comparison
+        result["columnwise_dgrad_comparison"] = colwise_comparison(s, inp, wgu, wdn, ev, sh)
         # decode-shaped forward over the GLM experts (serving side: weight-read-bound)
         result["decode_forward"] = {"workload": "glm5.2 shape, forward only (route + moe_fwd), nvfp4 weights, "
                                                 "LoRA r=64", "rows": decode_sweep(shape, wgu, wdn, ev, sh)}

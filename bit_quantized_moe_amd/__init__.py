@@ -6,7 +6,7 @@ the first call does, and raises if the library has not been built.
 """
 from ._lib import (BQMError, FMT_NF4, FMT_NVFP4, MoEDesc, QTensor, SCALE_PER_ROW, STAGES, STAGE_COUNT,
                    SCALE_PER_TENSOR, alloc_qtensor, bqm_abi_version, bqm_dequantize,
-                   bqm_last_error, bqm_lora_grad, bqm_moe_dgrad, bqm_moe_fwd,
+                   bqm_last_error, bqm_lora_grad, bqm_moe_dgrad, bqm_moe_dgrad_colwise, bqm_moe_fwd,
                    bqm_moe_workspace_size, bqm_permute, bqm_permute_workspace_size,
                    bqm_quantize_nf4, bqm_quantize_nvfp4, bqm_quantize_nvfp4_workspace_size,
                    bqm_route, load)

@@ -31,7 +31,7 @@ STATUS = {0: "BQM_OK", -1: "BQM_ERR_INVALID_ARG", -2: "BQM_ERR_SHAPE", -3: "BQM_
 EXPORTS = ["bqm_abi_version", "bqm_last_error", "bqm_quantize_nvfp4_workspace_size",
            "bqm_quantize_nvfp4", "bqm_quantize_nf4", "bqm_dequantize", "bqm_route",
            "bqm_permute_workspace_size", "bqm_permute", "bqm_moe_workspace_size", "bqm_moe_fwd",
-           "bqm_moe_dgrad", "bqm_lora_grad"]
+           "bqm_moe_dgrad", "bqm_moe_dgrad_colwise", "bqm_lora_grad"]
 
 
 class BQMError(RuntimeError):
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
         "bqm_moe_workspace_size": (sz, [C.POINTER(MoEDescC)]),
         "bqm_moe_fwd": (C.c_int, [C.POINTER(MoEDescC), vp, vp, vp, vp, vp, sz, vp]),
         "bqm_moe_dgrad": (C.c_int, [C.POINTER(MoEDescC), vp, vp, sz, vp, vp, vp]),
+        "bqm_moe_dgrad_colwise": (C.c_int, [C.POINTER(MoEDescC), C.POINTER(QTensorC), C.POINTER(QTensorC), vp, vp,
+                                            sz, vp, vp, vp]),
         "bqm_lora_grad": (C.c_int, [C.POINTER(MoEDescC), vp, vp, vp, sz, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
@@ -235,6 +237,13 @@ def bqm_moe_dgrad(d: MoEDesc, dy, ws, dx, dtopk_w=None, stream=None):
     dc = d.c()
     _check(load().bqm_moe_dgrad(C.byref(dc), _ptr(dy), _ptr(ws), ws.numel() * ws.element_size(),
                                 _ptr(dx), _ptr(dtopk_w), _stream(stream)))
+
+
+def bqm_moe_dgrad_colwise(d: MoEDesc, w_gu_col: QTensor, w_dn_col: QTensor, dy, ws, dx, dtopk_w=None, stream=None):
+    dc = d.c()
+    gc, nc = w_gu_col.c(), w_dn_col.c()
+    _check(load().bqm_moe_dgrad_colwise(C.byref(dc), C.byref(gc), C.byref(nc), _ptr(dy), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _ptr(dx), _ptr(dtopk_w), _stream(stream)))
 
 
 def bqm_lora_grad(d: MoEDesc, x, dy, ws, dA_gu, dB_gu, dA_dn, dB_dn, stream=None):

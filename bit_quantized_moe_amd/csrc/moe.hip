@@ -1533,7 +1533,9 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
   if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
 }
 
-template <int ASRC, int EPI>
+// LORN: the LoRA term takes an N-major B ([K = r rows][N cols], the dgrad's A_gu / A_dn)
+// through seg_lora_n; used when a dgrad runs on this K-major kernel over a columnwise copy
+template <int ASRC, int EPI, bool LORN = false>
 __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
@@ -1618,7 +1620,10 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
     int64_t arow2[ACH];
 #pragma unroll
     for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row(i), n_e - 1);
-    seg_lora<EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
+    if constexpr (LORN)
+      seg_lora_n(p.s2, e, nt, p.N, arow2, sm, vt, acc);
+    else
+      seg_lora<EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
   }
 
   if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
@@ -2093,11 +2098,11 @@ bool lora_folds_s_dec(const bqm_moe_desc *d, bool forward) {
 }
 
 // forward GEMM over NVFP4 weights: codes staged in LDS, decoded in registers
-template <int ASRC, int EPI>
+template <int ASRC, int EPI, bool LORN = false>
 bqm_status launch_fq(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
   static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
   const int grid = gemm_grid(R, p.E, p.NT);
-  fq::gemm_fwd_q4<ASRC, EPI><<<grid, fq::NTHR, 0, s>>>(p);
+  fq::gemm_fwd_q4<ASRC, EPI, LORN><<<grid, fq::NTHR, 0, s>>>(p);
   return launch_status(what);
 }
 
@@ -2283,16 +2288,22 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
   return launch_status("combine fwd");
 }
 
-extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, void *ws, size_t ws_bytes, uint16_t *dx,
-                                    float *dtopk_w, void *stream) {
-  BQM_TRY(check_desc(d, "bqm_moe_dgrad"));
+namespace bqm {
+namespace {
+// The dgrad.  col_gu / col_dn NULL: the GEMMs read the rowwise weights of d transposed.
+// Otherwise they read the columnwise copies (Q(W_gu^T) [E, H, 2I], Q(W_dn^T) [E, I, H])
+// K-major on the forward kernel.
+bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bqm_qtensor *col_dn, const uint16_t *dy,
+                      void *ws, size_t ws_bytes, uint16_t *dx, float *dtopk_w, void *stream, const char *who) {
+  BQM_TRY(check_desc(d, who));
   Ws w;
-  BQM_TRY(check_ws(d, ws, ws_bytes, "bqm_moe_dgrad", w));
+  BQM_TRY(check_ws(d, ws, ws_bytes, who, w));
+  const bool col = col_gu != nullptr;
   const int64_t R = d->T * d->k;
   if (R == 0) return BQM_OK;
-  BQM_REQUIRE(dy && dx, BQM_ERR_INVALID_ARG, "bqm_moe_dgrad: NULL pointer");
+  BQM_REQUIRE(dy && dx, BQM_ERR_INVALID_ARG, "%s: NULL pointer", who);
   BQM_REQUIRE(aligned16(dy) && aligned16(dx) && (!dtopk_w || aligned16(dtopk_w)), BQM_ERR_ALIGN,
-              "bqm_moe_dgrad: pointer not 16-byte aligned");
+              "%s: pointer not 16-byte aligned", who);
   hipStream_t s = as_stream(stream);
   const int H = (int)d->H, I = (int)d->I, r = d->r;
   const float ls = d->lora_scale;
@@ -2314,7 +2325,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.NT = (int)cdiv(r, 64);
     p.s1 = seg_bf16(dy, H, d->B_dn, H, r, H);
     p.out_scale = ls;
-    p.div_e = lora_folds_s_dec(d, false) ? d->w_dn.s_dec : nullptr;
+    p.div_e = lora_folds_s_dec(d, false) ? (col ? col_dn->s_dec : d->w_dn.s_dec) : nullptr;
     p.out0 = vdn;
     BQM_STAGE(d, BQM_STAGE_LORA_B_DN, s, (launch_lp<A_GATHER, true>(p, R, s, "lora_b^T down")));
   }
@@ -2323,12 +2334,14 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     GemmParams p = base_params(d, w);
     p.N = I;
     p.NT = (int)cdiv(I, 256);
-    p.s1 = seg_q(dy, H, d->w_dn, H);
+    p.s1 = seg_q(dy, H, col ? *col_dn : d->w_dn, H);
     p.s2 = seg_lora(vdn, d->A_dn, r, I, r);
     p.out0 = dh;
     p.h_in = w.at<float>(w.L.h);
     p.tw = w.at<float>(w.L.tw);
-    if (nf4)
+    if (col)
+      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fq<A_GATHER, EPI_DOWN_DGRAD, true>(p, R, s, "down dgrad (columnwise)")));
+    else if (nf4)
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
     else
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fd<A_GATHER, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
@@ -2340,7 +2353,7 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     p.NT = (int)cdiv(r, 64);
     p.s1 = seg_bf16(dh, 2 * I, d->B_gu, 2 * I, r, 2 * I);
     p.out_scale = ls;
-    p.div_e = lora_folds_s_dec(d, false) ? d->w_gu.s_dec : nullptr;
+    p.div_e = lora_folds_s_dec(d, false) ? (col ? col_gu->s_dec : d->w_gu.s_dec) : nullptr;
     p.out0 = vgu;
     BQM_STAGE(d, BQM_STAGE_LORA_B_GU, s, (launch_lp<A_ROWS, true>(p, R, s, "lora_b^T gate_up")));
   }
@@ -2349,10 +2362,12 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
     GemmParams p = base_params(d, w);
     p.N = H;
     p.NT = (int)cdiv(H, 256);
-    p.s1 = seg_q(dh, 2 * I, d->w_gu, 2 * I);
+    p.s1 = seg_q(dh, 2 * I, col ? *col_gu : d->w_gu, 2 * I);
     p.s2 = seg_lora(vgu, d->A_gu, r, H, r);
     p.out0 = dxr;
-    if (nf4)
+    if (col)
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fq<A_ROWS, EPI_STORE, true>(p, R, s, "gate_up dgrad (columnwise)")));
+    else if (nf4)
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
     else
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE>(p, R, s, "gate_up dgrad")));
@@ -2363,6 +2378,35 @@ extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, v
                                                                                   d->T, d->k, d->H, dx);
   mark(d, BQM_STAGE_COMBINE_DGRAD, 1, s);
   return launch_status("combine dgrad");
+}
+}  // namespace
+}  // namespace bqm
+
+extern "C" bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, void *ws, size_t ws_bytes, uint16_t *dx,
+                                    float *dtopk_w, void *stream) {
+  return dgrad_impl(d, nullptr, nullptr, dy, ws, ws_bytes, dx, dtopk_w, stream, "bqm_moe_dgrad");
+}
+
+extern "C" bqm_status bqm_moe_dgrad_colwise(const bqm_moe_desc *d, const bqm_qtensor *w_gu_col,
+                                            const bqm_qtensor *w_dn_col, const uint16_t *dy, void *ws,
+                                            size_t ws_bytes, uint16_t *dx, float *dtopk_w, void *stream) {
+  const char *who = "bqm_moe_dgrad_colwise";
+  BQM_TRY(check_desc(d, who));
+  BQM_REQUIRE(w_gu_col && w_dn_col, BQM_ERR_INVALID_ARG, "%s: columnwise copies are NULL", who);
+  BQM_REQUIRE(d->w_gu.fmt == BQM_FMT_NVFP4 && w_gu_col->fmt == BQM_FMT_NVFP4 && w_dn_col->fmt == BQM_FMT_NVFP4,
+              BQM_ERR_UNSUPPORTED, "%s: NVFP4 weights only", who);
+  BQM_REQUIRE(w_gu_col->scale_mode == BQM_SCALE_PER_TENSOR && w_dn_col->scale_mode == BQM_SCALE_PER_TENSOR,
+              BQM_ERR_INVALID_ARG, "%s: columnwise copies need per-tensor scales", who);
+  BQM_REQUIRE(w_gu_col->n_mat == d->E && w_gu_col->rows == d->H && w_gu_col->cols == 2 * d->I, BQM_ERR_SHAPE,
+              "%s: w_gu_col must be [E, H, 2I]", who);
+  BQM_REQUIRE(w_dn_col->n_mat == d->E && w_dn_col->rows == d->I && w_dn_col->cols == d->H, BQM_ERR_SHAPE,
+              "%s: w_dn_col must be [E, I, H]", who);
+  BQM_REQUIRE(w_gu_col->codes && w_gu_col->scales && w_gu_col->s_dec && w_dn_col->codes && w_dn_col->scales &&
+                  w_dn_col->s_dec,
+              BQM_ERR_INVALID_ARG, "%s: NULL pointer in a columnwise copy", who);
+  BQM_REQUIRE(aligned16(w_gu_col->codes) && aligned16(w_dn_col->codes), BQM_ERR_ALIGN,
+              "%s: codes not 16-byte aligned", who);
+  return dgrad_impl(d, w_gu_col, w_dn_col, dy, ws, ws_bytes, dx, dtopk_w, stream, who);
 }
 
 extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, const uint16_t *dy, void *ws,

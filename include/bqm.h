@@ -146,9 +146,11 @@ bqm_status bqm_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
  * [E, H, I], both rowwise quantized (NVFP4 per-tensor, or NF4).  LoRA per
  * expert in bf16: A_gu [E, r, H], B_gu [E, 2I, r], A_dn [E, r, I], B_dn [E, H, r]
  * (all NULL when r == 0).  H % 64 == 0, I % 64 == 0, 1 <= k <= min(E, 16),
- * 0 <= r <= 128.  act_quant = 1 selects the W4A4 path: the base GEMMs read
+ * 0 <= r <= 128.  act_quant = 1 selects the W4A4 path: the base GEMMs multiply
  * per-token NVFP4 (Four-Over-Six) activations while LoRA reads bf16 ones
- * (4-bitter page, section "Method"); NVFP4 weights only.
+ * (4-bitter page, section "Method"); NVFP4 weights only.  The quantized rows are
+ * expanded once into the workspace as bf16 val * sb (exact) and their per-row
+ * s_dec multiplies the FP32 accumulator.
  */
 /* Stages of the layer, for optional per-stage timing (stage_events below). */
 typedef enum {
@@ -213,6 +215,20 @@ bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, const int32_t *
  * Activation quantizers (W4A4) are the identity in this pass. */
 bqm_status bqm_moe_dgrad(const bqm_moe_desc *d, const uint16_t *dy, void *ws, size_t ws_bytes,
                          uint16_t *dx, float *dtopk_w, void *stream);
+
+/* The same input gradient over a second, columnwise quantization of the weights
+ * (the two-copy scheme the GLM page's section "Why can't we just transpose the
+ * one copy?" describes for FP4 tensor cores; a comparison variant here): w_gu_col
+ * = Q(W_gu^T) [E, H, 2I] and w_dn_col = Q(W_dn^T) [E, I, H], NVFP4 with per-tensor
+ * scales, each blocked along the dgrad's contraction axis and read K-major.  The
+ * base GEMMs then use DQ(Q(W^T))^T, not the forward's DQ(Q(W)).  The copies must
+ * carry the same per-tensor s_dec as d->w_gu and d->w_dn (quantizing W^T from its
+ * own amax gives exactly that: transposition keeps the amax), because
+ * bqm_lora_grad rescales by the rowwise s_dec.  Otherwise as bqm_moe_dgrad; the
+ * copies are caller-owned and read only. */
+bqm_status bqm_moe_dgrad_colwise(const bqm_moe_desc *d, const bqm_qtensor *w_gu_col,
+                                 const bqm_qtensor *w_dn_col, const uint16_t *dy, void *ws,
+                                 size_t ws_bytes, uint16_t *dx, float *dtopk_w, void *stream);
 
 /* LoRA weight gradients (the adapter is the trained part; per-expert A/B on
  * the 3-D stacks, nf4moe page, section "Does it actually train?"), from the

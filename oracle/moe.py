@@ -88,9 +88,28 @@ class LazyExperts:
         return self.cache[e]
 
 
+class ColumnwiseExperts:
+    """The second, columnwise quantization of an expert stack that FP4 tensor cores need
+    for the dgrad (GLM page, section "Why can't we just transpose the one copy?"): each
+    expert's W_e^T is quantized rowwise (NVFP4, per-tensor scale, Four-Over-Six), i.e.
+    with its 16-blocks along W_e's rows, and matrix(e) returns DQ(Q(W_e^T))^T, which
+    stands where the rowwise DQ(Q(W_e)) stands in the dgrad.  fetch(e) returns W_e as
+    float32 [rows, cols]."""
+
+    def __init__(self, fetch, four_over_six: bool = True):
+        self.fetch, self.fos = fetch, four_over_six
+        self.cache = {}
+
+    def matrix(self, e: int) -> np.ndarray:
+        if e not in self.cache:
+            xt = np.ascontiguousarray(fm.f32(self.fetch(e)).T)[None]
+            self.cache[e] = oq.dequantize_nvfp4_exact(oq.quantize_nvfp4(xt, self.fos))[0].T
+        return self.cache[e]
+
+
 def expert_matrix(q, e: int) -> np.ndarray:
     """Exact float64 DQ of expert e's 2-D slice (the GEMM operand)."""
-    if isinstance(q, LazyExperts):
+    if isinstance(q, (LazyExperts, ColumnwiseExperts)):
         return q.matrix(e)
     if isinstance(q, oq.NVFP4Tensor):
         one = oq.NVFP4Tensor(q.codes[e:e + 1], q.scales[e:e + 1], q.s_dec[e:e + 1],

@@ -46,8 +46,16 @@ def poison_experts(q, experts, fmt):
     torch.cuda.synchronize()
 
 
-def gpu_layer(inp: synth.LayerInputs, dev, lora_scale=1.0, poison_empty=False, lora=True):
-    """Forward + dgrad (+ LoRA grads) on the GPU.  Returns a dict of torch tensors."""
+def colwise_stacks_gpu(inp: synth.LayerInputs, dev):
+    """The columnwise copies Q(W_gu^T) [E, H, 2I] and Q(W_dn^T) [E, I, H] (NVFP4, per-tensor)."""
+    wgu_t = inp.w_gu.to(dev).transpose(1, 2).contiguous()
+    wdn_t = inp.w_dn.to(dev).transpose(1, 2).contiguous()
+    return quantize_stack_gpu(wgu_t, "nvfp4"), quantize_stack_gpu(wdn_t, "nvfp4")
+
+
+def gpu_layer(inp: synth.LayerInputs, dev, lora_scale=1.0, poison_empty=False, lora=True, colwise=False):
+    """Forward + dgrad (+ LoRA grads) on the GPU.  Returns a dict of torch tensors.
+    colwise: the dgrad runs over columnwise copies of the weights (bqm_moe_dgrad_colwise)."""
     import torch
     bqm = _bqm()
     s = inp.shape
@@ -76,7 +84,11 @@ def gpu_layer(inp: synth.LayerInputs, dev, lora_scale=1.0, poison_empty=False, l
     bqm.bqm_moe_fwd(d, x, idx, tw, out, ws)
     dx = torch.empty_like(out)
     dtw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
-    bqm.bqm_moe_dgrad(d, dout, ws, dx, dtw)
+    if colwise:
+        cgu, cdn = colwise_stacks_gpu(inp, dev)
+        bqm.bqm_moe_dgrad_colwise(d, cgu, cdn, dout, ws, dx, dtw)
+    else:
+        bqm.bqm_moe_dgrad(d, dout, ws, dx, dtw)
     res = dict(idx=idx, tw=tw, out=out, dx=dx, dtw=dtw, desc=d, ws=ws)
     if s.r and lora:
         g = dict(dA_gu=torch.empty((s.E, s.r, s.H), dtype=torch.float32, device=dev),
@@ -109,6 +121,14 @@ class HostInputs:
         dn = om.LazyExperts(lambda e: synth.f32_numpy(self._wdn[e]), s.fmt)
         lo = self.lora if self.lora is not None else [None] * 4
         return om.MoEWeights(s.fmt, gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant)
+
+    def weights_colwise(self, lora_scale=1.0):
+        """The same layer with the oracle's columnwise copies (DQ(Q(W^T))^T) as base weights."""
+        s = self.shape
+        gu = om.ColumnwiseExperts(lambda e: synth.f32_numpy(self._wgu[e]))
+        dn = om.ColumnwiseExperts(lambda e: synth.f32_numpy(self._wdn[e]))
+        lo = self.lora if self.lora is not None else [None] * 4
+        return om.MoEWeights("nvfp4", gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant)
 
 
 def _bf16_neighbours(a):
@@ -178,19 +198,21 @@ def resolve_w4a4_alternatives(g_out, g_dtw, o, h: HostInputs, rel_eps=2.0 ** -14
     return n_alt
 
 
-def oracle_layer(h: HostInputs, lora_scale=1.0, tokens=None, lora_experts=None):
+def oracle_layer(h: HostInputs, lora_scale=1.0, tokens=None, lora_experts=None, colwise=False):
     """Oracle forward + dgrad for the chosen tokens (all if None), and LoRA grads
-    for lora_experts (all experts if None and tokens is None)."""
+    for lora_experts (all experts if None and tokens is None).  colwise: the dgrad
+    uses the columnwise copies DQ(Q(W^T))^T."""
     s = h.shape
     w = h.weights(lora_scale)
+    wd = h.weights_colwise(lora_scale) if colwise else w
     idx, tw = orr.route(h.logits, s.k)
     out, cache = om.forward(w, h.x, idx, tw, tokens=tokens)
-    dx, dtw, bwd = om.dgrad(w, cache, h.dout, tw)
+    dx, dtw, bwd = om.dgrad(wd, cache, h.dout, tw)
     res = dict(idx=idx, tw=tw, out=out, dx=dx, dtw=dtw, tokens=cache["tokens"], w=w, cache=cache)
     if s.r and (tokens is None or lora_experts is not None):
         if lora_experts is not None:
             _, c2 = om.forward(w, h.x, idx, tw, experts=set(lora_experts))
-            _, _, b2 = om.dgrad(w, c2, h.dout, tw)
+            _, _, b2 = om.dgrad(wd, c2, h.dout, tw)
         else:
             c2, b2 = cache, bwd
         res["lora"] = om.lora_grad(w, c2, b2, s.E)

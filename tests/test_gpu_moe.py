@@ -19,13 +19,13 @@ def small(name, **kw):
     return synth.Shape(name, **base)
 
 
-def compare_full(shape, lora_scale=1.0, poison_empty=False):
+def compare_full(shape, lora_scale=1.0, poison_empty=False, colwise=False):
     dev = gpu()
-    log(f"layer {shape}")
+    log(f"layer {shape}" + (" (dgrad over columnwise copies)" if colwise else ""))
     inp = synth.layer_inputs(shape, device="cpu")
-    g = gpu_layer(inp, dev, lora_scale=lora_scale, poison_empty=poison_empty)
+    g = gpu_layer(inp, dev, lora_scale=lora_scale, poison_empty=poison_empty, colwise=colwise)
     h = HostInputs(inp)
-    o = oracle_layer(h, lora_scale=lora_scale)
+    o = oracle_layer(h, lora_scale=lora_scale, colwise=colwise)
     assert (g["idx"].cpu().numpy() == o["idx"]).all(), "routing indices"
     n_alt = resolve_w4a4_alternatives(np_f32(g["out"]), None, o, h)
     errs = {}
@@ -52,6 +52,13 @@ def test_small_nvfp4_partial_tiles():
     # (gate_up N = 2I = 384, down N = H = 320, dgrad N = I = 192 and H = 320) and
     # odd K-step counts (5, 3, 5, 6)
     compare_full(small("small_odd", H=320, I=192, T=260, E=12))
+
+
+def test_small_nvfp4_colwise_dgrad():
+    # the two-copy comparison variant: the dgrad over Q(W^T) read K-major, against the
+    # oracle's DQ(Q(W^T))^T; ragged tiles and partial column tiles included
+    compare_full(small("small_col", H=320, I=192, T=260, E=12), lora_scale=0.5, colwise=True)
+    compare_full(small("small_col2"), colwise=True)
 
 
 def test_small_nvfp4_no_lora():

@@ -86,6 +86,29 @@ def test_worked_example_with_four_over_six():
     assert (oq.unpack_nibbles(q.codes[0])[:, 3:] == 0).all()
 
 
+def test_worked_example_columnwise_copy():
+    # The page's column blocks {1,4}, {2,5}, {3,6} (amax 4, 5, 6) quantized as the rows of
+    # W^T, targets x*256.  {256, 1024}: k=6 sb=E4M3(170.7)=176, v=(1.45,5.82)->(1.5,6),
+    #   q*sb=(264,1056), error 8^2+32^2=1088; k=4 sb=256, v=(1,4), error 0 -> 4, DQ (1, 4).
+    # {512, 1280}: k=6 sb=E4M3(213.3)=208, v=(2.46,6.15)->(2,6), q*sb=(416,1248), error
+    #   96^2+32^2=10240; k=4 sb=320, v=(1.6,4)->(1.5,4), q*sb=(480,1280), error 1024 -> 4,
+    #   DQ (1.875, 5).
+    # {768, 1536}: k=6 sb=256, v=(3,6) exact; k=4 sb=384, v=(2,4) exact; the tie keeps 6.
+    from oracle import moe as om
+    g, W = _worked()
+    Wt = np.zeros((16, 16), dtype=np.float32)    # W^T padded: the column blocks become 16-blocks
+    Wt[:3, :2] = np.array(g["W"], dtype=np.float32).T
+    q = oq.quantize_nvfp4(Wt[None], four_over_six=True)
+    assert fm.e4m3_decode(q.scales[0, :3, 0]).tolist() == g["columnwise_block_scales"]
+    Wp = np.zeros((16, 3), dtype=np.float32)     # W padded with zero rows (16-blocks run along rows)
+    Wp[:2] = np.array(g["W"], dtype=np.float32)
+    col = om.ColumnwiseExperts(lambda e: Wp).matrix(0)[:2]
+    assert col.tolist() == g["columnwise_dq"]
+    # the rowwise copy of the same W gives other values in the column {1, 4}
+    dq_row = oq.dequantize_nvfp4(oq.quantize_nvfp4(W[None], four_over_six=True))[0][:, :3]
+    assert dq_row[:, 0].tolist() == [1, 4.5] and col[:, 0].tolist() == [1, 4]
+
+
 # ----------------------------------------------------------------------------
 # exact rational arithmetic and brute force
 # ----------------------------------------------------------------------------
