@@ -501,6 +501,23 @@ def main():
             ms = time_calls(ev, sh, lambda: (bqm.bqm_dequantize(wgu, ybuf), bqm.bqm_dequantize(wdn, ydn)))
             formats["nvfp4_dequantize"] = {"ms": ms, "GB/s": conv_bytes / ms / 1e6,
                                            "hbm_frac": conv_bytes / ms / 1e6 / PEAK_HBM_GBS}
+        if not args.no_quantizer:
+            # the strict FP32 reference form of the 4/6 choice (candidates scaled back up and
+            # compared with the original values) on the same stacks, and how often its choice
+            # agrees with the scaled-domain form used everywhere else
+            sgu = bqm.alloc_qtensor(bqm.FMT_NVFP4, s.E, 2 * s.I, s.H, device=dev)
+            sdn = bqm.alloc_qtensor(bqm.FMT_NVFP4, s.E, s.H, s.I, device=dev)
+            wsq2 = torch.empty(bqm.bqm_quantize_nvfp4_workspace_size(s.E, 2 * s.I, s.H, 0), dtype=torch.uint8,
+                               device=dev)
+            ms = time_calls(ev, sh, lambda: (bqm.bqm_quantize_nvfp4(inp.w_gu, 2, None, sgu, wsq2),
+                                             bqm.bqm_quantize_nvfp4(inp.w_dn, 2, None, sdn, wsq2)))
+            nblk = sgu.scales.numel() + sdn.scales.numel()
+            same = int((sgu.scales == wgu.scales).sum()) + int((sdn.scales == wdn.scales).sum())
+            formats["nvfp4_quantize_strict_4over6"] = {
+                "ms": ms, "GB/s": conv_bytes / ms / 1e6, "hbm_frac": conv_bytes / ms / 1e6 / PEAK_HBM_GBS,
+                "blocks": nblk, "same_choice_as_scaled_form": same / nblk}
+            del sgu, sdn, wsq2
+            torch.cuda.empty_cache()
         ngu = bqm.alloc_qtensor(bqm.FMT_NF4, s.E, 2 * s.I, s.H, device=dev)
         ndn = bqm.alloc_qtensor(bqm.FMT_NF4, s.E, s.H, s.I, device=dev)
         nf4_bytes = n_el * (2 + 0.5 + 4 / 64)

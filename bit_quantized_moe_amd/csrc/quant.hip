@@ -108,10 +108,40 @@ __device__ __forceinline__ float candidate(const float (&y)[16], float sb, float
   return err;
 }
 
+// The strict FP32 form of a candidate's error (the reference the 4-bitter page's fast
+// path is measured against): each candidate value is scaled back up to the original
+// domain, fl(fl(q * sb) * s_dec) (q * sb exact), and compared with the original x:
+// sum of fl(d * d), d = fl(x - that), in element order in FP32.  The codes are the same
+// as candidate()'s.
+__device__ __forceinline__ float strict_error(const float (&x)[16], float sb, float s_dec, uint32_t c_lo,
+                                              uint32_t c_hi) {
+  const uint32_t c[2] = {c_lo, c_hi};
+  float err = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    f32x2 q;
+    switch (p & 3) {
+      case 0: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 0); break;
+      case 1: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 1); break;
+      case 2: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 2); break;
+      default: q = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[p >> 2], 1.0f, 3); break;
+    }
+    const float d0 = x[2 * p] - (q.x * sb) * s_dec;
+    err = err + d0 * d0;
+    const float d1 = x[2 * p + 1] - (q.y * sb) * s_dec;
+    err = err + d1 * d1;
+  }
+  return err;
+}
+
+// 4/6 modes: off (scale t/6 only), the scaled-domain error (target scaled down once),
+// and the strict FP32 reference error
+constexpr int kFosOff = 0, kFosScaled = 1, kFosStrict = 2;
+
 // Quantize one block of 16 bf16 values held as 8 words; returns the E4M3 code.
 // rcp[c] = fl(1 / e4m3(c)) (0 for c = 0).
-template <bool kFos>
-__device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float s_enc, const float *rcp,
+template <int kMode>
+__device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float s_enc, float s_dec, const float *rcp,
                                                   uint32_t &lo, uint32_t &hi) {
   float y[16];
   float t = 0.0f;
@@ -123,12 +153,24 @@ __device__ __forceinline__ uint32_t quant_block16(const uint32_t (&w)[8], float 
   }
   uint32_t sb6, sb4;
   e4m3_pair(div6(t), t * 0.25f, sb6, sb4);  // t * 0.25 == t/4 exactly rounded
-  const float e6 = candidate(y, __builtin_amdgcn_cvt_f32_fp8(sb6, 0), rcp[sb6], lo, hi);
+  const float f6 = __builtin_amdgcn_cvt_f32_fp8(sb6, 0);
+  float e6 = candidate(y, f6, rcp[sb6], lo, hi);
   uint32_t sb = sb6;
-  if (kFos) {
+  if (kMode != kFosOff) {
     if (sb4 != sb6) {
       uint32_t l4, h4;
-      const float e4 = candidate(y, __builtin_amdgcn_cvt_f32_fp8(sb4, 0), rcp[sb4], l4, h4);
+      const float f4 = __builtin_amdgcn_cvt_f32_fp8(sb4, 0);
+      float e4 = candidate(y, f4, rcp[sb4], l4, h4);
+      if (kMode == kFosStrict) {
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x[2 * i] = bf16_lo(w[i]);
+          x[2 * i + 1] = bf16_hi(w[i]);
+        }
+        e6 = strict_error(x, f6, s_dec, lo, hi);
+        e4 = strict_error(x, f4, s_dec, l4, h4);
+      }
       if (e4 < e6) {
         sb = sb4;
         lo = l4;
@@ -229,7 +271,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_amax(const uint4 *__restrict__
 }
 
 // grid = n_mat * G workgroups; s_dec from amax (bf16 magnitude bits) or s_dec_in
-template <bool kFos>
+template <int kMode>
 __global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
     const uint4 *__restrict__ x, int64_t blocks_per_mat, int64_t G, const uint32_t *__restrict__ amax,
     const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes, uint8_t *__restrict__ scales,
@@ -253,7 +295,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
     uint32_t w[8];
     load_block16(xm + 2 * blk, w);
     uint32_t lo, hi;
-    const uint32_t sb = quant_block16<kFos>(w, s_enc, rcp, lo, hi);
+    const uint32_t sb = quant_block16<kMode>(w, s_enc, s_dec, rcp, lo, hi);
     st_nt(&cm[blk], make_uint2(lo, hi));
     __builtin_nontemporal_store((uint8_t)sb, &sm[blk]);
   }
@@ -261,7 +303,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
 
 // Per-row quantizer: one wave per row (the per-token activation scale, computed
 // across the row in the same kernel).  rows_total = n_mat * rows.
-template <bool kFos>
+template <int kMode>
 __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
     const uint4 *__restrict__ x, int64_t rows_total, int64_t blocks_per_row,
     const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes,
@@ -295,7 +337,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
     uint32_t w[8];
     load_block16(xr + 2 * blk, w);
     uint32_t lo, hi;
-    uint32_t sb = quant_block16<kFos>(w, s_enc, rcp, lo, hi);
+    uint32_t sb = quant_block16<kMode>(w, s_enc, s_dec, rcp, lo, hi);
     codes[row * blocks_per_row + blk] = make_uint2(lo, hi);
     scales[row * blocks_per_row + blk] = (uint8_t)sb;
   }
@@ -533,7 +575,9 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
   BQM_REQUIRE(aligned16(x), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: x not 16-byte aligned");
   BQM_REQUIRE(!s_dec_in || aligned16(s_dec_in), BQM_ERR_ALIGN,
               "bqm_quantize_nvfp4: s_dec_in not 16-byte aligned");
-  out->four_over_six = four_over_six ? 1 : 0;
+  BQM_REQUIRE(four_over_six >= kFosOff && four_over_six <= kFosStrict, BQM_ERR_INVALID_ARG,
+              "bqm_quantize_nvfp4: four_over_six must be 0, 1 or 2");
+  out->four_over_six = four_over_six;
   const float denom = four_over_six ? 6.0f * 256.0f : 6.0f * 448.0f;
   hipStream_t s = as_stream(stream);
   const uint4 *xv = reinterpret_cast<const uint4 *>(x);
@@ -543,12 +587,15 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
     const int64_t rows_total = n_mat * rows;
     const int64_t bpr = cols / 16;
     int grid = (int)cdiv(rows_total, kThreads / 64);
-    if (four_over_six)
-      nvfp4_quant_rows<true><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
-                                                       out->s_dec);
+    if (four_over_six == kFosStrict)
+      nvfp4_quant_rows<kFosStrict><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
+                                                             out->s_dec);
+    else if (four_over_six)
+      nvfp4_quant_rows<kFosScaled><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
+                                                             out->s_dec);
     else
-      nvfp4_quant_rows<false><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
-                                                        out->s_dec);
+      nvfp4_quant_rows<kFosOff><<<grid, kThreads, 0, s>>>(xv, rows_total, bpr, s_dec_in, denom, cv, sv,
+                                                          out->s_dec);
     return launch_status("nvfp4_quant_rows");
   }
   const int64_t blocks_per_mat = per_mat / 16;
@@ -568,12 +615,15 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
     st = launch_status("nvfp4_amax");
     if (st != BQM_OK) return st;
   }
-  if (four_over_six)
-    nvfp4_quant_tensor<true><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom, cv,
-                                                                   sv, out->s_dec);
+  if (four_over_six == kFosStrict)
+    nvfp4_quant_tensor<kFosStrict><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom,
+                                                                         cv, sv, out->s_dec);
+  else if (four_over_six)
+    nvfp4_quant_tensor<kFosScaled><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom,
+                                                                         cv, sv, out->s_dec);
   else
-    nvfp4_quant_tensor<false><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom, cv,
-                                                                    sv, out->s_dec);
+    nvfp4_quant_tensor<kFosOff><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom,
+                                                                      cv, sv, out->s_dec);
   return launch_status("nvfp4_quant_tensor");
 }
 

@@ -93,7 +93,12 @@ const char *bqm_last_error(void);
  *   BQM_SCALE_PER_ROW:    one per row (per-token activation scales).
  * M = 256 with four_over_six != 0 (then each 16-block tries the scale t/6 and
  * t/4 and keeps the one with the lower FP32 squared error, ties keeping t/6),
- * M = 448 otherwise.  s_dec_in (nullable, same shape as out->s_dec) replaces
+ * M = 448 otherwise.  four_over_six = 1 measures that error in the scaled domain
+ * (the target scaled down once by 1/s_dec, against q*sb: the page's fast path);
+ * four_over_six = 2 uses the strict FP32 reference instead (each candidate scaled
+ * back up, fl(fl(q*sb)*s_dec), against the original x); codes and candidate
+ * scales are computed the same way, only the choice may differ (at near-ties).
+ * out->four_over_six records the mode.  s_dec_in (nullable, same shape as out->s_dec) replaces
  * the amax-derived scale.  All rounding is round-to-nearest-even, E4M3 and E2M1
  * saturate.  Result codes and scales are deterministic bit patterns.
  * ws: per-tensor mode without s_dec_in needs bqm_quantize_nvfp4_workspace_size()

@@ -71,10 +71,15 @@ def global_decode_scale(amax, four_over_six: bool) -> tuple[np.ndarray, np.ndarr
     return s_dec, s_enc
 
 
-def _quantize_blocks(y: np.ndarray, four_over_six: bool):
+def _quantize_blocks(y: np.ndarray, four_over_six: bool, strict=None):
     """Quantize already-scaled blocks y [nb, 16] (float32).
 
-    Returns (magnitude codes [nb,16] uint8, scale bits [nb] uint8).
+    strict = (x [nb,16], s_dec [nb]) selects the strict FP32 reference error of the
+    4-bitter page (section "Four-Over-Six for RL Weights and Activations"): each
+    candidate is scaled back up, fl(fl(q*sb) * s_dec), and compared with the original
+    x; otherwise the error is taken in the scaled domain against y (the fast path that
+    scales the target down once).  Returns (magnitude codes [nb,16] uint8, scale bits
+    [nb] uint8).
     """
     ay = np.abs(y)
     t = ay.max(axis=1)                                    # block amax of the scaled target
@@ -87,7 +92,12 @@ def _quantize_blocks(y: np.ndarray, four_over_six: bool):
         v = (ay * r[:, None]).astype(np.float32)
         mag = fm.e2m1_mag_code(v)
         qs = (fm.E2M1_VALUES[mag] * sb[:, None]).astype(np.float32)   # exact
-        d = (ay - qs).astype(np.float32)
+        if strict is None:
+            d = (ay - qs).astype(np.float32)
+        else:
+            ax, sdec = strict
+            up = (qs * sdec[:, None]).astype(np.float32)                # one rounding
+            d = (np.abs(ax) - up).astype(np.float32)
         dd = (d * d).astype(np.float32)
         err = np.zeros(y.shape[0], dtype=np.float32)
         for i in range(BLOCK):                              # sequential FP32 sum
@@ -116,24 +126,30 @@ def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def _quantize_rows_with_scale(x: np.ndarray, s_enc_rows: np.ndarray, four_over_six: bool):
-    """x [rows, C] float32, s_enc per row [rows] -> (codes [rows,C/2], scales [rows,C/16])."""
+def _quantize_rows_with_scale(x: np.ndarray, s_enc_rows: np.ndarray, four_over_six: bool, s_dec_rows=None):
+    """x [rows, C] float32, s_enc per row [rows] -> (codes [rows,C/2], scales [rows,C/16]).
+    s_dec_rows (per row) given: the strict FP32 4/6 error."""
     rows, C = x.shape
     y = (x * s_enc_rows[:, None]).astype(np.float32)
     yb = y.reshape(rows * (C // BLOCK), BLOCK)
-    mag, sb = _quantize_blocks(yb, four_over_six)
+    strict = None
+    if s_dec_rows is not None:
+        strict = (x.reshape(-1, BLOCK), np.repeat(fm.f32(s_dec_rows), C // BLOCK))
+    mag, sb = _quantize_blocks(yb, four_over_six, strict)
     sign = np.signbit(x.reshape(-1, BLOCK)).astype(np.uint8) << 3
     nib = (mag | sign).reshape(rows, C)
     return pack_nibbles(nib), sb.reshape(rows, C // BLOCK)
 
 
 def quantize_nvfp4(x, four_over_six: bool = True, per_row: bool = False,
-                   s_dec_in=None) -> NVFP4Tensor:
+                   s_dec_in=None, strict: bool = False) -> NVFP4Tensor:
     """Rowwise NVFP4 quantization of a stack x [n_mat, rows, C] (bf16 values as float32).
 
     per_row=False: one FP32 scale per 2-D matrix (weights).  per_row=True: one
     per row (per-token activation scales).  s_dec_in, if given, replaces the
-    amax-derived decode scale ([n_mat] or [n_mat, rows]).
+    amax-derived decode scale ([n_mat] or [n_mat, rows]).  strict: the 4/6 choice
+    uses the strict FP32 reference error (candidates scaled back up, compared with
+    x) instead of the scaled-domain one; codes and candidate scales are the same.
     """
     x = fm.f32(x)
     if x.ndim == 2:
@@ -154,7 +170,10 @@ def quantize_nvfp4(x, four_over_six: bool = True, per_row: bool = False,
     scales = np.empty((n_mat, rows, C // BLOCK), dtype=np.uint8)
     for e in range(n_mat):
         se = s_enc[e] if per_row else np.full(rows, s_enc[e], dtype=np.float32)
-        codes[e], scales[e] = _quantize_rows_with_scale(x[e], se, four_over_six)
+        sd = None
+        if strict and four_over_six:
+            sd = s_dec[e] if per_row else np.full(rows, s_dec[e], dtype=np.float32)
+        codes[e], scales[e] = _quantize_rows_with_scale(x[e], se, four_over_six, sd)
     return NVFP4Tensor(codes, scales, s_dec.astype(np.float32), four_over_six, per_row)
 
 

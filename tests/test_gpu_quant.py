@@ -105,6 +105,29 @@ def test_nvfp4_dequantize_bit_exact(per_row):
     assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
 
 
+@pytest.mark.parametrize("per_row", [False, True])
+def test_nvfp4_strict_four_over_six_bit_exact(per_row):
+    """four_over_six = 2: the strict FP32 reference error for the 4/6 choice."""
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    shape = (3, 64, 256) if not per_row else (2, 33, 768)
+    log(f"nvfp4 strict 4/6 {shape} per_row={per_row}")
+    x = synth.normal(shape, 0.02 if not per_row else 1.0, (96, shape[1]), device="cpu", outliers=True).to(dev)
+    n, rows, cols = shape
+    mode = bqm.SCALE_PER_ROW if per_row else bqm.SCALE_PER_TENSOR
+    q = bqm.alloc_qtensor(bqm.FMT_NVFP4, n, rows, cols, device=dev, scale_mode=mode)
+    ws = torch.empty(max(bqm.bqm_quantize_nvfp4_workspace_size(n, rows, cols, mode), 16), dtype=torch.uint8, device=dev)
+    bqm.bqm_quantize_nvfp4(x, 2, None, q, ws)
+    for m in range(n):
+        ref = oq.quantize_nvfp4(np_f32(x[m:m + 1]), four_over_six=True, per_row=per_row, strict=True)
+        assert (np_u8(q.codes[m]) == ref.codes[0]).all(), f"matrix {m}: codes"
+        assert (np_u8(q.scales[m]) == ref.scales[0]).all(), f"matrix {m}: scales"
+        got_sd = np_f32(q.s_dec.view(n, -1)[m]) if per_row else np_f32(q.s_dec[m:m + 1])
+        assert (got_sd.view(np.uint32) == ref.s_dec.reshape(-1).view(np.uint32)).all()
+    assert q.four_over_six == 2
+
+
 @pytest.mark.parametrize("fos", [True, False])
 def test_nvfp4_block_scales_over_the_e4m3_range(fos):
     """Block scales E4M3(t/6) and E4M3(t/4) for every bf16 block maximum t in [2^-30, 2^13]:
