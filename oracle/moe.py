@@ -32,6 +32,13 @@ on the 3-D stacks, "nf4moe", section "Does it actually train?"):
     dB_dn = s (w dOut)^T (a_b A_dn^T)  dA_dn = s (w dOut B_dn)^T a_b
 Experts that receive no token get exact zeros.
 
+Shared-A layout ("Getting GLM-5.2 NVFP4 Post-Training off the ground", its
+serving part, row 3 of its table of issues: the adapter there has one LoRA-A
+common to all experts and a LoRA-B per expert): A_gu
+is [r, H] and A_dn [r, I], used by every expert in the formulas above, and
+dA_gu, dA_dn are the sums of those per-expert terms over all experts (the
+gradient of one matrix that every expert reads).
+
 Readings: s (the LoRA scale) defaults to 1, the pages give no alpha; LoRA reads
 the unquantized bf16 activations in W4A4; the activation quantizers are the
 identity in the backward (straight-through), the backward keeping bf16
@@ -54,16 +61,23 @@ class MoEWeights:
     fmt: str                    # "nvfp4" or "nf4"
     gu: object                  # NVFP4Tensor / NF4Tensor over [E, 2I, H]
     dn: object                  # NVFP4Tensor / NF4Tensor over [E, H, I]
-    A_gu: Optional[np.ndarray]  # [E, r, H]  (bf16 values)
+    A_gu: Optional[np.ndarray]  # [E, r, H]  (bf16 values); [r, H] when shared_a
     B_gu: Optional[np.ndarray]  # [E, 2I, r]
-    A_dn: Optional[np.ndarray]  # [E, r, I]
+    A_dn: Optional[np.ndarray]  # [E, r, I]; [r, I] when shared_a
     B_dn: Optional[np.ndarray]  # [E, H, r]
     lora_scale: float = 1.0
     act_quant: bool = False     # W4A4: per-token NVFP4 (+4/6) activations in the base GEMMs
+    shared_a: bool = False      # one LoRA-A for all experts, per-expert LoRA-B
 
     @property
     def r(self) -> int:
-        return 0 if self.A_gu is None else self.A_gu.shape[1]
+        return 0 if self.A_gu is None else self.A_gu.shape[-2]
+
+    def a_gu(self, e: int) -> np.ndarray:
+        return (self.A_gu if self.shared_a else self.A_gu[e]).astype(np.float64)
+
+    def a_dn(self, e: int) -> np.ndarray:
+        return (self.A_dn if self.shared_a else self.A_dn[e]).astype(np.float64)
 
 
 class LazyExperts:
@@ -176,7 +190,7 @@ def forward(w: MoEWeights, x, topk_idx, topk_w, tokens=None, round_points: bool 
         Xt = act_dq(X) if w.act_quant else X
         Wgu = expert_matrix(w.gu, e)
         h = Xt @ Wgu.T
-        U_gu = X @ w.A_gu[e].astype(np.float64).T if r else None
+        U_gu = X @ w.a_gu(e).T if r else None
         if r:
             h = h + s * (U_gu @ w.B_gu[e].astype(np.float64).T)
         I = h.shape[1] // 2
@@ -186,7 +200,7 @@ def forward(w: MoEWeights, x, topk_idx, topk_w, tokens=None, round_points: bool 
         at = act_dq(a_b) if w.act_quant else a_b
         Wdn = expert_matrix(w.dn, e)
         y = at @ Wdn.T
-        U_dn = a_b @ w.A_dn[e].astype(np.float64).T if r else None
+        U_dn = a_b @ w.a_dn(e).T if r else None
         if r:
             y = y + s * (U_dn @ w.B_dn[e].astype(np.float64).T)
         cache["per_expert"][e] = dict(fs=fs, t=t, X=X, g=g, u=u, a_b=a_b, y=y,
@@ -231,7 +245,7 @@ def dgrad(w: MoEWeights, cache, dout, topk_w, round_points: bool = True):
         da_u = dO @ Wdn
         V_dn = dO @ w.B_dn[e].astype(np.float64) if r else None
         if r:
-            da_u = da_u + s * (V_dn @ w.A_dn[e].astype(np.float64))
+            da_u = da_u + s * (V_dn @ w.a_dn(e))
         dtw[t, j] = np.einsum("nh,nh->n", dO, c["y"])
         wr = tw[t, j][:, None]
         da = wr * da_u
@@ -245,7 +259,7 @@ def dgrad(w: MoEWeights, cache, dout, topk_w, round_points: bool = True):
         dxr = dh_b @ Wgu
         V_gu = dh_b @ w.B_gu[e].astype(np.float64) if r else None
         if r:
-            dxr = dxr + s * (V_gu @ w.A_gu[e].astype(np.float64))
+            dxr = dxr + s * (V_gu @ w.a_gu(e))
         for i, f in enumerate(fs):
             dx_rows[int(f)] = dxr[i]
         bwd[e] = dict(dh_b=dh_b, V_gu=V_gu, V_dn=V_dn, wr=wr, dO=dO)
@@ -262,11 +276,12 @@ def dgrad(w: MoEWeights, cache, dout, topk_w, round_points: bool = True):
 
 
 def lora_grad(w: MoEWeights, cache, bwd, E: int):
-    """Per-expert LoRA gradients (float64): dA_gu [E,r,H], dB_gu [E,2I,r], dA_dn [E,r,I], dB_dn [E,H,r]."""
+    """LoRA gradients (float64): dA_gu [E,r,H], dB_gu [E,2I,r], dA_dn [E,r,I], dB_dn [E,H,r];
+    with shared_a, dA_gu [r,H] and dA_dn [r,I] are the sums over the experts."""
     r = w.r
     s = float(w.lora_scale)
-    H = w.A_gu.shape[2]
-    I = w.A_dn.shape[2]
+    H = w.A_gu.shape[-1]
+    I = w.A_dn.shape[-1]
     dA_gu = np.zeros((E, r, H))
     dB_gu = np.zeros((E, 2 * I, r))
     dA_dn = np.zeros((E, r, I))
@@ -278,6 +293,8 @@ def lora_grad(w: MoEWeights, cache, bwd, E: int):
         wdO = b["wr"] * b["dO"]
         dB_dn[e] = s * (wdO.T @ c["U_dn"])
         dA_dn[e] = s * ((b["wr"] * b["V_dn"]).T @ c["a_b"])
+    if w.shared_a:
+        return dA_gu.sum(axis=0), dB_gu, dA_dn.sum(axis=0), dB_dn
     return dA_gu, dB_gu, dA_dn, dB_dn
 
 

@@ -18,7 +18,7 @@ def _bf16(a):
     return fm.bf16_round(np.asarray(a, dtype=np.float32))
 
 
-def make_layer(E=4, H=32, I=16, k=2, T=6, r=4, seed=0, fmt="nvfp4", act_quant=False, s=1.0):
+def make_layer(E=4, H=32, I=16, k=2, T=6, r=4, seed=0, fmt="nvfp4", act_quant=False, s=1.0, shared_a=False):
     rng = np.random.default_rng(seed)
     x = _bf16(rng.standard_normal((T, H)))
     wgu = _bf16(rng.standard_normal((E, 2 * I, H)) * 0.2)
@@ -27,11 +27,14 @@ def make_layer(E=4, H=32, I=16, k=2, T=6, r=4, seed=0, fmt="nvfp4", act_quant=Fa
     B_gu = _bf16(rng.standard_normal((E, 2 * I, r)) * 0.1)
     A_dn = _bf16(rng.standard_normal((E, r, I)) * 0.1)
     B_dn = _bf16(rng.standard_normal((E, H, r)) * 0.1)
+    if shared_a:
+        A_gu, A_dn = A_gu[0], A_dn[0]
     if fmt == "nvfp4":
         gu, dn = oq.quantize_nvfp4(wgu), oq.quantize_nvfp4(wdn)
     else:
         gu, dn = oq.quantize_nf4(wgu), oq.quantize_nf4(wdn)
-    w = om.MoEWeights(fmt, gu, dn, A_gu, B_gu, A_dn, B_dn, lora_scale=s, act_quant=act_quant)
+    w = om.MoEWeights(fmt, gu, dn, A_gu, B_gu, A_dn, B_dn, lora_scale=s, act_quant=act_quant,
+                      shared_a=shared_a)
     lg = rng.standard_normal((T, E)).astype(np.float32)
     idx, tw = orr.route(lg, k)
     dout = _bf16(rng.standard_normal((T, H)))
@@ -88,18 +91,21 @@ def _torch_layer(w, x, idx, tw):
     k = idx.shape[1]
     s = w.lora_scale
     out = torch.zeros((T, H), dtype=torch.float64)
-    for e in range(w.A_gu.shape[0]):
+    for e in range(w.B_gu.shape[0]):
         tt, jj = np.nonzero(idx == e)
         if tt.size == 0:
             continue
         Wgu = torch.tensor(om.expert_matrix(w.gu, e))
         Wdn = torch.tensor(om.expert_matrix(w.dn, e))
+        # a shared A is one leaf that every expert reads: autograd sums its uses
+        Agu = lora["A_gu"] if w.shared_a else lora["A_gu"][e]
+        Adn = lora["A_dn"] if w.shared_a else lora["A_dn"][e]
         X = xs[tt]
-        h = X @ Wgu.T + s * (X @ lora["A_gu"][e].T) @ lora["B_gu"][e].T
+        h = X @ Wgu.T + s * (X @ Agu.T) @ lora["B_gu"][e].T
         I = Wdn.shape[1]
         g, u = h[:, :I], h[:, I:]
         a = torch.nn.functional.silu(g) * u
-        y = a @ Wdn.T + s * (a @ lora["A_dn"][e].T) @ lora["B_dn"][e].T
+        y = a @ Wdn.T + s * (a @ Adn.T) @ lora["B_dn"][e].T
         out = out.index_add(0, torch.tensor(tt), y * tws[tt, jj][:, None])
     return out, xs, tws, lora
 
@@ -116,6 +122,64 @@ def test_dgrad_and_lora_grads_match_torch_autograd():
     assert np.allclose(dtw, tws.grad.numpy(), rtol=1e-10, atol=1e-12)
     for mine, name in ((dA_gu, "A_gu"), (dB_gu, "B_gu"), (dA_dn, "A_dn"), (dB_dn, "B_dn")):
         assert np.allclose(mine, lora[name].grad.numpy(), rtol=1e-10, atol=1e-12), name
+
+
+def test_shared_a_grads_match_torch_autograd():
+    # one LoRA-A for every expert (the GLM page's adapter layout): its gradient is
+    # the sum of every expert's use; E=5 with T=7, k=2 leaves room for an idle expert
+    w, x, idx, tw, dout, _ = make_layer(E=5, H=32, I=16, k=2, T=7, r=4, seed=12, s=0.6, shared_a=True)
+    out, cache = om.forward(w, x, idx, tw, round_points=False)
+    dX, dtw, bwd = om.dgrad(w, cache, dout, tw, round_points=False)
+    dA_gu, dB_gu, dA_dn, dB_dn = om.lora_grad(w, cache, bwd, E=5)
+    assert dA_gu.shape == w.A_gu.shape and dA_dn.shape == w.A_dn.shape
+    tout, xs, tws, lora = _torch_layer(w, x, idx, tw)
+    assert np.allclose(out, tout.detach().numpy(), rtol=1e-12, atol=1e-12)
+    tout.backward(torch.tensor(np.asarray(dout, np.float64)))
+    assert np.allclose(dX, xs.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dtw, tws.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for mine, name in ((dA_gu, "A_gu"), (dB_gu, "B_gu"), (dA_dn, "A_dn"), (dB_dn, "B_dn")):
+        assert np.allclose(mine, lora[name].grad.numpy(), rtol=1e-10, atol=1e-12), name
+
+
+def test_shared_a_central_finite_differences():
+    # d<dOut, out>/dA along a random direction, for the shared gate_up and down A
+    w, x, idx, tw, dout, _ = make_layer(E=3, H=16, I=16, k=2, T=5, r=2, seed=13, s=0.8, shared_a=True)
+    x64 = np.asarray(x, np.float64)
+    d64 = np.asarray(dout, np.float64)
+    _, cache = om.forward(w, x64, idx, tw, round_points=False)
+    _, _, bwd = om.dgrad(w, cache, d64, tw, round_points=False)
+    grads = om.lora_grad(w, cache, bwd, E=3)
+    rng = np.random.default_rng(1)
+    eps = 1e-3
+    for name, g in (("A_gu", grads[0]), ("A_dn", grads[2])):
+        base = getattr(w, name).astype(np.float64)
+        v = rng.standard_normal(base.shape)
+
+        def loss(a):
+            wv = om.MoEWeights(w.fmt, w.gu, w.dn, **{**dict(A_gu=w.A_gu, B_gu=w.B_gu, A_dn=w.A_dn, B_dn=w.B_dn),
+                                                      name: a}, lora_scale=w.lora_scale, shared_a=True)
+            return (om.forward(wv, x64, idx, tw, round_points=False)[0] * d64).sum()
+        fd = (loss(base + eps * v) - loss(base - eps * v)) / (2 * eps)
+        assert np.isclose(fd, (g * v).sum(), rtol=1e-6), name
+
+
+def test_shared_a_equals_replicated_per_expert_a():
+    # the shared layout is the per-expert layout with E equal slices: same outputs,
+    # and the shared gradient is the sum of the per-expert ones (rounding points on)
+    w, x, idx, tw, dout, _ = make_layer(E=4, H=32, I=16, k=2, T=9, r=4, seed=14, s=0.5, shared_a=True)
+    rep = om.MoEWeights(w.fmt, w.gu, w.dn, np.repeat(w.A_gu[None], 4, 0), w.B_gu,
+                        np.repeat(w.A_dn[None], 4, 0), w.B_dn, lora_scale=w.lora_scale)
+    o1, c1 = om.forward(w, x, idx, tw)
+    o2, c2 = om.forward(rep, x, idx, tw)
+    assert (o1 == o2).all()
+    d1, t1, b1 = om.dgrad(w, c1, dout, tw)
+    d2, t2, b2 = om.dgrad(rep, c2, dout, tw)
+    assert (d1 == d2).all() and (t1 == t2).all()
+    g1 = om.lora_grad(w, c1, b1, E=4)
+    g2 = om.lora_grad(rep, c2, b2, E=4)
+    assert np.allclose(g1[0], g2[0].sum(0), rtol=1e-13, atol=1e-15)
+    assert np.allclose(g1[2], g2[2].sum(0), rtol=1e-13, atol=1e-15)
+    assert (g1[1] == g2[1]).all() and (g1[3] == g2[3]).all()
 
 
 def test_dgrad_central_finite_differences():
