@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes as C
+import dataclasses
 import json
 import os
 import sys
@@ -136,7 +137,7 @@ def token_sweep(shape, wgu, wdn, ev, sh, tokens=(438, 1024, 2048, 4096, 8192), r
         s = dataclasses.replace(shape, T=T, name=f"{shape.name}_T{T}")
         inp = synth.layer_inputs(s, device=dev, with_weights=False)
         d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn,
-                        B_dn=inp.B_dn)
+                        B_dn=inp.B_dn, lora_shared_a=int(s.shared_a))
         ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
         idx = torch.empty((T, s.k), dtype=torch.int32, device=dev)
         tw = torch.empty((T, s.k), dtype=torch.float32, device=dev)
@@ -197,15 +198,17 @@ def time_layer(s, inp, wgu, wdn, ev, sh, steps, warmup):
     import bit_quantized_moe_amd as bqm
     dev = torch.device("cuda")
     lora = dict(A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn, B_dn=inp.B_dn) if s.r else {}
-    d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, act_quant=int(s.act_quant), **lora)
+    d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, act_quant=int(s.act_quant),
+                    lora_shared_a=int(s.shared_a), **lora)
     ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
     idx = torch.empty((s.T, s.k), dtype=torch.int32, device=dev)
     tw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
     out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
     dx = torch.empty_like(out)
     dtw = torch.empty((s.T, s.k), dtype=torch.float32, device=dev)
+    ea = () if s.shared_a else (s.E,)
     g = [torch.empty(sz, dtype=torch.float32, device=dev) for sz in
-         ((s.E, s.r, s.H), (s.E, 2 * s.I, s.r), (s.E, s.r, s.I), (s.E, s.H, s.r))] if s.r else [None] * 4
+         (ea + (s.r, s.H), (s.E, 2 * s.I, s.r), ea + (s.r, s.I), (s.E, s.H, s.r))] if s.r else [None] * 4
 
     def step(events=None):
         d.stage_events = C.addressof(events) if events is not None else None
@@ -276,7 +279,7 @@ def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 64, 256), reps=20):
         s = dataclasses.replace(shape, T=T, name=f"{shape.name}_decode_T{T}")
         inp = synth.layer_inputs(s, device=dev, with_weights=False)
         d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn,
-                        B_dn=inp.B_dn)
+                        B_dn=inp.B_dn, lora_shared_a=int(s.shared_a))
         ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
         idx = torch.empty((T, s.k), dtype=torch.int32, device=dev)
         tw = torch.empty((T, s.k), dtype=torch.float32, device=dev)
@@ -550,12 +553,23 @@ def main():
         others["qwen3_30b_a3b_w4a4"] = config_block(s3, r3, "nvfp4-4over6-rowwise, activations nvfp4 per token")
         del inp3, q3gu, q3dn
         torch.cuda.empty_cache()
+        # the GLM layer with the adapter layout of the GLM page (one LoRA-A shared by all
+        # experts, per-expert LoRA-B) over the same NVFP4 experts
+        s_sh = dataclasses.replace(shape, shared_a=True, name="glm_shared_lora_a")
+        inp_sh = synth.layer_inputs(s_sh, device=dev, with_weights=False)
+        r_sh = time_layer(s_sh, inp_sh, wgu, wdn, ev, sh, max(3, args.steps // 2), 2)
+        others["glm_nvfp4_shared_lora_a"] = config_block(s_sh, r_sh, "nvfp4-4over6-rowwise, one LoRA-A for all "
+                                                                     "experts, per-expert LoRA-B")
+        del inp_sh
+        torch.cuda.empty_cache()
         result["other_configs"] = others
         # the two-copy scheme (a columnwise second quantization for the dgrad) as a comparison
         result["columnwise_dgrad_comparison"] = colwise_comparison(s, inp, wgu, wdn, ev, sh)
         # decode-shaped forward over the GLM experts (serving side: weight-read-bound)
         result["decode_forward"] = {"workload": "glm5.2 shape, forward only (route + moe_fwd), nvfp4 weights, "
-                                                "LoRA r=64", "rows": decode_sweep(shape, wgu, wdn, ev, sh)}
+                                                "LoRA r=64", "rows": decode_sweep(shape, wgu, wdn, ev, sh),
+                                    "rows_shared_lora_a": decode_sweep(dataclasses.replace(shape, shared_a=True),
+                                                                       wgu, wdn, ev, sh)}
 
     if args.sweep:
         torch.cuda.empty_cache()

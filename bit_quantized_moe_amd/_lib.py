@@ -50,7 +50,7 @@ class QTensorC(C.Structure):
 class MoEDescC(C.Structure):
     _fields_ = [("T", C.c_int64), ("H", C.c_int64), ("I", C.c_int64), ("E", C.c_int32),
                 ("k", C.c_int32), ("r", C.c_int32), ("act_quant", C.c_int32),
-                ("lora_scale", C.c_float), ("reserved", C.c_int32), ("w_gu", QTensorC),
+                ("lora_scale", C.c_float), ("lora_shared_a", C.c_int32), ("w_gu", QTensorC),
                 ("w_dn", QTensorC), ("A_gu", C.c_void_p), ("B_gu", C.c_void_p),
                 ("A_dn", C.c_void_p), ("B_dn", C.c_void_p), ("stage_events", C.c_void_p)]
 
@@ -215,10 +215,11 @@ class MoEDesc:
     lora_scale: float = 1.0
     act_quant: int = 0
     stage_events: Optional[int] = None   # address of a host array of 2*STAGE_COUNT hipEvent_t
+    lora_shared_a: int = 0               # 1: A_gu [r, H] and A_dn [r, I] shared by all experts
 
     def c(self) -> MoEDescC:
         return MoEDescC(self.T, self.H, self.I, self.E, self.k, self.r, int(self.act_quant),
-                        float(self.lora_scale), 0, self.w_gu.c(), self.w_dn.c(), _ptr(self.A_gu),
+                        float(self.lora_scale), int(self.lora_shared_a), self.w_gu.c(), self.w_dn.c(), _ptr(self.A_gu),
                         _ptr(self.B_gu), _ptr(self.A_dn), _ptr(self.B_dn), self.stage_events)
 
 

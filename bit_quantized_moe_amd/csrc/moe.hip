@@ -57,6 +57,7 @@ struct Seg {
   const void *b_sc;     // NVFP4 E4M3 scales / NF4 absmax
   const float *b_sd;    // NVFP4 per-expert decode scales
   int64_t b_rows, b_cols;  // one expert slice of the B stack is [b_rows, b_cols]
+  int64_t b_estride;       // bf16 B: elements from one expert's slice to the next (0: one matrix for all)
   int K;
   int kmod;  // > 0: B is indexed at k mod kmod (A holds a hi/lo pair of K = 2*kmod)
 };
@@ -247,7 +248,7 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       uint4 v = make_uint4(0, 0, 0, 0);
       const int kb = s.kmod ? kk % s.kmod : kk;
       if (wr >= 0 && kk < s.K)
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + wr * s.b_cols + kb);
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + wr * s.b_cols + kb);
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   } else if constexpr (BSRC == B_BF_N) {
@@ -262,7 +263,7 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       const int kb = s.kmod ? kk % s.kmod : kk;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (n < N && kk < s.K)
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * slice + (int64_t)kb * s.b_cols + n);
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + (int64_t)kb * s.b_cols + n);
       r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
     }
   }
@@ -1163,8 +1164,7 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG;
   const int row0 = (wid / WNG) * TM * 32;
   const int nk = (s.K + BK - 1) / BK;
-  const int64_t slice = s.b_rows * s.b_cols;
-  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * slice;
+  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
   int64_t wr[TN];
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
@@ -1445,7 +1445,7 @@ __device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, c
   static_assert(sizeof(sm.a[1]) * 2 >= BK * LSTR * 2, "LoRA tile fits two A stages");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
   const int nk = (s.K + BK - 1) / BK;
-  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * (s.b_rows * s.b_cols);
+  const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
   uint16_t *Bt = sm.a[1];
   ARegs ar;
   u32x4 bv[8];
@@ -1704,7 +1704,7 @@ __global__ void __launch_bounds__(NTHR, 2) gemm_lora_proj(GemmParams p) {
     asrc[j] = reinterpret_cast<const uint16_t *>(s.a) + arow * s.a_ld + 8 * ((lane & 7) ^ ((row >> 1) & 7));
   }
   const uint16_t *bsrc[2];
-  const uint16_t *bbase = reinterpret_cast<const uint16_t *>(s.b) + e * (s.b_rows * s.b_cols);
+  const uint16_t *bbase = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int row = 16 * (int)w + 8 * i + (lane >> 3);
@@ -1789,6 +1789,10 @@ struct WgradParams {
   int q_gather;
   const float *c_scale;  // per-expert factor of the output (NULL: none)
   float *C;
+  // > 0: one output for all experts (a shared LoRA-A) from `split` parts of the
+  // experts; C is then [split][M][N] partial sums
+  int split;
+  int E;
 };
 
 constexpr int WB = 64;  // wgrad tile (M and N) and row step
@@ -1847,25 +1851,19 @@ __device__ __forceinline__ void wgrad_store(const WgradParams &p, uint16_t *Ps, 
   }
 }
 
-__global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[WB * WS];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[WB * WS];
-  const int e = blockIdx.y;
-  const int ntn = (p.N + WB - 1) / WB;
-  const int mt = blockIdx.x / ntn, ntile = blockIdx.x % ntn;
-  const int m0 = mt * WB, n0 = ntile * WB;
-  const int rb = p.offsets[e], n_e = p.offsets[e + 1] - rb;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+// acc = sum over the n_e rows from rb of P[row][m0 + .] (x) Q[row][n0 + .] for this
+// wave's 32x32 quarter of the tile; the stage is free again on return
+__device__ __forceinline__ void wgrad_rows(const WgradParams &p, int rb, int n_e, int m0, int n0, uint16_t *Ps,
+                                           uint16_t *Qs, f32x16 &acc) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  f32x16 acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
   const int nk = (n_e + WB - 1) / WB;
+  if (nk == 0) return;
   WRegs r;
-  if (nk > 0) {
-    wgrad_load(p, rb, n_e, 0, m0, n0, r);
-    wgrad_store(p, Ps, Qs, r);
-  }
+  wgrad_load(p, rb, n_e, 0, m0, n0, r);
+  wgrad_store(p, Ps, Qs, r);
   __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
     if (ks + 1 < nk) wgrad_load(p, rb, n_e, (ks + 1) * WB, m0, n0, r);
@@ -1881,13 +1879,67 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
       __syncthreads();
     }
   }
-  const float cs = p.c_scale ? p.c_scale[e] : 1.0f;
+}
+
+// blockIdx.y: the expert, C[e] = c_scale[e] times its sum; or (SPLIT) the part e
+// of the experts, [e E / split, (e+1) E / split), whose sums times their c_scale
+// are added in FP32 in expert order into C[e], a partial sum of the one [M, N]
+// output (the second accumulator lives only in this variant: the per-expert one
+// stays within the registers of eight workgroups per CU)
+template <bool SPLIT>
+__global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[WB * WS];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[WB * WS];
+  const int e = blockIdx.y;
+  const int ntn = (p.N + WB - 1) / WB;
+  const int mt = blockIdx.x / ntn, ntile = blockIdx.x % ntn;
+  const int m0 = mt * WB, n0 = ntile * WB;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  f32x16 acc;
+  if constexpr (SPLIT) {
+    const int e0 = (int)((int64_t)e * p.E / p.split), e1 = (int)((int64_t)(e + 1) * p.E / p.split);
+    f32x16 tot;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tot[v] = 0.0f;
+    for (int ex = e0; ex < e1; ++ex) {
+      const int rb = p.offsets[ex];
+      wgrad_rows(p, rb, p.offsets[ex + 1] - rb, m0, n0, Ps, Qs, acc);
+      const float cs = p.c_scale ? p.c_scale[ex] : 1.0f;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) tot[v] += acc[v] * cs;
+    }
+    acc = tot;
+  } else {
+    const int rb = p.offsets[e];
+    wgrad_rows(p, rb, p.offsets[e + 1] - rb, m0, n0, Ps, Qs, acc);
+    const float cs = p.c_scale ? p.c_scale[e] : 1.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] *= cs;
+  }
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) {
     const int m = m0 + wm * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
     const int n = n0 + wn * 32 + (lane & 31);
-    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[vv] * cs;
+    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[vv];
   }
+}
+
+// C[i] = sum of part[s][i] over s = 0, 1, ..., split-1 in that order (the split
+// sums of lora_wgrad; n4 float4 per part)
+__global__ void __launch_bounds__(NTHR) sum_parts(const float4 *__restrict__ part, int split, int64_t n4,
+                                                  float4 *__restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * NTHR + threadIdx.x;
+  if (i >= n4) return;
+  float4 acc = part[i];
+  for (int q = 1; q < split; ++q) {
+    const float4 v = part[q * n4 + i];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  C[i] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -1943,9 +1995,12 @@ __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t perm, inv, off, tile_off, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
-      vgu, dxr;
+      vgu, dxr, part;
   size_t total;
 };
+
+// parts of the experts whose shared-A gradient sums run side by side
+int lora_split(int E) { return E < 64 ? E : 64; }
 
 Layout layout(const bqm_moe_desc *d) {
   const size_t T = d->T, H = d->H, I = d->I, E = d->E, k = d->k, r = d->r;
@@ -1981,6 +2036,8 @@ Layout layout(const bqm_moe_desc *d) {
   L.dh = take(R * 2 * I * 2);
   L.vgu = take(R * 2 * r * 2);
   L.dxr = take(R * H * 2);
+  // shared-A gradient: lora_split(R) partial sums of [r, max(H, I)] in FP32
+  L.part = take(d->lora_shared_a && r > 0 ? (size_t)lora_split((int)E) * r * (H > I ? H : I) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -1994,6 +2051,8 @@ bqm_status check_desc(const bqm_moe_desc *d, const char *who) {
   BQM_REQUIRE(d->r >= 0 && d->r <= 128 && d->r % 8 == 0, BQM_ERR_SHAPE,
               "%s: r=%d must be a multiple of 8 in [0, 128]", who, d->r);
   BQM_REQUIRE(d->T * d->k < (int64_t)1 << 31, BQM_ERR_SHAPE, "%s: too many routed rows", who);
+  BQM_REQUIRE(d->lora_shared_a == 0 || d->lora_shared_a == 1, BQM_ERR_INVALID_ARG,
+              "%s: lora_shared_a must be 0 or 1", who);
   const bqm_qtensor *w[2] = {&d->w_gu, &d->w_dn};
   const int64_t rows[2] = {2 * d->I, d->H}, cols[2] = {d->H, d->I};
   for (int i = 0; i < 2; ++i) {
@@ -2054,7 +2113,15 @@ Seg seg_bf16(const void *a, int64_t a_ld, const void *b, int64_t b_rows, int64_t
   s.b = b;
   s.b_rows = b_rows;
   s.b_cols = b_cols;
+  s.b_estride = b_rows * b_cols;
   s.K = K;
+  return s;
+}
+
+// A segment whose B is a LoRA-A: with a shared A (one [r, K] matrix read by every
+// expert) the expert stride is 0.
+Seg lora_a_seg(const bqm_moe_desc *d, Seg s) {
+  if (d->lora_shared_a) s.b_estride = 0;
   return s;
 }
 
@@ -2186,7 +2253,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     GemmParams p = base_params(d, w);
     p.N = r;
     p.NT = (int)cdiv(r, 64);
-    p.s1 = seg_bf16(x, H, d->A_gu, r, H, H);
+    p.s1 = lora_a_seg(d, seg_bf16(x, H, d->A_gu, r, H, H));
     p.out_scale = ls;
     p.div_e = fold_fwd ? d->w_gu.s_dec : nullptr;
     p.out0 = ugu;
@@ -2219,7 +2286,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     GemmParams p = base_params(d, w);
     p.N = r;
     p.NT = (int)cdiv(r, 64);
-    p.s1 = seg_bf16(a, I, d->A_dn, r, I, I);
+    p.s1 = lora_a_seg(d, seg_bf16(a, I, d->A_dn, r, I, I));
     p.out_scale = ls;
     p.div_e = fold_fwd ? d->w_dn.s_dec : nullptr;
     p.out0 = udn;
@@ -2335,7 +2402,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     p.N = I;
     p.NT = (int)cdiv(I, 256);
     p.s1 = seg_q(dy, H, col ? *col_dn : d->w_dn, H);
-    p.s2 = seg_lora(vdn, d->A_dn, r, I, r);
+    p.s2 = lora_a_seg(d, seg_lora(vdn, d->A_dn, r, I, r));
     p.out0 = dh;
     p.h_in = w.at<float>(w.L.h);
     p.tw = w.at<float>(w.L.tw);
@@ -2363,7 +2430,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     p.N = H;
     p.NT = (int)cdiv(H, 256);
     p.s1 = seg_q(dh, 2 * I, col ? *col_gu : d->w_gu, 2 * I);
-    p.s2 = seg_lora(vgu, d->A_gu, r, H, r);
+    p.s2 = lora_a_seg(d, seg_lora(vgu, d->A_gu, r, H, r));
     p.out0 = dxr;
     if (col)
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fq<A_ROWS, EPI_STORE, true>(p, R, s, "gate_up dgrad (columnwise)")));
@@ -2430,8 +2497,12 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   p.offsets = w.at<int32_t>(w.L.off);
   p.tw = w.at<float>(w.L.tw);
   p.k = d->k;
+  p.E = d->E;
+  const int split = lora_split(d->E);
+  // shared: C is the one [M, N] gradient of a shared A, summed over the experts in
+  // `split` parts (partials in the workspace, then added in part order)
   auto go = [&](int M, int N, const uint16_t *P, int64_t pld, int pg, int sp, const uint16_t *Q, int64_t qld, int qg,
-                const float *cs, float *C, const char *what) {
+                const float *cs, float *C, bool shared, const char *what) {
     p.M = M;
     p.N = N;
     p.P = P;
@@ -2442,11 +2513,21 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
     p.q_ld = qld;
     p.q_gather = qg;
     p.c_scale = cs;
-    p.C = C;
-    dim3 grid((unsigned)(cdiv(M, WB) * cdiv(N, WB)), (unsigned)d->E);
-    lora_wgrad<<<grid, NTHR, 0, s>>>(p);
-    return launch_status(what);
+    p.split = shared ? split : 0;
+    p.C = shared ? w.at<float>(w.L.part) : C;
+    dim3 grid((unsigned)(cdiv(M, WB) * cdiv(N, WB)), (unsigned)(shared ? split : d->E));
+    if (shared) lora_wgrad<true><<<grid, NTHR, 0, s>>>(p);
+    else lora_wgrad<false><<<grid, NTHR, 0, s>>>(p);
+    BQM_TRY(launch_status(what));
+    if (shared) {
+      const int64_t n4 = (int64_t)M * N / 4;
+      sum_parts<<<(unsigned)cdiv(n4, NTHR), NTHR, 0, s>>>(reinterpret_cast<const float4 *>(p.C), split, n4,
+                                                          reinterpret_cast<float4 *>(C));
+      BQM_TRY(launch_status(what));
+    }
+    return BQM_OK;
   };
+  const bool sh = d->lora_shared_a != 0;
   const uint16_t *dh = w.at<uint16_t>(w.L.dh), *ugu = w.at<uint16_t>(w.L.ugu), *vgu = w.at<uint16_t>(w.L.vgu);
   const uint16_t *udn = w.at<uint16_t>(w.L.udn), *vdn = w.at<uint16_t>(w.L.vdn), *a = w.at<uint16_t>(w.L.a);
   // dB_gu [2I, r] = dh^T U_gu' ; dA_gu [r, H] = V_gu'^T X ; U' and V' already carry the LoRA scale
@@ -2456,11 +2537,11 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   const float *fv_gu = lora_folds_s_dec(d, false) ? d->w_gu.s_dec : nullptr;
   const float *fu_dn = lora_folds_s_dec(d, true) ? d->w_dn.s_dec : nullptr;
   const float *fv_dn = lora_folds_s_dec(d, false) ? d->w_dn.s_dec : nullptr;
-  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, 2 * r, 0, fu_gu, dB_gu, "lora dB_gu"));
-  BQM_TRY(go(r, H, vgu, 2 * r, 0, 0, x, H, 1, fv_gu, dA_gu, "lora dA_gu"));
+  BQM_TRY(go(2 * I, r, dh, 2 * I, 0, 0, ugu, 2 * r, 0, fu_gu, dB_gu, false, "lora dB_gu"));
+  BQM_TRY(go(r, H, vgu, 2 * r, 0, 0, x, H, 1, fv_gu, dA_gu, sh, "lora dA_gu"));
   // dB_dn [H, r] = (w dY)^T U_dn' ; dA_dn [r, I] = (w V_dn')^T a
-  BQM_TRY(go(H, r, dy, H, 1, 1, udn, 2 * r, 0, fu_dn, dB_dn, "lora dB_dn"));
-  BQM_TRY(go(r, I, vdn, 2 * r, 0, 1, a, I, 0, fv_dn, dA_dn, "lora dA_dn"));
+  BQM_TRY(go(H, r, dy, H, 1, 1, udn, 2 * r, 0, fu_dn, dB_dn, false, "lora dB_dn"));
+  BQM_TRY(go(r, I, vdn, 2 * r, 0, 1, a, I, 0, fv_dn, dA_dn, sh, "lora dA_dn"));
   mark(d, BQM_STAGE_LORA_GRAD, 1, s);
   return BQM_OK;
 }

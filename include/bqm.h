@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define BQM_ABI_VERSION 1
+#define BQM_ABI_VERSION 2
 
 typedef enum {
   BQM_OK = 0,
@@ -182,9 +182,16 @@ typedef struct {
   int32_t E, k, r;
   int32_t act_quant;
   float lora_scale;
-  int32_t reserved;
+  /* 0: per-expert LoRA-A stacks A_gu [E, r, H], A_dn [E, r, I].  1: one LoRA-A
+   * common to all experts, A_gu [r, H] and A_dn [r, I], with per-expert B (the
+   * adapter layout of the GLM page, "Getting GLM-5.2 NVFP4 Post-Training off
+   * the ground", its serving part, row 3 of its table of issues).  Other values:
+   * BQM_ERR_INVALID_ARG. */
+  int32_t lora_shared_a;
   bqm_qtensor w_gu;
   bqm_qtensor w_dn;
+  /* bf16 LoRA matrices (NULL when r == 0): A_gu, B_gu [E, 2I, r], A_dn, B_dn
+   * [E, H, r]; the A shapes follow lora_shared_a. */
   const uint16_t *A_gu, *B_gu, *A_dn, *B_dn;
   /* Optional (NULL: no timing).  Host array of 2*BQM_STAGE_COUNT hipEvent_t
    * handles created by the caller; every stage that runs records events
@@ -244,7 +251,10 @@ bqm_status bqm_moe_dgrad_colwise(const bqm_moe_desc *d, const bqm_qtensor *w_gu_
  *   dB_dn = s (w dy)^T (a A_dn^T)  dA_dn = s (w dy B_dn)^T a
  * summed over each expert's rows, FP32 accumulation.  f32 outputs dA_gu
  * [E, r, H], dB_gu [E, 2I, r], dA_dn [E, r, I], dB_dn [E, H, r]; experts
- * without rows get zeros.  Requires r > 0. */
+ * without rows get zeros.  With lora_shared_a, dA_gu [r, H] and dA_dn [r, I]
+ * are sums over all routed rows of every expert (the gradient of the one
+ * shared matrix), added in a fixed order, so repeated calls give identical
+ * bits.  Requires r > 0. */
 bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, const uint16_t *dy, void *ws,
                          size_t ws_bytes, float *dA_gu, float *dB_gu, float *dA_dn, float *dB_dn,
                          void *stream);

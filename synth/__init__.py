@@ -44,6 +44,7 @@ class Shape:
     outliers: bool = True
     seed: int = 0
     weight_seed: int = -1          # -1: same as seed
+    shared_a: bool = False         # one LoRA-A for all experts: A_gu [r, H], A_dn [r, I]
 
     @property
     def wseed(self) -> int:
@@ -147,9 +148,9 @@ class LayerInputs:
     logits: object       # f32 [T, E]
     w_gu: object         # bf16 [E, 2I, H]
     w_dn: object         # bf16 [E, H, I]
-    A_gu: object         # bf16 [E, r, H]
+    A_gu: object         # bf16 [E, r, H] ([r, H] when shared)
     B_gu: object         # bf16 [E, 2I, r]
-    A_dn: object         # bf16 [E, r, I]
+    A_dn: object         # bf16 [E, r, I] ([r, I] when shared)
     B_dn: object         # bf16 [E, H, r]
     dout: object         # bf16 [T, H]
     router: object = None
@@ -170,9 +171,10 @@ def layer_inputs(shape: Shape, device="cpu", with_weights=True) -> LayerInputs:
     else:
         wgu = wdn = None
     if s.r:
-        agu = normal((s.E, s.r, s.H), 0.01, (sd, T_AGU), device=device)
+        ea = () if s.shared_a else (s.E,)
+        agu = normal(ea + (s.r, s.H), 0.01, (sd, T_AGU), device=device)
         bgu = normal((s.E, 2 * s.I, s.r), 0.01, (sd, T_BGU), device=device)
-        adn = normal((s.E, s.r, s.I), 0.01, (sd, T_ADN), device=device)
+        adn = normal(ea + (s.r, s.I), 0.01, (sd, T_ADN), device=device)
         bdn = normal((s.E, s.H, s.r), 0.01, (sd, T_BDN), device=device)
     else:
         agu = bgu = adn = bdn = None

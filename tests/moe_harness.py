@@ -78,7 +78,7 @@ def gpu_layer(inp: synth.LayerInputs, dev, lora_scale=1.0, poison_empty=False, l
     if s.r:
         lor = dict(A_gu=inp.A_gu.to(dev), B_gu=inp.B_gu.to(dev), A_dn=inp.A_dn.to(dev), B_dn=inp.B_dn.to(dev))
     d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, qgu, qdn, lora_scale=lora_scale,
-                    act_quant=int(s.act_quant), **lor)
+                    act_quant=int(s.act_quant), lora_shared_a=int(s.shared_a), **lor)
     ws = torch.empty(max(bqm.bqm_moe_workspace_size(d), 16), dtype=torch.uint8, device=dev)
     out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev)
     bqm.bqm_moe_fwd(d, x, idx, tw, out, ws)
@@ -91,9 +91,10 @@ def gpu_layer(inp: synth.LayerInputs, dev, lora_scale=1.0, poison_empty=False, l
         bqm.bqm_moe_dgrad(d, dout, ws, dx, dtw)
     res = dict(idx=idx, tw=tw, out=out, dx=dx, dtw=dtw, desc=d, ws=ws)
     if s.r and lora:
-        g = dict(dA_gu=torch.empty((s.E, s.r, s.H), dtype=torch.float32, device=dev),
+        ea = () if s.shared_a else (s.E,)
+        g = dict(dA_gu=torch.empty(ea + (s.r, s.H), dtype=torch.float32, device=dev),
                  dB_gu=torch.empty((s.E, 2 * s.I, s.r), dtype=torch.float32, device=dev),
-                 dA_dn=torch.empty((s.E, s.r, s.I), dtype=torch.float32, device=dev),
+                 dA_dn=torch.empty(ea + (s.r, s.I), dtype=torch.float32, device=dev),
                  dB_dn=torch.empty((s.E, s.H, s.r), dtype=torch.float32, device=dev))
         bqm.bqm_lora_grad(d, x, dout, ws, g["dA_gu"], g["dB_gu"], g["dA_dn"], g["dB_dn"])
         res.update(g)
@@ -120,7 +121,8 @@ class HostInputs:
         gu = om.LazyExperts(lambda e: synth.f32_numpy(self._wgu[e]), s.fmt)
         dn = om.LazyExperts(lambda e: synth.f32_numpy(self._wdn[e]), s.fmt)
         lo = self.lora if self.lora is not None else [None] * 4
-        return om.MoEWeights(s.fmt, gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant)
+        return om.MoEWeights(s.fmt, gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant,
+                             shared_a=s.shared_a)
 
     def weights_colwise(self, lora_scale=1.0):
         """The same layer with the oracle's columnwise copies (DQ(Q(W^T))^T) as base weights."""
@@ -128,7 +130,8 @@ class HostInputs:
         gu = om.ColumnwiseExperts(lambda e: synth.f32_numpy(self._wgu[e]))
         dn = om.ColumnwiseExperts(lambda e: synth.f32_numpy(self._wdn[e]))
         lo = self.lora if self.lora is not None else [None] * 4
-        return om.MoEWeights("nvfp4", gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant)
+        return om.MoEWeights("nvfp4", gu, dn, *lo, lora_scale=lora_scale, act_quant=s.act_quant,
+                             shared_a=s.shared_a)
 
 
 def _bf16_neighbours(a):
@@ -184,7 +187,7 @@ def resolve_w4a4_alternatives(g_out, g_dtw, o, h: HostInputs, rel_eps=2.0 ** -14
                 alt[col] = other[i][col]
                 y_alt = om.act_dq(alt[None])[0] @ Wdn.T
                 if w.r:
-                    y_alt = y_alt + w.lora_scale * ((alt @ w.A_dn[e].astype(np.float64).T)
+                    y_alt = y_alt + w.lora_scale * ((alt @ w.a_dn(e).T)
                                                     @ w.B_dn[e].astype(np.float64).T)
                 out_alt = o["out"][n] - wt * c["y"][i] + wt * y_alt
                 err = np.abs(out_alt - g_out[n]).max()

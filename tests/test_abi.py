@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.bqm_abi_version() == 1
+    assert lib.bqm_abi_version() == 2
 
 
 def _q(fmt=1, n=1, rows=4, cols=32, mode=0, codes=16, scales=16, sdec=16):
@@ -89,3 +89,24 @@ def test_empty_inputs_are_noops(lib):
     assert lib.bqm_dequantize(C.byref(q), None, None) == 0
     q = _q(fmt=2, n=0, cols=64)
     assert lib.bqm_quantize_nf4(None, C.byref(q), None) == 0
+
+
+def _desc(shared=0, T=64, H=256, I=128, E=8, k=2, r=8):
+    gu = _q(n=E, rows=2 * I, cols=H)
+    dn = _q(n=E, rows=H, cols=I)
+    return bqm.MoEDescC(T, H, I, E, k, r, 0, 1.0, shared, gu, dn, 16, 16, 16, 16, None)
+
+
+def test_moe_shared_lora_a_flag_and_workspace(lib):
+    # host-side only: the descriptor check runs before any device work
+    d = _desc(shared=3)
+    assert lib.bqm_moe_fwd(C.byref(d), 16, 16, 16, 16, None, 0, None) == -1
+    assert "lora_shared_a" in bqm.bqm_last_error()
+    d = _desc(shared=1)
+    assert lib.bqm_moe_fwd(C.byref(d), 16, 16, 16, 16, None, 0, None) == -5
+    # the shared-A gradient adds its partial sums: min(E, 64) parts of the experts,
+    # each [r, max(H, I)] FP32
+    for T, E, split in ((64, 8, 8), (16384, 256, 64), (3000, 40, 40)):
+        a = lib.bqm_moe_workspace_size(C.byref(_desc(0, T=T, E=E)))
+        b = lib.bqm_moe_workspace_size(C.byref(_desc(1, T=T, E=E)))
+        assert b - a == -(-split * 8 * 256 * 4 // 256) * 256, (T, E)

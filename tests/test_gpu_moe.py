@@ -36,6 +36,8 @@ def compare_full(shape, lora_scale=1.0, poison_empty=False, colwise=False):
         for name, ref in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), o["lora"]):
             got = g[name].cpu().numpy()
             errs[name] = assert_close(got, ref, name)
+            if shape.shared_a and name.startswith("dA"):
+                continue  # one shared matrix, not a per-expert stack
             hit = np.zeros(shape.E, bool)
             hit[o["idx"].reshape(-1)] = True
             assert (got[~hit] == 0).all(), f"{name}: experts without rows must get zeros"
@@ -81,6 +83,23 @@ def test_nvfp4_routed_only_poisoned_experts():
     assert np.isfinite(np_f32(g["out"])).all() and np.isfinite(np_f32(g["dx"])).all()
 
 
+def test_small_shared_lora_a():
+    # one LoRA-A for all experts, its gradients summed over 12 parts of one expert
+    # each; partial column tiles as in the ragged case above
+    compare_full(small("small_sh", H=320, I=192, T=600, E=12, shared_a=True), lora_scale=0.5)
+
+
+def test_small_shared_lora_a_nf4_w4a4_colwise():
+    # the same layout on the NF4 kernels with skewed routing and empty experts (64
+    # experts in parts of one, some empty), on the W4A4 path and on the columnwise dgrad
+    g, o = compare_full(small("small_sh_nf4", fmt="nf4", logits="zipf", E=64, T=700, k=4, r=8, shared_a=True),
+                        poison_empty=True)
+    assert (np.bincount(o["idx"].reshape(-1), minlength=64) == 0).sum() >= 16
+    compare_full(small("small_sh_w4a4", act_quant=True, H=768, I=384, T=600, shared_a=True))
+    # 96 experts: parts of one or two experts
+    compare_full(small("small_sh_col", shared_a=True, E=96, T=400), colwise=True)
+
+
 def test_tiny_workload():
     compare_full(synth.TINY)
 
@@ -102,10 +121,11 @@ def test_single_token_and_empty_batch():
     torch.cuda.synchronize()
 
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("shared_a", [False, True])
+def test_deterministic_bitwise(shared_a):
     import torch
     dev = gpu()
-    shape = small("det", T=150)
+    shape = small("det", T=150 if not shared_a else 1100, shared_a=shared_a)
     inp = synth.layer_inputs(shape, device="cpu")
     a = gpu_layer(inp, dev)
     b = gpu_layer(inp, dev)
@@ -160,3 +180,40 @@ def test_full_qwen_w4a4_sampled():
 
 def test_full_glm_nf4_sampled():
     sampled_full(synth.GLM_NF4, tokens=[1, 9000], lora_experts=[0])
+
+
+def test_full_glm_shared_lora_a_matches_replicated():
+    # At the full GLM size the shared-A gradient sums all 131072 routed rows, more
+    # than the oracle can take here.  Properties that hold at any size: the layer
+    # with one shared A gives bit-identical out, dX and routing-weight gradients to
+    # the per-expert layout holding E copies of that A (the kernels read the same
+    # values), the B gradients are bit-identical, and the shared dA equals the sum of
+    # the per-expert dA (the same per-expert FP32 sums, added in another order:
+    # relative 1e-5).  Out and dX rows of two tokens are also checked against the
+    # oracle.
+    import torch
+    dev = gpu()
+    shape = dataclasses.replace(synth.GLM, name="glm_shared_a", shared_a=True)
+    log("full-size GLM layer with a shared LoRA-A: generating inputs on the device")
+    inp = synth.layer_inputs(shape, device=dev)
+    sh = gpu_layer(inp, dev)
+    rep_inp = dataclasses.replace(inp, shape=synth.GLM,
+                                  A_gu=inp.A_gu.unsqueeze(0).expand(shape.E, -1, -1).contiguous(),
+                                  A_dn=inp.A_dn.unsqueeze(0).expand(shape.E, -1, -1).contiguous())
+    rep = gpu_layer(rep_inp, dev)
+    for k in ("out", "dx", "dtw", "dB_gu", "dB_dn"):
+        assert torch.equal(sh[k].view(torch.uint8) if sh[k].dtype == torch.bfloat16 else sh[k],
+                           rep[k].view(torch.uint8) if rep[k].dtype == torch.bfloat16 else rep[k]), k
+    for k in ("dA_gu", "dA_dn"):
+        ref = rep[k].double().sum(0)
+        err = (sh[k].double() - ref).norm() / ref.norm()
+        log(f"  {k}: shared vs sum of per-expert, rel Frobenius {err.item():.2e}")
+        assert err.item() < 1e-5, k
+    del rep, rep_inp
+    torch.cuda.empty_cache()
+    h = HostInputs(inp)
+    o = oracle_layer(h, tokens=[7, 15000])
+    toks = o["tokens"]
+    assert_close(np_f32(sh["out"][toks]), o["out"], "out rows")
+    assert_close(np_f32(sh["dx"][toks]), o["dx"], "dx rows")
+    log("  shared-A full-size checks ok")
