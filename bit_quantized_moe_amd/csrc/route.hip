@@ -99,13 +99,13 @@ __global__ void __launch_bounds__(256) perm_hist(const int32_t *__restrict__ idx
 
 // Pass 2 (one block): base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e];
 // offsets = exclusive prefix of the per-expert totals.  Optionally the prefix
-// of ceil(count / bm) (row tiles per expert) for the grouped GEMMs.
+// of ceil(count / bm) (row tiles per expert) for the grouped GEMMs.  The prefixes
+// over experts are a wave-level inclusive scan plus the totals of the waves before.
 __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, int nchunks, int E,
                                                   int32_t *__restrict__ offsets, int bm,
                                                   int32_t *__restrict__ tile_off) {
-  __shared__ int32_t tot[1025];
-  __shared__ int32_t til[1025];
-  int e = threadIdx.x;
+  __shared__ int32_t wsum[16][2];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   int32_t run = 0;
   if (e < E) {
     for (int c = 0; c < nchunks; ++c) {
@@ -113,36 +113,53 @@ __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, 
       counts[(int64_t)c * E + e] = run;
       run += v;
     }
-    tot[e] = run;
-    til[e] = bm > 0 ? (run + bm - 1) / bm : 0;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t s = 0, st = 0;
-    for (int i = 0; i < E; ++i) {
-      int32_t v = tot[i], w = til[i];
-      tot[i] = s;
-      til[i] = st;
-      s += v;
-      st += w;
+  const int32_t tiles = (e < E && bm > 0) ? (run + bm - 1) / bm : 0;
+  int32_t v = run, u = tiles;  // inclusive prefixes within the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t tv = __shfl_up(v, off, 64), tu = __shfl_up(u, off, 64);
+    if (lane >= off) {
+      v += tv;
+      u += tu;
     }
-    tot[E] = s;
-    til[E] = st;
+  }
+  if (lane == 63) {
+    wsum[wave][0] = v;
+    wsum[wave][1] = u;
   }
   __syncthreads();
-  if (e < E) {
-    for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += tot[e];
-    offsets[e] = tot[e];
-    if (tile_off) tile_off[e] = til[e];
+  int32_t bv = 0, bu = 0;  // totals of the waves before this one
+  for (int q = 0; q < wave; ++q) {
+    bv += wsum[q][0];
+    bu += wsum[q][1];
   }
-  if (threadIdx.x == 0) {
-    offsets[E] = tot[E];
-    if (tile_off) tile_off[E] = til[E];
+  const int32_t ex = bv + v - run, ext = bu + u - tiles;  // exclusive prefixes
+  if (e < E) {
+    for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += ex;
+    offsets[e] = ex;
+    if (tile_off) tile_off[e] = ext;
+  }
+  if (e == E - 1) {
+    offsets[E] = ex + run;
+    if (tile_off) tile_off[E] = ext + tiles;
   }
 }
 
-// Pass 3: one wave scatters its chunk in order; equal experts inside a group of
-// 64 pairs are ranked by lane, so the result is the stable order.
+// lanes of the wave whose value equals this lane's (0 <= value < 2048: eleven bits)
+__device__ __forceinline__ uint64_t lanes_equal(int v) {
+  uint64_t m = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 11; ++b) {
+    const bool bit = (v >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
+  }
+  return m;
+}
+
+// Pass 3: one wave scatters its chunk in order, 64 pairs at a time; equal experts
+// inside a group are ranked by lane, so the result is the stable order.
 __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ idx, int64_t R, int E,
                                                    const int32_t *__restrict__ base,
                                                    int32_t *__restrict__ perm,
@@ -152,18 +169,13 @@ __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ i
   for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
   __syncthreads();
   const int64_t b = (int64_t)blockIdx.x * kChunk;
-  for (int s = 0; s < kChunk; s += 64) {
+  const uint64_t below = (1ull << lane) - 1ull, upto = lane == 63 ? ~0ull : (2ull << lane) - 1ull;
+  for (int s = 0; s < kChunk && b + s < R; s += 64) {
     int64_t f = b + s + lane;
     int e = f < R ? idx[f] : -1;
-    int rank = 0;
-    bool last = true;
-    for (int q = 0; q < 64; ++q) {
-      int eq = __shfl(e, q, 64);
-      if (eq == e) {
-        if (q < lane) ++rank;
-        if (q > lane) last = false;
-      }
-    }
+    const uint64_t same = lanes_equal(e + 1);  // pairs past R (e = -1) match only each other
+    const int rank = __popcll(same & below);
+    const bool last = (same & ~upto) == 0ull;
     int pos = 0;
     if (e >= 0) pos = cnt[e] + rank;
     __syncthreads();

@@ -100,6 +100,16 @@ def test_small_shared_lora_a_nf4_w4a4_colwise():
     compare_full(small("small_sh_col", shared_a=True, E=96, T=400), colwise=True)
 
 
+def test_small_batches():
+    # decode-sized batches, where most row tiles hold one or two valid 32-row tiles:
+    # T = 8 over 64 experts with k = 8; partial column tiles at T = 40; 100 rows per
+    # expert; and T = 256 with the shared-A LoRA
+    compare_full(small("dec8", T=8, E=64, k=8, r=16), lora_scale=0.5)
+    compare_full(small("dec_odd", H=320, I=192, T=40, E=12))
+    compare_full(small("dec_rows", T=200, E=4, k=2, r=8))
+    compare_full(small("dec256", T=256, E=32, k=4, shared_a=True))
+
+
 def test_tiny_workload():
     compare_full(synth.TINY)
 
