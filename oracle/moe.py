@@ -84,7 +84,8 @@ class LazyExperts:
     """An expert stack quantized by this oracle one expert at a time, on first use.
 
     fetch(e) returns expert e's bf16 weights as float32 [rows, cols]; fmt is
-    "nvfp4" (per-tensor scale, Four-Over-Six) or "nf4".  Used for the full-size
+    "nvfp4" (per-tensor scale, Four-Over-Six), "nf4" or "nf4_nested" (NF4 with the
+    double-quantized absmax, nested per expert matrix).  Used for the full-size
     workloads, where only the experts a sampled token touches are needed.
     """
 
@@ -97,6 +98,8 @@ class LazyExperts:
             x = fm.f32(self.fetch(e))[None]
             if self.fmt == "nvfp4":
                 self.cache[e] = oq.dequantize_nvfp4_exact(oq.quantize_nvfp4(x, self.fos))[0]
+            elif self.fmt == "nf4_nested":
+                self.cache[e] = oq.dequantize_nf4_nested(oq.nest_absmax(oq.quantize_nf4(x)))[0].astype(np.float64)
             else:
                 self.cache[e] = oq.dequantize_nf4(oq.quantize_nf4(x))[0].astype(np.float64)
         return self.cache[e]
@@ -129,6 +132,9 @@ def expert_matrix(q, e: int) -> np.ndarray:
         one = oq.NVFP4Tensor(q.codes[e:e + 1], q.scales[e:e + 1], q.s_dec[e:e + 1],
                              q.four_over_six, q.per_row)
         return oq.dequantize_nvfp4_exact(one)[0]
+    if isinstance(q, oq.NF4Nested):
+        one = oq.NF4Nested(q.codes[e:e + 1], q.absmax_q[e:e + 1], q.group_scale[e:e + 1], q.offset[e:e + 1])
+        return oq.dequantize_nf4_nested(one)[0].astype(np.float64)
     one = oq.NF4Tensor(q.codes[e:e + 1], q.absmax[e:e + 1])
     return oq.dequantize_nf4(one)[0].astype(np.float64)
 

@@ -30,6 +30,16 @@ NF4 follows "nf4moe - QLoRA for a 743B Fused-MoE", section "The fix:
 dequant-on-forward for routed experts" (blocksize 64, absmax per block): the
 block is divided by its FP32 absmax (multiplied by the FP32 reciprocal) and each
 element takes the nearest codebook level, ties going to the lower level.
+
+Nested absmax (the same page names bnb's quant state as "absmax, nested code",
+section "Getting it to load"; it says nothing more, so this follows the published
+QLoRA double quantization): the FP32 absmax of one matrix, in row-major block
+order, has its mean subtracted (offset = the exactly rounded sum over the block
+count, in float64, rounded to FP32); each group of 256 consecutive blocks gets
+s2 = fl(max|d| / 448) and the codes e4m3(fl(d / s2)), d = fl(absmax - offset),
+E4M3 (OCP, round to nearest even, saturating, the sign bit set for d < 0)
+standing for the 8-bit float.  A group with max|d| = 0 has s2 = 0 and codes 0.  The NF4 codes themselves come
+from the exact absmax; dequantization uses absmax' = fl(fl(e4m3 * s2) + offset).
 """
 from __future__ import annotations
 
@@ -59,6 +69,14 @@ class NVFP4Tensor:
 class NF4Tensor:
     codes: np.ndarray    # uint8 [..., C/2]
     absmax: np.ndarray   # float32 [..., C/64]
+
+
+@dataclass
+class NF4Nested:
+    codes: np.ndarray        # uint8 [n_mat, rows, C/2], as in the plain tensor
+    absmax_q: np.ndarray     # uint8 E4M3 bits [n_mat, rows, C/64]
+    group_scale: np.ndarray  # float32 [n_mat, G]: s2 of each 256-block group, G = ceil(rows C / 64 / 256)
+    offset: np.ndarray       # float32 [n_mat]: the mean of the matrix's absmax
 
 
 def global_decode_scale(amax, four_over_six: bool) -> tuple[np.ndarray, np.ndarray]:
@@ -237,6 +255,57 @@ def nf4_values_f32(q: NF4Tensor, codebook=None) -> np.ndarray:
 def dequantize_nf4(q: NF4Tensor, codebook=None) -> np.ndarray:
     """bf16(fl32(c[code] * absmax)) as float32 values; also the GEMM operand."""
     return fm.bf16_round(nf4_values_f32(q, codebook))
+
+
+NEST_GROUP = 256
+E4M3_MAX = 448.0
+
+
+def nest_absmax(q: NF4Tensor) -> NF4Nested:
+    """Double quantization of the FP32 absmax, one matrix (leading index) at a time."""
+    import math
+    a = fm.f32(q.absmax)
+    n_mat = a.shape[0]
+    flat = a.reshape(n_mat, -1)
+    nb = flat.shape[1]
+    G = -(-nb // NEST_GROUP)
+    codes = np.zeros(flat.shape, dtype=np.uint8)
+    s2 = np.zeros((n_mat, G), dtype=np.float32)
+    offset = np.zeros(n_mat, dtype=np.float32)
+    for m in range(n_mat):
+        offset[m] = np.float32(math.fsum(float(v) for v in flat[m]) / nb)
+        d = (flat[m] - offset[m]).astype(np.float32)
+        for g in range(G):
+            dg = d[g * NEST_GROUP:(g + 1) * NEST_GROUP]
+            t = np.abs(dg).max()
+            sc = np.float32(t / F32(E4M3_MAX))
+            s2[m, g] = sc
+            if sc > 0:
+                y = (dg / sc).astype(np.float32)
+                mag = fm.e4m3_rne_satfinite(np.abs(y)).astype(np.uint8)
+                codes[m, g * NEST_GROUP:(g + 1) * NEST_GROUP] = mag | np.where(y < 0, 0x80, 0).astype(np.uint8)
+    return NF4Nested(q.codes, codes.reshape(a.shape), s2, offset)
+
+
+def unnest_absmax(n: NF4Nested) -> np.ndarray:
+    """absmax' = fl(fl(e4m3 * s2) + offset), float32 [n_mat, rows, C/64]."""
+    n_mat = n.absmax_q.shape[0]
+    flat = n.absmax_q.reshape(n_mat, -1)
+    g = np.arange(flat.shape[1]) // NEST_GROUP
+    v = fm.e4m3_decode(flat).astype(np.float32)
+    prod = (v * n.group_scale[:, g]).astype(np.float32)
+    return (prod + n.offset[:, None]).astype(np.float32).reshape(n.absmax_q.shape)
+
+
+def dequantize_nf4_nested(n: NF4Nested, codebook=None) -> np.ndarray:
+    """bf16(fl32(c[code] * absmax')) as float32 values; also the GEMM operand."""
+    return dequantize_nf4(NF4Tensor(n.codes, unnest_absmax(n)), codebook)
+
+
+def nf4_nested_bytes(n_elements: int, n_mat: int, rows_cols_per_mat: int) -> int:
+    """Codes, one byte per 64 elements, and per matrix the offset plus one FP32 per 256 blocks."""
+    groups = -(-(rows_cols_per_mat // NF4_BLOCK) // NEST_GROUP)
+    return n_elements // 2 + n_elements // 64 + 4 * n_mat * (1 + groups)
 
 
 def nvfp4_bytes(n_elements: int, n_mat: int) -> int:

@@ -269,3 +269,20 @@ def test_nf4_against_bf16_sanity_band():
     cos = (dq * db).sum() / np.linalg.norm(dq) / np.linalg.norm(db)
     assert 0.03 < fro < 0.3
     assert cos > 0.97
+
+
+def test_nf4_nested_layer_is_the_layer_over_its_dequantized_weights():
+    # the nested-absmax NF4 layer equals the plain-NF4 layer whose absmax is replaced
+    # by absmax' (the forward and dgrad see only the dequantized weights), and it
+    # stays close to the plain NF4 layer (absmax' within 2^-4 of each group's max |d|)
+    w, x, idx, tw, dout, (wgu, wdn) = make_layer(E=4, H=128, I=64, k=2, T=9, r=4, seed=15, fmt="nf4")
+    ngu, ndn = oq.nest_absmax(w.gu), oq.nest_absmax(w.dn)
+    wn = om.MoEWeights("nf4", ngu, ndn, w.A_gu, w.B_gu, w.A_dn, w.B_dn)
+    wp = om.MoEWeights("nf4", oq.NF4Tensor(ngu.codes, oq.unnest_absmax(ngu)),
+                       oq.NF4Tensor(ndn.codes, oq.unnest_absmax(ndn)), w.A_gu, w.B_gu, w.A_dn, w.B_dn)
+    o1, c1 = om.forward(wn, x, idx, tw)
+    o2, c2 = om.forward(wp, x, idx, tw)
+    assert (o1 == o2).all()
+    assert (om.dgrad(wn, c1, dout, tw)[0] == om.dgrad(wp, c2, dout, tw)[0]).all()
+    o3, _ = om.forward(w, x, idx, tw)
+    assert 0 < np.linalg.norm(o1 - o3) / np.linalg.norm(o3) < 0.05

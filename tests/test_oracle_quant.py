@@ -408,3 +408,101 @@ def test_nf4_round_trip_error_small():
     dq = oq.dequantize_nf4(oq.quantize_nf4(x))
     rel = np.linalg.norm(dq - x) / np.linalg.norm(x)
     assert 0.03 < rel < 0.15
+
+
+# ----------------------------------------------------------------------------
+# NF4 with nested (double-quantized) absmax
+# ----------------------------------------------------------------------------
+def _nf4_plain(absmax_rows):
+    """An NF4 tensor with the given absmax [n_mat, rows, nb] and zero codes."""
+    a = np.asarray(absmax_rows, dtype=np.float32)
+    n_mat, rows, nb = a.shape
+    return oq.NF4Tensor(np.zeros((n_mat, rows, nb * 32), dtype=np.uint8), a)
+
+
+def test_nested_absmax_hand_example():
+    # two blocks with absmax 1 and 3: offset 2, d = -1, +1, s2 = fl(1/448), and the
+    # codes are -448 and +448 (E4M3 0xFE / 0x7E); absmax' = 2 -/+ fl(448 fl(1/448))
+    n = oq.nest_absmax(_nf4_plain([[[1.0, 3.0]]]))
+    s2 = np.float32(np.float32(1.0) / np.float32(448.0))
+    assert n.offset[0] == np.float32(2.0) and n.group_scale[0, 0] == s2
+    assert list(n.absmax_q.reshape(-1)) == [0xFE, 0x7E]
+    back = oq.unnest_absmax(n).reshape(-1)
+    one = np.float32(np.float32(448.0) * s2)
+    assert back[0] == np.float32(np.float32(2.0) - one) and back[1] == np.float32(np.float32(2.0) + one)
+
+
+def test_nested_absmax_brute_force_and_bounds():
+    import math
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    # 2 matrices of 7 x 100 blocks: 700 blocks, groups of 256, 256, 188 (ragged last)
+    a = np.abs(rng.standard_normal((2, 7, 100)) * 0.03 + 0.05).astype(np.float32)
+    a[1, 3, :] = 0.0                                   # zero blocks inside a group
+    n = oq.nest_absmax(_nf4_plain(a))
+    assert n.group_scale.shape == (2, 3)
+    table = fm.e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    back = oq.unnest_absmax(n)
+    for m in range(2):
+        flat = a[m].reshape(-1)
+        exact = sum(Fraction(float(v)) for v in flat) / len(flat)
+        off = n.offset[m]
+        ulp = np.spacing(off)
+        assert abs(Fraction(float(off)) - exact) <= Fraction(float(ulp))      # the mean, to one FP32 ulp
+        d = (flat - off).astype(np.float32)
+        for g in range(3):
+            dg = d[g * 256:(g + 1) * 256]
+            t = float(np.abs(dg).max())
+            s2 = float(n.group_scale[m, g])
+            assert s2 == float(np.float32(np.float32(t) / np.float32(448.0)))
+            codes = n.absmax_q[m].reshape(-1)[g * 256:(g + 1) * 256]
+            y = (dg / np.float32(s2)).astype(np.float64)
+            for i in range(0, dg.size, 7):
+                # nearest finite E4M3 value (NaN codes excluded), ties to the even code
+                cand = [c for c in range(256) if c & 0x7F != 0x7F]
+                dist = [abs(table[c] - min(y[i], 448.0) if y[i] >= 0 else abs(table[c] - max(y[i], -448.0))) for c in cand]
+                best = min(dist)
+                ok = [c for c, dd in zip(cand, dist) if dd == best]
+                ok = [c for c in ok if (c & 0x80) == (0x80 if y[i] < 0 else 0)] or ok
+                if len(ok) > 1:
+                    ok = [c for c in ok if c % 2 == 0]
+                assert codes[i] in ok, (m, g, i, y[i], codes[i], ok)
+            # the E4M3 error bound: half a spacing, relative 2^-4 (normal) or 2^-10 absolute (subnormal)
+            bm = back[m].reshape(-1)[g * 256:(g + 1) * 256].astype(np.float64)
+            lim = s2 * np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) + 4 * np.spacing(np.float32(max(abs(off), t)))
+            assert (np.abs(bm - flat[g * 256:(g + 1) * 256]) <= lim).all()
+    del math
+
+
+def test_nested_absmax_constant_and_zero_matrices():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((1, 16, 256)) * 0.1).astype(np.float32)
+    q = oq.quantize_nf4(x)
+    const = oq.NF4Tensor(q.codes, np.full_like(q.absmax, np.float32(0.3125)))
+    n = oq.nest_absmax(const)
+    assert (n.group_scale == 0).all() and (n.absmax_q == 0).all()
+    assert (oq.unnest_absmax(n) == const.absmax).all()
+    assert (oq.dequantize_nf4_nested(n) == oq.dequantize_nf4(const)).all()
+    z = oq.quantize_nf4(np.zeros((1, 8, 128), np.float32))
+    nz = oq.nest_absmax(z)
+    assert (oq.dequantize_nf4_nested(nz) == 0).all() and nz.offset[0] == 0
+
+
+def test_nested_absmax_storage_and_error():
+    # storage: 4 + 8/64 + 32 / (64 * 256) bits per weight plus one FP32 per matrix
+    # (QLoRA's 0.127 bits of quantization constants per weight, from 0.5)
+    E, H, I = 256, 6144, 2048
+    n_el = E * 2 * I * H + E * H * I
+    b = oq.nf4_nested_bytes(E * 2 * I * H, E, 2 * I * H) + oq.nf4_nested_bytes(E * H * I, E, H * I)
+    const_bits = 8 * b / n_el - 4
+    assert abs(const_bits - (0.125 + 32 / (64 * 256))) < 1e-4
+    assert 8 * (oq.nf4_bytes(n_el)) / n_el - 4 == 0.5
+    # on N(0, 0.02) weights with outliers: absmax' is off by at most half an E4M3
+    # spacing of the largest |d| of a group, 2^-4 of it, and |d| <= max absmax
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((2, 128, 512)) * 0.02).astype(np.float32)
+    w[rng.random(w.shape) < 0.001] *= 20
+    q = oq.quantize_nf4(w)
+    n = oq.nest_absmax(q)
+    err = np.abs(oq.unnest_absmax(n) - q.absmax).max() / q.absmax.max()
+    assert 0 < err <= 2.0 ** -4
