@@ -530,6 +530,23 @@ def main():
         ms = time_calls(ev, sh, lambda: (bqm.bqm_dequantize(ngu, ybuf), bqm.bqm_dequantize(ndn, ydn)))
         formats["nf4_dequantize"] = {"ms": ms, "GB/s": nf4_bytes / ms / 1e6,
                                      "hbm_frac": nf4_bytes / ms / 1e6 / PEAK_HBM_GBS}
+        # nested (double-quantized) absmax: the nesting pass over the FP32 absmax, the
+        # dequantize from the nested form, and the storage of the two stacks
+        mgu = bqm.alloc_qtensor(bqm.FMT_NF4, s.E, 2 * s.I, s.H, device=dev, nested=1)
+        mdn = bqm.alloc_qtensor(bqm.FMT_NF4, s.E, s.H, s.I, device=dev, nested=1)
+        mgu.codes, mdn.codes = ngu.codes, ndn.codes
+        ms = time_calls(ev, sh, lambda: (bqm.bqm_nf4_nest(ngu, mgu), bqm.bqm_nf4_nest(ndn, mdn)))
+        nest_bytes = n_el * (4 / 64 + 1 / 64) + 4 * (mgu.s_dec.numel() + mdn.s_dec.numel())
+        nested_stack_bytes = n_el // 2 + n_el // 64 + 4 * (mgu.s_dec.numel() + mdn.s_dec.numel())
+        formats["nf4_nest"] = {"ms": ms, "GB/s": nest_bytes / ms / 1e6,
+                               "hbm_frac": nest_bytes / ms / 1e6 / PEAK_HBM_GBS,
+                               "stack_bytes_plain": int(n_el // 2 + n_el // 64 * 4),
+                               "stack_bytes_nested": int(nested_stack_bytes),
+                               "bits_per_weight_nested": 8 * nested_stack_bytes / n_el}
+        nfn_bytes = n_el * (2 + 0.5 + 1 / 64)
+        ms = time_calls(ev, sh, lambda: (bqm.bqm_dequantize(mgu, ybuf), bqm.bqm_dequantize(mdn, ydn)))
+        formats["nf4_nested_dequantize"] = {"ms": ms, "GB/s": nfn_bytes / ms / 1e6,
+                                            "hbm_frac": nfn_bytes / ms / 1e6 / PEAK_HBM_GBS}
         formats["workload"] = "gate_up [256,4096,6144] + down [256,6144,2048]; bytes = 2 (bf16) + 0.5 (codes) " \
                               "+ scale bytes per element"
         result["formats"] = formats
@@ -543,7 +560,10 @@ def main():
         inp5 = synth.layer_inputs(s5, device=dev, with_weights=False)
         r5 = time_layer(s5, inp5, ngu, ndn, ev, sh, max(3, args.steps // 2), 2)
         others["glm_nf4_zipf"] = config_block(s5, r5, "nf4-blocksize64")
-        del inp5, ngu, ndn
+        s5n = dataclasses.replace(s5, fmt="nf4_nested", name="glm_nf4_nested_zipf")
+        r5n = time_layer(s5n, inp5, mgu, mdn, ev, sh, max(3, args.steps // 2), 2)
+        others["glm_nf4_nested_zipf"] = config_block(s5n, r5n, "nf4-blocksize64, double-quantized absmax")
+        del inp5, ngu, ndn, mgu, mdn
         torch.cuda.empty_cache()
         s3 = synth.QWEN
         inp3 = synth.layer_inputs(s3, device=dev)

@@ -31,7 +31,7 @@ STATUS = {0: "BQM_OK", -1: "BQM_ERR_INVALID_ARG", -2: "BQM_ERR_SHAPE", -3: "BQM_
 EXPORTS = ["bqm_abi_version", "bqm_last_error", "bqm_quantize_nvfp4_workspace_size",
            "bqm_quantize_nvfp4", "bqm_quantize_nf4", "bqm_dequantize", "bqm_route",
            "bqm_permute_workspace_size", "bqm_permute", "bqm_moe_workspace_size", "bqm_moe_fwd",
-           "bqm_moe_dgrad", "bqm_moe_dgrad_colwise", "bqm_lora_grad"]
+           "bqm_moe_dgrad", "bqm_moe_dgrad_colwise", "bqm_lora_grad", "bqm_nf4_nest"]
 
 
 class BQMError(RuntimeError):
@@ -44,7 +44,7 @@ class QTensorC(C.Structure):
     _fields_ = [("fmt", C.c_int32), ("scale_mode", C.c_int32), ("n_mat", C.c_int64),
                 ("rows", C.c_int64), ("cols", C.c_int64), ("codes", C.c_void_p),
                 ("scales", C.c_void_p), ("s_dec", C.c_void_p), ("four_over_six", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("nested", C.c_int32)]
 
 
 class MoEDescC(C.Structure):
@@ -76,6 +76,7 @@ def load(path: str = LIB_PATH):
         "bqm_quantize_nvfp4_workspace_size": (sz, [i64, i64, i64, i32]),
         "bqm_quantize_nvfp4": (C.c_int, [vp, i32, vp, C.POINTER(QTensorC), vp, sz, vp]),
         "bqm_quantize_nf4": (C.c_int, [vp, C.POINTER(QTensorC), vp]),
+        "bqm_nf4_nest": (C.c_int, [C.POINTER(QTensorC), C.POINTER(QTensorC), vp]),
         "bqm_dequantize": (C.c_int, [C.POINTER(QTensorC), vp, vp]),
         "bqm_route": (C.c_int, [vp, i64, i32, i32, i32, vp, vp, vp]),
         "bqm_permute_workspace_size": (sz, [i64, i32, i32]),
@@ -124,24 +125,33 @@ class QTensor:
     scales: object
     s_dec: object = None
     four_over_six: int = 1
+    nested: int = 0          # NF4: 1 = double-quantized absmax (see bqm_nf4_nest)
 
     def c(self) -> QTensorC:
         return QTensorC(self.fmt, self.scale_mode, self.n_mat, self.rows, self.cols, _ptr(self.codes),
-                        _ptr(self.scales), _ptr(self.s_dec), self.four_over_six, 0)
+                        _ptr(self.scales), _ptr(self.s_dec), self.four_over_six, int(self.nested))
+
+
+def nf4_nest_groups(rows, cols) -> int:
+    """Groups of 256 absmax blocks per matrix of a nested NF4 stack."""
+    return -(-(rows * cols // 64) // 256)
 
 
 def alloc_qtensor(fmt, n_mat, rows, cols, device="cuda", scale_mode=SCALE_PER_TENSOR,
-                  four_over_six=1) -> QTensor:
+                  four_over_six=1, nested=0) -> QTensor:
     import torch
     codes = torch.empty((n_mat, rows, cols // 2), dtype=torch.uint8, device=device)
     if fmt == FMT_NVFP4:
         scales = torch.empty((n_mat, rows, cols // 16), dtype=torch.uint8, device=device)
         n = n_mat if scale_mode == SCALE_PER_TENSOR else n_mat * rows
         s_dec = torch.empty((max(n, 1),), dtype=torch.float32, device=device)
+    elif nested:
+        scales = torch.empty((n_mat, rows, cols // 64), dtype=torch.uint8, device=device)
+        s_dec = torch.empty((max(n_mat, 1), 1 + nf4_nest_groups(rows, cols)), dtype=torch.float32, device=device)
     else:
         scales = torch.empty((n_mat, rows, cols // 64), dtype=torch.float32, device=device)
         s_dec = None
-    return QTensor(fmt, scale_mode, n_mat, rows, cols, codes, scales, s_dec, four_over_six)
+    return QTensor(fmt, scale_mode, n_mat, rows, cols, codes, scales, s_dec, four_over_six, nested)
 
 
 # ----------------------------------------------------------------------------
@@ -174,6 +184,13 @@ def bqm_quantize_nf4(x, out: QTensor, stream=None):
     qc = out.c()
     _check(lib.bqm_quantize_nf4(_ptr(x), C.byref(qc), _stream(stream)))
     return out
+
+
+def bqm_nf4_nest(plain: QTensor, nested: QTensor, stream=None):
+    lib = load()
+    pc, nc = plain.c(), nested.c()
+    _check(lib.bqm_nf4_nest(C.byref(pc), C.byref(nc), _stream(stream)))
+    return nested
 
 
 def bqm_dequantize(q: QTensor, y, stream=None):

@@ -58,6 +58,7 @@ struct Seg {
   const float *b_sd;    // NVFP4 per-expert decode scales
   int64_t b_rows, b_cols;  // one expert slice of the B stack is [b_rows, b_cols]
   int64_t b_estride;       // bf16 B: elements from one expert's slice to the next (0: one matrix for all)
+  int b_nested;            // NF4: the absmax is the nested code (b_sc uint8, b_sd [offset, group scales])
   int K;
   int kmod;  // > 0: B is indexed at k mod kmod (A holds a hi/lo pair of K = 2*kmod)
 };
@@ -205,6 +206,23 @@ constexpr bool trans_b() {
   return BSRC == B_NF4_N || BSRC == B_BF_N;
 }
 
+// absmax of NF4 block blk (row-major block index within expert e's matrix) into
+// w[4]: the stored FP32 value, or from the nested code fl(fl(e4m3(q) * s2[blk / 256])
+// + offset), the two roundings kept apart (no contraction into an FMA).  (Forming
+// the nested value later, where the tile is decoded, measured slower for plain NF4.)
+__device__ __forceinline__ void nf4_absmax_load(const Seg &s, int e, int64_t blk, uint32_t *w) {
+#pragma clang fp contract(off)
+  const int64_t nb = s.b_rows * s.b_cols / 64;
+  if (!s.b_nested) {
+    w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * nb + blk]);
+    return;
+  }
+  const float *sdm = s.b_sd + e * (1 + (nb + 255) / 256);
+  const uint32_t q = reinterpret_cast<const uint8_t *>(s.b_sc)[e * nb + blk];
+  const float prod = __builtin_amdgcn_cvt_f32_fp8(q, 0) * sdm[1 + (blk >> 8)];
+  w[4] = __float_as_uint(prod + sdm[0]);
+}
+
 template <class C, int BSRC, int EPI>
 __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I, int k0, BRegs &r) {
   constexpr int BN = C::BN;
@@ -222,7 +240,7 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
     const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + wr * (s.b_cols / 2) + (k0 + kofs) / 2;
     const uint4 a = *reinterpret_cast<const uint4 *>(cp);
     r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-    r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + wr * (s.b_cols / 64) + k0 / 64]);
+    nf4_absmax_load(s, e, wr * (s.b_cols / 64) + k0 / 64, r.w);
   } else if constexpr (BSRC == B_NF4_N) {
     // N-major 4-bit weight [K rows][N cols]: one k row, 32 columns (16 B of codes) per thread
     static_assert(BN == 256 && C::NTHR == 512, "N-major 4-bit tile expects 256 columns and 512 threads");
@@ -233,7 +251,7 @@ __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I
       const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) +
                                                        kk * (s.b_cols / 2) + n / 2);
       r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      r.w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * (slice / 64) + kk * (s.b_cols / 64) + n / 64]);
+      nf4_absmax_load(s, e, kk * (s.b_cols / 64) + n / 64, r.w);
     } else {
       r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
     }
@@ -2068,6 +2086,12 @@ bqm_status check_desc(const bqm_moe_desc *d, const char *who) {
       BQM_REQUIRE(w[i]->scale_mode == BQM_SCALE_PER_TENSOR, BQM_ERR_UNSUPPORTED,
                   "%s: NVFP4 weights need one scale per expert matrix", who);
       BQM_REQUIRE(w[i]->s_dec && aligned16(w[i]->s_dec), BQM_ERR_INVALID_ARG, "%s: weight s_dec NULL/unaligned", who);
+      BQM_REQUIRE(w[i]->nested == 0, BQM_ERR_INVALID_ARG, "%s: nested is for NF4 only", who);
+    } else {
+      BQM_REQUIRE(w[i]->nested == 0 || w[i]->nested == 1, BQM_ERR_INVALID_ARG, "%s: nested must be 0 or 1", who);
+      if (w[i]->nested)
+        BQM_REQUIRE(w[i]->s_dec && aligned16(w[i]->s_dec), BQM_ERR_INVALID_ARG,
+                    "%s: nested NF4 weights need s_dec (offset and group scales)", who);
     }
   }
   BQM_REQUIRE(!d->act_quant || d->w_gu.fmt == BQM_FMT_NVFP4, BQM_ERR_UNSUPPORTED,
@@ -2141,6 +2165,7 @@ Seg seg_q(const void *a, int64_t a_ld, const bqm_qtensor &w, int K) {
   s.b_sd = w.s_dec;
   s.b_rows = w.rows;
   s.b_cols = w.cols;
+  s.b_nested = w.fmt == BQM_FMT_NF4 ? w.nested : 0;
   s.K = K;
   return s;
 }

@@ -483,9 +483,19 @@ __global__ void __launch_bounds__(kThreads) nf4_quant(const uint4 *__restrict__ 
   }
 }
 
-// NF4 dequantize: bf16(fl(level[code] * absmax)).
+// Nested absmax of one NF4 block: fl(fl(e4m3(q) * s2) + offset) (this file is
+// compiled without contraction, so the two roundings stay separate)
+__device__ __forceinline__ float nested_absmax(uint32_t q, const float *sdm, uint32_t blk) {
+  return __builtin_amdgcn_cvt_f32_fp8(q, 0) * sdm[1 + (blk >> 8)] + sdm[0];
+}
+
+// NF4 dequantize: bf16(fl(level[code] * absmax)); kNested: absmax' from the nested
+// code (scales uint8 [blocks], sd per matrix [offset, s2 of each 256-block group],
+// nb blocks and G groups per matrix)
+template <bool kNested>
 __global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restrict__ codes,
-                                                        const float *__restrict__ absmax, int64_t nunits,
+                                                        const void *__restrict__ scales, const float *__restrict__ sd,
+                                                        uint32_t nb, uint32_t G, int64_t nunits,
                                                         uint4 *__restrict__ y) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = c_nf4_levels[threadIdx.x];
@@ -498,7 +508,12 @@ __global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restri
     const int64_t u0 = base + it * kThreads + threadIdx.x;
     const int64_t u = u0 < nunits ? u0 : nunits - 1;
     c[it] = codes[u];
-    a[it] = absmax[u >> 3];
+    if constexpr (kNested) {
+      const uint32_t bg = (uint32_t)(u >> 3), m = bg / nb;
+      a[it] = nested_absmax(reinterpret_cast<const uint8_t *>(scales)[bg], sd + (int64_t)m * (1 + G), bg - m * nb);
+    } else {
+      a[it] = reinterpret_cast<const float *>(scales)[u >> 3];
+    }
   }
 #pragma unroll
   for (int it = 0; it < kDqIter; ++it) {
@@ -509,6 +524,68 @@ __global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restri
       for (int p = 0; p < 4; ++p)
         o[p] = pack_bf16_rne(lv[(c[it] >> (8 * p)) & 0xFu] * a[it], lv[(c[it] >> (8 * p + 4)) & 0xFu] * a[it]);
       st_nt(&y[u], make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
+}
+
+// Nested absmax, pass 1: one workgroup per matrix of nb blocks.  Every thread adds
+// a strided share of the FP32 absmax in FP64, the 256 partial sums are added in a
+// fixed tree, and offset = fl32(sum / nb) goes to sd[m (1 + G)].
+constexpr int64_t kNestGroup = 256;
+
+__global__ void __launch_bounds__(kThreads) nf4_nest_offset(const float *__restrict__ absmax, int64_t nb, int64_t G,
+                                                            float *__restrict__ sd) {
+  __shared__ double part[kThreads];
+  const int64_t m = blockIdx.x;
+  const float *a = absmax + m * nb;
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < nb; i += kThreads) acc += (double)a[i];
+  part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sd[m * (1 + G)] = (float)(part[0] / (double)nb);
+}
+
+// Pass 2: one wave per group of 256 blocks (all matrices' groups in one grid),
+// four blocks per lane: d = fl(a - offset), t = max |d| over the group,
+// s2 = fl(t / 448), code = e4m3(|fl(d / s2)|) with the sign bit for d < 0.
+__global__ void __launch_bounds__(kThreads) nf4_nest_groups(const float *__restrict__ absmax, int64_t nb, int64_t G,
+                                                            int64_t ngroups, uint8_t *__restrict__ qcodes,
+                                                            float *__restrict__ sd) {
+  const int64_t gg = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (gg >= ngroups) return;
+  const int64_t m = gg / G, g = gg - m * G;
+  const int lane = threadIdx.x & 63;
+  const float *a = absmax + m * nb;
+  float *sm = sd + m * (1 + G);
+  const float off = sm[0];
+  float d[4];
+  float t = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t bl = g * kNestGroup + 64 * j + lane;
+    d[j] = bl < nb ? a[bl] - off : 0.0f;
+    t = fmaxf(t, fabsf(d[j]));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) t = fmaxf(t, __shfl_xor(t, o, 64));
+  const float s2 = t / 448.0f;
+  if (lane == 0) sm[1 + g] = s2;
+  uint8_t *qm = qcodes + m * nb;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t bl = g * kNestGroup + 64 * j + lane;
+    if (bl < nb) {
+      uint32_t q = 0, unused;
+      if (s2 > 0.0f) {
+        const float yv = d[j] / s2;
+        e4m3_pair(fabsf(yv), 0.0f, q, unused);
+        q |= yv < 0.0f ? 0x80u : 0u;
+      }
+      qm[bl] = (uint8_t)q;
     }
   }
 }
@@ -528,6 +605,8 @@ bqm_status check_qtensor(const bqm_qtensor *q, const char *who, bool need_sdec) 
               "%s: unknown format %d", who, q->fmt);
   BQM_REQUIRE(q->n_mat >= 0 && q->rows >= 0 && q->cols >= 0, BQM_ERR_INVALID_ARG,
               "%s: negative size", who);
+  BQM_REQUIRE(q->nested == 0 || (q->fmt == BQM_FMT_NF4 && q->nested == 1), BQM_ERR_INVALID_ARG,
+              "%s: nested must be 0, or 1 for NF4", who);
   int64_t blk = q->fmt == BQM_FMT_NVFP4 ? 16 : 64;
   BQM_REQUIRE(q->cols % blk == 0, BQM_ERR_SHAPE, "%s: cols=%lld is not a multiple of %lld", who,
               (long long)q->cols, (long long)blk);
@@ -543,6 +622,11 @@ bqm_status check_qtensor(const bqm_qtensor *q, const char *who, bool need_sdec) 
       BQM_REQUIRE(q->s_dec, BQM_ERR_INVALID_ARG, "%s: s_dec pointer is NULL", who);
       BQM_REQUIRE(aligned16(q->s_dec), BQM_ERR_ALIGN, "%s: s_dec not 16-byte aligned", who);
     }
+  } else if (q->nested) {
+    BQM_REQUIRE(q->s_dec, BQM_ERR_INVALID_ARG, "%s: nested NF4 needs s_dec", who);
+    BQM_REQUIRE(aligned16(q->s_dec), BQM_ERR_ALIGN, "%s: s_dec not 16-byte aligned", who);
+    BQM_REQUIRE(q->n_mat * q->rows * q->cols / 64 < ((int64_t)1 << 31), BQM_ERR_SHAPE,
+                "%s: nested NF4 stack too large", who);
   }
   return BQM_OK;
 }
@@ -630,8 +714,8 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
 extern "C" bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out, void *stream) {
   bqm_status st = check_qtensor(out, "bqm_quantize_nf4", false);
   if (st != BQM_OK) return st;
-  BQM_REQUIRE(out->fmt == BQM_FMT_NF4, BQM_ERR_INVALID_ARG,
-              "bqm_quantize_nf4: out->fmt must be BQM_FMT_NF4");
+  BQM_REQUIRE(out->fmt == BQM_FMT_NF4 && !out->nested, BQM_ERR_INVALID_ARG,
+              "bqm_quantize_nf4: out must be plain NF4 (FP32 absmax; bqm_nf4_nest makes the nested form)");
   const int64_t n = out->n_mat * out->rows * out->cols;
   if (n == 0) return BQM_OK;
   BQM_REQUIRE(x, BQM_ERR_INVALID_ARG, "bqm_quantize_nf4: x is NULL");
@@ -660,10 +744,44 @@ extern "C" bqm_status bqm_dequantize(const bqm_qtensor *q, uint16_t *y, void *st
         n / 8, seg_units, reinterpret_cast<uint4 *>(y));
     return launch_status("nvfp4_dequant");
   }
-  nf4_dequant<<<dq_grid(n), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(q->codes),
-                                              reinterpret_cast<const float *>(q->scales), n / 8,
-                                              reinterpret_cast<uint4 *>(y));
+  const int64_t nb = q->rows * q->cols / 64;
+  if (q->nested)
+    nf4_dequant<true><<<dq_grid(n), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(q->codes), q->scales,
+                                                      q->s_dec, (uint32_t)nb, (uint32_t)cdiv(nb, kNestGroup), n / 8,
+                                                      reinterpret_cast<uint4 *>(y));
+  else
+    nf4_dequant<false><<<dq_grid(n), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(q->codes), q->scales,
+                                                       nullptr, 0, 0, n / 8, reinterpret_cast<uint4 *>(y));
   return launch_status("nf4_dequant");
+}
+
+extern "C" bqm_status bqm_nf4_nest(const bqm_qtensor *plain, bqm_qtensor *nested, void *stream) {
+  bqm_status st = check_qtensor(plain, "bqm_nf4_nest", false);
+  if (st != BQM_OK) return st;
+  st = check_qtensor(nested, "bqm_nf4_nest", false);
+  if (st != BQM_OK) return st;
+  BQM_REQUIRE(plain->fmt == BQM_FMT_NF4 && !plain->nested, BQM_ERR_INVALID_ARG,
+              "bqm_nf4_nest: plain must be NF4 with FP32 absmax");
+  BQM_REQUIRE(nested->fmt == BQM_FMT_NF4 && nested->nested == 1, BQM_ERR_INVALID_ARG,
+              "bqm_nf4_nest: nested must be NF4 with nested = 1");
+  BQM_REQUIRE(plain->n_mat == nested->n_mat && plain->rows == nested->rows && plain->cols == nested->cols,
+              BQM_ERR_SHAPE, "bqm_nf4_nest: shapes differ");
+  const int64_t n = plain->n_mat * plain->rows * plain->cols;
+  if (n == 0) return BQM_OK;
+  BQM_REQUIRE(plain->n_mat < ((int64_t)1 << 31), BQM_ERR_SHAPE, "bqm_nf4_nest: too many matrices");
+  hipStream_t s = as_stream(stream);
+  if (nested->codes != plain->codes &&
+      hipMemcpyAsync(nested->codes, plain->codes, (size_t)(n / 2), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return launch_status("bqm_nf4_nest: copy of the codes");
+  const int64_t nb = plain->rows * plain->cols / 64, G = cdiv(nb, kNestGroup);
+  const float *am = reinterpret_cast<const float *>(plain->scales);
+  nf4_nest_offset<<<(unsigned)plain->n_mat, kThreads, 0, s>>>(am, nb, G, nested->s_dec);
+  st = launch_status("nf4_nest_offset");
+  if (st != BQM_OK) return st;
+  const int64_t ngroups = plain->n_mat * G;
+  nf4_nest_groups<<<(unsigned)cdiv(ngroups, kThreads / 64), kThreads, 0, s>>>(
+      am, nb, G, ngroups, reinterpret_cast<uint8_t *>(nested->scales), nested->s_dec);
+  return launch_status("nf4_nest_groups");
 }
 
 namespace bqm {

@@ -57,11 +57,18 @@ typedef enum { BQM_SCALE_PER_TENSOR = 0, BQM_SCALE_PER_ROW = 1 } bqm_scale_mode;
  *           element 2j+1 the high nibble.  NVFP4: E2M1 with the sign in bit 3.
  *           NF4: index 0..15 into the NormalFloat codebook.
  *   scales: NVFP4: uint8 E4M3FN bits [n_mat, rows, cols/16];
- *           NF4: float absmax [n_mat, rows, cols/64].
- *   s_dec : NVFP4 only: float [n_mat] (per tensor) or [n_mat*rows] (per row);
+ *           NF4: float absmax [n_mat, rows, cols/64];
+ *           NF4 nested: uint8 E4M3FN bits [n_mat, rows, cols/64] (see below).
+ *   s_dec : NVFP4: float [n_mat] (per tensor) or [n_mat*rows] (per row);
  *           the value of an element is e2m1(code) * e4m3(scale) * s_dec.
- *           NULL for NF4.
- *   four_over_six: the mode the stack was quantized with (metadata). */
+ *           NF4: NULL.  NF4 nested: float [n_mat, 1 + G], G = ceil(rows*cols/64/256):
+ *           per matrix the offset, then the scale of each group of 256 blocks.
+ *   four_over_six: the mode the stack was quantized with (metadata).
+ *   nested: NF4 only.  1: the absmax is double-quantized (the nested code of
+ *           bnb's quant state that the nf4moe page names; read here as QLoRA's
+ *           double quantization): block b of a matrix (row-major block order)
+ *           has absmax' = fl(fl(e4m3(scales[b]) * s_dec[1 + b/256]) + s_dec[0]),
+ *           and an element decodes to bf16(fl(level[code] * absmax')). */
 typedef struct {
   int32_t fmt; /* bqm_format */
   int32_t scale_mode; /* bqm_scale_mode (NVFP4) */
@@ -70,7 +77,7 @@ typedef struct {
   void *scales;
   float *s_dec;
   int32_t four_over_six;
-  int32_t reserved;
+  int32_t nested;
 } bqm_qtensor;
 
 /* ABI version of the loaded library (BQM_ABI_VERSION). */
@@ -118,9 +125,23 @@ bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six, const fl
  * x: bf16 [n_mat, rows, cols], cols % 64 == 0; out->fmt == BQM_FMT_NF4. */
 bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out /* host struct */, void *stream);
 
+/* Nested (double-quantized) absmax of an NF4 stack (the nested code of bnb's
+ * quant state, nf4moe page, section "Getting it to load"; the page gives no
+ * details, so this is QLoRA's published double quantization with E4M3 as the
+ * 8-bit float).  Per matrix, over its absmax in row-major block order:
+ *   offset = fl32(sum / nb) (sum in FP64, nb blocks), d = fl(absmax - offset),
+ *   per group of 256 blocks s2 = fl(max|d| / 448) and codes e4m3_rne_sat(fl(d / s2))
+ *   (sign bit for d < 0; s2 = 0 gives codes 0).
+ * plain: an NF4 stack with FP32 absmax (as bqm_quantize_nf4 writes; read only).
+ * nested: the same shape, fmt BQM_FMT_NF4 and nested = 1; its scales (uint8
+ * [n_mat, rows, cols/64]) and s_dec (float [n_mat, 1 + G]) are written, and its
+ * codes get the plain codes (copied unless the two pointers are equal).  The
+ * FP64 sum is added in a fixed order, so repeated calls give identical bits. */
+bqm_status bqm_nf4_nest(const bqm_qtensor *plain, bqm_qtensor *nested, void *stream);
+
 /* Dequantize a stack to bf16 [n_mat, rows, cols]:
  *   NVFP4: bf16_rne(fl32(e2m1(code) * e4m3(scale)) * s_dec)  (one FP32 rounding)
- *   NF4:   bf16_rne(fl32(level[code] * absmax))
+ *   NF4:   bf16_rne(fl32(level[code] * absmax)), absmax' when nested
  * The same values (without the s_dec factor, which the GEMMs apply to their
  * FP32 accumulators) are what the MoE GEMMs multiply. */
 bqm_status bqm_dequantize(const bqm_qtensor *q /* host struct */, uint16_t *y, void *stream);

@@ -32,6 +32,12 @@ def quantize_stack_gpu(w, fmt):
     else:
         q = bqm.alloc_qtensor(bqm.FMT_NF4, E, rows, cols, device=w.device)
         bqm.bqm_quantize_nf4(w, q)
+        if fmt == "nf4_nested":
+            n = bqm.alloc_qtensor(bqm.FMT_NF4, E, rows, cols, device=w.device, nested=1)
+            n.codes = q.codes              # the nested stack keeps the plain codes
+            bqm.bqm_nf4_nest(q, n)
+            torch.cuda.synchronize()
+            return n
     return q
 
 
@@ -39,7 +45,7 @@ def poison_experts(q, experts, fmt):
     """Make the scales of the given experts decode to NaN (E4M3 0x7F / NaN absmax)."""
     import torch
     for e in experts:
-        if fmt == "nvfp4":
+        if fmt in ("nvfp4", "nf4_nested"):
             q.scales[e].fill_(0x7F)
         else:
             q.scales[e].fill_(float("nan"))

@@ -77,6 +77,14 @@ def test_small_nf4_skewed_with_empty_experts():
     assert (counts == 0).sum() >= 16
 
 
+def test_small_nf4_nested_absmax_skewed_with_empty_experts():
+    # NF4 weights with the double-quantized absmax (the GEMMs rebuild absmax' from
+    # the E4M3 code, the group scale and the offset); empty experts poisoned
+    g, o = compare_full(small("small_nf4n", fmt="nf4_nested", logits="zipf", E=64, T=200, k=4, r=8),
+                        poison_empty=True)
+    assert (np.bincount(o["idx"].reshape(-1), minlength=64) == 0).sum() >= 16
+
+
 def test_nvfp4_routed_only_poisoned_experts():
     shape = small("small_zipf", logits="zipf", E=48, T=128, k=4, r=8)
     g, o = compare_full(shape, poison_empty=True)
@@ -190,6 +198,11 @@ def test_full_qwen_w4a4_sampled():
 
 def test_full_glm_nf4_sampled():
     sampled_full(synth.GLM_NF4, tokens=[1, 9000], lora_experts=[0])
+
+
+def test_full_glm_nf4_nested_sampled():
+    sampled_full(dataclasses.replace(synth.GLM_NF4, fmt="nf4_nested", name="glm_nf4_nested"),
+                 tokens=[2, 7000], lora_experts=[5])
 
 
 def test_full_glm_shared_lora_a_matches_replicated():

@@ -169,6 +169,83 @@ def test_nf4_quantize_dequantize_bit_exact(shape):
     assert (np_f32(y).view(np.uint32) == oq.dequantize_nf4(ref).view(np.uint32)).all()
 
 
+def _check_nested(q_plain, n, x_host, mats=None):
+    """The nested stack n (from bqm_nf4_nest of q_plain) against the oracle's nesting
+    of its own NF4 quantization of x_host, matrix by matrix, bit for bit."""
+    for m in (range(x_host.shape[0]) if mats is None else mats):
+        ref = oq.nest_absmax(oq.quantize_nf4(x_host[m:m + 1]))
+        sd = np_f32(n.s_dec[m])
+        assert sd[0].view(np.uint32) == ref.offset[0].view(np.uint32), f"matrix {m}: offset"
+        assert (sd[1:].view(np.uint32) == ref.group_scale[0].view(np.uint32)).all(), f"matrix {m}: group scales"
+        got = np_u8(n.scales[m])
+        bad = np.nonzero(got != ref.absmax_q[0])
+        assert bad[0].size == 0, f"matrix {m}: {bad[0].size} nested codes differ"
+        assert (np_u8(n.codes[m]) == ref.codes[0]).all(), f"matrix {m}: codes"
+
+
+@pytest.mark.parametrize("shape", [(3, 7, 640), (2, 96, 512), (1, 1, 64), (2, 300, 128)])
+def test_nf4_nested_absmax_bit_exact(shape):
+    # 70, 768, 1 and 600 blocks per matrix: one ragged group, whole groups, one
+    # block, and a ragged third group; matrix 0 has a zero block, and a constant-
+    # absmax matrix (every block scaled to the same largest value) where available
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    log(f"nf4 nested {shape}")
+    x = synth.normal(shape, 0.02, (95, shape[1]), device="cpu", outliers=True)
+    x[0, 0, :64] = 0.0
+    if shape[0] > 1:
+        xb = x[1].reshape(-1, 64).float()
+        xb[:, 0] = 0.5                               # absmax 0.5 in every block
+        x[1] = xb.clamp(-0.5, 0.5).to(torch.bfloat16).reshape(x[1].shape)
+    xh = np_f32(x)
+    x = x.to(dev)
+    q = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev)
+    bqm.bqm_quantize_nf4(x, q)
+    n = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev, nested=1)
+    bqm.bqm_nf4_nest(q, n)                           # separate codes buffer: copied
+    torch.cuda.synchronize()
+    _check_nested(q, n, xh)
+    if shape[0] > 1:
+        assert (np_f32(n.s_dec[1])[1:] == 0).all()   # constant absmax: d = 0 everywhere
+    y = torch.empty_like(x)
+    bqm.bqm_dequantize(n, y)
+    ref = oq.dequantize_nf4_nested(oq.nest_absmax(oq.quantize_nf4(xh)))
+    assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
+    # nesting twice gives the same bits (the FP64 sum runs in a fixed order)
+    n2 = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev, nested=1)
+    n2.codes = q.codes
+    bqm.bqm_nf4_nest(q, n2)
+    assert torch.equal(n2.scales, n.scales) and torch.equal(n2.s_dec, n.s_dec)
+
+
+def test_nf4_nested_full_size_sampled():
+    """Nested absmax of the full gate_up stack [256, 4096, 6144] (1536 groups per
+    matrix); two matrices against the oracle, bit for bit."""
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    log("nested NF4 at full size: generating the gate_up stack on the device")
+    wgu, wdn = synth.quantizer_stacks(device=dev)
+    del wdn
+    torch.cuda.empty_cache()
+    q = bqm.alloc_qtensor(bqm.FMT_NF4, *wgu.shape, device=dev)
+    bqm.bqm_quantize_nf4(wgu, q)
+    n = bqm.alloc_qtensor(bqm.FMT_NF4, *wgu.shape, device=dev, nested=1)
+    n.codes = q.codes
+    bqm.bqm_nf4_nest(q, n)
+    torch.cuda.synchronize()
+    for m in (0, 201):
+        log(f"  matrix {m}: oracle quantize + nest")
+        ref = oq.nest_absmax(oq.quantize_nf4(np_f32(wgu[m:m + 1])))
+        sd = np_f32(n.s_dec[m])
+        assert sd[0].view(np.uint32) == ref.offset[0].view(np.uint32)
+        assert (sd[1:].view(np.uint32) == ref.group_scale[0].view(np.uint32)).all()
+        assert (np_u8(n.scales[m]) == ref.absmax_q[0]).all()
+    del q, n, wgu
+    torch.cuda.empty_cache()
+
+
 def test_nf4_codes_at_midpoints_and_bucket_edges():
     """NF4 coding near its decision points: in blocks whose absmax is 1 (so x / absmax
     is x), every midpoint between two levels, its bf16 neighbours, every multiple of
