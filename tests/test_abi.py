@@ -110,3 +110,23 @@ def test_moe_shared_lora_a_flag_and_workspace(lib):
         a = lib.bqm_moe_workspace_size(C.byref(_desc(0, T=T, E=E)))
         b = lib.bqm_moe_workspace_size(C.byref(_desc(1, T=T, E=E)))
         assert b - a == -(-split * 8 * 256 * 4 // 256) * 256, (T, E)
+
+
+def test_nf4_nest_rejects_bad_arguments(lib):
+    # host-side checks only (each call fails before any device work)
+    def q(fmt=2, n=1, rows=4, cols=64, nested=0, sdec=16):
+        return bqm.QTensorC(fmt, 0, n, rows, cols, 16, 16, sdec, 1, nested)
+    plain, nested = q(), q(nested=1)
+    bad = [(q(nested=1), nested, -1),            # plain side already nested
+           (plain, q(nested=0), -1),             # target not marked nested
+           (plain, q(nested=1, rows=8), -2),     # shapes differ
+           (plain, q(nested=1, sdec=None), -1),  # nested needs the offset / group scales
+           (plain, q(nested=2), -1),             # nested is 0 or 1
+           (q(fmt=1, cols=64), nested, -1)]      # NVFP4 stacks cannot be nested
+    for a, b, want in bad:
+        assert lib.bqm_nf4_nest(C.byref(a), C.byref(b), None) == want, bqm.bqm_last_error()
+    # the NF4 quantizer writes the plain form only; an NVFP4 stack cannot carry nested = 1
+    assert lib.bqm_quantize_nf4(16, C.byref(q(nested=1)), None) == -1
+    assert lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q(fmt=1, cols=64, nested=1)), 16, 64, None) == -1
+    # empty stacks are no-ops
+    assert lib.bqm_nf4_nest(C.byref(q(n=0)), C.byref(q(n=0, nested=1)), None) == 0
