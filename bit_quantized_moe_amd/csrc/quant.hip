@@ -528,21 +528,22 @@ __global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restri
   }
 }
 
-// Nested absmax, pass 1: one workgroup per matrix of nb blocks.  Every thread adds
-// a strided share of the FP32 absmax in FP64, the 256 partial sums are added in a
-// fixed tree, and offset = fl32(sum / nb) goes to sd[m (1 + G)].
+// Nested absmax, pass 1: one workgroup of 1024 threads per matrix of nb blocks.
+// Every thread adds a strided share of the FP32 absmax in FP64, the 1024 partial
+// sums are added in a fixed tree, and offset = fl32(sum / nb) goes to sd[m (1 + G)].
 constexpr int64_t kNestGroup = 256;
+constexpr int kNestSumThreads = 1024;
 
-__global__ void __launch_bounds__(kThreads) nf4_nest_offset(const float *__restrict__ absmax, int64_t nb, int64_t G,
-                                                            float *__restrict__ sd) {
-  __shared__ double part[kThreads];
+__global__ void __launch_bounds__(kNestSumThreads) nf4_nest_offset(const float *__restrict__ absmax, int64_t nb,
+                                                                   int64_t G, float *__restrict__ sd) {
+  __shared__ double part[kNestSumThreads];
   const int64_t m = blockIdx.x;
   const float *a = absmax + m * nb;
   double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < nb; i += kThreads) acc += (double)a[i];
+  for (int64_t i = threadIdx.x; i < nb; i += kNestSumThreads) acc += (double)a[i];
   part[threadIdx.x] = acc;
   __syncthreads();
-  for (int w = kThreads / 2; w > 0; w >>= 1) {
+  for (int w = kNestSumThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
     __syncthreads();
   }
@@ -775,7 +776,7 @@ extern "C" bqm_status bqm_nf4_nest(const bqm_qtensor *plain, bqm_qtensor *nested
     return launch_status("bqm_nf4_nest: copy of the codes");
   const int64_t nb = plain->rows * plain->cols / 64, G = cdiv(nb, kNestGroup);
   const float *am = reinterpret_cast<const float *>(plain->scales);
-  nf4_nest_offset<<<(unsigned)plain->n_mat, kThreads, 0, s>>>(am, nb, G, nested->s_dec);
+  nf4_nest_offset<<<(unsigned)plain->n_mat, kNestSumThreads, 0, s>>>(am, nb, G, nested->s_dec);
   st = launch_status("nf4_nest_offset");
   if (st != BQM_OK) return st;
   const int64_t ngroups = plain->n_mat * G;
