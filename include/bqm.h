@@ -231,7 +231,8 @@ size_t bqm_moe_workspace_size(const bqm_moe_desc *d);
  *   h = X~ DQ(W_gu[e])^T + s (X A_gu[e]^T) B_gu[e]^T,  a = silu(h[:, :I]) * h[:, I:],
  *   y = a~ DQ(W_dn[e])^T + s (a A_dn[e]^T) B_dn[e]^T
  * (nf4moe page, the QuantizedNaiveMoe forward; only experts that receive tokens
- * are read).  x bf16 [T, H], topk_idx i32 [T, k], topk_w f32 [T, k], y bf16
+ * are read; A_gu[e], A_dn[e] stand for the one shared A with lora_shared_a; the
+ * weights are NVFP4 or NF4, plain or nested).  x bf16 [T, H], topk_idx i32 [T, k], topk_w f32 [T, k], y bf16
  * [T, H] (the layer output).  Accumulation is FP32; the workspace keeps h in FP32 and
  * a (the down projection's bf16 operand) and the routed rows y in bf16, as the pages'
  * bf16 module does; the combine sums the k rows of a token in FP32. */
