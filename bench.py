@@ -403,9 +403,9 @@ def main():
         print(json.dumps({"copy_bytes_per_call": 1 << 30, "calls": 3}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the layer is built and timed on a single MI355X; "
-              "multi-GPU runs are not part of this build (see DESIGN.md for how it would shard).",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs and is timed on a single MI355X. "
+              "There is no multi-GPU path (expert parallelism would add one all-to-all of the "
+              "routed rows each way around these same kernels).", file=sys.stderr)
         sys.exit(2)
 
     import torch

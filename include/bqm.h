@@ -41,7 +41,7 @@ typedef enum {
   BQM_ERR_INVALID_ARG = -1, /* null pointer, bad enum, negative size */
   BQM_ERR_SHAPE = -2,       /* sizes that break a block or tile rule */
   BQM_ERR_ALIGN = -3,       /* a device pointer not 16-byte aligned */
-  BQM_ERR_UNSUPPORTED = -4, /* a valid request this build does not implement */
+  BQM_ERR_UNSUPPORTED = -4, /* a valid request the library does not implement */
   BQM_ERR_WORKSPACE = -5,   /* workspace missing or too small */
   BQM_ERR_HIP = -6          /* a HIP launch or runtime error */
 } bqm_status;
