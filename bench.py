@@ -96,7 +96,7 @@ def stage_flops(s):
     }
 
 
-def cpu_baseline(inp, shape, experts=(0, 1, 2, 3)):
+def cpu_baseline(inp, shape, experts=tuple(range(8))):
     """The oracle (float64 CPU definition) on all routed rows of a few experts, timed on the host."""
     import numpy as np
     from oracle import moe as om
