@@ -96,9 +96,21 @@ def stage_flops(s):
     }
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(inp, shape, experts=tuple(range(8))):
-    """The oracle (float64 CPU definition) on all routed rows of a few experts, timed on the host."""
-    import numpy as np
+    """The oracle (float64 CPU definition) on all routed rows of a few experts, timed on
+    the host.  The oracle's own quantization of the touched experts (the frozen weights
+    are quantized once per load, as on the GPU) runs before the timed region and is
+    reported on its own."""
     from oracle import moe as om
     from oracle import routing as orr
     from tests.moe_harness import HostInputs
@@ -106,6 +118,11 @@ def cpu_baseline(inp, shape, experts=tuple(range(8))):
     w = h.weights()
     idx, tw = orr.route(h.logits, shape.k)
     rows = int(sum((idx == e).sum() for e in experts))
+    tq = time.perf_counter()
+    for e in experts:
+        om.expert_matrix(w.gu, e)
+        om.expert_matrix(w.dn, e)
+    tq = time.perf_counter() - tq
     t0 = time.perf_counter()
     _, cache = om.forward(w, h.x, idx, tw, experts=set(experts))
     _, _, bwd = om.dgrad(w, cache, h.dout, tw)
@@ -117,16 +134,22 @@ def cpu_baseline(inp, shape, experts=tuple(range(8))):
         threads = max(i.get("num_threads", 1) for i in threadpool_info()) or threads
     except Exception:
         pass
+    per_matrix = (2 * shape.I * shape.H + shape.H * shape.I) * len(experts)
     return {"value": (rows / shape.k) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 oracle forward+dgrad+LoRA grads (incl. its own quantization of the touched "
-                      f"experts) over all {rows} routed rows of experts {list(experts)}; tokens = rows / k; "
-                      f"{dt:.1f} s"}
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"float64 oracle forward+dgrad+LoRA grads over all {rows} routed rows of experts "
+                      f"{list(experts)} (their NVFP4 weights quantized by the oracle beforehand); tokens = rows / k; "
+                      f"{dt:.1f} s",
+            "oracle_quantize": {"experts": len(experts), "elements": per_matrix, "s": round(tq, 2),
+                                "elements_per_s": per_matrix / tq}}
 
 
-def token_sweep(shape, wgu, wdn, ev, sh, tokens=(438, 1024, 2048, 4096, 8192), reps=5):
-    """Layer step (route + fwd + dgrad + LoRA grads) at smaller token counts over the
-    same quantized experts: where the per-step read of the hit experts' weights
-    (5.44 GB when every expert is hit) gives way to MFMA time."""
+def token_sweep(shape, wgu, wdn, ev, sh, tokens=(438, 1024, 2048, 4096, 8192, 16384), reps=5):
+    """Layer step (route + fwd + dgrad + LoRA grads) at token counts from the pages'
+    median SFT row (438) up over the same quantized experts: where the per-step read of
+    the hit experts' weights gives way to MFMA time.  Each of the four grouped GEMMs
+    reads one stack (gate_up or down) of every hit expert once, so a step reads the hit
+    experts' NVFP4 bytes twice (10.9 GB when all 256 are hit)."""
     import dataclasses
     import torch
     import bit_quantized_moe_amd as bqm
@@ -163,8 +186,11 @@ def token_sweep(shape, wgu, wdn, ev, sh, tokens=(438, 1024, 2048, 4096, 8192), r
         torch.cuda.synchronize()
         ms = ev.elapsed_ms(e[0], e[1]) / reps
         hit = int(torch.unique(idx).numel())
+        wbytes = 2 * hit * (2 * s.I * s.H + s.H * s.I) * (0.5 + 1 / 16)
         rows.append({"T": T, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
-                     "experts_hit": hit})
+                     "experts_hit": hit, "weight_bytes_per_step": int(wbytes),
+                     "weight_read_floor_ms": round(wbytes / (PEAK_HBM_GBS * 1e6), 4),
+                     "weight_read_frac": round(wbytes / (PEAK_HBM_GBS * 1e6) / ms, 4)})
         del inp, d, ws, idx, tw, out, dx, dtw, g
         torch.cuda.empty_cache()
     return rows
@@ -308,13 +334,12 @@ def colwise_comparison(s, inp, wgu, wdn, ev, sh, reps=5):
     columnwise copy dequantizes to different values)."""
     import torch
     import bit_quantized_moe_amd as bqm
-    from tests.moe_harness import quantize_stack_gpu
     dev = torch.device("cuda")
     t = inp.w_gu.transpose(1, 2).contiguous()
-    cgu = quantize_stack_gpu(t, "nvfp4")
+    cgu = bqm.quantize_stack(t, "nvfp4")
     del t
     t = inp.w_dn.transpose(1, 2).contiguous()
-    cdn = quantize_stack_gpu(t, "nvfp4")
+    cdn = bqm.quantize_stack(t, "nvfp4")
     del t
     torch.cuda.empty_cache()
     d = bqm.MoEDesc(s.T, s.H, s.I, s.E, s.k, s.r, wgu, wdn, A_gu=inp.A_gu, B_gu=inp.B_gu, A_dn=inp.A_dn,
@@ -386,10 +411,9 @@ def main():
     ap.add_argument("--no-quantizer", action="store_true")
     ap.add_argument("--main-only", action="store_true",
                     help="only the GLM NVFP4 layer step (and the quantizer unless --no-quantizer): no NF4, "
-                         "W4A4 or format-conversion figures")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the layer step at smaller token counts (extra kernel calls at other sizes)")
-    ap.add_argument("--no-sweep", action="store_true", help=argparse.SUPPRESS)  # the default
+                         "W4A4, format-conversion or token-sweep figures")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the layer step at smaller token counts (the token sweep)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -411,7 +435,6 @@ def main():
     import torch
     import bit_quantized_moe_amd as bqm
     import synth
-    from tests.moe_harness import quantize_stack_gpu
 
     dev = torch.device("cuda")
     bqm.load()
@@ -468,8 +491,8 @@ def main():
         wgu, wdn = qgu, qdn
         del wsq
     else:
-        wgu = quantize_stack_gpu(inp.w_gu, "nvfp4")
-        wdn = quantize_stack_gpu(inp.w_dn, "nvfp4")
+        wgu = bqm.quantize_stack(inp.w_gu, "nvfp4")
+        wdn = bqm.quantize_stack(inp.w_dn, "nvfp4")
 
     res = time_layer(s, inp, wgu, wdn, ev, sh, args.steps, args.warmup)
     sf = stage_flops(s)
@@ -567,8 +590,8 @@ def main():
         torch.cuda.empty_cache()
         s3 = synth.QWEN
         inp3 = synth.layer_inputs(s3, device=dev)
-        q3gu = quantize_stack_gpu(inp3.w_gu, "nvfp4")
-        q3dn = quantize_stack_gpu(inp3.w_dn, "nvfp4")
+        q3gu = bqm.quantize_stack(inp3.w_gu, "nvfp4")
+        q3dn = bqm.quantize_stack(inp3.w_dn, "nvfp4")
         r3 = time_layer(s3, inp3, q3gu, q3dn, ev, sh, max(3, args.steps), 2)
         others["qwen3_30b_a3b_w4a4"] = config_block(s3, r3, "nvfp4-4over6-rowwise, activations nvfp4 per token")
         del inp3, q3gu, q3dn
@@ -591,7 +614,7 @@ def main():
                                     "rows_shared_lora_a": decode_sweep(dataclasses.replace(shape, shared_a=True),
                                                                        wgu, wdn, ev, sh)}
 
-    if args.sweep:
+    if not args.no_sweep and not args.main_only:
         torch.cuda.empty_cache()
         result["token_sweep"] = token_sweep(shape, wgu, wdn, ev, sh)
     if not args.no_cpu_baseline:

@@ -154,6 +154,32 @@ def alloc_qtensor(fmt, n_mat, rows, cols, device="cuda", scale_mode=SCALE_PER_TE
     return QTensor(fmt, scale_mode, n_mat, rows, cols, codes, scales, s_dec, four_over_six, nested)
 
 
+def quantize_stack(w, fmt: str, stream=None) -> QTensor:
+    """Allocate and fill a rowwise-quantized stack from a bf16 [n_mat, rows, cols] tensor:
+    fmt "nvfp4" (per-tensor scale, Four-Over-Six), "nf4" or "nf4_nested" (NF4, then
+    bqm_nf4_nest; the nested stack keeps the plain codes).  Allocation plus the library
+    calls, nothing else."""
+    import torch
+    n_mat, rows, cols = w.shape
+    if fmt == "nvfp4":
+        q = alloc_qtensor(FMT_NVFP4, n_mat, rows, cols, device=w.device)
+        wsb = bqm_quantize_nvfp4_workspace_size(n_mat, rows, cols, SCALE_PER_TENSOR)
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=w.device)
+        bqm_quantize_nvfp4(w, 1, None, q, ws, stream)
+        return q
+    if fmt not in ("nf4", "nf4_nested"):
+        raise ValueError(f"unknown weight format {fmt!r}")
+    q = alloc_qtensor(FMT_NF4, n_mat, rows, cols, device=w.device)
+    bqm_quantize_nf4(w, q, stream)
+    if fmt == "nf4":
+        return q
+    n = alloc_qtensor(FMT_NF4, n_mat, rows, cols, device=w.device, nested=1)
+    n.codes = q.codes
+    bqm_nf4_nest(q, n, stream)
+    torch.cuda.synchronize()        # the plain FP32 absmax (q.scales) is freed on return
+    return n
+
+
 # ----------------------------------------------------------------------------
 # one wrapper per entry point
 # ----------------------------------------------------------------------------

@@ -2016,18 +2016,22 @@ __global__ void __launch_bounds__(NTHR) sum_parts(const float4 *__restrict__ par
 // combine, routing-weight gradient
 // ---------------------------------------------------------------------------
 // out[t][c] = sum_j w[t,j] * rows[inv[t*k+j]][c] (w = 1 when tw == NULL), j ascending,
-// FP32 accumulation over the bf16 routed rows
+// FP32 accumulation over the bf16 routed rows; pairs placed at or after *n_valid (an
+// expert index outside [0, E)) belong to no expert and add nothing
 __global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict__ rows, const int32_t *__restrict__ inv,
-                                                     const float *__restrict__ tw, int64_t T, int k, int64_t H,
-                                                     uint16_t *__restrict__ out) {
+                                                     const int32_t *__restrict__ n_valid, const float *__restrict__ tw,
+                                                     int64_t T, int k, int64_t H, uint16_t *__restrict__ out) {
   const int64_t cpr = H / 8;
+  const int32_t nv = *n_valid;
   for (int64_t it = (int64_t)blockIdx.x * NTHR + threadIdx.x; it < T * cpr; it += (int64_t)gridDim.x * NTHR) {
     const int64_t t = it / cpr, c = (it % cpr) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < k; ++j) {
       const int64_t f = t * k + j;
+      const int32_t pos = inv[f];
+      if (pos >= nv) continue;
       const float w = tw ? tw[f] : 1.0f;
-      const uint4 v = *reinterpret_cast<const uint4 *>(rows + (int64_t)inv[f] * H + c);
+      const uint4 v = *reinterpret_cast<const uint4 *>(rows + (int64_t)pos * H + c);
       acc[0] += w * bf16_lo(v.x); acc[1] += w * bf16_hi(v.x); acc[2] += w * bf16_lo(v.y); acc[3] += w * bf16_hi(v.y);
       acc[4] += w * bf16_lo(v.z); acc[5] += w * bf16_hi(v.z); acc[6] += w * bf16_lo(v.w); acc[7] += w * bf16_hi(v.w);
     }
@@ -2038,15 +2042,20 @@ __global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict_
   }
 }
 
-// dtw[f] = <dy[t], y[inv[f]]>, one wave per routed pair
+// dtw[f] = <dy[t], y[inv[f]]>, one wave per routed pair (0 for a pair of no expert)
 __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict__ dy, const uint16_t *__restrict__ y,
-                                                     const int32_t *__restrict__ inv, int64_t R, int k, int64_t H,
-                                                     float *__restrict__ dtw) {
+                                                     const int32_t *__restrict__ inv, const int32_t *__restrict__ n_valid,
+                                                     int64_t R, int k, int64_t H, float *__restrict__ dtw) {
   const int lane = threadIdx.x & 63;
   const int64_t f = (int64_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6);
   if (f >= R) return;
+  const int32_t pos = inv[f];
+  if (pos >= *n_valid) {
+    if (lane == 0) dtw[f] = 0.0f;
+    return;
+  }
   const uint16_t *a = dy + (f / k) * H;
-  const uint16_t *b = y + (int64_t)inv[f] * H;
+  const uint16_t *b = y + (int64_t)pos * H;
   float s = 0.0f;
   for (int64_t c = lane * 8; c < H; c += 64 * 8) {
     const uint4 va = *reinterpret_cast<const uint4 *>(a + c), vb = *reinterpret_cast<const uint4 *>(b + c);
@@ -2441,7 +2450,8 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_FWD, 0, s);
   combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(
-      w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), w.at<float>(w.L.tw), d->T, d->k, d->H, out);
+      w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off) + d->E, w.at<float>(w.L.tw), d->T, d->k,
+      d->H, out);
   mark(d, BQM_STAGE_COMBINE_FWD, 1, s);
   return launch_status("combine fwd");
 }
@@ -2471,8 +2481,8 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
   uint16_t *dxr = w.at<uint16_t>(w.L.dxr);
   if (dtopk_w) {
     mark(d, BQM_STAGE_DTOPK, 0, s);
-    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv), R, d->k,
-                                                          d->H, dtopk_w);
+    dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv),
+                                                          w.at<int32_t>(w.L.off) + d->E, R, d->k, d->H, dtopk_w);
     mark(d, BQM_STAGE_DTOPK, 1, s);
     BQM_TRY(launch_status("dtopk"));
   }
@@ -2534,8 +2544,8 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
   }
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_DGRAD, 0, s);
-  combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(dxr, w.at<int32_t>(w.L.inv), nullptr,
-                                                                                  d->T, d->k, d->H, dx);
+  combine_rows<<<(int)std::min<int64_t>(cdiv(items, NTHR), 65536), NTHR, 0, s>>>(
+      dxr, w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off) + d->E, nullptr, d->T, d->k, d->H, dx);
   mark(d, BQM_STAGE_COMBINE_DGRAD, 1, s);
   return launch_status("combine dgrad");
 }

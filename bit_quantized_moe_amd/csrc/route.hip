@@ -82,23 +82,29 @@ __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ lo
   }
 }
 
-// Pass 1: per-chunk expert histogram.
+// Expert index of a routed pair, with every index outside [0, E) sent to bucket E:
+// such a pair belongs to no expert, and the sort places it after offsets[E].
+__device__ __forceinline__ int bucket_of(int32_t e, int E) { return (uint32_t)e < (uint32_t)E ? e : E; }
+
+// Pass 1: per-chunk histogram of the E experts and the bucket of dropped pairs
+// (counts [nchunks][E + 1]).
 __global__ void __launch_bounds__(256) perm_hist(const int32_t *__restrict__ idx, int64_t R, int E,
                                                  int32_t *__restrict__ counts) {
   extern __shared__ int32_t hist[];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
   int64_t b = (int64_t)blockIdx.x * kChunk;
   for (int i = threadIdx.x; i < kChunk; i += blockDim.x) {
     int64_t f = b + i;
-    if (f < R) atomicAdd(&hist[idx[f]], 1);
+    if (f < R) atomicAdd(&hist[bucket_of(idx[f], E)], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) counts[(int64_t)blockIdx.x * E + e] = hist[e];
+  for (int e = threadIdx.x; e <= E; e += blockDim.x) counts[(int64_t)blockIdx.x * (E + 1) + e] = hist[e];
 }
 
 // Pass 2 (one block): base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e];
-// offsets = exclusive prefix of the per-expert totals.  Optionally the prefix
+// offsets = exclusive prefix of the per-expert totals; the dropped bucket E starts
+// at offsets[E].  Optionally the prefix
 // of ceil(count / bm) (row tiles per expert) for the grouped GEMMs.  The prefixes
 // over experts are a wave-level inclusive scan plus the totals of the waves before.
 __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, int nchunks, int E,
@@ -106,11 +112,12 @@ __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, 
                                                   int32_t *__restrict__ tile_off) {
   __shared__ int32_t wsum[16][2];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  const int64_t ld = E + 1;
   int32_t run = 0;
   if (e < E) {
     for (int c = 0; c < nchunks; ++c) {
-      int32_t v = counts[(int64_t)c * E + e];
-      counts[(int64_t)c * E + e] = run;
+      int32_t v = counts[c * ld + e];
+      counts[c * ld + e] = run;
       run += v;
     }
   }
@@ -136,13 +143,20 @@ __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, 
   }
   const int32_t ex = bv + v - run, ext = bu + u - tiles;  // exclusive prefixes
   if (e < E) {
-    for (int c = 0; c < nchunks; ++c) counts[(int64_t)c * E + e] += ex;
+    for (int c = 0; c < nchunks; ++c) counts[c * ld + e] += ex;
     offsets[e] = ex;
     if (tile_off) tile_off[e] = ext;
   }
   if (e == E - 1) {
     offsets[E] = ex + run;
     if (tile_off) tile_off[E] = ext + tiles;
+    // the dropped pairs follow every expert's rows, chunk by chunk
+    int32_t drun = ex + run;
+    for (int c = 0; c < nchunks; ++c) {
+      const int32_t v = counts[c * ld + E];
+      counts[c * ld + E] = drun;
+      drun += v;
+    }
   }
 }
 
@@ -166,13 +180,13 @@ __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ i
                                                    int32_t *__restrict__ inv) {
   extern __shared__ int32_t cnt[];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * E + e];
+  for (int e = lane; e <= E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * (E + 1) + e];
   __syncthreads();
   const int64_t b = (int64_t)blockIdx.x * kChunk;
   const uint64_t below = (1ull << lane) - 1ull, upto = lane == 63 ? ~0ull : (2ull << lane) - 1ull;
   for (int s = 0; s < kChunk && b + s < R; s += 64) {
     int64_t f = b + s + lane;
-    int e = f < R ? idx[f] : -1;
+    int e = f < R ? bucket_of(idx[f], E) : -1;
     const uint64_t same = lanes_equal(e + 1);  // pairs past R (e = -1) match only each other
     const int rank = __popcll(same & below);
     const bool last = (same & ~upto) == 0ull;
@@ -191,7 +205,7 @@ __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ i
 }  // namespace
 
 size_t permute_ws_bytes(int64_t R, int E) {
-  return (size_t)cdiv(R, kChunk) * (size_t)E * sizeof(int32_t);
+  return (size_t)cdiv(R, kChunk) * (size_t)(E + 1) * sizeof(int32_t);
 }
 
 bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
@@ -199,7 +213,7 @@ bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *pe
                           hipStream_t s) {
   const int nchunks = (int)cdiv(R, kChunk);
   if (R > 0) {
-    perm_hist<<<nchunks, 256, E * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws);
+    perm_hist<<<nchunks, 256, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws);
     bqm_status st = launch_status("perm_hist");
     if (st != BQM_OK) return st;
   }
@@ -207,7 +221,7 @@ bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *pe
   bqm_status st = launch_status("perm_scan");
   if (st != BQM_OK) return st;
   if (R > 0) {
-    perm_scatter<<<nchunks, 64, E * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws, perm, inv);
+    perm_scatter<<<nchunks, 64, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws, perm, inv);
     st = launch_status("perm_scatter");
   }
   return st;

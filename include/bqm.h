@@ -126,7 +126,8 @@ bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six, const fl
 bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out /* host struct */, void *stream);
 
 /* Nested (double-quantized) absmax of an NF4 stack (the nested code of bnb's
- * quant state, nf4moe page, section "Getting it to load"; the page gives no
+ * quant state, nf4moe page, section "The fix: dequant-on-forward for routed
+ * experts"; the page gives no
  * details, so this is QLoRA's published double quantization with E4M3 as the
  * 8-bit float).  Per matrix, over its absmax in row-major block order:
  *   offset = fl32(sum / nb) (sum in FP64, nb blocks), d = fl(absmax - offset),
@@ -139,9 +140,16 @@ bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out /* host struct *
  * FP64 sum is added in a fixed order, so repeated calls give identical bits. */
 bqm_status bqm_nf4_nest(const bqm_qtensor *plain, bqm_qtensor *nested, void *stream);
 
-/* Dequantize a stack to bf16 [n_mat, rows, cols]:
+/* Dequantize a stack to bf16 [n_mat, rows, cols] (the DQ of DQ(Q(W)): GLM page,
+ * section "The 4-bit base that was actually using 8-bit memory", where the one
+ * rowwise copy is dequantized to bf16 for the backward; 4-bitter page, section
+ * "Improving Gradient Stability", where the backward consumes DQ(Q(w));
+ * nf4moe page, section "The fix: dequant-on-forward for routed experts", for NF4):
  *   NVFP4: bf16_rne(fl32(e2m1(code) * e4m3(scale)) * s_dec)  (one FP32 rounding)
  *   NF4:   bf16_rne(fl32(level[code] * absmax)), absmax' when nested
+ * q: a stack as bqm_quantize_nvfp4 / bqm_quantize_nf4 / bqm_nf4_nest wrote it
+ * (read only); y: bf16 [n_mat, rows, cols], written.  Errors: a bad format, a
+ * NULL or unaligned pointer, or cols not a multiple of the block size.
  * The same values (without the s_dec factor, which the GEMMs apply to their
  * FP32 accumulators) are what the MoE GEMMs multiply. */
 bqm_status bqm_dequantize(const bqm_qtensor *q /* host struct */, uint16_t *y, void *stream);
@@ -157,10 +165,14 @@ bqm_status bqm_route(const float *logits, int64_t T, int32_t E, int32_t k, int32
                      int32_t *topk_idx, float *topk_w, void *stream);
 
 /* Stable counting sort of the R = T*k routed pairs f = t*k + j by expert (the
- * order in which the nf4moe module visits them: expert, then token, then slot).
+ * order in which the nf4moe module visits them: expert, then token, then slot;
+ * nf4moe page, section "The fix: dequant-on-forward for routed experts").
  * perm i32 [R]: perm[pos] = f.  inv i32 [R]: inv[f] = pos.  offsets i32 [E+1]:
  * exclusive prefix sum of per-expert counts.  Bit-exact, no atomics on the
- * result order.  Indices must lie in [0, E) (not checked on the device).
+ * result order.  A pair whose index lies outside [0, E) belongs to no expert:
+ * it is placed after every expert's rows (offsets[E] <= pos < R, in f order), so
+ * offsets[E] < R tells the caller that such pairs were dropped; the MoE calls
+ * treat their expert output and gradient as zero (dtopk_w 0).
  * ws: bqm_permute_workspace_size() bytes. */
 size_t bqm_permute_workspace_size(int64_t T, int32_t E, int32_t k);
 bqm_status bqm_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_t *perm,
@@ -206,7 +218,8 @@ typedef struct {
   /* 0: per-expert LoRA-A stacks A_gu [E, r, H], A_dn [E, r, I].  1: one LoRA-A
    * common to all experts, A_gu [r, H] and A_dn [r, I], with per-expert B (the
    * adapter layout of the GLM page, "Getting GLM-5.2 NVFP4 Post-Training off
-   * the ground", its serving part, row 3 of its table of issues).  Other values:
+   * the ground": its serving part, the paragraph on the non-fused NVFP4 MoE-LoRA
+   * path, which names a shared LoRA-A and per-expert LoRA-B).  Other values:
    * BQM_ERR_INVALID_ARG. */
   int32_t lora_shared_a;
   bqm_qtensor w_gu;

@@ -33,8 +33,8 @@ on the 3-D stacks, "nf4moe", section "Does it actually train?"):
 Experts that receive no token get exact zeros.
 
 Shared-A layout ("Getting GLM-5.2 NVFP4 Post-Training off the ground", its
-serving part, row 3 of its table of issues: the adapter there has one LoRA-A
-common to all experts and a LoRA-B per expert): A_gu
+serving part, the paragraph on the non-fused NVFP4 MoE-LoRA path: the adapter
+there has one LoRA-A common to all experts and a LoRA-B per expert): A_gu
 is [r, H] and A_dn [r, I], used by every expert in the formulas above, and
 dA_gu, dA_dn are the sums of those per-expert terms over all experts (the
 gradient of one matrix that every expert reads).

@@ -32,7 +32,8 @@ block is divided by its FP32 absmax (multiplied by the FP32 reciprocal) and each
 element takes the nearest codebook level, ties going to the lower level.
 
 Nested absmax (the same page names bnb's quant state as "absmax, nested code",
-section "Getting it to load"; it says nothing more, so this follows the published
+section "The fix: dequant-on-forward for routed experts"; it says nothing more,
+so this follows the published
 QLoRA double quantization): the FP32 absmax of one matrix, in row-major block
 order, has its mean subtracted (offset = the exactly rounded sum over the block
 count, in float64, rounded to FP32); each group of 256 consecutive blocks gets

@@ -14,6 +14,8 @@ datasets and checkpoints are not available, these stand in for them):
 * glm      E=256, H=6144, I=2048, k=8, T=16384, r=64  logits ~U(0,1)
 * qwen     E=128, H=2048, I=768,  k=8, T=8192,  r=64  logits ~U(0,1), W4A4
 * glm_nf4  glm with NF4 weights; logits = -1.1 ln(rank_e) + Gumbel, 16 experts masked to -inf
+* skew     logits ~U(0,1) with +1 on expert 0 for the first 23% of the tokens (one
+           expert with about twice the rows of the others; a parity-test recipe)
 * weights  ~N(0,0.02) with a Bernoulli(0.001) outlier mask multiplied by 20
   (the quantizer workload; tiny uses no outliers), LoRA A, B ~N(0,0.01),
   activations and output gradients ~N(0,1).
@@ -40,7 +42,7 @@ class Shape:
     r: int
     act_quant: bool = False
     fmt: str = "nvfp4"
-    logits: str = "uniform"      # "router" | "uniform" | "zipf"
+    logits: str = "uniform"      # "router" | "uniform" | "zipf" | "skew"
     outliers: bool = True
     seed: int = 0
     weight_seed: int = -1          # -1: same as seed
@@ -131,6 +133,10 @@ def logits(shape: Shape, x=None, router=None, device="cpu"):
             return torch.from_numpy(_rng(*key).random((T, E), dtype=np.float32))
         g = _dev_gen(device, *key)
         return torch.rand((T, E), generator=g, device=device, dtype=torch.float32)
+    if shape.logits == "skew":
+        lg = _rng(*key).random((T, E), dtype=np.float32)
+        lg[: (23 * T + 99) // 100, 0] += np.float32(1.0)
+        return torch.from_numpy(lg).to(device)
     # Zipf(1.1)-skewed: -1.1 ln(rank_e) + Gumbel(0,1); the 16 least popular masked out
     rng = _rng(*key)
     rank = rng.permutation(E) + 1

@@ -21,24 +21,7 @@ def _bqm():
 
 
 def quantize_stack_gpu(w, fmt):
-    import torch
-    bqm = _bqm()
-    E, rows, cols = w.shape
-    if fmt == "nvfp4":
-        q = bqm.alloc_qtensor(bqm.FMT_NVFP4, E, rows, cols, device=w.device)
-        wsb = bqm.bqm_quantize_nvfp4_workspace_size(E, rows, cols, bqm.SCALE_PER_TENSOR)
-        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=w.device)
-        bqm.bqm_quantize_nvfp4(w, 1, None, q, ws)
-    else:
-        q = bqm.alloc_qtensor(bqm.FMT_NF4, E, rows, cols, device=w.device)
-        bqm.bqm_quantize_nf4(w, q)
-        if fmt == "nf4_nested":
-            n = bqm.alloc_qtensor(bqm.FMT_NF4, E, rows, cols, device=w.device, nested=1)
-            n.codes = q.codes              # the nested stack keeps the plain codes
-            bqm.bqm_nf4_nest(q, n)
-            torch.cuda.synchronize()
-            return n
-    return q
+    return _bqm().quantize_stack(w, fmt)
 
 
 def poison_experts(q, experts, fmt):

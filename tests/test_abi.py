@@ -68,7 +68,8 @@ def test_workspace_sizes(lib):
     # the running amax of each matrix
     assert lib.bqm_quantize_nvfp4_workspace_size(4, 64, 256, 0) == 4 * 4
     assert lib.bqm_quantize_nvfp4_workspace_size(2, 4096, 6144, 0) == 2 * 4
-    assert lib.bqm_permute_workspace_size(16384, 256, 8) == 64 * 256 * 4
+    # per chunk of 2048 routed pairs: the E expert counts and the count of dropped pairs
+    assert lib.bqm_permute_workspace_size(16384, 256, 8) == 64 * 257 * 4
 
 
 def test_route_and_permute_reject_bad_args(lib):

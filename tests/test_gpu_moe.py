@@ -240,3 +240,115 @@ def test_full_glm_shared_lora_a_matches_replicated():
     assert_close(np_f32(sh["out"][toks]), o["out"], "out rows")
     assert_close(np_f32(sh["dx"][toks]), o["dx"], "dx rows")
     log("  shared-A full-size checks ok")
+
+
+# ----------------------------------------------------------------------------
+# experts with several full 256-row tiles, every row compared
+# ----------------------------------------------------------------------------
+def big_experts(name, **kw):
+    # R = 6000 routed rows over 8 experts; expert 0 gets the first 23% of the tokens on
+    # top of its share (about 1270 rows: five row tiles, the last one ragged), the
+    # others about 675 rows each (three row tiles)
+    base = dict(E=8, H=1024, I=512, k=2, T=3000, r=16, seed=21, logits="skew")
+    base.update(kw)
+    return synth.Shape(name, **base)
+
+
+def _check_rows_per_expert(o, E, least, most):
+    counts = np.bincount(o["idx"].reshape(-1), minlength=E)
+    log(f"  rows per expert {counts.tolist()}")
+    assert counts.min() >= least and counts.max() >= most
+
+
+def test_big_experts_nvfp4_every_row():
+    g, o = compare_full(big_experts("big"), lora_scale=0.5)
+    _check_rows_per_expert(o, 8, 600, 900)
+
+
+def test_big_experts_w4a4_every_row():
+    g, o = compare_full(big_experts("big_w4a4", act_quant=True))
+    _check_rows_per_expert(o, 8, 600, 900)
+
+
+def test_big_experts_nf4_every_row():
+    g, o = compare_full(big_experts("big_nf4", fmt="nf4"))
+    _check_rows_per_expert(o, 8, 600, 900)
+
+
+def test_lora_rank_72_and_128():
+    # r = 72: the LoRA projections' partial 64-column tile and the masked K tail of the
+    # up-projection segment; r = 128: two projection column tiles, U/V rows of 256
+    compare_full(small("r72", r=72), lora_scale=0.5)
+    compare_full(small("r128", r=128, H=320, I=192, T=260, E=12))
+    compare_full(small("r72_sh", r=72, shared_a=True, T=400))
+    compare_full(small("r128_nf4", r=128, fmt="nf4", logits="zipf", E=32, T=200), poison_empty=True)
+
+
+def test_out_of_range_expert_indices_are_dropped():
+    # caller-supplied indices outside [0, E) belong to no expert: the permutation puts
+    # those pairs after offsets[E], and they add nothing to out, dX or the LoRA
+    # gradients (their routing-weight gradient is 0).  The oracle sees the same layer
+    # with those pairs' routing weights set to 0 (any expert stands in for them).
+    import torch
+    import bit_quantized_moe_amd as bqm
+    dev = gpu()
+    shape = small("dropped", T=120, E=16, k=4, r=8)
+    inp = synth.layer_inputs(shape, device="cpu")
+    h = HostInputs(inp)
+    idx, tw = __import__("oracle.routing", fromlist=["route"]).route(h.logits, shape.k)
+    idx = idx.copy()
+    tw = tw.copy()
+    bad = [(3, 1, -1), (50, 0, 16), (50, 3, 1000), (119, 2, -7)]
+    for t, j, v in bad:
+        idx[t, j] = v
+    # oracle: the dropped pairs go to an expert the token does not use, with weight 0
+    idx_o = idx.copy()
+    for t, j, _ in bad:
+        idx_o[t, j] = next(e for e in range(shape.E) if e not in idx[t])
+        tw[t, j] = 0.0
+    w = h.weights()
+    from oracle import moe as om
+    out_o, cache = om.forward(w, h.x, idx_o, tw)
+    dx_o, dtw_o, bwd = om.dgrad(w, cache, h.dout, tw)
+    lora_o = om.lora_grad(w, cache, bwd, shape.E)
+
+    x, dout = inp.x.to(dev), inp.dout.to(dev)
+    qgu = bqm.quantize_stack(inp.w_gu.to(dev), "nvfp4")
+    qdn = bqm.quantize_stack(inp.w_dn.to(dev), "nvfp4")
+    idx_g = torch.from_numpy(idx.astype(np.int32)).to(dev)
+    tw_g = torch.from_numpy(tw.astype(np.float32)).to(dev)
+    # the permutation alone: offsets[E] counts the pairs that have an expert
+    R = shape.T * shape.k
+    perm = torch.empty(R, dtype=torch.int32, device=dev)
+    inv = torch.empty(R, dtype=torch.int32, device=dev)
+    off = torch.empty(shape.E + 1, dtype=torch.int32, device=dev)
+    pws = torch.empty(max(bqm.bqm_permute_workspace_size(shape.T, shape.E, shape.k), 16), dtype=torch.uint8,
+                      device=dev)
+    bqm.bqm_permute(idx_g, shape.T, shape.E, shape.k, perm, inv, off, pws)
+    torch.cuda.synchronize()
+    assert int(off[-1]) == R - len(bad)
+    p = perm.cpu().numpy()
+    assert sorted(p.tolist()) == list(range(R)) and (inv.cpu().numpy()[p] == np.arange(R)).all()
+    assert sorted(p[R - len(bad):].tolist()) == sorted(t * shape.k + j for t, j, _ in bad)
+
+    lor = dict(A_gu=inp.A_gu.to(dev), B_gu=inp.B_gu.to(dev), A_dn=inp.A_dn.to(dev), B_dn=inp.B_dn.to(dev))
+    d = bqm.MoEDesc(shape.T, shape.H, shape.I, shape.E, shape.k, shape.r, qgu, qdn, **lor)
+    ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+    out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty_like(out)
+    dtw = torch.empty((shape.T, shape.k), dtype=torch.float32, device=dev)
+    bqm.bqm_moe_fwd(d, x, idx_g, tw_g, out, ws)
+    bqm.bqm_moe_dgrad(d, dout, ws, dx, dtw)
+    gr = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in lora_o]
+    bqm.bqm_lora_grad(d, x, dout, ws, *gr)
+    torch.cuda.synchronize()
+    assert_close(np_f32(out), out_o, "out")
+    assert_close(np_f32(dx), dx_o, "dx")
+    keep = np.ones((shape.T, shape.k), bool)
+    for t, j, _ in bad:
+        keep[t, j] = False
+    g_dtw = dtw.cpu().numpy()
+    assert_close(g_dtw[keep], dtw_o[keep], "dtopk_w")
+    assert (g_dtw[~keep] == 0).all()
+    for name, got, ref in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), gr, lora_o):
+        assert_close(got.cpu().numpy(), ref, name)

@@ -286,3 +286,89 @@ def test_nf4_nested_layer_is_the_layer_over_its_dequantized_weights():
     assert (om.dgrad(wn, c1, dout, tw)[0] == om.dgrad(wp, c2, dout, tw)[0]).all()
     o3, _ = om.forward(w, x, idx, tw)
     assert 0 < np.linalg.norm(o1 - o3) / np.linalg.norm(o3) < 0.05
+
+
+def test_w4a4_operand_split_hand_derived():
+    """W4A4 on one token and one expert, every value derived by hand (4-bitter page,
+    section "Method": per-token NVFP4 activations feed the base GEMMs, the LoRA path
+    stays bf16; the backward keeps bf16 operands, so the quantizers pass gradients
+    through).  The pin fails if LoRA reads DQ(Q(X)) instead of X, if a is quantized
+    before its bf16 rounding, if the down LoRA reads DQ(Q(a_b)), or if the dgrad's
+    SwiGLU derivative uses the unquantized forward.
+
+    X = [4, 5, 6, 0, ..., 0] is row 1 of the GLM page's worked example padded to one
+    16-block.  Per token, amax = 6 gives s_dec = 6 / (6 * 256) = 2^-8, so the scaled
+    row is y = [1024, 1280, 1536] (t = 1536).  Scale-to-6: sb = 256, y / sb = [4, 5, 6],
+    5 ties between 4 and 6 and goes to the even code (4), error 256^2 = 65536.
+    Scale-to-4: sb = 384, y / sb = [2.67, 3.33, 4] -> [3, 3, 4], q * sb = [1152, 1152,
+    1536], error 128^2 + 128^2 = 32768 < 65536, so 4 wins: DQ(Q_row(X)) = [4.5, 4.5, 6].
+    The weights hold 0, 1 and one 6 that meets only zeros: amax 6 gives s_dec = 2^-8
+    exactly, and a block holding a single 1 scales to t = 256, where scale-to-4 (sb =
+    64, code 4: 256) is exact and beats scale-to-6 (sb = e4m3(42.7) = 44, code 6: 264),
+    so DQ = 1 exactly.  A row of a with a single nonzero v: t = fl(v * fl(1 / fl(v / 1536)))
+    lies within a few ulps of 1536, so both candidates give q * sb = 1536 (6 * 256 and
+    4 * 384; the tie keeps 6) and DQ = 1536 * fl32(v / 1536)."""
+    H = I = 16
+    x = np.zeros((1, H), np.float32)
+    x[0, :3] = [4, 5, 6]
+    wgu = np.zeros((1, 2 * I, H), np.float32)
+    wgu[0, 0, 0] = 1.0        # gate 0 reads x0
+    wgu[0, I, 2] = 1.0        # up 0 reads x2
+    wgu[0, 2 * I - 1, H - 1] = 6.0   # up 15 reads x15 = 0
+    wdn = np.zeros((1, H, I), np.float32)
+    wdn[0, 0, 0] = 1.0        # y0 reads a0
+    wdn[0, H - 1, I - 1] = 6.0       # y15 reads a15 = 0
+    A_gu = np.zeros((1, 1, H), np.float32)
+    A_gu[0, 0, 0] = 1.0       # U_gu = x0
+    B_gu = np.zeros((1, 2 * I, 1), np.float32)
+    B_gu[0, 0, 0] = 0.25      # gate 0 += 0.25 U_gu
+    A_dn = np.zeros((1, 1, I), np.float32)
+    A_dn[0, 0, 0] = 1.0       # U_dn = a0
+    B_dn = np.zeros((1, H, 1), np.float32)
+    B_dn[0, 0, 0] = 0.5       # y0 += 0.5 U_dn
+    B_dn[0, 5, 0] = 0.25      # y5 = 0.25 U_dn (LoRA only)
+    w = om.MoEWeights("nvfp4", oq.quantize_nvfp4(wgu), oq.quantize_nvfp4(wdn), A_gu, B_gu, A_dn, B_dn,
+                      act_quant=True)
+    assert (om.expert_matrix(w.gu, 0) == wgu[0]).all() and (om.expert_matrix(w.dn, 0) == wdn[0]).all()
+    assert (om.act_dq(x) == np.array([[4.5, 4.5, 6] + [0] * 13])).all()
+    idx = np.zeros((1, 1), np.int32)
+    tw = np.ones((1, 1))
+    out, cache = om.forward(w, x, idx, tw)
+
+    def silu(v):
+        return v / (1.0 + np.exp(-v))
+
+    g0 = 4.5 + 0.25 * 4.0                 # base on DQ(Q_row(X))[0], LoRA on the bf16 x0
+    u0 = 6.0                              # DQ(Q_row(X))[2]
+    a_b0 = float(torch.tensor(silu(g0) * u0, dtype=torch.float64).to(torch.bfloat16).double())
+    dq_a0 = 1536.0 * float(np.float32(a_b0) / np.float32(1536.0))
+    want = np.zeros(H)
+    want[0] = dq_a0 + 0.5 * a_b0
+    want[5] = 0.25 * a_b0
+    assert np.allclose(out[0], want, rtol=1e-14, atol=0)
+
+    # each misreading moves the result far outside that tolerance
+    g_bad = 4.5 + 0.25 * 4.5              # LoRA on DQ(Q(X))
+    a_bad = float(torch.tensor(silu(g_bad) * u0, dtype=torch.float64).to(torch.bfloat16).double())
+    unrounded = silu(g0) * u0             # a quantized before its bf16 rounding
+    dq_unrounded = 1536.0 * float(np.float32(unrounded) / np.float32(1536.0))
+    for alt in (dq_unrounded + 0.5 * unrounded, 1536.0 * float(np.float32(a_bad) / np.float32(1536.0)) + 0.5 * a_bad,
+                dq_a0 + 0.5 * dq_a0):     # the last: down LoRA on DQ(Q(a_b))
+        assert abs(alt - want[0]) > 1e-9 * abs(want[0])
+
+    # dgrad with dOut = e0 + e5: da_u0 = 1 (W_dn) + (1 * 0.5 + 1 * 0.25) * 1 (LoRA) = 1.75;
+    # SwiGLU' at the forward's g0 = 5.5 and u0 = 6; dX0 = dg (W_gu) + 0.25 dg (LoRA), dX2 = du
+    dout = np.zeros((1, H), np.float32)
+    dout[0, 0] = dout[0, 5] = 1.0
+    dX, dtw, _ = om.dgrad(w, cache, dout, tw)
+    sg = 1.0 / (1.0 + np.exp(-g0))
+    dg = float(torch.tensor(1.75 * u0 * sg * (1 + g0 * (1 - sg)), dtype=torch.float64).to(torch.bfloat16).double())
+    du = float(torch.tensor(1.75 * silu(g0), dtype=torch.float64).to(torch.bfloat16).double())
+    want_dx = np.zeros(H)
+    want_dx[0] = dg + 0.25 * dg
+    want_dx[2] = du
+    assert np.allclose(dX[0], want_dx, rtol=1e-14, atol=0)
+    assert np.isclose(dtw[0, 0], want[0] + want[5], rtol=1e-14)
+    g_st = 4.0 + 0.25 * 4.0               # SwiGLU' at the unquantized forward instead
+    sgb = 1.0 / (1.0 + np.exp(-g_st))
+    assert abs(1.75 * 4.0 * sgb * (1 + g_st * (1 - sgb)) * 1.25 - want_dx[0]) > 1e-3
