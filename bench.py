@@ -402,6 +402,76 @@ def config_block(s, res, weights):
             "stages_ms": res["stages_ms"], "stage_roofline": res["stage_roofline"]}
 
 
+def summarize_counters(root, min_us=300.0):
+    """Per-kernel table from a rocprofv3 --pmc --kernel-trace --output-format csv run under
+    root: launches, average duration, shader clock (GRBM_GUI_ACTIVE summed over the 8
+    XCDs / duration / 8), the MFMA-busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over the four
+    SIMDs of every busy CU cycle) and each counter's average per launch.  Launches
+    shorter than min_us are left out (the counters' start and stop dominate them)."""
+    import collections
+    import csv
+    import glob
+    import re
+    dur, name = {}, {}
+    for f in glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            name[r["Dispatch_Id"]] = re.sub(r"\(anonymous namespace\)::", "", r["Kernel_Name"])
+    ctr = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            ctr[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    agg = collections.defaultdict(lambda: [0, 0.0, collections.defaultdict(float)])
+    for d, t in dur.items():
+        if t < min_us * 1e3 or d not in ctr:
+            continue
+        a = agg[name[d]]
+        a[0] += 1
+        a[1] += t
+        for k, v in ctr[d].items():
+            a[2][k] += v
+    rows = []
+    for n, (c, t, cs) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        row = {"kernel": n.split("(")[0] if "bqm" in n else n[:90], "launches": c, "avg_us": round(t / c / 1e3, 1)}
+        if "GRBM_GUI_ACTIVE" in cs:
+            row["ghz"] = round(cs["GRBM_GUI_ACTIVE"] / t / 8, 3)
+        if "SQ_BUSY_CU_CYCLES" in cs and "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+            row["mfma_busy"] = round(cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * cs["SQ_BUSY_CU_CYCLES"]), 3)
+        if "SQ_LDS_BANK_CONFLICT" in cs and cs.get("SQ_LDS_IDX_ACTIVE"):
+            row["lds_bank_conflict_frac"] = round(cs["SQ_LDS_BANK_CONFLICT"] / cs["SQ_LDS_IDX_ACTIVE"], 3)
+        if cs.get("SQ_INSTS_MFMA"):
+            row["valu_per_mfma"] = round(cs["SQ_INSTS_VALU"] / cs["SQ_INSTS_MFMA"], 2) if "SQ_INSTS_VALU" in cs else None
+        for k in sorted(cs):
+            row[k] = cs[k] / c
+        rows.append(row)
+    return rows
+
+
+def library_gemm_reference(ev, sh):
+    """bf16 GEMMs of the vendor library (through torch) at the GLM gate_up shape, for
+    context beside the grouped 4-bit GEMM: one GEMM over all 131072 routed rows
+    [131072, 6144] x [6144, 4096] (one weight for all rows), and the per-expert batch
+    [256][512, 6144] x [256][6144, 4096] with bf16 weights (12.9 GB of them)."""
+    import torch
+    dev = torch.device("cuda")
+    fl = 2 * 131072 * 6144 * 4096
+    res = {}
+    a = torch.randn(256, 512, 6144, device=dev, dtype=torch.bfloat16)
+    w = torch.randn(4096, 6144, device=dev, dtype=torch.bfloat16)
+    a2 = a.view(-1, 6144)
+    ms = time_calls(ev, sh, lambda: torch.nn.functional.linear(a2, w), 5)
+    res["one_gemm_131072x6144x4096"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                        "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    del w
+    b = torch.randn(256, 6144, 4096, device=dev, dtype=torch.bfloat16)
+    ms = time_calls(ev, sh, lambda: torch.bmm(a, b), 5)
+    res["batched_256x512x6144x4096"] = {"ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 1),
+                                        "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+    del a, a2, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -414,9 +484,19 @@ def main():
                          "W4A4, format-conversion or token-sweep figures")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the layer step at smaller token counts (the token sweep)")
+    ap.add_argument("--workload", choices=["glm", "glm_nf4", "glm_nf4_nested", "qwen"],
+                    help="only the layer step of this workload (for profiling): prints its timings, no bench line")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print the per-kernel table of a rocprofv3 --pmc --kernel-trace csv run under DIR, no GPU")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="only time the vendor library's bf16 GEMMs at the GLM gate_up shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        for row in summarize_counters(args.summarize_counters):
+            print(json.dumps(row))
+        return
     if args.copy_calibration:
         import torch
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -438,6 +518,22 @@ def main():
 
     dev = torch.device("cuda")
     bqm.load()
+    if args.library_reference:
+        print(json.dumps(library_gemm_reference(HipEvents(), torch.cuda.current_stream().cuda_stream)), flush=True)
+        return
+    if args.workload:
+        ws_ = {"glm": synth.GLM, "glm_nf4": synth.GLM_NF4, "qwen": synth.QWEN,
+               "glm_nf4_nested": dataclasses.replace(synth.GLM_NF4, fmt="nf4_nested", name="glm_nf4_nested")}
+        s1 = ws_[args.workload]
+        inp1 = synth.layer_inputs(s1, device=dev)
+        wgu1 = bqm.quantize_stack(inp1.w_gu, s1.fmt)
+        wdn1 = bqm.quantize_stack(inp1.w_dn, s1.fmt)
+        inp1.w_gu = inp1.w_dn = None
+        torch.cuda.empty_cache()
+        r1 = time_layer(s1, inp1, wgu1, wdn1, HipEvents(), torch.cuda.current_stream().cuda_stream,
+                        args.steps, args.warmup)
+        print(json.dumps({"workload": s1.name, **r1}), flush=True)
+        return
     shape = synth.GLM
     s = shape
     inp = synth.layer_inputs(shape, device=dev)
@@ -608,6 +704,8 @@ def main():
         result["other_configs"] = others
         # the two-copy scheme (a columnwise second quantization for the dgrad) as a comparison
         result["columnwise_dgrad_comparison"] = colwise_comparison(s, inp, wgu, wdn, ev, sh)
+        # the vendor library's bf16 GEMMs at the gate_up shape, for context
+        result["library_bf16_gemm_reference"] = library_gemm_reference(ev, sh)
         # decode-shaped forward over the GLM experts (serving side: weight-read-bound)
         result["decode_forward"] = {"workload": "glm5.2 shape, forward only (route + moe_fwd), nvfp4 weights, "
                                                 "LoRA r=64", "rows": decode_sweep(shape, wgu, wdn, ev, sh),
