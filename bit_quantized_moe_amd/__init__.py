@@ -8,7 +8,8 @@ from ._lib import (BQMError, FMT_NF4, FMT_NVFP4, MoEDesc, QTensor, SCALE_PER_ROW
                    SCALE_PER_TENSOR, alloc_qtensor, bqm_abi_version, bqm_dequantize,
                    bqm_last_error, bqm_lora_grad, bqm_moe_dgrad, bqm_moe_dgrad_colwise, bqm_moe_fwd,
                    bqm_moe_workspace_size, bqm_permute, bqm_permute_workspace_size,
-                   bqm_nf4_nest, bqm_quantize_nf4, bqm_quantize_nvfp4, bqm_quantize_nvfp4_workspace_size,
+                   bqm_nf4_nest, bqm_quantize_nf4, bqm_quantize_nvfp4, bqm_quantize_nvfp4_noalloc,
+                   bqm_quantize_nvfp4_workspace_size,
                    bqm_route, load, nf4_nest_groups, quantize_stack)
 
 __all__ = [n for n in dir() if n.startswith("bqm_")] + [

@@ -29,7 +29,7 @@ STATUS = {0: "BQM_OK", -1: "BQM_ERR_INVALID_ARG", -2: "BQM_ERR_SHAPE", -3: "BQM_
           -4: "BQM_ERR_UNSUPPORTED", -5: "BQM_ERR_WORKSPACE", -6: "BQM_ERR_HIP"}
 
 EXPORTS = ["bqm_abi_version", "bqm_last_error", "bqm_quantize_nvfp4_workspace_size",
-           "bqm_quantize_nvfp4", "bqm_quantize_nf4", "bqm_dequantize", "bqm_route",
+           "bqm_quantize_nvfp4", "bqm_quantize_nvfp4_noalloc", "bqm_quantize_nf4", "bqm_dequantize", "bqm_route",
            "bqm_permute_workspace_size", "bqm_permute", "bqm_moe_workspace_size", "bqm_moe_fwd",
            "bqm_moe_dgrad", "bqm_moe_dgrad_colwise", "bqm_lora_grad", "bqm_nf4_nest"]
 
@@ -75,6 +75,7 @@ def load(path: str = LIB_PATH):
         "bqm_last_error": (C.c_char_p, []),
         "bqm_quantize_nvfp4_workspace_size": (sz, [i64, i64, i64, i32]),
         "bqm_quantize_nvfp4": (C.c_int, [vp, i32, vp, C.POINTER(QTensorC), vp, sz, vp]),
+        "bqm_quantize_nvfp4_noalloc": (C.c_int, [vp, i32, vp, C.POINTER(QTensorC), vp]),
         "bqm_quantize_nf4": (C.c_int, [vp, C.POINTER(QTensorC), vp]),
         "bqm_nf4_nest": (C.c_int, [C.POINTER(QTensorC), C.POINTER(QTensorC), vp]),
         "bqm_dequantize": (C.c_int, [C.POINTER(QTensorC), vp, vp]),
@@ -201,6 +202,15 @@ def bqm_quantize_nvfp4(x, four_over_six: int, s_dec_in, out: QTensor, ws=None, s
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.bqm_quantize_nvfp4(_ptr(x), int(four_over_six), _ptr(s_dec_in), C.byref(qc), _ptr(ws),
                                   wsb, _stream(stream)))
+    out.four_over_six = qc.four_over_six
+    return out
+
+
+def bqm_quantize_nvfp4_noalloc(x, four_over_six: int, s_dec_in, out: QTensor, stream=None):
+    lib = load()
+    qc = out.c()
+    _check(lib.bqm_quantize_nvfp4_noalloc(_ptr(x), int(four_over_six), _ptr(s_dec_in), C.byref(qc),
+                                          _stream(stream)))
     out.four_over_six = qc.four_over_six
     return out
 

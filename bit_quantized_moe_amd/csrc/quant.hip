@@ -23,6 +23,7 @@
 #include "nf4_levels.inc"
 
 #include <algorithm>
+#include <mutex>
 
 namespace bqm {
 namespace {
@@ -646,25 +647,50 @@ extern "C" size_t bqm_quantize_nvfp4_workspace_size(int64_t n_mat, int64_t rows,
   return (size_t)n_mat * sizeof(uint32_t);
 }
 
-extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six,
-                                         const float *s_dec_in, bqm_qtensor *out, void *ws,
-                                         size_t ws_bytes, void *stream) {
-  bqm_status st = check_qtensor(out, "bqm_quantize_nvfp4", true);
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the running amax of each matrix lives in a file-scope
+// device array (one copy per GPU, kept until the process ends) instead of a caller
+// workspace.  Host code never passes the array's name to a kernel (in host code it
+// is only a stand-in for the symbol): the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress and kept.
+static constexpr int64_t kScratchMats = 65536;  // matrices per call: 256 KiB per GPU
+static __device__ __align__(256) uint32_t scratch[kScratchMats];
+
+namespace bqm {
+namespace {
+
+// Checks of the quantizer arguments shared by both entry points (host only, nothing
+// launched).  Returns the number of matrices whose running amax the call needs
+// (0: per-row mode or caller scales).
+bqm_status check_quantize_nvfp4(const uint16_t *x, int32_t four_over_six, const float *s_dec_in,
+                                const bqm_qtensor *out, const char *who, int64_t &amax_slots) {
+  amax_slots = 0;
+  bqm_status st = check_qtensor(out, who, true);
   if (st != BQM_OK) return st;
-  BQM_REQUIRE(out->fmt == BQM_FMT_NVFP4, BQM_ERR_INVALID_ARG,
-              "bqm_quantize_nvfp4: out->fmt must be BQM_FMT_NVFP4");
+  BQM_REQUIRE(out->fmt == BQM_FMT_NVFP4, BQM_ERR_INVALID_ARG, "%s: out->fmt must be BQM_FMT_NVFP4", who);
+  const int64_t n_mat = out->n_mat, per_mat = out->rows * out->cols;
+  if (n_mat * per_mat == 0) return BQM_OK;
+  BQM_REQUIRE(x, BQM_ERR_INVALID_ARG, "%s: x is NULL", who);
+  BQM_REQUIRE(aligned16(x), BQM_ERR_ALIGN, "%s: x not 16-byte aligned", who);
+  BQM_REQUIRE(!s_dec_in || aligned16(s_dec_in), BQM_ERR_ALIGN, "%s: s_dec_in not 16-byte aligned", who);
+  BQM_REQUIRE(four_over_six >= kFosOff && four_over_six <= kFosStrict, BQM_ERR_INVALID_ARG,
+              "%s: four_over_six must be 0, 1 or 2", who);
+  if (out->scale_mode == BQM_SCALE_PER_TENSOR) {
+    const int64_t P = cdiv(per_mat / 8, kAmaxVec), G = cdiv(per_mat / 16, kQuantBlocks);
+    BQM_REQUIRE(n_mat * std::max(P, G) < ((int64_t)1 << 31), BQM_ERR_SHAPE, "%s: tensor too large", who);
+    if (!s_dec_in) amax_slots = n_mat;
+  }
+  return BQM_OK;
+}
+
+// The launches of a checked call.  amax: n_mat running-amax slots when amax_slots > 0.
+bqm_status quantize_nvfp4_launch(const uint16_t *x, int32_t four_over_six, const float *s_dec_in, bqm_qtensor *out,
+                                 uint32_t *amax, hipStream_t s) {
   const int64_t n_mat = out->n_mat, rows = out->rows, cols = out->cols;
   const int64_t per_mat = rows * cols;
-  if (n_mat * per_mat == 0) return BQM_OK;
-  BQM_REQUIRE(x, BQM_ERR_INVALID_ARG, "bqm_quantize_nvfp4: x is NULL");
-  BQM_REQUIRE(aligned16(x), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: x not 16-byte aligned");
-  BQM_REQUIRE(!s_dec_in || aligned16(s_dec_in), BQM_ERR_ALIGN,
-              "bqm_quantize_nvfp4: s_dec_in not 16-byte aligned");
-  BQM_REQUIRE(four_over_six >= kFosOff && four_over_six <= kFosStrict, BQM_ERR_INVALID_ARG,
-              "bqm_quantize_nvfp4: four_over_six must be 0, 1 or 2");
   out->four_over_six = four_over_six;
+  if (n_mat * per_mat == 0) return BQM_OK;
   const float denom = four_over_six ? 6.0f * 256.0f : 6.0f * 448.0f;
-  hipStream_t s = as_stream(stream);
   const uint4 *xv = reinterpret_cast<const uint4 *>(x);
   uint2 *cv = reinterpret_cast<uint2 *>(out->codes);
   uint8_t *sv = reinterpret_cast<uint8_t *>(out->scales);
@@ -685,14 +711,9 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
   }
   const int64_t blocks_per_mat = per_mat / 16;
   const int64_t P = cdiv(per_mat / 8, kAmaxVec), G = cdiv(blocks_per_mat, kQuantBlocks);
-  BQM_REQUIRE(n_mat * std::max(P, G) < ((int64_t)1 << 31), BQM_ERR_SHAPE, "bqm_quantize_nvfp4: tensor too large");
-  uint32_t *amax = nullptr;
+  bqm_status st = BQM_OK;
   if (!s_dec_in) {
-    const size_t need = bqm_quantize_nvfp4_workspace_size(n_mat, rows, cols, 0);
-    BQM_REQUIRE(ws && ws_bytes >= need, BQM_ERR_WORKSPACE,
-                "bqm_quantize_nvfp4: workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    BQM_REQUIRE(aligned16(ws), BQM_ERR_ALIGN, "bqm_quantize_nvfp4: ws not 16-byte aligned");
-    amax = reinterpret_cast<uint32_t *>(ws);
+    // a fill kernel, not a memset, so that the call can be captured in a graph
     clear_u32<<<(int)std::min<int64_t>(cdiv(n_mat, kThreads), 1024), kThreads, 0, s>>>(amax, n_mat);
     st = launch_status("clear_u32");
     if (st != BQM_OK) return st;
@@ -710,6 +731,77 @@ extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_si
     nvfp4_quant_tensor<kFosOff><<<(int)(n_mat * G), kThreads, 0, s>>>(xv, blocks_per_mat, G, amax, s_dec_in, denom,
                                                                       cv, sv, out->s_dec);
   return launch_status("nvfp4_quant_tensor");
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this GPU's `scratch` (the current device, which must be the
+// stream's device).
+bqm_status scratch_for(hipStream_t s, const char *who, uint32_t **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BQM_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (s) {
+    int sdev = -1;
+    e = hipStreamGetDevice(s, &sdev);
+    if (e != hipSuccess) return fail(BQM_ERR_HIP, "%s: hipStreamGetDevice: %s", who, hipGetErrorString(e));
+    BQM_REQUIRE(sdev == dev, BQM_ERR_INVALID_ARG, "%s: the stream belongs to device %d, device %d is current", who,
+                sdev, dev);
+  }
+  BQM_REQUIRE(dev >= 0 && dev < kMaxDevices, BQM_ERR_UNSUPPORTED, "%s: device index %d (at most %d devices)", who,
+              dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(BQM_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_ptr[dev] = reinterpret_cast<uint32_t *>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BQM_OK;
+}
+
+}  // namespace
+}  // namespace bqm
+
+extern "C" bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six,
+                                         const float *s_dec_in, bqm_qtensor *out, void *ws,
+                                         size_t ws_bytes, void *stream) {
+  const char *who = "bqm_quantize_nvfp4";
+  int64_t slots = 0;
+  bqm_status st = check_quantize_nvfp4(x, four_over_six, s_dec_in, out, who, slots);
+  if (st != BQM_OK) return st;
+  uint32_t *amax = nullptr;
+  if (slots > 0) {
+    const size_t need = bqm_quantize_nvfp4_workspace_size(out->n_mat, out->rows, out->cols, 0);
+    BQM_REQUIRE(ws && ws_bytes >= need, BQM_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, need,
+                ws_bytes);
+    BQM_REQUIRE(aligned16(ws), BQM_ERR_ALIGN, "%s: ws not 16-byte aligned", who);
+    amax = reinterpret_cast<uint32_t *>(ws);
+  }
+  return quantize_nvfp4_launch(x, four_over_six, s_dec_in, out, amax, as_stream(stream));
+}
+
+extern "C" bqm_status bqm_quantize_nvfp4_noalloc(const uint16_t *x, int32_t four_over_six, const float *s_dec_in,
+                                                 bqm_qtensor *out, void *stream) {
+  const char *who = "bqm_quantize_nvfp4_noalloc";
+  int64_t slots = 0;
+  bqm_status st = check_quantize_nvfp4(x, four_over_six, s_dec_in, out, who, slots);
+  if (st != BQM_OK) return st;
+  BQM_REQUIRE(slots <= kScratchMats, BQM_ERR_WORKSPACE,
+              "%s: %lld matrices need a running amax each; the static scratch holds %lld (pass s_dec_in, or use "
+              "bqm_quantize_nvfp4 with a workspace)",
+              who, (long long)slots, (long long)kScratchMats);
+  hipStream_t s = as_stream(stream);
+  uint32_t *amax = nullptr;
+  if (slots > 0) {
+    st = scratch_for(s, who, &amax);
+    if (st != BQM_OK) return st;
+  }
+  return quantize_nvfp4_launch(x, four_over_six, s_dec_in, out, amax, s);
 }
 
 extern "C" bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out, void *stream) {

@@ -118,6 +118,20 @@ bqm_status bqm_quantize_nvfp4(const uint16_t *x, int32_t four_over_six, const fl
                               bqm_qtensor *out /* host struct */, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* The same quantization for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): it takes no
+ * workspace and allocates nothing.  Per-tensor mode without s_dec_in keeps the
+ * running amax of each matrix in a static device array of the library (65536
+ * matrices, 256 KiB per GPU, held until the process ends); a call with more
+ * matrices returns BQM_ERR_WORKSPACE before anything is launched.  The array is
+ * cleared by a kernel at the start of every call that uses it.  Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.  The
+ * stream must belong to the current device.  Results are bit-identical to
+ * bqm_quantize_nvfp4's. */
+bqm_status bqm_quantize_nvfp4_noalloc(const uint16_t *x, int32_t four_over_six, const float *s_dec_in,
+                                      bqm_qtensor *out /* host struct */, void *stream);
+
 /* NF4 quantization, blocksize 64 along cols, FP32 absmax per block: each
  * element is multiplied by the FP32 reciprocal of its block's absmax and takes
  * the nearest of the 16 NormalFloat levels, ties going to the lower level.

@@ -131,3 +131,12 @@ def test_nf4_nest_rejects_bad_arguments(lib):
     assert lib.bqm_quantize_nvfp4(16, 1, None, C.byref(q(fmt=1, cols=64, nested=1)), 16, 64, None) == -1
     # empty stacks are no-ops
     assert lib.bqm_nf4_nest(C.byref(q(n=0)), C.byref(q(n=0, nested=1)), None) == 0
+
+
+def test_noalloc_quantizer_rejects_more_matrices_than_its_scratch(lib):
+    # 65537 matrices would need 65537 running-amax slots: refused before any launch
+    q = _q(n=65537, rows=1, cols=16)
+    st = lib.bqm_quantize_nvfp4_noalloc(16, 1, None, C.byref(q), None)
+    assert st == -5 and "65536" in bqm.bqm_last_error()
+    q = _q(cols=24)
+    assert lib.bqm_quantize_nvfp4_noalloc(16, 1, None, C.byref(q), None) == -2
