@@ -223,6 +223,42 @@ __device__ __forceinline__ void nf4_absmax_load(const Seg &s, int e, int64_t blk
   w[4] = __float_as_uint(prod + sdm[0]);
 }
 
+// Nested NF4: absmax' of every block of a stack, fl(fl(e4m3(q) * s2[group]) + offset)
+// in FP32 (the same two roundings as nf4_absmax_load), written to a workspace buffer so
+// that the GEMMs read it as plain FP32 absmax.  Matrix blockIdx.y, nb blocks per
+// matrix, G groups of 256 blocks per matrix; four blocks per thread when nb % 4 == 0.
+template <bool VEC4>
+__global__ void __launch_bounds__(256) nf4_unnest(const uint8_t *__restrict__ q, const float *__restrict__ sd,
+                                                  int64_t nb, int64_t G, float *__restrict__ out) {
+#pragma clang fp contract(off)
+  const int64_t m = blockIdx.y;
+  const float *sdm = sd + m * (1 + G);
+  const float off = sdm[0];
+  const uint8_t *qm = q + m * nb;
+  float *om = out + m * nb;
+  if constexpr (VEC4) {
+    for (int64_t b = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; b < nb; b += (int64_t)gridDim.x * 1024) {
+      const uint32_t c = *reinterpret_cast<const uint32_t *>(qm + b);
+      const float s2 = sdm[1 + (b >> 8)];  // the four blocks share a group (256 % 4 == 0)
+      float4 v;
+      v.x = __builtin_amdgcn_cvt_f32_fp8(c, 0) * s2;
+      v.y = __builtin_amdgcn_cvt_f32_fp8(c, 1) * s2;
+      v.z = __builtin_amdgcn_cvt_f32_fp8(c, 2) * s2;
+      v.w = __builtin_amdgcn_cvt_f32_fp8(c, 3) * s2;
+      v.x = v.x + off;
+      v.y = v.y + off;
+      v.z = v.z + off;
+      v.w = v.w + off;
+      *reinterpret_cast<float4 *>(om + b) = v;
+    }
+  } else {
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nb; b += (int64_t)gridDim.x * 256) {
+      const float prod = __builtin_amdgcn_cvt_f32_fp8(qm[b], 0) * sdm[1 + (b >> 8)];
+      om[b] = prod + off;
+    }
+  }
+}
+
 template <class C, int BSRC, int EPI>
 __device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I, int k0, BRegs &r) {
   constexpr int BN = C::BN;
@@ -912,11 +948,81 @@ __device__ __forceinline__ void a_frags(const uint16_t *As, int kk, int row0, in
     af[tm] = *reinterpret_cast<const bf16x8 *>(As + a_off(row0 + tm * 32 + (lane & 31), 4 * (lane >> 5) + kk));
 }
 
+// Weight formats of the register-decode kernels
+enum WFmt { WF_NVFP4 = 0, WF_NF4 = 1 };
+
 // this lane's codes (4 slices) and the two block scales of its weight columns
+// (NVFP4), or the decode table of each column's 64-block (NF4: the low and high
+// bytes of the 16 bf16 values bf16(level[c] * absmax), four entries per register)
 struct BCodes {
   u32x4 c[TN];
   float s[TN][2];
+  uint32_t lo[TN][4], hi[TN][4];
 };
+
+// ---- NF4 in registers ----
+// A 64-block of one weight column shares one FP32 absmax a, so its 16 possible
+// operands T[c] = bf16(fl(level[c] * a)) (the dequantized value, rounded to nearest
+// even) are computed once per column and K step, and every code is a table lookup
+// done with byte permutes: the 16 entries' low bytes sit in four registers, their
+// high bytes in four more, and v_perm picks four bytes at a time by code.
+constexpr float kNF4Levels[16] = BQM_NF4_LEVELS;
+
+__device__ __forceinline__ void nf4_table(float a, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+  uint32_t pr[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pr[j] = pack_bf16_rne(kNF4Levels[2 * j] * a, kNF4Levels[2 * j + 1] * a);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = __builtin_amdgcn_perm(pr[2 * i + 1], pr[2 * i], 0x06040200u);
+    hi[i] = __builtin_amdgcn_perm(pr[2 * i + 1], pr[2 * i], 0x07050301u);
+  }
+}
+
+// byte i of the result = plane byte x_i, for x_i = 0..15 in byte i of the code word:
+// s = x & 7 picks within entries 0-7 and 8-15, sel = i + 4 * bit3(x_i) chooses between them
+__device__ __forceinline__ uint32_t nf4_lut(const uint32_t (&t)[4], uint32_t s, uint32_t sel) {
+  const uint32_t a = __builtin_amdgcn_perm(t[1], t[0], s);
+  const uint32_t b = __builtin_amdgcn_perm(t[3], t[2], s);
+  return __builtin_amdgcn_perm(b, a, sel);
+}
+
+// the 8 codes of one slice (element 2j in the low nibble of byte j) -> 4 bf16 pairs, in
+// four parts so that the work can sit between MFMAs: part 0 and 1 look up the even
+// and odd elements' bytes, parts 2 and 3 interleave them into pairs (e0,e1) .. (e6,e7)
+struct NF4Tmp {
+  uint32_t so, xo, le, he, lo, ho;
+};
+
+template <int PART>
+__device__ __forceinline__ void nf4_part(uint32_t c, const uint32_t (&lo)[4], const uint32_t (&hi)[4], NF4Tmp &t,
+                                         u32x4 &out) {
+  if constexpr (PART == 0) {
+    // even elements: the low nibbles (bits 0-2 pick within a half, bit 3 the half)
+    const uint32_t se = c & 0x07070707u, xe = ((c >> 1) & 0x04040404u) | 0x03020100u;
+    t.so = (c >> 4) & 0x07070707u;
+    t.xo = ((c >> 5) & 0x04040404u) | 0x03020100u;
+    t.le = nf4_lut(lo, se, xe);
+    t.he = nf4_lut(hi, se, xe);
+  } else if constexpr (PART == 1) {
+    t.lo = nf4_lut(lo, t.so, t.xo);
+    t.ho = nf4_lut(hi, t.so, t.xo);
+  } else if constexpr (PART == 2) {
+    const uint32_t e01 = __builtin_amdgcn_perm(t.he, t.le, 0x05010400u), o01 = __builtin_amdgcn_perm(t.ho, t.lo, 0x05010400u);
+    out[0] = __builtin_amdgcn_perm(o01, e01, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(o01, e01, 0x07060302u);
+  } else {
+    const uint32_t e23 = __builtin_amdgcn_perm(t.he, t.le, 0x07030602u), o23 = __builtin_amdgcn_perm(t.ho, t.lo, 0x07030602u);
+    out[2] = __builtin_amdgcn_perm(o23, e23, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(o23, e23, 0x07060302u);
+  }
+}
+
+template <int PART>
+__device__ __forceinline__ void nf4_step(const BCodes &b, int tn, int kk, NF4Tmp &t, u32x4 &out) {
+  nf4_part<PART>(b.c[tn][kk], b.lo[tn], b.hi[tn], t, out);
+}
+
 
 template <int VT>
 __device__ __forceinline__ void mfmas(const bf16x8 (&af)[TM], const bf16x8 (&bf)[TN], int vt,
@@ -1027,6 +1133,12 @@ __device__ __forceinline__ void b_cook(const BRaw &r, int lane, BCodes &b) {
   }
 }
 
+// NF4: the scale word of a column is its FP32 absmax for the K step (one 64-block)
+__device__ __forceinline__ void b_cook_nf4(const BRaw &r, int tn, BCodes &b) {
+  b.c[tn] = r.c[tn];
+  nf4_table(__uint_as_float(r.sw[tn]), b.lo[tn], b.hi[tn]);
+}
+
 // bf16 pair p (0..3) of column tile tn's fragment of slice kk
 __device__ __forceinline__ uint32_t dec_pair(const BCodes &b, int tn, int kk, int p) {
   const uint32_t c = b.c[tn][kk];
@@ -1051,11 +1163,12 @@ __device__ __forceinline__ void mfma1(const bf16x8 &a, const u32x4 &b, f32x16 &a
 // One K step.  On entry af[0] / bf[0] hold slice 0 of stage `cur` and bc its codes.
 // DMA: issue the copies of the step at k2 into stage n2.  NEXT: a following step
 // exists (stage nx), whose slice 0 is loaded into af[0] / bf[0] at the end.
-template <int VT, bool DMA, bool NEXT>
+template <int VT, bool DMA, bool NEXT, int WF>
 __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrc &d, int wn, int row0,
                                         int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], BCodes &bc,
                                         f32x16 (&acc)[TM][TN]) {
   const uint16_t *As = sm.a[cur];
+  NF4Tmp nt;
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
     const int c = kk & 1, n = c ^ 1;
@@ -1066,7 +1179,15 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
       if (DMA && dma_slot<VT>(kk, tm) >= 0) dma_one<VT>(d, dma_slot<VT>(kk, tm), k2, sm, n2);
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
-      bf[n][tm >> 2][tm & 3] = dec_pair(bc, tm >> 2, kk + 1, tm & 3);
+      if constexpr (WF == WF_NVFP4) {
+        bf[n][tm >> 2][tm & 3] = dec_pair(bc, tm >> 2, kk + 1, tm & 3);
+      } else {
+        // the four parts of column tile tm / 4's slice kk+1
+        if ((tm & 3) == 0) nf4_step<0>(bc, tm >> 2, kk + 1, nt, bf[n][tm >> 2]);
+        if ((tm & 3) == 1) nf4_step<1>(bc, tm >> 2, kk + 1, nt, bf[n][tm >> 2]);
+        if ((tm & 3) == 2) nf4_step<2>(bc, tm >> 2, kk + 1, nt, bf[n][tm >> 2]);
+        if ((tm & 3) == 3) nf4_step<3>(bc, tm >> 2, kk + 1, nt, bf[n][tm >> 2]);
+      }
       FQ_PIN();
     }
   }
@@ -1096,17 +1217,37 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
       b_raw(sm.b[nx], sm.s[nx], wn, lane, raw);
     }
     if (DMA && dma_slot<VT>(3, tm) >= 0) dma_one<VT>(d, dma_slot<VT>(3, tm), k2, sm, n2);
-    if (NEXT && tm == 3) b_cook(raw, lane, bc);
-    if (NEXT && tm >= 4) {
-      const int q = 2 * (tm - 4);  // pairs q, q+1 of slice 0
-      bf[0][q >> 2][q & 3] = dec_pair(bc, q >> 2, 0, q & 3);
-      bf[0][(q + 1) >> 2][(q + 1) & 3] = dec_pair(bc, (q + 1) >> 2, 0, (q + 1) & 3);
+    if constexpr (WF == WF_NVFP4) {
+      if (NEXT && tm == 3) b_cook(raw, lane, bc);
+      if (NEXT && tm >= 4) {
+        const int q = 2 * (tm - 4);  // pairs q, q+1 of slice 0
+        bf[0][q >> 2][q & 3] = dec_pair(bc, q >> 2, 0, q & 3);
+        bf[0][(q + 1) >> 2][(q + 1) & 3] = dec_pair(bc, (q + 1) >> 2, 0, (q + 1) & 3);
+      }
+    } else {
+      // tables of column tiles 0 and 1, then the four parts of each one's slice 0
+      if (NEXT && tm == 3) b_cook_nf4(raw, 0, bc);
+      if (NEXT && tm == 4) nf4_step<0>(bc, 0, 0, nt, bf[0][0]);
+      if (NEXT && tm == 5) {
+        b_cook_nf4(raw, 1, bc);
+        nf4_step<1>(bc, 0, 0, nt, bf[0][0]);
+      }
+      if (NEXT && tm == 6) {
+        nf4_step<2>(bc, 0, 0, nt, bf[0][0]);
+        nf4_step<3>(bc, 0, 0, nt, bf[0][0]);
+        nf4_step<0>(bc, 1, 0, nt, bf[0][1]);
+      }
+      if (NEXT && tm == 7) {
+        nf4_step<1>(bc, 1, 0, nt, bf[0][1]);
+        nf4_step<2>(bc, 1, 0, nt, bf[0][1]);
+        nf4_step<3>(bc, 1, 0, nt, bf[0][1]);
+      }
     }
     FQ_PIN();
   }
 }
 
-template <int EPI, int VT>
+template <int EPI, int VT, int WF>
 __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
                                               Smem &sm, f32x16 (&acc)[TM][TN]) {
   constexpr int NDMA = VT + 3;
@@ -1133,23 +1274,35 @@ __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N
     b_raw(sm.b[0], sm.s[0], wn, lane, raw);
 #pragma unroll
     for (int tm = 0; tm < VT; ++tm) af[0][tm] = a_frag(sm.a[0], 0, row0 + 32 * tm, lane);
-    b_cook(raw, lane, bc);
+    if constexpr (WF == WF_NVFP4) {
+      b_cook(raw, lane, bc);
 #pragma unroll
-    for (int q = 0; q < 4 * TN; ++q) bf[0][q >> 2][q & 3] = dec_pair(bc, q >> 2, 0, q & 3);
+      for (int q = 0; q < 4 * TN; ++q) bf[0][q >> 2][q & 3] = dec_pair(bc, q >> 2, 0, q & 3);
+    } else {
+      NF4Tmp t;
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn) {
+        b_cook_nf4(raw, tn, bc);
+        nf4_step<0>(bc, tn, 0, t, bf[0][tn]);
+        nf4_step<1>(bc, tn, 0, t, bf[0][tn]);
+        nf4_step<2>(bc, tn, 0, t, bf[0][tn]);
+        nf4_step<3>(bc, tn, 0, t, bf[0][tn]);
+      }
+    }
   }
   int cur = 0, ks = 0;
   for (; ks + 2 < nk; ++ks) {
     const int nx = cur == NST - 1 ? 0 : cur + 1;
     const int n2 = nx == NST - 1 ? 0 : nx + 1;
-    step_q4<VT, true, true>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, bc, acc);
+    step_q4<VT, true, true, WF>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, bc, acc);
     cur = nx;
   }
   if (ks + 1 < nk) {
     const int nx = cur == NST - 1 ? 0 : cur + 1;
-    step_q4<VT, false, true>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
+    step_q4<VT, false, true, WF>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
     cur = nx;
   }
-  step_q4<VT, false, false>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
+  step_q4<VT, false, false, WF>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
   __syncthreads();  // the stages are reused by the next segment
 }
 #undef FQ_PIN
@@ -1553,8 +1706,9 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
 
 // LORN: the LoRA term takes an N-major B ([K = r rows][N cols], the dgrad's A_gu / A_dn)
 // through seg_lora_n; used when a dgrad runs on this K-major kernel over a columnwise copy
-template <int ASRC, int EPI, bool LORN = false>
+template <int ASRC, int EPI, bool LORN = false, int WF = WF_NVFP4>
 __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
+  static_assert(WF == WF_NVFP4 || (ASRC == A_GATHER || ASRC == A_ROWS), "NF4 weights take bf16 activations");
   __shared__ __attribute__((aligned(16))) Smem sm;
   // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
   const int total = p.tile_off[p.E] * p.NT;
@@ -1596,22 +1750,22 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   const int vtu = __builtin_amdgcn_readfirstlane(vt);  // every wave starts at row 0: vt is the tile's
   if (vtu > 6) {
     dma_rows<ASRC, 8>(p, rb, n_e, m0, arow);
-    seg_q4_direct<EPI, 8>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    seg_q4_direct<EPI, 8, WF>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
   } else if (vtu > 4) {
     dma_rows<ASRC, 6>(p, rb, n_e, m0, arow);
-    seg_q4_direct<EPI, 6>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    seg_q4_direct<EPI, 6, WF>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
   } else if (vtu > 2) {
     dma_rows<ASRC, 4>(p, rb, n_e, m0, arow);
-    seg_q4_direct<EPI, 4>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    seg_q4_direct<EPI, 4, WF>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
   } else {
     dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
-    seg_q4_direct<EPI, 2>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+    seg_q4_direct<EPI, 2, WF>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
   }
 
   // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
   // per row and expert (NVFP4 activations, val * sb rows) before the LoRA segment
-  float esc = 1.0f;
-  if constexpr (!kQA) esc = uniform_load(p.s1.b_sd + e);
+  float esc = 1.0f;  // NF4: the table values are the dequantized weights themselves
+  if constexpr (!kQA && WF == WF_NVFP4) esc = uniform_load(p.s1.b_sd + e);
   if constexpr (kQA) {
     const float sb = p.s1.b_sd[e];
 #pragma unroll
@@ -2074,7 +2228,7 @@ __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t perm, inv, off, tile_off, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
-      vgu, dxr, part;
+      vgu, dxr, part, absx;
   size_t total;
 };
 
@@ -2117,6 +2271,9 @@ Layout layout(const bqm_moe_desc *d) {
   L.dxr = take(R * H * 2);
   // shared-A gradient: lora_split(R) partial sums of [r, max(H, I)] in FP32
   L.part = take(d->lora_shared_a && r > 0 ? (size_t)lora_split((int)E) * r * (H > I ? H : I) * 4 : 0);
+  // nested NF4: FP32 absmax' of the larger stack (gate_up), rebuilt before each forward GEMM
+  const bool nested = d->w_gu.fmt == BQM_FMT_NF4 && (d->w_gu.nested || d->w_dn.nested);
+  L.absx = take(nested ? E * 2 * I * H / 64 * 4 : 0);
   L.total = o;
   return L;
 }
@@ -2255,11 +2412,11 @@ bool lora_folds_s_dec(const bqm_moe_desc *d, bool forward) {
 }
 
 // forward GEMM over NVFP4 weights: codes staged in LDS, decoded in registers
-template <int ASRC, int EPI, bool LORN = false>
+template <int ASRC, int EPI, bool LORN = false, int WF = fq::WF_NVFP4>
 bqm_status launch_fq(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
   static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
   const int grid = gemm_grid(R, p.E, p.NT);
-  fq::gemm_fwd_q4<ASRC, EPI, LORN><<<grid, fq::NTHR, 0, s>>>(p);
+  fq::gemm_fwd_q4<ASRC, EPI, LORN, WF><<<grid, fq::NTHR, 0, s>>>(p);
   return launch_status(what);
 }
 
@@ -2337,6 +2494,24 @@ bqm_status quantize_rows(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_
   return nvfp4_expand(codes, scales, n_rows * cols, expanded, s);
 }
 
+// The forward GEMMs read NF4 absmax as FP32: a nested stack's absmax' is expanded into
+// the workspace first and the segment points at it.
+bqm_status nf4_fp32_absmax(const bqm_qtensor &q, const Ws &w, Seg &seg, hipStream_t s) {
+  if (q.fmt != BQM_FMT_NF4 || !q.nested) return BQM_OK;
+  const int64_t nb = q.rows * q.cols / 64, G = cdiv(nb, 256);
+  float *out = w.at<float>(w.L.absx);
+  const uint8_t *qs = reinterpret_cast<const uint8_t *>(q.scales);
+  if (nb % 4 == 0)
+    nf4_unnest<true><<<dim3((unsigned)std::min<int64_t>(cdiv(nb, 1024), 256), (unsigned)q.n_mat), 256, 0, s>>>(
+        qs, q.s_dec, nb, G, out);
+  else
+    nf4_unnest<false><<<dim3((unsigned)std::min<int64_t>(cdiv(nb, 256), 256), (unsigned)q.n_mat), 256, 0, s>>>(
+        qs, q.s_dec, nb, G, out);
+  seg.b_sc = out;
+  seg.b_nested = 0;
+  return launch_status("nf4_unnest");
+}
+
 template <int ASRC_X>
 bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int64_t R, hipStream_t s, bool nf4) {
   const int H = (int)d->H, I = (int)d->I, r = d->r;
@@ -2370,9 +2545,12 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.outf = h;
     p.out1 = a;
     // (NF4 weights take bf16 activations only: check_desc rejects act_quant with them)
-    if (nf4)
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch<256, A_GATHER, B_NF4_K, B_BF_K, EPI_GATEUP>(p, R, s, "gate_up fwd")));
-    else
+    if (nf4) {
+      mark(d, BQM_STAGE_GATE_UP_FWD, 0, s);
+      BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
+      BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd")));
+      mark(d, BQM_STAGE_GATE_UP_FWD, 1, s);
+    } else
       BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd")));
   }
   constexpr bool aq = ASRC_X == A_GATHER_Q;
@@ -2401,9 +2579,12 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.s2 = seg_lora(udn, d->B_dn, H, r, r);
     if (!aq) p.s2.K = r;
     p.out0 = y;
-    if (nf4)
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch<256, A_ROWS, B_NF4_K, B_BF_K, EPI_STORE>(p, R, s, "down fwd")));
-    else if (aq)
+    if (nf4) {
+      mark(d, BQM_STAGE_DOWN_FWD, 0, s);
+      BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
+      BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd")));
+      mark(d, BQM_STAGE_DOWN_FWD, 1, s);
+    } else if (aq)
       BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd")));
     else
       BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE>(p, R, s, "down fwd")));
@@ -2510,8 +2691,12 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     p.tw = w.at<float>(w.L.tw);
     if (col)
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fq<A_GATHER, EPI_DOWN_DGRAD, true>(p, R, s, "down dgrad (columnwise)")));
-    else if (nf4)
-      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+    else if (nf4) {
+      mark(d, BQM_STAGE_DOWN_DGRAD, 0, s);
+      BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
+      BQM_TRY((launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+      mark(d, BQM_STAGE_DOWN_DGRAD, 1, s);
+    }
     else
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fd<A_GATHER, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
   }
@@ -2537,8 +2722,12 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     p.out0 = dxr;
     if (col)
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fq<A_ROWS, EPI_STORE, true>(p, R, s, "gate_up dgrad (columnwise)")));
-    else if (nf4)
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+    else if (nf4) {
+      mark(d, BQM_STAGE_GATE_UP_DGRAD, 0, s);
+      BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
+      BQM_TRY((launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+      mark(d, BQM_STAGE_GATE_UP_DGRAD, 1, s);
+    }
     else
       BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE>(p, R, s, "gate_up dgrad")));
   }
