@@ -106,7 +106,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(inp, shape, experts=tuple(range(8))):
+def cpu_baseline(inp, shape, experts=tuple(range(24))):
     """The oracle (float64 CPU definition) on all routed rows of a few experts, timed on
     the host.  The oracle's own quantization of the touched experts (the frozen weights
     are quantized once per load, as on the GPU) runs before the timed region and is

@@ -846,11 +846,14 @@ constexpr int NST = 3;  // LDS stages: copies run two K steps ahead
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+constexpr int DQS = 72;  // row stride (bf16) of the dgrad's decoded NF4 tiles
+
 struct Smem {
   uint16_t a[NST][BM * BK];  // bf16, swizzled 128-byte rows
   uint8_t b[NST][BN * 32];   // codes: 32 bytes per output column (forward), 128 per weight row (dgrad)
-  uint32_t s[NST][BN];       // E4M3 block scales of the K step
+  uint32_t s[NST][BN];       // E4M3 block scales of the K step (NF4: FP32 absmax)
   uint8_t t[BN / 64][256];   // dgrad: each wave's scales regrouped per 16-column block
+  uint16_t dq[BN / 64][BK * DQS];  // NF4 dgrad: each wave's decoded 64 x 64 weight tile
 };
 
 // LDS byte addresses of a stage's A, B and scale areas and the wave index, all
@@ -1591,6 +1594,184 @@ __device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N
   step_dq<VT, false, false>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
   __syncthreads();  // the stages are reused by the next segment
 }
+
+// ---- dgrad over NF4 weights ----
+// NF4 blocks run along the weight's columns, which are the dgrad's output, so along the
+// contraction every value has its own absmax and the lane-wise table of the forward does
+// not apply.  Each K step's weight rows are decoded row-major instead, one slice (16 rows)
+// ahead of the MFMAs, into a per-wave bf16 tile in LDS (64 rows x the wave's 64 columns,
+// row stride DQS), and the B fragments are read from it with the 16-bit transposing LDS
+// read.  Lane 4r+q decodes row r's columns 16q..16q+15: the wave's 64 columns are one NF4
+// block, so the four lanes of a row share one absmax and build its table together (each
+// computes four entries, gathered with quad DPP broadcasts).  k order: slice kk holds rows
+// 16kk..16kk+15 and lane group g rows 16kk+8g..+8, for the A fragments and the weight alike.
+
+// quad-shared table: lane q of a quad computes entries 4q..4q+3 from lv = levels[4q..4q+3]
+__device__ __forceinline__ void nf4_table_quad(float a, const float4 &lv, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+  const int pa = (int)pack_bf16_rne(lv.x * a, lv.y * a), pb = (int)pack_bf16_rne(lv.z * a, lv.w * a);
+  uint32_t pr[8];  // quad_perm(i, i, i, i): lane i of the quad to all four
+  pr[0] = (uint32_t)__builtin_amdgcn_mov_dpp(pa, 0x00, 0xF, 0xF, true);
+  pr[1] = (uint32_t)__builtin_amdgcn_mov_dpp(pb, 0x00, 0xF, 0xF, true);
+  pr[2] = (uint32_t)__builtin_amdgcn_mov_dpp(pa, 0x55, 0xF, 0xF, true);
+  pr[3] = (uint32_t)__builtin_amdgcn_mov_dpp(pb, 0x55, 0xF, 0xF, true);
+  pr[4] = (uint32_t)__builtin_amdgcn_mov_dpp(pa, 0xAA, 0xF, 0xF, true);
+  pr[5] = (uint32_t)__builtin_amdgcn_mov_dpp(pb, 0xAA, 0xF, 0xF, true);
+  pr[6] = (uint32_t)__builtin_amdgcn_mov_dpp(pa, 0xFF, 0xF, 0xF, true);
+  pr[7] = (uint32_t)__builtin_amdgcn_mov_dpp(pb, 0xFF, 0xF, 0xF, true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = __builtin_amdgcn_perm(pr[2 * i + 1], pr[2 * i], 0x06040200u);
+    hi[i] = __builtin_amdgcn_perm(pr[2 * i + 1], pr[2 * i], 0x07050301u);
+  }
+}
+
+// a lane's share of one slice: its row's codes (16 columns) and absmax, the table, the pairs
+struct DnRow {
+  uint32_t c[2];
+  float a;
+  uint32_t lo[4], hi[4];
+  NF4Tmp t;
+  u32x4 o[2];
+};
+
+// codes and absmax of slice kk's row for this lane from stage (codes, absmax) in LDS
+__device__ __forceinline__ void dn_load(const uint8_t *Bs, const uint32_t *Ss, int wn, int kk, int lane, DnRow &r) {
+  const int row = 16 * kk + (lane >> 2), q = lane & 3;
+  const int c = 2 * wn + (q >> 1);
+  const i32x2 v = *reinterpret_cast<const i32x2 *>(Bs + row * 128 + 16 * (c ^ (row & 7)) + 8 * (q & 1));
+  r.c[0] = (uint32_t)v[0];
+  r.c[1] = (uint32_t)v[1];
+  r.a = __uint_as_float(Ss[row * 4 + wn]);
+}
+
+// part p (0..5) of decoding and storing this lane's 16 values of slice kk into the wave's tile
+template <int P>
+__device__ __forceinline__ void dn_part(DnRow &r, const float4 &lv, uint16_t *Dq, int kk, int lane) {
+  if constexpr (P == 0) {
+    nf4_table_quad(r.a, lv, r.lo, r.hi);
+  } else if constexpr (P == 1) {
+    nf4_part<0>(r.c[0], r.lo, r.hi, r.t, r.o[0]);
+    nf4_part<1>(r.c[0], r.lo, r.hi, r.t, r.o[0]);
+  } else if constexpr (P == 2) {
+    nf4_part<2>(r.c[0], r.lo, r.hi, r.t, r.o[0]);
+    nf4_part<3>(r.c[0], r.lo, r.hi, r.t, r.o[0]);
+    nf4_part<0>(r.c[1], r.lo, r.hi, r.t, r.o[1]);
+  } else if constexpr (P == 3) {
+    nf4_part<1>(r.c[1], r.lo, r.hi, r.t, r.o[1]);
+    nf4_part<2>(r.c[1], r.lo, r.hi, r.t, r.o[1]);
+    nf4_part<3>(r.c[1], r.lo, r.hi, r.t, r.o[1]);
+    uint16_t *dst = Dq + (16 * kk + (lane >> 2)) * DQS + 16 * (lane & 3);
+    *reinterpret_cast<u32x4 *>(dst) = r.o[0];
+    *reinterpret_cast<u32x4 *>(dst + 8) = r.o[1];
+  }
+}
+
+__device__ __forceinline__ bf16x8 a_frag_n(const uint16_t *As, int kk, int row, int lane) {
+  return *reinterpret_cast<const bf16x8 *>(As + a_off(row + (lane & 31), 2 * kk + (lane >> 5)));
+}
+
+
+// One K step of the NF4 dgrad.  On entry af[0] / bf[0] hold slice 0 of stage cur.  In each
+// slice, after its MFMA pairs: the next slice's rows are decoded (from stage cur, or for the
+// next step's slice 0 from stage nx after the step barrier), written to the wave's tile and
+// read back transposed as the next slice's B fragments.
+template <int VT, bool DMA, bool NEXT>
+__device__ __forceinline__ void step_dn(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrcD &d, int wn, int row0,
+                                        int lane, const float4 &lv, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN],
+                                        f32x16 (&acc)[TM][TN]) {
+  const uint16_t *As = sm.a[cur];
+  uint16_t *Dq = sm.dq[wn];
+  DnRow r;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = kk & 1, n = c ^ 1;
+    const bool last = kk == 3;
+    const int kn = last ? 0 : kk + 1;  // the slice decoded and loaded here
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
+      if (!last) {
+        if (tm < VT) af[n][tm] = a_frag_n(As, kn, row0 + 32 * tm, lane);
+      } else if (NEXT && tm >= 1) {
+        if (tm - 1 < VT) af[n][tm - 1] = a_frag_n(sm.a[nx], 0, row0 + 32 * (tm - 1), lane);
+        if (tm == 7 && 7 < VT) af[n][7] = a_frag_n(sm.a[nx], 0, row0 + 224, lane);
+      }
+      if (DMA && dma_slot<VT>(kk, tm) >= 0) dma_one_d<VT>(d, dma_slot<VT>(kk, tm), k2, sm, n2);
+      FQ_PIN();
+      if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
+      if (last && tm == 0 && NEXT) {
+        // stage nx has landed for every wave, and every wave is done with stage cur
+        FQ_PIN();
+        if (DMA)
+          wait_vm<VT>();
+        else
+          wait_vm<0>();
+        barrier_lds();
+        FQ_PIN();
+      }
+      if (!last || NEXT) {
+        if (tm == 0) dn_load(last ? sm.b[nx] : sm.b[cur], last ? sm.s[nx] : sm.s[cur], wn, kn, lane, r);
+        if (tm == 1) dn_part<0>(r, lv, Dq, kn, lane);
+        if (tm == 2) dn_part<1>(r, lv, Dq, kn, lane);
+        if (tm == 3) dn_part<2>(r, lv, Dq, kn, lane);
+        if (tm == 4) dn_part<3>(r, lv, Dq, kn, lane);
+        if (tm == 5) bf[n][0] = __builtin_bit_cast(u32x4, b_frag_trans_s<DQS>(Dq, 16 * kn, 0, lane));
+        if (tm == 6) bf[n][1] = __builtin_bit_cast(u32x4, b_frag_trans_s<DQS>(Dq, 16 * kn, 32, lane));
+      }
+      FQ_PIN();
+    }
+  }
+}
+
+template <int EPI, int VT>
+__device__ __forceinline__ void seg_dn_direct(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
+                                              f32x16 (&acc)[TM][TN]) {
+  constexpr int NDMA = VT + 3;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int nk = s.K / BK;
+  const float4 lv = reinterpret_cast<const float4 *>(c_nf4)[lane & 3];
+  DmaSrcD d;
+  dma_src_d<VT>(s, arow, e, nt, N, d);
+#pragma unroll
+  for (int j = 0; j < NDMA; ++j) dma_one_d<VT>(d, j, 0, sm, 0);
+  if (nk > 1) {
+#pragma unroll
+    for (int j = 0; j < NDMA; ++j) dma_one_d<VT>(d, j, BK, sm, 1);
+    wait_vm<NDMA>();
+  } else {
+    wait_vm<0>();
+  }
+  barrier_lds();
+  bf16x8 af[2][TM];
+  u32x4 bf[2][TN];
+  {
+    uint16_t *Dq = sm.dq[wn];
+    DnRow r;
+    dn_load(sm.b[0], sm.s[0], wn, 0, lane, r);
+    dn_part<0>(r, lv, Dq, 0, lane);
+    dn_part<1>(r, lv, Dq, 0, lane);
+    dn_part<2>(r, lv, Dq, 0, lane);
+    dn_part<3>(r, lv, Dq, 0, lane);
+    bf[0][0] = __builtin_bit_cast(u32x4, b_frag_trans_s<DQS>(Dq, 0, 0, lane));
+    bf[0][1] = __builtin_bit_cast(u32x4, b_frag_trans_s<DQS>(Dq, 0, 32, lane));
+#pragma unroll
+    for (int tm = 0; tm < VT; ++tm) af[0][tm] = a_frag_n(sm.a[0], 0, row0 + 32 * tm, lane);
+  }
+  int cur = 0, ks = 0;
+  for (; ks + 2 < nk; ++ks) {
+    const int nx = cur == NST - 1 ? 0 : cur + 1;
+    const int n2 = nx == NST - 1 ? 0 : nx + 1;
+    step_dn<VT, true, true>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, lv, af, bf, acc);
+    cur = nx;
+  }
+  if (ks + 1 < nk) {
+    const int nx = cur == NST - 1 ? 0 : cur + 1;
+    step_dn<VT, false, true>(sm, cur, nx, 0, 0, d, wn, row0, lane, lv, af, bf, acc);
+    cur = nx;
+  }
+  step_dn<VT, false, false>(sm, cur, 0, 0, 0, d, wn, row0, lane, lv, af, bf, acc);
+  __syncthreads();  // the stages are reused by the next segment
+}
 #undef FQ_PIN
 
 // Segment 2 of the dgrad (LoRA): A = hi/lo pair rows (k >= K zeroed), B = the bf16
@@ -1644,7 +1825,7 @@ __device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, c
   }
 }
 
-template <int ASRC, int EPI>
+template <int ASRC, int EPI, int WF = WF_NVFP4>
 __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int total = p.tile_off[p.E] * p.NT;
@@ -1679,22 +1860,38 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
       for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
   // row tiles rounded up to even counts; the copies cover the tile's 32 vt rows only
   const int vtu = __builtin_amdgcn_readfirstlane(vt);  // every wave starts at row 0: vt is the tile's
-  if (vtu > 6) {
-    dma_rows<ASRC, 8>(p, rb, n_e, m0, arow);
-    seg_dq_direct<EPI, 8>(p.s1, e, nt, p.N, arow, sm, acc);
-  } else if (vtu > 4) {
-    dma_rows<ASRC, 6>(p, rb, n_e, m0, arow);
-    seg_dq_direct<EPI, 6>(p.s1, e, nt, p.N, arow, sm, acc);
-  } else if (vtu > 2) {
-    dma_rows<ASRC, 4>(p, rb, n_e, m0, arow);
-    seg_dq_direct<EPI, 4>(p.s1, e, nt, p.N, arow, sm, acc);
+  if constexpr (WF == WF_NF4) {
+    if (vtu > 6) {
+      dma_rows<ASRC, 8>(p, rb, n_e, m0, arow);
+      seg_dn_direct<EPI, 8>(p.s1, e, nt, p.N, arow, sm, acc);
+    } else if (vtu > 4) {
+      dma_rows<ASRC, 6>(p, rb, n_e, m0, arow);
+      seg_dn_direct<EPI, 6>(p.s1, e, nt, p.N, arow, sm, acc);
+    } else if (vtu > 2) {
+      dma_rows<ASRC, 4>(p, rb, n_e, m0, arow);
+      seg_dn_direct<EPI, 4>(p.s1, e, nt, p.N, arow, sm, acc);
+    } else {
+      dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
+      seg_dn_direct<EPI, 2>(p.s1, e, nt, p.N, arow, sm, acc);
+    }
   } else {
-    dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
-    seg_dq_direct<EPI, 2>(p.s1, e, nt, p.N, arow, sm, acc);
+    if (vtu > 6) {
+      dma_rows<ASRC, 8>(p, rb, n_e, m0, arow);
+      seg_dq_direct<EPI, 8>(p.s1, e, nt, p.N, arow, sm, acc);
+    } else if (vtu > 4) {
+      dma_rows<ASRC, 6>(p, rb, n_e, m0, arow);
+      seg_dq_direct<EPI, 6>(p.s1, e, nt, p.N, arow, sm, acc);
+    } else if (vtu > 2) {
+      dma_rows<ASRC, 4>(p, rb, n_e, m0, arow);
+      seg_dq_direct<EPI, 4>(p.s1, e, nt, p.N, arow, sm, acc);
+    } else {
+      dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
+      seg_dq_direct<EPI, 2>(p.s1, e, nt, p.N, arow, sm, acc);
+    }
   }
   // the per-expert FP32 decode scale multiplies the whole accumulator (the LoRA
-  // segment's A operand was stored divided by it)
-  const float esc = uniform_load(p.s1.b_sd + e);
+  // segment's A operand was stored divided by it); NF4 values are the weights themselves
+  const float esc = WF == WF_NF4 ? 1.0f : uniform_load(p.s1.b_sd + e);
   if (p.s2.K > 0) {
     int64_t arow2[ACH];
 #pragma unroll
@@ -2438,11 +2635,11 @@ bqm_status launch_lp(const GemmParams &p, int64_t R, hipStream_t s, const char *
 }
 
 // dgrad GEMM over the rowwise NVFP4 weight read transposed (codes staged in LDS)
-template <int ASRC, int EPI>
+template <int ASRC, int EPI, int WF = fq::WF_NVFP4>
 bqm_status launch_fd(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
   static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
   const int grid = gemm_grid(R, p.E, p.NT);
-  fq::gemm_dgrad_q4<ASRC, EPI><<<grid, fq::NTHR, 0, s>>>(p);
+  fq::gemm_dgrad_q4<ASRC, EPI, WF><<<grid, fq::NTHR, 0, s>>>(p);
   return launch_status(what);
 }
 
@@ -2694,7 +2891,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     else if (nf4) {
       mark(d, BQM_STAGE_DOWN_DGRAD, 0, s);
       BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
-      BQM_TRY((launch<256, A_GATHER, B_NF4_N, B_BF_N, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+      BQM_TRY((launch_fd<A_GATHER, EPI_DOWN_DGRAD, fq::WF_NF4>(p, R, s, "down dgrad")));
       mark(d, BQM_STAGE_DOWN_DGRAD, 1, s);
     }
     else
@@ -2725,7 +2922,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     else if (nf4) {
       mark(d, BQM_STAGE_GATE_UP_DGRAD, 0, s);
       BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
-      BQM_TRY((launch<256, A_ROWS, B_NF4_N, B_BF_N, EPI_STORE>(p, R, s, "gate_up dgrad")));
+      BQM_TRY((launch_fd<A_ROWS, EPI_STORE, fq::WF_NF4>(p, R, s, "gate_up dgrad")));
       mark(d, BQM_STAGE_GATE_UP_DGRAD, 1, s);
     }
     else
