@@ -11,16 +11,25 @@
 // exists.  Only experts that received rows are ever read.
 //
 // Structure: the routed pairs are sorted by expert (route.hip), so each expert
-// owns a contiguous segment of rows.  One templated grouped-GEMM kernel runs
-// every contraction: a 128 x BN output tile of one expert, a K loop in steps of
-// 64 through two LDS stages, the weight tile dequantized from 4-bit codes to
-// bf16 while it is staged (e2m1 * e4m3 and the NF4 levels are exact in bf16, the
-// FP32 per-tensor scale is applied to the accumulator), bf16 MFMA 32x32x16 with
-// FP32 accumulation, then an optional second K segment (the LoRA up-projection,
-// K = r) and a fused epilogue (SwiGLU, routing weight, SwiGLU backward).
-// Workgroups are mapped so that each of the 8 XCDs walks a contiguous range of
-// tiles: the tiles in flight on one XCD share an expert's activation rows and
-// weight rows in that XCD's L2.
+// owns a contiguous segment of rows.  Two grouped-GEMM kernels (namespace fq) run
+// the four weight contractions: a 256 x 256 output tile of one expert per
+// workgroup of four waves (one per SIMD, each owning 256 rows x 64 columns), a K
+// loop in steps of 64 through three LDS stages filled by direct-to-LDS copies two
+// steps ahead, bf16 MFMA 32x32x16 with FP32 accumulation, then the LoRA
+// up-projection as a short second segment and a fused epilogue (SwiGLU, routing
+// weight, SwiGLU backward).  The weights go to LDS as stored (4-bit codes and
+// their block scales) and are decoded in registers right before the MFMAs:
+//   - gemm_fwd_q4 reads the codes K-major (forward, and a dgrad over a columnwise
+//     copy); NVFP4 as e2m1 * e4m3 (exact in bf16; the FP32 per-tensor scale goes
+//     on the accumulator), NF4 through a per-column 16-entry table of
+//     bf16(level * absmax) looked up with byte permutes;
+//   - gemm_dgrad_q4 reads the single rowwise copy transposed (4-bit transposing
+//     LDS read, NVFP4), or for NF4 decodes its rows into a per-wave bf16 tile read
+//     back with the 16-bit transposing read.
+// The LoRA down-projections (N = r) stream through lp::gemm_lora_proj; the LoRA
+// weight gradients through lora_wgrad.  Workgroups are mapped so that each of the
+// 8 XCDs walks a contiguous range of tiles: the tiles in flight on one XCD share
+// an expert's activation rows and weight rows in that XCD's L2.
 #include "common.h"
 #include "internal.h"
 #include "nf4_levels.inc"
@@ -36,16 +45,12 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int BM = 256;       // output rows per tile (routed rows of one expert)
 constexpr int BK = 64;        // K step (one NF4 block, four NVFP4 blocks)
-constexpr int SK = BK + 8;    // LDS row stride in bf16 (16-byte pad)
 constexpr int NTHR = 256;
 
 // A operand rows: bf16 activations gathered by token (A_GATHER) or in routed order
 // (A_ROWS); the _Q forms are per-row NVFP4 activations expanded to bf16 val * sb
 // (exact), whose per-row decode scales (Seg::a_sd) multiply the accumulator.
 enum ASrc { A_GATHER = 0, A_ROWS = 1, A_GATHER_Q = 2, A_ROWS_Q = 3 };
-// B operand of the older staged kernel (moe_gemm): NF4 weights K-major (forward) or N-major (dgrad),
-// bf16 LoRA matrices, or none.  (NVFP4 weights run on the kernels of namespace fq.)
-enum BSrc { B_NF4_K = 2, B_NF4_N = 3, B_BF_K = 4, B_BF_N = 5, B_NONE = 6 };
 enum Epi { EPI_GATEUP = 0, EPI_STORE = 1, EPI_DOWN_DGRAD = 2, EPI_STORE_SPLIT = 4 };
 
 // One K segment of a contraction: A rows times one expert slice of a B stack.
@@ -80,16 +85,6 @@ struct GemmParams {
 
 __constant__ float c_nf4[16] = BQM_NF4_LEVELS;
 
-__device__ __forceinline__ uint32_t nf4_bf16(const float *lut, uint32_t code, float a) {
-  return f32_to_bf16(lut[code] * a);
-}
-
-__device__ __forceinline__ void nf4x8(const float *lut, uint32_t c, float a, uint32_t *o) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = nf4_bf16(lut, (c >> (8 * i)) & 0xFu, a) | (nf4_bf16(lut, (c >> (8 * i + 4)) & 0xFu, a) << 16);
-}
-
 // ---------------------------------------------------------------------------
 // tile-column -> weight-row mapping
 // ---------------------------------------------------------------------------
@@ -106,33 +101,6 @@ __device__ __forceinline__ int64_t b_row_of_col(int j, int nt, int N, int I) {
     int n = nt * BN + j;
     return n < N ? n : -1;
   }
-}
-
-// ---------------------------------------------------------------------------
-// tile shapes
-// ---------------------------------------------------------------------------
-// A tile is BM routed rows x BN output columns; WM x WN waves each own a
-// (BM/WM) x (BN/WN) block of 32x32 MFMA tiles.  The main GEMMs use 256 x 256
-// with 8 waves (two per SIMD, so one wave's dequantization overlaps the other's
-// MFMAs); the LoRA down-projections (N = r) use 256 x 64 with 4 waves.
-template <int BM_, int BN_, int WM_, int WN_>
-struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int NTHR = 64 * WM * WN;
-  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  static constexpr int ACH = BM * 8 / NTHR;  // 16-byte A chunks per thread per K step
-};
-using BigCfg = Cfg<256, 256, 4, 2>;
-
-// B tiles of N-major sources (the dgrad reads the rowwise weight transposed, and
-// the bf16 LoRA matrices there) stay in their natural [k][n] layout in LDS with a
-// row stride of BN + 32 bf16; MFMA fragments are read with the gfx950 transposing
-// LDS read.  Within each 16-lane group that read hands output lane 4a+b element b
-// of the 8-byte chunks addressed by lanes a, a+4, a+8, a+12, so lanes pointing at
-// rows k0 + s/4 and columns 4(s%4) deliver four consecutive k of one column each.
-template <int BN>
-constexpr int skt() {
-  return BN + 32;
 }
 
 typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -160,67 +128,6 @@ template <int SEL>
 __device__ __forceinline__ f32x2 fp4pair(uint32_t c, float sb) {
   f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, SEL);
   return v * sb;  // exact: <= 6 significant bits
-}
-
-// ---------------------------------------------------------------------------
-// A tile: BM rows x BK, staged to LDS as bf16 [BM][SK]
-// ---------------------------------------------------------------------------
-template <class C>
-struct ARegs {
-  uint4 v[C::ACH > 2 ? C::ACH : 2];
-};
-
-template <class C, int ASRC>
-__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[C::ACH], int k0, ARegs<C> &r) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < C::ACH; ++i) {
-    const int c = tid + C::NTHR * i;
-    const int kk = k0 + (c & 7) * 8;
-    if (arow[i] >= 0 && kk < s.K)
-      r.v[i] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.a) + arow[i] * s.a_ld + kk);
-    else
-      r.v[i] = make_uint4(0, 0, 0, 0);
-  }
-}
-
-template <class C, int ASRC>
-__device__ __forceinline__ void a_store(uint16_t *As, const ARegs<C> &r) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < C::ACH; ++i) {
-    const int c = tid + C::NTHR * i;
-    *reinterpret_cast<uint4 *>(As + (c >> 3) * SK + (c & 7) * 8) = r.v[i];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// B tile: BN output columns x BK, staged to LDS as bf16 [BN][SK] (k contiguous)
-// ---------------------------------------------------------------------------
-struct BRegs {
-  uint32_t w[32];
-};
-
-template <int BSRC>
-constexpr bool trans_b() {
-  return BSRC == B_NF4_N || BSRC == B_BF_N;
-}
-
-// absmax of NF4 block blk (row-major block index within expert e's matrix) into
-// w[4]: the stored FP32 value, or from the nested code fl(fl(e4m3(q) * s2[blk / 256])
-// + offset), the two roundings kept apart (no contraction into an FMA).  (Forming
-// the nested value later, where the tile is decoded, measured slower for plain NF4.)
-__device__ __forceinline__ void nf4_absmax_load(const Seg &s, int e, int64_t blk, uint32_t *w) {
-#pragma clang fp contract(off)
-  const int64_t nb = s.b_rows * s.b_cols / 64;
-  if (!s.b_nested) {
-    w[4] = __float_as_uint(reinterpret_cast<const float *>(s.b_sc)[e * nb + blk]);
-    return;
-  }
-  const float *sdm = s.b_sd + e * (1 + (nb + 255) / 256);
-  const uint32_t q = reinterpret_cast<const uint8_t *>(s.b_sc)[e * nb + blk];
-  const float prod = __builtin_amdgcn_cvt_f32_fp8(q, 0) * sdm[1 + (blk >> 8)];
-  w[4] = __float_as_uint(prod + sdm[0]);
 }
 
 // Nested NF4: absmax' of every block of a stack, fl(fl(e4m3(q) * s2[group]) + offset)
@@ -259,114 +166,6 @@ __global__ void __launch_bounds__(256) nf4_unnest(const uint8_t *__restrict__ q,
   }
 }
 
-template <class C, int BSRC, int EPI>
-__device__ __forceinline__ void b_load(const Seg &s, int e, int nt, int N, int I, int k0, BRegs &r) {
-  constexpr int BN = C::BN;
-  const int tid = threadIdx.x;
-  const int64_t slice = s.b_rows * s.b_cols;
-  if constexpr (BSRC == B_NF4_K) {
-    // K-major 4-bit weight [N rows][K cols]: 32 elements (16 B of codes) of one row per thread
-    static_assert(BN * BK / C::NTHR == 32, "K-major 4-bit tile expects 32 elements per thread");
-    const int j = tid >> 1, kofs = (tid & 1) * 32;
-    const int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
-    if (wr < 0) {
-      r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
-      return;
-    }
-    const uint8_t *cp = reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) + wr * (s.b_cols / 2) + (k0 + kofs) / 2;
-    const uint4 a = *reinterpret_cast<const uint4 *>(cp);
-    r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-    nf4_absmax_load(s, e, wr * (s.b_cols / 64) + k0 / 64, r.w);
-  } else if constexpr (BSRC == B_NF4_N) {
-    // N-major 4-bit weight [K rows][N cols]: one k row, 32 columns (16 B of codes) per thread
-    static_assert(BN == 256 && C::NTHR == 512, "N-major 4-bit tile expects 256 columns and 512 threads");
-    const int row = tid >> 3, chunk = tid & 7;
-    const int n = nt * BN + chunk * 32;
-    const int64_t kk = k0 + row;
-    if (n < N) {
-      const uint4 a = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2) +
-                                                       kk * (s.b_cols / 2) + n / 2);
-      r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
-      nf4_absmax_load(s, e, kk * (s.b_cols / 64) + n / 64, r.w);
-    } else {
-      r.w[0] = r.w[1] = r.w[2] = r.w[3] = r.w[4] = 0u;
-    }
-  } else if constexpr (BSRC == B_BF_K) {
-    // bf16 [N rows][K cols]: BN*8 chunks of 16 B
-    constexpr int CH = BN * 8 / C::NTHR;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + C::NTHR * i;
-      const int j = c >> 3, kk = k0 + (c & 7) * 8;
-      const int64_t wr = b_row_of_col<EPI, BN>(j, nt, N, I);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const int kb = s.kmod ? kk % s.kmod : kk;
-      if (wr >= 0 && kk < s.K)
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + wr * s.b_cols + kb);
-      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
-    }
-  } else if constexpr (BSRC == B_BF_N) {
-    // bf16 [K rows][N cols]: 64 rows x BN/8 chunks of 16 B, kept in natural layout
-    constexpr int CPR = BN / 8;
-    constexpr int CH = 64 * CPR / C::NTHR;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + C::NTHR * i;
-      const int row = c / CPR, n = nt * BN + (c % CPR) * 8;
-      const int kk = k0 + row;
-      const int kb = s.kmod ? kk % s.kmod : kk;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < N && kk < s.K)
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + (int64_t)kb * s.b_cols + n);
-      r.w[4 * i] = v.x; r.w[4 * i + 1] = v.y; r.w[4 * i + 2] = v.z; r.w[4 * i + 3] = v.w;
-    }
-  }
-}
-
-// Writes the loaded registers into Bs as bf16 (dequantizing 4-bit codes).
-template <class C, int BSRC>
-__device__ __forceinline__ void b_store(uint16_t *Bs, const BRegs &r, const float *lut) {
-  constexpr int BN = C::BN;
-  const int tid = threadIdx.x;
-  if constexpr (BSRC == B_NF4_K) {
-    const int j = tid >> 1, kofs = (tid & 1) * 32;
-    uint4 *dst = reinterpret_cast<uint4 *>(Bs + j * SK + kofs);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t o[4];
-      nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
-      dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  } else if constexpr (BSRC == B_NF4_N) {
-    // natural layout: row k, columns chunk*32 .. +32 (element pairs along n)
-    const int row = tid >> 3, chunk = tid & 7;
-    uint4 *dst = reinterpret_cast<uint4 *>(Bs + row * skt<BN>() + chunk * 32);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t o[4];
-      nf4x8(lut, r.w[q], __uint_as_float(r.w[4]), o);
-      dst[q] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  } else if constexpr (BSRC == B_BF_K) {
-    constexpr int CH = BN * 8 / C::NTHR;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + C::NTHR * i;
-      *reinterpret_cast<uint4 *>(Bs + (c >> 3) * SK + (c & 7) * 8) =
-          make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]);
-    }
-  } else if constexpr (BSRC == B_BF_N) {
-    constexpr int CPR = BN / 8;
-    constexpr int CH = 64 * CPR / C::NTHR;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + C::NTHR * i;
-      *reinterpret_cast<uint4 *>(Bs + (c / CPR) * skt<BN>() + (c % CPR) * 8) =
-          make_uint4(r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]);
-    }
-  }
-}
-
 // A wave-uniform float loaded once into a scalar register.  Loaded into a vector
 // register instead, its first use sits inside the epilogue's per-element branches,
 // and the wait for the load is then repeated before every store (each such wait
@@ -397,149 +196,10 @@ __device__ __forceinline__ bf16x8 b_frag_trans_s(const uint16_t *Bs, int kbase, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int BN>
-__device__ __forceinline__ bf16x8 b_frag_trans(const uint16_t *Bs, int kbase, int nbase, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int row = kbase + 8 * (g >> 1) + (s >> 2);
-  const int col = nbase + 16 * (g & 1) + 4 * (s & 3);
-  const uint16_t *p0 = Bs + row * skt<BN>() + col;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p0 + 4 * skt<BN>()));
-  const s16x4 h0 = lo, h1 = hi;
-  typedef __attribute__((ext_vector_type(8))) short s16x8;
-  const s16x8 v = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-template <class C, bool TRANS>
-__device__ __forceinline__ void mma_stage(const uint16_t *As, const uint16_t *Bs,
-                                          f32x16 (&acc)[C::TM][C::TN]) {
-  constexpr int TM = C::TM, TN = C::TN, WN = C::WN;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wm = wid / WN, wn = wid % WN;
-#pragma unroll
-  for (int kk = 0; kk < BK / 16; ++kk) {
-    bf16x8 af[TM], bfr[TN];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-      af[tm] = *reinterpret_cast<const bf16x8 *>(As + (wm * TM * 32 + tm * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-      if constexpr (TRANS)
-        bfr[tn] = b_frag_trans<C::BN>(Bs, kk * 16, wn * TN * 32 + tn * 32, lane);
-      else
-        bfr[tn] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * TN * 32 + tn * 32 + (lane & 31)) * SK + kk * 16 + (lane >> 5) * 8);
-    }
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
-        acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tm], bfr[tn], acc[tm][tn], 0, 0, 0);
-  }
-}
-
-template <class C>
-struct Smem {
-  static constexpr int BSZ = C::BN * SK > BK * skt<C::BN>() ? C::BN * SK : BK * skt<C::BN>();
-  uint16_t As[2][C::BM * SK];
-  uint16_t Bs[2][BSZ];
-};
-
-// Runs one K segment into acc.  arow: the A source rows of this thread's loads;
-// active: this wave has at least one valid row (else it skips its MFMAs).
-template <class C, int ASRC, int BSRC, int EPI>
-__device__ __forceinline__ void run_segment(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[C::ACH],
-                                            Smem<C> &sm, const float *lut, bool active,
-                                            f32x16 (&acc)[C::TM][C::TN]) {
-  const int nk = (s.K + BK - 1) / BK;
-  ARegs<C> ar;
-  BRegs br;
-  a_load<C, ASRC>(s, arow, 0, ar);
-  b_load<C, BSRC, EPI>(s, e, nt, N, I, 0, br);
-  a_store<C, ASRC>(sm.As[0], ar);
-  b_store<C, BSRC>(sm.Bs[0], br, lut);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const bool more = ks + 1 < nk;
-    if (more) {
-      a_load<C, ASRC>(s, arow, (ks + 1) * BK, ar);
-      b_load<C, BSRC, EPI>(s, e, nt, N, I, (ks + 1) * BK, br);
-    }
-    if (active) mma_stage<C, trans_b<BSRC>()>(sm.As[cur], sm.Bs[cur], acc);
-    if (more) {
-      a_store<C, ASRC>(sm.As[cur ^ 1], ar);
-      b_store<C, BSRC>(sm.Bs[cur ^ 1], br, lut);
-    }
-    __syncthreads();
-  }
-}
-
 // ---------------------------------------------------------------------------
 // epilogues: acc[tm][tn] element v of a wave holds row row0 + tm*32 + 8(v/4) +
 // 4(lane/32) + v%4 and column col0 + tn*32 + lane%32 of the tile
 // ---------------------------------------------------------------------------
-// SwiGLU backward of the down dgrad: da = w * da_u, dh = [dg, du] from the saved FP32
-// gate/up activations.  One 32-row block at a time, every load of the block (the
-// 16 rows' routing weights and their gate/up values) is issued before any store,
-// through restrict pointers, so the loads of a block overlap one another instead
-// of each waiting for the previous row's stores.
-template <int TM, int TN, int BN, bool FULL>
-__device__ __forceinline__ void epilogue_down_dgrad(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0,
-                                                    int n_e, int rb, int row0, int col0, int lane, float esc) {
-  const int32_t *__restrict__ perm = p.perm;
-  const float *__restrict__ tw = p.tw;
-  const float *__restrict__ hin = p.h_in;
-  uint16_t *__restrict__ out = p.out0;
-  const int64_t ld = 2 * (int64_t)p.I;
-  constexpr int VB = 32 / TN;  // rows per batch: 64 gate/up values in flight
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-    for (int v0 = 0; v0 < 16; v0 += VB) {
-      int64_t grow[VB];
-      int pf[VB];
-#pragma unroll
-      for (int j = 0; j < VB; ++j) {
-        const int v = v0 + j;
-        const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        grow[j] = rb + min(pos, n_e - 1);  // rows past the segment: loads of a valid row, no store
-        pf[j] = perm[grow[j]];
-      }
-      float w[VB], g[VB][TN], u[VB][TN];
-#pragma unroll
-      for (int j = 0; j < VB; ++j) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          int i = nt * BN + col0 + tn * 32 + (lane & 31);
-          i = i < p.N ? i : 0;
-          g[j][tn] = hin[grow[j] * ld + i];
-          u[j][tn] = hin[grow[j] * ld + p.I + i];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < VB; ++j) w[j] = tw[pf[j]];
-#pragma unroll
-      for (int j = 0; j < VB; ++j) {
-        const int v = v0 + j;
-        const int pos = m0 + row0 + tm * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (!FULL && pos >= n_e) continue;
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-          const int i = nt * BN + col0 + tn * 32 + (lane & 31);
-          if (!FULL && i >= p.N) continue;
-          const float sg = sigmoid_f(g[j][tn]);
-          const float da = w[j] * (acc[tm][tn][v] * esc);
-          const float dg = da * u[j][tn] * sg * (1.0f + g[j][tn] * (1.0f - sg));
-          const float du = da * g[j][tn] * sg;
-          out[grow[j] * ld + i] = (uint16_t)f32_to_bf16(dg);
-          out[grow[j] * ld + p.I + i] = (uint16_t)f32_to_bf16(du);
-        }
-      }
-    }
-  }
-}
-
 // FULL: every row and column of this wave's block is inside the output (the common
 // case), so the per-element bounds tests and their branches are left out.
 template <int TM, int TN, int BN, int EPI, bool FULL>
@@ -593,13 +253,6 @@ template <int TM, int TN, int BN, int EPI>
 __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc)[TM][TN], int e, int nt, int m0,
                                          int n_e, int rb, int row0, int col0, int lane, float esc) {
   const bool rows_in = m0 + row0 + TM * 32 <= n_e;
-  if constexpr (EPI == EPI_DOWN_DGRAD) {
-    if (rows_in && nt * BN + col0 + TN * 32 <= p.N)
-      epilogue_down_dgrad<TM, TN, BN, true>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
-    else
-      epilogue_down_dgrad<TM, TN, BN, false>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
-    return;
-  }
   const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
   const bool cols_in = EPI == EPI_GATEUP ? nt * (BN / 2) + col0 / 2 + (TN / 2) * 32 <= p.I
                                          : nt * BN + col0 + TN * 32 <= p.N;
@@ -725,87 +378,6 @@ __device__ __forceinline__ void epilogue_t(const GemmParams &p, const f32x16 (&a
     epilogue_t_body<TM, TN, BN, EPI, true>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
   else
     epilogue_t_body<TM, TN, BN, EPI, false>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
-}
-
-template <class C, int ASRC, int BSRC, int B2SRC, int EPI>
-__global__ void __launch_bounds__(C::NTHR) moe_gemm(GemmParams p) {
-  constexpr int TM = C::TM, TN = C::TN, WN = C::WN, BN = C::BN, BMc = C::BM;
-  __shared__ __attribute__((aligned(16))) Smem<C> sm;
-  __shared__ float lut[16];
-
-  // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
-  const int total = p.tile_off[p.E] * p.NT;
-  const int per = (total + 7) / 8;
-  const int li = blockIdx.x >> 3;
-  if (li >= per) return;
-  const int L = (blockIdx.x & 7) * per + li;
-  if (L >= total) return;
-  const int mt = L / p.NT, nt = L % p.NT;
-  int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.tile_off[mid] <= mt)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  const int e = lo;
-  const int rb = p.offsets[e];
-  const int n_e = p.offsets[e + 1] - rb;
-  const int m0 = (mt - p.tile_off[e]) * BMc;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WN, wn = wid % WN;
-  const bool active = m0 + wm * TM * 32 < n_e;
-
-  if constexpr (BSRC == B_NF4_K || BSRC == B_NF4_N) {
-    if (tid < 16) lut[tid] = c_nf4[tid];
-    __syncthreads();
-  }
-
-  // source rows of this thread's A loads (segment 1)
-  int64_t arow[C::ACH];
-#pragma unroll
-  for (int i = 0; i < C::ACH; ++i) {
-    const int row = (tid + C::NTHR * i) >> 3;
-    const int pos = m0 + row;
-    if (pos >= n_e)
-      arow[i] = -1;
-    else if (ASRC == A_GATHER || ASRC == A_GATHER_Q)
-      arow[i] = p.perm[rb + pos] / p.k;
-    else
-      arow[i] = rb + pos;
-  }
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
-
-  run_segment<C, ASRC, BSRC, EPI>(p.s1, e, nt, p.N, p.I, arow, sm, lut, active, acc);
-
-  // NF4 weights are dequantized exactly to their bf16 operand (no separate decode
-  // scale) and the activations are bf16 rows
-  static_assert(ASRC == A_GATHER || ASRC == A_ROWS, "bf16 activation rows");
-  const float esc = 1.0f;
-
-  if constexpr (B2SRC != B_NONE) {
-    if (p.s2.K > 0) {
-      int64_t arow2[C::ACH];
-#pragma unroll
-      for (int i = 0; i < C::ACH; ++i) {
-        const int pos = m0 + ((tid + C::NTHR * i) >> 3);
-        arow2[i] = pos < n_e ? (int64_t)(rb + pos) : -1;
-      }
-      run_segment<C, A_ROWS, B2SRC, EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, lut, active, acc);
-    }
-  }
-
-  // epilogue
-  if (!active) return;
-  epilogue<TM, TN, BN, EPI>(p, acc, e, nt, m0, n_e, rb, wm * TM * 32, wn * TN * 32, lane, esc);
 }
 
 // x *= s on an accumulator element that stays in its AGPR (VALU arithmetic cannot
@@ -1959,7 +1531,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
     seg_q4_direct<EPI, 2, WF>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
   }
 
-  // FP32 decode scales of segment 1 (see moe_gemm): per expert in the epilogue,
+  // FP32 decode scales of segment 1: per expert in the epilogue,
   // per row and expert (NVFP4 activations, val * sb rows) before the LoRA segment
   float esc = 1.0f;  // NF4: the table values are the dequantized weights themselves
   if constexpr (!kQA && WF == WF_NVFP4) esc = uniform_load(p.s1.b_sd + e);
@@ -2587,17 +2159,6 @@ Seg seg_q(const void *a, int64_t a_ld, const bqm_qtensor &w, int K) {
   s.b_nested = w.fmt == BQM_FMT_NF4 ? w.nested : 0;
   s.K = K;
   return s;
-}
-
-// the older staged kernel (NF4 weights)
-template <int BN, int ASRC, int BSRC, int B2SRC, int EPI>
-bqm_status launch(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
-  static_assert(BN == 256, "NF4 tiles are 256 columns wide");
-  using C = BigCfg;
-  static_assert(C::BM == BM, "tile offsets are computed for BM rows");
-  const int grid = gemm_grid(R, p.E, p.NT);
-  moe_gemm<C, ASRC, BSRC, B2SRC, EPI><<<grid, C::NTHR, 0, s>>>(p);
-  return launch_status(what);
 }
 
 // NVFP4 weights with bf16 activations apply the per-expert s_dec to the whole
