@@ -7,11 +7,11 @@ namespace bqm {
 
 // Stable counting sort of R routed pairs by expert (route.hip).  counts_ws needs
 // permute_ws_bytes(R, E).  If tile_off != NULL it also receives the prefix sum of
-// ceil(count_e / bm) over experts ([E+1] entries).
+// ceil(count_e / bm) over experts ([E+1] entries); tile_off2 likewise for bm2.
 size_t permute_ws_bytes(int64_t R, int E);
 bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
-                          int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off,
-                          hipStream_t s);
+                          int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off, int bm2,
+                          int32_t *tile_off2, hipStream_t s);
 
 // NVFP4 codes and E4M3 scales of n elements (n % 16 == 0) -> bf16 val * sb, exact
 // (quant.hip): the activation rows of the W4A4 GEMMs, whose per-row s_dec is applied

@@ -421,6 +421,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int DQS = 72;  // row stride (bf16) of the dgrad's decoded NF4 tiles
 
 struct Smem {
+  static constexpr int NS = NST, NSG = 0;
   uint16_t a[NST][BM * BK];  // bf16, swizzled 128-byte rows
   uint8_t b[NST][BN * 32];   // codes: 32 bytes per output column (forward), 128 per weight row (dgrad)
   uint32_t s[NST][BN];       // E4M3 block scales of the K step (NF4: FP32 absmax)
@@ -431,15 +432,19 @@ struct Smem {
 // LDS byte addresses of a stage's A, B and scale areas and the wave index, all
 // computed in scalar registers (the copies take their LDS address from M0)
 __device__ __forceinline__ uint32_t wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-__device__ __forceinline__ uint32_t smem_u32(const Smem &sm) { return (uint32_t)(uintptr_t)(const lds_void *)&sm; }
-__device__ __forceinline__ uint32_t lds_a(const Smem &sm, int st) {
-  return smem_u32(sm) + (uint32_t)offsetof(Smem, a) + (uint32_t)st * (uint32_t)sizeof(sm.a[0]);
+template <class SM>
+__device__ __forceinline__ uint32_t smem_u32(const SM &sm) { return (uint32_t)(uintptr_t)(const lds_void *)&sm; }
+template <class SM>
+__device__ __forceinline__ uint32_t lds_a(const SM &sm, int st) {
+  return smem_u32(sm) + (uint32_t)offsetof(SM, a) + (uint32_t)st * (uint32_t)sizeof(sm.a[0]);
 }
-__device__ __forceinline__ uint32_t lds_b(const Smem &sm, int st) {
-  return smem_u32(sm) + (uint32_t)offsetof(Smem, b) + (uint32_t)st * (uint32_t)sizeof(sm.b[0]);
+template <class SM>
+__device__ __forceinline__ uint32_t lds_b(const SM &sm, int st) {
+  return smem_u32(sm) + (uint32_t)offsetof(SM, b) + (uint32_t)st * (uint32_t)sizeof(sm.b[0]);
 }
-__device__ __forceinline__ uint32_t lds_s(const Smem &sm, int st) {
-  return smem_u32(sm) + (uint32_t)offsetof(Smem, s) + (uint32_t)st * (uint32_t)sizeof(sm.s[0]);
+template <class SM>
+__device__ __forceinline__ uint32_t lds_s(const SM &sm, int st) {
+  return smem_u32(sm) + (uint32_t)offsetof(SM, s) + (uint32_t)st * (uint32_t)sizeof(sm.s[0]);
 }
 
 // Workgroup barrier that orders LDS (waits for this wave's LDS operations, then
@@ -457,8 +462,10 @@ __device__ __forceinline__ void wait_vm() {
 
 __device__ __forceinline__ int a_off(int r, int c) { return r * BK + 8 * (c ^ ((r >> 1) & 7)); }
 
-// row of the tile owned by this thread's j-th A chunk
-__device__ __forceinline__ int a_row(int j) { return 64 * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3); }
+// row of the tile owned by this thread's j-th A chunk (NC chunks of 8 rows per wave,
+// 32 NC rows per tile)
+template <int NC = ACH>
+__device__ __forceinline__ int a_row(int j) { return 8 * NC * (threadIdx.x >> 6) + 8 * j + ((threadIdx.x & 63) >> 3); }
 
 // A row of this lane's direct copy j when a tile holds VT valid 32-row tiles: each wave
 // copies 8 VT rows (VT copies of 8 rows), so a tile copies only the 32 VT rows its
@@ -492,16 +499,17 @@ __device__ __forceinline__ void dma_b32(const void *g, uint32_t lds) {
 }
 
 // A rows through registers (the LoRA segment; k >= K zeroed when MASKK)
+template <int NC = ACH>
 struct ARegs {
-  u32x4 v[ACH];
+  u32x4 v[NC];
 };
 
-template <int ASRC, bool MASKK>
-__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[ACH], int k0, ARegs &r) {
+template <int ASRC, bool MASKK, int NC = ACH>
+__device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[ACH], int k0, ARegs<NC> &r) {
   const int tid = threadIdx.x;
   const uint16_t *a = reinterpret_cast<const uint16_t *>(s.a);
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
+  for (int i = 0; i < NC; ++i) {
     const int kk = k0 + (tid & 7) * 8;
     const bool ok = !MASKK || kk < s.K;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(a + arow[i] * s.a_ld + (ok ? kk : 0));
@@ -509,17 +517,18 @@ __device__ __forceinline__ void a_load(const Seg &s, const int64_t (&arow)[ACH],
   }
 }
 
-template <int ASRC>
-__device__ __forceinline__ void a_store(uint16_t *As, const ARegs &r) {
+template <int ASRC, int NC = ACH>
+__device__ __forceinline__ void a_store(uint16_t *As, const ARegs<NC> &r) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) *reinterpret_cast<u32x4 *>(As + a_off(a_row(i), tid & 7)) = r.v[i];
+  for (int i = 0; i < NC; ++i) *reinterpret_cast<u32x4 *>(As + a_off(a_row<NC>(i), tid & 7)) = r.v[i];
 }
 
-// A fragments of slice kk for row tiles 0..TM-1
-__device__ __forceinline__ void a_frags(const uint16_t *As, int kk, int row0, int lane, bf16x8 (&af)[TM]) {
+// A fragments of slice kk for row tiles 0..TMA-1
+template <int TMA = TM>
+__device__ __forceinline__ void a_frags(const uint16_t *As, int kk, int row0, int lane, bf16x8 (&af)[TMA]) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
+  for (int tm = 0; tm < TMA; ++tm)
     af[tm] = *reinterpret_cast<const bf16x8 *>(As + a_off(row0 + tm * 32 + (lane & 31), 4 * (lane >> 5) + kk));
 }
 
@@ -599,11 +608,11 @@ __device__ __forceinline__ void nf4_step(const BCodes &b, int tn, int kk, NF4Tmp
 }
 
 
-template <int VT>
-__device__ __forceinline__ void mfmas(const bf16x8 (&af)[TM], const bf16x8 (&bf)[TN], int vt,
-                                      f32x16 (&acc)[TM][TN]) {
+template <int VT, int TMA = TM>
+__device__ __forceinline__ void mfmas(const bf16x8 (&af)[TMA], const bf16x8 (&bf)[TN], int vt,
+                                      f32x16 (&acc)[TMA][TN]) {
 #pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
+  for (int tm = 0; tm < TMA; ++tm) {
     if (VT != VT_DYN || tm < vt) {
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn)
@@ -651,16 +660,62 @@ __device__ __forceinline__ void dma_src(const Seg &s, const int64_t (&arow)[ACH]
   d.s = scales + wr * (s.b_cols / 16);
 }
 
-// copy number j (0..VT+2) of the K step at k0 into stage st: A rows (j < VT), codes, scales
-template <int VT>
-__device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, const Smem &sm, int st) {
+// copies j < VT + 2 (A rows and codes) of the K step at k0 into stage st
+template <int VT, class SM>
+__device__ __forceinline__ void dma_ac(const DmaSrc &d, int j, int k0, const SM &sm, int st) {
   const uint32_t w = wave_id();
   if (j < VT)
     dma_b128(d.a[j] + k0, lds_a(sm, st) + (8 * VT * w + 8 * j) * BK * 2);
-  else if (j < VT + 2)
+  else
     dma_b128(d.c[j - VT] + k0 / 2, lds_b(sm, st) + (2 * w + j - VT) * 1024);
+}
+
+// copy number j (0..VT+2) of the K step at k0 into stage st: A rows (j < VT), codes, scales
+template <int VT, class SM>
+__device__ __forceinline__ void dma_one(const DmaSrc &d, int j, int k0, const SM &sm, int st) {
+  const uint32_t w = wave_id();
+  if (j < VT + 2)
+    dma_ac<VT>(d, j, k0, sm, st);
   else
     dma_b32(d.s + k0 / 16, lds_s(sm, st) + 256 * w);
+}
+
+// Scale groups (the few-rows configuration): the E4M3 scales (NF4: FP32 absmax) of four
+// consecutive K steps, 16 bytes of one weight row, go to LDS with one 16-byte copy lane
+// per column instead of one 4-byte copy per column and step, so a quarter of the copy
+// instructions carry the scales, and each touches a column's cache line once per four
+// steps.  The group of step ks lives in buffer (ks / 4) % NSG; the last group of a K
+// range is shifted back to end at the row's end (K >= 256, so that it starts >= 0).
+template <class SM>
+__device__ __forceinline__ uint32_t lds_sg(const SM &sm, int buf) {
+  return smem_u32(sm) + (uint32_t)offsetof(SM, sg) + (uint32_t)buf * (uint32_t)sizeof(sm.sg[0]);
+}
+__device__ __forceinline__ int sg_first(int g, int nk) { return min(4 * g, nk - 4); }
+// the group that starts at the K step at k0
+template <class SM>
+__device__ __forceinline__ void dma_sg(const DmaSrc &d, int k0, int nk, const SM &sm) {
+  const int g = k0 / (4 * BK);
+  dma_b128(d.s + 4 * sg_first(g, nk), lds_sg(sm, g % SM::NSG) + 1024 * wave_id());
+}
+// the scale word of column 0 for step ks (column c at index 4 c)
+template <class SM>
+__device__ __forceinline__ const uint32_t *sg_words(const SM &sm, int ks, int nk) {
+  const int g = ks >> 2;
+  return sm.sg[g % SM::NSG] + (ks - sg_first(g, nk));
+}
+
+// copy j (0 .. VT+2) of the K step at k0: A rows (j < VT), codes (two), then the scale
+// word, or with scale groups the group's copy, issued with the group's first step only
+template <int VT, bool SG, class SM>
+__device__ __forceinline__ void dma_any(const DmaSrc &d, int j, int k0, int nk, const SM &sm, int st) {
+  if constexpr (SG) {
+    if (j < VT + 2)
+      dma_ac<VT>(d, j, k0, sm, st);
+    else if (((k0 / BK) & 3) == 0)
+      dma_sg(d, k0, nk, sm);
+  } else {
+    dma_one<VT>(d, j, k0, sm, st);
+  }
 }
 
 // Where the VT + 3 copies of step ks+2 are issued inside step ks: the VT copies of A
@@ -689,12 +744,14 @@ struct BRaw {
   uint32_t sw[TN];
 };
 
+// SST: dwords between the scale words of consecutive columns
+template <int SST = 1>
 __device__ __forceinline__ void b_raw(const uint8_t *Bs, const uint32_t *Ss, int wn, int lane, BRaw &r) {
 #pragma unroll
   for (int tn = 0; tn < TN; ++tn) {
     const int col = wn * TN * 32 + tn * 32 + (lane & 31);
     r.c[tn] = *reinterpret_cast<const u32x4 *>(Bs + col * 32 + 16 * (lane >> 5));
-    r.sw[tn] = Ss[col];
+    r.sw[tn] = Ss[col * SST];
   }
 }
 
@@ -737,11 +794,14 @@ __device__ __forceinline__ void mfma1(const bf16x8 &a, const u32x4 &b, f32x16 &a
 
 // One K step.  On entry af[0] / bf[0] hold slice 0 of stage `cur` and bc its codes.
 // DMA: issue the copies of the step at k2 into stage n2.  NEXT: a following step
-// exists (stage nx), whose slice 0 is loaded into af[0] / bf[0] at the end.
-template <int VT, bool DMA, bool NEXT, int WF>
-__device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrc &d, int wn, int row0,
-                                        int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], BCodes &bc,
-                                        f32x16 (&acc)[TM][TN]) {
+// exists (stage nx), whose slice 0 is loaded into af[0] / bf[0] at the end; before
+// reading it the wave lets WV of its copies stay in flight (those of later steps).
+// TMA: row tiles of the accumulator (VT <= TMA of them are valid).
+// SG: scale groups (nk: K steps of the segment; sgn: the scale words of the next step)
+template <int VT, bool DMA, bool NEXT, int WF, int WV, int TMA, bool SG = false, class SM>
+__device__ __forceinline__ void step_q4(SM &sm, int cur, int nx, int n2, int k2, const DmaSrc &d, int wn, int row0,
+                                        int lane, bf16x8 (&af)[2][TMA], u32x4 (&bf)[2][TN], BCodes &bc,
+                                        f32x16 (&acc)[TMA][TN], int nk = 0, const uint32_t *sgn = nullptr) {
   const uint16_t *As = sm.a[cur];
   NF4Tmp nt;
 #pragma unroll
@@ -751,7 +811,7 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
     for (int tm = 0; tm < TM; ++tm) {
       if (tm < VT) mfma1(af[c][tm], bf[c][0], acc[tm][0]);
       if (tm < VT) af[n][tm] = a_frag(As, kk + 1, row0 + 32 * tm, lane);
-      if (DMA && dma_slot<VT>(kk, tm) >= 0) dma_one<VT>(d, dma_slot<VT>(kk, tm), k2, sm, n2);
+      if (DMA && dma_slot<VT>(kk, tm) >= 0) dma_any<VT, SG>(d, dma_slot<VT>(kk, tm), k2, nk, sm, n2);
       FQ_PIN();
       if (tm < VT) mfma1(af[c][tm], bf[c][1], acc[tm][1]);
       if constexpr (WF == WF_NVFP4) {
@@ -773,8 +833,8 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
     if (tm < VT) mfma1(af[1][tm], bf[1][0], acc[tm][0]);
     if (NEXT && tm >= 2 && tm - 2 < VT) af[0][tm - 2] = a_frag(sm.a[nx], 0, row0 + 32 * (tm - 2), lane);
     if (NEXT && tm == 7) {
-      if (VT > 6) af[0][6] = a_frag(sm.a[nx], 0, row0 + 192, lane);
-      if (VT > 7) af[0][7] = a_frag(sm.a[nx], 0, row0 + 224, lane);
+      if constexpr (VT > 6) af[0][6] = a_frag(sm.a[nx], 0, row0 + 192, lane);
+      if constexpr (VT > 7) af[0][7] = a_frag(sm.a[nx], 0, row0 + 224, lane);
     }
     FQ_PIN();
     if (tm < VT) mfma1(af[1][tm], bf[1][1], acc[tm][1]);
@@ -783,15 +843,15 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
       // cur (its last reads were issued in slice 2 and are drained here), so the
       // next step may copy into it
       FQ_PIN();
-      if (DMA)
-        wait_vm<VT>();
-      else
-        wait_vm<0>();
+      wait_vm<WV>();
       barrier_lds();
       FQ_PIN();
-      b_raw(sm.b[nx], sm.s[nx], wn, lane, raw);
+      if constexpr (SG)
+        b_raw<4>(sm.b[nx], sgn, wn, lane, raw);
+      else
+        b_raw(sm.b[nx], sm.s[nx], wn, lane, raw);
     }
-    if (DMA && dma_slot<VT>(3, tm) >= 0) dma_one<VT>(d, dma_slot<VT>(3, tm), k2, sm, n2);
+    if (DMA && dma_slot<VT>(3, tm) >= 0) dma_any<VT, SG>(d, dma_slot<VT>(3, tm), k2, nk, sm, n2);
     if constexpr (WF == WF_NVFP4) {
       if (NEXT && tm == 3) b_cook(raw, lane, bc);
       if (NEXT && tm >= 4) {
@@ -822,31 +882,74 @@ __device__ __forceinline__ void step_q4(Smem &sm, int cur, int nx, int n2, int k
   }
 }
 
-template <int EPI, int VT, int WF>
+// Copies a wave has in flight after those of a K step: the waits below count L later
+// steps as L sets of VT A-row copies and two code copies (and the scale word without
+// scale groups), leaving out scale groups, which only makes a wait longer.
+template <int VT, bool SG>
+__device__ __forceinline__ constexpr int later_copies(int L) {
+  return L * (VT + (SG ? 2 : 3));
+}
+
+// The last steps of the K loop, which issue no copies: tail step J (of D) waits until
+// the copies of at most D - 2 - J later steps are in flight.  Steps J < j0 do not
+// exist (K shorter than D steps).  (The step of tail step J is nk - D + J.)
+template <int VT, int WF, int TMA, bool SG, int J, int D, class SM>
+__device__ __forceinline__ void tail_q4(SM &sm, int &cur, int j0, int nk, const DmaSrc &d, int wn, int row0, int lane,
+                                        bf16x8 (&af)[2][TMA], u32x4 (&bf)[2][TN], BCodes &bc,
+                                        f32x16 (&acc)[TMA][TN]) {
+  if constexpr (J < D) {
+    if (J >= j0) {
+      const int nx = cur == SM::NS - 1 ? 0 : cur + 1;
+      constexpr bool kNext = J + 1 < D;
+      const uint32_t *sgn = nullptr;
+      if constexpr (SG && kNext) sgn = sg_words(sm, nk - D + J + 1, nk);
+      step_q4<VT, false, kNext, WF, kNext ? later_copies<VT, SG>(D - 2 - J) : 0, TMA, SG>(
+          sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, bc, acc, nk, sgn);
+      cur = nx;
+    }
+    tail_q4<VT, WF, TMA, SG, J + 1, D>(sm, cur, j0, nk, d, wn, row0, lane, af, bf, bc, acc);
+  }
+}
+
+// Segment 1: the K loop over the 4-bit weight with copies issued D = NS - 1 steps
+// ahead.  SG: scale groups (the segment's K is then at least 256).
+template <int EPI, int VT, int WF, int TMA, bool SG = false, class SM>
 __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
-                                              Smem &sm, f32x16 (&acc)[TM][TN]) {
-  constexpr int NDMA = VT + 3;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+                                              SM &sm, f32x16 (&acc)[TMA][TN]) {
+  constexpr int NDMA = VT + 3, D = SM::NS - 1;
+  static_assert(D >= 2 && later_copies<VT, SG>(D) + 1 < 64, "copies in flight fit the wait counter");
+  static_assert(!SG || D <= 4 * (SM::NSG - 1), "a scale group is written after its buffer's last reader");
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TMA * 32;
   const int nk = s.K / BK;
   DmaSrc d;
   dma_src<EPI, VT>(s, arow, e, nt, N, I, d);
-  // prologue: stage 0 <- step 0, stage 1 <- step 1; wait for stage 0 only
+  // prologue: stage j <- step j for j < D; wait for stage 0 only
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) dma_one<VT>(d, j, 0, sm, 0);
-  if (nk > 1) {
+  for (int j = 0; j < NDMA; ++j) dma_any<VT, SG>(d, j, 0, nk, sm, 0);
+  if (nk >= D) {
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j) dma_one<VT>(d, j, BK, sm, 1);
-    wait_vm<NDMA>();
+    for (int st = 1; st < D; ++st)
+#pragma unroll
+      for (int j = 0; j < NDMA; ++j) dma_any<VT, SG>(d, j, st * BK, nk, sm, st);
+    wait_vm<later_copies<VT, SG>(D - 1)>();
   } else {
+    if constexpr (D > 2) {
+      for (int st = 1; st < nk; ++st)
+#pragma unroll
+        for (int j = 0; j < NDMA; ++j) dma_any<VT, SG>(d, j, st * BK, nk, sm, st);
+    }
     wait_vm<0>();
   }
   barrier_lds();
-  bf16x8 af[2][TM];
+  bf16x8 af[2][TMA];
   u32x4 bf[2][TN];
   BCodes bc;
   {
     BRaw raw;
-    b_raw(sm.b[0], sm.s[0], wn, lane, raw);
+    if constexpr (SG)
+      b_raw<4>(sm.b[0], sg_words(sm, 0, nk), wn, lane, raw);
+    else
+      b_raw(sm.b[0], sm.s[0], wn, lane, raw);
 #pragma unroll
     for (int tm = 0; tm < VT; ++tm) af[0][tm] = a_frag(sm.a[0], 0, row0 + 32 * tm, lane);
     if constexpr (WF == WF_NVFP4) {
@@ -866,18 +969,28 @@ __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N
     }
   }
   int cur = 0, ks = 0;
-  for (; ks + 2 < nk; ++ks) {
-    const int nx = cur == NST - 1 ? 0 : cur + 1;
-    const int n2 = nx == NST - 1 ? 0 : nx + 1;
-    step_q4<VT, true, true, WF>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, bc, acc);
+  for (; ks + D < nk; ++ks) {
+    const int nx = cur == SM::NS - 1 ? 0 : cur + 1;
+    // stage of step ks + D, last read in step ks - 1
+    const int nd = D == 2 ? (nx == SM::NS - 1 ? 0 : nx + 1) : (cur == 0 ? SM::NS - 1 : cur - 1);
+    const uint32_t *sgn = nullptr;
+    if constexpr (SG) sgn = sg_words(sm, ks + 1, nk);
+    step_q4<VT, true, true, WF, later_copies<VT, SG>(D - 2) + VT, TMA, SG>(sm, cur, nx, nd, (ks + D) * BK, d, wn, row0,
+                                                                       lane, af, bf, bc, acc, nk, sgn);
     cur = nx;
   }
-  if (ks + 1 < nk) {
-    const int nx = cur == NST - 1 ? 0 : cur + 1;
-    step_q4<VT, false, true, WF>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
-    cur = nx;
+  if constexpr (D == 2) {
+    if (ks + 1 < nk) {
+      const int nx = cur == SM::NS - 1 ? 0 : cur + 1;
+      const uint32_t *sgn = nullptr;
+      if constexpr (SG) sgn = sg_words(sm, ks + 1, nk);
+      step_q4<VT, false, true, WF, 0, TMA, SG>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, bc, acc, nk, sgn);
+      cur = nx;
+    }
+    step_q4<VT, false, false, WF, 0, TMA, SG>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, bc, acc, nk, nullptr);
+  } else {
+    tail_q4<VT, WF, TMA, SG, 0, D>(sm, cur, nk >= D ? 0 : D - nk, nk, d, wn, row0, lane, af, bf, bc, acc);
   }
-  step_q4<VT, false, false, WF>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, bc, acc);
   __syncthreads();  // the stages are reused by the next segment
 }
 #undef FQ_PIN
@@ -887,15 +1000,16 @@ __device__ __forceinline__ void seg_q4_direct(const Seg &s, int e, int nt, int N
 // from global memory (it is small and stays in L2).  The loads of step ks+1 are
 // issued before the MFMAs of step ks, alternating between two LDS A buffers, so
 // the segment waits for global memory once, not once per slice.
+template <int NC = ACH>
 struct LoraRegs {
-  ARegs a;
+  ARegs<NC> a;
   bf16x8 b[4][TN];
 };
 
-template <int EPI>
+template <int EPI, int NC>
 __device__ __forceinline__ void lora_load(const Seg &s, const int64_t (&arow)[ACH], const uint16_t *bsrc,
-                                          const int64_t (&wr)[TN], int ks, int lane, LoraRegs &r) {
-  a_load<A_ROWS, true>(s, arow, ks * BK, r.a);
+                                          const int64_t (&wr)[TN], int ks, int lane, LoraRegs<NC> &r) {
+  a_load<A_ROWS, true, NC>(s, arow, ks * BK, r.a);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int kb = (ks * BK + 32 * (lane >> 5) + 8 * kk) % s.kmod;
@@ -904,11 +1018,12 @@ __device__ __forceinline__ void lora_load(const Seg &s, const int64_t (&arow)[AC
   }
 }
 
-template <int EPI>
+// TMA row tiles of 32 (arow: the A rows of this thread's TMA chunks, a_row<TMA>)
+template <int EPI, int TMA = TM, class SM>
 __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int I, const int64_t (&arow)[ACH],
-                                         Smem &sm, int vt, f32x16 (&acc)[TM][TN]) {
+                                         SM &sm, int vt, f32x16 (&acc)[TMA][TN]) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG;
-  const int row0 = (wid / WNG) * TM * 32;
+  const int row0 = (wid / WNG) * TMA * 32;
   const int nk = (s.K + BK - 1) / BK;
   const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
   int64_t wr[TN];
@@ -917,20 +1032,20 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
     int64_t w = b_row_of_col<EPI, BN>(wn * TN * 32 + tn * 32 + (lane & 31), nt, N, I);
     wr[tn] = w < 0 ? 0 : w;
   }
-  LoraRegs r[2];
+  LoraRegs<TMA> r[2];
   lora_load<EPI>(s, arow, bsrc, wr, 0, lane, r[0]);
   for (int ks = 0; ks < nk; ks += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (ks + h >= nk) break;
-      a_store<A_ROWS>(sm.a[h], r[h].a);
+      a_store<A_ROWS, TMA>(sm.a[h], r[h].a);
       if (ks + h + 1 < nk) lora_load<EPI>(s, arow, bsrc, wr, ks + h + 1, lane, r[h ^ 1]);
       __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 af[TM];
-        a_frags(sm.a[h], kk, row0, lane, af);
-        mfmas<VT_DYN>(af, r[h].b[kk], vt, acc);
+        bf16x8 af[TMA];
+        a_frags<TMA>(sm.a[h], kk, row0, lane, af);
+        mfmas<VT_DYN, TMA>(af, r[h].b[kk], vt, acc);
       }
     }
   }
@@ -1353,7 +1468,7 @@ __device__ __forceinline__ void seg_dn_direct(const Seg &s, int e, int nt, int N
 constexpr int LSTR = BN + 8;
 
 __device__ __forceinline__ void lora_n_load(const Seg &s, const int64_t (&arow)[ACH], const uint16_t *bsrc, int nt,
-                                            int N, int ks, ARegs &a, u32x4 (&bv)[8]) {
+                                            int N, int ks, ARegs<> &a, u32x4 (&bv)[8]) {
   const int tid = threadIdx.x;
   a_load<A_ROWS, true>(s, arow, ks * BK, a);
 #pragma unroll
@@ -1371,7 +1486,7 @@ __device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, c
   const int nk = (s.K + BK - 1) / BK;
   const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
   uint16_t *Bt = sm.a[1];
-  ARegs ar;
+  ARegs<> ar;
   u32x4 bv[8];
   lora_n_load(s, arow, bsrc, nt, N, 0, ar, bv);
   for (int ks = 0; ks < nk; ++ks) {
@@ -1568,6 +1683,96 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   }
 
   if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
+}
+
+// ---- Few routed rows per expert (decode-sized batches) ----
+// With a handful of rows per expert the forward is a stream of the hit experts'
+// weights, and what bounds it is how many weight bytes each CU keeps in flight.
+// This configuration runs the same K loop on 64-row tiles (one or two valid 32-row
+// tiles) with NS LDS stages of 17 KB, so that NS - 1 K steps of copies are in flight
+// per workgroup instead of two, and OCC workgroups per CU.
+constexpr int BMN = 64, TMN = BMN / 32;
+
+template <int NS_>
+struct SmemN {
+  static constexpr int NS = NS_, NSG = 2;
+  uint16_t a[NS_][BMN * BK];
+  uint8_t b[NS_][BN * 32];
+  uint32_t sg[NSG][BN * 4];  // scale groups: column c's 16 bytes at 16 c
+};
+
+// tile_off: prefix over experts of ceil(rows / BMN)
+template <int ASRC, int EPI, int WF, int NS, int OCC>
+__global__ void __launch_bounds__(NTHR, OCC) gemm_fwd_q4n(GemmParams p) {
+  static_assert(WF == WF_NVFP4 || (ASRC == A_GATHER || ASRC == A_ROWS), "NF4 weights take bf16 activations");
+  __shared__ __attribute__((aligned(16))) SmemN<NS> sm;
+  const int total = p.tile_off[p.E] * p.NT;
+  const int per = (total + 7) / 8;
+  const int li = blockIdx.x >> 3;
+  if (li >= per) return;
+  const int L = (blockIdx.x & 7) * per + li;
+  if (L >= total) return;
+  const int mt = L / p.NT, nt = L % p.NT;
+  int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= mt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int rb = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - rb;
+  const int m0 = (mt - p.tile_off[e]) * BMN;
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WNG;
+  const int rows_left = n_e - m0;  // >= 1: the tile exists
+  const int vt = rows_left >= BMN ? TMN : (rows_left + 31) / 32;
+  constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
+  int64_t arow[ACH];
+  f32x16 acc[TMN][TN];
+#pragma unroll
+  for (int tm = 0; tm < TMN; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  if (__builtin_amdgcn_readfirstlane(vt) > 1) {
+    dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
+    seg_q4_direct<EPI, 2, WF, TMN, true>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  } else {
+    dma_rows<ASRC, 1>(p, rb, n_e, m0, arow);
+    seg_q4_direct<EPI, 1, WF, TMN, true>(p.s1, e, nt, p.N, p.I, arow, sm, acc);
+  }
+  float esc = 1.0f;
+  if constexpr (!kQA && WF == WF_NVFP4) esc = uniform_load(p.s1.b_sd + e);
+  if constexpr (kQA) {
+    const float sb = p.s1.b_sd[e];
+#pragma unroll
+    for (int tm = 0; tm < TMN; ++tm) {
+      float sc = sb;
+      const int pos = m0 + tm * 32 + (lane & 31);
+      if (pos < n_e) {
+        const int64_t src = ASRC == A_GATHER_Q ? (int64_t)(p.perm[rb + pos] / p.k) : (int64_t)(rb + pos);
+        sc = sb * p.s1.a_sd[src];
+      }
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float x = acc[tm][tn][v];
+          scale_acc(x, sc);
+          acc[tm][tn][v] = x;
+        }
+    }
+  }
+  if (p.s2.K > 0) {
+    int64_t arow2[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row<TMN>(i < TMN ? i : 0), n_e - 1);
+    seg_lora<EPI, TMN>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
+  }
+  epilogue_t<TMN, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc);
 }
 }  // namespace fq
 
@@ -1996,7 +2201,7 @@ __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict_
 // host side
 // ---------------------------------------------------------------------------
 struct Layout {
-  size_t perm, inv, off, tile_off, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
+  size_t perm, inv, off, tile_off, tile_off_n, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
       vgu, dxr, part, absx;
   size_t total;
 };
@@ -2018,6 +2223,7 @@ Layout layout(const bqm_moe_desc *d) {
   L.inv = take(R * 4);
   L.off = take((E + 1) * 4);
   L.tile_off = take((E + 1) * 4);
+  L.tile_off_n = take((E + 1) * 4);
   L.counts = take(permute_ws_bytes((int64_t)R, (int)E));
   L.tw = take(R * 4);
   L.ugu = take(R * 2 * r * 2);
@@ -2111,9 +2317,11 @@ bqm_status check_ws(const bqm_moe_desc *d, void *ws, size_t ws_bytes, const char
   return BQM_OK;
 }
 
-int gemm_grid(int64_t R, int E, int NT) {
-  int64_t mt = cdiv(R, BM) + E;
-  int64_t g = mt * NT;
+// upper bound on the tiles of a grouped GEMM: every expert with rows adds at most
+// one partial row tile, and at most min(E, R) experts have rows
+int gemm_grid(int64_t R, int E, int NT, int bm = BM) {
+  const int64_t mt = cdiv(R, bm) + std::min<int64_t>(E, R);
+  const int64_t g = std::max<int64_t>(mt * NT, 1);
   return (int)((g + 7) / 8 * 8);
 }
 
@@ -2169,10 +2377,25 @@ bool lora_folds_s_dec(const bqm_moe_desc *d, bool forward) {
   return d->w_gu.fmt == BQM_FMT_NVFP4 && !(forward && d->act_quant);
 }
 
-// forward GEMM over NVFP4 weights: codes staged in LDS, decoded in registers
+// Decode-sized batches: with at most this many routed rows per expert on average the
+// forward GEMMs run on 64-row tiles (fq::gemm_fwd_q4n): kNSN LDS stages (76 KB) and
+// kOccN workgroups per CU
+constexpr int64_t kFewRowsPerExpert = 32;
+constexpr int kNSN = 4, kOccN = 2;
+bool few_rows(const bqm_moe_desc *d) { return d->T * d->k <= kFewRowsPerExpert * d->E; }
+
+// forward GEMM over 4-bit weights: codes staged in LDS, decoded in registers.
+// tile_off_n: the prefix of 64-row tiles per expert, to run the few-rows configuration
 template <int ASRC, int EPI, bool LORN = false, int WF = fq::WF_NVFP4>
-bqm_status launch_fq(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, const int32_t *tile_off_n = nullptr) {
   static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
+  if constexpr (!LORN) {
+    if (tile_off_n && p.s1.K >= 4 * BK) {  // scale groups of four K steps
+      p.tile_off = tile_off_n;
+      fq::gemm_fwd_q4n<ASRC, EPI, WF, kNSN, kOccN><<<gemm_grid(R, p.E, p.NT, fq::BMN), fq::NTHR, 0, s>>>(p);
+      return launch_status(what);
+    }
+  }
   const int grid = gemm_grid(R, p.E, p.NT);
   fq::gemm_fwd_q4<ASRC, EPI, LORN, WF><<<grid, fq::NTHR, 0, s>>>(p);
   return launch_status(what);
@@ -2279,6 +2502,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
   uint16_t *y = w.at<uint16_t>(w.L.y);
   uint16_t *a = w.at<uint16_t>(w.L.a);
   const bool fold_fwd = lora_folds_s_dec(d, true);
+  const int32_t *tn = few_rows(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
   // U_gu = s X A_gu^T   [R, r]  (divided by the expert's s_dec when that folds)
   if (r > 0) {
     GemmParams p = base_params(d, w);
@@ -2306,10 +2530,10 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     if (nf4) {
       mark(d, BQM_STAGE_GATE_UP_FWD, 0, s);
       BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
-      BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd")));
+      BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd", tn)));
       mark(d, BQM_STAGE_GATE_UP_FWD, 1, s);
     } else
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd", tn)));
   }
   constexpr bool aq = ASRC_X == A_GATHER_Q;
   if (aq)
@@ -2340,12 +2564,12 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     if (nf4) {
       mark(d, BQM_STAGE_DOWN_FWD, 0, s);
       BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
-      BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd")));
+      BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd", tn)));
       mark(d, BQM_STAGE_DOWN_FWD, 1, s);
     } else if (aq)
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd", tn)));
     else
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE>(p, R, s, "down fwd")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE>(p, R, s, "down fwd", tn)));
   }
   return BQM_OK;
 }
@@ -2373,7 +2597,8 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
                 "bqm_moe_fwd: pointer not 16-byte aligned");
   }
   BQM_STAGE(d, BQM_STAGE_PERMUTE, s, permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
-                         w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off), s));
+                         w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off), fq::BMN,
+                                                w.at<int32_t>(w.L.tile_off_n), s));
   if (R == 0) return BQM_OK;
   if (hipMemcpyAsync(w.at<float>(w.L.tw), topk_w, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return launch_status("bqm_moe_fwd: copy of routing weights");

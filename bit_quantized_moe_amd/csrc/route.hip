@@ -104,13 +104,15 @@ __global__ void __launch_bounds__(256) perm_hist(const int32_t *__restrict__ idx
 
 // Pass 2 (one block): base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e];
 // offsets = exclusive prefix of the per-expert totals; the dropped bucket E starts
-// at offsets[E].  Optionally the prefix
-// of ceil(count / bm) (row tiles per expert) for the grouped GEMMs.  The prefixes
-// over experts are a wave-level inclusive scan plus the totals of the waves before.
+// at offsets[E].  Optionally the prefixes
+// of ceil(count / bm) and ceil(count / bm2) (row tiles per expert) for the grouped
+// GEMMs.  The prefixes over experts are a wave-level inclusive scan plus the totals
+// of the waves before.
 __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, int nchunks, int E,
                                                   int32_t *__restrict__ offsets, int bm,
-                                                  int32_t *__restrict__ tile_off) {
-  __shared__ int32_t wsum[16][2];
+                                                  int32_t *__restrict__ tile_off, int bm2,
+                                                  int32_t *__restrict__ tile_off2) {
+  __shared__ int32_t wsum[16][3];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   const int64_t ld = E + 1;
   int32_t run = 0;
@@ -122,34 +124,40 @@ __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, 
     }
   }
   const int32_t tiles = (e < E && bm > 0) ? (run + bm - 1) / bm : 0;
-  int32_t v = run, u = tiles;  // inclusive prefixes within the wave
+  const int32_t tiles2 = (e < E && bm2 > 0) ? (run + bm2 - 1) / bm2 : 0;
+  int32_t v = run, u = tiles, u2 = tiles2;  // inclusive prefixes within the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int32_t tv = __shfl_up(v, off, 64), tu = __shfl_up(u, off, 64);
+    const int32_t tv = __shfl_up(v, off, 64), tu = __shfl_up(u, off, 64), tu2 = __shfl_up(u2, off, 64);
     if (lane >= off) {
       v += tv;
       u += tu;
+      u2 += tu2;
     }
   }
   if (lane == 63) {
     wsum[wave][0] = v;
     wsum[wave][1] = u;
+    wsum[wave][2] = u2;
   }
   __syncthreads();
-  int32_t bv = 0, bu = 0;  // totals of the waves before this one
+  int32_t bv = 0, bu = 0, bu2 = 0;  // totals of the waves before this one
   for (int q = 0; q < wave; ++q) {
     bv += wsum[q][0];
     bu += wsum[q][1];
+    bu2 += wsum[q][2];
   }
-  const int32_t ex = bv + v - run, ext = bu + u - tiles;  // exclusive prefixes
+  const int32_t ex = bv + v - run, ext = bu + u - tiles, ext2 = bu2 + u2 - tiles2;  // exclusive prefixes
   if (e < E) {
     for (int c = 0; c < nchunks; ++c) counts[c * ld + e] += ex;
     offsets[e] = ex;
     if (tile_off) tile_off[e] = ext;
+    if (tile_off2) tile_off2[e] = ext2;
   }
   if (e == E - 1) {
     offsets[E] = ex + run;
     if (tile_off) tile_off[E] = ext + tiles;
+    if (tile_off2) tile_off2[E] = ext2 + tiles2;
     // the dropped pairs follow every expert's rows, chunk by chunk
     int32_t drun = ex + run;
     for (int c = 0; c < nchunks; ++c) {
@@ -209,15 +217,15 @@ size_t permute_ws_bytes(int64_t R, int E) {
 }
 
 bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
-                          int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off,
-                          hipStream_t s) {
+                          int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off, int bm2,
+                          int32_t *tile_off2, hipStream_t s) {
   const int nchunks = (int)cdiv(R, kChunk);
   if (R > 0) {
     perm_hist<<<nchunks, 256, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws);
     bqm_status st = launch_status("perm_hist");
     if (st != BQM_OK) return st;
   }
-  perm_scan<<<1, 1024, 0, s>>>(counts_ws, nchunks, E, offsets, bm, tile_off);
+  perm_scan<<<1, 1024, 0, s>>>(counts_ws, nchunks, E, offsets, bm, tile_off, bm2, tile_off2);
   bqm_status st = launch_status("perm_scan");
   if (st != BQM_OK) return st;
   if (R > 0) {
@@ -270,5 +278,5 @@ extern "C" bqm_status bqm_permute(const int32_t *topk_idx, int64_t T, int32_t E,
                 "bqm_permute: pointer not 16-byte aligned");
   }
   return permute_launch(topk_idx, R, E, perm, inv, offsets, reinterpret_cast<int32_t *>(ws), 0,
-                        nullptr, as_stream(stream));
+                        nullptr, 0, nullptr, as_stream(stream));
 }

@@ -109,13 +109,17 @@ def test_small_shared_lora_a_nf4_w4a4_colwise():
 
 
 def test_small_batches():
-    # decode-sized batches, where most row tiles hold one or two valid 32-row tiles:
-    # T = 8 over 64 experts with k = 8; partial column tiles at T = 40; 100 rows per
-    # expert; and T = 256 with the shared-A LoRA
+    # decode-sized batches (at most 32 routed rows per expert on average: the forward
+    # runs the 64-row tile configuration), where most row tiles hold one or two valid
+    # 32-row tiles: T = 8 over 64 experts with k = 8; partial column tiles at T = 40;
+    # 100 rows per expert (the 256-row tiles again); T = 256 with the shared-A LoRA;
+    # NVFP4 activations; LoRA rank 72 (masked K tail of the up-projection segment)
     compare_full(small("dec8", T=8, E=64, k=8, r=16), lora_scale=0.5)
     compare_full(small("dec_odd", H=320, I=192, T=40, E=12))
     compare_full(small("dec_rows", T=200, E=4, k=2, r=8))
     compare_full(small("dec256", T=256, E=32, k=4, shared_a=True))
+    compare_full(small("dec_w4a4", act_quant=True, H=768, I=384, T=64, E=16, k=4))
+    compare_full(small("dec_r72", r=72, T=60, E=16, k=4), lora_scale=0.5)
 
 
 def test_tiny_workload():
@@ -162,6 +166,8 @@ def sampled_full(shape, tokens, lora_experts):
     log(f"full-size {shape.name}: generating inputs on the device")
     inp = synth.layer_inputs(shape, device=dev)
     g = gpu_layer(inp, dev)
+    if lora_experts == "first":
+        lora_experts = [int(g["idx"][tokens[0], 0])]
     log(f"  GPU layer done; oracle on tokens {tokens} and experts {lora_experts}")
     h = HostInputs(inp)
     o = oracle_layer(h, tokens=tokens, lora_experts=lora_experts)
@@ -194,6 +200,13 @@ def test_full_qwen_w4a4_sampled():
     # resolve_w4a4_alternatives).  24 tokens (192 routed rows) are sampled.
     toks = list(range(0, 8192, 8192 // 24))[:24]
     sampled_full(synth.QWEN, tokens=toks, lora_experts=[100])
+
+
+def test_full_glm_decode_batch_sampled():
+    # the GLM shape at T = 64 (about two rows per hit expert), as the decode-shaped
+    # forward is timed: two tokens' rows and the LoRA gradients of token 0's first expert
+    shape = dataclasses.replace(synth.GLM, T=64, name="glm_t64")
+    sampled_full(shape, tokens=[0, 41], lora_experts="first")
 
 
 def test_full_glm_nf4_sampled():
