@@ -211,8 +211,10 @@ def stage_bytes(s):
         "combine_dgrad": R * H * 2 + T * H * 2 + R * 4,
         "dtopk": T * H * 2 + R * H * 2 + R * 8,
         "lora_grad": R * (2 * I + H + H + I) * 2 + 4 * uv + R * 4 + E * r * (2 * H + 3 * I) * 4,
-        "act_quant_x": T * H * (2 + 0.5 + 1 / 16) + T * 4,
-        "act_quant_a": R * I * (2 + 0.5 + 1 / 16) + R * 4,
+        # per-token NVFP4 of x and a: read bf16, write codes, scales, s_dec and the bf16
+        # rows of val * sb the W4A4 GEMMs multiply (one pass)
+        "act_quant_x": T * H * (2 + 0.5 + 1 / 16 + 2) + T * 4,
+        "act_quant_a": R * I * (2 + 0.5 + 1 / 16 + 2) + R * 4,
     }
 
 

@@ -13,9 +13,11 @@ bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *pe
                           int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off, int bm2,
                           int32_t *tile_off2, hipStream_t s);
 
-// NVFP4 codes and E4M3 scales of n elements (n % 16 == 0) -> bf16 val * sb, exact
-// (quant.hip): the activation rows of the W4A4 GEMMs, whose per-row s_dec is applied
-// to the accumulator.
-bqm_status nvfp4_expand(const uint8_t *codes, const uint8_t *scales, int64_t n, uint16_t *y, hipStream_t s);
+// Per-token NVFP4 (Four-Over-Six) of n_rows bf16 rows of cols elements (cols % 16 == 0,
+// 16-byte aligned pointers), and in the same pass the rows of val * sb in bf16, exact
+// (quant.hip): the activation rows of the W4A4 GEMMs, whose per-row s_dec is applied to
+// the accumulator.
+bqm_status nvfp4_quantize_rows_expand(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_t *codes,
+                                      uint8_t *scales, float *s_dec, uint16_t *expanded, hipStream_t s);
 
 }  // namespace bqm

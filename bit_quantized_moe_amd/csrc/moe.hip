@@ -1032,14 +1032,16 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
     int64_t w = b_row_of_col<EPI, BN>(wn * TN * 32 + tn * 32 + (lane & 31), nt, N, I);
     wr[tn] = w < 0 ? 0 : w;
   }
+  // the loads of the first two steps are in flight together (K = 2r: one wait, not two);
+  // step ks + 2 is loaded into the registers step ks has finished with
   LoraRegs<TMA> r[2];
   lora_load<EPI>(s, arow, bsrc, wr, 0, lane, r[0]);
+  if (nk > 1) lora_load<EPI>(s, arow, bsrc, wr, 1, lane, r[1]);
   for (int ks = 0; ks < nk; ks += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       if (ks + h >= nk) break;
       a_store<A_ROWS, TMA>(sm.a[h], r[h].a);
-      if (ks + h + 1 < nk) lora_load<EPI>(s, arow, bsrc, wr, ks + h + 1, lane, r[h ^ 1]);
       __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -1047,6 +1049,7 @@ __device__ __forceinline__ void seg_lora(const Seg &s, int e, int nt, int N, int
         a_frags<TMA>(sm.a[h], kk, row0, lane, af);
         mfmas<VT_DYN, TMA>(af, r[h].b[kk], vt, acc);
       }
+      if (ks + h + 2 < nk) lora_load<EPI>(s, arow, bsrc, wr, ks + h + 2, lane, r[h]);
     }
   }
   __syncthreads();
@@ -2457,22 +2460,12 @@ inline void mark(const bqm_moe_desc *d, int stage, int end, hipStream_t s) {
     mark(d, st, 1, s);            \
   } while (0)
 
-// rows [n_rows, cols] -> per-row NVFP4 (Four-Over-Six) into the given buffers, then the
+// rows [n_rows, cols] -> per-row NVFP4 (Four-Over-Six) into the given buffers, and the
 // rows of val * sb in bf16 (exact) that the forward GEMMs multiply, their per-row s_dec
-// applied to the accumulator
+// applied to the accumulator (one pass: 4-bitter page, Method)
 bqm_status quantize_rows(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_t *codes, uint8_t *scales, float *sd,
                          uint16_t *expanded, hipStream_t s) {
-  bqm_qtensor q{};
-  q.fmt = BQM_FMT_NVFP4;
-  q.scale_mode = BQM_SCALE_PER_ROW;
-  q.n_mat = 1;
-  q.rows = n_rows;
-  q.cols = cols;
-  q.codes = codes;
-  q.scales = scales;
-  q.s_dec = sd;
-  BQM_TRY(bqm_quantize_nvfp4(x, 1, nullptr, &q, nullptr, 0, s));
-  return nvfp4_expand(codes, scales, n_rows * cols, expanded, s);
+  return nvfp4_quantize_rows_expand(x, n_rows, cols, codes, scales, sd, expanded, s);
 }
 
 // The forward GEMMs read NF4 absmax as FP32: a nested stack's absmax' is expanded into

@@ -302,13 +302,22 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_tensor(
   }
 }
 
+// bf16 pair P (elements 2P, 2P+1) of a code word times its block scale: exact
+template <int P>
+__device__ __forceinline__ uint32_t nvfp4_val_sb(uint32_t c, float sb) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, P);
+  return pack_bf16_rne(v.x * sb, v.y * sb);
+}
+
 // Per-row quantizer: one wave per row (the per-token activation scale, computed
-// across the row in the same kernel).  rows_total = n_mat * rows.
-template <int kMode>
+// across the row in the same kernel).  rows_total = n_mat * rows.  kExp: the same
+// pass also writes each block's values times its block scale as bf16 (exact), the
+// rows the W4A4 GEMMs multiply (their per-row s_dec goes on the accumulator).
+template <int kMode, bool kExp = false>
 __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
     const uint4 *__restrict__ x, int64_t rows_total, int64_t blocks_per_row,
     const float *__restrict__ s_dec_in, float denom, uint2 *__restrict__ codes,
-    uint8_t *__restrict__ scales, float *__restrict__ s_dec_out) {
+    uint8_t *__restrict__ scales, float *__restrict__ s_dec_out, uint4 *__restrict__ expanded = nullptr) {
   __shared__ float rcp[128];
   fill_rcp(rcp);
   const int lane = threadIdx.x & 63;
@@ -341,6 +350,14 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
     uint32_t sb = quant_block16<kMode>(w, s_enc, s_dec, rcp, lo, hi);
     codes[row * blocks_per_row + blk] = make_uint2(lo, hi);
     scales[row * blocks_per_row + blk] = (uint8_t)sb;
+    if constexpr (kExp) {
+      const float sbf = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
+      uint4 *y = expanded + 2 * (row * blocks_per_row + blk);
+      y[0] = make_uint4(nvfp4_val_sb<0>(lo, sbf), nvfp4_val_sb<1>(lo, sbf), nvfp4_val_sb<2>(lo, sbf),
+                        nvfp4_val_sb<3>(lo, sbf));
+      y[1] = make_uint4(nvfp4_val_sb<0>(hi, sbf), nvfp4_val_sb<1>(hi, sbf), nvfp4_val_sb<2>(hi, sbf),
+                        nvfp4_val_sb<3>(hi, sbf));
+    }
   }
 }
 
@@ -878,11 +895,16 @@ extern "C" bqm_status bqm_nf4_nest(const bqm_qtensor *plain, bqm_qtensor *nested
 }
 
 namespace bqm {
-// Per-row NVFP4 codes -> bf16 rows of val * sb (no s_dec), n elements.
-bqm_status nvfp4_expand(const uint8_t *codes, const uint8_t *scales, int64_t n, uint16_t *y, hipStream_t s) {
-  if (n == 0) return BQM_OK;
-  nvfp4_dequant<false><<<dq_grid(n), kThreads, 0, s>>>(reinterpret_cast<const uint32_t *>(codes), scales, nullptr,
-                                                       n / 8, n / 8, reinterpret_cast<uint4 *>(y));
-  return launch_status("nvfp4_expand");
+// Per-token NVFP4 with Four-Over-Six of n_rows rows (cols % 16 == 0, 16-byte aligned
+// pointers): codes, scales and per-row s_dec, and in the same pass the bf16 rows of
+// val * sb (no s_dec), exact.
+bqm_status nvfp4_quantize_rows_expand(const uint16_t *x, int64_t n_rows, int64_t cols, uint8_t *codes,
+                                      uint8_t *scales, float *s_dec, uint16_t *expanded, hipStream_t s) {
+  if (n_rows * cols == 0) return BQM_OK;
+  const int grid = (int)cdiv(n_rows, kThreads / 64);
+  nvfp4_quant_rows<kFosScaled, true><<<grid, kThreads, 0, s>>>(
+      reinterpret_cast<const uint4 *>(x), n_rows, cols / 16, nullptr, 6.0f * 256.0f, reinterpret_cast<uint2 *>(codes),
+      scales, s_dec, reinterpret_cast<uint4 *>(expanded));
+  return launch_status("nvfp4_quant_rows (expanded)");
 }
 }  // namespace bqm
