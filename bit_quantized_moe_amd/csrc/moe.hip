@@ -1924,52 +1924,64 @@ __global__ void __launch_bounds__(NTHR, 2) gemm_lora_proj(GemmParams p) {
 
 // LoRA-A projection for a few rows per expert (decode-sized batches): out[row][n] =
 // osc * sum_k A_row[k] * B[e][n][k] (B K-major [N][K]) stored as hi/lo bf16 pairs like
-// the tiled projection above.  A workgroup takes expert e and 16 outputs for all of the
-// expert's rows, each wave 4 of them; the lanes split K in 8-element pieces and add
-// their FP32 partial sums in a fixed butterfly.  The tiled kernel walks K in 64-deep
-// steps with one 256-row tile per expert, which leaves most of the GPU idle when the
-// batch is a few tokens.
+// the tiled projection above.  A workgroup takes expert e and 4 outputs for all of the
+// expert's rows, one per wave; the lanes split K in 8-element pieces (four 512-wide
+// slices' loads in flight at a time) and add their FP32 partial sums in a fixed
+// butterfly.  The tiled kernel walks K in 64-deep steps with one 256-row tile per
+// expert, which leaves most of the GPU idle when the batch is a few tokens.
 template <int ASRC>
 __global__ void __launch_bounds__(256) lora_proj_rows(GemmParams p) {
   const int e = blockIdx.y;
   const int rb = p.offsets[e], n_e = p.offsets[e + 1] - rb;
   if (n_e == 0) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n0 = blockIdx.x * 16 + 4 * w;
+  const int lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);  // one output column per wave
+  if (n >= p.N) return;
   const Seg &s = p.s1;
   const int K = s.K;
-  const uint16_t *bmat = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
+  const uint16_t *brow = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + (int64_t)n * s.b_cols;
   const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
   for (int i = 0; i < n_e; ++i) {
     const int64_t arow = ASRC == A_GATHER ? (int64_t)(p.perm[rb + i] / p.k) : (int64_t)(rb + i);
     const uint16_t *ar = reinterpret_cast<const uint16_t *>(s.a) + arow * s.a_ld;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k0 = 8 * lane; k0 < K; k0 += 512) {
-      const uint4 xa = *reinterpret_cast<const uint4 *>(ar + k0);
-      const uint32_t xv[4] = {xa.x, xa.y, xa.z, xa.w};
+    float acc = 0.0f;  // this lane's k = 8 lane + 512 j .. +8, summed in order of k
+    int k0 = 8 * lane;
+    // four 512-wide K slices at a time: their loads are in flight together
+    for (; k0 + 3 * 512 < K; k0 += 4 * 512) {
+      uint4 xa[4], ba[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (n0 + j < p.N) {
-          const uint4 ba = *reinterpret_cast<const uint4 *>(bmat + (int64_t)(n0 + j) * s.b_cols + k0);
-          const uint32_t bv[4] = {ba.x, ba.y, ba.z, ba.w};
+      for (int u = 0; u < 4; ++u) {
+        xa[u] = *reinterpret_cast<const uint4 *>(ar + k0 + 512 * u);
+        ba[u] = *reinterpret_cast<const uint4 *>(brow + k0 + 512 * u);
+      }
 #pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            acc[j] += bf16_lo(xv[h]) * bf16_lo(bv[h]);
-            acc[j] += bf16_hi(xv[h]) * bf16_hi(bv[h]);
-          }
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t xv[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w}, bv[4] = {ba[u].x, ba[u].y, ba[u].z, ba[u].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc += bf16_lo(xv[h]) * bf16_lo(bv[h]);
+          acc += bf16_hi(xv[h]) * bf16_hi(bv[h]);
         }
       }
     }
+    for (; k0 < K; k0 += 512) {
+      const uint4 xa = *reinterpret_cast<const uint4 *>(ar + k0);
+      const uint4 ba = *reinterpret_cast<const uint4 *>(brow + k0);
+      const uint32_t xv[4] = {xa.x, xa.y, xa.z, xa.w}, bv[4] = {ba.x, ba.y, ba.z, ba.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int h = 0; h < 4; ++h) {
+        acc += bf16_lo(xv[h]) * bf16_lo(bv[h]);
+        acc += bf16_hi(xv[h]) * bf16_hi(bv[h]);
+      }
+    }
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) acc[j] += __shfl_xor(acc[j], o, 64);
-    if (lane < 4 && n0 + lane < p.N) {
-      const float val = (lane == 0 ? acc[0] : lane == 1 ? acc[1] : lane == 2 ? acc[2] : acc[3]) * osc;
+    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (lane == 0) {
+      const float val = acc * osc;
       const uint32_t hb = f32_to_bf16(val);
       const float lo2 = val - __uint_as_float(hb << 16);
-      p.out0[(int64_t)(rb + i) * 2 * p.N + n0 + lane] = (uint16_t)hb;
-      p.out0[(int64_t)(rb + i) * 2 * p.N + p.N + n0 + lane] = (uint16_t)f32_to_bf16(lo2);
+      p.out0[(int64_t)(rb + i) * 2 * p.N + n] = (uint16_t)hb;
+      p.out0[(int64_t)(rb + i) * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
     }
   }
 }
@@ -2413,7 +2425,7 @@ template <int ASRC, bool BNM>
 bqm_status launch_lp(const GemmParams &p, int64_t R, hipStream_t s, const char *what, int64_t T = -1) {
   static_assert(lp::BM == BM, "tile offsets are computed for BM rows");
   if (!BNM && T >= 0 && T <= kFewTokens) {
-    lora_proj_rows<ASRC><<<dim3((unsigned)cdiv(p.N, 16), (unsigned)p.E), 256, 0, s>>>(p);
+    lora_proj_rows<ASRC><<<dim3((unsigned)cdiv(p.N, 4), (unsigned)p.E), 256, 0, s>>>(p);
     return launch_status(what);
   }
   const int grid = gemm_grid(R, p.E, p.NT);

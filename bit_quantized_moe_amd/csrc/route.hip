@@ -210,6 +210,84 @@ __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ i
   }
 }
 
+// One chunk (R <= kChunk, decode-sized batches): the histogram, the scans and the
+// ordered scatter of the three passes above in one launch of one workgroup.  Expert
+// counts, offsets, tile prefixes, perm and inv are those of the three passes.
+__global__ void __launch_bounds__(1024) perm_one(const int32_t *__restrict__ idx, int R, int E,
+                                                 int32_t *__restrict__ offsets, int bm, int32_t *__restrict__ tile_off,
+                                                 int bm2, int32_t *__restrict__ tile_off2, int32_t *__restrict__ perm,
+                                                 int32_t *__restrict__ inv) {
+  extern __shared__ int32_t cnt[];  // E + 1 buckets
+  __shared__ int32_t wsum[16][3];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int e = t; e <= E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (int f = t; f < R; f += 1024) atomicAdd(&cnt[bucket_of(idx[f], E)], 1);
+  __syncthreads();
+  const int e = t;
+  const int32_t run = e < E ? cnt[e] : 0;
+  const int32_t tiles = (e < E && bm > 0) ? (run + bm - 1) / bm : 0;
+  const int32_t tiles2 = (e < E && bm2 > 0) ? (run + bm2 - 1) / bm2 : 0;
+  int32_t v = run, u = tiles, u2 = tiles2;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t tv = __shfl_up(v, off, 64), tu = __shfl_up(u, off, 64), tu2 = __shfl_up(u2, off, 64);
+    if (lane >= off) {
+      v += tv;
+      u += tu;
+      u2 += tu2;
+    }
+  }
+  if (lane == 63) {
+    wsum[wave][0] = v;
+    wsum[wave][1] = u;
+    wsum[wave][2] = u2;
+  }
+  __syncthreads();
+  int32_t bv = 0, bu = 0, bu2 = 0;
+  for (int q = 0; q < wave; ++q) {
+    bv += wsum[q][0];
+    bu += wsum[q][1];
+    bu2 += wsum[q][2];
+  }
+  const int32_t ex = bv + v - run, ext = bu + u - tiles, ext2 = bu2 + u2 - tiles2;
+  if (e < E) {
+    offsets[e] = ex;
+    if (tile_off) tile_off[e] = ext;
+    if (tile_off2) tile_off2[e] = ext2;
+  }
+  if (e == E - 1) {
+    offsets[E] = ex + run;
+    if (tile_off) tile_off[E] = ext + tiles;
+    if (tile_off2) tile_off2[E] = ext2 + tiles2;
+  }
+  __syncthreads();  // every count has been read
+  if (e < E) cnt[e] = ex;
+  if (e == E - 1) cnt[E] = ex + run;  // the dropped pairs follow every expert's rows
+  __syncthreads();
+  // wave 0 places the pairs in order, 64 at a time (equal experts ranked by lane)
+  const uint64_t below = (1ull << lane) - 1ull, upto = lane == 63 ? ~0ull : (2ull << lane) - 1ull;
+  for (int s0 = 0; s0 < R; s0 += 64) {
+    int pos = 0, bk = -1;
+    bool last = false;
+    if (wave == 0) {
+      const int f = s0 + lane;
+      bk = f < R ? bucket_of(idx[f], E) : -1;
+      const uint64_t same = lanes_equal(bk + 1);
+      const int rank = __popcll(same & below);
+      last = (same & ~upto) == 0ull;
+      if (bk >= 0) pos = cnt[bk] + rank;
+    }
+    __syncthreads();
+    if (wave == 0 && bk >= 0) {
+      perm[pos] = s0 + lane;
+      inv[s0 + lane] = pos;
+      if (last) cnt[bk] = pos + 1;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int64_t R, int E) {
@@ -219,6 +297,11 @@ size_t permute_ws_bytes(int64_t R, int E) {
 bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
                           int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off, int bm2,
                           int32_t *tile_off2, hipStream_t s) {
+  if (R > 0 && R <= kChunk) {
+    perm_one<<<1, 1024, (E + 1) * sizeof(int32_t), s>>>(topk_idx, (int)R, E, offsets, bm, tile_off, bm2, tile_off2,
+                                                         perm, inv);
+    return launch_status("perm_one");
+  }
   const int nchunks = (int)cdiv(R, kChunk);
   if (R > 0) {
     perm_hist<<<nchunks, 256, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws);

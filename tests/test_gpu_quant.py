@@ -298,11 +298,13 @@ def test_nvfp4_dequantize_shapes(shape, per_row):
 
 # (the permutation ranks equal experts within each 64-pair group by lane: E = 16 with
 # ties puts many equal experts in every group; E = 1000 is not a multiple of the
-# 64-lane scan width; E = 1024 is the largest expert count, several 2048-pair chunks)
+# 64-lane scan width; E = 1024 is the largest expert count, several 2048-pair chunks;
+# up to 2048 routed pairs run the one-workgroup form, ties and E = 1024 included)
 @pytest.mark.parametrize("T,E,k,kind", [(64, 8, 2, "normal"), (1000, 256, 8, "uniform"),
                                         (333, 128, 8, "ties"), (50, 64, 16, "zipf"), (1, 1, 1, "normal"),
                                         (5000, 16, 2, "ties"), (700, 1000, 3, "zipf"),
-                                        (3000, 1024, 4, "uniform")])
+                                        (3000, 1024, 4, "uniform"), (300, 16, 4, "ties"),
+                                        (200, 1024, 8, "uniform"), (256, 1000, 8, "zipf")])
 def test_route_and_permute_bit_exact(T, E, k, kind):
     import torch
     dev = gpu()
