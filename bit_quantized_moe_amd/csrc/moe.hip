@@ -2006,6 +2006,11 @@ struct WgradParams {
   // experts; C is then [split][M][N] partial sums
   int split;
   int E;
+  // per-expert outputs: row chunks (see wgrad_chunks) and the partial sums of the
+  // experts with more than one chunk
+  const int32_t *chunk_off, *slot_off;
+  int chunk;
+  float *part;
 };
 
 constexpr int WB = 64;  // wgrad tile (M and N) and row step
@@ -2094,22 +2099,98 @@ __device__ __forceinline__ void wgrad_rows(const WgradParams &p, int rb, int n_e
   }
 }
 
-// blockIdx.y: the expert, C[e] = c_scale[e] times its sum; or (SPLIT) the part e
-// of the experts, [e E / split, (e+1) E / split), whose sums times their c_scale
-// are added in FP32 in expert order into C[e], a partial sum of the one [M, N]
-// output (the second accumulator lives only in this variant: the per-expert one
-// stays within the registers of eight workgroups per CU)
+// Row chunks of the per-expert gradients: an expert's rows are cut into chunks of
+// p.chunk rows, one workgroup per chunk and output tile, so that the few experts with
+// many rows under skewed routing do not keep one long K loop running after the rest.
+// chunk_off[e] is the prefix of the chunk counts max(1, ceil(n_e / chunk)) (an expert
+// without rows keeps one chunk, which writes its zero gradient); slot_off[e] the prefix
+// of the counts of the experts with more than one chunk, whose chunks write FP32
+// partial sums to slots slot_off[e] + j, added in chunk order by wgrad_sum_chunks.
+// multi[0] is the number of such experts and multi[1 + i] the i-th of them.  One
+// workgroup of 1024 threads, E <= 1024, inclusive scans in LDS.
+__global__ void __launch_bounds__(1024) wgrad_chunks(const int32_t *__restrict__ offsets, int E, int chunk,
+                                                     int32_t *__restrict__ chunk_off, int32_t *__restrict__ slot_off,
+                                                     int32_t *__restrict__ multi) {
+  __shared__ int32_t a[1024], b[1024], m[1024];
+  const int t = threadIdx.x;
+  int nc = 0, ns = 0;
+  if (t < E) {
+    const int n = offsets[t + 1] - offsets[t];
+    nc = n > chunk ? (n + chunk - 1) / chunk : 1;
+    ns = nc > 1 ? nc : 0;
+  }
+  a[t] = nc;
+  b[t] = ns;
+  m[t] = ns > 0;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int va = t >= d ? a[t - d] : 0, vb = t >= d ? b[t - d] : 0, vm = t >= d ? m[t - d] : 0;
+    __syncthreads();
+    a[t] += va;
+    b[t] += vb;
+    m[t] += vm;
+    __syncthreads();
+  }
+  if (t == 0) {
+    chunk_off[0] = slot_off[0] = 0;
+    multi[0] = m[1023];
+  }
+  if (t < E) {
+    chunk_off[t + 1] = a[t];
+    slot_off[t + 1] = b[t];
+    if (ns > 0) multi[m[t]] = t;  // 1 + (its rank among them)
+  }
+}
+
+// C[e] = c_scale[e] times the sum of expert e's chunk partials in chunk order, for the
+// experts with more than one chunk: blockIdx.y = the rank of e among them (multi, see
+// wgrad_chunks), a grid-stride loop over the n4 float4 of the output
+__global__ void __launch_bounds__(NTHR) wgrad_sum_chunks(const float4 *__restrict__ part,
+                                                         const int32_t *__restrict__ chunk_off,
+                                                         const int32_t *__restrict__ slot_off,
+                                                         const int32_t *__restrict__ multi,
+                                                         const float *__restrict__ c_scale, int64_t n4,
+                                                         float4 *__restrict__ C) {
+  if ((int)blockIdx.y >= multi[0]) return;
+  const int e = multi[1 + blockIdx.y];
+  const int nch = chunk_off[e + 1] - chunk_off[e];
+  const float cs = c_scale ? c_scale[e] : 1.0f;
+  const float4 *pe = part + (int64_t)slot_off[e] * n4;
+  for (int64_t i = (int64_t)blockIdx.x * NTHR + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NTHR) {
+    float4 acc = pe[i];
+    for (int j = 1; j < nch; ++j) {
+      const float4 v = pe[(int64_t)j * n4 + i];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    acc.x *= cs;
+    acc.y *= cs;
+    acc.z *= cs;
+    acc.w *= cs;
+    C[(int64_t)e * n4 + i] = acc;
+  }
+}
+
+// blockIdx.y: a row chunk of one expert (see wgrad_chunks): C[e] = c_scale[e] times
+// its sum when the expert has one chunk, else the chunk's partial sum; or (SPLIT)
+// the part e of the experts, [e E / split, (e+1) E / split), whose sums times their
+// c_scale are added in FP32 in expert order into C[e], a partial sum of the one
+// [M, N] output (the second accumulator lives only in this variant: the per-expert
+// one stays within the registers of eight workgroups per CU)
 template <bool SPLIT>
 __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ps[WB * WS];
   __shared__ __attribute__((aligned(16))) uint16_t Qs[WB * WS];
-  const int e = blockIdx.y;
+  int e = blockIdx.y;
   const int ntn = (p.N + WB - 1) / WB;
   const int mt = blockIdx.x / ntn, ntile = blockIdx.x % ntn;
   const int m0 = mt * WB, n0 = ntile * WB;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   f32x16 acc;
+  float *out = nullptr;  // this workgroup's [M, N] output (set below)
   if constexpr (SPLIT) {
     const int e0 = (int)((int64_t)e * p.E / p.split), e1 = (int)((int64_t)(e + 1) * p.E / p.split);
     f32x16 tot;
@@ -2123,18 +2204,36 @@ __global__ void __launch_bounds__(NTHR) lora_wgrad(WgradParams p) {
       for (int v = 0; v < 16; ++v) tot[v] += acc[v] * cs;
     }
     acc = tot;
+    out = p.C + (int64_t)e * p.M * p.N;
   } else {
-    const int rb = p.offsets[e];
-    wgrad_rows(p, rb, p.offsets[e + 1] - rb, m0, n0, Ps, Qs, acc);
-    const float cs = p.c_scale ? p.c_scale[e] : 1.0f;
+    const int c = blockIdx.y;
+    if (c >= p.chunk_off[p.E]) return;
+    int lo = 0, hi = p.E;  // the expert of chunk c: largest e with chunk_off[e] <= c
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.chunk_off[mid] <= c)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    e = lo;
+    const int j = c - p.chunk_off[e], nch = p.chunk_off[e + 1] - p.chunk_off[e];
+    const int rb = p.offsets[e], r0 = j * p.chunk;
+    wgrad_rows(p, rb + r0, min(p.chunk, p.offsets[e + 1] - rb - r0), m0, n0, Ps, Qs, acc);
+    if (nch > 1) {
+      out = p.part + (int64_t)(p.slot_off[e] + j) * p.M * p.N;
+    } else {
+      const float cs = p.c_scale ? p.c_scale[e] : 1.0f;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] *= cs;
+      for (int v = 0; v < 16; ++v) acc[v] *= cs;
+      out = p.C + (int64_t)e * p.M * p.N;
+    }
   }
 #pragma unroll
   for (int vv = 0; vv < 16; ++vv) {
     const int m = m0 + wm * 32 + 8 * (vv >> 2) + 4 * (lane >> 5) + (vv & 3);
     const int n = n0 + wn * 32 + (lane & 31);
-    if (m < p.M && n < p.N) p.C[((int64_t)e * p.M + m) * p.N + n] = acc[vv];
+    if (m < p.M && n < p.N) out[(int64_t)m * p.N + n] = acc[vv];
   }
 }
 
@@ -2217,12 +2316,16 @@ __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict_
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t perm, inv, off, tile_off, tile_off_n, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
-      vgu, dxr, part, absx;
+      vgu, dxr, part, wchunk, wpart, absx;
   size_t total;
 };
 
 // parts of the experts whose shared-A gradient sums run side by side
 int lora_split(int E) { return E < 64 ? E : 64; }
+
+// rows per chunk of the per-expert LoRA gradients (wgrad_chunks): 2048, raised for very
+// large batches so that the chunks (at most E + R / chunk) fit the grid's y dimension
+int wgrad_chunk(int64_t R) { return (int)std::max<int64_t>(2048, cdiv(R, 32768)); }
 
 Layout layout(const bqm_moe_desc *d) {
   const size_t T = d->T, H = d->H, I = d->I, E = d->E, k = d->k, r = d->r;
@@ -2261,6 +2364,10 @@ Layout layout(const bqm_moe_desc *d) {
   L.dxr = take(R * H * 2);
   // shared-A gradient: lora_split(R) partial sums of [r, max(H, I)] in FP32
   L.part = take(d->lora_shared_a && r > 0 ? (size_t)lora_split((int)E) * r * (H > I ? H : I) * 4 : 0);
+  // per-expert gradients: chunk prefixes and the chunk partial sums (at most 2 R / chunk
+  // of them, each at most [r, max(2I, H)])
+  L.wchunk = take(r > 0 ? 3 * (E + 1) * 4 : 0);
+  L.wpart = take(r > 0 ? 2 * (size_t)cdiv((int64_t)R, wgrad_chunk((int64_t)R)) * r * (2 * I > H ? 2 * I : H) * 4 : 0);
   // nested NF4: FP32 absmax' of the larger stack (gate_up), rebuilt before each forward GEMM
   const bool nested = d->w_gu.fmt == BQM_FMT_NF4 && (d->w_gu.nested || d->w_dn.nested);
   L.absx = take(nested ? E * 2 * I * H / 64 * 4 : 0);
@@ -2779,6 +2886,20 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
   p.k = d->k;
   p.E = d->E;
   const int split = lora_split(d->E);
+  const int64_t R = d->T * d->k;
+  p.chunk = wgrad_chunk(R);
+  int32_t *chunk_off = w.at<int32_t>(w.L.wchunk);
+  p.chunk_off = chunk_off;
+  p.slot_off = chunk_off + d->E + 1;
+  p.part = w.at<float>(w.L.wpart);
+  const int32_t *multi = chunk_off + 2 * (d->E + 1);
+  wgrad_chunks<<<1, 1024, 0, s>>>(p.offsets, d->E, p.chunk, chunk_off, chunk_off + d->E + 1,
+                                  chunk_off + 2 * (d->E + 1));
+  BQM_TRY(launch_status("lora grad chunks"));
+  // bounds: sum over e of max(1, ceil(n_e / chunk)) <= E + R / chunk chunks, and at most
+  // R / chunk experts have more than one
+  const unsigned n_chunks = (unsigned)(d->E + R / p.chunk);
+  const unsigned n_multi = (unsigned)std::max<int64_t>(1, std::min<int64_t>(d->E, R / p.chunk));
   // shared: C is the one [M, N] gradient of a shared A, summed over the experts in
   // `split` parts (partials in the workspace, then added in part order)
   auto go = [&](int M, int N, const uint16_t *P, int64_t pld, int pg, int sp, const uint16_t *Q, int64_t qld, int qg,
@@ -2795,10 +2916,17 @@ extern "C" bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, co
     p.c_scale = cs;
     p.split = shared ? split : 0;
     p.C = shared ? w.at<float>(w.L.part) : C;
-    dim3 grid((unsigned)(cdiv(M, WB) * cdiv(N, WB)), (unsigned)(shared ? split : d->E));
+    dim3 grid((unsigned)(cdiv(M, WB) * cdiv(N, WB)), shared ? (unsigned)split : n_chunks);
     if (shared) lora_wgrad<true><<<grid, NTHR, 0, s>>>(p);
     else lora_wgrad<false><<<grid, NTHR, 0, s>>>(p);
     BQM_TRY(launch_status(what));
+    if (!shared) {
+      const int64_t n4 = (int64_t)M * N / 4;
+      wgrad_sum_chunks<<<dim3((unsigned)std::min<int64_t>(cdiv(n4, NTHR), 64), n_multi), NTHR, 0, s>>>(
+          reinterpret_cast<const float4 *>(p.part), p.chunk_off, p.slot_off, multi, cs, n4,
+          reinterpret_cast<float4 *>(C));
+      BQM_TRY(launch_status(what));
+    }
     if (shared) {
       const int64_t n4 = (int64_t)M * N / 4;
       sum_parts<<<(unsigned)cdiv(n4, NTHR), NTHR, 0, s>>>(reinterpret_cast<const float4 *>(p.C), split, n4,

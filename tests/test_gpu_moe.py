@@ -122,6 +122,35 @@ def test_small_batches():
     compare_full(small("dec_r72", r=72, T=60, E=16, k=4), lora_scale=0.5)
 
 
+def test_few_rows_activation_dynamic_range():
+    # a decode-sized batch (the 64-row tile configuration) whose tokens are scaled by
+    # 2^40 and 2^-40, one all-zero token and one token whose elements span 2^-30 .. 2^30,
+    # compared row by row (the whole-array norms would only see the largest row)
+    import torch
+    dev = gpu()
+    shape = small("dec_range", T=24, E=16, k=4, r=16)
+    inp = synth.layer_inputs(shape, device="cpu")
+    x = inp.x.float()
+    x[0] *= 2.0 ** 40
+    x[1] *= 2.0 ** -40
+    x[2] = 0.0
+    x[3] *= torch.exp2(torch.linspace(-30.0, 30.0, shape.H).round())
+    inp.x = x.to(torch.bfloat16)   # power-of-two factors: exact in bf16
+    log(f"layer {shape} with rows scaled by 2^40, 2^-40, 0 and 2^-30..2^30")
+    g = gpu_layer(inp, dev)
+    o = oracle_layer(HostInputs(inp))
+    assert (g["idx"].cpu().numpy() == o["idx"]).all(), "routing indices"
+    out, dx = np_f32(g["out"]), np_f32(g["dx"])
+    assert (out[2] == 0).all(), "an all-zero token gives an all-zero output"
+    for t in range(shape.T):
+        if t != 2:
+            assert_close(out[t], o["out"][t], f"out row {t}")
+        assert_close(dx[t], o["dx"][t], f"dx row {t}")
+    assert_close(g["dtw"].cpu().numpy(), o["dtw"], "dtopk_w")
+    for name, ref in zip(("dA_gu", "dB_gu", "dA_dn", "dB_dn"), o["lora"]):
+        assert_close(g[name].cpu().numpy(), ref, name)
+
+
 def test_tiny_workload():
     compare_full(synth.TINY)
 
@@ -281,6 +310,16 @@ def test_big_experts_nvfp4_every_row():
 def test_big_experts_w4a4_every_row():
     g, o = compare_full(big_experts("big_w4a4", act_quant=True))
     _check_rows_per_expert(o, 8, 600, 900)
+
+
+def test_lora_gradients_over_row_chunks():
+    # the per-expert LoRA gradients cut an expert's rows into chunks of 2048 (one
+    # workgroup per chunk, partial sums added in chunk order): with k = 1 over 3 experts
+    # and 23% of the tokens pushed to expert 0, it gets about 3400 rows (two chunks), the
+    # others about 1800 (one); every row of the layer compared
+    g, o = compare_full(small("wgrad_chunks", E=3, k=1, T=7000, logits="skew", r=16))
+    counts = np.bincount(o["idx"].reshape(-1), minlength=3)
+    assert counts.max() > 2048 and counts.min() <= 2048, counts
 
 
 def test_big_experts_nf4_every_row():
