@@ -309,6 +309,28 @@ __device__ __forceinline__ uint32_t nvfp4_val_sb(uint32_t c, float sb) {
   return pack_bf16_rne(v.x * sb, v.y * sb);
 }
 
+// block `idx` (row-major over the rows) of the per-row quantizer: codes, scale and,
+// with kExp, the bf16 values times the block scale
+template <int kMode, bool kExp>
+__device__ __forceinline__ void quant_row_block(const uint32_t (&w)[8], int64_t idx, float s_enc, float s_dec,
+                                                const float *rcp, uint2 *__restrict__ codes,
+                                                uint8_t *__restrict__ scales, uint4 *__restrict__ expanded) {
+  uint32_t lo, hi;
+  const uint32_t sb = quant_block16<kMode>(w, s_enc, s_dec, rcp, lo, hi);
+  codes[idx] = make_uint2(lo, hi);
+  scales[idx] = (uint8_t)sb;
+  if constexpr (kExp) {
+    const float sbf = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
+    uint4 *y = expanded + 2 * idx;
+    y[0] = make_uint4(nvfp4_val_sb<0>(lo, sbf), nvfp4_val_sb<1>(lo, sbf), nvfp4_val_sb<2>(lo, sbf),
+                      nvfp4_val_sb<3>(lo, sbf));
+    y[1] = make_uint4(nvfp4_val_sb<0>(hi, sbf), nvfp4_val_sb<1>(hi, sbf), nvfp4_val_sb<2>(hi, sbf),
+                      nvfp4_val_sb<3>(hi, sbf));
+  }
+}
+
+constexpr int kRowKeep = 4;  // blocks per lane the per-row quantizer keeps in registers
+
 // Per-row quantizer: one wave per row (the per-token activation scale, computed
 // across the row in the same kernel).  rows_total = n_mat * rows.  kExp: the same
 // pass also writes each block's values times its block scale as bf16 (exact), the
@@ -325,6 +347,35 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
   if (row >= rows_total) return;
   const uint4 *xr = x + row * blocks_per_row * 2;
   float s_dec, s_enc;
+  // Rows of at most 64 kRowKeep blocks stay in registers between the row maximum and
+  // the quantization (each lane holds its blocks lane, lane + 64, ...): one read of
+  // the row, one memory round trip per row instead of two.
+  if (!s_dec_in && blocks_per_row <= 64 * kRowKeep) {
+    uint32_t w[kRowKeep][8];
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int j = 0; j < kRowKeep; ++j) {
+      const int64_t blk = lane + 64 * j;
+      if (blk < blocks_per_row) {
+        load_block16(xr + 2 * blk, w[j]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t a = absmax_bits_u32(w[j][i]);
+          mx = mx > a ? mx : a;
+        }
+      }
+    }
+    mx = wave_max_u(mx);
+    global_scale(__uint_as_float(mx << 16), denom, s_dec, s_enc);
+    if (lane == 0) s_dec_out[row] = s_dec;
+#pragma unroll
+    for (int j = 0; j < kRowKeep; ++j) {
+      const int64_t blk = lane + 64 * j;
+      if (blk < blocks_per_row) quant_row_block<kMode, kExp>(w[j], row * blocks_per_row + blk, s_enc, s_dec, rcp,
+                                                             codes, scales, expanded);
+    }
+    return;
+  }
   if (s_dec_in) {
     s_dec = s_dec_in[row];
     s_enc = 1.0f / s_dec;
@@ -346,18 +397,7 @@ __global__ void __launch_bounds__(kThreads) nvfp4_quant_rows(
   for (int64_t blk = lane; blk < blocks_per_row; blk += 64) {
     uint32_t w[8];
     load_block16(xr + 2 * blk, w);
-    uint32_t lo, hi;
-    uint32_t sb = quant_block16<kMode>(w, s_enc, s_dec, rcp, lo, hi);
-    codes[row * blocks_per_row + blk] = make_uint2(lo, hi);
-    scales[row * blocks_per_row + blk] = (uint8_t)sb;
-    if constexpr (kExp) {
-      const float sbf = __builtin_amdgcn_cvt_f32_fp8(sb, 0);
-      uint4 *y = expanded + 2 * (row * blocks_per_row + blk);
-      y[0] = make_uint4(nvfp4_val_sb<0>(lo, sbf), nvfp4_val_sb<1>(lo, sbf), nvfp4_val_sb<2>(lo, sbf),
-                        nvfp4_val_sb<3>(lo, sbf));
-      y[1] = make_uint4(nvfp4_val_sb<0>(hi, sbf), nvfp4_val_sb<1>(hi, sbf), nvfp4_val_sb<2>(hi, sbf),
-                        nvfp4_val_sb<3>(hi, sbf));
-    }
+    quant_row_block<kMode, kExp>(w, row * blocks_per_row + blk, s_enc, s_dec, rcp, codes, scales, expanded);
   }
 }
 
