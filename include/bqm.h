@@ -251,7 +251,8 @@ typedef struct {
  * bqm_lora_grad for this descriptor (host only).  The forward saves the
  * routing permutation, the gate/up activations h [R, 2I], a [R, I], the LoRA
  * intermediates and the expert outputs y [R, H] in it; the dgrad adds
- * dh [R, 2I] and its LoRA intermediates for bqm_lora_grad. */
+ * dh [R, 2I] and its LoRA intermediates for bqm_lora_grad, which uses the rest
+ * for partial sums (the row chunks of experts with more than 2048 rows). */
 size_t bqm_moe_workspace_size(const bqm_moe_desc *d);
 
 /* Forward: out[t] = sum_j topk_w[t,j] * y(t,j) with, for expert e = topk_idx[t,j],
@@ -300,10 +301,11 @@ bqm_status bqm_moe_dgrad_colwise(const bqm_moe_desc *d, const bqm_qtensor *w_gu_
  *   dB_dn = s (w dy)^T (a A_dn^T)  dA_dn = s (w dy B_dn)^T a
  * summed over each expert's rows, FP32 accumulation.  f32 outputs dA_gu
  * [E, r, H], dB_gu [E, 2I, r], dA_dn [E, r, I], dB_dn [E, H, r]; experts
- * without rows get zeros.  With lora_shared_a, dA_gu [r, H] and dA_dn [r, I]
- * are sums over all routed rows of every expert (the gradient of the one
- * shared matrix), added in a fixed order, so repeated calls give identical
- * bits.  Requires r > 0. */
+ * without rows get zeros.  An expert's rows are summed in chunks of 2048 whose
+ * FP32 partial sums are added in chunk order.  With lora_shared_a, dA_gu [r, H]
+ * and dA_dn [r, I] are sums over all routed rows of every expert (the gradient
+ * of the one shared matrix), added in a fixed order; either way repeated calls
+ * give identical bits.  Requires r > 0. */
 bqm_status bqm_lora_grad(const bqm_moe_desc *d, const uint16_t *x, const uint16_t *dy, void *ws,
                          size_t ws_bytes, float *dA_gu, float *dB_gu, float *dA_dn, float *dB_dn,
                          void *stream);
