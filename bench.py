@@ -394,6 +394,18 @@ def time_calls(ev, sh, fn, reps=3):
     return ev.elapsed_ms(e[0], e[1]) / reps
 
 
+def row_tiles(logits, s):
+    """256-row tiles of the grouped GEMMs under a routing: the sum over experts of
+    ceil(rows / 256), with the top-k of the logits as the library's router picks them."""
+    import torch
+    import bit_quantized_moe_amd as bqm
+    idx = torch.empty((s.T, s.k), dtype=torch.int32, device=logits.device)
+    tw = torch.empty((s.T, s.k), dtype=torch.float32, device=logits.device)
+    bqm.bqm_route(logits, s.T, s.E, s.k, 0, idx, tw)
+    n = torch.bincount(idx.reshape(-1).long(), minlength=s.E)
+    return {"tiles": int(((n + 255) // 256).sum()), "rows_min": int(n.min()), "rows_max": int(n.max())}
+
+
 def config_block(s, res, weights):
     return {"workload": s.name, "E": s.E, "H": s.H, "I": s.I, "k": s.k, "T": s.T, "r": s.r,
             "weights": weights, "act_quant": bool(s.act_quant), "routing": s.logits,
@@ -702,6 +714,17 @@ def main():
         others["glm_nvfp4_shared_lora_a"] = config_block(s_sh, r_sh, "nvfp4-4over6-rowwise, one LoRA-A for all "
                                                                      "experts, per-expert LoRA-B")
         del inp_sh
+        torch.cuda.empty_cache()
+        # the same GLM layer with every expert at exactly R / E rows: the synthetic routing's
+        # spread (446-579 rows per expert at this shape) leaves a mostly empty third 256-row
+        # tile on every expert above 512 rows, each a full pass over its weights
+        s_bal = dataclasses.replace(shape, logits="balanced", name="glm_balanced_routing")
+        inp_bal = synth.layer_inputs(s_bal, device=dev, with_weights=False)
+        r_bal = time_layer(s_bal, inp_bal, wgu, wdn, ev, sh, max(3, args.steps // 2), 2)
+        others["glm_nvfp4_balanced_routing"] = config_block(s_bal, r_bal, "nvfp4-4over6-rowwise")
+        others["glm_nvfp4_balanced_routing"]["row_tiles_256"] = {
+            "synthetic_routing": row_tiles(inp.logits, shape), "balanced_routing": row_tiles(inp_bal.logits, s_bal)}
+        del inp_bal
         torch.cuda.empty_cache()
         result["other_configs"] = others
         # the two-copy scheme (a columnwise second quantization for the dgrad) as a comparison

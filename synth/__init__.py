@@ -16,6 +16,8 @@ datasets and checkpoints are not available, these stand in for them):
 * glm_nf4  glm with NF4 weights; logits = -1.1 ln(rank_e) + Gumbel, 16 experts masked to -inf
 * skew     logits ~U(0,1) with +1 on expert 0 for the first 23% of the tokens (one
            expert with about twice the rows of the others; a parity-test recipe)
+* balanced logits 1 on experts (k t + j) mod E, j < k, and 0 elsewhere: every expert gets
+           exactly T k / E rows when E divides T k (a reference routing for timing)
 * weights  ~N(0,0.02) with a Bernoulli(0.001) outlier mask multiplied by 20
   (the quantizer workload; tiny uses no outliers), LoRA A, B ~N(0,0.01),
   activations and output gradients ~N(0,1).
@@ -42,7 +44,7 @@ class Shape:
     r: int
     act_quant: bool = False
     fmt: str = "nvfp4"
-    logits: str = "uniform"      # "router" | "uniform" | "zipf" | "skew"
+    logits: str = "uniform"      # "router" | "uniform" | "zipf" | "skew" | "balanced"
     outliers: bool = True
     seed: int = 0
     weight_seed: int = -1          # -1: same as seed
@@ -133,6 +135,12 @@ def logits(shape: Shape, x=None, router=None, device="cpu"):
             return torch.from_numpy(_rng(*key).random((T, E), dtype=np.float32))
         g = _dev_gen(device, *key)
         return torch.rand((T, E), generator=g, device=device, dtype=torch.float32)
+    if shape.logits == "balanced":
+        torch_ = _torch()
+        e = (shape.k * torch_.arange(T)[:, None] + torch_.arange(shape.k)[None, :]) % E
+        lg = torch_.zeros((T, E), dtype=torch_.float32)
+        lg.scatter_(1, e, 1.0)
+        return lg.to(device)
     if shape.logits == "skew":
         lg = _rng(*key).random((T, E), dtype=np.float32)
         lg[: (23 * T + 99) // 100, 0] += np.float32(1.0)
