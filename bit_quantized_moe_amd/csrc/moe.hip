@@ -81,6 +81,14 @@ struct GemmParams {
   float *outf;            // FP32 output (the gate/up activations h)
   const float *h_in;      // saved FP32 gate/up activations (dgrad epilogue)
   const float *tw;        // routing weight of pair f (dgrad epilogue)
+  // Remainder tiles (the training-size forward): an expert whose rows past its last full
+  // 256-row tile number at most 64 has those rows computed by the 64-row kernel.
+  // tile_rem: the prefix of those tiles (one per such expert); the 256-row kernel then
+  // skips them (its tiles per expert: tile_off minus tile_rem), and the 64-row kernel,
+  // with rem_rows set, takes tile_rem as its tile prefix and starts each expert's rows
+  // after its full 256-row tiles.
+  const int32_t *tile_rem;
+  int rem_rows;
 };
 
 __constant__ float c_nf4[16] = BQM_NF4_LEVELS;
@@ -1597,18 +1605,20 @@ template <int ASRC, int EPI, bool LORN = false, int WF = WF_NVFP4>
 __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   static_assert(WF == WF_NVFP4 || (ASRC == A_GATHER || ASRC == A_ROWS), "NF4 weights take bf16 activations");
   __shared__ __attribute__((aligned(16))) Smem sm;
+  // the tile prefix: 256-row tiles, less the remainder tiles the 64-row kernel takes
+  auto toff = [&](int e) { return p.tile_off[e] - (p.tile_rem ? p.tile_rem[e] : 0); };
   // tile decode: XCD x (= blockIdx % 8) walks tiles [x*per, (x+1)*per)
-  const int total = p.tile_off[p.E] * p.NT;
+  const int total = toff(p.E) * p.NT;
   const int per = (total + 7) / 8;
   const int li = blockIdx.x >> 3;
   if (li >= per) return;
   const int L = (blockIdx.x & 7) * per + li;
   if (L >= total) return;
   const int mt = L / p.NT, nt = L % p.NT;
-  int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
+  int lo = 0, hi = p.E;  // largest e with toff(e) <= mt
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (p.tile_off[mid] <= mt)
+    if (toff(mid) <= mt)
       lo = mid;
     else
       hi = mid;
@@ -1616,7 +1626,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
   const int e = lo;
   const int rb = p.offsets[e];
   const int n_e = p.offsets[e + 1] - rb;
-  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int m0 = (mt - toff(e)) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
   const int rows_left = n_e - m0 - row0;  // this wave's valid 32-row tiles: vt (0 skips every MFMA)
   const int vt = rows_left <= 0 ? 0 : (rows_left >= TM * 32 ? TM : (rows_left + 31) / 32);
@@ -1727,7 +1737,7 @@ __global__ void __launch_bounds__(NTHR, OCC) gemm_fwd_q4n(GemmParams p) {
   const int e = lo;
   const int rb = p.offsets[e];
   const int n_e = p.offsets[e + 1] - rb;
-  const int m0 = (mt - p.tile_off[e]) * BMN;
+  const int m0 = (p.rem_rows ? n_e / BM * BM : 0) + (mt - p.tile_off[e]) * BMN;
   const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WNG;
   const int rows_left = n_e - m0;  // >= 1: the tile exists
   const int vt = rows_left >= BMN ? TMN : (rows_left + 31) / 32;
@@ -2506,10 +2516,20 @@ constexpr int64_t kFewRowsPerExpert = 32;
 constexpr int kNSN = 4, kOccN = 2;
 bool few_rows(const bqm_moe_desc *d) { return d->T * d->k <= kFewRowsPerExpert * d->E; }
 
+// Training-size forward: an expert whose rows past its last full 256-row tile number at
+// most kRemRows (rows spread around a multiple of 256) has those rows computed by the
+// 64-row kernel (two workgroups per CU) rather than in a mostly empty 256-row tile.
+// Both forward GEMMs need K >= 256 (the 64-row kernel's scale groups).
+constexpr int kRemRows = 64;
+bool rem_split(const bqm_moe_desc *d) { return !few_rows(d) && d->H >= 4 * BK && d->I >= 4 * BK; }
+
 // forward GEMM over 4-bit weights: codes staged in LDS, decoded in registers.
 // tile_off_n: the prefix of 64-row tiles per expert, to run the few-rows configuration
+// tile_rem: the prefix of remainder tiles (rem_split), computed by the 64-row kernel
+// after the 256-row kernel has taken the other tiles
 template <int ASRC, int EPI, bool LORN = false, int WF = fq::WF_NVFP4>
-bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, const int32_t *tile_off_n = nullptr) {
+bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, const int32_t *tile_off_n = nullptr,
+                     const int32_t *tile_rem = nullptr) {
   static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
   if constexpr (!LORN) {
     if (tile_off_n && p.s1.K >= 4 * BK) {  // scale groups of four K steps
@@ -2518,9 +2538,23 @@ bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, c
       return launch_status(what);
     }
   }
+  const bool rem = !LORN && tile_rem && p.s1.K >= 4 * BK;
+  p.tile_rem = rem ? tile_rem : nullptr;
   const int grid = gemm_grid(R, p.E, p.NT);
   fq::gemm_fwd_q4<ASRC, EPI, LORN, WF><<<grid, fq::NTHR, 0, s>>>(p);
-  return launch_status(what);
+  const bqm_status st = launch_status(what);
+  if (st != BQM_OK) return st;
+  if constexpr (!LORN) {
+    if (rem) {
+      p.tile_off = tile_rem;
+      p.tile_rem = nullptr;
+      p.rem_rows = 1;
+      const int64_t g = std::max<int64_t>(std::min<int64_t>(p.E, R) * p.NT, 1);
+      fq::gemm_fwd_q4n<ASRC, EPI, WF, kNSN, kOccN><<<(int)((g + 7) / 8 * 8), fq::NTHR, 0, s>>>(p);
+      return launch_status(what);
+    }
+  }
+  return BQM_OK;
 }
 
 // LoRA projections (N = r) streamed through LDS by direct copies
@@ -2615,6 +2649,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
   uint16_t *a = w.at<uint16_t>(w.L.a);
   const bool fold_fwd = lora_folds_s_dec(d, true);
   const int32_t *tn = few_rows(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
+  const int32_t *trem = rem_split(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;  // remainder tiles
   // U_gu = s X A_gu^T   [R, r]  (divided by the expert's s_dec when that folds)
   if (r > 0) {
     GemmParams p = base_params(d, w);
@@ -2642,10 +2677,10 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     if (nf4) {
       mark(d, BQM_STAGE_GATE_UP_FWD, 0, s);
       BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
-      BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd", tn)));
+      BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd", tn, trem)));
       mark(d, BQM_STAGE_GATE_UP_FWD, 1, s);
     } else
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd", tn)));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd", tn, trem)));
   }
   constexpr bool aq = ASRC_X == A_GATHER_Q;
   if (aq)
@@ -2676,12 +2711,12 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     if (nf4) {
       mark(d, BQM_STAGE_DOWN_FWD, 0, s);
       BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
-      BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd", tn)));
+      BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd", tn, trem)));
       mark(d, BQM_STAGE_DOWN_FWD, 1, s);
     } else if (aq)
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd", tn)));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd", tn, trem)));
     else
-      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE>(p, R, s, "down fwd", tn)));
+      BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS, EPI_STORE>(p, R, s, "down fwd", tn, trem)));
   }
   return BQM_OK;
 }
@@ -2709,8 +2744,8 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
                 "bqm_moe_fwd: pointer not 16-byte aligned");
   }
   BQM_STAGE(d, BQM_STAGE_PERMUTE, s, permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
-                         w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off), fq::BMN,
-                                                w.at<int32_t>(w.L.tile_off_n), s));
+                         w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off),
+                         rem_split(d) ? -kRemRows : fq::BMN, w.at<int32_t>(w.L.tile_off_n), s));
   if (R == 0) return BQM_OK;
   if (hipMemcpyAsync(w.at<float>(w.L.tw), topk_w, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return launch_status("bqm_moe_fwd: copy of routing weights");

@@ -102,11 +102,23 @@ __global__ void __launch_bounds__(256) perm_hist(const int32_t *__restrict__ idx
   for (int e = threadIdx.x; e <= E; e += blockDim.x) counts[(int64_t)blockIdx.x * (E + 1) + e] = hist[e];
 }
 
+// row tiles of an expert with n rows for the second prefix: ceil(n / bm2), or with
+// bm2 < 0 one remainder tile when 0 < n mod bm <= -bm2
+__device__ __forceinline__ int32_t tiles_2(int32_t n, int bm, int bm2) {
+  if (bm2 > 0) return (n + bm2 - 1) / bm2;
+  if (bm2 < 0 && bm > 0) {
+    const int32_t r = n % bm;
+    return r > 0 && r <= -bm2 ? 1 : 0;
+  }
+  return 0;
+}
+
 // Pass 2 (one block): base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e];
 // offsets = exclusive prefix of the per-expert totals; the dropped bucket E starts
 // at offsets[E].  Optionally the prefixes
 // of ceil(count / bm) and ceil(count / bm2) (row tiles per expert) for the grouped
-// GEMMs.  The prefixes over experts are a wave-level inclusive scan plus the totals
+// GEMMs; with bm2 < 0 the second prefix instead counts one tile per expert whose rows
+// past its last full bm-row tile number between 1 and -bm2 (rem_tile).  The prefixes over experts are a wave-level inclusive scan plus the totals
 // of the waves before.
 __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, int nchunks, int E,
                                                   int32_t *__restrict__ offsets, int bm,
@@ -124,7 +136,7 @@ __global__ void __launch_bounds__(1024) perm_scan(int32_t *__restrict__ counts, 
     }
   }
   const int32_t tiles = (e < E && bm > 0) ? (run + bm - 1) / bm : 0;
-  const int32_t tiles2 = (e < E && bm2 > 0) ? (run + bm2 - 1) / bm2 : 0;
+  const int32_t tiles2 = e < E ? tiles_2(run, bm, bm2) : 0;
   int32_t v = run, u = tiles, u2 = tiles2;  // inclusive prefixes within the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -227,7 +239,7 @@ __global__ void __launch_bounds__(1024) perm_one(const int32_t *__restrict__ idx
   const int e = t;
   const int32_t run = e < E ? cnt[e] : 0;
   const int32_t tiles = (e < E && bm > 0) ? (run + bm - 1) / bm : 0;
-  const int32_t tiles2 = (e < E && bm2 > 0) ? (run + bm2 - 1) / bm2 : 0;
+  const int32_t tiles2 = e < E ? tiles_2(run, bm, bm2) : 0;
   int32_t v = run, u = tiles, u2 = tiles2;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {

@@ -312,6 +312,18 @@ def test_big_experts_w4a4_every_row():
     _check_rows_per_expert(o, 8, 600, 900)
 
 
+def test_remainder_tiles():
+    # about 525 rows per expert: an expert whose rows past its last full 256-row tile number
+    # at most 64 has them computed by the 64-row kernel after the 256-row one (the others
+    # keep a partial 256-row tile); every row compared, NVFP4, W4A4 and NF4 weights
+    g, o = compare_full(small("rem", E=8, k=2, T=2100, r=16))
+    counts = np.bincount(o["idx"].reshape(-1), minlength=8)
+    rem = counts % 256
+    assert ((rem > 0) & (rem <= 64)).any() and (rem > 64).any(), counts
+    compare_full(small("rem_w4a4", E=8, k=2, T=2100, r=16, act_quant=True))
+    compare_full(small("rem_nf4", E=8, k=2, T=2100, r=16, fmt="nf4"))
+
+
 def test_lora_gradients_over_row_chunks():
     # the per-expert LoRA gradients cut an expert's rows into chunks of 2048 (one
     # workgroup per chunk, partial sums added in chunk order): with k = 1 over 3 experts
