@@ -430,6 +430,7 @@ constexpr int DQS = 72;  // row stride (bf16) of the dgrad's decoded NF4 tiles
 
 struct Smem {
   static constexpr int NS = NST, NSG = 0;
+  static constexpr int lora_b_bytes = 2 * BM * BK * 2;  // stages 1 and 2 of a[] (seg_lora_n)
   uint16_t a[NST][BM * BK];  // bf16, swizzled 128-byte rows
   uint8_t b[NST][BN * 32];   // codes: 32 bytes per output column (forward), 128 per weight row (dgrad)
   uint32_t s[NST][BN];       // E4M3 block scales of the K step (NF4: FP32 absmax)
@@ -1110,8 +1111,8 @@ __device__ __forceinline__ void dma_src_d(const Seg &s, const int64_t (&arow)[AC
 }
 
 // copy j (0..VT+2) of the K step at k0 into stage st: A rows (j < VT), codes, scales
-template <int VT>
-__device__ __forceinline__ void dma_one_d(const DmaSrcD &d, int j, int k0, const Smem &sm, int st) {
+template <int VT, class SM>
+__device__ __forceinline__ void dma_one_d(const DmaSrcD &d, int j, int k0, const SM &sm, int st) {
   const uint32_t w = wave_id();
   if (j < VT)
     dma_b128(d.a[j] + k0, lds_a(sm, st) + (8 * VT * w + 8 * j) * BK * 2);
@@ -1163,10 +1164,10 @@ __device__ __forceinline__ uint32_t dec_pair_d(const DRaw &r, int tn, int kk, in
 
 #define FQ_PIN() __builtin_amdgcn_sched_barrier(0)
 
-template <int VT, bool DMA, bool NEXT>
-__device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k2, const DmaSrcD &d, int wn, int row0,
-                                        int lane, bf16x8 (&af)[2][TM], u32x4 (&bf)[2][TN], DRaw &raw,
-                                        f32x16 (&acc)[TM][TN]) {
+template <int VT, bool DMA, bool NEXT, int TMA, class SM>
+__device__ __forceinline__ void step_dq(SM &sm, int cur, int nx, int n2, int k2, const DmaSrcD &d, int wn, int row0,
+                                        int lane, bf16x8 (&af)[2][TMA], u32x4 (&bf)[2][TN], DRaw &raw,
+                                        f32x16 (&acc)[TMA][TN]) {
   const uint16_t *As = sm.a[cur];
 #pragma unroll
   for (int kk = 0; kk < 3; ++kk) {
@@ -1238,11 +1239,12 @@ __device__ __forceinline__ void step_dq(Smem &sm, int cur, int nx, int n2, int k
   }
 }
 
-template <int EPI, int VT>
-__device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
-                                              f32x16 (&acc)[TM][TN]) {
+template <int EPI, int VT, int TMA, class SM>
+__device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], SM &sm,
+                                              f32x16 (&acc)[TMA][TN]) {
+  static_assert(SM::NS == 3, "the copies run two K steps ahead through three stages");
   constexpr int NDMA = VT + 3;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, wn = wid % WNG, row0 = (wid / WNG) * TMA * 32;
   const int nk = s.K / BK;
   DmaSrcD d;
   dma_src_d<VT>(s, arow, e, nt, N, d);
@@ -1256,7 +1258,7 @@ __device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N
     wait_vm<0>();
   }
   barrier_lds();
-  bf16x8 af[2][TM];
+  bf16x8 af[2][TMA];
   u32x4 bf[2][TN];
   DRaw raw;
   {
@@ -1281,15 +1283,15 @@ __device__ __forceinline__ void seg_dq_direct(const Seg &s, int e, int nt, int N
   for (; ks + 2 < nk; ++ks) {
     const int nx = cur == NST - 1 ? 0 : cur + 1;
     const int n2 = nx == NST - 1 ? 0 : nx + 1;
-    step_dq<VT, true, true>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, raw, acc);
+    step_dq<VT, true, true, TMA>(sm, cur, nx, n2, (ks + 2) * BK, d, wn, row0, lane, af, bf, raw, acc);
     cur = nx;
   }
   if (ks + 1 < nk) {
     const int nx = cur == NST - 1 ? 0 : cur + 1;
-    step_dq<VT, false, true>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
+    step_dq<VT, false, true, TMA>(sm, cur, nx, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
     cur = nx;
   }
-  step_dq<VT, false, false>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
+  step_dq<VT, false, false, TMA>(sm, cur, 0, 0, 0, d, wn, row0, lane, af, bf, raw, acc);
   __syncthreads();  // the stages are reused by the next segment
 }
 
@@ -1478,10 +1480,11 @@ __device__ __forceinline__ void seg_dn_direct(const Seg &s, int e, int nt, int N
 // transposing LDS read.
 constexpr int LSTR = BN + 8;
 
+template <int NC = ACH>
 __device__ __forceinline__ void lora_n_load(const Seg &s, const int64_t (&arow)[ACH], const uint16_t *bsrc, int nt,
-                                            int N, int ks, ARegs<> &a, u32x4 (&bv)[8]) {
+                                            int N, int ks, ARegs<NC> &a, u32x4 (&bv)[8]) {
   const int tid = threadIdx.x;
-  a_load<A_ROWS, true>(s, arow, ks * BK, a);
+  a_load<A_ROWS, true, NC>(s, arow, ks * BK, a);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int c = tid + NTHR * i, row = c >> 5, col = nt * BN + 8 * (c & 31);
@@ -1490,34 +1493,37 @@ __device__ __forceinline__ void lora_n_load(const Seg &s, const int64_t (&arow)[
   }
 }
 
-__device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], Smem &sm,
-                                           int vt, f32x16 (&acc)[TM][TN]) {
-  static_assert(sizeof(sm.a[1]) * 2 >= BK * LSTR * 2, "LoRA tile fits two A stages");
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
+// TMA row tiles of 32 (arow: the A rows of this thread's TMA chunks, a_row<TMA>); the
+// LoRA-B tile sits from stage 1's A area on (SM::lora_b_fits: it fits the stages after it)
+template <int TMA = TM, class SM>
+__device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, const int64_t (&arow)[ACH], SM &sm,
+                                           int vt, f32x16 (&acc)[TMA][TN]) {
+  static_assert(SM::lora_b_bytes >= BK * LSTR * 2, "LoRA tile fits the stages");
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TMA * 32;
   const int nk = (s.K + BK - 1) / BK;
   const uint16_t *bsrc = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride;
   uint16_t *Bt = sm.a[1];
-  ARegs<> ar;
+  ARegs<TMA> ar;
   u32x4 bv[8];
-  lora_n_load(s, arow, bsrc, nt, N, 0, ar, bv);
+  lora_n_load<TMA>(s, arow, bsrc, nt, N, 0, ar, bv);
   for (int ks = 0; ks < nk; ++ks) {
-    a_store<A_ROWS>(sm.a[0], ar);
+    a_store<A_ROWS, TMA>(sm.a[0], ar);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int c = tid + NTHR * i;
       *reinterpret_cast<u32x4 *>(Bt + (c >> 5) * LSTR + 8 * (c & 31)) = bv[i];
     }
-    if (ks + 1 < nk) lora_n_load(s, arow, bsrc, nt, N, ks + 1, ar, bv);  // lands during this step's MFMAs
+    if (ks + 1 < nk) lora_n_load<TMA>(s, arow, bsrc, nt, N, ks + 1, ar, bv);  // lands during this step's MFMAs
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 af[TM], bl[TN];
+      bf16x8 af[TMA], bl[TN];
 #pragma unroll
       for (int tn = 0; tn < TN; ++tn) bl[tn] = b_frag_trans_s<LSTR>(Bt, 16 * kk, wn * TN * 32 + tn * 32, lane);
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
+      for (int tm = 0; tm < TMA; ++tm)
         af[tm] = *reinterpret_cast<const bf16x8 *>(sm.a[0] + a_off(row0 + tm * 32 + (lane & 31), 2 * kk + (lane >> 5)));
-      mfmas<VT_DYN>(af, bl, vt, acc);
+      mfmas<VT_DYN, TMA>(af, bl, vt, acc);
     }
     __syncthreads();
   }
@@ -1526,7 +1532,9 @@ __device__ __forceinline__ void seg_lora_n(const Seg &s, int e, int nt, int N, c
 template <int ASRC, int EPI, int WF = WF_NVFP4>
 __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
   __shared__ __attribute__((aligned(16))) Smem sm;
-  const int total = p.tile_off[p.E] * p.NT;
+  // the tile prefix: 256-row tiles, less the remainder tiles the 64-row kernel takes
+  auto toff = [&](int e) { return p.tile_off[e] - (p.tile_rem ? p.tile_rem[e] : 0); };
+  const int total = toff(p.E) * p.NT;
   const int per = (total + 7) / 8;
   const int li = blockIdx.x >> 3;
   if (li >= per) return;
@@ -1536,7 +1544,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
   int lo = 0, hi = p.E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (p.tile_off[mid] <= mt)
+    if (toff(mid) <= mt)
       lo = mid;
     else
       hi = mid;
@@ -1544,7 +1552,7 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
   const int e = lo;
   const int rb = p.offsets[e];
   const int n_e = p.offsets[e + 1] - rb;
-  const int m0 = (mt - p.tile_off[e]) * BM;
+  const int m0 = (mt - toff(e)) * BM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, wn = wid % WNG, row0 = (wid / WNG) * TM * 32;
   const int rows_left = n_e - m0 - row0;
   const int vt = rows_left <= 0 ? 0 : (rows_left >= TM * 32 ? TM : (rows_left + 31) / 32);
@@ -1784,6 +1792,73 @@ __global__ void __launch_bounds__(NTHR, OCC) gemm_fwd_q4n(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row<TMN>(i < TMN ? i : 0), n_e - 1);
     seg_lora<EPI, TMN>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
+  }
+  epilogue_t<TMN, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc);
+}
+
+// The NVFP4 dgrad on 64-row tiles: the same transposed weight read and K loop as
+// gemm_dgrad_q4 (three stages, copies two K steps ahead), with stages of 17 KB so that
+// kOccD workgroups share a CU.  The LoRA segment's B tile (64 x LSTR bf16) takes the
+// A stages 1 and 2 and the code stages after them.
+struct SmemD {
+  static constexpr int NS = NST, NSG = 0;
+  static constexpr int lora_b_bytes = 2 * BMN * BK * 2 + NST * BN * 32;
+  uint16_t a[NST][BMN * BK];
+  uint8_t b[NST][BN * 32];  // 64 weight rows of 128 code bytes
+  uint32_t s[NST][BN];
+  uint8_t t[BN / 64][256];
+};
+static_assert(offsetof(SmemD, b) == sizeof(SmemD::a), "the LoRA tile runs from a[1] into b[]");
+constexpr int kOccD = 2;
+
+// tile_off: prefix over experts of the 64-row tiles (few rows), or of the remainder
+// tiles when rem_rows is set (each expert's rows past its full 256-row tiles)
+template <int ASRC, int EPI>
+__global__ void __launch_bounds__(NTHR, kOccD) gemm_dgrad_q4n(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) SmemD sm;
+  const int total = p.tile_off[p.E] * p.NT;
+  const int per = (total + 7) / 8;
+  const int li = blockIdx.x >> 3;
+  if (li >= per) return;
+  const int L = (blockIdx.x & 7) * per + li;
+  if (L >= total) return;
+  const int mt = L / p.NT, nt = L % p.NT;
+  int lo = 0, hi = p.E;  // largest e with tile_off[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.tile_off[mid] <= mt)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int e = lo;
+  const int rb = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - rb;
+  const int m0 = (p.rem_rows ? n_e / BM * BM : 0) + (mt - p.tile_off[e]) * BMN;
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) % WNG;
+  const int rows_left = n_e - m0;  // >= 1: the tile exists
+  const int vt = rows_left >= BMN ? TMN : (rows_left + 31) / 32;
+  int64_t arow[ACH];
+  f32x16 acc[TMN][TN];
+#pragma unroll
+  for (int tm = 0; tm < TMN; ++tm)
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[tm][tn][v] = 0.0f;
+  if (__builtin_amdgcn_readfirstlane(vt) > 1) {
+    dma_rows<ASRC, 2>(p, rb, n_e, m0, arow);
+    seg_dq_direct<EPI, 2, TMN>(p.s1, e, nt, p.N, arow, sm, acc);
+  } else {
+    dma_rows<ASRC, 1>(p, rb, n_e, m0, arow);
+    seg_dq_direct<EPI, 1, TMN>(p.s1, e, nt, p.N, arow, sm, acc);
+  }
+  const float esc = uniform_load(p.s1.b_sd + e);
+  if (p.s2.K > 0) {
+    int64_t arow2[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row<TMN>(i < TMN ? i : 0), n_e - 1);
+    seg_lora_n<TMN>(p.s2, e, nt, p.N, arow2, sm, vt, acc);
   }
   epilogue_t<TMN, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc);
 }
@@ -2574,12 +2649,28 @@ bqm_status launch_lp(const GemmParams &p, int64_t R, hipStream_t s, const char *
   return launch_status(what);
 }
 
-// dgrad GEMM over the rowwise NVFP4 weight read transposed (codes staged in LDS)
+// dgrad GEMM over the rowwise weight read transposed (codes staged in LDS); tile_off_n
+// and tile_rem as for launch_fq (NVFP4 only: the NF4 dgrad keeps the 256-row tiles)
 template <int ASRC, int EPI, int WF = fq::WF_NVFP4>
-bqm_status launch_fd(const GemmParams &p, int64_t R, hipStream_t s, const char *what) {
+bqm_status launch_fd(GemmParams p, int64_t R, hipStream_t s, const char *what, const int32_t *tile_off_n = nullptr,
+                     const int32_t *tile_rem = nullptr) {
   static_assert(fq::BM == BM, "tile offsets are computed for BM rows");
-  const int grid = gemm_grid(R, p.E, p.NT);
-  fq::gemm_dgrad_q4<ASRC, EPI, WF><<<grid, fq::NTHR, 0, s>>>(p);
+  constexpr bool kQ = WF == fq::WF_NVFP4;
+  if (kQ && tile_off_n) {
+    p.tile_off = tile_off_n;
+    fq::gemm_dgrad_q4n<ASRC, EPI><<<gemm_grid(R, p.E, p.NT, fq::BMN), fq::NTHR, 0, s>>>(p);
+    return launch_status(what);
+  }
+  const bool rem = kQ && tile_rem;
+  p.tile_rem = rem ? tile_rem : nullptr;
+  fq::gemm_dgrad_q4<ASRC, EPI, WF><<<gemm_grid(R, p.E, p.NT), fq::NTHR, 0, s>>>(p);
+  const bqm_status st = launch_status(what);
+  if (st != BQM_OK || !rem) return st;
+  p.tile_off = tile_rem;
+  p.tile_rem = nullptr;
+  p.rem_rows = 1;
+  const int64_t g = std::max<int64_t>(std::min<int64_t>(p.E, R) * p.NT, 1);
+  fq::gemm_dgrad_q4n<ASRC, EPI><<<(int)((g + 7) / 8 * 8), fq::NTHR, 0, s>>>(p);
   return launch_status(what);
 }
 
@@ -2790,6 +2881,9 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
   uint16_t *vdn = w.at<uint16_t>(w.L.vdn), *vgu = w.at<uint16_t>(w.L.vgu);
   uint16_t *dh = w.at<uint16_t>(w.L.dh);
   uint16_t *dxr = w.at<uint16_t>(w.L.dxr);
+  // the 64-row tiles of the permutation, as in the forward
+  const int32_t *tn = few_rows(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
+  const int32_t *trem = rem_split(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
   if (dtopk_w) {
     mark(d, BQM_STAGE_DTOPK, 0, s);
     dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv),
@@ -2828,7 +2922,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
       mark(d, BQM_STAGE_DOWN_DGRAD, 1, s);
     }
     else
-      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fd<A_GATHER, EPI_DOWN_DGRAD>(p, R, s, "down dgrad")));
+      BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fd<A_GATHER, EPI_DOWN_DGRAD>(p, R, s, "down dgrad", tn, trem)));
   }
   // V_gu = s dh B_gu  [R, r]
   if (r > 0) {
@@ -2859,7 +2953,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
       mark(d, BQM_STAGE_GATE_UP_DGRAD, 1, s);
     }
     else
-      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE>(p, R, s, "gate_up dgrad")));
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_DGRAD, s, (launch_fd<A_ROWS, EPI_STORE>(p, R, s, "gate_up dgrad", tn, trem)));
   }
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_DGRAD, 0, s);

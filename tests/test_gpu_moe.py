@@ -109,8 +109,8 @@ def test_small_shared_lora_a_nf4_w4a4_colwise():
 
 
 def test_small_batches():
-    # decode-sized batches (at most 32 routed rows per expert on average: the forward
-    # runs the 64-row tile configuration), where most row tiles hold one or two valid
+    # decode-sized batches (at most 32 routed rows per expert on average: the forward and
+    # the NVFP4 dgrad run the 64-row tile configuration), where most row tiles hold one or two valid
     # 32-row tiles: T = 8 over 64 experts with k = 8; partial column tiles at T = 40;
     # 100 rows per expert (the 256-row tiles again); T = 256 with the shared-A LoRA;
     # NVFP4 activations; LoRA rank 72 (masked K tail of the up-projection segment)
@@ -314,8 +314,9 @@ def test_big_experts_w4a4_every_row():
 
 def test_remainder_tiles():
     # about 525 rows per expert: an expert whose rows past its last full 256-row tile number
-    # at most 64 has them computed by the 64-row kernel after the 256-row one (the others
-    # keep a partial 256-row tile); every row compared, NVFP4, W4A4 and NF4 weights
+    # at most 64 has them computed by the 64-row kernels after the 256-row ones (forward, and
+    # the NVFP4 dgrad; the others keep a partial 256-row tile); every row compared, NVFP4,
+    # W4A4 and NF4 weights
     g, o = compare_full(small("rem", E=8, k=2, T=2100, r=16))
     counts = np.bincount(o["idx"].reshape(-1), minlength=8)
     rem = counts % 256
