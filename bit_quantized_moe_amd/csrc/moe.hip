@@ -26,6 +26,9 @@
 //   - gemm_dgrad_q4 reads the single rowwise copy transposed (4-bit transposing
 //     LDS read, NVFP4), or for NF4 decodes its rows into a per-wave bf16 tile read
 //     back with the 16-bit transposing read.
+// With at most one routed row per expert on average (decode-sized batches), the
+// forward GEMMs run gv::fwd_stream instead: no LDS stages for the weights, whose codes
+// stream from HBM straight into registers, 16x16x32 MFMAs over up to 16 rows per pass.
 // The LoRA down-projections (N = r) stream through lp::gemm_lora_proj; the LoRA
 // weight gradients through lora_wgrad.  Workgroups are mapped so that each of the
 // 8 XCDs walks a contiguous range of tiles: the tiles in flight on one XCD share
@@ -89,6 +92,7 @@ struct GemmParams {
   // after its full 256-row tiles.
   const int32_t *tile_rem;
   int rem_rows;
+  int rows_pass;  // the weight-streaming forward: rows per pass (its activation rows in LDS)
 };
 
 __constant__ float c_nf4[16] = BQM_NF4_LEVELS;
@@ -1865,6 +1869,340 @@ __global__ void __launch_bounds__(NTHR, kOccD) gemm_dgrad_q4n(GemmParams p) {
 }  // namespace fq
 
 // ---------------------------------------------------------------------------
+// Weight-streaming forward for decode-sized batches (NVFP4 weights)
+// ---------------------------------------------------------------------------
+// With about one routed row per expert each weight byte feeds one or two rows, and
+// the forward GEMMs are a stream of the hit experts' 4-bit weights.  This kernel keeps
+// no stage in LDS and has no barrier in its K loop.  A workgroup of four waves takes
+// up to 16 of one expert's rows per pass (the M of a 16x16x32 bf16 MFMA) and 32
+// output columns: the gate and up columns of 16 consecutive i, or 32 consecutive
+// columns.  The waves split K into 128-deep blocks (wave w takes blocks w, w + 4, ...).
+// In a block, lane L loads 16 code bytes (32 consecutive k) and the two E4M3 scales
+// of column L % 16 of each column set at k0 + 32 (L / 16), PF blocks ahead, straight
+// into registers, and the same 32 activations of row L % 16 (small, and hot in L2);
+// MFMA m of the block takes their k = 8m .. 8m + 7 (one permutation of k for both
+// operands).  The four waves' FP32 partial sums are added in LDS in wave order, then
+// the LoRA up-projection (split over the waves the same way, 32 deep per MFMA), the
+// per-expert (and, for NVFP4 activations, per-row) decode scales and the epilogue.
+namespace gv {
+constexpr int NTHR = 256, NW = NTHR / 64;
+constexpr int KB = 128;  // K per block
+constexpr int RP = 16;   // rows per pass at most (the MFMA's M)
+constexpr int PF = 4;    // blocks of loads in flight per wave
+constexpr int OCC = 4;   // workgroups per CU (at most 128 registers per lane)
+constexpr int COLS = 32; // output columns per workgroup (two sets of 16)
+constexpr int XLDS = 24 * 1024;  // LDS for a pass's activation rows
+constexpr int RED_BYTES = NW * 4 * 64 * 16;  // the waves' partial sums (aliasing the rows)
+constexpr int LSL = 2;   // LoRA up-projection: 32-deep slices per wave (its K at most 32 NW LSL)
+// word 3 of a raw buffer resource on this GPU family (32-bit elements, no swizzle)
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// LDS bytes of the scales of a workgroup's 32 weight rows (K / 16 bytes each)
+__host__ __device__ constexpr int scale_lds_bytes(int64_t K) { return (int)(32 * (K / 16)); }
+
+struct Blk {
+  u32x4 c[2];  // 32 codes of this lane's column in each set (element 2b in the low nibble of byte b)
+};
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, const f32x4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// the 8 weights of MFMA m (code word m, block scale m / 2) as bf16 pairs (exact)
+template <int M>
+__device__ __forceinline__ u32x4 dec8(const u32x4 &c, float sb) {
+  u32x4 r;
+  f32x2 v = fp4pair<0>(c[M], sb);
+  r[0] = pack_exact(v.x, v.y);
+  v = fp4pair<1>(c[M], sb);
+  r[1] = pack_exact(v.x, v.y);
+  v = fp4pair<2>(c[M], sb);
+  r[2] = pack_exact(v.x, v.y);
+  v = fp4pair<3>(c[M], sb);
+  r[3] = pack_exact(v.x, v.y);
+  return r;
+}
+
+// the codes of one block: byte offsets of the block in this lane's rows (the expert's
+// slice is the buffer; a lane past K in a half block reads its row's start)
+__device__ __forceinline__ void load_blk(Blk &b, __amdgpu_buffer_rsrc_t rc, const uint32_t (&oc)[2], int k) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    b.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, oc[j] + (uint32_t)(k / 2), 0, 0));
+}
+
+// one MFMA's weights decoded right before it (the scheduling barriers keep the decode
+// of the whole block from being hoisted, which would hold 32 more registers); xr: this
+// lane's activations at the block's k (LDS, zero past K)
+// sw: the block's two E4M3 scales of this lane's column in each set (bytes 0, 1)
+__device__ __forceinline__ void use_blk(const Blk &b, const uint32_t (&sw)[2], const uint16_t *xr, f32x4 (&acc)[2]) {
+  float sb[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    sb[j][0] = e4m3_hw<0>(sw[j]);
+    sb[j][1] = e4m3_hw<1>(sw[j]);
+  }
+  u32x4 x = *reinterpret_cast<const u32x4 *>(xr);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma16(x, dec8<0>(b.c[j], sb[j][0]), acc[j]);
+  __builtin_amdgcn_sched_barrier(0);
+  x = *reinterpret_cast<const u32x4 *>(xr + 8);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma16(x, dec8<1>(b.c[j], sb[j][0]), acc[j]);
+  __builtin_amdgcn_sched_barrier(0);
+  x = *reinterpret_cast<const u32x4 *>(xr + 16);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma16(x, dec8<2>(b.c[j], sb[j][1]), acc[j]);
+  __builtin_amdgcn_sched_barrier(0);
+  x = *reinterpret_cast<const u32x4 *>(xr + 24);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) acc[j] = mfma16(x, dec8<3>(b.c[j], sb[j][1]), acc[j]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// tile_off: the prefix of 64-row tiles per expert; NT: column blocks of COLS;
+// rows_pass rows of K activations (rounded up to a block) fit the dynamic LDS
+template <int ASRC, int EPI>
+__global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
+  static_assert(EPI == EPI_GATEUP || EPI == EPI_STORE, "forward epilogues");
+  constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
+  constexpr bool kGather = ASRC == A_GATHER || ASRC == A_GATHER_Q;
+  // dynamic LDS: the scales of the 32 weight rows [32][SS], then the pass's activation
+  // rows [rows_pass][Kp], which after the K loop hold the waves' partial sums
+  // [NW][4][64]: base sums of sets 0, 1, then LoRA sums of sets 0, 1
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  __shared__ int tile_info[4];
+  const int mt = blockIdx.x / p.NT, cb = blockIdx.x % p.NT;
+  // the expert of row tile mt, found by all threads at once: one load per expert
+  {
+    int hit = 0;
+    for (int e = threadIdx.x; e < p.E; e += NTHR) {
+      const int t0 = p.tile_off[e], t1 = p.tile_off[e + 1], o0 = p.offsets[e], o1 = p.offsets[e + 1];
+      if (t0 <= mt && mt < t1) {
+        tile_info[0] = e;
+        tile_info[1] = o0;
+        tile_info[2] = o1 - o0;
+        tile_info[3] = t0;
+        hit = 1;
+      }
+    }
+    if (!__syncthreads_or(hit)) return;  // past the last tile: the grid is an upper bound
+  }
+  const int e = __builtin_amdgcn_readfirstlane(tile_info[0]);
+  const int rb = __builtin_amdgcn_readfirstlane(tile_info[1]);
+  const int n_e = __builtin_amdgcn_readfirstlane(tile_info[2]);
+  const int m0 = (mt - __builtin_amdgcn_readfirstlane(tile_info[3])) * 64, mend = min(m0 + 64, n_e);
+  const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the block loop branches on it
+
+  // this lane's weight column in each set (columns past the output read column 0)
+  const Seg &s = p.s1;
+  int col[2];
+  bool col_ok[2];
+  if constexpr (EPI == EPI_GATEUP) {
+    const int i = cb * 16 + c;
+    col_ok[0] = col_ok[1] = i < p.I;
+    col[0] = col_ok[0] ? i : 0;
+    col[1] = col_ok[0] ? p.I + i : 0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = cb * COLS + 16 * j + c;
+      col_ok[j] = n < p.N;
+      col[j] = col_ok[j] ? n : 0;
+    }
+  }
+  const int K = s.K;
+  // the expert's slice of codes and of scales as buffers (loads past them read 0)
+  const int64_t slice = s.b_rows * s.b_cols;
+  const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2)), 0, (int)(slice / 2), kRsrcWord3);
+  uint32_t oc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) oc[j] = (uint32_t)col[j] * (uint32_t)(s.b_cols / 2) + 16 * g;
+  const int nkb = (K + KB - 1) / KB;
+  const int nb = nkb > w ? (nkb - w + NW - 1) / NW : 0;  // this wave's blocks w + NW j
+  const int Kp = nkb * KB, K8 = K / 8, Kp8 = Kp / 8;      // LDS row stride: K rounded up, zero past K
+  // the E4M3 scales of the workgroup's 32 weight rows (K / 16 bytes each, contiguous in
+  // HBM per set of 16 rows) go to LDS once, by direct copies: 2-byte loads of each lane's
+  // own scales would cost one memory transaction per row and block
+  const int SB = K / 16;  // scale bytes per weight row (a multiple of 4)
+  uint8_t *sc = reinterpret_cast<uint8_t *>(xs);
+  uint16_t *xa = reinterpret_cast<uint16_t *>(sc + scale_lds_bytes(K));  // the activation rows after them
+  f32x4(*red)[4][64] = reinterpret_cast<f32x4(*)[4][64]>(xa);
+  const float esc = kQA ? 1.0f : uniform_load(s.b_sd + e);
+  const Seg &l = p.s2;
+  const uint16_t *bl[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bl[j] = reinterpret_cast<const uint16_t *>(l.b) + e * l.b_estride + (int64_t)col[j] * l.b_cols;
+
+  for (int r0 = m0; r0 < mend; r0 += p.rows_pass) {
+    const int nr = min(p.rows_pass, mend - r0);
+    // the pass's activation rows go global -> LDS by direct copies (1 KB per wave and
+    // copy), then every lane's first PF blocks of weights and its LoRA operands are
+    // requested, and only then is the copy waited for
+    for (int q = threadIdx.x; q < nr * (Kp8 - K8); q += NTHR) {
+      const int row = q / (Kp8 - K8), ch = K8 + q - row * (Kp8 - K8);
+      *reinterpret_cast<u32x4 *>(xa + row * Kp + 8 * ch) = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (r0 == m0) {
+      // set j's 16 weight rows hold 16 SB contiguous bytes of scales (16-byte aligned)
+      const uint8_t *sg = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16);
+      for (int j = 0; j < 2; ++j) {
+        const int64_t r0j = EPI == EPI_GATEUP ? (j ? (int64_t)p.I + cb * 16 : cb * 16) : (int64_t)cb * COLS + 16 * j;
+        const uint8_t *src = sg + r0j * SB;
+        for (int c0 = 64 * w; c0 < SB; c0 += 64 * NW) {  // 16-byte chunks of the 16 SB bytes
+          const uint32_t dst = (uint32_t)(uintptr_t)(const fq::lds_void *)(sc + 16 * j * SB + 16 * c0);
+          if (c0 + lane < SB) fq::dma_b128(src + 16 * (c0 + lane), dst);
+        }
+      }
+    }
+    for (int row = 0; row < nr; ++row) {
+      const int64_t src = kGather ? (int64_t)(p.perm[rb + r0 + row] / p.k) : (int64_t)(rb + r0 + row);
+      const uint16_t *xg = reinterpret_cast<const uint16_t *>(s.a) + src * s.a_ld;
+      for (int c0 = 64 * w; c0 < K8; c0 += 64 * NW) {
+        const uint32_t dst = (uint32_t)(uintptr_t)(const fq::lds_void *)(xa + row * Kp + 8 * c0);
+        if (c0 + lane < K8) fq::dma_b128(xg + 8 * (c0 + lane), dst);
+      }
+    }
+    const bool xok = c < nr;
+    const int pos = r0 + min(c, nr - 1);
+    const uint16_t *xrow = xa + min(c, nr - 1) * Kp + 32 * g;
+    // this lane's scale pair of a block at k: bytes (k + 32 g) / 16 of its rows (clamped
+    // into the row past K, where the activations are zero)
+    const uint8_t *srow0 = sc + c * SB, *srow1 = sc + (16 + c) * SB;
+    auto scales = [&](int k, uint32_t(&sw)[2]) {
+      const int o = min(k + 32 * g, K - 32) / 16;
+      sw[0] = *reinterpret_cast<const uint16_t *>(srow0 + o);
+      sw[1] = *reinterpret_cast<const uint16_t *>(srow1 + o);
+    };
+
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    Blk buf[PF];
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      if (u < nb) {
+        const int k = (w + NW * u) * KB;
+        load_blk(buf[u], rc, oc, k + 32 * g < K ? k : 0);
+      }
+    }
+    // LoRA up-projection operands (A = the hi/lo pair rows at k < s2.K, B = the expert's
+    // LoRA matrix at k mod kmod), 32-deep slices w, w + NW, ... of this wave
+    u32x4 la[LSL], lb[LSL][2];
+    const uint16_t *ar = reinterpret_cast<const uint16_t *>(l.a) + (int64_t)(rb + pos) * l.a_ld;
+#pragma unroll
+    for (int q = 0; q < LSL; ++q) {
+      const int k = 32 * (w + NW * q) + 8 * g;
+      const bool ok = k < l.K;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      la[q] = (ok && xok) ? *reinterpret_cast<const u32x4 *>(ar + k) : z;
+      const int kb = ok ? k % l.kmod : 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) lb[q][j] = ok ? *reinterpret_cast<const u32x4 *>(bl[j] + kb) : z;
+    }
+    // the direct copies are not tracked by the compiler's wait counts: wait for every load
+    // issued so far (the row copies are the oldest), then the barrier
+    fq::wait_vm<0>();
+    __syncthreads();
+
+    // steady state: every slot is refilled right after use, no branch between loads (so
+    // that each use waits only for its own block); then the last blocks without refills
+    int j0 = 0;
+    auto use = [&](int u, int j) {
+      const int k = (w + NW * j) * KB;
+      uint32_t sw[2];
+      scales(k, sw);
+      use_blk(buf[u], sw, xrow + k, acc);
+    };
+    for (; j0 + 2 * PF <= nb; j0 += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        use(u, j0 + u);
+        const int kn = (w + NW * (j0 + u + PF)) * KB;
+        load_blk(buf[u], rc, oc, kn + 32 * g < K ? kn : 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      if (j0 + u < nb) {
+        use(u, j0 + u);
+        if (j0 + u + PF < nb) {
+          const int kn = (w + NW * (j0 + u + PF)) * KB;
+          load_blk(buf[u], rc, oc, kn + 32 * g < K ? kn : 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+      if (j0 + PF + u < nb) use(u, j0 + PF + u);
+    f32x4 lacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int q = 0; q < LSL; ++q)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) lacc[j] = mfma16(la[q], lb[q][j], lacc[j]);
+
+    // the four waves' partial sums, added in wave order by wave 0
+    __syncthreads();  // every wave is done reading the activation rows
+    red[w][0][lane] = acc[0];
+    red[w][1][lane] = acc[1];
+    red[w][2][lane] = lacc[0];
+    red[w][3][lane] = lacc[1];
+    __syncthreads();
+    if (w == 0) {
+      f32x4 v[2], lv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        v[j] = red[0][j][lane];
+        lv[j] = red[0][2 + j][lane];
+#pragma unroll
+        for (int q = 1; q < NW; ++q) {
+          v[j] += red[q][j][lane];
+          lv[j] += red[q][2 + j][lane];
+        }
+      }
+      // lane (c, g) holds rows 4 g + t (t = 0..3) of column c of each set
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int row = 4 * g + t;
+        if (row >= nr) continue;
+        const int64_t grow = rb + r0 + row;
+        float val[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) val[j] = v[j][t];
+        if constexpr (kQA) {
+          const int64_t src = kGather ? (int64_t)(p.perm[grow] / p.k) : grow;
+          const float sc = p.s1.b_sd[e] * p.s1.a_sd[src];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) val[j] *= sc;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) val[j] += lv[j][t];
+        if constexpr (EPI == EPI_GATEUP) {
+          if (col_ok[0]) {
+            const int i = cb * 16 + c;
+            const float gv = val[0] * esc, uv = val[1] * esc;
+            float *hrow = p.outf + grow * 2 * p.I;
+            hrow[i] = gv;
+            hrow[p.I + i] = uv;
+            p.out1[grow * p.I + i] = (uint16_t)f32_to_bf16(gv * sigmoid_f(gv) * uv);
+          }
+        } else {
+          const float sc = esc * p.out_scale;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            if (col_ok[j]) p.out0[grow * p.N + cb * COLS + 16 * j + c] = (uint16_t)f32_to_bf16(val[j] * sc);
+        }
+      }
+    }
+    __syncthreads();  // red and xs are reused by the next pass
+  }
+}
+}  // namespace gv
+
+// ---------------------------------------------------------------------------
 // LoRA projections (N = r): U = s X A^T (A K-major [r][K]) and V = s dY B
 // (B N-major [K][r]), per routed row, stored as hi/lo bf16 pairs.
 // ---------------------------------------------------------------------------
@@ -2591,6 +2929,14 @@ constexpr int64_t kFewRowsPerExpert = 32;
 constexpr int kNSN = 4, kOccN = 2;
 bool few_rows(const bqm_moe_desc *d) { return d->T * d->k <= kFewRowsPerExpert * d->E; }
 
+// Decode-sized batches with at most kStreamRowsPerExpert routed rows per expert on
+// average (NVFP4 weights): the forward GEMMs stream the weights (gv::fwd_stream)
+constexpr int64_t kStreamRowsPerExpert = 1;
+static_assert(kStreamRowsPerExpert <= kFewRowsPerExpert, "the streaming forward reads the 64-row tile prefix");
+bool stream_rows(const bqm_moe_desc *d) {
+  return d->w_gu.fmt == BQM_FMT_NVFP4 && d->T * d->k <= kStreamRowsPerExpert * d->E;
+}
+
 // Training-size forward: an expert whose rows past its last full 256-row tile number at
 // most kRemRows (rows spread around a multiple of 256) has those rows computed by the
 // 64-row kernel (two workgroups per CU) rather than in a mostly empty 256-row tile.
@@ -2630,6 +2976,24 @@ bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, c
     }
   }
   return BQM_OK;
+}
+
+// weight-streaming forward (few rows per expert): tile_off_n is the prefix of 64-row
+// tiles per expert; the output columns go in blocks of gv::COLS (gate_up: 16 i-values)
+template <int ASRC, int EPI>
+bqm_status launch_gv(GemmParams p, int64_t R, int64_t T, hipStream_t s, const char *what, const int32_t *tile_off_n) {
+  p.tile_off = tile_off_n;
+  p.NT = (int)(EPI == EPI_GATEUP ? cdiv(p.I, gv::COLS / 2) : cdiv(p.N, gv::COLS));
+  // rows per pass: at most RP, as many as fit XLDS, and never more than T (an expert
+  // gets at most one row per token); the activation rows of a pass live in LDS
+  const int64_t K = p.s1.K;
+  const int64_t Kp = cdiv(K, gv::KB) * gv::KB;
+  p.rows_pass = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)gv::RP, gv::XLDS / (2 * Kp), T}));
+  const size_t lds = gv::scale_lds_bytes(K) + std::max<size_t>((size_t)p.rows_pass * Kp * 2, gv::RED_BYTES);
+  BQM_REQUIRE(p.s2.K <= 32 * gv::NW * gv::LSL, BQM_ERR_UNSUPPORTED, "%s: LoRA K %d above the streaming kernel's %d",
+              what, p.s2.K, 32 * gv::NW * gv::LSL);
+  gv::fwd_stream<ASRC, EPI><<<gemm_grid(R, p.E, p.NT, fq::BMN), gv::NTHR, lds, s>>>(p);
+  return launch_status(what);
 }
 
 // LoRA projections (N = r) streamed through LDS by direct copies
@@ -2770,7 +3134,9 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
       BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd", tn, trem)));
       mark(d, BQM_STAGE_GATE_UP_FWD, 1, s);
-    } else
+    } else if (stream_rows(d))
+      BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_gv<ASRC_X, EPI_GATEUP>(p, R, d->T, s, "gate_up fwd", tn)));
+    else
       BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd", tn, trem)));
   }
   constexpr bool aq = ASRC_X == A_GATHER_Q;
@@ -2804,6 +3170,11 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
       BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd", tn, trem)));
       mark(d, BQM_STAGE_DOWN_FWD, 1, s);
+    } else if (stream_rows(d)) {
+      if (aq)
+        BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_gv<A_ROWS_Q, EPI_STORE>(p, R, d->T, s, "down fwd", tn)));
+      else
+        BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_gv<A_ROWS, EPI_STORE>(p, R, d->T, s, "down fwd", tn)));
     } else if (aq)
       BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_fq<A_ROWS_Q, EPI_STORE>(p, R, s, "down fwd", tn, trem)));
     else

@@ -122,6 +122,21 @@ def test_small_batches():
     compare_full(small("dec_r72", r=72, T=60, E=16, k=4), lora_scale=0.5)
 
 
+def test_streaming_forward():
+    # decode-sized batches with at most one routed row per expert on average (T k <= E):
+    # the forward streams the weights, 16 rows of an expert per pass, K split over four
+    # waves.  T = 1; zipf routing over 128 experts (experts above 16 rows: several
+    # passes; the 16 empty experts NaN-poisoned, never read); one expert with about 70
+    # rows (two 64-row tiles); H = 320, I = 192 (a half 128-deep block ends each K);
+    # NVFP4 activations; LoRA rank 72 with the shared A
+    compare_full(small("st_one", T=1, E=16, k=8))
+    compare_full(small("st_zipf", logits="zipf", E=128, T=32, k=4), poison_empty=True)
+    compare_full(small("st_skew", logits="skew", E=300, T=300, k=1, r=8))
+    compare_full(small("st_odd", H=320, I=192, E=12, T=3, k=4))
+    compare_full(small("st_w4a4", act_quant=True, H=768, I=384, E=16, T=4, k=4))
+    compare_full(small("st_r72_sh", r=72, shared_a=True, E=32, T=8, k=4), lora_scale=0.5)
+
+
 def test_few_rows_activation_dynamic_range():
     # a decode-sized batch (the 64-row tile configuration) whose tokens are scaled by
     # 2^40 and 2^-40, one all-zero token and one token whose elements span 2^-30 .. 2^30,
@@ -236,6 +251,13 @@ def test_full_glm_decode_batch_sampled():
     # forward is timed: two tokens' rows and the LoRA gradients of token 0's first expert
     shape = dataclasses.replace(synth.GLM, T=64, name="glm_t64")
     sampled_full(shape, tokens=[0, 41], lora_experts="first")
+
+
+def test_full_glm_streaming_forward_sampled():
+    # the GLM shape at T = 32 (256 routed rows over 256 experts: the weight-streaming
+    # forward), two tokens' rows and the LoRA gradients of token 0's first expert
+    shape = dataclasses.replace(synth.GLM, T=32, name="glm_t32")
+    sampled_full(shape, tokens=[0, 17], lora_experts="first")
 
 
 def test_full_glm_nf4_sampled():
