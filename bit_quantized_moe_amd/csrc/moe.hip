@@ -1891,16 +1891,18 @@ constexpr int RP = 16;   // rows per pass at most (the MFMA's M)
 constexpr int PF = 4;    // blocks of loads in flight per wave
 constexpr int OCC = 4;   // workgroups per CU (at most 128 registers per lane)
 constexpr int COLS = 32; // output columns per workgroup (two sets of 16)
-constexpr int XLDS = 24 * 1024;  // LDS for a pass's activation rows
+constexpr int LDS_BUDGET = 36 * 1024;  // LDS for the weight rows' scales and a pass's activation rows
 constexpr int RED_BYTES = NW * 4 * 64 * 16;  // the waves' partial sums (aliasing the rows)
-constexpr int LSL = 2;   // LoRA up-projection: 32-deep slices per wave (its K at most 32 NW LSL)
+constexpr int LSL = 2;   // LoRA up-projection with KS: 32-deep slices per wave (its K at most 32 NW LSL)
+constexpr int KSPLIT_MIN = 4096;  // the waves split K from this K on
 // word 3 of a raw buffer resource on this GPU family (32-bit elements, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-// LDS bytes of the scales of a workgroup's 32 weight rows (K / 16 bytes each)
-__host__ __device__ constexpr int scale_lds_bytes(int64_t K) { return (int)(32 * (K / 16)); }
+// LDS bytes of the scales of the weight rows a workgroup reads (K / 16 bytes each):
+// 32 rows when its waves split K, NW times as many when each takes a column block
+__host__ __device__ constexpr int scale_lds_bytes(int64_t K, bool ks) { return (int)((ks ? 32 : 32 * NW) * (K / 16)); }
 
 struct Blk {
   u32x4 c[2];  // 32 codes of this lane's column in each set (element 2b in the low nibble of byte b)
@@ -1964,18 +1966,23 @@ __device__ __forceinline__ void use_blk(const Blk &b, const uint32_t (&sw)[2], c
 }
 
 // tile_off: the prefix of 64-row tiles per expert; NT: column blocks of COLS;
-// rows_pass rows of K activations (rounded up to a block) fit the dynamic LDS
-template <int ASRC, int EPI>
+// rows_pass rows of K activations (rounded up to a block) fit the dynamic LDS.
+// KS: the four waves split K (wave w takes blocks w, w + 4, ...) of the workgroup's one
+// column block and add their partial sums in LDS; otherwise each wave takes a whole
+// column block (the workgroup NW of them, sharing the activation rows), which gives
+// each wave a long enough run of blocks when K is short.
+template <int ASRC, int EPI, bool KS>
 __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
   static_assert(EPI == EPI_GATEUP || EPI == EPI_STORE, "forward epilogues");
   constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
   constexpr bool kGather = ASRC == A_GATHER || ASRC == A_GATHER_Q;
-  // dynamic LDS: the scales of the 32 weight rows [32][SS], then the pass's activation
-  // rows [rows_pass][Kp], which after the K loop hold the waves' partial sums
-  // [NW][4][64]: base sums of sets 0, 1, then LoRA sums of sets 0, 1
+  constexpr int WS = KS ? NW : 1;  // block stride of a wave
+  // dynamic LDS: the scales of the weight rows [KS ? 32 : 32 NW][K / 16], then the pass's
+  // activation rows [rows_pass][Kp], which after the K loop (KS) hold the waves' partial
+  // sums [NW][4][64]: base sums of sets 0, 1, then LoRA sums of sets 0, 1
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ int tile_info[4];
-  const int mt = blockIdx.x / p.NT, cb = blockIdx.x % p.NT;
+  const int mt = blockIdx.x / p.NT, cbq = blockIdx.x % p.NT;
   // the expert of row tile mt, found by all threads at once: one load per expert
   {
     int hit = 0;
@@ -1997,26 +2004,32 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
   const int m0 = (mt - __builtin_amdgcn_readfirstlane(tile_info[3])) * 64, mend = min(m0 + 64, n_e);
   const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the block loop branches on it
+  const int cb = KS ? cbq : cbq * NW + w;  // this wave's column block
+  const int kw0 = KS ? w : 0;              // this wave's first block
 
-  // this lane's weight column in each set (columns past the output read column 0)
+  // this lane's weight column in each set (a wave past the last column block reads the
+  // last 16 rows and stores nothing)
   const Seg &s = p.s1;
-  int col[2];
+  int col[2], row0[2];  // row0: the first weight row of each set
   bool col_ok[2];
   if constexpr (EPI == EPI_GATEUP) {
     const int i = cb * 16 + c;
+    row0[0] = min(cb * 16, p.I - 16);
+    row0[1] = p.I + row0[0];
     col_ok[0] = col_ok[1] = i < p.I;
-    col[0] = col_ok[0] ? i : 0;
-    col[1] = col_ok[0] ? p.I + i : 0;
+    col[0] = col_ok[0] ? i : row0[0];
+    col[1] = col_ok[0] ? p.I + i : row0[1];
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = cb * COLS + 16 * j + c;
+      row0[j] = min(cb * COLS + 16 * j, p.N - 16);
       col_ok[j] = n < p.N;
-      col[j] = col_ok[j] ? n : 0;
+      col[j] = col_ok[j] ? n : row0[j];
     }
   }
   const int K = s.K;
-  // the expert's slice of codes and of scales as buffers (loads past them read 0)
+  // the expert's slice of codes as a buffer (loads past it read 0)
   const int64_t slice = s.b_rows * s.b_cols;
   const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(reinterpret_cast<const uint8_t *>(s.b) + e * (slice / 2)), 0, (int)(slice / 2), kRsrcWord3);
@@ -2024,14 +2037,15 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) oc[j] = (uint32_t)col[j] * (uint32_t)(s.b_cols / 2) + 16 * g;
   const int nkb = (K + KB - 1) / KB;
-  const int nb = nkb > w ? (nkb - w + NW - 1) / NW : 0;  // this wave's blocks w + NW j
-  const int Kp = nkb * KB, K8 = K / 8, Kp8 = Kp / 8;      // LDS row stride: K rounded up, zero past K
-  // the E4M3 scales of the workgroup's 32 weight rows (K / 16 bytes each, contiguous in
-  // HBM per set of 16 rows) go to LDS once, by direct copies: 2-byte loads of each lane's
-  // own scales would cost one memory transaction per row and block
+  const int nb = nkb > kw0 ? (nkb - kw0 + WS - 1) / WS : 0;  // this wave's blocks kw0 + WS j
+  const int Kp = nkb * KB, K8 = K / 8, Kp8 = Kp / 8;  // LDS row stride: K rounded up, zero past K
+  // the E4M3 scales of the waves' weight rows (K / 16 bytes each, contiguous in HBM per
+  // set of 16 rows) go to LDS once, by direct copies: 2-byte loads of each lane's own
+  // scales would cost one memory transaction per row and block
   const int SB = K / 16;  // scale bytes per weight row (a multiple of 4)
   uint8_t *sc = reinterpret_cast<uint8_t *>(xs);
-  uint16_t *xa = reinterpret_cast<uint16_t *>(sc + scale_lds_bytes(K));  // the activation rows after them
+  uint8_t *scw = sc + (KS ? 0 : w * 32 * SB);  // this wave's rows
+  uint16_t *xa = reinterpret_cast<uint16_t *>(sc + scale_lds_bytes(K, KS));  // the activation rows after them
   f32x4(*red)[4][64] = reinterpret_cast<f32x4(*)[4][64]>(xa);
   const float esc = kQA ? 1.0f : uniform_load(s.b_sd + e);
   const Seg &l = p.s2;
@@ -2052,10 +2066,9 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
       // set j's 16 weight rows hold 16 SB contiguous bytes of scales (16-byte aligned)
       const uint8_t *sg = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16);
       for (int j = 0; j < 2; ++j) {
-        const int64_t r0j = EPI == EPI_GATEUP ? (j ? (int64_t)p.I + cb * 16 : cb * 16) : (int64_t)cb * COLS + 16 * j;
-        const uint8_t *src = sg + r0j * SB;
-        for (int c0 = 64 * w; c0 < SB; c0 += 64 * NW) {  // 16-byte chunks of the 16 SB bytes
-          const uint32_t dst = (uint32_t)(uintptr_t)(const fq::lds_void *)(sc + 16 * j * SB + 16 * c0);
+        const uint8_t *src = sg + (int64_t)row0[j] * SB;
+        for (int c0 = KS ? 64 * w : 0; c0 < SB; c0 += 64 * WS) {  // 16-byte chunks of the 16 SB bytes
+          const uint32_t dst = (uint32_t)(uintptr_t)(const fq::lds_void *)(scw + 16 * j * SB + 16 * c0);
           if (c0 + lane < SB) fq::dma_b128(src + 16 * (c0 + lane), dst);
         }
       }
@@ -2073,7 +2086,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
     const uint16_t *xrow = xa + min(c, nr - 1) * Kp + 32 * g;
     // this lane's scale pair of a block at k: bytes (k + 32 g) / 16 of its rows (clamped
     // into the row past K, where the activations are zero)
-    const uint8_t *srow0 = sc + c * SB, *srow1 = sc + (16 + c) * SB;
+    const uint8_t *srow0 = scw + (col[0] - row0[0]) * SB, *srow1 = scw + (16 + col[1] - row0[1]) * SB;
     auto scales = [&](int k, uint32_t(&sw)[2]) {
       const int o = min(k + 32 * g, K - 32) / 16;
       sw[0] = *reinterpret_cast<const uint16_t *>(srow0 + o);
@@ -2085,23 +2098,26 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       if (u < nb) {
-        const int k = (w + NW * u) * KB;
+        const int k = (kw0 + WS * u) * KB;
         load_blk(buf[u], rc, oc, k + 32 * g < K ? k : 0);
       }
     }
     // LoRA up-projection operands (A = the hi/lo pair rows at k < s2.K, B = the expert's
-    // LoRA matrix at k mod kmod), 32-deep slices w, w + NW, ... of this wave
-    u32x4 la[LSL], lb[LSL][2];
+    // LoRA matrix at k mod kmod): with KS, this wave's 32-deep slices w, w + NW, ...
+    // requested now; otherwise every slice, after the K loop
     const uint16_t *ar = reinterpret_cast<const uint16_t *>(l.a) + (int64_t)(rb + pos) * l.a_ld;
-#pragma unroll
-    for (int q = 0; q < LSL; ++q) {
-      const int k = 32 * (w + NW * q) + 8 * g;
+    auto lora_ops = [&](int k, u32x4 &la, u32x4(&lb)[2]) {
       const bool ok = k < l.K;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      la[q] = (ok && xok) ? *reinterpret_cast<const u32x4 *>(ar + k) : z;
+      la = (ok && xok) ? *reinterpret_cast<const u32x4 *>(ar + k) : z;
       const int kb = ok ? k % l.kmod : 0;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) lb[q][j] = ok ? *reinterpret_cast<const u32x4 *>(bl[j] + kb) : z;
+      for (int j = 0; j < 2; ++j) lb[j] = ok ? *reinterpret_cast<const u32x4 *>(bl[j] + kb) : z;
+    };
+    u32x4 la[KS ? LSL : 1], lb[KS ? LSL : 1][2];
+    if constexpr (KS) {
+#pragma unroll
+      for (int q = 0; q < LSL; ++q) lora_ops(32 * (w + NW * q) + 8 * g, la[q], lb[q]);
     }
     // the direct copies are not tracked by the compiler's wait counts: wait for every load
     // issued so far (the row copies are the oldest), then the barrier
@@ -2112,7 +2128,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
     // that each use waits only for its own block); then the last blocks without refills
     int j0 = 0;
     auto use = [&](int u, int j) {
-      const int k = (w + NW * j) * KB;
+      const int k = (kw0 + WS * j) * KB;
       uint32_t sw[2];
       scales(k, sw);
       use_blk(buf[u], sw, xrow + k, acc);
@@ -2121,7 +2137,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
         use(u, j0 + u);
-        const int kn = (w + NW * (j0 + u + PF)) * KB;
+        const int kn = (kw0 + WS * (j0 + u + PF)) * KB;
         load_blk(buf[u], rc, oc, kn + 32 * g < K ? kn : 0);
       }
     }
@@ -2130,7 +2146,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
       if (j0 + u < nb) {
         use(u, j0 + u);
         if (j0 + u + PF < nb) {
-          const int kn = (w + NW * (j0 + u + PF)) * KB;
+          const int kn = (kw0 + WS * (j0 + u + PF)) * KB;
           load_blk(buf[u], rc, oc, kn + 32 * g < K ? kn : 0);
         }
       }
@@ -2139,30 +2155,49 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
     for (int u = 0; u < PF; ++u)
       if (j0 + PF + u < nb) use(u, j0 + PF + u);
     f32x4 lacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    if constexpr (KS) {
 #pragma unroll
-    for (int q = 0; q < LSL; ++q)
+      for (int q = 0; q < LSL; ++q)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) lacc[j] = mfma16(la[q], lb[q][j], lacc[j]);
+        for (int j = 0; j < 2; ++j) lacc[j] = mfma16(la[q], lb[q][j], lacc[j]);
+    } else {
+#pragma unroll 2
+      for (int k0 = 0; k0 < l.K; k0 += 32) {
+        lora_ops(k0 + 8 * g, la[0], lb[0]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) lacc[j] = mfma16(la[0], lb[0][j], lacc[j]);
+      }
+    }
 
-    // the four waves' partial sums, added in wave order by wave 0
-    __syncthreads();  // every wave is done reading the activation rows
-    red[w][0][lane] = acc[0];
-    red[w][1][lane] = acc[1];
-    red[w][2][lane] = lacc[0];
-    red[w][3][lane] = lacc[1];
-    __syncthreads();
-    if (w == 0) {
-      f32x4 v[2], lv[2];
+    f32x4 v[2], lv[2];
+    if constexpr (KS) {
+      // the four waves' partial sums, added in wave order by wave 0
+      __syncthreads();  // every wave is done reading the activation rows
+      red[w][0][lane] = acc[0];
+      red[w][1][lane] = acc[1];
+      red[w][2][lane] = lacc[0];
+      red[w][3][lane] = lacc[1];
+      __syncthreads();
+      if (w == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        v[j] = red[0][j][lane];
-        lv[j] = red[0][2 + j][lane];
+        for (int j = 0; j < 2; ++j) {
+          v[j] = red[0][j][lane];
+          lv[j] = red[0][2 + j][lane];
 #pragma unroll
-        for (int q = 1; q < NW; ++q) {
-          v[j] += red[q][j][lane];
-          lv[j] += red[q][2 + j][lane];
+          for (int q = 1; q < NW; ++q) {
+            v[j] += red[q][j][lane];
+            lv[j] += red[q][2 + j][lane];
+          }
         }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        v[j] = acc[j];
+        lv[j] = lacc[j];
+      }
+    }
+    if (!KS || w == 0) {
       // lane (c, g) holds rows 4 g + t (t = 0..3) of column c of each set
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -2929,12 +2964,15 @@ constexpr int64_t kFewRowsPerExpert = 32;
 constexpr int kNSN = 4, kOccN = 2;
 bool few_rows(const bqm_moe_desc *d) { return d->T * d->k <= kFewRowsPerExpert * d->E; }
 
-// Decode-sized batches with at most kStreamRowsPerExpert routed rows per expert on
-// average (NVFP4 weights): the forward GEMMs stream the weights (gv::fwd_stream)
-constexpr int64_t kStreamRowsPerExpert = 1;
-static_assert(kStreamRowsPerExpert <= kFewRowsPerExpert, "the streaming forward reads the 64-row tile prefix");
-bool stream_rows(const bqm_moe_desc *d) {
-  return d->w_gu.fmt == BQM_FMT_NVFP4 && d->T * d->k <= kStreamRowsPerExpert * d->E;
+// Decode-sized batches (NVFP4 weights): a forward GEMM streams the weights
+// (gv::fwd_stream) with at most this many routed rows per expert on average.  Measured
+// on the GLM shape: gate_up streams faster up to 2 rows (its 12 KB activation rows fit
+// two per pass), down up to at least 4.
+constexpr int64_t kStreamRowsGateUp = 2, kStreamRowsDown = 4;
+static_assert(kStreamRowsGateUp <= kFewRowsPerExpert && kStreamRowsDown <= kFewRowsPerExpert,
+              "the streaming forward reads the 64-row tile prefix");
+bool stream_rows(const bqm_moe_desc *d, int64_t per_expert) {
+  return d->w_gu.fmt == BQM_FMT_NVFP4 && d->T * d->k <= per_expert * d->E;
 }
 
 // Training-size forward: an expert whose rows past its last full 256-row tile number at
@@ -2983,16 +3021,25 @@ bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, c
 template <int ASRC, int EPI>
 bqm_status launch_gv(GemmParams p, int64_t R, int64_t T, hipStream_t s, const char *what, const int32_t *tile_off_n) {
   p.tile_off = tile_off_n;
-  p.NT = (int)(EPI == EPI_GATEUP ? cdiv(p.I, gv::COLS / 2) : cdiv(p.N, gv::COLS));
-  // rows per pass: at most RP, as many as fit XLDS, and never more than T (an expert
-  // gets at most one row per token); the activation rows of a pass live in LDS
+  const int NT = (int)(EPI == EPI_GATEUP ? cdiv(p.I, gv::COLS / 2) : cdiv(p.N, gv::COLS));
+  // rows per pass: at most RP, as many as fit the LDS budget beside the scales, and never
+  // more than T (an expert gets at most one row per token); a pass's rows live in LDS
   const int64_t K = p.s1.K;
   const int64_t Kp = cdiv(K, gv::KB) * gv::KB;
-  p.rows_pass = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)gv::RP, gv::XLDS / (2 * Kp), T}));
-  const size_t lds = gv::scale_lds_bytes(K) + std::max<size_t>((size_t)p.rows_pass * Kp * 2, gv::RED_BYTES);
-  BQM_REQUIRE(p.s2.K <= 32 * gv::NW * gv::LSL, BQM_ERR_UNSUPPORTED, "%s: LoRA K %d above the streaming kernel's %d",
-              what, p.s2.K, 32 * gv::NW * gv::LSL);
-  gv::fwd_stream<ASRC, EPI><<<gemm_grid(R, p.E, p.NT, fq::BMN), gv::NTHR, lds, s>>>(p);
+  // the waves split K when K is long (enough blocks per wave), else each takes a column block
+  const bool ks = K >= gv::KSPLIT_MIN;
+  const int64_t xlds = gv::LDS_BUDGET - gv::scale_lds_bytes(K, ks);
+  p.rows_pass = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)gv::RP, xlds / (2 * Kp), T}));
+  const size_t xb = (size_t)p.rows_pass * Kp * 2;
+  const size_t lds = gv::scale_lds_bytes(K, ks) + (ks ? std::max<size_t>(xb, gv::RED_BYTES) : xb);
+  BQM_REQUIRE(!ks || p.s2.K <= 32 * gv::NW * gv::LSL, BQM_ERR_UNSUPPORTED,
+              "%s: LoRA K %d above the streaming kernel's %d", what, p.s2.K, 32 * gv::NW * gv::LSL);
+  p.NT = ks ? NT : (int)cdiv(NT, gv::NW);
+  const int grid = gemm_grid(R, p.E, p.NT, fq::BMN);
+  if (ks)
+    gv::fwd_stream<ASRC, EPI, true><<<grid, gv::NTHR, lds, s>>>(p);
+  else
+    gv::fwd_stream<ASRC, EPI, false><<<grid, gv::NTHR, lds, s>>>(p);
   return launch_status(what);
 }
 
@@ -3134,7 +3181,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       BQM_TRY(nf4_fp32_absmax(d->w_gu, w, p.s1, s));
       BQM_TRY((launch_fq<A_GATHER, EPI_GATEUP, false, fq::WF_NF4>(p, R, s, "gate_up fwd", tn, trem)));
       mark(d, BQM_STAGE_GATE_UP_FWD, 1, s);
-    } else if (stream_rows(d))
+    } else if (stream_rows(d, kStreamRowsGateUp))
       BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_gv<ASRC_X, EPI_GATEUP>(p, R, d->T, s, "gate_up fwd", tn)));
     else
       BQM_STAGE(d, BQM_STAGE_GATE_UP_FWD, s, (launch_fq<ASRC_X, EPI_GATEUP>(p, R, s, "gate_up fwd", tn, trem)));
@@ -3170,7 +3217,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
       BQM_TRY(nf4_fp32_absmax(d->w_dn, w, p.s1, s));
       BQM_TRY((launch_fq<A_ROWS, EPI_STORE, false, fq::WF_NF4>(p, R, s, "down fwd", tn, trem)));
       mark(d, BQM_STAGE_DOWN_FWD, 1, s);
-    } else if (stream_rows(d)) {
+    } else if (stream_rows(d, kStreamRowsDown)) {
       if (aq)
         BQM_STAGE(d, BQM_STAGE_DOWN_FWD, s, (launch_gv<A_ROWS_Q, EPI_STORE>(p, R, d->T, s, "down fwd", tn)));
       else

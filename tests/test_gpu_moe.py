@@ -123,13 +123,19 @@ def test_small_batches():
 
 
 def test_streaming_forward():
-    # decode-sized batches with at most one routed row per expert on average (T k <= E):
-    # the forward streams the weights, 16 rows of an expert per pass, K split over four
-    # waves.  T = 1; zipf routing over 128 experts (experts above 16 rows: several
+    # decode-sized batches with a few routed rows per expert on average (T k <= 2 E for
+    # gate_up, <= 4 E for down): the forward streams the weights, up to 16 rows of an
+    # expert per pass.  T = 1; zipf routing over 128 experts (experts above 16 rows: several
     # passes; the 16 empty experts NaN-poisoned, never read); one expert with about 70
     # rows (two 64-row tiles); H = 320, I = 192 (a half 128-deep block ends each K);
-    # NVFP4 activations; LoRA rank 72 with the shared A
+    # NVFP4 activations; LoRA rank 72 with the shared A; 2 and 4 rows per expert on
+    # average (both forward GEMMs streaming, then down only); K of 4096 (the waves split
+    # K; shorter K gives each wave its own column block), bf16 and NVFP4 activations
     compare_full(small("st_one", T=1, E=16, k=8))
+    compare_full(small("st_2", T=8, E=16, k=4))
+    compare_full(small("st_4", act_quant=True, H=768, I=384, T=16, E=16, k=4))
+    compare_full(small("st_ks", H=256, I=4096, E=8, T=3, k=2))
+    compare_full(small("st_ks_q", act_quant=True, H=256, I=4096, E=8, T=3, k=2))
     compare_full(small("st_zipf", logits="zipf", E=128, T=32, k=4), poison_empty=True)
     compare_full(small("st_skew", logits="skew", E=300, T=300, k=1, r=8))
     compare_full(small("st_odd", H=320, I=192, E=12, T=3, k=4))
