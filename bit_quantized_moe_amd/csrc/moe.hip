@@ -2389,9 +2389,22 @@ __global__ void __launch_bounds__(NTHR, 2) gemm_lora_proj(GemmParams p) {
 // expert, which leaves most of the GPU idle when the batch is a few tokens.
 template <int ASRC>
 __global__ void __launch_bounds__(256) lora_proj_rows(GemmParams p) {
-  const int e = blockIdx.y;
-  const int rb = p.offsets[e], n_e = p.offsets[e + 1] - rb;
-  if (n_e == 0) return;
+  // workgroup row blockIdx.y: one 64-row tile of the prefix p.tile_off (at most 16 tokens:
+  // one tile per expert with rows), its expert found by all threads at once
+  __shared__ int tile_e;
+  const int mt = blockIdx.y;
+  {
+    int hit = 0;
+    for (int e = threadIdx.x; e < p.E; e += 256)
+      if (p.tile_off[e] <= mt && mt < p.tile_off[e + 1]) {
+        tile_e = e;
+        hit = 1;
+      }
+    if (!__syncthreads_or(hit)) return;  // past the last tile: the grid is an upper bound
+  }
+  const int e = tile_e;
+  const int m0 = (mt - p.tile_off[e]) * 64;
+  const int rb = p.offsets[e] + m0, n_e = min(p.offsets[e + 1] - rb, 64);  // this tile's rows
   const int lane = threadIdx.x & 63;
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);  // one output column per wave
   if (n >= p.N) return;
@@ -3049,10 +3062,16 @@ bqm_status launch_gv(GemmParams p, int64_t R, int64_t T, hipStream_t s, const ch
 constexpr int64_t kFewTokens = 16;
 
 template <int ASRC, bool BNM>
-bqm_status launch_lp(const GemmParams &p, int64_t R, hipStream_t s, const char *what, int64_t T = -1) {
+bqm_status launch_lp(const GemmParams &p, int64_t R, hipStream_t s, const char *what, int64_t T = -1,
+                     const int32_t *tile_off_n = nullptr) {
   static_assert(lp::BM == BM, "tile offsets are computed for BM rows");
-  if (!BNM && T >= 0 && T <= kFewTokens) {
-    lora_proj_rows<ASRC><<<dim3((unsigned)cdiv(p.N, 4), (unsigned)p.E), 256, 0, s>>>(p);
+  if (!BNM && T >= 0 && T <= kFewTokens && tile_off_n) {
+    // one workgroup row per 64-row tile of tile_off_n (one per expert with rows when
+    // every token routes to distinct experts); the grid is an upper bound on the tiles
+    GemmParams q = p;
+    q.tile_off = tile_off_n;
+    const int64_t tiles = std::max<int64_t>(cdiv(R, fq::BMN) + std::min<int64_t>(p.E, R), 1);
+    lora_proj_rows<ASRC><<<dim3((unsigned)cdiv(p.N, 4), (unsigned)tiles), 256, 0, s>>>(q);
     return launch_status(what);
   }
   const int grid = gemm_grid(R, p.E, p.NT);
@@ -3161,7 +3180,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.out_scale = ls;
     p.div_e = fold_fwd ? d->w_gu.s_dec : nullptr;
     p.out0 = ugu;
-    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch_lp<A_GATHER, false>(p, R, s, "lora_a gate_up", d->T)));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch_lp<A_GATHER, false>(p, R, s, "lora_a gate_up", d->T, tn)));
   }
   // h = X~ W~_gu^T + U_gu B_gu^T; a = silu(g) u
   {
@@ -3200,7 +3219,7 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
     p.out_scale = ls;
     p.div_e = fold_fwd ? d->w_dn.s_dec : nullptr;
     p.out0 = udn;
-    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch_lp<A_ROWS, false>(p, R, s, "lora_a down", d->T)));
+    BQM_STAGE(d, BQM_STAGE_LORA_A_DN, s, (launch_lp<A_ROWS, false>(p, R, s, "lora_a down", d->T, tn)));
   }
   // y = a~ W~_dn^T + U_dn B_dn^T
   {
@@ -3254,10 +3273,9 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
   }
   BQM_STAGE(d, BQM_STAGE_PERMUTE, s, permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
                          w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off),
-                         rem_split(d) ? -kRemRows : fq::BMN, w.at<int32_t>(w.L.tile_off_n), s));
+                         rem_split(d) ? -kRemRows : fq::BMN, w.at<int32_t>(w.L.tile_off_n), s, topk_w,
+                         w.at<float>(w.L.tw)));  // (and the copy of the routing weights)
   if (R == 0) return BQM_OK;
-  if (hipMemcpyAsync(w.at<float>(w.L.tw), topk_w, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
-    return launch_status("bqm_moe_fwd: copy of routing weights");
   const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
   if (d->act_quant) {
     BQM_STAGE(d, BQM_STAGE_ACT_QUANT_X, s,

@@ -15,7 +15,40 @@ namespace {
 
 constexpr int kChunk = 2048;  // routed pairs per histogram/scatter chunk
 
-// One wave per token: the E logits are spread over the 64 lanes (up to 16 per lane).
+// Wave-wide reductions with DPP moves inside each row of 16 lanes (xor 1, xor 2, the
+// half-row mirror, the row mirror), then the four rows' results read from lanes 0, 16,
+// 32 and 48: a few cycles each, where a butterfly of cross-lane shuffles waits for the
+// LDS crossbar at every step.
+template <class F>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, F op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = op(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const uint32_t a = op((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = op((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return op(a, b);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  return __uint_as_float(wave_reduce_u32(__float_as_uint(v), [](uint32_t x, uint32_t y) {
+    return __float_as_uint(__uint_as_float(x) + __uint_as_float(y));
+  }));
+}
+// float -> uint32 with the same order (-inf lowest; NaN above +inf or below -inf by sign)
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// One wave per token: the E logits are spread over the 64 lanes (NJ <= 16 per lane,
+// E <= 64 NJ).
+template <int NJ>
 __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ logits, int64_t T,
                                                    int E, int k, int renorm,
                                                    int32_t *__restrict__ topk_idx,
@@ -24,24 +57,26 @@ __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ lo
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float *lg = logits + t * E;
-  float v[16];
+  float v[NJ];
   float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     int e = lane + 64 * j;
     v[j] = e < E ? lg[e] : -INFINITY;
     mx = fmaxf(mx, v[j]);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  // the maximum over the wave (fmaxf ignores NaN, as the lane-local maximum does)
+  {
+    const uint32_t km = wave_max_u32(mx != mx ? 0u : order_key(mx));
+    mx = __uint_as_float((km & 0x80000000u) ? (km & 0x7FFFFFFFu) : ~km);
+  }
   float sum = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     int e = lane + 64 * j;
     if (e < E) sum += expf(v[j] - mx);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  sum = wave_sum_f32(sum);
   uint32_t taken = 0u;  // bit j: this lane's slot j already chosen
   float wsum = 0.0f;
   float wsel[16];
@@ -51,7 +86,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ lo
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       int e = lane + 64 * j;
       bool ok = e < E && !((taken >> j) & 1u);
       if (ok && (v[j] > bv || (v[j] == bv && e < bi))) {
@@ -59,15 +94,11 @@ __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ lo
         bi = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      float ov = __shfl_xor(bv, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    // the wave's best: the largest value, then among the lanes holding it the lowest index
+    const uint32_t kb = order_key(bv);
+    const uint32_t kmax = wave_max_u32(kb);
+    bi = (int)wave_min_u32(kb == kmax ? (uint32_t)bi : 0x7FFFFFFFu);
+    bv = __uint_as_float((kmax & 0x80000000u) ? (kmax & 0x7FFFFFFFu) : ~kmax);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     float w = expf(bv - mx) / sum;
     wsel[r] = w;
@@ -228,10 +259,13 @@ __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ i
 __global__ void __launch_bounds__(1024) perm_one(const int32_t *__restrict__ idx, int R, int E,
                                                  int32_t *__restrict__ offsets, int bm, int32_t *__restrict__ tile_off,
                                                  int bm2, int32_t *__restrict__ tile_off2, int32_t *__restrict__ perm,
-                                                 int32_t *__restrict__ inv) {
+                                                 int32_t *__restrict__ inv, const float *__restrict__ w_in,
+                                                 float *__restrict__ w_out) {
   extern __shared__ int32_t cnt[];  // E + 1 buckets
   __shared__ int32_t wsum[16][3];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (w_in)
+    for (int f = t; f < R; f += 1024) w_out[f] = w_in[f];
   for (int e = t; e <= E; e += 1024) cnt[e] = 0;
   __syncthreads();
   for (int f = t; f < R; f += 1024) atomicAdd(&cnt[bucket_of(idx[f], E)], 1);
@@ -308,11 +342,15 @@ size_t permute_ws_bytes(int64_t R, int E) {
 
 bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
                           int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off, int bm2,
-                          int32_t *tile_off2, hipStream_t s) {
+                          int32_t *tile_off2, hipStream_t s, const float *w_in, float *w_out) {
   if (R > 0 && R <= kChunk) {
     perm_one<<<1, 1024, (E + 1) * sizeof(int32_t), s>>>(topk_idx, (int)R, E, offsets, bm, tile_off, bm2, tile_off2,
-                                                         perm, inv);
+                                                         perm, inv, w_in, w_out);
     return launch_status("perm_one");
+  }
+  if (R > 0 && w_in) {
+    if (hipMemcpyAsync(w_out, w_in, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+      return launch_status("copy of routing weights");
   }
   const int nchunks = (int)cdiv(R, kChunk);
   if (R > 0) {
@@ -344,8 +382,18 @@ extern "C" bqm_status bqm_route(const float *logits, int64_t T, int32_t E, int32
   BQM_REQUIRE(logits && topk_idx && topk_w, BQM_ERR_INVALID_ARG, "bqm_route: NULL pointer");
   BQM_REQUIRE(aligned16(logits) && aligned16(topk_idx) && aligned16(topk_w), BQM_ERR_ALIGN,
               "bqm_route: pointer not 16-byte aligned");
-  route_kernel<<<(unsigned)cdiv(T, 4), 256, 0, as_stream(stream)>>>(logits, T, E, k, renorm,
-                                                                    topk_idx, topk_w);
+  const unsigned grid = (unsigned)cdiv(T, 4);
+  hipStream_t s = as_stream(stream);
+  if (E <= 64)
+    route_kernel<1><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w);
+  else if (E <= 128)
+    route_kernel<2><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w);
+  else if (E <= 256)
+    route_kernel<4><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w);
+  else if (E <= 512)
+    route_kernel<8><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w);
+  else
+    route_kernel<16><<<grid, 256, 0, s>>>(logits, T, E, k, renorm, topk_idx, topk_w);
   return launch_status("route_kernel");
 }
 

@@ -299,12 +299,14 @@ def test_nvfp4_dequantize_shapes(shape, per_row):
 # (the permutation ranks equal experts within each 64-pair group by lane: E = 16 with
 # ties puts many equal experts in every group; E = 1000 is not a multiple of the
 # 64-lane scan width; E = 1024 is the largest expert count, several 2048-pair chunks;
-# up to 2048 routed pairs run the one-workgroup form, ties and E = 1024 included)
+# up to 2048 routed pairs run the one-workgroup form, ties and E = 1024 included; the
+# router keeps 1, 2, 4, 8 or 16 logits per lane: E = 1 .. 1024 covers each)
 @pytest.mark.parametrize("T,E,k,kind", [(64, 8, 2, "normal"), (1000, 256, 8, "uniform"),
                                         (333, 128, 8, "ties"), (50, 64, 16, "zipf"), (1, 1, 1, "normal"),
                                         (5000, 16, 2, "ties"), (700, 1000, 3, "zipf"),
                                         (3000, 1024, 4, "uniform"), (300, 16, 4, "ties"),
-                                        (200, 1024, 8, "uniform"), (256, 1000, 8, "zipf")])
+                                        (200, 1024, 8, "uniform"), (256, 1000, 8, "zipf"),
+                                        (400, 512, 6, "ties"), (20, 300, 2, "zipf"), (9, 65, 5, "ties")])
 def test_route_and_permute_bit_exact(T, E, k, kind):
     import torch
     dev = gpu()
