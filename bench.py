@@ -292,7 +292,7 @@ def time_layer(s, inp, wgu, wdn, ev, sh, steps, warmup):
     return res
 
 
-def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 64, 256), reps=20):
+def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 32, 64, 256), reps=20, warmup=3):
     """Decode-shaped forward (route + moe_fwd only) at a few tokens over the same
     quantized experts and LoRA: the time against reading each hit expert's NVFP4
     weights (codes + E4M3 scales of gate_up and down) once."""
@@ -317,6 +317,8 @@ def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 64, 256), reps=20):
             bqm.bqm_route(inp.logits, T, s.E, s.k, 0, idx, tw)
             bqm.bqm_moe_fwd(d, inp.x, idx, tw, out, ws)
 
+        for _ in range(warmup):
+            run()
         ms = time_calls(ev, sh, run, reps)
         hit = int(torch.unique(idx).numel())
         wbytes = hit * per_expert
@@ -502,6 +504,9 @@ def main():
                     help="only the layer step of this workload (for profiling): prints its timings, no bench line")
     ap.add_argument("--summarize-counters", metavar="DIR",
                     help="print the per-kernel table of a rocprofv3 --pmc --kernel-trace csv run under DIR, no GPU")
+    ap.add_argument("--decode-tokens", type=int, metavar="T",
+                    help="only the decode-shaped forward (route + moe_fwd) of the GLM shape at T tokens, "
+                         "`steps` times after `warmup` (for profiling): prints its timings, no bench line")
     ap.add_argument("--library-reference", action="store_true",
                     help="only time the vendor library's bf16 GEMMs at the GLM gate_up shape")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -534,6 +539,18 @@ def main():
     bqm.load()
     if args.library_reference:
         print(json.dumps(library_gemm_reference(HipEvents(), torch.cuda.current_stream().cuda_stream)), flush=True)
+        return
+    if args.decode_tokens:
+        s1 = synth.GLM
+        inp1 = synth.layer_inputs(s1, device=dev)
+        wgu1 = bqm.quantize_stack(inp1.w_gu, s1.fmt)
+        wdn1 = bqm.quantize_stack(inp1.w_dn, s1.fmt)
+        del inp1
+        torch.cuda.empty_cache()
+        ev = HipEvents()
+        rows = decode_sweep(s1, wgu1, wdn1, ev, torch.cuda.current_stream().cuda_stream,
+                            tokens=(args.decode_tokens,), reps=args.steps, warmup=args.warmup)
+        print(json.dumps({"workload": "glm5.2 decode forward", **rows[0]}), flush=True)
         return
     if args.workload:
         ws_ = {"glm": synth.GLM, "glm_nf4": synth.GLM_NF4, "qwen": synth.QWEN,
