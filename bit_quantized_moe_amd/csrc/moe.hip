@@ -93,6 +93,9 @@ struct GemmParams {
   const int32_t *tile_rem;
   int rem_rows;
   int rows_pass;  // the weight-streaming forward: rows per pass (its activation rows in LDS)
+  // EPI_DOWN_DGRAD: per routed row and output column tile, the sum over the tile's columns
+  // of da_u * a (the routing-weight gradient's share of the tile), [R][NT]; NULL: none
+  float *dtw_part;
 };
 
 __constant__ float c_nf4[16] = BQM_NF4_LEVELS;
@@ -281,7 +284,8 @@ __device__ __forceinline__ void epilogue(const GemmParams &p, const f32x16 (&acc
 // load) per 4 values instead of one per value, and one routing weight per row.
 template <int TM, int TN, int BN, int EPI, bool FULL>
 __device__ __forceinline__ void epilogue_t_body(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0,
-                                                int n_e, int rb, int row0, int col0, int lane, float esc) {
+                                                int n_e, int rb, int row0, int col0, int lane, float esc,
+                                                float (&dp)[TM], bool dtw) {
   static_assert(EPI == EPI_STORE || EPI == EPI_GATEUP || EPI == EPI_DOWN_DGRAD, "transposed epilogues");
   const int g = lane >> 5;
   const float sc = esc * p.out_scale;
@@ -364,9 +368,13 @@ __device__ __forceinline__ void epilogue_t_body(const GemmParams &p, const f32x1
                 for (int h = 0; h < 2; ++h) {
                   const int j = 2 * t + h;
                   const float sg = sigmoid_f(gg[j]);
-                  const float da = w * (acc[tm][tn][4 * q + j] * esc);
+                  const float dau = acc[tm][tn][4 * q + j] * esc;
+                  const float da = w * dau;
                   dgv[h] = da * uu[j] * sg * (1.0f + gg[j] * (1.0f - sg));
                   duv[h] = da * gg[j] * sg;
+                  // routing-weight gradient: da_u times the forward's bf16 a (the same
+                  // expression and rounding as the gate_up epilogue)
+                  if (dtw) dp[tm] += dau * __uint_as_float(f32_to_bf16(gg[j] * sg * uu[j]) << 16);
                 }
                 dg2[t] = f32_to_bf16(dgv[0]) | (f32_to_bf16(dgv[1]) << 16);
                 du2[t] = f32_to_bf16(duv[0]) | (f32_to_bf16(duv[1]) << 16);
@@ -380,16 +388,50 @@ __device__ __forceinline__ void epilogue_t_body(const GemmParams &p, const f32x1
   }
 }
 
+// dp (EPI_DOWN_DGRAD with p.dtw_part set): per 32-row tile, this lane's sum of da_u * a
+// over its columns, added to dp[tm]
 template <int TM, int TN, int BN, int EPI>
 __device__ __forceinline__ void epilogue_t(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0, int n_e,
-                                           int rb, int row0, int col0, int lane, float esc) {
+                                           int rb, int row0, int col0, int lane, float esc, float (&dp)[TM]) {
   const bool rows_in = m0 + row0 + TM * 32 <= n_e;
   const bool cols_in = EPI == EPI_GATEUP ? nt * (BN / 2) + col0 / 2 + (TN / 2) * 32 <= p.I
                                          : nt * BN + col0 + TN * 32 <= p.N;
+  const bool dtw = EPI == EPI_DOWN_DGRAD && p.dtw_part != nullptr;
   if (rows_in && cols_in)
-    epilogue_t_body<TM, TN, BN, EPI, true>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+    epilogue_t_body<TM, TN, BN, EPI, true>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc, dp, dtw);
   else
-    epilogue_t_body<TM, TN, BN, EPI, false>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc);
+    epilogue_t_body<TM, TN, BN, EPI, false>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc, dp, dtw);
+}
+template <int TM, int TN, int BN, int EPI>
+__device__ __forceinline__ void epilogue_t(const GemmParams &p, const f32x16 (&acc)[TM][TN], int nt, int m0, int n_e,
+                                           int rb, int row0, int col0, int lane, float esc) {
+  float dp[TM];
+  epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, col0, lane, esc, dp);
+}
+
+// The routing-weight gradient's partial sums of one output tile (4 waves of 64 columns,
+// TM 32-row tiles): lanes L and L ^ 32 hold the two halves of a wave's columns for row
+// L % 32, the four waves' sums are added in wave order through LDS (lds: TM * 128 floats,
+// free: the caller has finished its stages), and the tile's rows get part[row][nt].
+template <int TM>
+__device__ __forceinline__ void dtw_tile(const GemmParams &p, float (&dp)[TM], int nt, int m0, int n_e, int rb,
+                                         int wn, int lane, float *lds) {
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) dp[tm] += __shfl_xor(dp[tm], 32, 64);
+  __syncthreads();
+  if (lane < 32) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) lds[wn * TM * 32 + tm * 32 + lane] = dp[tm];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < TM * 32; i += blockDim.x) {
+    const int pos = m0 + i;
+    if (pos < n_e) {
+      float s = lds[i];
+      for (int q = 1; q < 4; ++q) s += lds[q * TM * 32 + i];
+      p.dtw_part[(int64_t)(rb + pos) * p.NT + nt] = s;
+    }
+  }
 }
 
 // x *= s on an accumulator element that stays in its AGPR (VALU arithmetic cannot
@@ -1608,7 +1650,10 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_dgrad_q4(GemmParams p) {
     for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row(i), n_e - 1);
     seg_lora_n(p.s2, e, nt, p.N, arow2, sm, vt, acc);
   }
-  if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
+  float dp[TM] = {};  // EPI_DOWN_DGRAD: the routing-weight gradient's partial sums
+  if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc, dp);
+  if constexpr (EPI == EPI_DOWN_DGRAD)
+    if (p.dtw_part) dtw_tile<TM>(p, dp, nt, m0, n_e, rb, wn, lane, reinterpret_cast<float *>(&sm));
 }
 
 // LORN: the LoRA term takes an N-major B ([K = r rows][N cols], the dgrad's A_gu / A_dn)
@@ -1707,7 +1752,10 @@ __global__ void __launch_bounds__(NTHR, 1) gemm_fwd_q4(GemmParams p) {
       seg_lora<EPI>(p.s2, e, nt, p.N, p.I, arow2, sm, vt, acc);
   }
 
-  if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc);
+  float dp[TM] = {};  // EPI_DOWN_DGRAD: the routing-weight gradient's partial sums
+  if (vt > 0) epilogue_t<TM, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, row0, wn * TN * 32, lane, esc, dp);
+  if constexpr (EPI == EPI_DOWN_DGRAD)
+    if (p.dtw_part) dtw_tile<TM>(p, dp, nt, m0, n_e, rb, wn, lane, reinterpret_cast<float *>(&sm));
 }
 
 // ---- Few routed rows per expert (decode-sized batches) ----
@@ -1864,7 +1912,10 @@ __global__ void __launch_bounds__(NTHR, kOccD) gemm_dgrad_q4n(GemmParams p) {
     for (int i = 0; i < ACH; ++i) arow2[i] = rb + min(m0 + a_row<TMN>(i < TMN ? i : 0), n_e - 1);
     seg_lora_n<TMN>(p.s2, e, nt, p.N, arow2, sm, vt, acc);
   }
-  epilogue_t<TMN, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc);
+  float dp[TMN] = {};  // EPI_DOWN_DGRAD: the routing-weight gradient's partial sums
+  epilogue_t<TMN, TN, BN, EPI>(p, acc, nt, m0, n_e, rb, 0, wn * TN * 32, lane, esc, dp);
+  if constexpr (EPI == EPI_DOWN_DGRAD)
+    if (p.dtw_part) dtw_tile<TMN>(p, dp, nt, m0, n_e, rb, wn, lane, reinterpret_cast<float *>(&sm));
 }
 }  // namespace fq
 
@@ -2782,12 +2833,28 @@ __global__ void __launch_bounds__(NTHR) dtopk_kernel(const uint16_t *__restrict_
   if (lane == 0) dtw[f] = s;
 }
 
+// d(top-k w) from the down dgrad's partial sums: pair f's row inv[f] has nt partial sums
+// of da_u * a (one per output column tile of I), added in tile order; a dropped pair
+// (row past the experts' segments) gets 0.  The sum over i of da_u * a equals the sum over
+// h of dy * y: y = a W~^T + the LoRA term is linear in a.
+__global__ void __launch_bounds__(NTHR) dtopk_sum(const float *__restrict__ part, int nt,
+                                                  const int32_t *__restrict__ inv, const int32_t *__restrict__ n_valid,
+                                                  int64_t R, float *__restrict__ dtw) {
+  const int64_t f = (int64_t)blockIdx.x * NTHR + threadIdx.x;
+  if (f >= R) return;
+  const int32_t pos = inv[f];
+  float s = 0.0f;
+  if (pos < *n_valid)
+    for (int q = 0; q < nt; ++q) s += part[(int64_t)pos * nt + q];
+  dtw[f] = s;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Layout {
   size_t perm, inv, off, tile_off, tile_off_n, counts, tw, ugu, udn, h, a, y, xq_c, xq_s, xq_d, xq_b, aq_c, aq_s, aq_d, aq_b, vdn, dh,
-      vgu, dxr, part, wchunk, wpart, absx;
+      vgu, dxr, part, wchunk, wpart, absx, dtwp;
   size_t total;
 };
 
@@ -2839,6 +2906,8 @@ Layout layout(const bqm_moe_desc *d) {
   // of them, each at most [r, max(2I, H)])
   L.wchunk = take(r > 0 ? 3 * (E + 1) * 4 : 0);
   L.wpart = take(r > 0 ? 2 * (size_t)cdiv((int64_t)R, wgrad_chunk((int64_t)R)) * r * (2 * I > H ? 2 * I : H) * 4 : 0);
+  // the routing-weight gradient's partial sums per routed row and down-dgrad column tile
+  L.dtwp = take(d->act_quant ? 0 : (size_t)R * cdiv(I, 256) * 4);
   // nested NF4: FP32 absmax' of the larger stack (gate_up), rebuilt before each forward GEMM
   const bool nested = d->w_gu.fmt == BQM_FMT_NF4 && (d->w_gu.nested || d->w_dn.nested);
   L.absx = take(nested ? E * 2 * I * H / 64 * 4 : 0);
@@ -3320,7 +3389,13 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
   // the 64-row tiles of the permutation, as in the forward
   const int32_t *tn = few_rows(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
   const int32_t *trem = rem_split(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
-  if (dtopk_w) {
+  // d(top-k w) = dy . y per routed pair.  With bf16 activations the down dgrad adds up
+  // da_u * a per column tile in its epilogue (y is linear in a) and dtopk_sum adds the
+  // tiles.  The rows of y are read back instead with NVFP4 activations (y's base term is
+  // linear in the quantized a, its LoRA term in the bf16 a) and for the dgrad over
+  // columnwise copies (whose DQ(Q(W^T))^T is not the forward's weight).
+  const bool fused_dtw = dtopk_w && !d->act_quant && !col;
+  if (dtopk_w && !fused_dtw) {
     mark(d, BQM_STAGE_DTOPK, 0, s);
     dtopk_kernel<<<(int)cdiv(R, NTHR / 64), NTHR, 0, s>>>(dy, w.at<uint16_t>(w.L.y), w.at<int32_t>(w.L.inv),
                                                           w.at<int32_t>(w.L.off) + d->E, R, d->k, d->H, dtopk_w);
@@ -3349,6 +3424,7 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     p.out0 = dh;
     p.h_in = w.at<float>(w.L.h);
     p.tw = w.at<float>(w.L.tw);
+    p.dtw_part = fused_dtw ? w.at<float>(w.L.dtwp) : nullptr;
     if (col)
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fq<A_GATHER, EPI_DOWN_DGRAD, true>(p, R, s, "down dgrad (columnwise)")));
     else if (nf4) {
@@ -3359,6 +3435,13 @@ bqm_status dgrad_impl(const bqm_moe_desc *d, const bqm_qtensor *col_gu, const bq
     }
     else
       BQM_STAGE(d, BQM_STAGE_DOWN_DGRAD, s, (launch_fd<A_GATHER, EPI_DOWN_DGRAD>(p, R, s, "down dgrad", tn, trem)));
+    if (fused_dtw) {
+      mark(d, BQM_STAGE_DTOPK, 0, s);
+      dtopk_sum<<<(int)cdiv(R, NTHR), NTHR, 0, s>>>(w.at<float>(w.L.dtwp), p.NT, w.at<int32_t>(w.L.inv),
+                                                    w.at<int32_t>(w.L.off) + d->E, R, dtopk_w);
+      mark(d, BQM_STAGE_DTOPK, 1, s);
+      BQM_TRY(launch_status("dtopk_sum"));
+    }
   }
   // V_gu = s dh B_gu  [R, r]
   if (r > 0) {
