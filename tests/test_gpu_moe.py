@@ -128,7 +128,8 @@ def test_streaming_forward():
     # expert per pass.  T = 1; zipf routing over 128 experts (experts above 16 rows: several
     # passes; the 16 empty experts NaN-poisoned, never read); one expert with about 70
     # rows (two 64-row tiles); H = 320, I = 192 (a half 128-deep block ends each K);
-    # NVFP4 activations; LoRA rank 72 with the shared A; 2 and 4 rows per expert on
+    # NVFP4 activations; LoRA rank 72 with the shared A; no LoRA; H = I = 64 (one half
+    # block); 2 and 4 rows per expert on
     # average (both forward GEMMs streaming, then down only); K of 4096 (the waves split
     # K; shorter K gives each wave its own column block), bf16 and NVFP4 activations
     compare_full(small("st_one", T=1, E=16, k=8))
@@ -141,6 +142,8 @@ def test_streaming_forward():
     compare_full(small("st_odd", H=320, I=192, E=12, T=3, k=4))
     compare_full(small("st_w4a4", act_quant=True, H=768, I=384, E=16, T=4, k=4))
     compare_full(small("st_r72_sh", r=72, shared_a=True, E=32, T=8, k=4), lora_scale=0.5)
+    compare_full(small("st_r0", r=0, E=16, T=4, k=4))
+    compare_full(small("st_k64", H=64, I=64, E=8, T=2, k=2))
 
 
 def test_few_rows_activation_dynamic_range():
