@@ -613,6 +613,9 @@ def main():
                  "algorithmic_bytes": conv_bytes,
                  "note": "per-tensor scale from the stack's own amax: the input is read twice (amax pass, "
                          "then quantize pass); algorithmic bytes count one read",
+                 # the bytes this mode has to move: the bf16 stacks twice, the codes and scales once
+                 "two_read_bytes": conv_bytes + n_el * 2,
+                 "two_read_hbm_frac": (conv_bytes + n_el * 2) / qms / 1e6 / PEAK_HBM_GBS,
                  "given_scale": {"ms": gms, "GB/s": conv_bytes / gms / 1e6,
                                  "hbm_frac": conv_bytes / gms / 1e6 / PEAK_HBM_GBS}}
         wgu, wdn = qgu, qdn
