@@ -8,8 +8,8 @@ namespace bqm {
 // Stable counting sort of R routed pairs by expert (route.hip).  counts_ws needs
 // permute_ws_bytes(R, E).  If tile_off != NULL it also receives the prefix sum of
 // ceil(count_e / bm) over experts ([E+1] entries); tile_off2 likewise for bm2.  With
-// w_in, the R routing weights are also copied to w_out (inside the one-launch
-// permutation of decode-sized batches).
+// w_in, the R routing weights are also copied to w_out (by the permutation's own
+// kernels: no separate copy).
 size_t permute_ws_bytes(int64_t R, int E);
 bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *perm, int32_t *inv,
                           int32_t *offsets, int32_t *counts_ws, int bm, int32_t *tile_off, int bm2,

@@ -228,12 +228,20 @@ __device__ __forceinline__ uint64_t lanes_equal(int v) {
 __global__ void __launch_bounds__(64) perm_scatter(const int32_t *__restrict__ idx, int64_t R, int E,
                                                    const int32_t *__restrict__ base,
                                                    int32_t *__restrict__ perm,
-                                                   int32_t *__restrict__ inv) {
+                                                   int32_t *__restrict__ inv, const float *__restrict__ w_in,
+                                                   float *__restrict__ w_out) {
   extern __shared__ int32_t cnt[];
   const int lane = threadIdx.x;
   for (int e = lane; e <= E; e += 64) cnt[e] = base[(int64_t)blockIdx.x * (E + 1) + e];
-  __syncthreads();
   const int64_t b = (int64_t)blockIdx.x * kChunk;
+  if (w_in)  // this chunk's routing weights, copied on the way (16 bytes per lane and step)
+    for (int64_t f = b + 4 * lane; f < b + kChunk && f < R; f += 256) {
+      if (f + 4 <= R)
+        *reinterpret_cast<float4 *>(w_out + f) = *reinterpret_cast<const float4 *>(w_in + f);
+      else
+        for (int64_t g = f; g < R; ++g) w_out[g] = w_in[g];
+    }
+  __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull, upto = lane == 63 ? ~0ull : (2ull << lane) - 1ull;
   for (int s = 0; s < kChunk && b + s < R; s += 64) {
     int64_t f = b + s + lane;
@@ -348,10 +356,6 @@ bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *pe
                                                          perm, inv, w_in, w_out);
     return launch_status("perm_one");
   }
-  if (R > 0 && w_in) {
-    if (hipMemcpyAsync(w_out, w_in, R * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
-      return launch_status("copy of routing weights");
-  }
   const int nchunks = (int)cdiv(R, kChunk);
   if (R > 0) {
     perm_hist<<<nchunks, 256, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws);
@@ -362,7 +366,7 @@ bqm_status permute_launch(const int32_t *topk_idx, int64_t R, int E, int32_t *pe
   bqm_status st = launch_status("perm_scan");
   if (st != BQM_OK) return st;
   if (R > 0) {
-    perm_scatter<<<nchunks, 64, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws, perm, inv);
+    perm_scatter<<<nchunks, 64, (E + 1) * sizeof(int32_t), s>>>(topk_idx, R, E, counts_ws, perm, inv, w_in, w_out);
     st = launch_status("perm_scatter");
   }
   return st;
