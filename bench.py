@@ -292,7 +292,7 @@ def time_layer(s, inp, wgu, wdn, ev, sh, steps, warmup):
     return res
 
 
-def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 32, 64, 256), reps=20, warmup=3):
+def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 32, 64, 256), reps=20, warmup=3, graph=True):
     """Decode-shaped forward (route + moe_fwd only) at a few tokens over the same
     quantized experts and LoRA: the time against reading each hit expert's NVFP4
     weights (codes + E4M3 scales of gate_up and down) once."""
@@ -320,9 +320,26 @@ def decode_sweep(shape, wgu, wdn, ev, sh, tokens=(1, 8, 32, 64, 256), reps=20, w
         for _ in range(warmup):
             run()
         ms = time_calls(ev, sh, run, reps)
+        # the same forward captured once in a HIP graph and replayed (no launch work on the
+        # host per forward): captured on a side stream after warmup, replayed on this one
+        gms = None
+        if graph:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                run()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run()
+            torch.cuda.synchronize()
+            gms = time_calls(ev, sh, g.replay, reps)
+            del g
         hit = int(torch.unique(idx).numel())
         wbytes = hit * per_expert
-        rows.append({"T": T, "ms_per_forward": round(ms, 4), "experts_hit": hit,
+        rows.append({"T": T, "ms_per_forward": round(ms, 4),
+                     "ms_per_forward_graph_replay": None if gms is None else round(gms, 4), "experts_hit": hit,
                      "hit_weight_bytes": int(wbytes), "weight_read_GB/s": round(wbytes / (ms * 1e-3) / 1e9, 1),
                      "weight_read_frac": round(wbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
         del inp, d, ws, idx, tw, out

@@ -146,6 +146,67 @@ def test_streaming_forward():
     compare_full(small("st_k64", H=64, I=64, E=8, T=2, k=2))
 
 
+def test_decode_forward_graph_replay():
+    # the decode-shaped forward (route + moe_fwd, the weight-streaming GEMMs) captured once
+    # in a HIP graph and replayed: the library launches only kernels on the caller's stream
+    # (no copies, fills or host synchronization), so every replay, with eager forwards on
+    # other inputs and host synchronizations between the replays, gives the eager bits
+    import torch
+    import bit_quantized_moe_amd as bqm
+    dev = gpu()
+    shape = small("graph", T=4, E=16, k=4)
+    ia = synth.layer_inputs(shape, device="cpu")
+    ib = synth.layer_inputs(dataclasses.replace(shape, seed=shape.seed + 1), device="cpu")
+    qgu = bqm.quantize_stack(ia.w_gu.to(dev), shape.fmt)
+    qdn = bqm.quantize_stack(ia.w_dn.to(dev), shape.fmt)
+    d = bqm.MoEDesc(shape.T, shape.H, shape.I, shape.E, shape.k, shape.r, qgu, qdn, A_gu=ia.A_gu.to(dev),
+                    B_gu=ia.B_gu.to(dev), A_dn=ia.A_dn.to(dev), B_dn=ia.B_dn.to(dev))
+    ws = torch.empty(bqm.bqm_moe_workspace_size(d), dtype=torch.uint8, device=dev)
+    x = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=dev)
+    lg = torch.empty((shape.T, shape.E), dtype=torch.float32, device=dev)
+    idx = torch.empty((shape.T, shape.k), dtype=torch.int32, device=dev)
+    tw = torch.empty((shape.T, shape.k), dtype=torch.float32, device=dev)
+    out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=dev)
+
+    def load(inp):
+        x.copy_(inp.x.to(dev))
+        lg.copy_(inp.logits.to(dev))
+
+    def run():
+        bqm.bqm_route(lg, shape.T, shape.E, shape.k, 0, idx, tw)
+        bqm.bqm_moe_fwd(d, x, idx, tw, out, ws)
+
+    ref = {}
+    for name, inp in (("a", ia), ("b", ib)):
+        load(inp)
+        run()
+        torch.cuda.synchronize()
+        ref[name] = (out.clone(), idx.clone())
+    assert not torch.equal(ref["a"][0], ref["b"][0])
+    load(ia)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for rep, name in enumerate("abab"):
+        load(ia if name == "a" else ib)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[name][0]) and torch.equal(idx, ref[name][1]), f"replay {rep} ({name})"
+        # eager work between the replays: a forward on the other input into other buffers
+        other = ib if name == "a" else ia
+        o2 = torch.empty_like(out)
+        bqm.bqm_moe_fwd(d, other.x.to(dev), idx.clone(), tw.clone(), o2, ws)
+        torch.cuda.synchronize()
+    log("  graph replays match the eager forward bit for bit")
+
+
 def test_few_rows_activation_dynamic_range():
     # a decode-sized batch (the 64-row tile configuration) whose tokens are scaled by
     # 2^40 and 2^-40, one all-zero token and one token whose elements span 2^-30 .. 2^30,
