@@ -743,6 +743,14 @@ def main():
         others["qwen3_30b_a3b_w4a4"] = config_block(s3, r3, "nvfp4-4over6-rowwise, activations nvfp4 per token")
         del inp3, q3gu, q3dn
         torch.cuda.empty_cache()
+        # the tiny workload (8 experts, 64 tokens): every launch is a few microseconds
+        s1t = synth.TINY
+        inp1t = synth.layer_inputs(s1t, device=dev)
+        q1gu = bqm.quantize_stack(inp1t.w_gu, s1t.fmt)
+        q1dn = bqm.quantize_stack(inp1t.w_dn, s1t.fmt)
+        r1t = time_layer(s1t, inp1t, q1gu, q1dn, ev, sh, max(10, args.steps), 3)
+        others["tiny"] = config_block(s1t, r1t, "nvfp4-4over6-rowwise")
+        del inp1t, q1gu, q1dn
         # the GLM layer with the adapter layout of the GLM page (one LoRA-A shared by all
         # experts, per-expert LoRA-B) over the same NVFP4 experts
         s_sh = dataclasses.replace(shape, shared_a=True, name="glm_shared_lora_a")
