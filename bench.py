@@ -451,9 +451,12 @@ def summarize_counters(root, min_us=300.0):
             dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             name[r["Dispatch_Id"]] = re.sub(r"\(anonymous namespace\)::", "", r["Kernel_Name"])
     ctr = collections.defaultdict(lambda: collections.defaultdict(float))
-    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv*"), recursive=True):
         for r in csv.DictReader(open(f)):
             ctr[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+            if r["Dispatch_Id"] not in dur:  # no kernel trace kept: the counter rows carry the times
+                dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                name[r["Dispatch_Id"]] = re.sub(r"\(anonymous namespace\)::", "", r["Kernel_Name"])
     agg = collections.defaultdict(lambda: [0, 0.0, collections.defaultdict(float)])
     for d, t in dur.items():
         if t < min_us * 1e3 or d not in ctr:
