@@ -586,26 +586,109 @@ __global__ void __launch_bounds__(kThreads) nf4_dequant(const uint32_t *__restri
   }
 }
 
-// Nested absmax, pass 1: one workgroup of 1024 threads per matrix of nb blocks.
-// Every thread adds a strided share of the FP32 absmax in FP64, the 1024 partial
-// sums are added in a fixed tree, and offset = fl32(sum / nb) goes to sd[m (1 + G)].
+// Nested absmax, pass 1: one workgroup of 1024 threads per matrix of nb blocks, and
+// offset = fl32(fl64(sum) / nb) to sd[m (1 + G)], where fl64(sum) is the exact sum of
+// the matrix's FP32 absmax rounded once to the nearest double (ties to even), so the
+// result depends on neither the order of the additions nor the number of threads.
+// The exact sum is an integer in units of 2^-149 (the least FP32 subnormal): each
+// value is its 24-bit significand shifted to its exponent, split over two 32-bit
+// limbs, and every thread adds its strided share into its own 64-bit limb counters
+// in LDS (no carries needed below 2^31 values).  The threads' counters are then
+// added in a tree (integer sums: exact in any order), and thread 0 propagates the
+// carries and rounds the top 53 bits.
 constexpr int64_t kNestGroup = 256;
 constexpr int kNestSumThreads = 1024;
+// 320 bits of two's complement: FP32 magnitudes up to 2^128 from 2^-149, times up to
+// 2^31 values, and the sign
+constexpr int kSumLimbs = 10;
+
+// the exact sum held in limb counters (limb j weighs 2^(32 j - 149)), rounded to the
+// nearest double, ties to even
+__device__ double limbs_to_f64(const int64_t (&acc)[kSumLimbs]) {
+  uint32_t l[kSumLimbs];
+  int64_t c = 0;
+#pragma unroll
+  for (int j = 0; j < kSumLimbs; ++j) {
+    const int64_t v = acc[j] + c;
+    l[j] = (uint32_t)((uint64_t)v & 0xffffffffu);
+    c = v >> 32;  // arithmetic: the carry or borrow into the next limb
+  }
+  const bool neg = c < 0;
+  if (neg) {  // magnitude of the two's complement value
+    uint64_t cy = 1;
+#pragma unroll
+    for (int j = 0; j < kSumLimbs; ++j) {
+      const uint64_t v = (uint64_t)(~l[j]) + cy;
+      l[j] = (uint32_t)v;
+      cy = v >> 32;
+    }
+  }
+  int h = kSumLimbs - 1;
+  while (h >= 0 && l[h] == 0) --h;
+  if (h < 0) return 0.0;
+  // bits [32 (h - 3), 32 (h + 1)) of the magnitude as a 128-bit window hi:lo
+  uint64_t hi = ((uint64_t)l[h] << 32) | (h >= 1 ? l[h - 1] : 0u);
+  uint64_t lo = ((uint64_t)(h >= 2 ? l[h - 2] : 0u) << 32) | (h >= 3 ? l[h - 3] : 0u);
+  bool sticky = false;
+  for (int j = 0; j < h - 3; ++j) sticky |= l[j] != 0;
+  const int lz = __clzll(hi);  // < 32: limb h is not zero
+  if (lz) {
+    hi = (hi << lz) | (lo >> (64 - lz));
+    lo <<= lz;
+  }
+  int top = 32 * h + 31 - lz;  // the leading bit, in units of 2^-149
+  uint64_t mant = hi >> 11;    // 53 bits
+  const bool half = (hi >> 10) & 1u;
+  sticky |= (hi & 0x3ffu) != 0 || lo != 0;
+  if (half && (sticky || (mant & 1u))) {
+    ++mant;
+    if (mant >> 53) {
+      mant >>= 1;
+      ++top;
+    }
+  }
+  const double r = ldexp((double)mant, top - 52 - 149);
+  return neg ? -r : r;
+}
 
 __global__ void __launch_bounds__(kNestSumThreads) nf4_nest_offset(const float *__restrict__ absmax, int64_t nb,
                                                                    int64_t G, float *__restrict__ sd) {
-  __shared__ double part[kNestSumThreads];
+  __shared__ unsigned long long acc[kSumLimbs][kNestSumThreads];
+  const int t = threadIdx.x;
   const int64_t m = blockIdx.x;
   const float *a = absmax + m * nb;
-  double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < nb; i += kNestSumThreads) acc += (double)a[i];
-  part[threadIdx.x] = acc;
+#pragma unroll
+  for (int j = 0; j < kSumLimbs; ++j) acc[j][t] = 0ull;
+  for (int64_t i = t; i < nb; i += kNestSumThreads) {
+    const uint32_t u = __float_as_uint(a[i]);
+    const uint32_t ex = (u >> 23) & 0xffu, fr = u & 0x7fffffu;
+    const uint64_t sig = ex ? (fr | 0x800000u) : fr;
+    if (!sig) continue;
+    const int b = ex ? (int)ex - 1 : 0;  // the significand's lowest bit, in units of 2^-149
+    const uint64_t sh = sig << (b & 31);
+    const int li = b >> 5;               // at most 8 (finite values: b <= 253)
+    uint64_t l0 = sh & 0xffffffffu, l1 = sh >> 32;
+    if (u >> 31) {  // negative values (not written by the quantizer) subtract, modulo 2^64
+      l0 = 0ull - l0;
+      l1 = 0ull - l1;
+    }
+    atomicAdd(&acc[li][t], (unsigned long long)l0);  // this thread's own counters
+    atomicAdd(&acc[li + 1][t], (unsigned long long)l1);
+  }
   __syncthreads();
   for (int w = kNestSumThreads / 2; w > 0; w >>= 1) {
-    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    if (t < w) {
+#pragma unroll
+      for (int j = 0; j < kSumLimbs; ++j) acc[j][t] += acc[j][t + w];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) sd[m * (1 + G)] = (float)(part[0] / (double)nb);
+  if (t == 0) {
+    int64_t s[kSumLimbs];
+#pragma unroll
+    for (int j = 0; j < kSumLimbs; ++j) s[j] = (int64_t)acc[j][0];
+    sd[m * (1 + G)] = (float)(limbs_to_f64(s) / (double)nb);
+  }
 }
 
 // Pass 2: one wave per group of 256 blocks (all matrices' groups in one grid),

@@ -144,14 +144,16 @@ bqm_status bqm_quantize_nf4(const uint16_t *x, bqm_qtensor *out /* host struct *
  * experts"; the page gives no
  * details, so this is QLoRA's published double quantization with E4M3 as the
  * 8-bit float).  Per matrix, over its absmax in row-major block order:
- *   offset = fl32(sum / nb) (sum in FP64, nb blocks), d = fl(absmax - offset),
+ *   offset = fl32(fl64(sum) / nb) (nb blocks; fl64(sum) is the exact sum of the
+ *   matrix's absmax rounded once to the nearest double), d = fl(absmax - offset),
  *   per group of 256 blocks s2 = fl(max|d| / 448) and codes e4m3_rne_sat(fl(d / s2))
  *   (sign bit for d < 0; s2 = 0 gives codes 0).
  * plain: an NF4 stack with FP32 absmax (as bqm_quantize_nf4 writes; read only).
  * nested: the same shape, fmt BQM_FMT_NF4 and nested = 1; its scales (uint8
  * [n_mat, rows, cols/64]) and s_dec (float [n_mat, 1 + G]) are written, and its
  * codes get the plain codes (copied unless the two pointers are equal).  The
- * FP64 sum is added in a fixed order, so repeated calls give identical bits. */
+ * sum is exact (integer fixed point) before its one rounding, so the result does
+ * not depend on the order of the additions; at most 2^31 blocks per matrix. */
 bqm_status bqm_nf4_nest(const bqm_qtensor *plain, bqm_qtensor *nested, void *stream);
 
 /* Dequantize a stack to bf16 [n_mat, rows, cols] (the DQ of DQ(Q(W)): GLM page,

@@ -212,11 +212,47 @@ def test_nf4_nested_absmax_bit_exact(shape):
     bqm.bqm_dequantize(n, y)
     ref = oq.dequantize_nf4_nested(oq.nest_absmax(oq.quantize_nf4(xh)))
     assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
-    # nesting twice gives the same bits (the FP64 sum runs in a fixed order)
+    # nesting twice gives the same bits (the offset comes from the exact sum)
     n2 = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev, nested=1)
     n2.codes = q.codes
     bqm.bqm_nf4_nest(q, n2)
     assert torch.equal(n2.scales, n.scales) and torch.equal(n2.s_dec, n.s_dec)
+
+
+def test_nf4_nested_offset_is_the_rounded_exact_sum():
+    """The nesting offset is fl32(fl64(exact sum) / nb): absmax 2^70, 2^46 and three of
+    2^16 in a matrix of 4096 blocks (every other block zero).  The exact sum rounds to
+    2^70 + 2^46 + 2^18, and divided by 2^12 it lies just above the FP32 midpoint
+    2^58 + 2^34, so the offset is 2^58 + 2^35; adding 2^16 to 2^70 + 2^46 one at a time
+    in FP64 loses each of them and ends on the midpoint itself, which rounds to 2^58.
+    A second matrix spreads absmax over 2^-120 .. 2^120 (random blocks)."""
+    import torch
+    dev = gpu()
+    bqm = _bqm()
+    shape = (2, 64, 4096)
+    log(f"nf4 nested offset, exact sum {shape}")
+    x = torch.zeros(shape, dtype=torch.float32)
+    for blk, v in ((0, 2.0 ** 70), (1, 2.0 ** 46), (2, 2.0 ** 16), (3, 2.0 ** 16), (4, 2.0 ** 16)):
+        x[0].view(-1)[64 * blk] = v
+    rng = np.random.default_rng(123)
+    e = rng.integers(-120, 121, size=shape[1] * shape[2] // 64)
+    mag = np.ldexp(1.0 + rng.integers(0, 128, size=e.size) / 128.0, e)
+    x[1].view(-1, 64)[:, 0] = torch.from_numpy(mag.astype(np.float32))
+    x = x.to(torch.bfloat16)
+    xh = np_f32(x)
+    off = oq.nest_absmax(oq.quantize_nf4(xh[0:1])).offset[0]
+    assert off == np.float32(2.0 ** 58 + 2.0 ** 35)     # the oracle's own arithmetic
+    xd = x.to(dev)
+    q = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev)
+    bqm.bqm_quantize_nf4(xd, q)
+    n = bqm.alloc_qtensor(bqm.FMT_NF4, *shape, device=dev, nested=1)
+    bqm.bqm_nf4_nest(q, n)
+    torch.cuda.synchronize()
+    _check_nested(q, n, xh)
+    y = torch.empty_like(xd)
+    bqm.bqm_dequantize(n, y)
+    ref = oq.dequantize_nf4_nested(oq.nest_absmax(oq.quantize_nf4(xh)))
+    assert (np_f32(y).view(np.uint32) == ref.view(np.uint32)).all()
 
 
 def test_nf4_nested_full_size_sampled():
