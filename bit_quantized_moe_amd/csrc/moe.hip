@@ -1944,7 +1944,7 @@ constexpr int OCC = 4;   // workgroups per CU (at most 128 registers per lane)
 constexpr int COLS = 32; // output columns per workgroup (two sets of 16)
 constexpr int LDS_BUDGET = 36 * 1024;  // LDS for the weight rows' scales and a pass's activation rows
 constexpr int RED_BYTES = NW * 4 * 64 * 16;  // the waves' partial sums (aliasing the rows)
-constexpr int LSL = 2;   // LoRA up-projection with KS: 32-deep slices per wave (its K at most 32 NW LSL)
+constexpr int LSL = 2;   // LoRA up-projection with KS > 1: 32-deep slices per wave (its K at most 32 KS LSL)
 constexpr int KSPLIT_MIN = 4096;  // the waves split K from this K on
 // word 3 of a raw buffer resource on this GPU family (32-bit elements, no swizzle)
 constexpr int kRsrcWord3 = 0x00020000;
@@ -1952,8 +1952,8 @@ constexpr int kRsrcWord3 = 0x00020000;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 // LDS bytes of the scales of the weight rows a workgroup reads (K / 16 bytes each):
-// 32 rows when its waves split K, NW times as many when each takes a column block
-__host__ __device__ constexpr int scale_lds_bytes(int64_t K, bool ks) { return (int)((ks ? 32 : 32 * NW) * (K / 16)); }
+// 32 rows per column block, NW / ks column blocks when ks waves split each one's K
+__host__ __device__ constexpr int scale_lds_bytes(int64_t K, int ks) { return (int)(32 * (NW / ks) * (K / 16)); }
 
 struct Blk {
   u32x4 c[2];  // 32 codes of this lane's column in each set (element 2b in the low nibble of byte b)
@@ -2018,19 +2018,22 @@ __device__ __forceinline__ void use_blk(const Blk &b, const uint32_t (&sw)[2], c
 
 // tile_off: the prefix of 64-row tiles per expert; NT: column blocks of COLS;
 // rows_pass rows of K activations (rounded up to a block) fit the dynamic LDS.
-// KS: the four waves split K (wave w takes blocks w, w + 4, ...) of the workgroup's one
-// column block and add their partial sums in LDS; otherwise each wave takes a whole
-// column block (the workgroup NW of them, sharing the activation rows), which gives
-// each wave a long enough run of blocks when K is short.
-template <int ASRC, int EPI, bool KS>
+// KS waves share a column block and split its K (wave w takes blocks w % KS,
+// w % KS + KS, ...), adding their partial sums in LDS; the workgroup holds NW / KS
+// column blocks, which share the activation rows.  KS = 1 gives each wave a whole
+// column block (a long enough run of blocks when K is short); KS = NW splits long K
+// four ways; KS = 2 halves each wave's run when there are too few workgroups to fill
+// the chip with whole column blocks.
+template <int ASRC, int EPI, int KS>
 __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
   static_assert(EPI == EPI_GATEUP || EPI == EPI_STORE, "forward epilogues");
+  static_assert(KS == 1 || KS == 2 || KS == NW, "waves per column block");
   constexpr bool kQA = ASRC == A_GATHER_Q || ASRC == A_ROWS_Q;
   constexpr bool kGather = ASRC == A_GATHER || ASRC == A_GATHER_Q;
-  constexpr int WS = KS ? NW : 1;  // block stride of a wave
-  // dynamic LDS: the scales of the weight rows [KS ? 32 : 32 NW][K / 16], then the pass's
-  // activation rows [rows_pass][Kp], which after the K loop (KS) hold the waves' partial
-  // sums [NW][4][64]: base sums of sets 0, 1, then LoRA sums of sets 0, 1
+  constexpr int WS = KS;  // block stride of a wave
+  // dynamic LDS: the scales of the weight rows [32 NW / KS][K / 16], then the pass's
+  // activation rows [rows_pass][Kp], which after the K loop (KS > 1) hold the waves'
+  // partial sums [NW][4][64]: base sums of sets 0, 1, then LoRA sums of sets 0, 1
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   __shared__ int tile_info[4];
   const int mt = blockIdx.x / p.NT, cbq = blockIdx.x % p.NT;
@@ -2055,8 +2058,8 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
   const int m0 = (mt - __builtin_amdgcn_readfirstlane(tile_info[3])) * 64, mend = min(m0 + 64, n_e);
   const int lane = threadIdx.x & 63, c = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: the block loop branches on it
-  const int cb = KS ? cbq : cbq * NW + w;  // this wave's column block
-  const int kw0 = KS ? w : 0;              // this wave's first block
+  const int cb = cbq * (NW / KS) + w / KS;  // this wave's column block
+  const int kw0 = w % KS;                    // this wave's first block
 
   // this lane's weight column in each set (a wave past the last column block reads the
   // last 16 rows and stores nothing)
@@ -2095,7 +2098,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
   // scales would cost one memory transaction per row and block
   const int SB = K / 16;  // scale bytes per weight row (a multiple of 4)
   uint8_t *sc = reinterpret_cast<uint8_t *>(xs);
-  uint8_t *scw = sc + (KS ? 0 : w * 32 * SB);  // this wave's rows
+  uint8_t *scw = sc + (w / KS) * 32 * SB;  // this wave's rows
   uint16_t *xa = reinterpret_cast<uint16_t *>(sc + scale_lds_bytes(K, KS));  // the activation rows after them
   f32x4(*red)[4][64] = reinterpret_cast<f32x4(*)[4][64]>(xa);
   const float esc = kQA ? 1.0f : uniform_load(s.b_sd + e);
@@ -2118,7 +2121,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
       const uint8_t *sg = reinterpret_cast<const uint8_t *>(s.b_sc) + e * (slice / 16);
       for (int j = 0; j < 2; ++j) {
         const uint8_t *src = sg + (int64_t)row0[j] * SB;
-        for (int c0 = KS ? 64 * w : 0; c0 < SB; c0 += 64 * WS) {  // 16-byte chunks of the 16 SB bytes
+        for (int c0 = 64 * kw0; c0 < SB; c0 += 64 * WS) {  // 16-byte chunks of the 16 SB bytes
           const uint32_t dst = (uint32_t)(uintptr_t)(const fq::lds_void *)(scw + 16 * j * SB + 16 * c0);
           if (c0 + lane < SB) fq::dma_b128(src + 16 * (c0 + lane), dst);
         }
@@ -2154,8 +2157,8 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
       }
     }
     // LoRA up-projection operands (A = the hi/lo pair rows at k < s2.K, B = the expert's
-    // LoRA matrix at k mod kmod): with KS, this wave's 32-deep slices w, w + NW, ...
-    // requested now; otherwise every slice, after the K loop
+    // LoRA matrix at k mod kmod): with KS > 1, this wave's 32-deep slices kw0, kw0 + KS,
+    // ... requested now; otherwise every slice, after the K loop
     const uint16_t *ar = reinterpret_cast<const uint16_t *>(l.a) + (int64_t)(rb + pos) * l.a_ld;
     auto lora_ops = [&](int k, u32x4 &la, u32x4(&lb)[2]) {
       const bool ok = k < l.K;
@@ -2165,10 +2168,10 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) lb[j] = ok ? *reinterpret_cast<const u32x4 *>(bl[j] + kb) : z;
     };
-    u32x4 la[KS ? LSL : 1], lb[KS ? LSL : 1][2];
-    if constexpr (KS) {
+    u32x4 la[KS > 1 ? LSL : 1], lb[KS > 1 ? LSL : 1][2];
+    if constexpr (KS > 1) {
 #pragma unroll
-      for (int q = 0; q < LSL; ++q) lora_ops(32 * (w + NW * q) + 8 * g, la[q], lb[q]);
+      for (int q = 0; q < LSL; ++q) lora_ops(32 * (kw0 + KS * q) + 8 * g, la[q], lb[q]);
     }
     // the direct copies are not tracked by the compiler's wait counts: wait for every load
     // issued so far (the row copies are the oldest), then the barrier
@@ -2206,7 +2209,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
     for (int u = 0; u < PF; ++u)
       if (j0 + PF + u < nb) use(u, j0 + PF + u);
     f32x4 lacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    if constexpr (KS) {
+    if constexpr (KS > 1) {
 #pragma unroll
       for (int q = 0; q < LSL; ++q)
 #pragma unroll
@@ -2221,23 +2224,23 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
     }
 
     f32x4 v[2], lv[2];
-    if constexpr (KS) {
-      // the four waves' partial sums, added in wave order by wave 0
+    if constexpr (KS > 1) {
+      // the partial sums of a column block's KS waves, added in wave order by its first
       __syncthreads();  // every wave is done reading the activation rows
       red[w][0][lane] = acc[0];
       red[w][1][lane] = acc[1];
       red[w][2][lane] = lacc[0];
       red[w][3][lane] = lacc[1];
       __syncthreads();
-      if (w == 0) {
+      if (kw0 == 0) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          v[j] = red[0][j][lane];
-          lv[j] = red[0][2 + j][lane];
+          v[j] = red[w][j][lane];
+          lv[j] = red[w][2 + j][lane];
 #pragma unroll
-          for (int q = 1; q < NW; ++q) {
-            v[j] += red[q][j][lane];
-            lv[j] += red[q][2 + j][lane];
+          for (int q = 1; q < KS; ++q) {
+            v[j] += red[w + q][j][lane];
+            lv[j] += red[w + q][2 + j][lane];
           }
         }
       }
@@ -2248,7 +2251,7 @@ __global__ void __launch_bounds__(NTHR, OCC) fwd_stream(GemmParams p) {
         lv[j] = lacc[j];
       }
     }
-    if (!KS || w == 0) {
+    if (kw0 == 0) {
       // lane (c, g) holds rows 4 g + t (t = 0..3) of column c of each set
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -3098,6 +3101,18 @@ bqm_status launch_fq(GemmParams p, int64_t R, hipStream_t s, const char *what, c
   return BQM_OK;
 }
 
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cus[dev];
+}
+
 // weight-streaming forward (few rows per expert): tile_off_n is the prefix of 64-row
 // tiles per expert; the output columns go in blocks of gv::COLS (gate_up: 16 i-values)
 template <int ASRC, int EPI>
@@ -3108,20 +3123,28 @@ bqm_status launch_gv(GemmParams p, int64_t R, int64_t T, hipStream_t s, const ch
   // more than T (an expert gets at most one row per token); a pass's rows live in LDS
   const int64_t K = p.s1.K;
   const int64_t Kp = cdiv(K, gv::KB) * gv::KB;
-  // the waves split K when K is long (enough blocks per wave), else each takes a column block
-  const bool ks = K >= gv::KSPLIT_MIN;
+  // the four waves split K when K is long (enough blocks per wave); else each takes a
+  // column block, or two waves share one when that leaves fewer workgroups than the
+  // chip holds at once (one round: halving each wave's run of dependent blocks beats
+  // the extra partial-sum step) and each of the two gets a block
+  int ks = K >= gv::KSPLIT_MIN ? gv::NW : 1;
+  if (ks == 1 && K >= 2 * gv::KB && p.s2.K <= 32 * 2 * gv::LSL &&
+      gemm_grid(R, p.E, (int)cdiv(NT, gv::NW / 2), fq::BMN) <= device_cus() * gv::OCC)
+    ks = 2;
   const int64_t xlds = gv::LDS_BUDGET - gv::scale_lds_bytes(K, ks);
   p.rows_pass = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)gv::RP, xlds / (2 * Kp), T}));
   const size_t xb = (size_t)p.rows_pass * Kp * 2;
-  const size_t lds = gv::scale_lds_bytes(K, ks) + (ks ? std::max<size_t>(xb, gv::RED_BYTES) : xb);
-  BQM_REQUIRE(!ks || p.s2.K <= 32 * gv::NW * gv::LSL, BQM_ERR_UNSUPPORTED,
-              "%s: LoRA K %d above the streaming kernel's %d", what, p.s2.K, 32 * gv::NW * gv::LSL);
-  p.NT = ks ? NT : (int)cdiv(NT, gv::NW);
+  const size_t lds = gv::scale_lds_bytes(K, ks) + (ks > 1 ? std::max<size_t>(xb, gv::RED_BYTES) : xb);
+  BQM_REQUIRE(ks == 1 || p.s2.K <= 32 * ks * gv::LSL, BQM_ERR_UNSUPPORTED,
+              "%s: LoRA K %d above the streaming kernel's %d", what, p.s2.K, 32 * ks * gv::LSL);
+  p.NT = (int)cdiv(NT, gv::NW / ks);
   const int grid = gemm_grid(R, p.E, p.NT, fq::BMN);
-  if (ks)
-    gv::fwd_stream<ASRC, EPI, true><<<grid, gv::NTHR, lds, s>>>(p);
+  if (ks == gv::NW)
+    gv::fwd_stream<ASRC, EPI, gv::NW><<<grid, gv::NTHR, lds, s>>>(p);
+  else if (ks == 2)
+    gv::fwd_stream<ASRC, EPI, 2><<<grid, gv::NTHR, lds, s>>>(p);
   else
-    gv::fwd_stream<ASRC, EPI, false><<<grid, gv::NTHR, lds, s>>>(p);
+    gv::fwd_stream<ASRC, EPI, 1><<<grid, gv::NTHR, lds, s>>>(p);
   return launch_status(what);
 }
 
