@@ -35,6 +35,7 @@
 // an expert's activation rows and weight rows in that XCD's L2.
 #include "common.h"
 #include "internal.h"
+#include "perm_dev.h"
 #include "nf4_levels.inc"
 
 #include <type_traits>
@@ -2441,6 +2442,56 @@ __global__ void __launch_bounds__(NTHR, 2) gemm_lora_proj(GemmParams p) {
 // slices' loads in flight at a time) and add their FP32 partial sums in a fixed
 // butterfly.  The tiled kernel walks K in 64-deep steps with one 256-row tile per
 // expert, which leaves most of the GPU idle when the batch is a few tokens.
+// one wave: the dot product of activation row arow of s.a with the weight row brow
+// over K = s.K; lane takes k = 8 lane + 512 j .. +8 and sums its products in order of
+// k, four 512-wide slices' loads in flight at a time, then the lanes are added
+__device__ __forceinline__ float lora_row_dot(const Seg &s, const uint16_t *brow, int64_t arow, int lane) {
+  const int K = s.K;
+  const uint16_t *ar = reinterpret_cast<const uint16_t *>(s.a) + arow * s.a_ld;
+  float acc = 0.0f;
+  int k0 = 8 * lane;
+  for (; k0 + 3 * 512 < K; k0 += 4 * 512) {
+    uint4 xa[4], ba[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      xa[u] = *reinterpret_cast<const uint4 *>(ar + k0 + 512 * u);
+      ba[u] = *reinterpret_cast<const uint4 *>(brow + k0 + 512 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t xv[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w}, bv[4] = {ba[u].x, ba[u].y, ba[u].z, ba[u].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc += bf16_lo(xv[h]) * bf16_lo(bv[h]);
+        acc += bf16_hi(xv[h]) * bf16_hi(bv[h]);
+      }
+    }
+  }
+  for (; k0 < K; k0 += 512) {
+    const uint4 xa = *reinterpret_cast<const uint4 *>(ar + k0);
+    const uint4 ba = *reinterpret_cast<const uint4 *>(brow + k0);
+    const uint32_t xv[4] = {xa.x, xa.y, xa.z, xa.w}, bv[4] = {ba.x, ba.y, ba.z, ba.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      acc += bf16_lo(xv[h]) * bf16_lo(bv[h]);
+      acc += bf16_hi(xv[h]) * bf16_hi(bv[h]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  return acc;
+}
+
+// output row `row`, column n of the [R, 2N] hi/lo pair layout (lane 0 stores)
+__device__ __forceinline__ void lora_row_store(const GemmParams &p, int64_t row, int n, float val, int lane) {
+  if (lane == 0) {
+    const uint32_t hb = f32_to_bf16(val);
+    const float lo2 = val - __uint_as_float(hb << 16);
+    p.out0[row * 2 * p.N + n] = (uint16_t)hb;
+    p.out0[row * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
+  }
+}
+
 template <int ASRC>
 __global__ void __launch_bounds__(256) lora_proj_rows(GemmParams p) {
   // workgroup row blockIdx.y: one 64-row tile of the prefix p.tile_off (at most 16 tokens:
@@ -2463,24 +2514,75 @@ __global__ void __launch_bounds__(256) lora_proj_rows(GemmParams p) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);  // one output column per wave
   if (n >= p.N) return;
   const Seg &s = p.s1;
-  const int K = s.K;
   const uint16_t *brow = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + (int64_t)n * s.b_cols;
   const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
   for (int i = 0; i < n_e; ++i) {
     const int64_t arow = ASRC == A_GATHER ? (int64_t)(p.perm[rb + i] / p.k) : (int64_t)(rb + i);
-    const uint16_t *ar = reinterpret_cast<const uint16_t *>(s.a) + arow * s.a_ld;
-    float acc = 0.0f;  // this lane's k = 8 lane + 512 j .. +8, summed in order of k
-    int k0 = 8 * lane;
-    // four 512-wide K slices at a time: their loads are in flight together
-    for (; k0 + 3 * 512 < K; k0 += 4 * 512) {
-      uint4 xa[4], ba[4];
+    lora_row_store(p, rb + i, n, lora_row_dot(s, brow, arow, lane) * osc, lane);
+  }
+}
+
+// The one-workgroup permutation and the forward's first LoRA projection (U = s X A^T
+// over gathered token rows) in one launch, for decode-sized batches (at most 1024
+// routed pairs): workgroup 0 runs the permutation; every other workgroup takes one
+// routed pair and 16 / wpc output columns, wpc waves per column (1, 2 or 4: as many as
+// keep the grid within one round of the chip), each wave the 512-wide K slices
+// q, q + wpc, ... (four slices' loads in flight at a time), the waves' sums added in
+// order through LDS.  A projection workgroup places its
+// pair's row itself, where the stable counting sort puts it (the number of pairs of
+// lower experts plus the pair's rank among its expert's pairs), so it does not wait
+// for workgroup 0; a dropped pair (expert index outside [0, E)) has no row.
+struct PermArgs {
+  const int32_t *idx;
+  int R, E;
+  int32_t *offsets;
+  int bm;
+  int32_t *tile_off;
+  int bm2;
+  int32_t *tile_off2;
+  int32_t *perm, *inv;
+  const float *w_in;
+  float *w_out;
+};
+constexpr int kPermLoraWaves = 16;  // waves per projection workgroup
+
+__global__ void __launch_bounds__(1024) perm_lora_rows(PermArgs a, GemmParams p, int wpc) {
+  if (blockIdx.x == 0) {
+    extern __shared__ int32_t cnt[];  // E + 1 buckets
+    perm_one_body(a.idx, a.R, a.E, a.offsets, a.bm, a.tile_off, a.bm2, a.tile_off2, a.perm, a.inv, a.w_in, a.w_out,
+                  cnt);
+    return;
+  }
+  __shared__ float part[kPermLoraWaves];
+  const int cols = kPermLoraWaves / wpc;  // output columns of this workgroup
+  const int ncg = (p.N + cols - 1) / cols;
+  const int f = (blockIdx.x - 1) / ncg;  // the routed pair (the grid holds R of them)
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = ((blockIdx.x - 1) % ncg) * cols + wave % cols, kq = wave / cols;
+  const int e = bucket_of(a.idx[f], a.E);
+  const int q = threadIdx.x;  // one pair per thread: R <= 1024
+  const int bq = q < a.R ? bucket_of(a.idx[q], a.E) : a.E + 1;
+  const int lower = __syncthreads_count(bq < e);
+  const int before = __syncthreads_count(q < f && bq == e);
+  if (e >= a.E) return;  // the whole workgroup
+  const bool ok = n < p.N;
+  const Seg &s = p.s1;
+  const int K = s.K;
+  const uint16_t *brow = reinterpret_cast<const uint16_t *>(s.b) + e * s.b_estride + (int64_t)(ok ? n : 0) * s.b_cols;
+  const uint16_t *ar = reinterpret_cast<const uint16_t *>(s.a) + (int64_t)(f / p.k) * s.a_ld;
+  float acc = 0.0f;  // this lane's k = 8 lane + 512 (kq + wpc j) .. +8, in order of k
+  const int step = 512 * wpc;
+  for (int k0 = 8 * lane + 512 * kq; k0 < K; k0 += 4 * step) {
+    uint4 xa[4], ba[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        xa[u] = *reinterpret_cast<const uint4 *>(ar + k0 + 512 * u);
-        ba[u] = *reinterpret_cast<const uint4 *>(brow + k0 + 512 * u);
+    for (int u = 0; u < 4; ++u)
+      if (k0 + step * u < K) {
+        xa[u] = *reinterpret_cast<const uint4 *>(ar + k0 + step * u);
+        ba[u] = *reinterpret_cast<const uint4 *>(brow + k0 + step * u);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 4; ++u)
+      if (k0 + step * u < K) {
         const uint32_t xv[4] = {xa[u].x, xa[u].y, xa[u].z, xa[u].w}, bv[4] = {ba[u].x, ba[u].y, ba[u].z, ba[u].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -2488,26 +2590,16 @@ __global__ void __launch_bounds__(256) lora_proj_rows(GemmParams p) {
           acc += bf16_hi(xv[h]) * bf16_hi(bv[h]);
         }
       }
-    }
-    for (; k0 < K; k0 += 512) {
-      const uint4 xa = *reinterpret_cast<const uint4 *>(ar + k0);
-      const uint4 ba = *reinterpret_cast<const uint4 *>(brow + k0);
-      const uint32_t xv[4] = {xa.x, xa.y, xa.z, xa.w}, bv[4] = {ba.x, ba.y, ba.z, ba.w};
+  }
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        acc += bf16_lo(xv[h]) * bf16_lo(bv[h]);
-        acc += bf16_hi(xv[h]) * bf16_hi(bv[h]);
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) {
-      const float val = acc * osc;
-      const uint32_t hb = f32_to_bf16(val);
-      const float lo2 = val - __uint_as_float(hb << 16);
-      p.out0[(int64_t)(rb + i) * 2 * p.N + n] = (uint16_t)hb;
-      p.out0[(int64_t)(rb + i) * 2 * p.N + p.N + n] = (uint16_t)f32_to_bf16(lo2);
-    }
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (lane == 0) part[wave] = acc;
+  __syncthreads();
+  if (kq == 0 && ok) {
+    float sum = part[wave];
+    for (int i = 1; i < wpc; ++i) sum += part[wave + cols * i];
+    const float osc = p.div_e ? p.out_scale / uniform_load(p.div_e + e) : p.out_scale;
+    lora_row_store(p, lower + before, n, sum * osc, lane);
   }
 }
 
@@ -3252,8 +3344,30 @@ bqm_status nf4_fp32_absmax(const bqm_qtensor &q, const Ws &w, Seg &seg, hipStrea
   return launch_status("nf4_unnest");
 }
 
+// U_gu = s X A_gu^T [R, r] (divided by the expert's s_dec when that folds)
+GemmParams lora_a_gu_params(const bqm_moe_desc *d, const Ws &w, const uint16_t *x) {
+  GemmParams p = base_params(d, w);
+  p.N = d->r;
+  p.NT = (int)cdiv(d->r, 64);
+  p.s1 = lora_a_seg(d, seg_bf16(x, d->H, d->A_gu, d->r, d->H, (int)d->H));
+  p.out_scale = d->lora_scale;
+  p.div_e = lora_folds_s_dec(d, true) ? d->w_gu.s_dec : nullptr;
+  p.out0 = w.at<uint16_t>(w.L.ugu);
+  return p;
+}
+
+// Decode-sized batches: the permutation and U_gu in one launch (perm_lora_rows) where
+// U_gu would run on the row kernel anyway (at most kFewTokens tokens) and the
+// permutation is the one-workgroup form; at most 1024 routed pairs
+bool fuse_perm_lora(const bqm_moe_desc *d) {
+  const int64_t R = d->T * d->k;
+  return d->r > 0 && d->T <= kFewTokens && R > 0 && R <= 1024 && few_rows(d);
+}
+
+// u_done: U_gu was computed with the permutation
 template <int ASRC_X>
-bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int64_t R, hipStream_t s, bool nf4) {
+bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int64_t R, hipStream_t s, bool nf4,
+                     bool u_done) {
   const int H = (int)d->H, I = (int)d->I, r = d->r;
   const float ls = d->lora_scale;
   uint16_t *ugu = w.at<uint16_t>(w.L.ugu), *udn = w.at<uint16_t>(w.L.udn);
@@ -3263,15 +3377,8 @@ bqm_status fwd_gemms(const bqm_moe_desc *d, const Ws &w, const uint16_t *x, int6
   const bool fold_fwd = lora_folds_s_dec(d, true);
   const int32_t *tn = few_rows(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;
   const int32_t *trem = rem_split(d) ? w.at<int32_t>(w.L.tile_off_n) : nullptr;  // remainder tiles
-  // U_gu = s X A_gu^T   [R, r]  (divided by the expert's s_dec when that folds)
-  if (r > 0) {
-    GemmParams p = base_params(d, w);
-    p.N = r;
-    p.NT = (int)cdiv(r, 64);
-    p.s1 = lora_a_seg(d, seg_bf16(x, H, d->A_gu, r, H, H));
-    p.out_scale = ls;
-    p.div_e = fold_fwd ? d->w_gu.s_dec : nullptr;
-    p.out0 = ugu;
+  if (r > 0 && !u_done) {
+    const GemmParams p = lora_a_gu_params(d, w, x);
     BQM_STAGE(d, BQM_STAGE_LORA_A_GU, s, (launch_lp<A_GATHER, false>(p, R, s, "lora_a gate_up", d->T, tn)));
   }
   // h = X~ W~_gu^T + U_gu B_gu^T; a = silu(g) u
@@ -3363,19 +3470,37 @@ extern "C" bqm_status bqm_moe_fwd(const bqm_moe_desc *d, const uint16_t *x, cons
     BQM_REQUIRE(aligned16(x) && aligned16(topk_idx) && aligned16(topk_w) && aligned16(out), BQM_ERR_ALIGN,
                 "bqm_moe_fwd: pointer not 16-byte aligned");
   }
-  BQM_STAGE(d, BQM_STAGE_PERMUTE, s, permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
-                         w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off),
-                         rem_split(d) ? -kRemRows : fq::BMN, w.at<int32_t>(w.L.tile_off_n), s, topk_w,
-                         w.at<float>(w.L.tw)));  // (and the copy of the routing weights)
+  const bool fused = fuse_perm_lora(d);
+  if (fused) {
+    // the permutation (and the copy of the routing weights) with U_gu
+    PermArgs pa{topk_idx, (int)R, d->E, w.at<int32_t>(w.L.off), BM, w.at<int32_t>(w.L.tile_off),
+                rem_split(d) ? -kRemRows : fq::BMN, w.at<int32_t>(w.L.tile_off_n), w.at<int32_t>(w.L.perm),
+                w.at<int32_t>(w.L.inv), topk_w, w.at<float>(w.L.tw)};
+    const GemmParams p = lora_a_gu_params(d, w, x);
+    // waves per output column: the most that keep the grid within the chip's slots for
+    // workgroups of 1024 threads (two per CU)
+    int wpc = 4;
+    while (wpc > 1 && 1 + R * cdiv(d->r, kPermLoraWaves / wpc) > 2 * (int64_t)device_cus()) wpc /= 2;
+    const int grid = 1 + (int)R * (int)cdiv(d->r, kPermLoraWaves / wpc);
+    mark(d, BQM_STAGE_PERMUTE, 0, s);
+    perm_lora_rows<<<grid, 1024, (d->E + 1) * sizeof(int32_t), s>>>(pa, p, wpc);
+    mark(d, BQM_STAGE_PERMUTE, 1, s);
+    BQM_TRY(launch_status("permutation and lora_a gate_up"));
+  } else {
+    BQM_STAGE(d, BQM_STAGE_PERMUTE, s, permute_launch(topk_idx, R, d->E, w.at<int32_t>(w.L.perm), w.at<int32_t>(w.L.inv), w.at<int32_t>(w.L.off),
+                           w.at<int32_t>(w.L.counts), BM, w.at<int32_t>(w.L.tile_off),
+                           rem_split(d) ? -kRemRows : fq::BMN, w.at<int32_t>(w.L.tile_off_n), s, topk_w,
+                           w.at<float>(w.L.tw)));  // (and the copy of the routing weights)
+  }
   if (R == 0) return BQM_OK;
   const bool nf4 = d->w_gu.fmt == BQM_FMT_NF4;
   if (d->act_quant) {
     BQM_STAGE(d, BQM_STAGE_ACT_QUANT_X, s,
               quantize_rows(x, d->T, d->H, w.at<uint8_t>(w.L.xq_c), w.at<uint8_t>(w.L.xq_s), w.at<float>(w.L.xq_d),
                             w.at<uint16_t>(w.L.xq_b), s));
-    BQM_TRY(fwd_gemms<A_GATHER_Q>(d, w, x, R, s, nf4));
+    BQM_TRY(fwd_gemms<A_GATHER_Q>(d, w, x, R, s, nf4, fused));
   } else {
-    BQM_TRY(fwd_gemms<A_GATHER>(d, w, x, R, s, nf4));
+    BQM_TRY(fwd_gemms<A_GATHER>(d, w, x, R, s, nf4, fused));
   }
   const int64_t items = d->T * (d->H / 8);
   mark(d, BQM_STAGE_COMBINE_FWD, 0, s);
