@@ -2885,15 +2885,29 @@ __global__ void __launch_bounds__(NTHR) combine_rows(const uint16_t *__restrict_
   for (int64_t it = (int64_t)blockIdx.x * NTHR + threadIdx.x; it < T * cpr; it += (int64_t)gridDim.x * NTHR) {
     const int64_t t = it / cpr, c = (it % cpr) * 8;
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int64_t f = t * k + j;
-      const int32_t pos = inv[f];
-      if (pos >= nv) continue;
-      const float w = tw ? tw[f] : 1.0f;
-      const uint4 v = *reinterpret_cast<const uint4 *>(rows + (int64_t)pos * H + c);
-      acc[0] += w * bf16_lo(v.x); acc[1] += w * bf16_hi(v.x); acc[2] += w * bf16_lo(v.y); acc[3] += w * bf16_hi(v.y);
-      acc[4] += w * bf16_lo(v.z); acc[5] += w * bf16_hi(v.z); acc[6] += w * bf16_lo(v.w); acc[7] += w * bf16_hi(v.w);
-    }
+    // the token's row positions, then its rows, each set of loads in flight together
+    // (k <= 16), then the sum in pair order
+    int32_t pos[16];
+    float w[16];
+    uint4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k) {
+        pos[j] = inv[t * k + j];
+        w[j] = tw ? tw[t * k + j] : 1.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k && pos[j] < nv) v[j] = *reinterpret_cast<const uint4 *>(rows + (int64_t)pos[j] * H + c);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j < k && pos[j] < nv) {
+        const float wj = w[j];
+        acc[0] += wj * bf16_lo(v[j].x); acc[1] += wj * bf16_hi(v[j].x);
+        acc[2] += wj * bf16_lo(v[j].y); acc[3] += wj * bf16_hi(v[j].y);
+        acc[4] += wj * bf16_lo(v[j].z); acc[5] += wj * bf16_hi(v[j].z);
+        acc[6] += wj * bf16_lo(v[j].w); acc[7] += wj * bf16_hi(v[j].w);
+      }
     uint32_t o[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) o[h] = f32_to_bf16(acc[2 * h]) | (f32_to_bf16(acc[2 * h + 1]) << 16);
