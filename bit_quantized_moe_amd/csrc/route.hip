@@ -79,9 +79,8 @@ __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ lo
   }
   sum = wave_sum_f32(sum);
   uint32_t taken = 0u;  // bit j: this lane's slot j already chosen
-  float wsum = 0.0f;
-  float wsel[16];
-  int isel[16];
+  float vsel = -INFINITY;  // lane r: the value and index chosen in round r
+  int isel = 0;
   for (int r = 0; r < k; ++r) {
     // lane-local best among untaken slots (larger value, then lower index)
     float bv = -INFINITY;
@@ -101,16 +100,20 @@ __global__ void __launch_bounds__(256) route_kernel(const float *__restrict__ lo
     bi = (int)wave_min_u32(kb == kmax ? (uint32_t)bi : 0x7FFFFFFFu);
     bv = __uint_as_float((kmax & 0x80000000u) ? (kmax & 0x7FFFFFFFu) : ~kmax);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    float w = expf(bv - mx) / sum;
-    wsel[r] = w;
-    isel[r] = bi;
-    wsum += w;
-  }
-  if (lane == 0) {
-    for (int r = 0; r < k; ++r) {
-      topk_idx[t * k + r] = isel[r];
-      topk_w[t * k + r] = renorm ? wsel[r] / wsum : wsel[r];
+    if (lane == r) {
+      vsel = bv;
+      isel = bi;
     }
+  }
+  // the chosen experts' softmax probabilities, lane r for round r (out of the selection
+  // loop, whose rounds depend on each other), and their sum in round order
+  const float w = lane < k ? expf(vsel - mx) / sum : 0.0f;
+  float wsum = 0.0f;
+  if (renorm)
+    for (int r = 0; r < k; ++r) wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), r));
+  if (lane < k) {
+    topk_idx[t * k + lane] = isel;
+    topk_w[t * k + lane] = renorm ? w / wsum : w;
   }
 }
 
