@@ -146,6 +146,17 @@ def test_streaming_forward():
     compare_full(small("st_k64", H=64, I=64, E=8, T=2, k=2))
 
 
+def test_fused_permutation_lora_a():
+    # up to 16 tokens the permutation and the gate_up LoRA-A projection share one launch,
+    # whose projection workgroups split K over 4, 2 or 1 waves per column as the grid
+    # allows: 4 (T = 2), 2 (rank 72: a partial last column group) and 1 (T = 16, k = 8,
+    # r = 64: 128 routed pairs; also with the shared A and NVFP4 activations)
+    compare_full(small("fz_w4", T=2, E=16, k=4, r=64))
+    compare_full(small("fz_w2", T=8, E=32, k=4, r=72), lora_scale=0.5)
+    compare_full(small("fz_w1", T=16, E=32, k=8, r=64))
+    compare_full(small("fz_w1_sh", T=16, E=32, k=8, r=64, shared_a=True, act_quant=True, H=768, I=384))
+
+
 def test_decode_forward_graph_replay():
     # the decode-shaped forward (route + moe_fwd, the weight-streaming GEMMs) captured once
     # in a HIP graph and replayed: the library launches only kernels on the caller's stream
@@ -441,21 +452,24 @@ def test_lora_rank_72_and_128():
     compare_full(small("r128_nf4", r=128, fmt="nf4", logits="zipf", E=32, T=200), poison_empty=True)
 
 
-def test_out_of_range_expert_indices_are_dropped():
+@pytest.mark.parametrize("T,bad", [(120, [(3, 1, -1), (50, 0, 16), (50, 3, 1000), (119, 2, -7)]),
+                                   (12, [(3, 1, -1), (5, 0, 16), (5, 3, 1000), (11, 2, -7)])])
+def test_out_of_range_expert_indices_are_dropped(T, bad):
     # caller-supplied indices outside [0, E) belong to no expert: the permutation puts
     # those pairs after offsets[E], and they add nothing to out, dX or the LoRA
     # gradients (their routing-weight gradient is 0).  The oracle sees the same layer
     # with those pairs' routing weights set to 0 (any expert stands in for them).
+    # T = 120 sorts in three passes; T = 12 runs the one-workgroup permutation fused
+    # with the gate_up LoRA-A projection, whose workgroups skip the dropped pairs
     import torch
     import bit_quantized_moe_amd as bqm
     dev = gpu()
-    shape = small("dropped", T=120, E=16, k=4, r=8)
+    shape = small("dropped", T=T, E=16, k=4, r=8)
     inp = synth.layer_inputs(shape, device="cpu")
     h = HostInputs(inp)
     idx, tw = __import__("oracle.routing", fromlist=["route"]).route(h.logits, shape.k)
     idx = idx.copy()
     tw = tw.copy()
-    bad = [(3, 1, -1), (50, 0, 16), (50, 3, 1000), (119, 2, -7)]
     for t, j, v in bad:
         idx[t, j] = v
     # oracle: the dropped pairs go to an expert the token does not use, with weight 0
